@@ -1,0 +1,274 @@
+#!/usr/bin/env python3
+"""Throughput of the tiled half-precision GEMM on one MI355X; prints ONE JSON line.
+
+A step is one call of tg_gemm over the 8192-cube fp16 workload with the fused
+bias + GELU(tanh) epilogue (inputs resident in HBM), which runs every stage of
+the tiled path: tile raster, global->LDS staging, swizzled LDS, the
+double-buffered k-loop, MFMA accumulation, the fused epilogue and the store.
+The 4096-cube (MFMA-bound, no epilogue) and the M=16 decode shape (HBM-bound,
+the skinny kernel) are timed as secondary lines in the same JSON object.
+
+Timing: W warm-up launches, then K launches back to back on torch's current
+stream (the stream tg_gemm is given), bracketed by torch.cuda.synchronize()
+and HIP events recorded on that stream; the per-launch time is the events'
+elapsed time / K.  The skinny shape rotates over 8 independent operand sets
+(720 MB, more than the 256 MB Infinity Cache) so every launch streams B from
+HBM.
+
+Roofline: FLOPs = 2*M*N*K (padded-tile work and the epilogue's few flops per
+output are not counted); algorithmic bytes = every operand once + C once (+
+bias).  Peaks are MI355X's published dense fp16/bf16 MFMA rate (2.5 PFLOP/s)
+and HBM3E bandwidth (8 TB/s).  The CPU baseline is the oracle (test
+infrastructure, untuned) timed on a bounded sample of rows of the same
+workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_MFMA_F16_TFLOPS = 2500.0   # MI355X dense fp16/bf16 MFMA
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
+METRIC = "GEMM TFLOP/s and % MFMA peak at 4096³/8192³ fp16; HBM GB/s at M=16"
+MAIN = "gemm_f16_8192x8192x8192_bias_gelu_tanh"
+SQUARE = "gemm_f16_4096x4096x4096"
+SKINNY = "gemm_f16_skinny_16x11008x4096"
+KERNEL_SOURCES = ["gemm_tiled.hip", "gemm_skinny.hip", "tg_device.h", "tg_launch.h", "tg_gemm_host.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+# ---------------------------------------------------------------- accounting
+
+def gemm_flops(M: int, N: int, K: int) -> int:
+    """Multiply-adds counted as two flops: 2*M*N*K."""
+    return 2 * M * N * K
+
+
+def gemm_alg_bytes(M: int, N: int, K: int, elt: int = 2, bias: bool = False) -> int:
+    """Each operand read once, C written once (the ideal of perfect on-chip reuse)."""
+    return elt * (M * K + K * N + M * N + (N if bias else 0))
+
+
+def naive_input_bytes(M: int, N: int, K: int, elt: int = 2) -> int:
+    """Inputs read by a one-output-at-a-time kernel: K values of A and K of B per output."""
+    return M * N * 2 * K * elt
+
+
+def staged_tile_bytes(bm: int, bn: int, bk: int, stages: int, elt: int = 2) -> int:
+    """On-chip staging of one A tile and one B tile per pipeline stage."""
+    return stages * (bm * bk + bk * bn) * elt
+
+
+def accumulator_regs_per_thread(bm: int, bn: int, threads: int, acc_bytes: int = 4) -> int:
+    """32-bit registers per thread holding a bm x bn accumulator."""
+    return bm * bn * acc_bytes // 4 // threads
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "tiled_dense_gemm_tg_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
+    were taken on the current kernel sources; else None."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("kernel_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------- timing
+
+def time_gemm(torch, tg, w, sets, steps, warmup):
+    """Per-launch time (ms) of tg_gemm over `sets` rotating operand sets."""
+    stream = torch.cuda.current_stream()
+    handle = stream.cuda_stream
+    calls = []
+    for A, B, bias, C in sets:
+        calls.append((A.data_ptr(), B.data_ptr(), bias.data_ptr() if bias is not None else None, C.data_ptr()))
+
+    def launch(i):
+        a, b, bi, c = calls[i % len(calls)]
+        st = tg.tg_gemm(w.M, w.N, w.K, w.dtype, a, b, bi, w.epilogue, c, handle)
+        if st != tg.TG_OK:
+            raise RuntimeError(f"tg_gemm failed: {tg.tg_status_string(st)}")
+
+    for i in range(warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(steps):
+        launch(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return ev0.elapsed_time(ev1) / steps, wall
+
+
+def device_operands(torch, I, w, copies=1):
+    ops = I.make_operands(w)
+    tdt = torch.float16 if w.dtype == I.F16 else torch.bfloat16
+
+    def dev(bits, shape):
+        import numpy as np
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(tdt).reshape(shape).to("cuda")
+
+    A = dev(ops.A, (w.M, w.K))
+    B = dev(ops.B, (w.K, w.N))
+    bias = dev(ops.bias, (w.N,)) if ops.bias is not None else None
+    sets = []
+    for c in range(copies):
+        sets.append((A if c == 0 else A.clone(), B if c == 0 else B.clone(),
+                     None if bias is None else (bias if c == 0 else bias.clone()),
+                     torch.empty((w.M, w.N), dtype=tdt, device="cuda")))
+    return ops, sets
+
+
+def cpu_baseline(I, w, ops, budget_s):
+    """The oracle on a bounded sample of rows of workload w (test infrastructure)."""
+    import numpy as np
+    import oracle
+    rows = ops.rows[:4]
+    t0 = time.perf_counter()
+    oracle.gemm(w.M, w.N, w.K, w.dtype, ops.A, ops.B, ops.bias, w.epilogue, rows)
+    probe = time.perf_counter() - t0
+    n = int(max(4, min(w.M, 4 * budget_s / max(probe, 1e-3))))
+    rng = np.random.Generator(np.random.PCG64(w.seeds["rows"] + 17))
+    rows = np.sort(rng.choice(w.M, size=n, replace=False)).astype(np.int64)
+    t0 = time.perf_counter()
+    oracle.gemm(w.M, w.N, w.K, w.dtype, ops.A, ops.B, ops.bias, w.epilogue, rows)
+    dt = time.perf_counter() - t0
+    return {
+        "value": round(gemm_flops(n, w.N, w.K) / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": oracle.max_threads(),
+        "kind": "oracle",
+        "sample": f"{n} of {w.M} rows of {w.name} (all {w.N} columns, K={w.K}), fp64 accumulate, "
+                  f"{dt:.2f} s wall incl. decoding B",
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for the CPU baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this GEMM runs on a single "
+              "MI355X and has no multi-GPU path.", file=sys.stderr)
+        return 2
+
+    import torch
+    import tiled_dense_gemm_tg_amd as tg
+    from tiled_dense_gemm_tg_amd import inputs as I
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    tg.load_library()
+    props = torch.cuda.get_device_properties(0)
+    log(f"device {props.name} ({getattr(props, 'gcnArchName', '?')}), {props.multi_processor_count} CUs")
+
+    w = I.WORKLOADS[MAIN]
+    log(f"main workload {w.name}: generating inputs")
+    ops, sets = device_operands(torch, I, w)
+    ms, wall = time_gemm(torch, tg, w, sets, args.steps, args.warmup)
+    flops = gemm_flops(w.M, w.N, w.K)
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"{w.name}: {ms * 1e3:.1f} us/launch, {tflops:.1f} TFLOP/s")
+
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "inputs": "fp16", "accumulate": "fp32",
+                   "output": "fp16", "epilogue": "bias + GELU(tanh)", "path": "tiled", "parallelism": "none"},
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": PEAK_MFMA_F16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_MFMA_F16_TFLOPS, 4),
+            "traffic": measured_traffic(w.name),
+            "algorithmic_flops_per_launch": flops,
+            "algorithmic_bytes_per_launch": gemm_alg_bytes(w.M, w.N, w.K, bias=True),
+            "timed_region_wall_s": round(wall, 4),
+        },
+    }
+    del sets
+    torch.cuda.empty_cache()
+
+    if not args.no_secondary:
+        sec = {}
+        w2 = I.WORKLOADS[SQUARE]
+        log(f"secondary {w2.name}")
+        _, sets2 = device_operands(torch, I, w2)
+        ms2, _ = time_gemm(torch, tg, w2, sets2, max(args.steps, 50), args.warmup)
+        t2 = gemm_flops(w2.M, w2.N, w2.K) / (ms2 * 1e-3) / 1e12
+        sec[w2.name] = {"us_per_launch": round(ms2 * 1e3, 2), "TFLOP/s": round(t2, 2),
+                        "frac_mfma_peak": round(t2 / PEAK_MFMA_F16_TFLOPS, 4), "path": "tiled",
+                        "traffic": measured_traffic(w2.name)}
+        del sets2
+        torch.cuda.empty_cache()
+        w4 = I.WORKLOADS[SKINNY]
+        log(f"secondary {w4.name} (8 rotating operand sets)")
+        _, sets4 = device_operands(torch, I, w4, copies=8)
+        ms4, _ = time_gemm(torch, tg, w4, sets4, max(args.steps, 400), args.warmup)
+        hot, _ = time_gemm(torch, tg, w4, sets4[:1], max(args.steps, 400), args.warmup)
+        nbytes = gemm_alg_bytes(w4.M, w4.N, w4.K)
+        gbps = nbytes / (ms4 * 1e-3) / 1e9
+        sec[w4.name] = {"us_per_launch": round(ms4 * 1e3, 3), "GB/s": round(gbps, 1),
+                        "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
+                        "hot_cache_GB/s_not_the_metric": round(nbytes / (hot * 1e-3) / 1e9, 1),
+                        "TFLOP/s": round(gemm_flops(w4.M, w4.N, w4.K) / (ms4 * 1e-3) / 1e12, 2),
+                        "path": "skinny", "traffic": measured_traffic(w4.name)}
+        log(f"{w4.name}: {ms4 * 1e3:.2f} us, {gbps:.0f} GB/s")
+        del sets4
+        result["secondary"] = sec
+
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline(I, w, ops, args.cpu_budget)
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,138 @@
+/*
+ * tg_gemm.h -- C interface of the MI355X (gfx950) tiled half-precision GEMM.
+ *
+ * The operation is the dense matrix product of the TileLang pages' central
+ * example ("TileLang: writing LLM GPU kernels by thinking in tiles", section
+ * 2 "The basic idea: a GPU should reuse data", and section 3's listing
+ * signature: A is MxK, B is KxN, C is MxN, 16-bit inputs and output with a
+ * 32-bit float accumulator), optionally followed by the fused epilogue of
+ * "Designing high-performance GPU kernels with TileLang", part 3 "Epilogue
+ * fusion": C = GELU(A*B + bias), computed while the product is still in
+ * registers.
+ *
+ *   C[i,j] = epi( sum_k A[i,k] * B[k,j] )          (sum accumulated in fp32)
+ *   epi(y) = y                                      TG_EPI_NONE
+ *          = y + bias[j]                            TG_EPI_BIAS
+ *          = gelu_tanh(y + bias[j])                 TG_EPI_BIAS_GELU_TANH
+ *   gelu_tanh(x) = 0.5*x*(1 + tanh(sqrt(2/pi)*(x + 0.044715*x^3)))
+ *
+ * followed by one round-to-nearest-even conversion to the output format.
+ *
+ * Layout and ownership
+ *   All matrices are dense, row-major and packed: A has row stride K, B has
+ *   row stride N, C has row stride N (no leading-dimension arguments).  A, B,
+ *   bias and C are all of `dtype`; bias has N entries and is indexed by the
+ *   column j.  All pointers are DEVICE pointers owned by the caller; the
+ *   library allocates nothing, keeps no per-call state and never frees.
+ *   No alignment is required: aligned pointers and K, N multiples of 8 only
+ *   select a faster kernel.
+ *
+ * Execution
+ *   tg_gemm enqueues its kernel on `stream` (a hipStream_t; NULL means the
+ *   default stream) and returns without synchronising: TG_OK means
+ *   "enqueued".  The call is thread-safe.  Validation happens on the host
+ *   before any HIP call, so argument errors never touch the device.
+ *
+ * Errors (returned, never thrown or aborted)
+ *   TG_ERR_INVALID_ARG  a negative M, N or K; an unknown dtype, epilogue or
+ *                       path; A or B NULL while M*K or K*N is non-zero; C NULL
+ *                       while M*N is non-zero; bias NULL with a bias epilogue
+ *                       or non-NULL with TG_EPI_NONE; C overlapping A, B or
+ *                       bias.
+ *   TG_ERR_UNSUPPORTED  an operand larger than 4 GiB, or an explicit path
+ *                       (tg_gemm_path) whose shape/alignment requirements the
+ *                       arguments do not meet.
+ *   TG_ERR_LAUNCH       the HIP runtime reported an error for the launch.
+ *
+ * Degenerate shapes
+ *   M == 0 or N == 0: nothing to compute, TG_OK, no launch.
+ *   K == 0: the sum is empty, so C = epi(0), i.e. bias / GELU(bias) / 0.
+ */
+#ifndef TG_GEMM_H
+#define TG_GEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { TG_F16 = 0, TG_BF16 = 1 } tg_dtype;
+
+typedef enum {
+    TG_EPI_NONE = 0,
+    TG_EPI_BIAS = 1,
+    TG_EPI_BIAS_GELU_TANH = 2
+} tg_epilogue;
+
+typedef enum {
+    TG_OK = 0,
+    TG_ERR_INVALID_ARG = 1,
+    TG_ERR_UNSUPPORTED = 2,
+    TG_ERR_LAUNCH = 3
+} tg_status;
+
+/*
+ * Kernel families.  TG_PATH_AUTO lets the library choose:
+ *   TG_PATH_SKINNY         M <= 16 (the decode-shaped product): streams B from
+ *                          HBM once; needs K % 8 == 0, N % 4 == 0, A 16-byte
+ *                          aligned, B, C and bias 8-byte aligned.
+ *   TG_PATH_TILED          256x256x64 MFMA tiles staged through LDS with
+ *                          16-byte loads; needs K % 8 == 0, N % 8 == 0, A, B
+ *                          and C 16-byte aligned, bias 8-byte aligned.
+ *   TG_PATH_TILED_GENERIC  the same tiling with element-granular loads and
+ *                          stores: any shape, any alignment.
+ *   TG_PATH_NONE           (reported by tg_gemm_plan only) nothing to launch.
+ */
+typedef enum {
+    TG_PATH_AUTO = 0,
+    TG_PATH_TILED = 1,
+    TG_PATH_TILED_GENERIC = 2,
+    TG_PATH_SKINNY = 3,
+    TG_PATH_NONE = 4
+} tg_path;
+
+/*
+ * C = epi(A*B [+ bias]) as described above, enqueued on `stream`.
+ *   M, N, K   matrix sizes (>= 0)
+ *   dtype     format of A, B, bias and C
+ *   A         device pointer, M x K, row-major
+ *   B         device pointer, K x N, row-major
+ *   bias      device pointer, N entries; NULL iff epilogue == TG_EPI_NONE
+ *   C         device pointer, M x N, row-major; written, never read
+ *   stream    hipStream_t or NULL
+ */
+tg_status tg_gemm(int64_t M, int64_t N, int64_t K, tg_dtype dtype,
+                  const void *A, const void *B, const void *bias, tg_epilogue epilogue,
+                  void *C, void *stream);
+
+/*
+ * As tg_gemm, but runs the kernel family `path` (TG_PATH_AUTO behaves as
+ * tg_gemm).  Returns TG_ERR_UNSUPPORTED when the arguments do not meet the
+ * family's requirements listed above.  Meant for tests and benchmarks that
+ * compare kernel families on the same inputs.
+ */
+tg_status tg_gemm_path(tg_path path, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
+                       const void *A, const void *B, const void *bias, tg_epilogue epilogue,
+                       void *C, void *stream);
+
+/*
+ * Validates the arguments exactly as tg_gemm does and reports in *path_out
+ * the kernel family tg_gemm would launch (TG_PATH_NONE when there is nothing
+ * to do).  Pure host code: makes no HIP call, reads no device memory.
+ */
+tg_status tg_gemm_plan(int64_t M, int64_t N, int64_t K, tg_dtype dtype,
+                       const void *A, const void *B, const void *bias, tg_epilogue epilogue,
+                       const void *C, tg_path *path_out);
+
+/* Static, human-readable name of a status code ("TG_OK", ...). */
+const char *tg_status_string(tg_status status);
+
+/* Static version string of the library. */
+const char *tg_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TG_GEMM_H */

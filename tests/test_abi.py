@@ -1,0 +1,141 @@
+"""The C interface on the host: exports, argument checks and kernel-family choice.
+
+None of these calls reaches the GPU: tg_gemm_plan is pure host code, and
+tg_gemm returns before any HIP call when its arguments are invalid or there is
+nothing to compute.  Pointers here are made-up integers that are never
+dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import tiled_dense_gemm_tg_amd as tg
+from tiled_dense_gemm_tg_amd import inputs as I
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tg_gemm.h")
+
+# made-up, suitably aligned device addresses in disjoint ranges
+PA, PB, PC, PBIAS = 0x7F0000000000, 0x7F1000000000, 0x7F2000000000, 0x7F3000000000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(tg_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(tg.LIBRARY):
+        pytest.fail("libtg_gemm.so is not built (run __graft_entry__.build())")
+    return tg.load_library()
+
+
+def test_header_declares_the_interface():
+    assert declared_functions() == sorted(tg.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_version_and_status_strings(lib):
+    assert "gfx950" in tg.tg_version()
+    assert tg.tg_status_string(tg.TG_OK) == "TG_OK"
+    assert tg.tg_status_string(tg.TG_ERR_INVALID_ARG) == "TG_ERR_INVALID_ARG"
+    assert tg.tg_status_string(tg.TG_ERR_UNSUPPORTED) == "TG_ERR_UNSUPPORTED"
+    assert tg.tg_status_string(tg.TG_ERR_LAUNCH) == "TG_ERR_LAUNCH"
+    assert tg.tg_status_string(99) == "TG_UNKNOWN_STATUS"
+
+
+def plan(M, N, K, dtype=I.F16, A=PA, B=PB, bias=None, epi=I.EPI_NONE, C=PC):
+    return tg.tg_gemm_plan(M, N, K, dtype, A, B, bias, epi, C)
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(M=-1, N=4, K=4), tg.TG_ERR_INVALID_ARG),
+    (dict(M=4, N=-1, K=4), tg.TG_ERR_INVALID_ARG),
+    (dict(M=4, N=4, K=-1), tg.TG_ERR_INVALID_ARG),
+    (dict(M=4, N=4, K=4, dtype=2), tg.TG_ERR_INVALID_ARG),
+    (dict(M=4, N=4, K=4, epi=3), tg.TG_ERR_INVALID_ARG),
+    (dict(M=4, N=4, K=4, A=None), tg.TG_ERR_INVALID_ARG),
+    (dict(M=4, N=4, K=4, B=None), tg.TG_ERR_INVALID_ARG),
+    (dict(M=4, N=4, K=4, C=None), tg.TG_ERR_INVALID_ARG),
+    (dict(M=4, N=4, K=4, epi=I.EPI_BIAS), tg.TG_ERR_INVALID_ARG),            # bias missing
+    (dict(M=4, N=4, K=4, epi=I.EPI_BIAS_GELU_TANH), tg.TG_ERR_INVALID_ARG),
+    (dict(M=4, N=4, K=4, bias=PBIAS), tg.TG_ERR_INVALID_ARG),                # bias without epilogue
+    (dict(M=4, N=4, K=4, C=PA + 8), tg.TG_ERR_INVALID_ARG),                  # C overlaps A
+    (dict(M=4, N=4, K=4, C=PB - 8), tg.TG_ERR_INVALID_ARG),                  # C overlaps B
+    (dict(M=4, N=4, K=4, epi=I.EPI_BIAS, bias=PC + 30), tg.TG_ERR_INVALID_ARG),  # bias inside C
+    (dict(M=1 << 16, N=1 << 15, K=8), tg.TG_ERR_UNSUPPORTED),              # C has 2^31 elements
+    (dict(M=8, N=8, K=(1 << 30) + 8), tg.TG_ERR_UNSUPPORTED),
+])
+def test_invalid_arguments(lib, args, status):
+    st, _ = plan(**args)
+    assert st == status
+    # tg_gemm rejects them the same way, before any HIP call
+    a = dict(dtype=I.F16, A=PA, B=PB, bias=None, epi=I.EPI_NONE, C=PC)
+    a.update(args)
+    st2 = tg.tg_gemm(a["M"], a["N"], a["K"], a["dtype"], a["A"], a["B"], a["bias"], a["epi"], a["C"], None)
+    assert st2 == status
+
+
+def test_plan_rejects_null_output_pointer(lib):
+    assert lib.tg_gemm_plan(4, 4, 4, 0, PA, PB, None, 0, PC, None) == tg.TG_ERR_INVALID_ARG
+
+
+def test_unknown_path_is_invalid(lib):
+    assert tg.tg_gemm_path(7, 4, 4, 4, I.F16, PA, PB, None, I.EPI_NONE, PC, None) == tg.TG_ERR_INVALID_ARG
+    assert tg.tg_gemm_path(tg.TG_PATH_NONE, 4, 4, 4, I.F16, PA, PB, None, I.EPI_NONE, PC, None) \
+        == tg.TG_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("M,N,K", [(0, 5, 5), (5, 0, 5), (0, 0, 0)])
+def test_empty_output_is_a_noop(lib, M, N, K):
+    assert plan(M, N, K, A=None, B=None, C=None) == (tg.TG_OK, tg.TG_PATH_NONE)
+    # nothing is launched, so this is safe without a GPU
+    assert tg.tg_gemm(M, N, K, I.F16, None, None, None, I.EPI_NONE, None, None) == tg.TG_OK
+
+
+def test_empty_K_allows_null_operands(lib):
+    assert plan(64, 64, 0, A=None, B=None, bias=PBIAS, epi=I.EPI_BIAS) == (tg.TG_OK, tg.TG_PATH_TILED)
+
+
+@pytest.mark.parametrize("M,N,K,ptrs,path", [
+    (16, 11008, 4096, {}, tg.TG_PATH_SKINNY),          # decode shape
+    (1, 4, 8, {}, tg.TG_PATH_SKINNY),
+    (16, 12, 8, {}, tg.TG_PATH_SKINNY),                 # N % 4 == 0 is enough
+    (17, 11008, 4096, {}, tg.TG_PATH_TILED),
+    (16, 11008, 4100, {}, tg.TG_PATH_TILED_GENERIC),    # K % 8 != 0
+    (16, 11010, 4096, {}, tg.TG_PATH_TILED_GENERIC),    # N % 4 != 0
+    (16, 11008, 4096, {"A": PA + 8}, tg.TG_PATH_TILED_GENERIC),
+    (4096, 4096, 4096, {}, tg.TG_PATH_TILED),
+    (8192, 8192, 8192, {"bias": PBIAS, "epi": I.EPI_BIAS_GELU_TANH}, tg.TG_PATH_TILED),
+    (4000, 4093, 4111, {"bias": PBIAS, "epi": I.EPI_BIAS_GELU_TANH, "dtype": I.BF16}, tg.TG_PATH_TILED_GENERIC),
+    (4000, 4096, 4104, {}, tg.TG_PATH_TILED),           # ragged M is fine for the vector path
+    (256, 256, 256, {"C": PC + 8}, tg.TG_PATH_TILED_GENERIC),
+    (256, 256, 256, {"B": PB + 2}, tg.TG_PATH_TILED_GENERIC),
+    (256, 256, 256, {"bias": PBIAS + 2, "epi": I.EPI_BIAS}, tg.TG_PATH_TILED_GENERIC),
+])
+def test_kernel_family_choice(lib, M, N, K, ptrs, path):
+    assert plan(M, N, K, **ptrs) == (tg.TG_OK, path)
+
+
+def test_explicit_path_requirements(lib):
+    # the skinny family needs M <= 16; the vector tiled family needs K % 8 == 0
+    assert tg.tg_gemm_path(tg.TG_PATH_SKINNY, 17, 64, 64, I.F16, PA, PB, None, 0, PC, None) == tg.TG_ERR_UNSUPPORTED
+    assert tg.tg_gemm_path(tg.TG_PATH_TILED, 64, 64, 60, I.F16, PA, PB, None, 0, PC, None) == tg.TG_ERR_UNSUPPORTED
+    assert tg.tg_gemm_path(tg.TG_PATH_TILED, 64, 64, 64, I.F16, PA + 4, PB, None, 0, PC, None) \
+        == tg.TG_ERR_UNSUPPORTED
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(tg, "_lib", None)
+    monkeypatch.setattr(tg, "LIBRARY", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        tg.load_library()

@@ -1,1 +1,134 @@
-"""MI355X-native tiled half-precision GEMM (gfx950), behind a C-ABI library."""
+"""MI355X-native tiled half-precision GEMM (gfx950), behind a C-ABI library.
+
+Thin ctypes binding of ``libtg_gemm.so`` (include/tg_gemm.h).  Functions with
+the C names take raw integers (device pointers, a hipStream_t handle) and
+return the C status; :func:`gemm` is a convenience over torch tensors that
+passes their device pointers and torch's current stream.  Every step of the
+computation runs in the HIP kernels; this module only marshals arguments.
+If the library has not been built this module raises instead of falling back
+to anything else.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+from .inputs import BF16, EPI_BIAS, EPI_BIAS_GELU_TANH, EPI_NONE, F16  # noqa: F401
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(PKG, "libtg_gemm.so")
+
+TG_OK = 0
+TG_ERR_INVALID_ARG = 1
+TG_ERR_UNSUPPORTED = 2
+TG_ERR_LAUNCH = 3
+
+TG_PATH_AUTO = 0
+TG_PATH_TILED = 1
+TG_PATH_TILED_GENERIC = 2
+TG_PATH_SKINNY = 3
+TG_PATH_NONE = 4
+PATH_NAMES = {TG_PATH_AUTO: "auto", TG_PATH_TILED: "tiled", TG_PATH_TILED_GENERIC: "tiled_generic",
+              TG_PATH_SKINNY: "skinny", TG_PATH_NONE: "none"}
+
+EXPORTED = ("tg_gemm", "tg_gemm_path", "tg_gemm_plan", "tg_status_string", "tg_version")
+
+_lib = None
+
+
+class TgError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {tg_status_string(status)} ({status})")
+        self.status = status
+
+
+def load_library():
+    """Load libtg_gemm.so (after torch, so both share one HIP runtime)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIBRARY):
+        raise RuntimeError(f"{LIBRARY} is not built; run `python -m tiled_dense_gemm_tg_amd.build` "
+                           "(or __graft_entry__.build()) first")
+    try:
+        import torch  # noqa: F401  -- loads the HIP runtime the library must share
+    except ImportError:
+        pass
+    lib = ctypes.CDLL(LIBRARY)
+    i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    lib.tg_gemm.argtypes = [i64, i64, i64, ci, vp, vp, vp, ci, vp, vp]
+    lib.tg_gemm.restype = ci
+    lib.tg_gemm_path.argtypes = [ci, i64, i64, i64, ci, vp, vp, vp, ci, vp, vp]
+    lib.tg_gemm_path.restype = ci
+    lib.tg_gemm_plan.argtypes = [i64, i64, i64, ci, vp, vp, vp, ci, vp, ctypes.POINTER(ci)]
+    lib.tg_gemm_plan.restype = ci
+    lib.tg_status_string.argtypes = [ci]
+    lib.tg_status_string.restype = ctypes.c_char_p
+    lib.tg_version.argtypes = []
+    lib.tg_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def tg_gemm(M, N, K, dtype, A, B, bias, epilogue, C, stream) -> int:
+    """C-ABI tg_gemm: pointers and stream are integers (0 / None for NULL)."""
+    return load_library().tg_gemm(M, N, K, dtype, A, B, bias, epilogue, C, stream)
+
+
+def tg_gemm_path(path, M, N, K, dtype, A, B, bias, epilogue, C, stream) -> int:
+    return load_library().tg_gemm_path(path, M, N, K, dtype, A, B, bias, epilogue, C, stream)
+
+
+def tg_gemm_plan(M, N, K, dtype, A, B, bias, epilogue, C):
+    """Returns (status, path) without touching the GPU."""
+    out = ctypes.c_int(-1)
+    st = load_library().tg_gemm_plan(M, N, K, dtype, A, B, bias, epilogue, C, ctypes.byref(out))
+    return st, out.value
+
+
+def tg_status_string(status: int) -> str:
+    return load_library().tg_status_string(status).decode()
+
+
+def tg_version() -> str:
+    return load_library().tg_version().decode()
+
+
+_EPI = {"none": EPI_NONE, "bias": EPI_BIAS, "bias_gelu_tanh": EPI_BIAS_GELU_TANH, "gelu": EPI_BIAS_GELU_TANH}
+
+
+def gemm(A, B, bias=None, epilogue: str = "none", out=None, path: int = TG_PATH_AUTO, stream=None):
+    """epilogue(A @ B [+ bias]) on torch device tensors (fp16 or bf16, row-major).
+
+    Returns ``out`` (allocated when not given).  Runs on ``stream`` or torch's
+    current stream; asynchronous like any torch op.
+    """
+    import torch
+    if A.dtype not in (torch.float16, torch.bfloat16):
+        raise TypeError("A must be float16 or bfloat16")
+    if B.dtype != A.dtype or (bias is not None and bias.dtype != A.dtype):
+        raise TypeError("A, B and bias must share one dtype")
+    if A.dim() != 2 or B.dim() != 2 or A.shape[1] != B.shape[0]:
+        raise ValueError(f"shapes {tuple(A.shape)} @ {tuple(B.shape)} do not chain")
+    for name, t in (("A", A), ("B", B), ("bias", bias), ("out", out)):
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    M, K = A.shape
+    N = B.shape[1]
+    epi = _EPI[epilogue]
+    if (epi == EPI_NONE) != (bias is None):
+        raise ValueError("bias must be given exactly when the epilogue uses it")
+    if bias is not None and bias.numel() != N:
+        raise ValueError("bias must have N entries")
+    if out is None:
+        out = torch.empty((M, N), dtype=A.dtype, device=A.device)
+    elif out.shape != (M, N) or out.dtype != A.dtype:
+        raise ValueError("out has the wrong shape or dtype")
+    dtype = F16 if A.dtype == torch.float16 else BF16
+    s = (stream if stream is not None else torch.cuda.current_stream(A.device)).cuda_stream
+    st = tg_gemm_path(path, M, N, K, dtype, A.data_ptr(), B.data_ptr(),
+                      bias.data_ptr() if bias is not None else None, epi, out.data_ptr(), s)
+    if st != TG_OK:
+        raise TgError(st, "tg_gemm")
+    return out

@@ -1,0 +1,165 @@
+// gemm_skinny.hip -- the M <= 16 (decode-shaped) GEMM for gfx950.
+//
+// With at most 16 rows of A the product does 2*M flops per B element, far
+// below what keeps MFMA busy, so the kernel is shaped by HBM: B is read from
+// memory exactly once, in 8-byte pieces that coalesce into 128-byte row
+// segments, with many loads in flight per lane.  The first TileLang page
+// ("TileLang: writing LLM GPU kernels by thinking in tiles", section 2,
+// "A back-of-the-envelope calculation") frames the same point: what costs is
+// moving each value, not the arithmetic.
+//
+// Layout of the work:
+//   * one workgroup per 64-column slab of B and C; its 8 waves split the K
+//     range into contiguous parts and each streams its part of the slab;
+//   * per 32-k step a lane loads rows kb + 8 h + r (r = 0..7, h = lane/16) of
+//     the four columns 4 p .. 4 p + 3 (p = lane % 16) and transposes them in
+//     registers (v_perm_b32) into four 8-k column vectors;
+//   * v_mfma_f32_16x16x32 takes those vectors as its 16-row operand (row p of
+//     MFMA j is column 4 p + j) and the 16 x 32 slice of A (8 k of row p per
+//     lane, one 16-byte load from L2) as its 16-column operand, so the 16
+//     MFMA columns are the (at most 16) rows of A;
+//   * the 8 waves' fp32 partial sums are added in LDS in a fixed order (no
+//     atomics, so results are reproducible), then the fused epilogue and
+//     8-byte stores.
+// Rows m >= M and k >= K are zero-filled in both operands.
+#include "tg_device.h"
+#include "tg_launch.h"
+
+namespace tg {
+namespace {
+
+constexpr int SLAB = 64;       // columns per workgroup
+constexpr int WAVES = 8;       // waves per workgroup, splitting K
+constexpr int UNROLL = 4;      // 32-k steps whose loads are in flight together
+constexpr int NTHREADS = 64 * WAVES;
+
+template <class T, int EPI>
+__global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args) {
+    __shared__ float red[WAVES][16][64];
+    const int M = args.M, N = args.N, K = args.K;
+    const uint16_t *__restrict__ A = args.A;
+    const uint16_t *__restrict__ B = args.B;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int p = lane & 15;
+    const int h = lane >> 4;
+    const int nb = blockIdx.x * SLAB;
+    const int ncol = nb + 4 * p;              // N % 4 == 0: all four columns valid or none
+    const bool col_ok = ncol < N;
+    const bool row_ok = p < M;
+
+    const int steps = (K + 31) / 32;
+    const int s_begin = (int)(((int64_t)steps * wave) / WAVES);
+    const int s_end = (int)(((int64_t)steps * (wave + 1)) / WAVES);
+
+    f32x4 acc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int s0 = s_begin; s0 < s_end; s0 += UNROLL) {
+        u32x2 vb[UNROLL][8];
+        u32x4 va[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const int kb = (s0 + u) * 32 + 8 * h;
+            const bool live = s0 + u < s_end;
+            u32x4 a = {0u, 0u, 0u, 0u};
+            if (live && row_ok && kb < K)          // K % 8 == 0: the 8 k are all valid or none
+                a = *reinterpret_cast<const u32x4 *>(A + (uint32_t)p * (uint32_t)K + kb);
+            va[u] = a;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                u32x2 b = {0u, 0u};
+                if (live && col_ok && kb + r < K)
+                    b = *reinterpret_cast<const u32x2 *>(B + (uint32_t)(kb + r) * (uint32_t)N + ncol);
+                vb[u][r] = b;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int d = j >> 1;
+                u32x4 w;
+                if (j & 1) {
+                    w.x = perm_hi(vb[u][0][d], vb[u][1][d]);
+                    w.y = perm_hi(vb[u][2][d], vb[u][3][d]);
+                    w.z = perm_hi(vb[u][4][d], vb[u][5][d]);
+                    w.w = perm_hi(vb[u][6][d], vb[u][7][d]);
+                } else {
+                    w.x = perm_lo(vb[u][0][d], vb[u][1][d]);
+                    w.y = perm_lo(vb[u][2][d], vb[u][3][d]);
+                    w.z = perm_lo(vb[u][4][d], vb[u][5][d]);
+                    w.w = perm_lo(vb[u][6][d], vb[u][7][d]);
+                }
+                acc[j] = T::mfma16(w, va[u], acc[j]);
+            }
+        }
+    }
+
+    // acc[j][e] is D_j[row 4 h + e][col p]: C[m = p][n = nb + 16 h + 4 e + j].
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            red[wave][4 * e + j][lane] = acc[j][e];
+    __syncthreads();
+    if (wave != 0)
+        return;
+
+    uint16_t *__restrict__ C = args.C;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int n = nb + 16 * h + 4 * e;
+        float y[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float s = 0.f;
+#pragma unroll
+            for (int w = 0; w < WAVES; ++w)
+                s += red[w][4 * e + j][lane];
+            y[j] = s;
+        }
+        if (!row_ok || n >= N)
+            continue;
+        float bv[4] = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (EPI != EPI_NONE) {
+            const u32x2 raw = *reinterpret_cast<const u32x2 *>(args.bias + n);
+            bv[0] = T::to_f32((uint16_t)(raw.x & 0xffff));
+            bv[1] = T::to_f32((uint16_t)(raw.x >> 16));
+            bv[2] = T::to_f32((uint16_t)(raw.y & 0xffff));
+            bv[3] = T::to_f32((uint16_t)(raw.y >> 16));
+        }
+        uint16_t o[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            o[j] = T::from_f32(epilogue<EPI>(y[j], bv[j]));
+        *reinterpret_cast<u32x2 *>(C + (uint32_t)p * (uint32_t)N + n) = u32x2{pack2(o[0], o[1]), pack2(o[2], o[3])};
+    }
+}
+
+template <class T, int EPI>
+hipError_t launch_typed(const GemmArgs &a, hipStream_t stream) {
+    const int slabs = (a.N + SLAB - 1) / SLAB;
+    hipLaunchKernelGGL((gemm_skinny_kernel<T, EPI>), dim3(slabs), dim3(NTHREADS), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <class T>
+hipError_t launch_epi(int epi, const GemmArgs &a, hipStream_t stream) {
+    switch (epi) {
+    case EPI_NONE: return launch_typed<T, EPI_NONE>(a, stream);
+    case EPI_BIAS: return launch_typed<T, EPI_BIAS>(a, stream);
+    default: return launch_typed<T, EPI_BIAS_GELU_TANH>(a, stream);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_skinny(int dtype, int epi, const GemmArgs &a, hipStream_t stream) {
+    return dtype == 0 ? launch_epi<F16>(epi, a, stream) : launch_epi<BF16>(epi, a, stream);
+}
+
+}  // namespace tg

@@ -1,0 +1,147 @@
+// tg_gemm_host.hip -- the C interface (include/tg_gemm.h): argument checks,
+// choice of kernel family and the launch on the caller's stream.
+//
+// Everything before the launch is plain host arithmetic on the arguments: no
+// HIP call, no device memory access, no allocation and no state, so invalid
+// arguments never reach the device and concurrent calls need no locking.
+#include "tg_gemm.h"
+#include "tg_launch.h"
+
+#include <stdint.h>
+
+#define TG_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int64_t kMaxElements = (int64_t(1) << 31) - 1;  // per operand: below 4 GiB of 16-bit values
+constexpr int64_t kMaxDim = int64_t(1) << 30;
+
+bool aligned(const void *p, uintptr_t bytes) { return (reinterpret_cast<uintptr_t>(p) % bytes) == 0; }
+
+// Number of elements of an r x c operand, or -1 if it exceeds kMaxElements.
+int64_t elements(int64_t r, int64_t c) {
+    if (r == 0 || c == 0)
+        return 0;
+    if (r > kMaxElements / c)
+        return -1;
+    return r * c;
+}
+
+bool overlaps(const void *p, int64_t pbytes, const void *q, int64_t qbytes) {
+    if (!p || !q || pbytes <= 0 || qbytes <= 0)
+        return false;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+    return a < b + static_cast<uintptr_t>(qbytes) && b < a + static_cast<uintptr_t>(pbytes);
+}
+
+struct Checked {
+    tg_status status;
+    bool noop;
+};
+
+Checked check_args(int64_t M, int64_t N, int64_t K, int dtype, const void *A, const void *B,
+                   const void *bias, int epilogue, const void *C) {
+    if (M < 0 || N < 0 || K < 0)
+        return {TG_ERR_INVALID_ARG, false};
+    if (dtype != TG_F16 && dtype != TG_BF16)
+        return {TG_ERR_INVALID_ARG, false};
+    if (epilogue != TG_EPI_NONE && epilogue != TG_EPI_BIAS && epilogue != TG_EPI_BIAS_GELU_TANH)
+        return {TG_ERR_INVALID_ARG, false};
+    if (epilogue == TG_EPI_NONE && bias != nullptr)
+        return {TG_ERR_INVALID_ARG, false};
+    if (M == 0 || N == 0)
+        return {TG_OK, true};
+    if (epilogue != TG_EPI_NONE && bias == nullptr)
+        return {TG_ERR_INVALID_ARG, false};
+    if (C == nullptr || (K > 0 && (A == nullptr || B == nullptr)))
+        return {TG_ERR_INVALID_ARG, false};
+    const int64_t na = elements(M, K), nb = elements(K, N), nc = elements(M, N);
+    const int64_t nbias = epilogue != TG_EPI_NONE ? N : 0;
+    if (overlaps(C, 2 * (nc < 0 ? kMaxElements : nc), A, 2 * (na < 0 ? kMaxElements : na)) ||
+        overlaps(C, 2 * (nc < 0 ? kMaxElements : nc), B, 2 * (nb < 0 ? kMaxElements : nb)) ||
+        overlaps(C, 2 * (nc < 0 ? kMaxElements : nc), bias, 2 * nbias))
+        return {TG_ERR_INVALID_ARG, false};
+    if (na < 0 || nb < 0 || nc < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
+        return {TG_ERR_UNSUPPORTED, false};
+    return {TG_OK, false};
+}
+
+bool skinny_ok(int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *bias, const void *C) {
+    return M <= 16 && K % 8 == 0 && N % 4 == 0 && aligned(A, 16) && aligned(B, 8) && aligned(C, 8) &&
+           aligned(bias, 8);
+}
+
+bool tiled_ok(int64_t N, int64_t K, const void *A, const void *B, const void *bias, const void *C) {
+    return K % 8 == 0 && N % 8 == 0 && aligned(A, 16) && aligned(B, 16) && aligned(C, 16) && aligned(bias, 8);
+}
+
+tg_path auto_path(int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *bias,
+                  const void *C) {
+    if (skinny_ok(M, N, K, A, B, bias, C))
+        return TG_PATH_SKINNY;
+    if (tiled_ok(N, K, A, B, bias, C))
+        return TG_PATH_TILED;
+    return TG_PATH_TILED_GENERIC;
+}
+
+}  // namespace
+
+TG_EXPORT tg_status tg_gemm_plan(int64_t M, int64_t N, int64_t K, tg_dtype dtype, const void *A,
+                                 const void *B, const void *bias, tg_epilogue epilogue, const void *C,
+                                 tg_path *path_out) {
+    if (path_out == nullptr)
+        return TG_ERR_INVALID_ARG;
+    const Checked c = check_args(M, N, K, dtype, A, B, bias, epilogue, C);
+    if (c.status != TG_OK)
+        return c.status;
+    *path_out = c.noop ? TG_PATH_NONE : auto_path(M, N, K, A, B, bias, C);
+    return TG_OK;
+}
+
+TG_EXPORT tg_status tg_gemm_path(tg_path path, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
+                                 const void *A, const void *B, const void *bias, tg_epilogue epilogue,
+                                 void *C, void *stream) {
+    if (path != TG_PATH_AUTO && path != TG_PATH_TILED && path != TG_PATH_TILED_GENERIC && path != TG_PATH_SKINNY)
+        return TG_ERR_INVALID_ARG;
+    const Checked c = check_args(M, N, K, dtype, A, B, bias, epilogue, C);
+    if (c.status != TG_OK || c.noop)
+        return c.status;
+    if (path == TG_PATH_AUTO)
+        path = auto_path(M, N, K, A, B, bias, C);
+    else if ((path == TG_PATH_SKINNY && !skinny_ok(M, N, K, A, B, bias, C)) ||
+             (path == TG_PATH_TILED && !tiled_ok(N, K, A, B, bias, C)))
+        return TG_ERR_UNSUPPORTED;
+
+    tg::GemmArgs a;
+    a.M = static_cast<int>(M);
+    a.N = static_cast<int>(N);
+    a.K = static_cast<int>(K);
+    a.A = static_cast<const uint16_t *>(A);
+    a.B = static_cast<const uint16_t *>(B);
+    a.bias = static_cast<const uint16_t *>(bias);
+    a.C = static_cast<uint16_t *>(C);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (path == TG_PATH_SKINNY)
+        e = tg::launch_skinny(dtype, epilogue, a, s);
+    else
+        e = tg::launch_tiled(dtype, epilogue, path == TG_PATH_TILED, a, s);
+    return e == hipSuccess ? TG_OK : TG_ERR_LAUNCH;
+}
+
+TG_EXPORT tg_status tg_gemm(int64_t M, int64_t N, int64_t K, tg_dtype dtype, const void *A, const void *B,
+                            const void *bias, tg_epilogue epilogue, void *C, void *stream) {
+    return tg_gemm_path(TG_PATH_AUTO, M, N, K, dtype, A, B, bias, epilogue, C, stream);
+}
+
+TG_EXPORT const char *tg_status_string(tg_status status) {
+    switch (status) {
+    case TG_OK: return "TG_OK";
+    case TG_ERR_INVALID_ARG: return "TG_ERR_INVALID_ARG";
+    case TG_ERR_UNSUPPORTED: return "TG_ERR_UNSUPPORTED";
+    case TG_ERR_LAUNCH: return "TG_ERR_LAUNCH";
+    }
+    return "TG_UNKNOWN_STATUS";
+}
+
+TG_EXPORT const char *tg_version(void) { return "tg_gemm 0.1.0 gfx950"; }

@@ -1,0 +1,27 @@
+// tg_launch.h -- internal interface between the host library and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tg {
+
+// Validated arguments of one GEMM; sizes fit in int32 because every operand
+// is at most 4 GiB (2^31 16-bit elements).
+struct GemmArgs {
+    int M, N, K;
+    const uint16_t *A;     // M x K row-major
+    const uint16_t *B;     // K x N row-major
+    const uint16_t *bias;  // N entries or nullptr
+    uint16_t *C;           // M x N row-major
+};
+
+// dtype: 0 fp16, 1 bf16; epi: 0 none, 1 bias, 2 bias + GELU(tanh).
+// vec: 16-byte loads (K % 8 == 0, N % 8 == 0, aligned operands) or
+// element-granular loads and stores.
+hipError_t launch_tiled(int dtype, int epi, bool vec, const GemmArgs &a, hipStream_t stream);
+
+// M <= 16, K % 8 == 0, N % 4 == 0, aligned operands.
+hipError_t launch_skinny(int dtype, int epi, const GemmArgs &a, hipStream_t stream);
+
+}  // namespace tg
