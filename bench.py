@@ -151,11 +151,14 @@ def cpu_baseline(I, w, ops, budget_s):
     """The oracle on a bounded sample of rows of workload w (test infrastructure)."""
     import numpy as np
     import oracle
-    rows = ops.rows[:4]
-    t0 = time.perf_counter()
-    oracle.gemm(w.M, w.N, w.K, w.dtype, ops.A, ops.B, ops.bias, w.epilogue, rows)
-    probe = time.perf_counter() - t0
-    n = int(max(4, min(w.M, 4 * budget_s / max(probe, 1e-3))))
+    probes = []
+    for k in (2, 34):
+        t0 = time.perf_counter()
+        oracle.gemm(w.M, w.N, w.K, w.dtype, ops.A, ops.B, ops.bias, w.epilogue, ops.rows[:k])
+        probes.append(time.perf_counter() - t0)
+    per_row = max((probes[1] - probes[0]) / 32, 1e-6)
+    fixed = max(probes[0] - 2 * per_row, 0.0)
+    n = int(max(4, min(w.M, (budget_s - fixed) / per_row)))
     rng = np.random.Generator(np.random.PCG64(w.seeds["rows"] + 17))
     rows = np.sort(rng.choice(w.M, size=n, replace=False)).astype(np.int64)
     t0 = time.perf_counter()
@@ -179,6 +182,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for the CPU baseline")
+    ap.add_argument("--workload", default=MAIN, help="workload timed as the main line (for profiling runs)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run torch's device copy of MIB MiB, 10 times (to scale HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this GEMM runs on a single "
@@ -192,17 +198,29 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {args.copy_calibration} MiB 10 times")
+        return 0
     tg.load_library()
     props = torch.cuda.get_device_properties(0)
     log(f"device {props.name} ({getattr(props, 'gcnArchName', '?')}), {props.multi_processor_count} CUs")
 
-    w = I.WORKLOADS[MAIN]
+    w = I.WORKLOADS[args.workload]
     log(f"main workload {w.name}: generating inputs")
     ops, sets = device_operands(torch, I, w)
     ms, wall = time_gemm(torch, tg, w, sets, args.steps, args.warmup)
     flops = gemm_flops(w.M, w.N, w.K)
     tflops = flops / (ms * 1e-3) / 1e12
     log(f"{w.name}: {ms * 1e3:.1f} us/launch, {tflops:.1f} TFLOP/s")
+    path_name = {I.EPI_NONE: "none", I.EPI_BIAS: "bias", I.EPI_BIAS_GELU_TANH: "bias + GELU(tanh)"}[w.epilogue]
+    st, path = tg.tg_gemm_plan(w.M, w.N, w.K, w.dtype, *[sets[0][i].data_ptr() if sets[0][i] is not None else None
+                                                        for i in (0, 1, 2)], w.epilogue, sets[0][3].data_ptr())
 
     result = {
         "metric": METRIC,
@@ -215,10 +233,11 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        "dtype": I.DTYPE_NAMES[w.dtype],
         "data": "synthetic",
-        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "inputs": "fp16", "accumulate": "fp32",
-                   "output": "fp16", "epilogue": "bias + GELU(tanh)", "path": "tiled", "parallelism": "none"},
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "inputs": I.DTYPE_NAMES[w.dtype],
+                   "accumulate": "fp32", "output": I.DTYPE_NAMES[w.dtype], "epilogue": path_name,
+                   "path": tg.PATH_NAMES.get(path, "?"), "parallelism": "none"},
         "roofline": {
             "bound": "mfma",
             "achieved": round(tflops, 2),
@@ -227,7 +246,7 @@ def main() -> int:
             "frac": round(tflops / PEAK_MFMA_F16_TFLOPS, 4),
             "traffic": measured_traffic(w.name),
             "algorithmic_flops_per_launch": flops,
-            "algorithmic_bytes_per_launch": gemm_alg_bytes(w.M, w.N, w.K, bias=True),
+            "algorithmic_bytes_per_launch": gemm_alg_bytes(w.M, w.N, w.K, bias=w.epilogue != I.EPI_NONE),
             "timed_region_wall_s": round(wall, 4),
         },
     }

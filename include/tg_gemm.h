@@ -39,7 +39,8 @@
  *                       while M*N is non-zero; bias NULL with a bias epilogue
  *                       or non-NULL with TG_EPI_NONE; C overlapping A, B or
  *                       bias.
- *   TG_ERR_UNSUPPORTED  an operand larger than 4 GiB, or an explicit path
+ *   TG_ERR_UNSUPPORTED  an operand of 2^31 or more elements (4 GiB), a
+ *                       dimension above 2^30, or an explicit path
  *                       (tg_gemm_path) whose shape/alignment requirements the
  *                       arguments do not meet.
  *   TG_ERR_LAUNCH       the HIP runtime reported an error for the launch.
@@ -79,7 +80,8 @@ typedef enum {
  *                          aligned, B, C and bias 8-byte aligned.
  *   TG_PATH_TILED          256x256x64 MFMA tiles staged through LDS with
  *                          16-byte loads; needs K % 8 == 0, N % 8 == 0, A, B
- *                          and C 16-byte aligned, bias 8-byte aligned.
+ *                          and C 16-byte aligned, bias 8-byte aligned, and A
+ *                          and B each smaller than 2 GiB.
  *   TG_PATH_TILED_GENERIC  the same tiling with element-granular loads and
  *                          stores: any shape, any alignment.
  *   TG_PATH_NONE           (reported by tg_gemm_plan only) nothing to launch.

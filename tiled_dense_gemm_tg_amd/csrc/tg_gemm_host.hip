@@ -71,15 +71,19 @@ bool skinny_ok(int64_t M, int64_t N, int64_t K, const void *A, const void *B, co
            aligned(bias, 8);
 }
 
-bool tiled_ok(int64_t N, int64_t K, const void *A, const void *B, const void *bias, const void *C) {
-    return K % 8 == 0 && N % 8 == 0 && aligned(A, 16) && aligned(B, 16) && aligned(C, 16) && aligned(bias, 8);
+// The vector tiled kernel masks loads by adding 2^31 to their byte offsets,
+// so A and B must each stay below 2 GiB there.
+bool tiled_ok(int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *bias, const void *C) {
+    const int64_t two_gib = int64_t(1) << 31;
+    return K % 8 == 0 && N % 8 == 0 && aligned(A, 16) && aligned(B, 16) && aligned(C, 16) && aligned(bias, 8) &&
+           2 * M * K < two_gib && 2 * K * N < two_gib;
 }
 
 tg_path auto_path(int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *bias,
                   const void *C) {
     if (skinny_ok(M, N, K, A, B, bias, C))
         return TG_PATH_SKINNY;
-    if (tiled_ok(N, K, A, B, bias, C))
+    if (tiled_ok(M, N, K, A, B, bias, C))
         return TG_PATH_TILED;
     return TG_PATH_TILED_GENERIC;
 }
@@ -109,7 +113,7 @@ TG_EXPORT tg_status tg_gemm_path(tg_path path, int64_t M, int64_t N, int64_t K, 
     if (path == TG_PATH_AUTO)
         path = auto_path(M, N, K, A, B, bias, C);
     else if ((path == TG_PATH_SKINNY && !skinny_ok(M, N, K, A, B, bias, C)) ||
-             (path == TG_PATH_TILED && !tiled_ok(N, K, A, B, bias, C)))
+             (path == TG_PATH_TILED && !tiled_ok(M, N, K, A, B, bias, C)))
         return TG_ERR_UNSUPPORTED;
 
     tg::GemmArgs a;
