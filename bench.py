@@ -41,7 +41,8 @@ METRIC = "GEMM TFLOP/s and % MFMA peak at 4096³/8192³ fp16; HBM GB/s at M=16"
 MAIN = "gemm_f16_8192x8192x8192_bias_gelu_tanh"
 SQUARE = "gemm_f16_4096x4096x4096"
 SKINNY = "gemm_f16_skinny_16x11008x4096"
-KERNEL_SOURCES = ["gemm_tiled.hip", "gemm_skinny.hip", "tg_device.h", "tg_launch.h", "tg_gemm_host.hip"]
+KERNEL_SOURCES = ["gemm_tiled.hip", "gemm_tiled_generic.hip", "gemm_skinny.hip", "tg_device.h", "tg_tile.h",
+                  "tg_launch.h", "tg_gemm_host.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 

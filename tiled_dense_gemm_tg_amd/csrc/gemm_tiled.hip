@@ -1,4 +1,4 @@
-// gemm_tiled.hip -- tiled MFMA GEMM for gfx950 (MI355X).
+// gemm_tiled.hip -- tiled MFMA GEMM for gfx950 (MI355X), vector path.
 //
 // The tiling is the one the TileLang pages teach ("TileLang: writing LLM GPU
 // kernels by thinking in tiles", section 2 and the section 3 listing; "TileLang:
@@ -7,283 +7,277 @@
 // workgroup per output tile, a loop over k-slices that copies an A tile and a B
 // tile from global memory into on-chip memory, a tile matrix multiply into a
 // register accumulator held in fp32, and one write-back of the tile after the
-// loop, with the copies of later slices overlapping the multiply of the
-// current one.  The sizes and mechanics are chosen for CDNA4 rather than taken
-// from the pages' NVIDIA example:
+// loop, with the copies of later slices in flight while the current one is
+// multiplied.  Sizes and mechanics are chosen for CDNA4 rather than taken from
+// the pages' NVIDIA example:
 //
-//   * tile 256 x 256 x 64, 256 threads = 4 wave64s, each wave owning a
-//     128 x 128 quarter of C as 4 x 4 v_mfma_f32_32x32x16 accumulators
-//     (256 fp32 values per lane, held in AGPRs);
-//   * two LDS stages of 2 x 32 KB (128 KB of the 160 KB LDS) and one barrier per
-//     k-slice; a slice's global loads are issued two k-steps before the end of
-//     the previous slice and written to LDS one k-step into the current one, so
-//     a full slice of MFMA work hides their latency;
-//   * both operands are stored in LDS K-contiguous ([row][64 k]), because a
-//     16-bit MFMA takes eight consecutive k of one row (A) or one column (B)
-//     per lane.  A arrives that way; B (row-major K x N) is transposed in
-//     registers on its way into LDS: each thread loads an 8 k x 8 n block
-//     with eight 16-byte loads and rebuilds it as 8 n x 8 k with v_perm_b32;
-//   * a 16-byte-chunk XOR swizzle within each 128-byte LDS row (see swz);
-//   * MFMA fragments are double-buffered in registers: the reads for k-step
-//     s+1 are issued between the MFMAs of step s, and instruction-group hints
-//     interleave the LDS writes and global loads with the MFMAs too, so the
-//     matrix unit is fed from one wave per SIMD without waiting on LDS;
-//   * the MFMA is issued with the B fragment as its first operand, so each
-//     lane ends up with 4 consecutive output columns of one row, stored as a
-//     single 8-byte write after the fused epilogue;
-//   * workgroups are remapped so that each XCD (8 on MI355X, dispatched
-//     round-robin) works on a contiguous, grouped block of tiles, which keeps
-//     the A and B panels those tiles share inside that XCD's L2.
+//   * tile 256 x 256, 256 threads = 4 wave64s, each owning a 128 x 128 quarter
+//     of C as 4 x 4 v_mfma_f32_32x32x16 accumulators (256 fp32 values per lane,
+//     in AGPRs);
+//   * k-slices of 32 in a ring of 4 LDS stages (4 x 32 KB of the 160 KB LDS),
+//     filled by buffer loads that write LDS directly (buffer_load_dwordx4 ...
+//     lds): no staging registers, no LDS store instructions, and each slice is
+//     requested two slices before it is used, so a whole slice of MFMA work
+//     hides the memory latency twice over; one barrier per slice;
+//   * A is staged as [256 m][32 k] (k-contiguous, what a 16-bit MFMA operand
+//     holds per lane) and read with ds_read_b128; B stays [32 k][256 n] as in
+//     memory and its MFMA fragments come from ds_read_b64_tr_b16, which hands
+//     each lane one column of a 4 x 16 block of 16-bit values (lane i of a
+//     16-lane group gets element i%4 of the 8 bytes addressed by lane
+//     4 j + i/4, for j = 0..3);
+//   * XOR swizzles on the 16-byte chunks of both tiles make the fragment
+//     reads bank-conflict free; since a direct load writes its 64 lanes' data
+//     contiguously, the swizzle is applied to which global chunk each lane
+//     fetches;
+//   * MFMA fragments are double-buffered in registers: the reads for the next
+//     k-step are issued between the MFMAs of the current one;
+//   * the MFMA takes the B fragment first, so each lane ends up with 4
+//     consecutive output columns of a row, stored with one 8-byte write after
+//     the fused bias + GELU(tanh) epilogue (tg_tile.h);
+//   * XCD-aware grouped raster of the tiles (tg_tile.h).
 //
-// Global loads are raw buffer loads over each operand's exact byte range: the
-// hardware returns zero for offsets beyond the range, so edge tiles need no
-// branches and no access can leave the operand.  k >= K is forced out of range
-// in both A and B (the K tail must be zero on both sides); rows m >= M and
+// The direct loads are issued from inline assembly and their completion is
+// awaited with explicit vmcnt waits: the compiler cannot tell that the LDS
+// they write is not the LDS being read, and would otherwise wait for every
+// load in flight before each use of LDS data.
+//
+// Loads are range-checked buffer loads over each operand's exact byte range;
+// an out-of-range lane writes zeros.  k >= K is pushed out of range (offset +
+// 2^31) in both A and B, so the K tail is zero on both sides; rows m >= M and
 // columns n >= N are never stored, so what they load does not matter.
-#include "tg_device.h"
-#include "tg_launch.h"
+#include "tg_tile.h"
 
 #include <type_traits>
 
 namespace tg {
 namespace {
 
-constexpr int BM = 256;
-constexpr int BN = 256;
-constexpr int BK = 64;
-constexpr int NTHREADS = 256;
-constexpr int CHUNKS = BK / 8;            // 16-byte chunks per LDS row
-constexpr int TILE_U4 = BM * CHUNKS;      // 16-byte slots per operand per stage (32 KB)
-constexpr int GROUP_M = 4;                // tile rows per raster group
-constexpr int NUM_XCD = 8;
-constexpr uint32_t OOB = 0xFFFFFFF0u;     // byte offset beyond every operand (< 2^32 - 32 bytes)
-// Added to an offset below 2^31 it lands beyond any operand of the vector
-// path, whose operands are limited to 2^31 bytes; an additive bump (rather
-// than a select) keeps the compiler from turning the mask into a branch.
-constexpr uint32_t OOB_BUMP = 0x80000000u;
-static_assert(BM == BN, "A and B tiles share one LDS layout");
+using tile::BM;
+using tile::BN;
+using tile::NTHREADS;
+constexpr int BK = 32;
+constexpr int STAGES = 4;
+constexpr int A_BYTES = BM * BK * 2;              // 16 KB: [256 m][32 k]
+constexpr int B_BYTES = BK * BN * 2;              // 16 KB: [32 k][256 n]
+constexpr int STAGE_BYTES = A_BYTES + B_BYTES;    // 32 KB
+constexpr uint32_t OOB_BUMP = 0x80000000u;        // + offset < 2^31 -> beyond any operand (< 2 GiB)
 
-// sched_group_barrier masks
-constexpr int SG_VALU = 0x002;
-constexpr int SG_MFMA = 0x008;
-constexpr int SG_VMEM_READ = 0x020;
-constexpr int SG_DS_READ = 0x100;
-constexpr int SG_DS_WRITE = 0x200;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-// XOR swizzle of a row's 16-byte chunk index.  A fragment read takes one
-// logical chunk from 32 consecutive rows.  f(row) permutes the 8 chunk slots
-// so that any 8 consecutive rows (one 128-byte pass over 32 four-byte banks)
-// use 8 different slots, and any 16 consecutive rows split by parity into
-// two sets of 8 different slots (one 256-byte pass over 64 banks covers two
-// 128-byte rows).
-__device__ __forceinline__ int swz(int row, int chunk) {
-    return chunk ^ (((row >> 1) ^ (row << 2)) & 7);
-}
-__device__ __forceinline__ int lds_slot(int row, int chunk) {
-    return row * CHUNKS + swz(row, chunk);
+// A row = 32 k = 4 chunks of 16 B.  A fragment read takes one logical chunk
+// from 32 consecutive rows; with this swizzle any 8 consecutive rows of one
+// parity and any 16 consecutive rows of one residue mod 4 use 4 different
+// slots, which keeps both 32-bank (8 lanes x 16 B) and 64-bank (16 lanes)
+// passes conflict free.
+__device__ __forceinline__ int a_swz(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
+
+// B row = 256 n = 32 chunks.  A transposed read pass touches 4 consecutive
+// k-rows (k % 4 = 0..3) and 2 (32-bank pass) or 4 (64-bank pass) adjacent
+// chunks; g(k%4) = {0, 10, 4, 14} gives those 4 rows distinct bits 1-2 and
+// distinct bits 2-3 of the slot, so every pass hits distinct banks.
+__device__ __forceinline__ int b_swz(int k) { return ((k & 1) ? 10 : 0) ^ ((k & 2) ? 4 : 0); }
+
+__device__ __forceinline__ uint32_t lds_address(const void *p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p;
 }
 
-__device__ __forceinline__ void tile_of_workgroup(int M, int N, int &tm, int &tn) {
-    const int tiles_m = (M + BM - 1) / BM;
-    const int tiles_n = (N + BN - 1) / BN;
-    const int total = tiles_m * tiles_n;
-    int w = blockIdx.x;
-    if (total % NUM_XCD == 0)
-        w = (w % NUM_XCD) * (total / NUM_XCD) + w / NUM_XCD;
-    const int per_group = GROUP_M * tiles_n;
-    const int grp = w / per_group;
-    const int first_m = grp * GROUP_M;
-    const int rows = min(tiles_m - first_m, GROUP_M);
-    const int rem = w - grp * per_group;
-    tm = first_m + rem % rows;
-    tn = rem / rows;
+// Buffer resource words for the inline-asm load: base, stride 0, byte range,
+// word 3 of the gfx9 family (32-bit data format).
+__device__ __forceinline__ i32x4 rsrc_words(const void *base, uint32_t bytes) {
+    const uint64_t p = reinterpret_cast<uint64_t>(base);
+    return i32x4{(int)(uint32_t)p, (int)(uint32_t)(p >> 32), (int)bytes, 0x00020000};
 }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void *base, uint32_t bytes) {
-    // raw buffer (stride 0), range checked against `bytes`; 0x00020000 is the
-    // gfx9-family word 3 (32-bit data format) of the buffer resource
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+// One 16-byte-per-lane buffer load into LDS at m0 + 16 * lane.
+__device__ __forceinline__ void dma16(const i32x4 &rsrc, uint32_t voffset, uint32_t m0) {
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voffset), "s"(rsrc), "{m0}"(m0));
 }
 
-// ---- global -> registers ------------------------------------------------
-// Thread t: A chunk c = t % 8 (8 k) of rows t/8 + 32 i (i = 0..7);
-//           B rows 8 g + r (g = t % 8, r = 0..7) of the 8 columns 8 (t/8)...
-struct Loader {
-    __amdgpu_buffer_rsrc_t ra, rb;
-    uint32_t a_row_off;   // byte offset of (m0 + t/8, 8 (t%8)) in A
-    uint32_t a_row_step;  // bytes between rows i and i+1 (32 rows of A)
-    uint32_t b_col_off;   // byte offset of (8 (t%8), n0 + 8 (t/8)) in B
-    uint32_t b_row;       // bytes per row of B
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Per-lane addressing of the 8 direct loads that fill one stage.  Wave w,
+// lane L, load q = 0..3:
+//   A: tile rows 64 w + 16 q + L/4, physical chunk L%4 -> logical chunk
+//      c = L%4 ^ a_swz(row) (8 k); destination m0 = stage + 4096 w + 1024 q;
+//   B: k-rows 8 w + 2 q + L/32, physical chunk L%32 -> logical chunk
+//      c = L%32 ^ b_swz(k) (8 n); destination m0 = stage + 16 KB + 4096 w + 1024 q.
+struct Dma {
+    i32x4 ra, rb;
+    uint32_t a_off;      // byte offset of this lane's A chunk for q = 0, k0 = 0
+    uint32_t a_qstep;    // 16 rows of A in bytes
+    int a_k;             // first k of the lane's A chunk within the slice
+    uint32_t b_off[4];   // byte offset of this lane's B chunk for load q, k0 = 0
+    int b_k[4];          // k-row of load q within the slice
+    uint32_t b_row;      // bytes per row of B
+    uint32_t m0_a, m0_b; // LDS destinations of load q = 0 in stage 0
     int K;
-    int ak;               // first k of this thread's A chunk, relative to k0
-    int bk;               // first k of this thread's B rows, relative to k0
 
-    __device__ __forceinline__ Loader(const GemmArgs &g, int m0, int n0, int tid) {
-        ra = buffer_of(g.A, 2u * (uint32_t)g.M * (uint32_t)g.K);
-        rb = buffer_of(g.B, 2u * (uint32_t)g.K * (uint32_t)g.N);
+    __device__ __forceinline__ Dma(const GemmArgs &g, int m0, int n0, int wave, int lane, uint32_t lds0) {
+        ra = rsrc_words(g.A, 2u * (uint32_t)g.M * (uint32_t)g.K);
+        rb = rsrc_words(g.B, 2u * (uint32_t)g.K * (uint32_t)g.N);
         K = g.K;
-        ak = 8 * (tid & 7);
-        bk = 8 * (tid & 7);
-        a_row_off = 2u * ((uint32_t)(m0 + (tid >> 3)) * (uint32_t)g.K + (uint32_t)ak);
-        a_row_step = 64u * (uint32_t)g.K;
+        const int arow = 64 * wave + (lane >> 2);
+        const int ac = (lane & 3) ^ a_swz(lane >> 2);
+        a_k = 8 * ac;
+        a_off = 2u * ((uint32_t)(m0 + arow) * (uint32_t)g.K + (uint32_t)a_k);
+        a_qstep = 32u * (uint32_t)g.K;
         b_row = 2u * (uint32_t)g.N;
-        b_col_off = (uint32_t)bk * b_row + 2u * (uint32_t)(n0 + 8 * (tid >> 3));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int k = 8 * wave + 2 * q + (lane >> 5);
+            const int c = (lane & 31) ^ b_swz(k);
+            b_k[q] = k;
+            b_off[q] = (uint32_t)k * b_row + 2u * (uint32_t)(n0 + 8 * c);
+        }
+        m0_a = lds0 + 4096u * (uint32_t)wave;
+        m0_b = lds0 + (uint32_t)A_BYTES + 4096u * (uint32_t)wave;
     }
 
-    // 16-byte loads (K % 8 == 0, N % 8 == 0, 16-byte aligned operands)
-    __device__ __forceinline__ void load_vec(u32x4 (&xa)[8], u32x4 (&xb)[8], int k0) const {
-        const uint32_t a_bump = (k0 + ak < K) ? 0u : OOB_BUMP;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t off = a_row_off + (uint32_t)i * a_row_step + 2u * (uint32_t)k0 + a_bump;
-            xa[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)off, 0, 0);
-        }
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const uint32_t bump = (k0 + bk + r < K) ? 0u : OOB_BUMP;
-            const uint32_t off = b_col_off + (uint32_t)(k0 + r) * b_row + bump;
-            xb[r] = __builtin_amdgcn_raw_buffer_load_b128(rb, (int)off, 0, 0);
+    // Direct load d (0..7) of k-slice kt into LDS stage st: A load d/2 for
+    // even d, B load d/2 for odd d.
+    __device__ __forceinline__ void issue_one(int kt, int st, int d) const {
+        const int k0 = kt * BK;
+        const int q = d >> 1;
+        const uint32_t sbase = (uint32_t)st * (uint32_t)STAGE_BYTES;
+        if ((d & 1) == 0) {
+            const uint32_t bump = (k0 + a_k < K) ? 0u : OOB_BUMP;
+            dma16(ra, a_off + (uint32_t)q * a_qstep + 2u * (uint32_t)k0 + bump, m0_a + sbase + 1024u * q);
+        } else {
+            const uint32_t bump = (k0 + b_k[q] < K) ? 0u : OOB_BUMP;
+            dma16(rb, b_off[q] + (uint32_t)k0 * b_row + bump, m0_b + sbase + 1024u * q);
         }
     }
 
-    // element loads (any shape, any alignment); the k >= K mask is applied per
-    // element, rows and columns past the edges are handled as for load_vec
-    __device__ __forceinline__ void load_elem(u32x4 (&xa)[8], u32x4 (&xb)[8], int k0) const {
+    // Request k-slice kt into LDS stage st.
+    __device__ __forceinline__ void issue(int kt, int st) const {
+        const int k0 = kt * BK;
+        const uint32_t sbase = (uint32_t)st * (uint32_t)STAGE_BYTES;
+        const uint32_t a_bump = (k0 + a_k < K) ? 0u : OOB_BUMP;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            uint16_t e[8];
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const bool ok = k0 + ak + q < K;
-                const uint32_t off = ok ? a_row_off + (uint32_t)i * a_row_step + 2u * (uint32_t)(k0 + q) : OOB;
-                e[q] = __builtin_amdgcn_raw_buffer_load_b16(ra, (int)off, 0, 0);
-            }
-            xa[i] = u32x4{pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]), pack2(e[6], e[7])};
-        }
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            uint16_t e[8];
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const bool ok = k0 + bk + r < K;
-                const uint32_t off = ok ? b_col_off + (uint32_t)(k0 + r) * b_row + 2u * q : OOB;
-                e[q] = __builtin_amdgcn_raw_buffer_load_b16(rb, (int)off, 0, 0);
-            }
-            xb[r] = u32x4{pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]), pack2(e[6], e[7])};
+        for (int q = 0; q < 4; ++q) {
+            dma16(ra, a_off + (uint32_t)q * a_qstep + 2u * (uint32_t)k0 + a_bump, m0_a + sbase + 1024u * q);
+            const uint32_t b_bump = (k0 + b_k[q] < K) ? 0u : OOB_BUMP;
+            dma16(rb, b_off[q] + (uint32_t)k0 * b_row + b_bump, m0_b + sbase + 1024u * q);
         }
     }
 };
 
-// ---- registers -> LDS ---------------------------------------------------
-__device__ __forceinline__ void store_a(u32x4 *__restrict__ As, const u32x4 (&xa)[8], int tid) {
-    const int c = tid & 7;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        As[lds_slot((tid >> 3) + 32 * i, c)] = xa[i];
-}
+// Per-lane LDS byte offsets (within a stage) of the fragment reads of k-step
+// s (16 k each):
+//   A, ds_read_b128: row wm*128 + 32 i + l%32, logical chunk 2 s + l/32;
+//   B, ds_read_b64_tr_b16 twice (k 0..3 and 4..7 of the lane's 8): lane
+//      16 G + q addresses k-row 16 s + 8 (G/2) + q/4 (+4), columns
+//      wn*128 + 32 j + 16 (G%2) + 4 (q%4) .. +3, so that lane l receives
+//      column wn*128 + 32 j + l%32, k = 16 s + 8 (l/32) + 0..7.
+struct FragAddr {
+    uint32_t a[2][4];    // [s][i]
+    uint32_t b[2][4];    // [s][j], first read; the second is +4 rows = +2048 bytes
 
-// xb[r] holds B[k = 8g + r][n = 8c .. 8c+7]; write column n = 8c + j as the
-// 8 consecutive k of LDS row n, chunk g.
-__device__ __forceinline__ void store_b(u32x4 *__restrict__ Bs, const u32x4 (&xb)[8], int tid) {
-    const int g = tid & 7;
-    const int c = tid >> 3;
+    __device__ __forceinline__ FragAddr(int wm, int wn, int lane) {
+        const int lr = lane & 31;
+        const int row0 = wm * 128 + lr;
+        const int sw = a_swz(lr);                     // a_swz depends on row bits 1..3 only
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int d = j >> 1;
-        u32x4 w;
-        if (j & 1) {
-            w.x = perm_hi(xb[0][d], xb[1][d]);
-            w.y = perm_hi(xb[2][d], xb[3][d]);
-            w.z = perm_hi(xb[4][d], xb[5][d]);
-            w.w = perm_hi(xb[6][d], xb[7][d]);
-        } else {
-            w.x = perm_lo(xb[0][d], xb[1][d]);
-            w.y = perm_lo(xb[2][d], xb[3][d]);
-            w.z = perm_lo(xb[4][d], xb[5][d]);
-            w.w = perm_lo(xb[6][d], xb[7][d]);
-        }
-        Bs[lds_slot(8 * c + j, g)] = w;
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int c = 2 * s + (lane >> 5);
+                a[s][i] = 16u * (uint32_t)((row0 + 32 * i) * 4 + (c ^ sw));
+            }
+        const int G = lane >> 4;
+        const int q = lane & 15;
+        const int kr = 8 * (G >> 1) + (q >> 2);      // k-row for s = 0, first read; kr % 4 = q / 4
+        const int bsw = b_swz(kr);
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int n = wn * 128 + 32 * j + 16 * (G & 1) + 4 * (q & 3);
+                const int c = (n >> 3) ^ bsw;
+                b[s][j] = (uint32_t)A_BYTES + 512u * (uint32_t)(kr + 16 * s) + 16u * (uint32_t)c +
+                          8u * (uint32_t)(q & 1);
+            }
     }
-}
+};
 
-// ---- LDS -> MFMA --------------------------------------------------------
-// Wave (wm, wn) owns rows wm*128.. and columns wn*128.. of the tile.  For
-// k-step s (16 k), lane l reads chunk 2 s + l/32 of row 32 i + l%32 of A and
-// of row (column of B) 32 j + l%32.
 struct Frag {
     u32x4 a[4], b[4];
 };
 
-__device__ __forceinline__ void read_frag(Frag &f, const u32x4 *__restrict__ As, const u32x4 *__restrict__ Bs,
-                                          int s, int wm, int wn, int lane) {
-    const int lr = lane & 31;
-    const int kc = 2 * s + (lane >> 5);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        f.a[i] = As[lds_slot(wm * 128 + 32 * i + lr, kc)];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-        f.b[j] = Bs[lds_slot(wn * 128 + 32 * j + lr, kc)];
+__device__ __forceinline__ u32x4 lds_u4(uint32_t byte) {
+    return *(__attribute__((address_space(3))) const u32x4 *)(uintptr_t)byte;
 }
 
-// acc[i][j] = D with D[n][m] = sum_k B[k][n] A[m][k]: lane l holds m = l%32
-// and n = 8 (e/4) + 4 (l/32) + e%4 for its 16 values e.
-template <class T>
-__device__ __forceinline__ void mfma_step(const Frag &f, f32x16 (&acc)[4][4]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            acc[i][j] = T::mfma32(f.b[j], f.a[i], acc[i][j]);
+__device__ __forceinline__ u32x2 lds_tr(uint32_t byte) {
+    const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(uintptr_t)byte);
+    return __builtin_bit_cast(u32x2, v);
 }
 
-// Ordering hints for one k-step of 16 MFMAs: the 8 fragment reads of the
-// next step go one after each of the first 8 MFMAs, then (VALU, EXTRA) groups
-// of the other work of the step go after the MFMAs, first the 8 second-half
-// MFMAs and, with FIRST_HALF, also after the first 8.
-template <int EXTRA_MASK, int EXTRA_PER_MFMA, int VALU_PER_MFMA, bool FIRST_HALF>
-__device__ __forceinline__ void interleave_hint() {
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
-        if constexpr (FIRST_HALF && EXTRA_PER_MFMA > 0)
-            __builtin_amdgcn_sched_group_barrier(EXTRA_MASK, EXTRA_PER_MFMA, 0);
-    }
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-        if constexpr (VALU_PER_MFMA > 0)
-            __builtin_amdgcn_sched_group_barrier(SG_VALU, VALU_PER_MFMA, 0);
-        if constexpr (EXTRA_PER_MFMA > 0)
-            __builtin_amdgcn_sched_group_barrier(EXTRA_MASK, EXTRA_PER_MFMA, 0);
+// Fragment read number r (0..11) of k-step s: r < 4 is A row-block r, then
+// B column-block (r-4)/2, first (k 0..3) or second (k 4..7) half.
+__device__ __forceinline__ void read_one(Frag &f, const FragAddr &ad, uint32_t stage, int s, int r) {
+    if (r < 4) {
+        f.a[r] = lds_u4(stage + ad.a[s][r]);
+    } else {
+        const int j = (r - 4) >> 1;
+        if (((r - 4) & 1) == 0) {
+            const u32x2 v = lds_tr(stage + ad.b[s][j]);
+            f.b[j].x = v.x;
+            f.b[j].y = v.y;
+        } else {
+            const u32x2 v = lds_tr(stage + ad.b[s][j] + 2048u);
+            f.b[j].z = v.x;
+            f.b[j].w = v.y;
+        }
     }
 }
 
-template <class T, int EPI, bool VEC>
+// One k-step in a fixed issue order: MFMA q (A block q/4 x B block q%4),
+// then fragment read q of the next step (q < 12), then one direct load
+// after MFMAs 1, 5, 9, 13 (`dma(d)` for d = 0..3).  sched_barrier keeps the
+// compiler from regrouping: spreading the direct loads lets the memory
+// pipeline take them while the matrix unit stays busy.
+template <class T, bool READ, bool DMA, typename DmaFn>
+__device__ __forceinline__ void kstep(const Frag &cur, Frag &nxt, f32x16 (&acc)[4][4], const FragAddr &ad,
+                                      uint32_t rstage, int rs, DmaFn dma) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        acc[q >> 2][q & 3] = T::mfma32(cur.b[q & 3], cur.a[q >> 2], acc[q >> 2][q & 3]);
+        if constexpr (READ) {
+            if (q < 12)
+                read_one(nxt, ad, rstage, rs, q);
+        }
+        if constexpr (DMA) {
+            if ((q & 3) == 1)
+                dma(q >> 2);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+template <class T, int EPI>
 __global__ __launch_bounds__(NTHREADS) void gemm_tiled_kernel(GemmArgs args) {
-    __shared__ u32x4 smem[4 * TILE_U4];  // A stage 0, A stage 1, B stage 0, B stage 1
-    const int M = args.M, N = args.N, K = args.K;
-
+    __shared__ __attribute__((aligned(16))) u32x4 smem[STAGES * STAGE_BYTES / 16];
     int tm, tn;
-    tile_of_workgroup(M, N, tm, tn);
+    tile::tile_of_workgroup(args.M, args.N, tm, tn);
     const int m0 = tm * BM;
     const int n0 = tn * BN;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave >> 1;
     const int wn = wave & 1;
-
-    const Loader ld(args, m0, n0, tid);
-    auto load = [&](u32x4 (&xa)[8], u32x4 (&xb)[8], int kt) __attribute__((always_inline)) {
-        if constexpr (VEC)
-            ld.load_vec(xa, xb, kt * BK);
-        else
-            ld.load_elem(xa, xb, kt * BK);
-    };
-    auto A_st = [&](int st) { return smem + st * TILE_U4; };
-    auto B_st = [&](int st) { return smem + (2 + st) * TILE_U4; };
+    const uint32_t lds0 = lds_address(smem);
+    const Dma dma(args, m0, n0, wave, lane, lds0);
+    const FragAddr fad(wm, wn, lane);
+    auto stage = [&](int st) { return lds0 + (uint32_t)st * (uint32_t)STAGE_BYTES; };
 
     f32x16 acc[4][4];
 #pragma unroll
@@ -292,149 +286,95 @@ __global__ __launch_bounds__(NTHREADS) void gemm_tiled_kernel(GemmArgs args) {
         for (int j = 0; j < 4; ++j)
             acc[i][j] = f32x16{};
 
-    const int nk = (K + BK - 1) / BK;
-    u32x4 xa[8], xb[8];
+    const int nk = (args.K + BK - 1) / BK;
     Frag f0, f1;
+    // Prologue: request slices 0..2, wait for slice 0.
     if (nk > 0) {
-        load(xa, xb, 0);
-        store_a(A_st(0), xa, tid);
-        store_b(B_st(0), xb, tid);
+        dma.issue(0, 0);
         if (nk > 1)
-            load(xa, xb, 1);
-        __syncthreads();
-        read_frag(f0, A_st(0), B_st(0), 0, wm, wn, lane);
+            dma.issue(1, 1);
+        if (nk > 2) {
+            dma.issue(2, 2);
+            wait_vmcnt<16>();
+        } else if (nk > 1) {
+            wait_vmcnt<8>();
+        } else {
+            wait_vmcnt<0>();
+        }
+    }
+    __syncthreads();
+    if (nk > 0) {
+#pragma unroll
+        for (int r = 0; r < 12; ++r)
+            read_one(f0, fad, stage(0), 0, r);
     }
 
-    // One k-slice t in LDS stage t&1, its fragments for step 0 already in f0
-    // and slice t+1 already in xa/xb:
-    //   step 0: MFMA f0 | read step 1 -> f1
-    //   step 1: MFMA f1 | read step 2 -> f0 | write xa/xb (slice t+1) to the other stage
-    //   step 2: MFMA f0 | read step 3 -> f1 | issue global loads of slice t+2
-    //   barrier (slice t+1 complete in LDS, all reads of slice t done)
-    //   step 3: MFMA f1 | read step 0 of slice t+1 -> f0
-    // The other stage was last read in slice t-1, before the previous barrier.
-    auto slice = [&](int t, auto store_next, auto load_next2, auto read_next) __attribute__((always_inline)) {
-        const int cur = t & 1;
-        const u32x4 *As = A_st(cur);
-        const u32x4 *Bs = B_st(cur);
-
-        read_frag(f1, As, Bs, 1, wm, wn, lane);
-        mfma_step<T>(f0, acc);
-        if constexpr (VEC)
-            interleave_hint<0, 0, 0, false>();
-        __builtin_amdgcn_sched_barrier(0);
-
-        read_frag(f0, As, Bs, 2, wm, wn, lane);
-        if constexpr (decltype(store_next)::value) {
-            store_a(A_st(cur ^ 1), xa, tid);
-            store_b(B_st(cur ^ 1), xb, tid);
+    // Slice t in stage t%4, fragments of its first k-step already in f0:
+    //   step 0: MFMAs on f0, reads of step 1 into f1, first half of the
+    //           direct loads of slice t+3 into stage (t+3)%4 (that stage was
+    //           last read in slice t-1, before the previous barrier);
+    //   wait until this wave's loads of slice t+1 have landed, barrier
+    //           (everyone's have, and everyone's reads of slice t are done);
+    //   step 1: MFMAs on f1, reads of step 0 of slice t+1 into f0, second
+    //           half of the direct loads of slice t+3.
+    // Loads issued after slice t+1's when waiting: all 8 of slice t+2 and
+    // the first 4 of slice t+3, hence vmcnt(12) in the steady state.
+    auto slice = [&](int t, auto issue, auto wait, auto next) __attribute__((always_inline)) {
+        const uint32_t st = stage(t & 3);
+        constexpr bool ISSUE = decltype(issue)::value;
+        constexpr bool NEXT = decltype(next)::value;
+        const int kt = t + 3;
+        auto dma_lo = [&](int d) __attribute__((always_inline)) { dma.issue_one(kt, kt & 3, d); };
+        auto dma_hi = [&](int d) __attribute__((always_inline)) { dma.issue_one(kt, kt & 3, d + 4); };
+        kstep<T, true, ISSUE>(f0, f1, acc, fad, st, 1, dma_lo);
+        if constexpr (NEXT) {
+            wait_vmcnt<decltype(wait)::value>();
+            __syncthreads();
         }
-        mfma_step<T>(f1, acc);
-        if constexpr (VEC)
-            interleave_hint<SG_DS_WRITE, 1, 4, true>();
-        __builtin_amdgcn_sched_barrier(0);
-
-        read_frag(f1, As, Bs, 3, wm, wn, lane);
-        if constexpr (decltype(load_next2)::value)
-            load(xa, xb, t + 2);
-        mfma_step<T>(f0, acc);
-        if constexpr (VEC)
-            interleave_hint<SG_VMEM_READ, 2, 2, false>();
-        __syncthreads();
-
-        if constexpr (decltype(read_next)::value)
-            read_frag(f0, A_st(cur ^ 1), B_st(cur ^ 1), 0, wm, wn, lane);
-        mfma_step<T>(f1, acc);
-        if constexpr (VEC)
-            interleave_hint<0, 0, 0, false>();
-        __builtin_amdgcn_sched_barrier(0);
+        kstep<T, NEXT, ISSUE>(f1, f0, acc, fad, stage((t + 1) & 3), 0, dma_hi);
     };
-
     using yes = std::true_type;
     using no = std::false_type;
+    using w12 = std::integral_constant<int, 12>;
+    using w8 = std::integral_constant<int, 8>;
+    using w0 = std::integral_constant<int, 0>;
     int t = 0;
-    for (; t + 2 < nk; ++t)
-        slice(t, yes{}, yes{}, yes{});
-    if (t + 1 < nk) {
-        slice(t, yes{}, no{}, yes{});
+    for (; t + 3 < nk; ++t)
+        slice(t, yes{}, w12{}, yes{});
+    if (t + 3 == nk && t < nk) {
+        slice(t, no{}, w8{}, yes{});
         ++t;
     }
-    if (t < nk)
-        slice(t, no{}, no{}, no{});
-
-    // ---- fused epilogue and store ------------------------------------------
-    const int lr = lane & 31;
-    const int lh = lane >> 5;
-    const __amdgpu_buffer_rsrc_t rc = buffer_of(args.C, 2u * (uint32_t)M * (uint32_t)N);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int n = n0 + wn * 128 + 32 * j + 8 * q + 4 * lh;
-            float bv[4] = {0.f, 0.f, 0.f, 0.f};
-            if constexpr (EPI != EPI_NONE) {
-                if constexpr (VEC) {
-                    if (n < N) {
-                        const u32x2 raw = *reinterpret_cast<const u32x2 *>(args.bias + n);
-                        bv[0] = T::to_f32((uint16_t)(raw.x & 0xffff));
-                        bv[1] = T::to_f32((uint16_t)(raw.x >> 16));
-                        bv[2] = T::to_f32((uint16_t)(raw.y & 0xffff));
-                        bv[3] = T::to_f32((uint16_t)(raw.y >> 16));
-                    }
-                } else {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (n + r < N)
-                            bv[r] = T::to_f32(args.bias[n + r]);
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int m = m0 + wm * 128 + 32 * i + lr;
-                uint16_t o[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    o[r] = T::from_f32(epilogue<EPI>(acc[i][j][4 * q + r], bv[r]));
-                const uint32_t base = 2u * ((uint32_t)m * (uint32_t)N + (uint32_t)n);
-                if constexpr (VEC) {
-                    const uint32_t off = (m < M && n < N) ? base : OOB;
-                    __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack2(o[0], o[1]), pack2(o[2], o[3])}, rc,
-                                                          (int)off, 0, 0);
-                } else {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const uint32_t off = (m < M && n + r < N) ? base + 2u * r : OOB;
-                        __builtin_amdgcn_raw_buffer_store_b16(o[r], rc, (int)off, 0, 0);
-                    }
-                }
-            }
-        }
+    if (t + 2 == nk && t < nk) {
+        slice(t, no{}, w0{}, yes{});
+        ++t;
     }
+    if (t + 1 == nk)
+        slice(t, no{}, w0{}, no{});
+
+    tile::store_tile<T, EPI, true>(args, acc, m0, n0, wm, wn, lane);
 }
 
 template <class T, int EPI>
-hipError_t launch_typed(bool vec, const GemmArgs &a, hipStream_t stream) {
+hipError_t launch_typed(const GemmArgs &a, hipStream_t stream) {
     const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-    if (vec)
-        hipLaunchKernelGGL((gemm_tiled_kernel<T, EPI, true>), dim3(tiles), dim3(NTHREADS), 0, stream, a);
-    else
-        hipLaunchKernelGGL((gemm_tiled_kernel<T, EPI, false>), dim3(tiles), dim3(NTHREADS), 0, stream, a);
+    hipLaunchKernelGGL((gemm_tiled_kernel<T, EPI>), dim3(tiles), dim3(NTHREADS), 0, stream, a);
     return hipGetLastError();
 }
 
 template <class T>
-hipError_t launch_epi(int epi, bool vec, const GemmArgs &a, hipStream_t stream) {
+hipError_t launch_epi(int epi, const GemmArgs &a, hipStream_t stream) {
     switch (epi) {
-    case EPI_NONE: return launch_typed<T, EPI_NONE>(vec, a, stream);
-    case EPI_BIAS: return launch_typed<T, EPI_BIAS>(vec, a, stream);
-    default: return launch_typed<T, EPI_BIAS_GELU_TANH>(vec, a, stream);
+    case EPI_NONE: return launch_typed<T, EPI_NONE>(a, stream);
+    case EPI_BIAS: return launch_typed<T, EPI_BIAS>(a, stream);
+    default: return launch_typed<T, EPI_BIAS_GELU_TANH>(a, stream);
     }
 }
 
 }  // namespace
 
-hipError_t launch_tiled(int dtype, int epi, bool vec, const GemmArgs &a, hipStream_t stream) {
-    return dtype == 0 ? launch_epi<F16>(epi, vec, a, stream) : launch_epi<BF16>(epi, vec, a, stream);
+hipError_t launch_tiled_vec(int dtype, int epi, const GemmArgs &a, hipStream_t stream) {
+    return dtype == 0 ? launch_epi<F16>(epi, a, stream) : launch_epi<BF16>(epi, a, stream);
 }
 
 }  // namespace tg

@@ -128,8 +128,10 @@ TG_EXPORT tg_status tg_gemm_path(tg_path path, int64_t M, int64_t N, int64_t K, 
     hipError_t e;
     if (path == TG_PATH_SKINNY)
         e = tg::launch_skinny(dtype, epilogue, a, s);
+    else if (path == TG_PATH_TILED)
+        e = tg::launch_tiled_vec(dtype, epilogue, a, s);
     else
-        e = tg::launch_tiled(dtype, epilogue, path == TG_PATH_TILED, a, s);
+        e = tg::launch_tiled_generic(dtype, epilogue, a, s);
     return e == hipSuccess ? TG_OK : TG_ERR_LAUNCH;
 }
 

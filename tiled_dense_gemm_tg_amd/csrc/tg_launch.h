@@ -17,9 +17,13 @@ struct GemmArgs {
 };
 
 // dtype: 0 fp16, 1 bf16; epi: 0 none, 1 bias, 2 bias + GELU(tanh).
-// vec: 16-byte loads (K % 8 == 0, N % 8 == 0, aligned operands) or
-// element-granular loads and stores.
-hipError_t launch_tiled(int dtype, int epi, bool vec, const GemmArgs &a, hipStream_t stream);
+
+// 256 x 256 tiles with 16-byte direct-to-LDS loads: K % 8 == 0, N % 8 == 0,
+// A, B, C 16-byte aligned, bias 8-byte aligned, A and B below 2 GiB.
+hipError_t launch_tiled_vec(int dtype, int epi, const GemmArgs &a, hipStream_t stream);
+
+// 256 x 256 tiles with element-granular loads and stores: any shape.
+hipError_t launch_tiled_generic(int dtype, int epi, const GemmArgs &a, hipStream_t stream);
 
 // M <= 16, K % 8 == 0, N % 4 == 0, aligned operands.
 hipError_t launch_skinny(int dtype, int epi, const GemmArgs &a, hipStream_t stream);
