@@ -111,8 +111,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 //      c = L%32 ^ b_swz(k) (8 n); destination m0 = stage + 16 KB + 4096 w + 1024 q.
 struct Dma {
     i32x4 ra, rb;
-    uint32_t a_off;      // byte offset of this lane's A chunk for q = 0, k0 = 0
-    uint32_t a_qstep;    // 16 rows of A in bytes
+    uint32_t a_off[4];   // byte offset of this lane's A chunk for load q, k0 = 0
     int a_k;             // first k of the lane's A chunk within the slice
     uint32_t b_off[4];   // byte offset of this lane's B chunk for load q, k0 = 0
     int b_k[4];          // k-row of load q within the slice
@@ -127,11 +126,10 @@ struct Dma {
         const int arow = 64 * wave + (lane >> 2);
         const int ac = (lane & 3) ^ a_swz(lane >> 2);
         a_k = 8 * ac;
-        a_off = 2u * ((uint32_t)(m0 + arow) * (uint32_t)g.K + (uint32_t)a_k);
-        a_qstep = 32u * (uint32_t)g.K;
         b_row = 2u * (uint32_t)g.N;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
+            a_off[q] = 2u * ((uint32_t)(m0 + arow + 16 * q) * (uint32_t)g.K + (uint32_t)a_k);
             const int k = 8 * wave + 2 * q + (lane >> 5);
             const int c = (lane & 31) ^ b_swz(k);
             b_k[q] = k;
@@ -142,31 +140,31 @@ struct Dma {
     }
 
     // Direct load d (0..7) of k-slice kt into LDS stage st: A load d/2 for
-    // even d, B load d/2 for odd d.
+    // even d, B load d/2 for odd d.  FULL: the slice lies inside [0, K), so
+    // no lane needs the K mask (only the last slice can be partial).
+    template <bool FULL>
     __device__ __forceinline__ void issue_one(int kt, int st, int d) const {
         const int k0 = kt * BK;
         const int q = d >> 1;
         const uint32_t sbase = (uint32_t)st * (uint32_t)STAGE_BYTES;
         if ((d & 1) == 0) {
-            const uint32_t bump = (k0 + a_k < K) ? 0u : OOB_BUMP;
-            dma16(ra, a_off + (uint32_t)q * a_qstep + 2u * (uint32_t)k0 + bump, m0_a + sbase + 1024u * q);
+            uint32_t off = a_off[q] + 2u * (uint32_t)k0;
+            if constexpr (!FULL)
+                off += (k0 + a_k < K) ? 0u : OOB_BUMP;
+            dma16(ra, off, m0_a + sbase + 1024u * q);
         } else {
-            const uint32_t bump = (k0 + b_k[q] < K) ? 0u : OOB_BUMP;
-            dma16(rb, b_off[q] + (uint32_t)k0 * b_row + bump, m0_b + sbase + 1024u * q);
+            uint32_t off = b_off[q] + (uint32_t)k0 * b_row;
+            if constexpr (!FULL)
+                off += (k0 + b_k[q] < K) ? 0u : OOB_BUMP;
+            dma16(rb, off, m0_b + sbase + 1024u * q);
         }
     }
 
     // Request k-slice kt into LDS stage st.
     __device__ __forceinline__ void issue(int kt, int st) const {
-        const int k0 = kt * BK;
-        const uint32_t sbase = (uint32_t)st * (uint32_t)STAGE_BYTES;
-        const uint32_t a_bump = (k0 + a_k < K) ? 0u : OOB_BUMP;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            dma16(ra, a_off + (uint32_t)q * a_qstep + 2u * (uint32_t)k0 + a_bump, m0_a + sbase + 1024u * q);
-            const uint32_t b_bump = (k0 + b_k[q] < K) ? 0u : OOB_BUMP;
-            dma16(rb, b_off[q] + (uint32_t)k0 * b_row + b_bump, m0_b + sbase + 1024u * q);
-        }
+        for (int d = 0; d < 8; ++d)
+            issue_one<false>(kt, st, d);
     }
 };
 
@@ -319,13 +317,17 @@ __global__ __launch_bounds__(NTHREADS) void gemm_tiled_kernel(GemmArgs args) {
     //           half of the direct loads of slice t+3.
     // Loads issued after slice t+1's when waiting: all 8 of slice t+2 and
     // the first 4 of slice t+3, hence vmcnt(12) in the steady state.
+    // ISSUE: 0 = no loads, 1 = loads of a full slice, 2 = loads of the
+    // (possibly partial) last slice.
     auto slice = [&](int t, auto issue, auto wait, auto next) __attribute__((always_inline)) {
         const uint32_t st = stage(t & 3);
-        constexpr bool ISSUE = decltype(issue)::value;
+        constexpr int ISSUE_KIND = decltype(issue)::value;
+        constexpr bool ISSUE = ISSUE_KIND != 0;
+        constexpr bool FULL = ISSUE_KIND == 1;
         constexpr bool NEXT = decltype(next)::value;
         const int kt = t + 3;
-        auto dma_lo = [&](int d) __attribute__((always_inline)) { dma.issue_one(kt, kt & 3, d); };
-        auto dma_hi = [&](int d) __attribute__((always_inline)) { dma.issue_one(kt, kt & 3, d + 4); };
+        auto dma_lo = [&](int d) __attribute__((always_inline)) { dma.issue_one<FULL>(kt, kt & 3, d); };
+        auto dma_hi = [&](int d) __attribute__((always_inline)) { dma.issue_one<FULL>(kt, kt & 3, d + 4); };
         kstep<T, true, ISSUE>(f0, f1, acc, fad, st, 1, dma_lo);
         if constexpr (NEXT) {
             wait_vmcnt<decltype(wait)::value>();
@@ -335,22 +337,29 @@ __global__ __launch_bounds__(NTHREADS) void gemm_tiled_kernel(GemmArgs args) {
     };
     using yes = std::true_type;
     using no = std::false_type;
+    using none = std::integral_constant<int, 0>;
+    using full = std::integral_constant<int, 1>;
+    using last = std::integral_constant<int, 2>;
     using w12 = std::integral_constant<int, 12>;
     using w8 = std::integral_constant<int, 8>;
     using w0 = std::integral_constant<int, 0>;
     int t = 0;
-    for (; t + 3 < nk; ++t)
-        slice(t, yes{}, w12{}, yes{});
+    for (; t + 4 < nk; ++t)
+        slice(t, full{}, w12{}, yes{});
+    if (t + 3 < nk) {
+        slice(t, last{}, w12{}, yes{});
+        ++t;
+    }
     if (t + 3 == nk && t < nk) {
-        slice(t, no{}, w8{}, yes{});
+        slice(t, none{}, w8{}, yes{});
         ++t;
     }
     if (t + 2 == nk && t < nk) {
-        slice(t, no{}, w0{}, yes{});
+        slice(t, none{}, w0{}, yes{});
         ++t;
     }
     if (t + 1 == nk)
-        slice(t, no{}, w0{}, no{});
+        slice(t, none{}, w0{}, no{});
 
     tile::store_tile<T, EPI, true>(args, acc, m0, n0, wm, wn, lane);
 }
