@@ -41,6 +41,7 @@ METRIC = "GEMM TFLOP/s and % MFMA peak at 4096³/8192³ fp16; HBM GB/s at M=16"
 MAIN = "gemm_f16_8192x8192x8192_bias_gelu_tanh"
 SQUARE = "gemm_f16_4096x4096x4096"
 SKINNY = "gemm_f16_skinny_16x11008x4096"
+RAGGED = "gemm_bf16_4000x4093x4111_bias_gelu_tanh"
 KERNEL_SOURCES = ["gemm_tiled.hip", "gemm_tiled_generic.hip", "gemm_skinny.hip", "tg_device.h", "tg_tile.h",
                   "tg_launch.h", "tg_gemm_host.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -280,6 +281,16 @@ def main() -> int:
                         "path": "skinny", "traffic": measured_traffic(w4.name)}
         log(f"{w4.name}: {ms4 * 1e3:.2f} us, {gbps:.0f} GB/s")
         del sets4
+        torch.cuda.empty_cache()
+        w3 = I.WORKLOADS[RAGGED]
+        log(f"secondary {w3.name}")
+        _, sets3 = device_operands(torch, I, w3)
+        ms3, _ = time_gemm(torch, tg, w3, sets3, max(args.steps // 2, 20), args.warmup)
+        t3 = gemm_flops(w3.M, w3.N, w3.K) / (ms3 * 1e-3) / 1e12
+        sec[w3.name] = {"us_per_launch": round(ms3 * 1e3, 2), "TFLOP/s": round(t3, 2),
+                        "frac_mfma_peak": round(t3 / PEAK_MFMA_F16_TFLOPS, 4), "path": "tiled_generic",
+                        "traffic": measured_traffic(w3.name)}
+        del sets3
         result["secondary"] = sec
 
     if not args.no_cpu_baseline:

@@ -39,8 +39,8 @@
  *                       while M*N is non-zero; bias NULL with a bias epilogue
  *                       or non-NULL with TG_EPI_NONE; C overlapping A, B or
  *                       bias.
- *   TG_ERR_UNSUPPORTED  an operand of 2^31 or more elements (4 GiB), a
- *                       dimension above 2^30, or an explicit path
+ *   TG_ERR_UNSUPPORTED  an operand of more than 2^31 - 64 elements (just
+ *                       under 4 GiB), a dimension above 2^30, or an explicit path
  *                       (tg_gemm_path) whose shape/alignment requirements the
  *                       arguments do not meet.
  *   TG_ERR_LAUNCH       the HIP runtime reported an error for the launch.

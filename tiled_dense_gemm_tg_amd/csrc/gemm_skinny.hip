@@ -18,10 +18,12 @@
 //     MFMA j is column 4 p + j) and the 16 x 32 slice of A (8 k of row p per
 //     lane, one 16-byte load from L2) as its 16-column operand, so the 16
 //     MFMA columns are the (at most 16) rows of A;
+//   * loads come in batches of 4 steps, double-buffered in registers, so the
+//     next batch is in flight while the current one is multiplied;
 //   * the 8 waves' fp32 partial sums are added in LDS in a fixed order (no
 //     atomics, so results are reproducible), then the fused epilogue and
 //     8-byte stores.
-// Rows m >= M and k >= K are zero-filled in both operands.
+// Loads are range-checked buffer loads; k >= K reads zero in both operands.
 #include "tg_device.h"
 #include "tg_launch.h"
 
@@ -32,6 +34,7 @@ constexpr int SLAB = 64;       // columns per workgroup
 constexpr int WAVES = 8;       // waves per workgroup, splitting K
 constexpr int UNROLL = 4;      // 32-k steps whose loads are in flight together
 constexpr int NTHREADS = 64 * WAVES;
+constexpr uint32_t OOB = 0xFFFFFFF0u;    // byte offset beyond every operand
 
 template <class T, int EPI>
 __global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args) {
@@ -46,7 +49,6 @@ __global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args) {
     const int h = lane >> 4;
     const int nb = blockIdx.x * SLAB;
     const int ncol = nb + 4 * p;              // N % 4 == 0: all four columns valid or none
-    const bool col_ok = ncol < N;
     const bool row_ok = p < M;
 
     const int steps = (K + 31) / 32;
@@ -58,25 +60,36 @@ __global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args) {
     for (int j = 0; j < 4; ++j)
         acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int s0 = s_begin; s0 < s_end; s0 += UNROLL) {
-        u32x2 vb[UNROLL][8];
-        u32x4 va[UNROLL];
+    // Batches of UNROLL 32-k steps, double-buffered in registers: the loads
+    // of the next batch are in flight while the current one is multiplied.
+    // Range-checked buffer loads (out of range reads zero): k >= K and steps
+    // past this wave's range read zero in both operands; rows m >= M and
+    // columns n >= N only reach outputs that are never stored.
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(A), (short)0,
+                                                                        (int)(2u * (uint32_t)M * (uint32_t)K),
+                                                                        0x00020000);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(B), (short)0,
+                                                                        (int)(2u * (uint32_t)K * (uint32_t)N),
+                                                                        0x00020000);
+    const uint32_t a_row = 2u * (uint32_t)p * (uint32_t)K;
+    const uint32_t b_col = 2u * (uint32_t)ncol;
+    const uint32_t b_row = 2u * (uint32_t)N;
+    auto load_batch = [&](u32x2 (&vb)[UNROLL][8], u32x4 (&va)[UNROLL], int s0) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             const int kb = (s0 + u) * 32 + 8 * h;
             const bool live = s0 + u < s_end;
-            u32x4 a = {0u, 0u, 0u, 0u};
-            if (live && row_ok && kb < K)          // K % 8 == 0: the 8 k are all valid or none
-                a = *reinterpret_cast<const u32x4 *>(A + (uint32_t)p * (uint32_t)K + kb);
-            va[u] = a;
+            // K % 8 == 0: the 8 k of the A chunk are all valid or none
+            const uint32_t aoff = (live && kb < K) ? a_row + 2u * (uint32_t)kb : OOB;
+            va[u] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)aoff, 0, 0);
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
-                u32x2 b = {0u, 0u};
-                if (live && col_ok && kb + r < K)
-                    b = *reinterpret_cast<const u32x2 *>(B + (uint32_t)(kb + r) * (uint32_t)N + ncol);
-                vb[u][r] = b;
+                const uint32_t boff = (live && kb + r < K) ? (uint32_t)(kb + r) * b_row + b_col : OOB;
+                vb[u][r] = __builtin_amdgcn_raw_buffer_load_b64(rb, (int)boff, 0, 0);
             }
         }
+    };
+    auto mma_batch = [&](const u32x2 (&vb)[UNROLL][8], const u32x4 (&va)[UNROLL]) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
 #pragma unroll
@@ -97,6 +110,24 @@ __global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args) {
                 acc[j] = T::mfma16(w, va[u], acc[j]);
             }
         }
+    };
+    u32x2 vb0[UNROLL][8], vb1[UNROLL][8];
+    u32x4 va0[UNROLL], va1[UNROLL];
+    int s0 = s_begin;
+    if (s0 < s_end)
+        load_batch(vb0, va0, s0);
+    while (s0 < s_end) {
+        const int s1 = s0 + UNROLL;
+        if (s1 < s_end)
+            load_batch(vb1, va1, s1);
+        mma_batch(vb0, va0);
+        if (s1 >= s_end)
+            break;
+        const int s2 = s1 + UNROLL;
+        if (s2 < s_end)
+            load_batch(vb0, va0, s2);
+        mma_batch(vb1, va1);
+        s0 = s2;
     }
 
     // acc[j][e] is D_j[row 4 h + e][col p]: C[m = p][n = nb + 16 h + 4 e + j].

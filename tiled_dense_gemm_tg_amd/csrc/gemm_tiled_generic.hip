@@ -2,14 +2,15 @@
 // any alignment (gfx950).
 //
 // Same tiling as the vector kernel (gemm_tiled.hip) and the same fragment
-// layout and epilogue, but operands are fetched element by element, so odd K
-// or N and 2-byte-aligned pointers are fine.  Elements travel through
+// layout and epilogue, but rows of A and B may start at any 2-byte boundary
+// (odd K or N, 2-byte-aligned pointers), so operands cannot go straight to
+// LDS as aligned 16-byte pieces.  Each 8-element chunk is fetched as a
+// dword-aligned 16-byte load plus one dword and shifted into place, through
 // registers: each thread gathers an 8 k x 8 m block of A and an 8 k x 8 n
-// block of B per 64-wide k-slice, packs them, transposes B in registers with
-// v_perm_b32 (both LDS tiles are K-contiguous, [row][64 k]) and writes them
-// into the other of two LDS stages while the MFMAs run on the current one.
-// Loads are range-checked buffer loads: k >= K reads as zero in both operands;
-// rows past M and columns past N are never stored.
+// block of B per 64-wide k-slice, transposes B in registers with v_perm_b32
+// (both LDS tiles are K-contiguous, [row][64 k]) and writes them into the
+// other of two LDS stages while the MFMAs run on the current one.  Stores are
+// element-granular.  Loads are range-checked buffer loads.
 #include "tg_tile.h"
 
 #include <type_traits>
@@ -32,45 +33,80 @@ __device__ __forceinline__ int lds_slot(int row, int chunk) {
     return row * CHUNKS + (chunk ^ (((row >> 1) ^ (row << 2)) & 7));
 }
 
+// Out-of-range byte offset for these loads: it and offset + 16 both stay
+// beyond every operand (operands are below 2^32 - 32 bytes).
+constexpr uint32_t OOB_G = 0xFFFFFFE0u;
+
+// Buffer over [p, p + bytes) whose base is rounded down to 4 bytes, so that
+// every dword-aligned offset is a dword-aligned address; `adj` (0 or 2) is
+// added to all offsets.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t dword_buffer(const void *p, uint32_t bytes, uint32_t &adj) {
+    adj = (uint32_t)((uintptr_t)p & 2u);
+    return tile::buffer_of((const char *)p - adj, bytes + adj);
+}
+
+// 8 consecutive 16-bit elements at byte offset `ob` (2-byte aligned) of a
+// buffer of `limit` bytes: the 16 bytes at the enclosing dword-aligned offset
+// plus the next dword, shifted down by 0 or 2 bytes (v_alignbyte_b32).  A
+// 16-byte load that crosses the end of the buffer reads as all zeros, so a
+// chunk whose bytes straddle the end (only the last chunks of an operand) is
+// fetched element by element instead.  With ob = OOB_G everything reads 0.
+__device__ __forceinline__ u32x4 load8(__amdgpu_buffer_rsrc_t r, uint32_t ob, uint32_t limit) {
+    const uint32_t o4 = ob & ~3u;
+    const uint32_t sh = ob & 2u;
+    if (o4 >= limit || o4 + 16u + 2u * sh <= limit) {
+        const u32x4 d = __builtin_amdgcn_raw_buffer_load_b128(r, (int)o4, 0, 0);
+        const uint32_t e = __builtin_amdgcn_raw_buffer_load_b32(r, (int)(o4 + 16u), 0, 0);
+        return u32x4{__builtin_amdgcn_alignbyte(d.y, d.x, sh), __builtin_amdgcn_alignbyte(d.z, d.y, sh),
+                     __builtin_amdgcn_alignbyte(d.w, d.z, sh), __builtin_amdgcn_alignbyte(e, d.w, sh)};
+    }
+    uint16_t v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+        v[q] = __builtin_amdgcn_raw_buffer_load_b16(r, (int)(ob + 2u * q), 0, 0);
+    return u32x4{pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])};
+}
+
 // Thread t gathers A chunk c = t % 8 (8 k) of rows t/8 + 32 i (i = 0..7) and
-// B rows 8 (t%8) + r (r = 0..7) of the 8 columns 8 (t/8) ...
+// B rows 8 (t%8) + r (r = 0..7) of the 8 columns 8 (t/8) ...  Elements k >= K
+// are zeroed in both operands (A per element, B per row); rows past M and
+// columns past N only reach outputs that are never stored.
 struct Gather {
     __amdgpu_buffer_rsrc_t ra, rb;
     uint32_t a_row_off, a_row_step, b_col_off, b_row;
+    uint32_t a_limit, b_limit;   // buffer sizes in bytes
     int K, kq;
 
     __device__ __forceinline__ Gather(const GemmArgs &g, int m0, int n0, int tid) {
-        ra = tile::buffer_of(g.A, 2u * (uint32_t)g.M * (uint32_t)g.K);
-        rb = tile::buffer_of(g.B, 2u * (uint32_t)g.K * (uint32_t)g.N);
+        uint32_t a_adj, b_adj;
+        ra = dword_buffer(g.A, 2u * (uint32_t)g.M * (uint32_t)g.K, a_adj);
+        rb = dword_buffer(g.B, 2u * (uint32_t)g.K * (uint32_t)g.N, b_adj);
+        a_limit = a_adj + 2u * (uint32_t)g.M * (uint32_t)g.K;
+        b_limit = b_adj + 2u * (uint32_t)g.K * (uint32_t)g.N;
         K = g.K;
         kq = 8 * (tid & 7);
-        a_row_off = 2u * ((uint32_t)(m0 + (tid >> 3)) * (uint32_t)g.K + (uint32_t)kq);
+        a_row_off = a_adj + 2u * ((uint32_t)(m0 + (tid >> 3)) * (uint32_t)g.K + (uint32_t)kq);
         a_row_step = 64u * (uint32_t)g.K;
         b_row = 2u * (uint32_t)g.N;
-        b_col_off = (uint32_t)kq * b_row + 2u * (uint32_t)(n0 + 8 * (tid >> 3));
+        b_col_off = b_adj + (uint32_t)kq * b_row + 2u * (uint32_t)(n0 + 8 * (tid >> 3));
     }
 
     __device__ __forceinline__ void load(u32x4 (&xa)[8], u32x4 (&xb)[8], int k0) const {
+        // number of this thread's 8 A elements with k < K (same for all rows)
+        const int nv = K - (k0 + kq);
+        u32x4 amask;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            amask[i] = (2 * i + 1 < nv) ? 0xFFFFFFFFu : ((2 * i < nv) ? 0x0000FFFFu : 0u);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            uint16_t e[8];
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const uint32_t off =
-                    (k0 + kq + q < K) ? a_row_off + (uint32_t)i * a_row_step + 2u * (uint32_t)(k0 + q) : OOB;
-                e[q] = __builtin_amdgcn_raw_buffer_load_b16(ra, (int)off, 0, 0);
-            }
-            xa[i] = u32x4{pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]), pack2(e[6], e[7])};
+            const uint32_t off = (nv > 0) ? a_row_off + (uint32_t)i * a_row_step + 2u * (uint32_t)k0 : OOB_G;
+            xa[i] = load8(ra, off, a_limit) & amask;
         }
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-            uint16_t e[8];
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const uint32_t off = (k0 + kq + r < K) ? b_col_off + (uint32_t)(k0 + r) * b_row + 2u * q : OOB;
-                e[q] = __builtin_amdgcn_raw_buffer_load_b16(rb, (int)off, 0, 0);
-            }
-            xb[r] = u32x4{pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]), pack2(e[6], e[7])};
+            const uint32_t off = (k0 + kq + r < K) ? b_col_off + (uint32_t)(k0 + r) * b_row : OOB_G;
+            xb[r] = load8(rb, off, b_limit);
         }
     }
 };

@@ -13,7 +13,9 @@
 
 namespace {
 
-constexpr int64_t kMaxElements = (int64_t(1) << 31) - 1;  // per operand: below 4 GiB of 16-bit values
+// Per operand: kernels address operands with 32-bit byte offsets and keep
+// offsets of at least 2^32 - 32 for "out of range", so operands stay below that.
+constexpr int64_t kMaxElements = (int64_t(1) << 31) - 64;
 constexpr int64_t kMaxDim = int64_t(1) << 30;
 
 bool aligned(const void *p, uintptr_t bytes) { return (reinterpret_cast<uintptr_t>(p) % bytes) == 0; }
