@@ -18,7 +18,7 @@
 //     MFMA j is column 4 p + j) and the 16 x 32 slice of A (8 k of row p per
 //     lane, one 16-byte load from L2) as its 16-column operand, so the 16
 //     MFMA columns are the (at most 16) rows of A;
-//   * loads come in batches of 4 steps, double-buffered in registers, so the
+//   * loads come in batches of 2 steps, double-buffered in registers, so the
 //     next batch is in flight while the current one is multiplied;
 //   * the 8 waves' fp32 partial sums are added in LDS in a fixed order (no
 //     atomics, so results are reproducible), then the fused epilogue and
@@ -32,7 +32,7 @@ namespace {
 
 constexpr int SLAB = 64;       // columns per workgroup
 constexpr int WAVES = 8;       // waves per workgroup, splitting K
-constexpr int UNROLL = 4;      // 32-k steps whose loads are in flight together
+constexpr int UNROLL = 2;      // 32-k steps per load batch (two batches in flight)
 constexpr int NTHREADS = 64 * WAVES;
 constexpr uint32_t OOB = 0xFFFFFFF0u;    // byte offset beyond every operand
 
