@@ -232,3 +232,20 @@ def test_runs_on_a_non_default_stream():
         out = run(M, N, K, I.BF16, A, B, stream=s)
     s.synchronize()
     check_tolerance(I.BF16, to_bits(out), ref64, "side stream")
+
+
+@pytest.mark.parametrize("dtype,M,N,K", [
+    (I.F16, 2304, 8192, 200),    # 288 tiles, a multiple of the 8 XCDs
+    (I.BF16, 4350, 4360, 96),    # 306 tiles, ragged in M and N
+    (I.F16, 16384, 4096, 64),    # 1024 tiles, four per workgroup on 256 CUs
+])
+def test_persistent_grid_covers_every_tile(dtype, M, N, K):
+    """More tiles than compute units: each workgroup of the vector kernel
+    walks several tiles; every output must be written once, exactly."""
+    A = I.small_int_bits((M, K), dtype, 80)
+    B = I.small_int_bits((K, N), dtype, 81)
+    bias = I.small_int_bits((N,), dtype, 82)
+    log(f"[persistent] dtype={dtype} M={M} N={N} K={K}")
+    out = run(M, N, K, dtype, A, B, bias, I.EPI_BIAS, expect_path=tg.TG_PATH_TILED)
+    _, refq = oracle.gemm(M, N, K, dtype, A, B, bias, I.EPI_BIAS)
+    check_exact(to_bits(out), refq, f"persistent {M}x{N}x{K}")

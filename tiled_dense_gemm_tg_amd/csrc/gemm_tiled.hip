@@ -261,129 +261,149 @@ __device__ __forceinline__ void kstep(const Frag &cur, Frag &nxt, f32x16 (&acc)[
     }
 }
 
+// Persistent: the grid has at most one workgroup per CU, and workgroup g
+// computes tiles g, g + G, g + 2G, ... (G = grid size, a multiple of the 8
+// XCDs when the tile count allows, so every tile of a workgroup stays on its
+// XCD in the raster), which removes the dispatch gap between tiles.
 template <class T, int EPI>
 __global__ __launch_bounds__(NTHREADS) void gemm_tiled_kernel(GemmArgs args) {
     __shared__ __attribute__((aligned(16))) u32x4 smem[STAGES * STAGE_BYTES / 16];
-    int tm, tn;
-    tile::tile_of_workgroup(args.M, args.N, tm, tn);
-    const int m0 = tm * BM;
-    const int n0 = tn * BN;
-    const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave >> 1;
     const int wn = wave & 1;
     const uint32_t lds0 = lds_address(smem);
-    const Dma dma(args, m0, n0, wave, lane, lds0);
-    const FragAddr fad(wm, wn, lane);
     auto stage = [&](int st) { return lds0 + (uint32_t)st * (uint32_t)STAGE_BYTES; };
-
-    f32x16 acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            acc[i][j] = f32x16{};
-
+    const int total = ((args.M + BM - 1) / BM) * ((args.N + BN - 1) / BN);
     const int nk = (args.K + BK - 1) / BK;
-    Frag f0, f1;
-    // Prologue: request slices 0..2, wait for slice 0.
-    if (nk > 0) {
-        dma.issue(0, 0);
-        if (nk > 1)
-            dma.issue(1, 1);
-        if (nk > 2) {
-            dma.issue(2, 2);
-            wait_vmcnt<16>();
-        } else if (nk > 1) {
-            wait_vmcnt<8>();
-        } else {
-            wait_vmcnt<0>();
-        }
-    }
-    __syncthreads();
-    if (nk > 0) {
+
+    for (int w = blockIdx.x; w < total; w += gridDim.x) {
+        // The lane id is made opaque per tile so that the per-lane addresses
+        // below are recomputed for each tile instead of being hoisted out of
+        // the tile loop, where they would stay live through the k-loop.
+        int lane = threadIdx.x & 63;
+        asm volatile("" : "+v"(lane));
+        const FragAddr fad(wm, wn, lane);
+        int tm, tn;
+        tile::tile_of_workgroup(args.M, args.N, w, tm, tn);
+        const int m0 = tm * BM;
+        const int n0 = tn * BN;
+        const Dma dma(args, m0, n0, wave, lane, lds0);
+
+        f32x16 acc[4][4];
 #pragma unroll
-        for (int r = 0; r < 12; ++r)
-            read_one(f0, fad, stage(0), 0, r);
-    }
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = f32x16{};
 
-    // Slice t in stage t%4, fragments of its first k-step already in f0:
-    //   step 0: MFMAs on f0, reads of step 1 into f1, first half of the
-    //           direct loads of slice t+3 into stage (t+3)%4 (that stage was
-    //           last read in slice t-1, before the previous barrier);
-    //   wait until this wave's loads of slice t+1 have landed, barrier
-    //           (everyone's have, and everyone's reads of slice t are done);
-    //   step 1: MFMAs on f1, reads of step 0 of slice t+1 into f0, second
-    //           half of the direct loads of slice t+3.
-    // Loads issued after slice t+1's when waiting: all 8 of slice t+2 and
-    // the first 4 of slice t+3, hence vmcnt(12) in the steady state.
-    // ISSUE: 0 = no loads, 1 = loads of a full slice, 2 = loads of the
-    // (possibly partial) last slice.
-    auto slice = [&](int t, auto issue, auto wait, auto next) __attribute__((always_inline)) {
-        const uint32_t st = stage(t & 3);
-        constexpr int ISSUE_KIND = decltype(issue)::value;
-        constexpr bool ISSUE = ISSUE_KIND != 0;
-        constexpr bool FULL = ISSUE_KIND == 1;
-        constexpr bool NEXT = decltype(next)::value;
-        const int kt = t + 3;
-        auto dma_lo = [&](int d) __attribute__((always_inline)) { dma.issue_one<FULL>(kt, kt & 3, d); };
-        auto dma_hi = [&](int d) __attribute__((always_inline)) { dma.issue_one<FULL>(kt, kt & 3, d + 4); };
-        kstep<T, true, ISSUE>(f0, f1, acc, fad, st, 1, dma_lo);
-        if constexpr (NEXT) {
-            wait_vmcnt<decltype(wait)::value>();
-            __syncthreads();
+        Frag f0, f1;
+        // Prologue: request slices 0..2, wait for slice 0.  The previous
+        // tile's C stores are older than these loads, so the same counts hold.
+        if (nk > 0) {
+            dma.issue(0, 0);
+            if (nk > 1)
+                dma.issue(1, 1);
+            if (nk > 2) {
+                dma.issue(2, 2);
+                wait_vmcnt<16>();
+            } else if (nk > 1) {
+                wait_vmcnt<8>();
+            } else {
+                wait_vmcnt<0>();
+            }
         }
-        kstep<T, NEXT, ISSUE>(f1, f0, acc, fad, stage((t + 1) & 3), 0, dma_hi);
-    };
-    using yes = std::true_type;
-    using no = std::false_type;
-    using none = std::integral_constant<int, 0>;
-    using full = std::integral_constant<int, 1>;
-    using last = std::integral_constant<int, 2>;
-    using w12 = std::integral_constant<int, 12>;
-    using w8 = std::integral_constant<int, 8>;
-    using w0 = std::integral_constant<int, 0>;
-    int t = 0;
-    for (; t + 4 < nk; ++t)
-        slice(t, full{}, w12{}, yes{});
-    if (t + 3 < nk) {
-        slice(t, last{}, w12{}, yes{});
-        ++t;
-    }
-    if (t + 3 == nk && t < nk) {
-        slice(t, none{}, w8{}, yes{});
-        ++t;
-    }
-    if (t + 2 == nk && t < nk) {
-        slice(t, none{}, w0{}, yes{});
-        ++t;
-    }
-    if (t + 1 == nk)
-        slice(t, none{}, w0{}, no{});
+        __syncthreads();
+        if (nk > 0) {
+#pragma unroll
+            for (int r = 0; r < 12; ++r)
+                read_one(f0, fad, stage(0), 0, r);
+        }
 
-    tile::store_tile<T, EPI, true>(args, acc, m0, n0, wm, wn, lane);
+        // Slice t in stage t%4, fragments of its first k-step already in f0:
+        //   step 0: MFMAs on f0, reads of step 1 into f1, first half of the
+        //           direct loads of slice t+3 into stage (t+3)%4 (that stage was
+        //           last read in slice t-1, before the previous barrier);
+        //   wait until this wave's loads of slice t+1 have landed, barrier
+        //           (everyone's have, and everyone's reads of slice t are done);
+        //   step 1: MFMAs on f1, reads of step 0 of slice t+1 into f0, second
+        //           half of the direct loads of slice t+3.
+        // Loads issued after slice t+1's when waiting: all 8 of slice t+2 and
+        // the first 4 of slice t+3, hence vmcnt(12) in the steady state.
+        // ISSUE: 0 = no loads, 1 = loads of a full slice, 2 = loads of the
+        // (possibly partial) last slice.
+        auto slice = [&](int t, auto issue, auto wait, auto next) __attribute__((always_inline)) {
+            const uint32_t st = stage(t & 3);
+            constexpr int ISSUE_KIND = decltype(issue)::value;
+            constexpr bool ISSUE = ISSUE_KIND != 0;
+            constexpr bool FULL = ISSUE_KIND == 1;
+            constexpr bool NEXT = decltype(next)::value;
+            const int kt = t + 3;
+            auto dma_lo = [&](int d) __attribute__((always_inline)) { dma.issue_one<FULL>(kt, kt & 3, d); };
+            auto dma_hi = [&](int d) __attribute__((always_inline)) { dma.issue_one<FULL>(kt, kt & 3, d + 4); };
+            kstep<T, true, ISSUE>(f0, f1, acc, fad, st, 1, dma_lo);
+            if constexpr (NEXT) {
+                wait_vmcnt<decltype(wait)::value>();
+                __syncthreads();
+            }
+            kstep<T, NEXT, ISSUE>(f1, f0, acc, fad, stage((t + 1) & 3), 0, dma_hi);
+        };
+        using yes = std::true_type;
+        using no = std::false_type;
+        using none = std::integral_constant<int, 0>;
+        using full = std::integral_constant<int, 1>;
+        using last = std::integral_constant<int, 2>;
+        using w12 = std::integral_constant<int, 12>;
+        using w8 = std::integral_constant<int, 8>;
+        using w0 = std::integral_constant<int, 0>;
+        int t = 0;
+        for (; t + 4 < nk; ++t)
+            slice(t, full{}, w12{}, yes{});
+        if (t + 3 < nk) {
+            slice(t, last{}, w12{}, yes{});
+            ++t;
+        }
+        if (t + 3 == nk && t < nk) {
+            slice(t, none{}, w8{}, yes{});
+            ++t;
+        }
+        if (t + 2 == nk && t < nk) {
+            slice(t, none{}, w0{}, yes{});
+            ++t;
+        }
+        if (t + 1 == nk)
+            slice(t, none{}, w0{}, no{});
+
+        tile::store_tile<T, EPI, true>(args, acc, m0, n0, wm, wn, lane);
+        // every wave is done reading LDS before the next tile's loads land
+        __syncthreads();
+    }
 }
 
 template <class T, int EPI>
-hipError_t launch_typed(const GemmArgs &a, hipStream_t stream) {
-    const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-    hipLaunchKernelGGL((gemm_tiled_kernel<T, EPI>), dim3(tiles), dim3(NTHREADS), 0, stream, a);
+hipError_t launch_typed(const GemmArgs &a, int grid, hipStream_t stream) {
+    hipLaunchKernelGGL((gemm_tiled_kernel<T, EPI>), dim3(grid), dim3(NTHREADS), 0, stream, a);
     return hipGetLastError();
 }
 
 template <class T>
-hipError_t launch_epi(int epi, const GemmArgs &a, hipStream_t stream) {
+hipError_t launch_epi(int epi, const GemmArgs &a, int grid, hipStream_t stream) {
     switch (epi) {
-    case EPI_NONE: return launch_typed<T, EPI_NONE>(a, stream);
-    case EPI_BIAS: return launch_typed<T, EPI_BIAS>(a, stream);
-    default: return launch_typed<T, EPI_BIAS_GELU_TANH>(a, stream);
+    case EPI_NONE: return launch_typed<T, EPI_NONE>(a, grid, stream);
+    case EPI_BIAS: return launch_typed<T, EPI_BIAS>(a, grid, stream);
+    default: return launch_typed<T, EPI_BIAS_GELU_TANH>(a, grid, stream);
     }
 }
 
 }  // namespace
 
-hipError_t launch_tiled_vec(int dtype, int epi, const GemmArgs &a, hipStream_t stream) {
-    return dtype == 0 ? launch_epi<F16>(epi, a, stream) : launch_epi<BF16>(epi, a, stream);
+hipError_t launch_tiled_vec(int dtype, int epi, const GemmArgs &a, int num_cu, hipStream_t stream) {
+    const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+    int grid = tiles;
+    if (num_cu > 0 && tiles > num_cu) {
+        // one workgroup per CU, rounded down to a multiple of the XCD count
+        grid = num_cu >= tile::NUM_XCD ? num_cu - num_cu % tile::NUM_XCD : num_cu;
+    }
+    return dtype == 0 ? launch_epi<F16>(epi, a, grid, stream) : launch_epi<BF16>(epi, a, grid, stream);
 }
 
 }  // namespace tg

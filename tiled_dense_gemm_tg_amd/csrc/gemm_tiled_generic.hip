@@ -160,7 +160,7 @@ template <class T, int EPI>
 __global__ __launch_bounds__(NTHREADS) void gemm_tiled_generic_kernel(GemmArgs args) {
     __shared__ u32x4 smem[4 * TILE_U4];  // A stage 0, A stage 1, B stage 0, B stage 1
     int tm, tn;
-    tile::tile_of_workgroup(args.M, args.N, tm, tn);
+    tile::tile_of_workgroup(args.M, args.N, blockIdx.x, tm, tn);
     const int m0 = tm * BM;
     const int n0 = tn * BN;
     const int tid = threadIdx.x;

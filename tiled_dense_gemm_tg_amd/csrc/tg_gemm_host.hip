@@ -1,12 +1,14 @@
 // tg_gemm_host.hip -- the C interface (include/tg_gemm.h): argument checks,
 // choice of kernel family and the launch on the caller's stream.
 //
-// Everything before the launch is plain host arithmetic on the arguments: no
-// HIP call, no device memory access, no allocation and no state, so invalid
-// arguments never reach the device and concurrent calls need no locking.
+// Argument checks are plain host arithmetic: no HIP call, no device memory
+// access and no allocation, so invalid arguments never reach the device.  The
+// only state is a per-device cache of the compute-unit count (one HIP query
+// per device, stored atomically), so concurrent calls need no locking.
 #include "tg_gemm.h"
 #include "tg_launch.h"
 
+#include <atomic>
 #include <stdint.h>
 
 #define TG_EXPORT extern "C" __attribute__((visibility("default")))
@@ -81,6 +83,24 @@ bool tiled_ok(int64_t M, int64_t N, int64_t K, const void *A, const void *B, con
            2 * M * K < two_gib && 2 * K * N < two_gib;
 }
 
+// Compute units of the device that `stream` belongs to (0 if unknown: the
+// launchers then use one workgroup per tile).
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_num_cu[kMaxDevices];
+
+int num_cu_of(hipStream_t stream) {
+    int dev = -1;
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return 0;
+    int n = g_num_cu[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            return 0;
+        g_num_cu[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
 tg_path auto_path(int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *bias,
                   const void *C) {
     if (skinny_ok(M, N, K, A, B, bias, C))
@@ -131,7 +151,7 @@ TG_EXPORT tg_status tg_gemm_path(tg_path path, int64_t M, int64_t N, int64_t K, 
     if (path == TG_PATH_SKINNY)
         e = tg::launch_skinny(dtype, epilogue, a, s);
     else if (path == TG_PATH_TILED)
-        e = tg::launch_tiled_vec(dtype, epilogue, a, s);
+        e = tg::launch_tiled_vec(dtype, epilogue, a, num_cu_of(s), s);
     else
         e = tg::launch_tiled_generic(dtype, epilogue, a, s);
     return e == hipSuccess ? TG_OK : TG_ERR_LAUNCH;

@@ -20,7 +20,8 @@ struct GemmArgs {
 
 // 256 x 256 tiles with 16-byte direct-to-LDS loads: K % 8 == 0, N % 8 == 0,
 // A, B, C 16-byte aligned, bias 8-byte aligned, A and B below 2 GiB.
-hipError_t launch_tiled_vec(int dtype, int epi, const GemmArgs &a, hipStream_t stream);
+// Persistent: at most num_cu workgroups (num_cu <= 0: one per tile).
+hipError_t launch_tiled_vec(int dtype, int epi, const GemmArgs &a, int num_cu, hipStream_t stream);
 
 // 256 x 256 tiles with element-granular loads and stores: any shape.
 hipError_t launch_tiled_generic(int dtype, int epi, const GemmArgs &a, hipStream_t stream);

@@ -16,16 +16,16 @@ constexpr int GROUP_M = 4;                // tile rows per raster group
 constexpr int NUM_XCD = 8;
 constexpr uint32_t OOB = 0xFFFFFFF0u;     // byte offset beyond every operand (< 2^32 - 32 bytes)
 
-// Workgroups are dispatched round-robin over the 8 XCDs.  Give each XCD a
-// contiguous range of logical tiles, and walk them GROUP_M tile-rows at a
-// time, column by column, so that the tiles running together on one XCD share
-// A row-panels and B column-panels in that XCD's L2.  A bijection on
-// [0, tiles) for any grid.
-__device__ __forceinline__ void tile_of_workgroup(int M, int N, int &tm, int &tn) {
+// Workgroups are dispatched round-robin over the 8 XCDs, so tile id w runs
+// on XCD w % 8 (also for a persistent grid whose size is a multiple of 8).
+// Give each XCD a contiguous range of logical tiles, and walk them GROUP_M
+// tile-rows at a time, column by column, so that the tiles running together
+// on one XCD share A row-panels and B column-panels in that XCD's L2.  A
+// bijection on [0, tiles).
+__device__ __forceinline__ void tile_of_workgroup(int M, int N, int w, int &tm, int &tn) {
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BN - 1) / BN;
     const int total = tiles_m * tiles_n;
-    int w = blockIdx.x;
     if (total % NUM_XCD == 0)
         w = (w % NUM_XCD) * (total / NUM_XCD) + w / NUM_XCD;
     const int per_group = GROUP_M * tiles_n;
