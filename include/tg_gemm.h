@@ -78,10 +78,12 @@ typedef enum {
  *   TG_PATH_SKINNY         M <= 16 (the decode-shaped product): streams B from
  *                          HBM once; needs K % 8 == 0, N % 4 == 0, A 16-byte
  *                          aligned, B, C and bias 8-byte aligned.
- *   TG_PATH_TILED          256x256x64 MFMA tiles staged through LDS with
+ *   TG_PATH_TILED          256x256 MFMA tiles staged through LDS with
  *                          16-byte loads; needs K % 8 == 0, N % 8 == 0, A, B
  *                          and C 16-byte aligned, bias 8-byte aligned, and A
- *                          and B each smaller than 2 GiB.
+ *                          and B, each padded to whole tiles, below 2 GiB
+ *                          less 64 KiB: 2 (M + 256) K and 2 (K + 32) (N + 256)
+ *                          both below 2^31 - 65536.
  *   TG_PATH_TILED_GENERIC  the same tiling with element-granular loads and
  *                          stores: any shape, any alignment.
  *   TG_PATH_NONE           (reported by tg_gemm_plan only) nothing to launch.

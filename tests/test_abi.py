@@ -118,6 +118,10 @@ def test_empty_K_allows_null_operands(lib):
     (8192, 8192, 8192, {"bias": PBIAS, "epi": I.EPI_BIAS_GELU_TANH}, tg.TG_PATH_TILED),
     (4000, 4093, 4111, {"bias": PBIAS, "epi": I.EPI_BIAS_GELU_TANH, "dtype": I.BF16}, tg.TG_PATH_TILED_GENERIC),
     (4000, 4096, 4104, {}, tg.TG_PATH_TILED),           # ragged M is fine for the vector path
+    (130808, 256, 8192, {}, tg.TG_PATH_TILED),          # 2 (M + 256) K just below 2^31 - 64 Ki
+    (130812, 256, 8192, {}, tg.TG_PATH_TILED_GENERIC),  # ... and at it
+    (256, 130296, 8192, {}, tg.TG_PATH_TILED),          # 2 (K + 32) (N + 256) just below
+    (256, 130304, 8192, {}, tg.TG_PATH_TILED_GENERIC),
     (256, 256, 256, {"C": PC + 8}, tg.TG_PATH_TILED_GENERIC),
     (256, 256, 256, {"B": PB + 2}, tg.TG_PATH_TILED_GENERIC),
     (256, 256, 256, {"bias": PBIAS + 2, "epi": I.EPI_BIAS}, tg.TG_PATH_TILED_GENERIC),

@@ -48,6 +48,7 @@
 #include "tg_tile.h"
 
 #include <type_traits>
+#include <utility>
 
 namespace tg {
 namespace {
@@ -60,7 +61,7 @@ constexpr int STAGES = 4;
 constexpr int A_BYTES = BM * BK * 2;              // 16 KB: [256 m][32 k]
 constexpr int B_BYTES = BK * BN * 2;              // 16 KB: [32 k][256 n]
 constexpr int STAGE_BYTES = A_BYTES + B_BYTES;    // 32 KB
-constexpr uint32_t OOB_BUMP = 0x80000000u;        // + offset < 2^31 -> beyond any operand (< 2 GiB)
+constexpr uint32_t OOB_BUMP = 0x80000000u;        // + offset < 2^31 - 64 KiB -> beyond the operand's buffer
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -90,9 +91,16 @@ __device__ __forceinline__ i32x4 rsrc_words(const void *base, uint32_t bytes) {
     return i32x4{(int)(uint32_t)p, (int)(uint32_t)(p >> 32), (int)bytes, 0x00020000};
 }
 
-// One 16-byte-per-lane buffer load into LDS at m0 + 16 * lane.
+// One 16-byte-per-lane buffer load into LDS: lane L reads 16 bytes at byte
+// offset voffset + OFF of the buffer and writes them to LDS at m0 + OFF + 16 L
+// (the instruction offset moves both addresses).  Loads that share m0 keep
+// the wave from rewriting m0 between them, which stalls until the previous
+// direct load has taken its value.
+template <int OFF>
 __device__ __forceinline__ void dma16(const i32x4 &rsrc, uint32_t voffset, uint32_t m0) {
-    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voffset), "s"(rsrc), "{m0}"(m0));
+    static_assert(OFF >= 0 && OFF < 4096, "12-bit instruction offset");
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen offset:%3 lds" ::"v"(voffset), "s"(rsrc), "{m0}"(m0),
+                 "i"(OFF));
 }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
@@ -106,22 +114,28 @@ __device__ __forceinline__ void wait_vmcnt() {
 // Per-lane addressing of the 8 direct loads that fill one stage.  Wave w,
 // lane L, load q = 0..3:
 //   A: tile rows 64 w + 16 q + L/4, physical chunk L%4 -> logical chunk
-//      c = L%4 ^ a_swz(row) (8 k); destination m0 = stage + 4096 w + 1024 q;
+//      c = L%4 ^ a_swz(row) (8 k); destination stage + 4096 w + 1024 q;
 //   B: k-rows 8 w + 2 q + L/32, physical chunk L%32 -> logical chunk
-//      c = L%32 ^ b_swz(k) (8 n); destination m0 = stage + 16 KB + 4096 w + 1024 q.
+//      c = L%32 ^ b_swz(k) (8 n); destination stage + 16 KB + 4096 w + 1024 q.
+// The four loads of one operand share m0 (stage + 4096 w, or + 16 KB) and
+// reach their destination through the instruction offset 1024 q, which is
+// also added to the memory offset; the lane offsets subtract it back.  So
+// that they stay non-negative, the buffers start 4 KB before the operands
+// (offsets are operand offsets + 4096) and are 4 KB longer.
 struct Dma {
+    static constexpr uint32_t SHIFT = 4096;
     i32x4 ra, rb;
-    uint32_t a_off[4];   // byte offset of this lane's A chunk for load q, k0 = 0
+    uint32_t a_off[4];   // buffer offset of this lane's A chunk for load q, k0 = 0, minus 1024 q
     int a_k;             // first k of the lane's A chunk within the slice
-    uint32_t b_off[4];   // byte offset of this lane's B chunk for load q, k0 = 0
+    uint32_t b_off[4];   // buffer offset of this lane's B chunk for load q, k0 = 0, minus 1024 q
     int b_k[4];          // k-row of load q within the slice
     uint32_t b_row;      // bytes per row of B
     uint32_t m0_a, m0_b; // LDS destinations of load q = 0 in stage 0
     int K;
 
     __device__ __forceinline__ Dma(const GemmArgs &g, int m0, int n0, int wave, int lane, uint32_t lds0) {
-        ra = rsrc_words(g.A, 2u * (uint32_t)g.M * (uint32_t)g.K);
-        rb = rsrc_words(g.B, 2u * (uint32_t)g.K * (uint32_t)g.N);
+        ra = rsrc_words((const char *)g.A - SHIFT, 2u * (uint32_t)g.M * (uint32_t)g.K + SHIFT);
+        rb = rsrc_words((const char *)g.B - SHIFT, 2u * (uint32_t)g.K * (uint32_t)g.N + SHIFT);
         K = g.K;
         const int arow = 64 * wave + (lane >> 2);
         const int ac = (lane & 3) ^ a_swz(lane >> 2);
@@ -129,42 +143,47 @@ struct Dma {
         b_row = 2u * (uint32_t)g.N;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            a_off[q] = 2u * ((uint32_t)(m0 + arow + 16 * q) * (uint32_t)g.K + (uint32_t)a_k);
+            a_off[q] = SHIFT - 1024u * q + 2u * ((uint32_t)(m0 + arow + 16 * q) * (uint32_t)g.K + (uint32_t)a_k);
             const int k = 8 * wave + 2 * q + (lane >> 5);
             const int c = (lane & 31) ^ b_swz(k);
             b_k[q] = k;
-            b_off[q] = (uint32_t)k * b_row + 2u * (uint32_t)(n0 + 8 * c);
+            b_off[q] = SHIFT - 1024u * q + (uint32_t)k * b_row + 2u * (uint32_t)(n0 + 8 * c);
         }
         m0_a = lds0 + 4096u * (uint32_t)wave;
         m0_b = lds0 + (uint32_t)A_BYTES + 4096u * (uint32_t)wave;
     }
 
-    // Direct load d (0..7) of k-slice kt into LDS stage st: A load d/2 for
-    // even d, B load d/2 for odd d.  FULL: the slice lies inside [0, K), so
+    // Direct load d (0..7) of k-slice kt into LDS stage st: A load d for
+    // d < 4, B load d - 4 otherwise.  FULL: the slice lies inside [0, K), so
     // no lane needs the K mask (only the last slice can be partial).
-    template <bool FULL>
-    __device__ __forceinline__ void issue_one(int kt, int st, int d) const {
+    template <bool FULL, int D>
+    __device__ __forceinline__ void issue_one(int kt, int st) const {
+        constexpr int q = D & 3;
         const int k0 = kt * BK;
-        const int q = d >> 1;
         const uint32_t sbase = (uint32_t)st * (uint32_t)STAGE_BYTES;
-        if ((d & 1) == 0) {
+        if constexpr (D < 4) {
             uint32_t off = a_off[q] + 2u * (uint32_t)k0;
             if constexpr (!FULL)
                 off += (k0 + a_k < K) ? 0u : OOB_BUMP;
-            dma16(ra, off, m0_a + sbase + 1024u * q);
+            dma16<1024 * q>(ra, off, m0_a + sbase);
         } else {
             uint32_t off = b_off[q] + (uint32_t)k0 * b_row;
             if constexpr (!FULL)
                 off += (k0 + b_k[q] < K) ? 0u : OOB_BUMP;
-            dma16(rb, off, m0_b + sbase + 1024u * q);
+            dma16<1024 * q>(rb, off, m0_b + sbase);
         }
     }
 
     // Request k-slice kt into LDS stage st.
     __device__ __forceinline__ void issue(int kt, int st) const {
-#pragma unroll
-        for (int d = 0; d < 8; ++d)
-            issue_one<false>(kt, st, d);
+        issue_one<false, 0>(kt, st);
+        issue_one<false, 1>(kt, st);
+        issue_one<false, 2>(kt, st);
+        issue_one<false, 3>(kt, st);
+        issue_one<false, 4>(kt, st);
+        issue_one<false, 5>(kt, st);
+        issue_one<false, 6>(kt, st);
+        issue_one<false, 7>(kt, st);
     }
 };
 
@@ -243,22 +262,27 @@ __device__ __forceinline__ void read_one(Frag &f, const FragAddr &ad, uint32_t s
 // after MFMAs 1, 5, 9, 13 (`dma(d)` for d = 0..3).  sched_barrier keeps the
 // compiler from regrouping: spreading the direct loads lets the memory
 // pipeline take them while the matrix unit stays busy.
+template <class T, bool READ, bool DMA, int Q, typename DmaFn>
+__device__ __forceinline__ void kstep_one(const Frag &cur, Frag &nxt, f32x16 (&acc)[4][4], const FragAddr &ad,
+                                          uint32_t rstage, int rs, DmaFn &dma) {
+    acc[Q >> 2][Q & 3] = T::mfma32(cur.b[Q & 3], cur.a[Q >> 2], acc[Q >> 2][Q & 3]);
+    if constexpr (READ && Q < 12)
+        read_one(nxt, ad, rstage, rs, Q);
+    if constexpr (DMA && (Q & 3) == 1)
+        dma(std::integral_constant<int, (Q >> 2)>{});
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <class T, bool READ, bool DMA, typename DmaFn, int... Q>
+__device__ __forceinline__ void kstep_seq(const Frag &cur, Frag &nxt, f32x16 (&acc)[4][4], const FragAddr &ad,
+                                          uint32_t rstage, int rs, DmaFn &dma, std::integer_sequence<int, Q...>) {
+    (kstep_one<T, READ, DMA, Q>(cur, nxt, acc, ad, rstage, rs, dma), ...);
+}
+
 template <class T, bool READ, bool DMA, typename DmaFn>
 __device__ __forceinline__ void kstep(const Frag &cur, Frag &nxt, f32x16 (&acc)[4][4], const FragAddr &ad,
                                       uint32_t rstage, int rs, DmaFn dma) {
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-        acc[q >> 2][q & 3] = T::mfma32(cur.b[q & 3], cur.a[q >> 2], acc[q >> 2][q & 3]);
-        if constexpr (READ) {
-            if (q < 12)
-                read_one(nxt, ad, rstage, rs, q);
-        }
-        if constexpr (DMA) {
-            if ((q & 3) == 1)
-                dma(q >> 2);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    }
+    kstep_seq<T, READ, DMA>(cur, nxt, acc, ad, rstage, rs, dma, std::make_integer_sequence<int, 16>{});
 }
 
 // Persistent: the grid has at most one workgroup per CU, and workgroup g
@@ -338,8 +362,12 @@ __global__ __launch_bounds__(NTHREADS) void gemm_tiled_kernel(GemmArgs args) {
             constexpr bool FULL = ISSUE_KIND == 1;
             constexpr bool NEXT = decltype(next)::value;
             const int kt = t + 3;
-            auto dma_lo = [&](int d) __attribute__((always_inline)) { dma.issue_one<FULL>(kt, kt & 3, d); };
-            auto dma_hi = [&](int d) __attribute__((always_inline)) { dma.issue_one<FULL>(kt, kt & 3, d + 4); };
+            auto dma_lo = [&](auto d) __attribute__((always_inline)) {
+                dma.template issue_one<FULL, decltype(d)::value>(kt, kt & 3);
+            };
+            auto dma_hi = [&](auto d) __attribute__((always_inline)) {
+                dma.template issue_one<FULL, decltype(d)::value + 4>(kt, kt & 3);
+            };
             kstep<T, true, ISSUE>(f0, f1, acc, fad, st, 1, dma_lo);
             if constexpr (NEXT) {
                 wait_vmcnt<decltype(wait)::value>();

@@ -75,12 +75,15 @@ bool skinny_ok(int64_t M, int64_t N, int64_t K, const void *A, const void *B, co
            aligned(bias, 8);
 }
 
-// The vector tiled kernel masks loads by adding 2^31 to their byte offsets,
-// so A and B must each stay below 2 GiB there.
+// The vector tiled kernel addresses A and B through buffers that start 4 KiB
+// before each operand and masks loads by adding 2^31 to their byte offsets,
+// also for rows and k-rows of the padding past the operand's end; all such
+// offsets must stay below 2^32, so each operand, padded to whole tiles, stays
+// below 2 GiB less 64 KiB.
 bool tiled_ok(int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *bias, const void *C) {
-    const int64_t two_gib = int64_t(1) << 31;
+    const int64_t limit = (int64_t(1) << 31) - 65536;
     return K % 8 == 0 && N % 8 == 0 && aligned(A, 16) && aligned(B, 16) && aligned(C, 16) && aligned(bias, 8) &&
-           2 * M * K < two_gib && 2 * K * N < two_gib;
+           2 * (M + 256) * K < limit && 2 * (K + 32) * (N + 256) < limit;
 }
 
 // Compute units of the device that `stream` belongs to (0 if unknown: the

@@ -19,7 +19,8 @@ struct GemmArgs {
 // dtype: 0 fp16, 1 bf16; epi: 0 none, 1 bias, 2 bias + GELU(tanh).
 
 // 256 x 256 tiles with 16-byte direct-to-LDS loads: K % 8 == 0, N % 8 == 0,
-// A, B, C 16-byte aligned, bias 8-byte aligned, A and B below 2 GiB.
+// A, B, C 16-byte aligned, bias 8-byte aligned, 2 (M + 256) K and
+// 2 (K + 32) (N + 256) below 2^31 - 65536.
 // Persistent: at most num_cu workgroups (num_cu <= 0: one per tile).
 hipError_t launch_tiled_vec(int dtype, int epi, const GemmArgs &a, int num_cu, hipStream_t stream);
 
