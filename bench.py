@@ -49,6 +49,11 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 # ---------------------------------------------------------------- accounting
 
+# Elementwise passes the unfused form adds after the product, each reading
+# and writing M x N 16-bit values (4 bytes per element).
+EPILOGUE_PASSES = {0: 0, 1: 1, 2: 2}
+
+
 def gemm_flops(M: int, N: int, K: int) -> int:
     """Multiply-adds counted as two flops: 2*M*N*K."""
     return 2 * M * N * K
@@ -101,8 +106,9 @@ def log(msg: str) -> None:
 
 # ---------------------------------------------------------------- timing
 
-def time_gemm(torch, tg, w, sets, steps, warmup):
-    """Per-launch time (ms) of tg_gemm over `sets` rotating operand sets."""
+def time_gemm(torch, tg, w, sets, steps, warmup, unfused=False):
+    """Per-launch time (ms) of tg_gemm (or, with `unfused`, of the three-launch
+    tg_gemm_unfused) over `sets` rotating operand sets."""
     stream = torch.cuda.current_stream()
     handle = stream.cuda_stream
     calls = []
@@ -111,7 +117,8 @@ def time_gemm(torch, tg, w, sets, steps, warmup):
 
     def launch(i):
         a, b, bi, c = calls[i % len(calls)]
-        st = tg.tg_gemm(w.M, w.N, w.K, w.dtype, a, b, bi, w.epilogue, c, handle)
+        fn = tg.tg_gemm_unfused if unfused else tg.tg_gemm
+        st = fn(w.M, w.N, w.K, w.dtype, a, b, bi, w.epilogue, c, handle)
         if st != tg.TG_OK:
             raise RuntimeError(f"tg_gemm failed: {tg.tg_status_string(st)}")
 
@@ -252,6 +259,13 @@ def main() -> int:
             "timed_region_wall_s": round(wall, 4),
         },
     }
+    fusion = {}
+    if not args.no_secondary and w.epilogue != I.EPI_NONE:
+        log(f"{w.name}: unfused (product, bias pass, GELU pass)")
+        msu, _ = time_gemm(torch, tg, w, sets, max(args.steps // 2, 20), args.warmup, unfused=True)
+        fusion[w.name] = {"fused_us": round(ms * 1e3, 2), "unfused_us": round(msu * 1e3, 2),
+                          "fusion_speedup": round(msu / ms, 3),
+                          "unfused_extra_bytes": EPILOGUE_PASSES[w.epilogue] * 4 * w.M * w.N}
     del sets
     torch.cuda.empty_cache()
 
@@ -290,7 +304,13 @@ def main() -> int:
         sec[w3.name] = {"us_per_launch": round(ms3 * 1e3, 2), "TFLOP/s": round(t3, 2),
                         "frac_mfma_peak": round(t3 / PEAK_MFMA_F16_TFLOPS, 4), "path": "tiled_generic",
                         "traffic": measured_traffic(w3.name)}
+        log(f"{w3.name}: unfused")
+        ms3u, _ = time_gemm(torch, tg, w3, sets3, max(args.steps // 2, 20), args.warmup, unfused=True)
+        fusion[w3.name] = {"fused_us": round(ms3 * 1e3, 2), "unfused_us": round(ms3u * 1e3, 2),
+                           "fusion_speedup": round(ms3u / ms3, 3),
+                           "unfused_extra_bytes": EPILOGUE_PASSES[w3.epilogue] * 4 * w3.M * w3.N}
         del sets3
+        sec["epilogue_fusion"] = fusion
         result["secondary"] = sec
 
     if not args.no_cpu_baseline:

@@ -129,6 +129,43 @@ tg_status tg_gemm_plan(int64_t M, int64_t N, int64_t K, tg_dtype dtype,
                        const void *A, const void *B, const void *bias, tg_epilogue epilogue,
                        const void *C, tg_path *path_out);
 
+/*
+ * Elementwise epilogue steps as passes of their own over a matrix in device
+ * memory -- the unfused form of the epilogue that the fourth TileLang page
+ * ("Designing high-performance GPU kernels with TileLang", part 3 "Epilogue
+ * fusion") measures the fused one against:
+ *   TG_EW_BIAS_ADD   Y[m][n] = X[m][n] + bias[n]
+ *   TG_EW_GELU_TANH  Y[m][n] = GELU_tanh(X[m][n])    (bias must be NULL)
+ * computed in fp32 from the 16-bit inputs and rounded to nearest even once.
+ *   M, N    matrix sizes (>= 0); M == 0 or N == 0 is a no-op
+ *   dtype   format of X, Y and bias
+ *   bias    device pointer, N entries (TG_EW_BIAS_ADD only)
+ *   X, Y    device pointers, M x N row-major; Y == X (in place) is allowed,
+ *           any other overlap of Y with X or bias is TG_ERR_INVALID_ARG
+ *   stream  hipStream_t or NULL
+ * Any alignment works; N % 8 == 0 with 16-byte aligned X, Y and bias takes
+ * the 16-byte path.  TG_ERR_UNSUPPORTED: M x N above 2^31 - 64 elements.
+ */
+typedef enum {
+    TG_EW_BIAS_ADD = 0,
+    TG_EW_GELU_TANH = 1
+} tg_elementwise_op;
+
+tg_status tg_elementwise(tg_elementwise_op op, int64_t M, int64_t N, tg_dtype dtype,
+                         const void *bias, const void *X, void *Y, void *stream);
+
+/*
+ * The same result as tg_gemm up to rounding, computed unfused: the product
+ * without epilogue is written to C, then TG_EW_BIAS_ADD and (for
+ * TG_EPI_BIAS_GELU_TANH) TG_EW_GELU_TANH run in place on C -- one, two or
+ * three launches, each intermediate rounded to `dtype` in C.  Same arguments
+ * and errors as tg_gemm.  A baseline for measuring what fusion saves, not a
+ * faster path.
+ */
+tg_status tg_gemm_unfused(int64_t M, int64_t N, int64_t K, tg_dtype dtype,
+                          const void *A, const void *B, const void *bias, tg_epilogue epilogue,
+                          void *C, void *stream);
+
 /* Static, human-readable name of a status code ("TG_OK", ...). */
 const char *tg_status_string(tg_status status);
 

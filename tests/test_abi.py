@@ -138,6 +138,36 @@ def test_explicit_path_requirements(lib):
         == tg.TG_ERR_UNSUPPORTED
 
 
+def ew(op=tg.TG_EW_BIAS_ADD, M=4, N=8, dtype=I.F16, bias=PBIAS, X=PA, Y=PC):
+    return tg.tg_elementwise(op, M, N, dtype, bias, X, Y, None)
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(M=-1), tg.TG_ERR_INVALID_ARG),
+    (dict(N=-1), tg.TG_ERR_INVALID_ARG),
+    (dict(op=2), tg.TG_ERR_INVALID_ARG),
+    (dict(dtype=2), tg.TG_ERR_INVALID_ARG),
+    (dict(bias=None), tg.TG_ERR_INVALID_ARG),                              # add without bias
+    (dict(op=tg.TG_EW_GELU_TANH), tg.TG_ERR_INVALID_ARG),                  # GELU with a bias
+    (dict(X=None), tg.TG_ERR_INVALID_ARG),
+    (dict(Y=None), tg.TG_ERR_INVALID_ARG),
+    (dict(Y=PA + 2), tg.TG_ERR_INVALID_ARG),                                # Y overlaps X, not in place
+    (dict(Y=PBIAS + 4), tg.TG_ERR_INVALID_ARG),                             # Y overlaps bias
+    (dict(M=1 << 16, N=1 << 15), tg.TG_ERR_UNSUPPORTED),                    # 2^31 elements
+    (dict(M=0), tg.TG_OK),                                                  # nothing to do
+    (dict(N=0, op=tg.TG_EW_GELU_TANH, bias=None), tg.TG_OK),
+])
+def test_elementwise_argument_checks(lib, args, status):
+    assert ew(**args) == status
+
+
+def test_unfused_checks_arguments_like_tg_gemm(lib):
+    assert tg.tg_gemm_unfused(4, 4, 4, I.F16, PA, PB, None, I.EPI_BIAS, PC, None) == tg.TG_ERR_INVALID_ARG
+    assert tg.tg_gemm_unfused(4, 4, 4, I.F16, PA, PB, PBIAS, I.EPI_NONE, PC, None) == tg.TG_ERR_INVALID_ARG
+    assert tg.tg_gemm_unfused(4, 4, 4, I.F16, PA, PB, None, I.EPI_NONE, PA, None) == tg.TG_ERR_INVALID_ARG
+    assert tg.tg_gemm_unfused(0, 4, 4, I.F16, None, None, PBIAS, I.EPI_BIAS, None, None) == tg.TG_OK
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(tg, "_lib", None)
     monkeypatch.setattr(tg, "LIBRARY", str(tmp_path / "missing.so"))

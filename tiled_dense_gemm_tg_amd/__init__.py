@@ -32,7 +32,11 @@ TG_PATH_NONE = 4
 PATH_NAMES = {TG_PATH_AUTO: "auto", TG_PATH_TILED: "tiled", TG_PATH_TILED_GENERIC: "tiled_generic",
               TG_PATH_SKINNY: "skinny", TG_PATH_NONE: "none"}
 
-EXPORTED = ("tg_gemm", "tg_gemm_path", "tg_gemm_plan", "tg_status_string", "tg_version")
+TG_EW_BIAS_ADD = 0
+TG_EW_GELU_TANH = 1
+
+EXPORTED = ("tg_gemm", "tg_gemm_path", "tg_gemm_plan", "tg_elementwise", "tg_gemm_unfused", "tg_status_string",
+            "tg_version")
 
 _lib = None
 
@@ -63,6 +67,10 @@ def load_library():
     lib.tg_gemm_path.restype = ci
     lib.tg_gemm_plan.argtypes = [i64, i64, i64, ci, vp, vp, vp, ci, vp, ctypes.POINTER(ci)]
     lib.tg_gemm_plan.restype = ci
+    lib.tg_elementwise.argtypes = [ci, i64, i64, ci, vp, vp, vp, vp]
+    lib.tg_elementwise.restype = ci
+    lib.tg_gemm_unfused.argtypes = [i64, i64, i64, ci, vp, vp, vp, ci, vp, vp]
+    lib.tg_gemm_unfused.restype = ci
     lib.tg_status_string.argtypes = [ci]
     lib.tg_status_string.restype = ctypes.c_char_p
     lib.tg_version.argtypes = []
@@ -87,6 +95,14 @@ def tg_gemm_plan(M, N, K, dtype, A, B, bias, epilogue, C):
     return st, out.value
 
 
+def tg_elementwise(op, M, N, dtype, bias, X, Y, stream) -> int:
+    return load_library().tg_elementwise(op, M, N, dtype, bias, X, Y, stream)
+
+
+def tg_gemm_unfused(M, N, K, dtype, A, B, bias, epilogue, C, stream) -> int:
+    return load_library().tg_gemm_unfused(M, N, K, dtype, A, B, bias, epilogue, C, stream)
+
+
 def tg_status_string(status: int) -> str:
     return load_library().tg_status_string(status).decode()
 
@@ -98,11 +114,14 @@ def tg_version() -> str:
 _EPI = {"none": EPI_NONE, "bias": EPI_BIAS, "bias_gelu_tanh": EPI_BIAS_GELU_TANH, "gelu": EPI_BIAS_GELU_TANH}
 
 
-def gemm(A, B, bias=None, epilogue: str = "none", out=None, path: int = TG_PATH_AUTO, stream=None):
+def gemm(A, B, bias=None, epilogue: str = "none", out=None, path: int = TG_PATH_AUTO, stream=None,
+         unfused: bool = False):
     """epilogue(A @ B [+ bias]) on torch device tensors (fp16 or bf16, row-major).
 
     Returns ``out`` (allocated when not given).  Runs on ``stream`` or torch's
-    current stream; asynchronous like any torch op.
+    current stream; asynchronous like any torch op.  ``unfused=True`` calls
+    tg_gemm_unfused (the product, then the epilogue steps as separate passes;
+    ``path`` must then be TG_PATH_AUTO).
     """
     import torch
     if A.dtype not in (torch.float16, torch.bfloat16):
@@ -127,8 +146,46 @@ def gemm(A, B, bias=None, epilogue: str = "none", out=None, path: int = TG_PATH_
         raise ValueError("out has the wrong shape or dtype")
     dtype = F16 if A.dtype == torch.float16 else BF16
     s = (stream if stream is not None else torch.cuda.current_stream(A.device)).cuda_stream
-    st = tg_gemm_path(path, M, N, K, dtype, A.data_ptr(), B.data_ptr(),
-                      bias.data_ptr() if bias is not None else None, epi, out.data_ptr(), s)
+    if unfused:
+        if path != TG_PATH_AUTO:
+            raise ValueError("the unfused form chooses its own kernel family")
+        st = tg_gemm_unfused(M, N, K, dtype, A.data_ptr(), B.data_ptr(),
+                             bias.data_ptr() if bias is not None else None, epi, out.data_ptr(), s)
+    else:
+        st = tg_gemm_path(path, M, N, K, dtype, A.data_ptr(), B.data_ptr(),
+                          bias.data_ptr() if bias is not None else None, epi, out.data_ptr(), s)
     if st != TG_OK:
-        raise TgError(st, "tg_gemm")
+        raise TgError(st, "tg_gemm_unfused" if unfused else "tg_gemm")
+    return out
+
+
+_EW = {"bias_add": TG_EW_BIAS_ADD, "gelu_tanh": TG_EW_GELU_TANH}
+
+
+def elementwise(op: str, X, bias=None, out=None, stream=None):
+    """One elementwise epilogue step over a 2-D torch device tensor: ``op`` is
+    "bias_add" (X + bias[n], bias of N entries) or "gelu_tanh".  ``out`` may
+    be X itself (in place); allocated when not given."""
+    import torch
+    if X.dtype not in (torch.float16, torch.bfloat16) or X.dim() != 2:
+        raise TypeError("X must be a 2-D float16 or bfloat16 tensor")
+    ew = _EW[op]
+    if (ew == TG_EW_BIAS_ADD) != (bias is not None):
+        raise ValueError("bias must be given exactly for bias_add")
+    M, N = X.shape
+    if bias is not None and (bias.numel() != N or bias.dtype != X.dtype):
+        raise ValueError("bias must have N entries of X's dtype")
+    if out is None:
+        out = torch.empty_like(X)
+    elif out.shape != X.shape or out.dtype != X.dtype:
+        raise ValueError("out has the wrong shape or dtype")
+    for name, t in (("X", X), ("bias", bias), ("out", out)):
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    dtype = F16 if X.dtype == torch.float16 else BF16
+    s = (stream if stream is not None else torch.cuda.current_stream(X.device)).cuda_stream
+    st = tg_elementwise(ew, M, N, dtype, bias.data_ptr() if bias is not None else None, X.data_ptr(),
+                        out.data_ptr(), s)
+    if st != TG_OK:
+        raise TgError(st, "tg_elementwise")
     return out

@@ -165,6 +165,47 @@ TG_EXPORT tg_status tg_gemm(int64_t M, int64_t N, int64_t K, tg_dtype dtype, con
     return tg_gemm_path(TG_PATH_AUTO, M, N, K, dtype, A, B, bias, epilogue, C, stream);
 }
 
+TG_EXPORT tg_status tg_elementwise(tg_elementwise_op op, int64_t M, int64_t N, tg_dtype dtype, const void *bias,
+                                   const void *X, void *Y, void *stream) {
+    if (M < 0 || N < 0)
+        return TG_ERR_INVALID_ARG;
+    if (dtype != TG_F16 && dtype != TG_BF16)
+        return TG_ERR_INVALID_ARG;
+    if (op != TG_EW_BIAS_ADD && op != TG_EW_GELU_TANH)
+        return TG_ERR_INVALID_ARG;
+    if ((op == TG_EW_BIAS_ADD) != (bias != nullptr))
+        return TG_ERR_INVALID_ARG;
+    if (M == 0 || N == 0)
+        return TG_OK;
+    if (X == nullptr || Y == nullptr)
+        return TG_ERR_INVALID_ARG;
+    const int64_t n = elements(M, N);
+    const int64_t ybytes = 2 * (n < 0 ? kMaxElements : n);
+    if ((X != Y && overlaps(Y, ybytes, X, ybytes)) || overlaps(Y, ybytes, bias, 2 * N))
+        return TG_ERR_INVALID_ARG;
+    if (n < 0)
+        return TG_ERR_UNSUPPORTED;
+    const bool vec = N % 8 == 0 && aligned(X, 16) && aligned(Y, 16) && (bias == nullptr || aligned(bias, 16));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t e = tg::launch_elementwise(dtype, op, M, static_cast<int>(N), static_cast<const uint16_t *>(bias),
+                                                static_cast<const uint16_t *>(X), static_cast<uint16_t *>(Y), vec,
+                                                num_cu_of(s), s);
+    return e == hipSuccess ? TG_OK : TG_ERR_LAUNCH;
+}
+
+TG_EXPORT tg_status tg_gemm_unfused(int64_t M, int64_t N, int64_t K, tg_dtype dtype, const void *A, const void *B,
+                                    const void *bias, tg_epilogue epilogue, void *C, void *stream) {
+    const Checked c = check_args(M, N, K, dtype, A, B, bias, epilogue, C);
+    if (c.status != TG_OK || c.noop)
+        return c.status;
+    tg_status st = tg_gemm_path(TG_PATH_AUTO, M, N, K, dtype, A, B, nullptr, TG_EPI_NONE, C, stream);
+    if (st == TG_OK && epilogue != TG_EPI_NONE)
+        st = tg_elementwise(TG_EW_BIAS_ADD, M, N, dtype, bias, C, C, stream);
+    if (st == TG_OK && epilogue == TG_EPI_BIAS_GELU_TANH)
+        st = tg_elementwise(TG_EW_GELU_TANH, M, N, dtype, nullptr, C, C, stream);
+    return st;
+}
+
 TG_EXPORT const char *tg_status_string(tg_status status) {
     switch (status) {
     case TG_OK: return "TG_OK";

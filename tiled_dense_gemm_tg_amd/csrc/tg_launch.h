@@ -30,4 +30,11 @@ hipError_t launch_tiled_generic(int dtype, int epi, const GemmArgs &a, hipStream
 // M <= 16, K % 8 == 0, N % 4 == 0, aligned operands.
 hipError_t launch_skinny(int dtype, int epi, const GemmArgs &a, hipStream_t stream);
 
+// Elementwise passes over an M x N matrix: Y = X + bias[n] or Y = GELU_tanh(X)
+// (Y may be X).  vec: N % 8 == 0 and X, Y (and bias for the add) 16-byte
+// aligned.  At most 8 workgroups per CU (num_cu <= 0: 256 CUs assumed).
+enum EwOp { EW_BIAS_ADD = 0, EW_GELU_TANH = 1 };
+hipError_t launch_elementwise(int dtype, int op, int64_t M, int N, const uint16_t *bias, const uint16_t *X,
+                              uint16_t *Y, bool vec, int num_cu, hipStream_t stream);
+
 }  // namespace tg
