@@ -137,6 +137,14 @@ def time_gemm(torch, tg, w, sets, steps, warmup, unfused=False):
     return ev0.elapsed_time(ev1) / steps, wall
 
 
+def path_of(tg, w, operand_set):
+    """Name of the kernel family tg_gemm picks for these operands."""
+    A, B, bias, C = operand_set
+    st, path = tg.tg_gemm_plan(w.M, w.N, w.K, w.dtype, A.data_ptr(), B.data_ptr(),
+                               bias.data_ptr() if bias is not None else None, w.epilogue, C.data_ptr())
+    return tg.PATH_NAMES.get(path, "?") if st == tg.TG_OK else "error"
+
+
 def device_operands(torch, I, w, copies=1):
     ops = I.make_operands(w)
     tdt = torch.float16 if w.dtype == I.F16 else torch.bfloat16
@@ -277,7 +285,7 @@ def main() -> int:
         ms2, _ = time_gemm(torch, tg, w2, sets2, max(args.steps, 50), args.warmup)
         t2 = gemm_flops(w2.M, w2.N, w2.K) / (ms2 * 1e-3) / 1e12
         sec[w2.name] = {"us_per_launch": round(ms2 * 1e3, 2), "TFLOP/s": round(t2, 2),
-                        "frac_mfma_peak": round(t2 / PEAK_MFMA_F16_TFLOPS, 4), "path": "tiled",
+                        "frac_mfma_peak": round(t2 / PEAK_MFMA_F16_TFLOPS, 4), "path": path_of(tg, w2, sets2[0]),
                         "traffic": measured_traffic(w2.name)}
         del sets2
         torch.cuda.empty_cache()
@@ -292,7 +300,7 @@ def main() -> int:
                         "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
                         "hot_cache_GB/s_not_the_metric": round(nbytes / (hot * 1e-3) / 1e9, 1),
                         "TFLOP/s": round(gemm_flops(w4.M, w4.N, w4.K) / (ms4 * 1e-3) / 1e12, 2),
-                        "path": "skinny", "traffic": measured_traffic(w4.name)}
+                        "path": path_of(tg, w4, sets4[0]), "traffic": measured_traffic(w4.name)}
         log(f"{w4.name}: {ms4 * 1e3:.2f} us, {gbps:.0f} GB/s")
         del sets4
         torch.cuda.empty_cache()
@@ -302,7 +310,7 @@ def main() -> int:
         ms3, _ = time_gemm(torch, tg, w3, sets3, max(args.steps // 2, 20), args.warmup)
         t3 = gemm_flops(w3.M, w3.N, w3.K) / (ms3 * 1e-3) / 1e12
         sec[w3.name] = {"us_per_launch": round(ms3 * 1e3, 2), "TFLOP/s": round(t3, 2),
-                        "frac_mfma_peak": round(t3 / PEAK_MFMA_F16_TFLOPS, 4), "path": "tiled_generic",
+                        "frac_mfma_peak": round(t3 / PEAK_MFMA_F16_TFLOPS, 4), "path": path_of(tg, w3, sets3[0]),
                         "traffic": measured_traffic(w3.name)}
         log(f"{w3.name}: unfused")
         ms3u, _ = time_gemm(torch, tg, w3, sets3, max(args.steps // 2, 20), args.warmup, unfused=True)

@@ -78,14 +78,18 @@ typedef enum {
  *   TG_PATH_SKINNY         M <= 16 (the decode-shaped product): streams B from
  *                          HBM once; needs K % 8 == 0, N % 4 == 0, A 16-byte
  *                          aligned, B, C and bias 8-byte aligned.
- *   TG_PATH_TILED          256x256 MFMA tiles staged through LDS with
- *                          16-byte loads; needs K % 8 == 0, N % 8 == 0, A, B
- *                          and C 16-byte aligned, bias 8-byte aligned, and A
- *                          and B, each padded to whole tiles, below 2 GiB
+ *   TG_PATH_TILED          256x256 MFMA tiles staged through LDS by 16-byte
+ *                          direct loads; any shape and alignment as long as A
+ *                          and B, each padded to whole tiles, stay below 2 GiB
  *                          less 64 KiB: 2 (M + 256) K and 2 (K + 32) (N + 256)
- *                          both below 2^31 - 65536.
- *   TG_PATH_TILED_GENERIC  the same tiling with element-granular loads and
- *                          stores: any shape, any alignment.
+ *                          both below 2^31 - 65536.  Fastest with K % 8 == 0,
+ *                          N % 8 == 0, A, B, C 16-byte and bias 8-byte
+ *                          aligned.
+ *   TG_PATH_TILED_GENERIC  the same tiling with loads gathered through
+ *                          registers and element-granular stores: any shape
+ *                          and alignment up to the per-operand limit; chosen
+ *                          automatically only for operands too large for
+ *                          TG_PATH_TILED.
  *   TG_PATH_NONE           (reported by tg_gemm_plan only) nothing to launch.
  */
 typedef enum {

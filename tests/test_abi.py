@@ -111,30 +111,34 @@ def test_empty_K_allows_null_operands(lib):
     (1, 4, 8, {}, tg.TG_PATH_SKINNY),
     (16, 12, 8, {}, tg.TG_PATH_SKINNY),                 # N % 4 == 0 is enough
     (17, 11008, 4096, {}, tg.TG_PATH_TILED),
-    (16, 11008, 4100, {}, tg.TG_PATH_TILED_GENERIC),    # K % 8 != 0
-    (16, 11010, 4096, {}, tg.TG_PATH_TILED_GENERIC),    # N % 4 != 0
-    (16, 11008, 4096, {"A": PA + 8}, tg.TG_PATH_TILED_GENERIC),
+    (16, 11008, 4100, {}, tg.TG_PATH_TILED),            # K % 8 != 0: not skinny, tiled takes any shape
+    (16, 11010, 4096, {}, tg.TG_PATH_TILED),            # N % 4 != 0
+    (16, 11008, 4096, {"A": PA + 8}, tg.TG_PATH_TILED),
     (4096, 4096, 4096, {}, tg.TG_PATH_TILED),
     (8192, 8192, 8192, {"bias": PBIAS, "epi": I.EPI_BIAS_GELU_TANH}, tg.TG_PATH_TILED),
-    (4000, 4093, 4111, {"bias": PBIAS, "epi": I.EPI_BIAS_GELU_TANH, "dtype": I.BF16}, tg.TG_PATH_TILED_GENERIC),
+    (4000, 4093, 4111, {"bias": PBIAS, "epi": I.EPI_BIAS_GELU_TANH, "dtype": I.BF16}, tg.TG_PATH_TILED),
     (4000, 4096, 4104, {}, tg.TG_PATH_TILED),           # ragged M is fine for the vector path
     (130808, 256, 8192, {}, tg.TG_PATH_TILED),          # 2 (M + 256) K just below 2^31 - 64 Ki
     (130812, 256, 8192, {}, tg.TG_PATH_TILED_GENERIC),  # ... and at it
     (256, 130296, 8192, {}, tg.TG_PATH_TILED),          # 2 (K + 32) (N + 256) just below
     (256, 130304, 8192, {}, tg.TG_PATH_TILED_GENERIC),
-    (256, 256, 256, {"C": PC + 8}, tg.TG_PATH_TILED_GENERIC),
-    (256, 256, 256, {"B": PB + 2}, tg.TG_PATH_TILED_GENERIC),
-    (256, 256, 256, {"bias": PBIAS + 2, "epi": I.EPI_BIAS}, tg.TG_PATH_TILED_GENERIC),
+    (256, 256, 256, {"C": PC + 8}, tg.TG_PATH_TILED),
+    (256, 256, 256, {"B": PB + 2}, tg.TG_PATH_TILED),
+    (256, 256, 256, {"bias": PBIAS + 2, "epi": I.EPI_BIAS}, tg.TG_PATH_TILED),
+    (256, 257, 255, {"A": PA + 2, "C": PC + 6}, tg.TG_PATH_TILED),
 ])
 def test_kernel_family_choice(lib, M, N, K, ptrs, path):
     assert plan(M, N, K, **ptrs) == (tg.TG_OK, path)
 
 
 def test_explicit_path_requirements(lib):
-    # the skinny family needs M <= 16; the vector tiled family needs K % 8 == 0
+    # the skinny family needs M <= 16, K % 8 == 0, N % 4 == 0 and alignment;
+    # the tiled family needs operands below its size limit
     assert tg.tg_gemm_path(tg.TG_PATH_SKINNY, 17, 64, 64, I.F16, PA, PB, None, 0, PC, None) == tg.TG_ERR_UNSUPPORTED
-    assert tg.tg_gemm_path(tg.TG_PATH_TILED, 64, 64, 60, I.F16, PA, PB, None, 0, PC, None) == tg.TG_ERR_UNSUPPORTED
-    assert tg.tg_gemm_path(tg.TG_PATH_TILED, 64, 64, 64, I.F16, PA + 4, PB, None, 0, PC, None) \
+    assert tg.tg_gemm_path(tg.TG_PATH_SKINNY, 16, 64, 60, I.F16, PA, PB, None, 0, PC, None) == tg.TG_ERR_UNSUPPORTED
+    assert tg.tg_gemm_path(tg.TG_PATH_SKINNY, 16, 64, 64, I.F16, PA + 4, PB, None, 0, PC, None) \
+        == tg.TG_ERR_UNSUPPORTED
+    assert tg.tg_gemm_path(tg.TG_PATH_TILED, 130812, 256, 8192, I.F16, PA, PB, None, 0, PC, None) \
         == tg.TG_ERR_UNSUPPORTED
 
 

@@ -26,7 +26,7 @@ pytestmark = pytest.mark.gpu
 EXPECTED_PATH = {
     "gemm_f16_256x256x256": tg.TG_PATH_TILED,
     "gemm_f16_4096x4096x4096": tg.TG_PATH_TILED,
-    "gemm_bf16_4000x4093x4111_bias_gelu_tanh": tg.TG_PATH_TILED_GENERIC,
+    "gemm_bf16_4000x4093x4111_bias_gelu_tanh": tg.TG_PATH_TILED,
     "gemm_f16_skinny_16x11008x4096": tg.TG_PATH_SKINNY,
     "gemm_f16_8192x8192x8192_bias_gelu_tanh": tg.TG_PATH_TILED,
 }
@@ -69,9 +69,7 @@ def test_workload_small_integers_bit_exact(name):
 
 
 def _families(M, N, K):
-    fams = [tg.TG_PATH_TILED_GENERIC]
-    if K % 8 == 0 and N % 8 == 0:
-        fams.append(tg.TG_PATH_TILED)
+    fams = [tg.TG_PATH_TILED_GENERIC, tg.TG_PATH_TILED]
     if M <= 16 and K % 8 == 0 and N % 4 == 0:
         fams.append(tg.TG_PATH_SKINNY)
     return fams
@@ -249,3 +247,71 @@ def test_persistent_grid_covers_every_tile(dtype, M, N, K):
     out = run(M, N, K, dtype, A, B, bias, I.EPI_BIAS, expect_path=tg.TG_PATH_TILED)
     _, refq = oracle.gemm(M, N, K, dtype, A, B, bias, I.EPI_BIAS)
     check_exact(to_bits(out), refq, f"persistent {M}x{N}x{K}")
+
+
+def _offset_tensor(bits, dtype, shape, offset):
+    """A device tensor of `shape` starting `offset` elements into its buffer."""
+    n = int(np.prod(shape))
+    flat = to_device(np.concatenate([np.zeros(offset, np.uint16), np.ascontiguousarray(bits).reshape(-1)]), dtype)
+    return flat[offset:offset + n].view(*shape)
+
+
+@pytest.mark.parametrize("dtype", [I.F16, I.BF16])
+@pytest.mark.parametrize("M,N,K,offsets", [
+    (520, 264, 328, (1, 0, 0, 0)),    # A 2-byte aligned, shapes aligned
+    (520, 264, 328, (0, 3, 0, 0)),    # B
+    (520, 264, 328, (0, 0, 1, 1)),    # C and bias
+    (300, 263, 201, (1, 1, 1, 1)),    # everything ragged and misaligned
+])
+def test_tiled_any_alignment(dtype, M, N, K, offsets):
+    """The tiled family at 2-byte-aligned operands (unaligned direct loads,
+    grouped 8-byte stores) against the oracle, bit-exact on integers."""
+    import torch
+    oa, ob, oc, obias = offsets
+    for kind in ("random", "integers"):
+        if kind == "random":
+            A = I.random_bits((M, K), ("uniform", -1.0, 1.0), dtype, 400)
+            B = I.random_bits((K, N), ("uniform", -1.0, 1.0), dtype, 401)
+            bias = I.random_bits((N,), ("uniform", -0.5, 0.5), dtype, 402)
+            epi = I.EPI_BIAS_GELU_TANH
+        else:
+            A = I.small_int_bits((M, K), dtype, 403)
+            B = I.small_int_bits((K, N), dtype, 404)
+            bias = I.small_int_bits((N,), dtype, 405)
+            epi = I.EPI_BIAS
+        ref64, refq = oracle.gemm(M, N, K, dtype, A, B, bias, epi)
+        a = _offset_tensor(A, dtype, (M, K), oa)
+        b = _offset_tensor(B, dtype, (K, N), ob)
+        bb = _offset_tensor(bias, dtype, (N,), obias)
+        c = _offset_tensor(np.full(M * N, 0x7E00, np.uint16), dtype, (M, N), oc)   # NaN-filled
+        log(f"[align] dtype={dtype} {M}x{N}x{K} offsets={offsets} {kind}")
+        st, p = tg.tg_gemm_plan(M, N, K, dtype, a.data_ptr(), b.data_ptr(), bb.data_ptr(), epi, c.data_ptr())
+        assert st == tg.TG_OK and p == tg.TG_PATH_TILED
+        tg.gemm(a, b, bb, {I.EPI_BIAS: "bias", I.EPI_BIAS_GELU_TANH: "bias_gelu_tanh"}[epi], out=c)
+        torch.cuda.synchronize()
+        if kind == "random":
+            check_tolerance(dtype, to_bits(c), ref64, f"align {offsets}")
+        else:
+            check_exact(to_bits(c), refq, f"align {offsets}")
+
+
+@pytest.mark.parametrize("path", [tg.TG_PATH_TILED, tg.TG_PATH_TILED_GENERIC])
+@pytest.mark.parametrize("K", [37, 8, 33])
+def test_k_tail_does_not_mix_rows(path, K):
+    """Rows of A alternate between finite values and +inf at k = 0.  With K
+    not a multiple of 8 the 16-byte chunk that crosses k = K of an even row
+    also covers the first elements of the odd row after it; those must not
+    enter the sum (inf * 0 would turn the even row into NaN)."""
+    M, N = 64, 72
+    dtype = I.F16
+    A = I.random_bits((M, K), ("uniform", -1.0, 1.0), dtype, 410)
+    inf = np.uint16(0x7C00)
+    A = A.reshape(M, K).copy()
+    A[1::2, 0] = inf
+    B = I.random_bits((K, N), ("uniform", 0.5, 1.0), dtype, 411)    # positive: odd rows are +inf
+    ref64, _ = oracle.gemm(M, N, K, dtype, A.reshape(-1), B)
+    log(f"[k-tail] path={tg.PATH_NAMES[path]} K={K}")
+    out = oracle.decode(dtype, to_bits(run(M, N, K, dtype, A.reshape(-1), B, path=path)))
+    assert np.isposinf(out[1::2]).all()
+    check_tolerance(dtype, to_bits(run(M, N, K, dtype, A.reshape(-1), B, path=path))[0::2], ref64[0::2],
+                    "even rows")

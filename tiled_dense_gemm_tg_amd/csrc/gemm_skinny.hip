@@ -44,7 +44,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args) {
     const uint16_t *__restrict__ B = args.B;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: loop control stays scalar
     const int p = lane & 15;
     const int h = lane >> 4;
     const int nb = blockIdx.x * SLAB;
@@ -74,19 +74,26 @@ __global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args) {
     const uint32_t a_row = 2u * (uint32_t)p * (uint32_t)K;
     const uint32_t b_col = 2u * (uint32_t)ncol;
     const uint32_t b_row = 2u * (uint32_t)N;
+    // Offsets of masked loads are OR-ed with OOB; the mask goes through an
+    // empty asm so the compiler keeps the OR instead of turning the choice
+    // into a branch around each load.
+    auto mask_of = [&](bool ok) __attribute__((always_inline)) {
+        uint32_t m = ok ? 0u : OOB;
+        asm volatile("" : "+v"(m));
+        return m;
+    };
     auto load_batch = [&](u32x2 (&vb)[UNROLL][8], u32x4 (&va)[UNROLL], int s0) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             const int kb = (s0 + u) * 32 + 8 * h;
-            const bool live = s0 + u < s_end;
-            // K % 8 == 0: the 8 k of the A chunk are all valid or none
-            const uint32_t aoff = (live && kb < K) ? a_row + 2u * (uint32_t)kb : OOB;
-            va[u] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)aoff, 0, 0);
+            // K % 8 == 0, so rows kb .. kb + 7 (and the A chunk's 8 k) are
+            // all inside [0, K) or all outside.
+            const uint32_t mk = mask_of(s0 + u < s_end && kb < K);
+            va[u] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)((a_row + 2u * (uint32_t)kb) | mk), 0, 0);
+            const uint32_t boff = (uint32_t)kb * b_row + b_col;
 #pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const uint32_t boff = (live && kb + r < K) ? (uint32_t)(kb + r) * b_row + b_col : OOB;
-                vb[u][r] = __builtin_amdgcn_raw_buffer_load_b64(rb, (int)boff, 0, 0);
-            }
+            for (int r = 0; r < 8; ++r)
+                vb[u][r] = __builtin_amdgcn_raw_buffer_load_b64(rb, (int)((boff + (uint32_t)r * b_row) | mk), 0, 0);
         }
     };
     auto mma_batch = [&](const u32x2 (&vb)[UNROLL][8], const u32x4 (&va)[UNROLL]) __attribute__((always_inline)) {
@@ -111,23 +118,23 @@ __global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args) {
             }
         }
     };
+    // Every batch's loads are issued before the previous batch is
+    // multiplied (sched_barrier keeps that order); loads past the wave's
+    // range are masked, read nothing and give zeros.
     u32x2 vb0[UNROLL][8], vb1[UNROLL][8];
     u32x4 va0[UNROLL], va1[UNROLL];
-    int s0 = s_begin;
-    if (s0 < s_end)
-        load_batch(vb0, va0, s0);
-    while (s0 < s_end) {
-        const int s1 = s0 + UNROLL;
-        if (s1 < s_end)
-            load_batch(vb1, va1, s1);
+    load_batch(vb0, va0, s_begin);
+    for (int s0 = s_begin; s0 < s_end; s0 += 2 * UNROLL) {
+        load_batch(vb1, va1, s0 + UNROLL);
+        __builtin_amdgcn_sched_barrier(0);
         mma_batch(vb0, va0);
-        if (s1 >= s_end)
+        __builtin_amdgcn_sched_barrier(0);
+        if (s0 + UNROLL >= s_end)
             break;
-        const int s2 = s1 + UNROLL;
-        if (s2 < s_end)
-            load_batch(vb0, va0, s2);
+        load_batch(vb0, va0, s0 + 2 * UNROLL);
+        __builtin_amdgcn_sched_barrier(0);
         mma_batch(vb1, va1);
-        s0 = s2;
+        __builtin_amdgcn_sched_barrier(0);
     }
 
     // acc[j][e] is D_j[row 4 h + e][col p]: C[m = p][n = nb + 16 h + 4 e + j].

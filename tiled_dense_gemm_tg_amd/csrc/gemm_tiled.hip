@@ -1,4 +1,4 @@
-// gemm_tiled.hip -- tiled MFMA GEMM for gfx950 (MI355X), vector path.
+// gemm_tiled.hip -- tiled MFMA GEMM for gfx950 (MI355X), direct-load path.
 //
 // The tiling is the one the TileLang pages teach ("TileLang: writing LLM GPU
 // kernels by thinking in tiles", section 2 and the section 3 listing; "TileLang:
@@ -40,6 +40,10 @@
 // awaited with explicit vmcnt waits: the compiler cannot tell that the LDS
 // they write is not the LDS being read, and would otherwise wait for every
 // load in flight before each use of LDS data.
+//
+// Rows need not be 16-byte aligned: the direct loads take 2-byte-aligned
+// addresses, and the few chunks that then hold wrong data in the last
+// k-slice are rewritten before use (fix_last_slice below).
 //
 // Loads are range-checked buffer loads over each operand's exact byte range;
 // an out-of-range lane writes zeros.  k >= K is pushed out of range (offset +
@@ -289,7 +293,56 @@ __device__ __forceinline__ void kstep(const Frag &cur, Frag &nxt, f32x16 (&acc)[
 // computes tiles g, g + G, g + 2G, ... (G = grid size, a multiple of the 8
 // XCDs when the tile count allows, so every tile of a workgroup stays on its
 // XCD in the raster), which removes the dispatch gap between tiles.
-template <class T, int EPI>
+// Shapes with K % 8 != 0 or N % 8 != 0 (GEN): the direct loads still move
+// 16 bytes per lane, now at 2-byte-aligned addresses, which the hardware
+// takes.  Two kinds of chunk in the last k-slice then hold wrong data:
+//   * the chunk of each A row that crosses k = K carries the next row's first
+//     elements (not zeros) past K, and for the last row of A it crosses the
+//     end of the buffer, so the range check zeroes it whole;
+//   * the chunk of B's last row that crosses n = N crosses the end of the
+//     buffer and is zeroed whole.
+// fix_last_slice() rewrites exactly those chunks in LDS from element loads
+// (past K or N the loads are out of range and read zero), after the slice's
+// direct loads have landed and before the barrier that publishes it.  Each
+// chunk is rewritten by a lane of the wave whose direct load wrote it, so
+// that wave's own wait orders the two writes.  Chunks of B rows crossing
+// n = N elsewhere only feed columns that are never stored.
+template <class T>
+__device__ __forceinline__ void fix_last_slice(const GemmArgs &g, int m0, int n0, int kl, uint32_t stage) {
+    const int k0 = kl * BK;
+    const int tid = threadIdx.x;
+    if (g.K % 8 != 0) {
+        const __amdgpu_buffer_rsrc_t ra = tile::buffer_of(g.A, 2u * (uint32_t)g.M * (uint32_t)g.K);
+        const int r = tid;                       // tile row r was loaded by wave r / 64 = this wave
+        const int cp = (g.K - k0) >> 3;          // the crossing chunk (< 4: the slice holds K - 1)
+        const int v = (g.K - k0) & 7;            // its elements below K
+        const uint32_t row = (uint32_t)(m0 + r); // rows >= M read zero (beyond the buffer)
+        const uint32_t base = 2u * (row * (uint32_t)g.K + (uint32_t)(k0 + 8 * cp));
+        uint16_t e[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            e[q] = q < v ? __builtin_amdgcn_raw_buffer_load_b16(ra, (int)(base + 2u * q), 0, 0) : (uint16_t)0;
+        const u32x4 chunk = {pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]), pack2(e[6], e[7])};
+        *(__attribute__((address_space(3))) u32x4 *)(uintptr_t)(stage + 64u * r + 16u * (cp ^ a_swz(r))) = chunk;
+    }
+    if (g.N % 8 != 0 && n0 <= g.N - 1 && g.N - 1 < n0 + BN) {
+        const int r = g.K - 1 - k0;              // B's last row, loaded by wave r / 8
+        if (tid == 64 * (r >> 3)) {
+            const __amdgpu_buffer_rsrc_t rb = tile::buffer_of(g.B, 2u * (uint32_t)g.K * (uint32_t)g.N);
+            const int c = (g.N - 1 - n0) >> 3;
+            const uint32_t base = 2u * ((uint32_t)(g.K - 1) * (uint32_t)g.N + (uint32_t)(n0 + 8 * c));
+            uint16_t e[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                e[q] = __builtin_amdgcn_raw_buffer_load_b16(rb, (int)(base + 2u * q), 0, 0);
+            const u32x4 chunk = {pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]), pack2(e[6], e[7])};
+            *(__attribute__((address_space(3))) u32x4 *)(uintptr_t)(stage + (uint32_t)A_BYTES + 512u * r +
+                                                                    16u * (c ^ b_swz(r))) = chunk;
+        }
+    }
+}
+
+template <class T, int EPI, bool GEN>
 __global__ __launch_bounds__(NTHREADS) void gemm_tiled_kernel(GemmArgs args) {
     __shared__ __attribute__((aligned(16))) u32x4 smem[STAGES * STAGE_BYTES / 16];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -334,6 +387,8 @@ __global__ __launch_bounds__(NTHREADS) void gemm_tiled_kernel(GemmArgs args) {
                 wait_vmcnt<8>();
             } else {
                 wait_vmcnt<0>();
+                if constexpr (GEN)
+                    fix_last_slice<T>(args, m0, n0, 0, stage(0));
             }
         }
         __syncthreads();
@@ -371,6 +426,9 @@ __global__ __launch_bounds__(NTHREADS) void gemm_tiled_kernel(GemmArgs args) {
             kstep<T, true, ISSUE>(f0, f1, acc, fad, st, 1, dma_lo);
             if constexpr (NEXT) {
                 wait_vmcnt<decltype(wait)::value>();
+                // with nothing left in flight, slice t + 1 is the last one
+                if constexpr (GEN && decltype(wait)::value == 0)
+                    fix_last_slice<T>(args, m0, n0, t + 1, stage((t + 1) & 3));
                 __syncthreads();
             }
             kstep<T, NEXT, ISSUE>(f1, f0, acc, fad, stage((t + 1) & 3), 0, dma_hi);
@@ -401,37 +459,41 @@ __global__ __launch_bounds__(NTHREADS) void gemm_tiled_kernel(GemmArgs args) {
         if (t + 1 == nk)
             slice(t, none{}, w0{}, no{});
 
-        tile::store_tile<T, EPI, true>(args, acc, m0, n0, wm, wn, lane);
+        tile::store_tile<T, EPI, GEN ? tile::STORE_GROUP : tile::STORE_VEC>(args, acc, m0, n0, wm, wn, lane);
         // every wave is done reading LDS before the next tile's loads land
         __syncthreads();
     }
 }
 
 template <class T, int EPI>
-hipError_t launch_typed(const GemmArgs &a, int grid, hipStream_t stream) {
-    hipLaunchKernelGGL((gemm_tiled_kernel<T, EPI>), dim3(grid), dim3(NTHREADS), 0, stream, a);
+hipError_t launch_typed(const GemmArgs &a, bool gen, int grid, hipStream_t stream) {
+    if (gen)
+        hipLaunchKernelGGL((gemm_tiled_kernel<T, EPI, true>), dim3(grid), dim3(NTHREADS), 0, stream, a);
+    else
+        hipLaunchKernelGGL((gemm_tiled_kernel<T, EPI, false>), dim3(grid), dim3(NTHREADS), 0, stream, a);
     return hipGetLastError();
 }
 
 template <class T>
-hipError_t launch_epi(int epi, const GemmArgs &a, int grid, hipStream_t stream) {
+hipError_t launch_epi(int epi, const GemmArgs &a, bool gen, int grid, hipStream_t stream) {
     switch (epi) {
-    case EPI_NONE: return launch_typed<T, EPI_NONE>(a, grid, stream);
-    case EPI_BIAS: return launch_typed<T, EPI_BIAS>(a, grid, stream);
-    default: return launch_typed<T, EPI_BIAS_GELU_TANH>(a, grid, stream);
+    case EPI_NONE: return launch_typed<T, EPI_NONE>(a, gen, grid, stream);
+    case EPI_BIAS: return launch_typed<T, EPI_BIAS>(a, gen, grid, stream);
+    default: return launch_typed<T, EPI_BIAS_GELU_TANH>(a, gen, grid, stream);
     }
 }
 
 }  // namespace
 
-hipError_t launch_tiled_vec(int dtype, int epi, const GemmArgs &a, int num_cu, hipStream_t stream) {
+hipError_t launch_tiled_vec(int dtype, int epi, const GemmArgs &a, bool aligned, int num_cu, hipStream_t stream) {
     const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
     int grid = tiles;
     if (num_cu > 0 && tiles > num_cu) {
         // one workgroup per CU, rounded down to a multiple of the XCD count
         grid = num_cu >= tile::NUM_XCD ? num_cu - num_cu % tile::NUM_XCD : num_cu;
     }
-    return dtype == 0 ? launch_epi<F16>(epi, a, grid, stream) : launch_epi<BF16>(epi, a, grid, stream);
+    return dtype == 0 ? launch_epi<F16>(epi, a, !aligned, grid, stream)
+                      : launch_epi<BF16>(epi, a, !aligned, grid, stream);
 }
 
 }  // namespace tg

@@ -1,5 +1,6 @@
 // gemm_tiled_generic.hip -- the 256 x 256 tiled MFMA GEMM for any shape and
-// any alignment (gfx950).
+// any alignment (gfx950), for operands beyond the direct-load kernel's size
+// limit (2 GiB per padded operand), up to 2^31 - 64 elements.
 //
 // Same tiling as the vector kernel (gemm_tiled.hip) and the same fragment
 // layout and epilogue, but rows of A and B may start at any 2-byte boundary
@@ -45,27 +46,51 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t dword_buffer(const void *p, ui
     return tile::buffer_of((const char *)p - adj, bytes + adj);
 }
 
-// 8 consecutive 16-bit elements at byte offset `ob` (2-byte aligned) of a
-// buffer of `limit` bytes: the 16 bytes at the enclosing dword-aligned offset
-// plus the next dword, shifted down by 0 or 2 bytes (v_alignbyte_b32).  A
-// 16-byte load that crosses the end of the buffer reads as all zeros, so a
-// chunk whose bytes straddle the end (only the last chunks of an operand) is
-// fetched element by element instead.  With ob = OOB_G everything reads 0.
-__device__ __forceinline__ u32x4 load8(__amdgpu_buffer_rsrc_t r, uint32_t ob, uint32_t limit) {
-    const uint32_t o4 = ob & ~3u;
-    const uint32_t sh = ob & 2u;
-    if (o4 >= limit || o4 + 16u + 2u * sh <= limit) {
-        const u32x4 d = __builtin_amdgcn_raw_buffer_load_b128(r, (int)o4, 0, 0);
-        const uint32_t e = __builtin_amdgcn_raw_buffer_load_b32(r, (int)(o4 + 16u), 0, 0);
+// One chunk = 8 consecutive 16-bit elements at byte offset `ob` (2-byte
+// aligned) of a buffer of `limit` bytes, fetched as the 16 bytes at the
+// enclosing dword-aligned offset o4 plus the next dword, shifted down by
+// sh = 0 or 2 bytes (v_alignbyte_b32).  A 16-byte load that crosses the end of
+// the buffer reads as all zeros, so a chunk whose bytes straddle the end
+// (only the last chunks of an operand) is fetched element by element instead.
+// The loads of all chunks are issued before any result is used, so they are
+// all in flight together: issue() for every chunk, then fix() (the rare
+// straddling chunks), then value().
+struct Chunk {
+    u32x4 d;
+    uint32_t e;
+    uint32_t ob, sh;
+    bool straddle;
+
+    __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t limit) {
+        ob = off;
+        const uint32_t o4 = off & ~3u;
+        sh = off & 2u;
+        straddle = o4 < limit && o4 + 16u + 2u * sh > limit;
+        // straddling chunks skip the vector loads (offset pushed out of
+        // range); the empty asm keeps the choice an OR instead of a branch
+        uint32_t m = straddle ? OOB_G : 0u;
+        asm volatile("" : "+v"(m));
+        d = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(o4 | m), 0, 0);
+        e = __builtin_amdgcn_raw_buffer_load_b32(r, (int)((o4 + 16u) | m), 0, 0);
+    }
+
+    __device__ __forceinline__ void fix(__amdgpu_buffer_rsrc_t r) {
+        if (straddle) {
+            uint16_t v[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                v[q] = __builtin_amdgcn_raw_buffer_load_b16(r, (int)(ob + 2u * q), 0, 0);
+            d = u32x4{pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])};
+            e = 0u;
+            sh = 0u;
+        }
+    }
+
+    __device__ __forceinline__ u32x4 value() const {
         return u32x4{__builtin_amdgcn_alignbyte(d.y, d.x, sh), __builtin_amdgcn_alignbyte(d.z, d.y, sh),
                      __builtin_amdgcn_alignbyte(d.w, d.z, sh), __builtin_amdgcn_alignbyte(e, d.w, sh)};
     }
-    uint16_t v[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q)
-        v[q] = __builtin_amdgcn_raw_buffer_load_b16(r, (int)(ob + 2u * q), 0, 0);
-    return u32x4{pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])};
-}
+};
 
 // Thread t gathers A chunk c = t % 8 (8 k) of rows t/8 + 32 i (i = 0..7) and
 // B rows 8 (t%8) + r (r = 0..7) of the 8 columns 8 (t/8) ...  Elements k >= K
@@ -94,20 +119,33 @@ struct Gather {
     __device__ __forceinline__ void load(u32x4 (&xa)[8], u32x4 (&xb)[8], int k0) const {
         // number of this thread's 8 A elements with k < K (same for all rows)
         const int nv = K - (k0 + kq);
+        Chunk ca[8], cb[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t off = (nv > 0) ? a_row_off + (uint32_t)i * a_row_step + 2u * (uint32_t)k0 : OOB_G;
+            ca[i].issue(ra, off, a_limit);
+        }
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const uint32_t off = (k0 + kq + r < K) ? b_col_off + (uint32_t)(k0 + r) * b_row : OOB_G;
+            cb[r].issue(rb, off, b_limit);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            ca[i].fix(ra);
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+            cb[r].fix(rb);
         u32x4 amask;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             amask[i] = (2 * i + 1 < nv) ? 0xFFFFFFFFu : ((2 * i < nv) ? 0x0000FFFFu : 0u);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t off = (nv > 0) ? a_row_off + (uint32_t)i * a_row_step + 2u * (uint32_t)k0 : OOB_G;
-            xa[i] = load8(ra, off, a_limit) & amask;
-        }
+        for (int i = 0; i < 8; ++i)
+            xa[i] = ca[i].value() & amask;
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const uint32_t off = (k0 + kq + r < K) ? b_col_off + (uint32_t)(k0 + r) * b_row : OOB_G;
-            xb[r] = load8(rb, off, b_limit);
-        }
+        for (int r = 0; r < 8; ++r)
+            xb[r] = cb[r].value();
     }
 };
 
@@ -206,7 +244,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_tiled_generic_kernel(GemmArgs a
         }
         __syncthreads();
     }
-    tile::store_tile<T, EPI, false>(args, acc, m0, n0, wm, wn, lane);
+    tile::store_tile<T, EPI, tile::STORE_ELEM>(args, acc, m0, n0, wm, wn, lane);
 }
 
 template <class T, int EPI>

@@ -75,15 +75,20 @@ bool skinny_ok(int64_t M, int64_t N, int64_t K, const void *A, const void *B, co
            aligned(bias, 8);
 }
 
-// The vector tiled kernel addresses A and B through buffers that start 4 KiB
-// before each operand and masks loads by adding 2^31 to their byte offsets,
-// also for rows and k-rows of the padding past the operand's end; all such
-// offsets must stay below 2^32, so each operand, padded to whole tiles, stays
-// below 2 GiB less 64 KiB.
-bool tiled_ok(int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *bias, const void *C) {
+// The tiled kernel addresses A and B through buffers that start 4 KiB before
+// each operand and masks loads by adding 2^31 to their byte offsets, also for
+// rows and k-rows of the padding past the operand's end; all such offsets
+// must stay below 2^32, so each operand, padded to whole tiles, stays below
+// 2 GiB less 64 KiB.  Any shape and any 2-byte alignment within that.
+bool tiled_fits(int64_t M, int64_t N, int64_t K) {
     const int64_t limit = (int64_t(1) << 31) - 65536;
-    return K % 8 == 0 && N % 8 == 0 && aligned(A, 16) && aligned(B, 16) && aligned(C, 16) && aligned(bias, 8) &&
-           2 * (M + 256) * K < limit && 2 * (K + 32) * (N + 256) < limit;
+    return 2 * (M + 256) * K < limit && 2 * (K + 32) * (N + 256) < limit;
+}
+
+// The tiled kernel's instance without last-slice fix-ups and with 8-byte
+// stores everywhere.
+bool tiled_aligned(int64_t N, int64_t K, const void *A, const void *B, const void *bias, const void *C) {
+    return K % 8 == 0 && N % 8 == 0 && aligned(A, 16) && aligned(B, 16) && aligned(C, 16) && aligned(bias, 8);
 }
 
 // Compute units of the device that `stream` belongs to (0 if unknown: the
@@ -108,7 +113,7 @@ tg_path auto_path(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
                   const void *C) {
     if (skinny_ok(M, N, K, A, B, bias, C))
         return TG_PATH_SKINNY;
-    if (tiled_ok(M, N, K, A, B, bias, C))
+    if (tiled_fits(M, N, K))
         return TG_PATH_TILED;
     return TG_PATH_TILED_GENERIC;
 }
@@ -138,7 +143,7 @@ TG_EXPORT tg_status tg_gemm_path(tg_path path, int64_t M, int64_t N, int64_t K, 
     if (path == TG_PATH_AUTO)
         path = auto_path(M, N, K, A, B, bias, C);
     else if ((path == TG_PATH_SKINNY && !skinny_ok(M, N, K, A, B, bias, C)) ||
-             (path == TG_PATH_TILED && !tiled_ok(M, N, K, A, B, bias, C)))
+             (path == TG_PATH_TILED && !tiled_fits(M, N, K)))
         return TG_ERR_UNSUPPORTED;
 
     tg::GemmArgs a;
@@ -154,7 +159,7 @@ TG_EXPORT tg_status tg_gemm_path(tg_path path, int64_t M, int64_t N, int64_t K, 
     if (path == TG_PATH_SKINNY)
         e = tg::launch_skinny(dtype, epilogue, a, s);
     else if (path == TG_PATH_TILED)
-        e = tg::launch_tiled_vec(dtype, epilogue, a, num_cu_of(s), s);
+        e = tg::launch_tiled_vec(dtype, epilogue, a, tiled_aligned(N, K, A, B, bias, C), num_cu_of(s), s);
     else
         e = tg::launch_tiled_generic(dtype, epilogue, a, s);
     return e == hipSuccess ? TG_OK : TG_ERR_LAUNCH;

@@ -18,11 +18,13 @@ struct GemmArgs {
 
 // dtype: 0 fp16, 1 bf16; epi: 0 none, 1 bias, 2 bias + GELU(tanh).
 
-// 256 x 256 tiles with 16-byte direct-to-LDS loads: K % 8 == 0, N % 8 == 0,
-// A, B, C 16-byte aligned, bias 8-byte aligned, 2 (M + 256) K and
-// 2 (K + 32) (N + 256) below 2^31 - 65536.
+// 256 x 256 tiles with 16-byte direct-to-LDS loads, any K and N and 2-byte
+// alignment, as long as 2 (M + 256) K and 2 (K + 32) (N + 256) stay below
+// 2^31 - 65536.  aligned: K % 8 == 0, N % 8 == 0, A, B, C 16-byte and bias
+// 8-byte aligned, which takes the instance without last-slice fix-ups and
+// with 8-byte stores throughout.
 // Persistent: at most num_cu workgroups (num_cu <= 0: one per tile).
-hipError_t launch_tiled_vec(int dtype, int epi, const GemmArgs &a, int num_cu, hipStream_t stream);
+hipError_t launch_tiled_vec(int dtype, int epi, const GemmArgs &a, bool aligned, int num_cu, hipStream_t stream);
 
 // 256 x 256 tiles with element-granular loads and stores: any shape.
 hipError_t launch_tiled_generic(int dtype, int epi, const GemmArgs &a, hipStream_t stream);

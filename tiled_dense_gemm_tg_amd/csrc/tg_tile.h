@@ -56,13 +56,18 @@ __device__ __forceinline__ void mfma_step(const u32x4 (&a)[4], const u32x4 (&b)[
             acc[i][j] = T::mfma32(b[j], a[i], acc[i][j]);
 }
 
+// How store_tile writes C: element by element (any shape and alignment);
+// 8-byte groups of four columns (N % 4 == 0, C and bias 8-byte aligned); or
+// 8-byte groups wherever a group lies inside the row and elements elsewhere
+// (any N and 2-byte alignment: the hardware takes unaligned 8-byte accesses,
+// but a group that crossed the row end would write into the next row).
+enum StoreMode { STORE_ELEM = 0, STORE_VEC = 1, STORE_GROUP = 2 };
+
 // Fused epilogue and store.  Lane l of wave (wm, wn) holds, in acc[i][j][e],
 // C[m][n] with m = m0 + wm*128 + 32 i + l%32 and
 // n = n0 + wn*128 + 32 j + 8 (e/4) + 4 (l/32) + e%4: four consecutive columns
-// per (i, j, e/4).  VEC: N % 8 == 0 and 8-byte aligned C and bias, so the four
-// columns are stored (and their bias loaded) as one 8-byte access; otherwise
-// element by element.
-template <class T, int EPI, bool VEC>
+// per (i, j, e/4).
+template <class T, int EPI, int MODE>
 __device__ __forceinline__ void store_tile(const GemmArgs &args, const f32x16 (&acc)[4][4], int m0, int n0, int wm,
                                            int wn, int lane) {
     const int M = args.M, N = args.N;
@@ -76,7 +81,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs &args, const f32x16 (&
             const int n = n0 + wn * 128 + 32 * j + 8 * q + 4 * lh;
             float bv[4] = {0.f, 0.f, 0.f, 0.f};
             if constexpr (EPI != EPI_NONE) {
-                if constexpr (VEC) {
+                if constexpr (MODE == STORE_VEC) {
                     if (n < N) {
                         const u32x2 raw = *reinterpret_cast<const u32x2 *>(args.bias + n);
                         bv[0] = T::to_f32((uint16_t)(raw.x & 0xffff));
@@ -99,10 +104,21 @@ __device__ __forceinline__ void store_tile(const GemmArgs &args, const f32x16 (&
                 for (int r = 0; r < 4; ++r)
                     o[r] = T::from_f32(epilogue<EPI>(acc[i][j][4 * q + r], bv[r]));
                 const uint32_t base = 2u * ((uint32_t)m * (uint32_t)N + (uint32_t)n);
-                if constexpr (VEC) {
+                const u32x2 packed = u32x2{pack2(o[0], o[1]), pack2(o[2], o[3])};
+                if constexpr (MODE == STORE_VEC) {
                     const uint32_t off = (m < M && n < N) ? base : OOB;
-                    __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack2(o[0], o[1]), pack2(o[2], o[3])}, rc,
-                                                          (int)off, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b64(packed, rc, (int)off, 0, 0);
+                } else if constexpr (MODE == STORE_GROUP) {
+                    if (n + 3 < N) {
+                        const uint32_t off = m < M ? base : OOB;
+                        __builtin_amdgcn_raw_buffer_store_b64(packed, rc, (int)off, 0, 0);
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const uint32_t off = (m < M && n + r < N) ? base + 2u * r : OOB;
+                            __builtin_amdgcn_raw_buffer_store_b16(o[r], rc, (int)off, 0, 0);
+                        }
+                    }
                 } else {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
