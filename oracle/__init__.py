@@ -62,8 +62,11 @@ def _load():
         lib.tg_oracle_max_threads.argtypes = []
         lib.tg_oracle_gemm.argtypes = [i64, i64, i64, ctypes.c_int, u16p, u16p, u16p, ctypes.c_int,
                                        i64p, i64, f64p, u16p]
+        u8p = ctypes.POINTER(ctypes.c_uint8)
+        lib.tg_oracle_gemm_w4.argtypes = [i64, i64, i64, ctypes.c_int, u16p, u8p, u16p, i64, u16p, ctypes.c_int,
+                                          i64p, i64, f64p, u16p]
         for f in (lib.tg_oracle_decode, lib.tg_oracle_encode, lib.tg_oracle_gelu_tanh,
-                  lib.tg_oracle_max_threads, lib.tg_oracle_gemm):
+                  lib.tg_oracle_max_threads, lib.tg_oracle_gemm, lib.tg_oracle_gemm_w4):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -145,4 +148,43 @@ def gemm(M: int, N: int, K: int, dtype: int, A, B, bias=None, epilogue: int = EP
                                 nrows, _ptr(out64, ctypes.c_double), _ptr(outq, ctypes.c_uint16))
     if rc != 0:
         raise ValueError(f"tg_oracle_gemm failed ({rc})")
+    return out64, outq
+
+
+def gemm_w4(M: int, N: int, K: int, dtype: int, A, Q, scales, group: int, bias=None,
+            epilogue: int = EPI_NONE, rows=None) -> Tuple[np.ndarray, np.ndarray]:
+    """Rows ``rows`` (default: all) of epilogue(A @ W [+ bias]) with the
+    weights W[k, n] = (Q[k, n] - 8) * scales[k // group, n].
+
+    A: (M, K) uint16 bit patterns; Q: (K, N) uint8 values 0..15 (one per
+    byte, unpacked); scales: (K // group, N) uint16 bit patterns; bias: (N,)
+    or None.  Returns (ref64, refq) as :func:`gemm`.
+    """
+    A = None if A is None else _u16(A)
+    Q = None if Q is None else np.ascontiguousarray(Q, dtype=np.uint8)
+    S = None if scales is None else _u16(scales)
+    if K > 0 and M > 0 and (A is None or A.size != M * K):
+        raise ValueError("A has the wrong size")
+    if K > 0 and N > 0 and (Q is None or Q.size != K * N):
+        raise ValueError("Q has the wrong size")
+    if K > 0 and N > 0 and (S is None or group <= 0 or S.size != (K // group) * N):
+        raise ValueError("scales have the wrong size")
+    bias_a = None
+    if bias is not None:
+        bias_a = _u16(bias)
+        if bias_a.size != N:
+            raise ValueError("bias has the wrong size")
+    if rows is None:
+        rows_a, nrows = None, M
+    else:
+        rows_a = np.ascontiguousarray(rows, dtype=np.int64)
+        nrows = rows_a.size
+    out64 = np.empty((nrows, N), dtype=np.float64)
+    outq = np.empty((nrows, N), dtype=np.uint16)
+    rc = _load().tg_oracle_gemm_w4(M, N, K, dtype, _ptr(A, ctypes.c_uint16), _ptr(Q, ctypes.c_uint8),
+                                   _ptr(S, ctypes.c_uint16), group, _ptr(bias_a, ctypes.c_uint16), epilogue,
+                                   _ptr(rows_a, ctypes.c_int64), nrows, _ptr(out64, ctypes.c_double),
+                                   _ptr(outq, ctypes.c_uint16))
+    if rc != 0:
+        raise ValueError(f"tg_oracle_gemm_w4 failed ({rc})")
     return out64, outq

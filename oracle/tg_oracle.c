@@ -165,46 +165,15 @@ int tg_oracle_max_threads(void)
 }
 
 /*
- * C rows `rows[0..nrows)` (or all M rows when rows == NULL, nrows == M) of
- * epilogue(A*B [+ bias]).  A is MxK, B is KxN, bias has N entries, all
- * row-major 16-bit patterns of `dtype`.  out64 and outq are nrows x N,
- * row r holding C row rows[r].
+ * Steps 2-4 on decoded operands: C rows `rows[0..nrows)` (or all M rows when
+ * rows == NULL) of epilogue(A*B [+ bias]) with B given as doubles Bd (KxN)
+ * and the bias as doubles biasd (N entries).
  */
-int tg_oracle_gemm(int64_t M, int64_t N, int64_t K, int dtype,
-                   const uint16_t *A, const uint16_t *B, const uint16_t *bias, int epilogue,
-                   const int64_t *rows, int64_t nrows, double *out64, uint16_t *outq)
+static void gemm_decoded(int64_t M, int64_t N, int64_t K, int dtype, const uint16_t *A, const double *Bd,
+                         const double *biasd, int epilogue, const int64_t *rows, int64_t nrows,
+                         double *out64, uint16_t *outq)
 {
-    if (M < 0 || N < 0 || K < 0 || nrows < 0)
-        return OR_BAD_ARG;
-    if (dtype != OR_F16 && dtype != OR_BF16)
-        return OR_BAD_ARG;
-    if (epilogue != OR_EPI_NONE && epilogue != OR_EPI_BIAS && epilogue != OR_EPI_BIAS_GELU_TANH)
-        return OR_BAD_ARG;
-    if (rows == NULL && nrows != M)
-        return OR_BAD_ARG;
-    if (nrows == 0 || N == 0)
-        return OR_OK;
-    if (!out64 || !outq || (epilogue != OR_EPI_NONE && !bias) || (K > 0 && (!A || !B)))
-        return OR_BAD_ARG;
-    for (int64_t r = 0; rows && r < nrows; ++r)
-        if (rows[r] < 0 || rows[r] >= M)
-            return OR_BAD_ARG;
-
-    /* Step 1: decode B and bias once. */
-    double *Bd = (double *)malloc((size_t)(K > 0 ? K : 1) * (size_t)N * sizeof(double));
-    double *biasd = (double *)malloc((size_t)N * sizeof(double));
-    if (!Bd || !biasd) {
-        free(Bd);
-        free(biasd);
-        return OR_NO_MEMORY;
-    }
-    #pragma omp parallel for schedule(static)
-    for (int64_t k = 0; k < K; ++k)
-        for (int64_t j = 0; j < N; ++j)
-            Bd[k * N + j] = decode(dtype, B[k * N + j]);
-    for (int64_t j = 0; j < N; ++j)
-        biasd[j] = (epilogue != OR_EPI_NONE) ? decode(dtype, bias[j]) : 0.0;
-
+    (void)M;
     #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t r = 0; r < nrows; ++r) {
         const int64_t i = rows ? rows[r] : r;
@@ -229,6 +198,110 @@ int tg_oracle_gemm(int64_t M, int64_t N, int64_t K, int dtype,
             outq[r * N + j] = encode(dtype, y);
         }
     }
+}
+
+static int check_common(int64_t M, int64_t N, int64_t K, int dtype, int epilogue, const int64_t *rows,
+                        int64_t nrows)
+{
+    if (M < 0 || N < 0 || K < 0 || nrows < 0)
+        return OR_BAD_ARG;
+    if (dtype != OR_F16 && dtype != OR_BF16)
+        return OR_BAD_ARG;
+    if (epilogue != OR_EPI_NONE && epilogue != OR_EPI_BIAS && epilogue != OR_EPI_BIAS_GELU_TANH)
+        return OR_BAD_ARG;
+    if (rows == NULL && nrows != M)
+        return OR_BAD_ARG;
+    for (int64_t r = 0; rows && r < nrows; ++r)
+        if (rows[r] < 0 || rows[r] >= M)
+            return OR_BAD_ARG;
+    return OR_OK;
+}
+
+/*
+ * C rows `rows[0..nrows)` (or all M rows when rows == NULL, nrows == M) of
+ * epilogue(A*B [+ bias]).  A is MxK, B is KxN, bias has N entries, all
+ * row-major 16-bit patterns of `dtype`.  out64 and outq are nrows x N,
+ * row r holding C row rows[r].
+ */
+int tg_oracle_gemm(int64_t M, int64_t N, int64_t K, int dtype,
+                   const uint16_t *A, const uint16_t *B, const uint16_t *bias, int epilogue,
+                   const int64_t *rows, int64_t nrows, double *out64, uint16_t *outq)
+{
+    int rc = check_common(M, N, K, dtype, epilogue, rows, nrows);
+    if (rc != OR_OK)
+        return rc;
+    if (nrows == 0 || N == 0)
+        return OR_OK;
+    if (!out64 || !outq || (epilogue != OR_EPI_NONE && !bias) || (K > 0 && (!A || !B)))
+        return OR_BAD_ARG;
+
+    /* Step 1: decode B and bias once. */
+    double *Bd = (double *)malloc((size_t)(K > 0 ? K : 1) * (size_t)N * sizeof(double));
+    double *biasd = (double *)malloc((size_t)N * sizeof(double));
+    if (!Bd || !biasd) {
+        free(Bd);
+        free(biasd);
+        return OR_NO_MEMORY;
+    }
+    #pragma omp parallel for schedule(static)
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t j = 0; j < N; ++j)
+            Bd[k * N + j] = decode(dtype, B[k * N + j]);
+    for (int64_t j = 0; j < N; ++j)
+        biasd[j] = (epilogue != OR_EPI_NONE) ? decode(dtype, bias[j]) : 0.0;
+
+    gemm_decoded(M, N, K, dtype, A, Bd, biasd, epilogue, rows, nrows, out64, outq);
+    free(Bd);
+    free(biasd);
+    return OR_OK;
+}
+
+/*
+ * The same product with B held as 4-bit weights, the weight-only quantized
+ * GEMM of LLM inference that the first TileLang page ("TileLang: writing LLM
+ * GPU kernels by thinking in tiles", section 5, "Quantized LLM inference")
+ * describes: packed integer weights are turned back into 16-bit values and
+ * fed to the matrix product.  Here that turning back is written out as its
+ * definition, for every weight:
+ *
+ *   b_kj = (q_kj - 8) * s_gj,   g = k / group,
+ *
+ * with q_kj in 0..15 (one value per byte of Q, KxN row-major), and s the
+ * scales (K/group x N row-major 16-bit patterns of `dtype`), decoded exactly.
+ * The product (q - 8) * s is exact in double.  Then steps 2-4 as above.
+ */
+int tg_oracle_gemm_w4(int64_t M, int64_t N, int64_t K, int dtype, const uint16_t *A, const uint8_t *Q,
+                      const uint16_t *scales, int64_t group, const uint16_t *bias, int epilogue,
+                      const int64_t *rows, int64_t nrows, double *out64, uint16_t *outq)
+{
+    int rc = check_common(M, N, K, dtype, epilogue, rows, nrows);
+    if (rc != OR_OK)
+        return rc;
+    if (group <= 0 || K % group != 0)
+        return OR_BAD_ARG;
+    if (nrows == 0 || N == 0)
+        return OR_OK;
+    if (!out64 || !outq || (epilogue != OR_EPI_NONE && !bias) || (K > 0 && (!A || !Q || !scales)))
+        return OR_BAD_ARG;
+    for (int64_t i = 0; i < K * N; ++i)
+        if (Q[i] > 15)
+            return OR_BAD_ARG;
+
+    double *Bd = (double *)malloc((size_t)(K > 0 ? K : 1) * (size_t)N * sizeof(double));
+    double *biasd = (double *)malloc((size_t)N * sizeof(double));
+    if (!Bd || !biasd) {
+        free(Bd);
+        free(biasd);
+        return OR_NO_MEMORY;
+    }
+    #pragma omp parallel for schedule(static)
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t j = 0; j < N; ++j)
+            Bd[k * N + j] = ((double)Q[k * N + j] - 8.0) * decode(dtype, scales[(k / group) * N + j]);
+    for (int64_t j = 0; j < N; ++j)
+        biasd[j] = (epilogue != OR_EPI_NONE) ? decode(dtype, bias[j]) : 0.0;
+
+    gemm_decoded(M, N, K, dtype, A, Bd, biasd, epilogue, rows, nrows, out64, outq);
     free(Bd);
     free(biasd);
     return OR_OK;

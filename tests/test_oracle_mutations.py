@@ -24,9 +24,14 @@ MUTANTS = {
     "f16_subnormal_scale": ("v = ldexp((double)f, -24);", "v = ldexp((double)f, -25);"),
     "bf16_exponent_bias": ("v = ldexp((double)(f + 128), e - 134);", "v = ldexp((double)(f + 128), e - 133);"),
     "gelu_constant": ("0.044715 * y * y * y", "0.04715 * y * y * y"),
+    "w4_zero_point": ("((double)Q[k * N + j] - 8.0)", "((double)Q[k * N + j] - 7.0)"),
+    "w4_q_transposed": ("((double)Q[k * N + j] - 8.0)", "((double)Q[j * K + k] - 8.0)"),
+    "w4_scale_group_shift": ("scales[(k / group) * N + j]", "scales[((k / group + 1) % (K / group)) * N + j]"),
+    "w4_scale_transposed": ("scales[(k / group) * N + j]", "scales[j * (K / group) + k / group]"),
+    "w4_sign": ("((double)Q[k * N + j] - 8.0) *", "(8.0 - (double)Q[k * N + j]) *"),
 }
 
-FAST_PINS = ["tests/test_oracle_codec.py", "tests/test_oracle_gemm.py",
+FAST_PINS = ["tests/test_oracle_codec.py", "tests/test_oracle_gemm.py", "tests/test_oracle_w4.py",
              "-k", "not workload_shapes and not blas and not thread_count"]
 
 
