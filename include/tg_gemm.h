@@ -170,6 +170,48 @@ tg_status tg_gemm_unfused(int64_t M, int64_t N, int64_t K, tg_dtype dtype,
                           const void *A, const void *B, const void *bias, tg_epilogue epilogue,
                           void *C, void *stream);
 
+/*
+ * Weight-only 4-bit GEMM, the quantized-inference product that the first
+ * TileLang page ("TileLang: writing LLM GPU kernels by thinking in tiles",
+ * section 5, "Quantized LLM inference") describes: weights stay packed in
+ * memory and are dequantized in registers on their way into the product.
+ *
+ *   C = epi(A * W [+ bias]),   W[k][n] = (q[k][n] - 8) * scales[k / group][n]
+ *
+ * with q[k][n] in 0..15.  The weights are first packed once into the layout
+ * the kernel streams (tg_w4_pack); the product then reads K*N/2 bytes of
+ * weights instead of 2*K*N.  fp32 accumulation; each group's scale multiplies
+ * the fp32 partial product of that group, and the integers q - 8 enter the
+ * matrix instruction exactly.
+ */
+
+/* Bytes of the packed weights of a K x N matrix: 32 * K * ceil(N / 64)
+ * (N padded to 64 columns); -1 unless K >= 0, N >= 0 and K % 32 == 0. */
+int64_t tg_w4_packed_bytes(int64_t K, int64_t N);
+
+/*
+ * Packs q (device, K x N bytes row-major, one value 0..15 per byte; higher
+ * bits are ignored) into `packed` (device, tg_w4_packed_bytes(K, N) bytes,
+ * 16-byte aligned), enqueued on `stream`.  Errors: INVALID_ARG for K % 32 != 0,
+ * negative sizes, null pointers with K*N > 0, packed misaligned or
+ * overlapping q; UNSUPPORTED above 2^31 - 64 packed or unpacked bytes.
+ */
+tg_status tg_w4_pack(int64_t K, int64_t N, const void *q, void *packed, void *stream);
+
+/*
+ * The product itself.  A (M x K), scales (K/group x N), bias (N), C (M x N)
+ * are 16-bit values of `dtype`, row-major, device pointers, any 2-byte
+ * alignment; packed as written by tg_w4_pack for the same K and N.
+ * group is 32, 64, 128 or 256 and divides K.  Any M (the kernel handles 16
+ * rows per workgroup; best for M <= 16).  Same epilogue, bias and degenerate
+ * shape rules as tg_gemm (K == 0 gives epi(0 + bias)); C must not overlap
+ * any input.  UNSUPPORTED when an operand exceeds 2^31 - 64 elements or
+ * bytes, or M exceeds 16 * 65535.
+ */
+tg_status tg_gemm_w4(int64_t M, int64_t N, int64_t K, tg_dtype dtype, const void *A, const void *packed,
+                     const void *scales, int64_t group, const void *bias, tg_epilogue epilogue, void *C,
+                     void *stream);
+
 /* Static, human-readable name of a status code ("TG_OK", ...). */
 const char *tg_status_string(tg_status status);
 

@@ -172,6 +172,49 @@ def test_unfused_checks_arguments_like_tg_gemm(lib):
     assert tg.tg_gemm_unfused(0, 4, 4, I.F16, None, None, PBIAS, I.EPI_BIAS, None, None) == tg.TG_OK
 
 
+def test_w4_packed_size(lib):
+    assert tg.tg_w4_packed_bytes(4096, 11008) == 32 * 4096 * 172
+    assert tg.tg_w4_packed_bytes(32, 1) == 32 * 32
+    assert tg.tg_w4_packed_bytes(0, 5) == 0
+    assert tg.tg_w4_packed_bytes(48, 64) == -1          # K % 32 != 0
+    assert tg.tg_w4_packed_bytes(-32, 64) == -1
+
+
+def w4(M=16, N=64, K=128, dtype=I.F16, A=PA, packed=PB, scales=PBIAS + 4096, group=32, bias=None,
+       epi=I.EPI_NONE, C=PC):
+    return tg.tg_gemm_w4(M, N, K, dtype, A, packed, scales, group, bias, epi, C, None)
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(M=-1), tg.TG_ERR_INVALID_ARG),
+    (dict(dtype=3), tg.TG_ERR_INVALID_ARG),
+    (dict(epi=3), tg.TG_ERR_INVALID_ARG),
+    (dict(group=48), tg.TG_ERR_INVALID_ARG),
+    (dict(group=256), tg.TG_ERR_INVALID_ARG),             # K % group != 0
+    (dict(K=100, group=32), tg.TG_ERR_INVALID_ARG),
+    (dict(bias=PBIAS), tg.TG_ERR_INVALID_ARG),             # bias with no epilogue
+    (dict(epi=I.EPI_BIAS), tg.TG_ERR_INVALID_ARG),         # epilogue without bias
+    (dict(A=None), tg.TG_ERR_INVALID_ARG),
+    (dict(packed=None), tg.TG_ERR_INVALID_ARG),
+    (dict(scales=None), tg.TG_ERR_INVALID_ARG),
+    (dict(C=None), tg.TG_ERR_INVALID_ARG),
+    (dict(C=PA + 64), tg.TG_ERR_INVALID_ARG),              # C overlaps A
+    (dict(C=PB + 64), tg.TG_ERR_INVALID_ARG),              # C overlaps the packed weights
+    (dict(M=16 * 65536), tg.TG_ERR_UNSUPPORTED),
+    (dict(M=0), tg.TG_OK),
+])
+def test_w4_argument_checks(lib, args, status):
+    assert w4(**args) == status
+
+
+def test_w4_pack_argument_checks(lib):
+    assert tg.tg_w4_pack(48, 64, PA, PB, None) == tg.TG_ERR_INVALID_ARG       # K % 32
+    assert tg.tg_w4_pack(64, 64, None, PB, None) == tg.TG_ERR_INVALID_ARG
+    assert tg.tg_w4_pack(64, 64, PA, PB + 8, None) == tg.TG_ERR_INVALID_ARG   # packed misaligned
+    assert tg.tg_w4_pack(64, 64, PA, PA + 1024, None) == tg.TG_ERR_INVALID_ARG  # overlap
+    assert tg.tg_w4_pack(0, 64, None, None, None) == tg.TG_OK
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(tg, "_lib", None)
     monkeypatch.setattr(tg, "LIBRARY", str(tmp_path / "missing.so"))

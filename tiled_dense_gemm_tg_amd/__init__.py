@@ -35,8 +35,8 @@ PATH_NAMES = {TG_PATH_AUTO: "auto", TG_PATH_TILED: "tiled", TG_PATH_TILED_GENERI
 TG_EW_BIAS_ADD = 0
 TG_EW_GELU_TANH = 1
 
-EXPORTED = ("tg_gemm", "tg_gemm_path", "tg_gemm_plan", "tg_elementwise", "tg_gemm_unfused", "tg_status_string",
-            "tg_version")
+EXPORTED = ("tg_gemm", "tg_gemm_path", "tg_gemm_plan", "tg_elementwise", "tg_gemm_unfused", "tg_w4_packed_bytes",
+            "tg_w4_pack", "tg_gemm_w4", "tg_status_string", "tg_version")
 
 _lib = None
 
@@ -71,6 +71,12 @@ def load_library():
     lib.tg_elementwise.restype = ci
     lib.tg_gemm_unfused.argtypes = [i64, i64, i64, ci, vp, vp, vp, ci, vp, vp]
     lib.tg_gemm_unfused.restype = ci
+    lib.tg_w4_packed_bytes.argtypes = [i64, i64]
+    lib.tg_w4_packed_bytes.restype = i64
+    lib.tg_w4_pack.argtypes = [i64, i64, vp, vp, vp]
+    lib.tg_w4_pack.restype = ci
+    lib.tg_gemm_w4.argtypes = [i64, i64, i64, ci, vp, vp, vp, i64, vp, ci, vp, vp]
+    lib.tg_gemm_w4.restype = ci
     lib.tg_status_string.argtypes = [ci]
     lib.tg_status_string.restype = ctypes.c_char_p
     lib.tg_version.argtypes = []
@@ -101,6 +107,18 @@ def tg_elementwise(op, M, N, dtype, bias, X, Y, stream) -> int:
 
 def tg_gemm_unfused(M, N, K, dtype, A, B, bias, epilogue, C, stream) -> int:
     return load_library().tg_gemm_unfused(M, N, K, dtype, A, B, bias, epilogue, C, stream)
+
+
+def tg_w4_packed_bytes(K, N) -> int:
+    return load_library().tg_w4_packed_bytes(K, N)
+
+
+def tg_w4_pack(K, N, q, packed, stream) -> int:
+    return load_library().tg_w4_pack(K, N, q, packed, stream)
+
+
+def tg_gemm_w4(M, N, K, dtype, A, packed, scales, group, bias, epilogue, C, stream) -> int:
+    return load_library().tg_gemm_w4(M, N, K, dtype, A, packed, scales, group, bias, epilogue, C, stream)
 
 
 def tg_status_string(status: int) -> str:
@@ -188,4 +206,49 @@ def elementwise(op: str, X, bias=None, out=None, stream=None):
                         out.data_ptr(), s)
     if st != TG_OK:
         raise TgError(st, "tg_elementwise")
+    return out
+
+
+def w4_pack(q, stream=None):
+    """Packs 4-bit weights ``q`` (a (K, N) uint8 GPU tensor, values 0..15)
+    into the layout :func:`gemm_w4` reads; returns a new uint8 tensor."""
+    import torch
+    if q.dtype != torch.uint8 or q.dim() != 2 or not q.is_cuda or not q.is_contiguous():
+        raise TypeError("q must be a contiguous 2-D uint8 GPU tensor")
+    K, N = q.shape
+    nbytes = tg_w4_packed_bytes(K, N)
+    if nbytes < 0:
+        raise ValueError("K must be a multiple of 32")
+    packed = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    s = (stream if stream is not None else torch.cuda.current_stream(q.device)).cuda_stream
+    st = tg_w4_pack(K, N, q.data_ptr(), packed.data_ptr(), s)
+    if st != TG_OK:
+        raise TgError(st, "tg_w4_pack")
+    return packed
+
+
+def gemm_w4(A, packed, scales, group: int, N: int, bias=None, epilogue: str = "none", out=None, stream=None):
+    """epilogue(A @ W [+ bias]) with W[k, n] = (q[k, n] - 8) * scales[k // group, n]
+    and q packed by :func:`w4_pack`; A (M, K) and scales (K // group, N) share
+    one 16-bit dtype."""
+    import torch
+    if A.dtype not in (torch.float16, torch.bfloat16) or A.dim() != 2:
+        raise TypeError("A must be a 2-D float16 or bfloat16 tensor")
+    M, K = A.shape
+    if scales.dtype != A.dtype or scales.numel() != (K // group) * N:
+        raise ValueError("scales must be (K // group, N) of A's dtype")
+    epi = _EPI[epilogue]
+    if (epi == EPI_NONE) != (bias is None):
+        raise ValueError("bias must be given exactly when the epilogue uses it")
+    if out is None:
+        out = torch.empty((M, N), dtype=A.dtype, device=A.device)
+    for name, t in (("A", A), ("packed", packed), ("scales", scales), ("bias", bias), ("out", out)):
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    dtype = F16 if A.dtype == torch.float16 else BF16
+    s = (stream if stream is not None else torch.cuda.current_stream(A.device)).cuda_stream
+    st = tg_gemm_w4(M, N, K, dtype, A.data_ptr(), packed.data_ptr(), scales.data_ptr(), group,
+                    bias.data_ptr() if bias is not None else None, epi, out.data_ptr(), s)
+    if st != TG_OK:
+        raise TgError(st, "tg_gemm_w4")
     return out

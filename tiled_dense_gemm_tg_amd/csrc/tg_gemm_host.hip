@@ -211,6 +211,75 @@ TG_EXPORT tg_status tg_gemm_unfused(int64_t M, int64_t N, int64_t K, tg_dtype dt
     return st;
 }
 
+TG_EXPORT int64_t tg_w4_packed_bytes(int64_t K, int64_t N) {
+    if (K < 0 || N < 0 || K % 32 != 0 || K > kMaxDim || N > kMaxDim)
+        return -1;
+    return 32 * K * ((N + 63) / 64);
+}
+
+TG_EXPORT tg_status tg_w4_pack(int64_t K, int64_t N, const void *q, void *packed, void *stream) {
+    const int64_t bytes = tg_w4_packed_bytes(K, N);
+    if (bytes < 0)
+        return TG_ERR_INVALID_ARG;
+    if (K == 0 || N == 0)
+        return TG_OK;
+    if (q == nullptr || packed == nullptr || !aligned(packed, 16))
+        return TG_ERR_INVALID_ARG;
+    if (overlaps(packed, bytes, q, K * N))
+        return TG_ERR_INVALID_ARG;
+    if (bytes > kMaxElements || elements(K, N) < 0)
+        return TG_ERR_UNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t e = tg::launch_w4_pack(static_cast<int>(K), static_cast<int>(N),
+                                            static_cast<const uint8_t *>(q), static_cast<uint8_t *>(packed), s);
+    return e == hipSuccess ? TG_OK : TG_ERR_LAUNCH;
+}
+
+TG_EXPORT tg_status tg_gemm_w4(int64_t M, int64_t N, int64_t K, tg_dtype dtype, const void *A, const void *packed,
+                               const void *scales, int64_t group, const void *bias, tg_epilogue epilogue, void *C,
+                               void *stream) {
+    if (M < 0 || N < 0 || K < 0)
+        return TG_ERR_INVALID_ARG;
+    if (dtype != TG_F16 && dtype != TG_BF16)
+        return TG_ERR_INVALID_ARG;
+    if (epilogue != TG_EPI_NONE && epilogue != TG_EPI_BIAS && epilogue != TG_EPI_BIAS_GELU_TANH)
+        return TG_ERR_INVALID_ARG;
+    if (epilogue == TG_EPI_NONE && bias != nullptr)
+        return TG_ERR_INVALID_ARG;
+    if (group != 32 && group != 64 && group != 128 && group != 256)
+        return TG_ERR_INVALID_ARG;
+    if (K % group != 0)
+        return TG_ERR_INVALID_ARG;
+    if (M == 0 || N == 0)
+        return TG_OK;
+    if (epilogue != TG_EPI_NONE && bias == nullptr)
+        return TG_ERR_INVALID_ARG;
+    if (C == nullptr || (K > 0 && (A == nullptr || packed == nullptr || scales == nullptr)))
+        return TG_ERR_INVALID_ARG;
+    const int64_t na = elements(M, K), nc = elements(M, N), ns = elements(K / group, N);
+    const int64_t pbytes = tg_w4_packed_bytes(K, N);
+    const int64_t cb = 2 * (nc < 0 ? kMaxElements : nc);
+    if (overlaps(C, cb, A, 2 * (na < 0 ? kMaxElements : na)) || overlaps(C, cb, packed, pbytes) ||
+        overlaps(C, cb, scales, 2 * (ns < 0 ? kMaxElements : ns)) ||
+        overlaps(C, cb, bias, epilogue != TG_EPI_NONE ? 2 * N : 0))
+        return TG_ERR_INVALID_ARG;
+    if (na < 0 || nc < 0 || ns < 0 || pbytes < 0 || pbytes > kMaxElements || M > 16 * 65535 || N > kMaxDim ||
+        K > kMaxDim)
+        return TG_ERR_UNSUPPORTED;
+    tg::GemmArgs a;
+    a.M = static_cast<int>(M);
+    a.N = static_cast<int>(N);
+    a.K = static_cast<int>(K);
+    a.A = static_cast<const uint16_t *>(A);
+    a.B = nullptr;
+    a.bias = static_cast<const uint16_t *>(bias);
+    a.C = static_cast<uint16_t *>(C);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t e = tg::launch_w4(dtype, epilogue, a, static_cast<const uint8_t *>(packed),
+                                       static_cast<const uint16_t *>(scales), static_cast<int>(group), s);
+    return e == hipSuccess ? TG_OK : TG_ERR_LAUNCH;
+}
+
 TG_EXPORT const char *tg_status_string(tg_status status) {
     switch (status) {
     case TG_OK: return "TG_OK";

@@ -32,6 +32,14 @@ hipError_t launch_tiled_generic(int dtype, int epi, const GemmArgs &a, hipStream
 // M <= 16, K % 8 == 0, N % 4 == 0, aligned operands.
 hipError_t launch_skinny(int dtype, int epi, const GemmArgs &a, hipStream_t stream);
 
+// Weight-only 4-bit product: packed weights in the layout of launch_w4_pack,
+// scales (K/group x N), group in {32, 64, 128, 256}, K % group == 0; any M
+// (16-row blocks), any N, 2-byte alignment.
+hipError_t launch_w4(int dtype, int epi, const GemmArgs &a, const uint8_t *packed, const uint16_t *scales, int group,
+                     hipStream_t stream);
+// q: K x N bytes (values 0..15), K % 32 == 0 -> packed (ceil(N/64) * 32 * K bytes).
+hipError_t launch_w4_pack(int K, int N, const uint8_t *q, uint8_t *packed, hipStream_t stream);
+
 // Elementwise passes over an M x N matrix: Y = X + bias[n] or Y = GELU_tanh(X)
 // (Y may be X).  vec: N % 8 == 0 and X, Y (and bias for the add) 16-byte
 // aligned.  At most 8 workgroups per CU (num_cu <= 0: 256 CUs assumed).

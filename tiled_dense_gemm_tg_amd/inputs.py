@@ -152,3 +152,15 @@ def make_small_int_operands(w: Workload, with_bias: bool = True) -> Operands:
     B = small_int_bits((w.K, w.N), w.dtype, s["B"] + 500)
     bias = small_int_bits((w.N,), w.dtype, s["bias"] + 500) if (with_bias and w.epilogue != EPI_NONE) else None
     return Operands(w, A, B, bias, sampled_rows(w))
+
+
+def w4_weights(K: int, N: int, seed: int) -> np.ndarray:
+    """4-bit weight codes, uniform over 0..15, one per byte, (K, N)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return rng.integers(0, 16, size=(K, N)).astype(np.uint8)
+
+
+# The weight-only 4-bit product timed beside the 16-bit decode shape: the same
+# M, N, K, with 128-row scale groups.
+W4_WORKLOAD = dict(name="gemm_w4_f16_16x11008x4096_g128", M=16, N=11008, K=4096, group=128, dtype=F16,
+                   a_dist=("normal", 0.0, 1.0), scale_dist=("uniform", 0.001, 0.01), seeds=(6001, 6002, 6003))
