@@ -44,8 +44,8 @@ MAIN = "gemm_f16_8192x8192x8192_bias_gelu_tanh"
 SQUARE = "gemm_f16_4096x4096x4096"
 SKINNY = "gemm_f16_skinny_16x11008x4096"
 RAGGED = "gemm_bf16_4000x4093x4111_bias_gelu_tanh"
-KERNEL_SOURCES = ["gemm_tiled.hip", "gemm_tiled_generic.hip", "gemm_skinny.hip", "tg_device.h", "tg_tile.h",
-                  "tg_launch.h", "tg_gemm_host.hip"]
+KERNEL_SOURCES = ["gemm_tiled.hip", "gemm_tiled_generic.hip", "gemm_skinny.hip", "gemm_w4.hip", "tg_device.h",
+                  "tg_tile.h", "tg_launch.h", "tg_gemm_host.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -365,7 +365,7 @@ def main() -> int:
                       "frac_hbm_peak": round(qgbps / PEAK_HBM_GBPS, 4),
                       "hot_cache_us_not_the_metric": round(hotq * 1e3, 3),
                       "algorithmic_bytes": qbytes, "speedup_vs_16bit_weights": round(ms4 / msq, 3),
-                      "path": "w4"}
+                      "path": "w4", "traffic": measured_traffic(wname)}
         log(f"{wname}: {msq * 1e3:.2f} us, {qgbps:.0f} GB/s, {ms4 / msq:.2f}x the 16-bit weights")
         torch.cuda.empty_cache()
         w3 = I.WORKLOADS[RAGGED]
