@@ -342,6 +342,99 @@ __device__ __forceinline__ void fix_last_slice(const GemmArgs &g, int m0, int n0
     }
 }
 
+// Epilogue and store through LDS.  After the k-loop the 128 KiB stage ring
+// is free and holds the whole 256 x 256 C tile of 16-bit values (512-byte
+// rows).  Each lane applies the epilogue to its accumulators and writes its
+// 4-column groups to LDS (16-byte chunk index XOR row % 32: the 32 rows one
+// instruction touches land on different chunks); then every wave copies whole
+// rows out, 16 bytes per lane, 2 rows of 512 bytes per instruction, so HBM
+// sees full row segments instead of 16-byte pieces of 32 rows (which, at
+// 2-byte-aligned row starts, split across write sectors).  Chunks that cross
+// column N go out element by element.  The caller's barrier after this keeps
+// the next tile's loads from overwriting LDS before every wave has read it.
+template <class T, int EPI, bool ALIGNED>
+__device__ __forceinline__ void store_tile_lds(const GemmArgs &args, const f32x16 (&acc)[4][4], int m0, int n0,
+                                               int wm, int wn, int lane, uint32_t lds0) {
+    const int M = args.M, N = args.N;
+    const int lr = lane & 31;
+    const int lh = lane >> 5;
+    // The bias of all 16 four-column groups of this lane, requested at once
+    // (range-checked: columns past N read zero), before the barrier.
+    uint32_t braw[4][4][2];
+    if constexpr (EPI != EPI_NONE) {
+        const __amdgpu_buffer_rsrc_t rb = tile::buffer_of(args.bias, 2u * (uint32_t)N);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t off = 2u * (uint32_t)(n0 + wn * 128 + 32 * j + 8 * q + 4 * lh);
+                if constexpr (ALIGNED) {   // N % 8 == 0: a group is all inside or all outside
+                    const u32x2 raw = __builtin_amdgcn_raw_buffer_load_b64(rb, (int)off, 0, 0);
+                    braw[j][q][0] = raw.x;
+                    braw[j][q][1] = raw.y;
+                } else {
+                    uint16_t e[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        e[r] = __builtin_amdgcn_raw_buffer_load_b16(rb, (int)(off + 2u * r), 0, 0);
+                    braw[j][q][0] = pack2(e[0], e[1]);
+                    braw[j][q][1] = pack2(e[2], e[3]);
+                }
+            }
+    }
+    __syncthreads();   // every wave is done reading the last slice
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int col = wn * 128 + 32 * j + 8 * q + 4 * lh;
+            float bv[4] = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (EPI != EPI_NONE) {
+                bv[0] = T::to_f32((uint16_t)(braw[j][q][0] & 0xffff));
+                bv[1] = T::to_f32((uint16_t)(braw[j][q][0] >> 16));
+                bv[2] = T::to_f32((uint16_t)(braw[j][q][1] & 0xffff));
+                bv[3] = T::to_f32((uint16_t)(braw[j][q][1] >> 16));
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = wm * 128 + 32 * i + lr;
+                uint16_t o[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    o[r] = T::from_f32(epilogue<EPI>(acc[i][j][4 * q + r], bv[r]));
+                const uint32_t chunk = (uint32_t)(col >> 3) ^ (uint32_t)(row & 31);
+                const uint32_t addr = lds0 + 512u * (uint32_t)row + 16u * chunk + 8u * (uint32_t)lh;
+                *(__attribute__((address_space(3))) u32x2 *)(uintptr_t)addr =
+                    u32x2{pack2(o[0], o[1]), pack2(o[2], o[3])};
+            }
+        }
+    }
+    __syncthreads();
+    const __amdgpu_buffer_rsrc_t rc = tile::buffer_of(args.C, 2u * (uint32_t)M * (uint32_t)N);
+    const int tid = threadIdx.x;
+#pragma unroll 4
+    for (int it = 0; it < 32; ++it) {
+        const int idx = it * NTHREADS + tid;
+        const int row = idx >> 5;
+        const int c = idx & 31;
+        const int m = m0 + row;
+        const int n = n0 + 8 * c;
+        const u32x4 v = *(__attribute__((address_space(3))) const u32x4 *)(uintptr_t)(
+            lds0 + 512u * (uint32_t)row + 16u * (uint32_t)(c ^ (row & 31)));
+        const uint32_t base = 2u * ((uint32_t)m * (uint32_t)N + (uint32_t)n);
+        if (ALIGNED || n + 8 <= N) {
+            const uint32_t off = (m < M && n < N) ? base : tile::OOB;
+            __builtin_amdgcn_raw_buffer_store_b128(v, rc, (int)off, 0, 0);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t off = (m < M && n + e < N) ? base + 2u * e : tile::OOB;
+                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(v[e >> 1] >> (16 * (e & 1))), rc, (int)off, 0, 0);
+            }
+        }
+    }
+}
+
 template <class T, int EPI, bool GEN>
 __global__ __launch_bounds__(NTHREADS) void gemm_tiled_kernel(GemmArgs args) {
     __shared__ __attribute__((aligned(16))) u32x4 smem[STAGES * STAGE_BYTES / 16];
@@ -459,7 +552,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_tiled_kernel(GemmArgs args) {
         if (t + 1 == nk)
             slice(t, none{}, w0{}, no{});
 
-        tile::store_tile<T, EPI, GEN ? tile::STORE_GROUP : tile::STORE_VEC>(args, acc, m0, n0, wm, wn, lane);
+        store_tile_lds<T, EPI, !GEN>(args, acc, m0, n0, wm, wn, lane, lds0);
         // every wave is done reading LDS before the next tile's loads land
         __syncthreads();
     }
