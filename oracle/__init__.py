@@ -65,8 +65,10 @@ def _load():
         u8p = ctypes.POINTER(ctypes.c_uint8)
         lib.tg_oracle_gemm_w4.argtypes = [i64, i64, i64, ctypes.c_int, u16p, u8p, u16p, i64, u16p, ctypes.c_int,
                                           i64p, i64, f64p, u16p]
+        lib.tg_oracle_attention.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int, u16p, u16p, u16p, ctypes.c_int,
+                                            ctypes.c_double, i64p, i64, f64p, u16p]
         for f in (lib.tg_oracle_decode, lib.tg_oracle_encode, lib.tg_oracle_gelu_tanh,
-                  lib.tg_oracle_max_threads, lib.tg_oracle_gemm, lib.tg_oracle_gemm_w4):
+                  lib.tg_oracle_max_threads, lib.tg_oracle_gemm, lib.tg_oracle_gemm_w4, lib.tg_oracle_attention):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -187,4 +189,36 @@ def gemm_w4(M: int, N: int, K: int, dtype: int, A, Q, scales, group: int, bias=N
                                    _ptr(outq, ctypes.c_uint16))
     if rc != 0:
         raise ValueError(f"tg_oracle_gemm_w4 failed ({rc})")
+    return out64, outq
+
+
+def attention(Bn: int, Sq: int, Sk: int, H: int, D: int, dtype: int, Q, K, V, causal: bool = False,
+              scale: Optional[float] = None, queries=None) -> Tuple[np.ndarray, np.ndarray]:
+    """softmax(scale * Q K^T) V for the queries ``queries`` (an (n, 3) array of
+    (batch, position, head); default: all, in (b, i, h) order), BSHD layout:
+    Q (Bn, Sq, H, D), K and V (Bn, Sk, H, D) uint16 bit patterns.  ``scale``
+    defaults to 1/sqrt(D); ``causal`` (Sq == Sk) lets query i see keys 0..i.
+    Returns (ref64, refq), each (n, D)."""
+    Qa = _u16(Q)
+    Ka = None if K is None else _u16(K)
+    Va = None if V is None else _u16(V)
+    if Qa.size != Bn * Sq * H * D:
+        raise ValueError("Q has the wrong size")
+    if Sk > 0 and (Ka is None or Va is None or Ka.size != Bn * Sk * H * D or Va.size != Bn * Sk * H * D):
+        raise ValueError("K or V has the wrong size")
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    if queries is None:
+        b, i, h = np.meshgrid(np.arange(Bn), np.arange(Sq), np.arange(H), indexing="ij")
+        queries = np.stack([b.ravel(), i.ravel(), h.ravel()], axis=1)
+    qa = np.ascontiguousarray(queries, dtype=np.int64).reshape(-1, 3)
+    nq = qa.shape[0]
+    out64 = np.empty((nq, D), dtype=np.float64)
+    outq = np.empty((nq, D), dtype=np.uint16)
+    rc = _load().tg_oracle_attention(Bn, Sq, Sk, H, D, dtype, _ptr(Qa, ctypes.c_uint16), _ptr(Ka, ctypes.c_uint16),
+                                     _ptr(Va, ctypes.c_uint16), 1 if causal else 0, float(scale),
+                                     _ptr(qa, ctypes.c_int64), nq, _ptr(out64, ctypes.c_double),
+                                     _ptr(outq, ctypes.c_uint16))
+    if rc != 0:
+        raise ValueError(f"tg_oracle_attention failed ({rc})")
     return out64, outq

@@ -306,3 +306,89 @@ int tg_oracle_gemm_w4(int64_t M, int64_t N, int64_t K, int dtype, const uint16_t
     free(biasd);
     return OR_OK;
 }
+
+/*
+ * Attention forward, written out from its definition as the first TileLang
+ * page states it ("TileLang: writing LLM GPU kernels by thinking in tiles",
+ * section 5, "FlashAttention": S = Q K^T / sqrt(d), P = softmax(S), O = P V),
+ * which FlashAttention computes blockwise with an online softmax and reaches
+ * up to rounding.  Layout BSHD as in the second page's listing ("TileLang: you
+ * write the dataflow, the compiler owns the schedule", "FlashAttention, in
+ * tiles"): Q is [batch][Sq][heads][D] row-major, K and V [batch][Sk][heads][D],
+ * O like Q.  For each requested query (b, i, h), in double:
+ *
+ *   s_j = scale * sum_d Q[b][i][h][d] * K[b][j][h][d]   for the allowed keys j,
+ *   m   = max_j s_j,   p_j = exp(s_j - m),   l = sum_j p_j,
+ *   O[b][i][h][d] = (sum_j p_j * V[b][j][h][d]) / l,
+ *
+ * where the allowed keys are all j < Sk, or with `causal` (Sq == Sk) the keys
+ * j <= i.  Sums run in ascending j (and d).  `queries` lists (b, i, h)
+ * triples; out64 and outq are nq x D.
+ */
+int tg_oracle_attention(int64_t Bn, int64_t Sq, int64_t Sk, int64_t H, int64_t D, int dtype, const uint16_t *Q,
+                        const uint16_t *K, const uint16_t *V, int causal, double scale, const int64_t *queries,
+                        int64_t nq, double *out64, uint16_t *outq)
+{
+    if (Bn < 0 || Sq < 0 || Sk < 0 || H < 0 || D < 0 || nq < 0)
+        return OR_BAD_ARG;
+    if (dtype != OR_F16 && dtype != OR_BF16)
+        return OR_BAD_ARG;
+    if (causal && Sq != Sk)
+        return OR_BAD_ARG;
+    if (nq == 0 || D == 0)
+        return OR_OK;
+    if (!queries || !out64 || !outq || !Q || (Sk > 0 && (!K || !V)))
+        return OR_BAD_ARG;
+    for (int64_t r = 0; r < nq; ++r) {
+        const int64_t *t = queries + 3 * r;
+        if (t[0] < 0 || t[0] >= Bn || t[1] < 0 || t[1] >= Sq || t[2] < 0 || t[2] >= H)
+            return OR_BAD_ARG;
+    }
+    int bad = 0;
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nq; ++r) {
+        const int64_t b = queries[3 * r], i = queries[3 * r + 1], h = queries[3 * r + 2];
+        const int64_t nk = causal ? i + 1 : Sk;
+        double *o = out64 + r * D;
+        double *s = (double *)malloc((size_t)(nk > 0 ? nk : 1) * sizeof(double));
+        double *q = (double *)malloc((size_t)D * sizeof(double));
+        if (!s || !q) {
+            free(s);
+            free(q);
+            #pragma omp atomic write
+            bad = 1;
+            continue;
+        }
+        for (int64_t d = 0; d < D; ++d)
+            q[d] = decode(dtype, Q[((b * Sq + i) * H + h) * D + d]);
+        double m = -INFINITY;
+        for (int64_t j = 0; j < nk; ++j) {
+            double acc = 0.0;
+            const uint16_t *krow = K + ((b * Sk + j) * H + h) * D;
+            for (int64_t d = 0; d < D; ++d)
+                acc += q[d] * decode(dtype, krow[d]);
+            s[j] = scale * acc;
+            if (s[j] > m)
+                m = s[j];
+        }
+        double l = 0.0;
+        for (int64_t j = 0; j < nk; ++j) {
+            s[j] = exp(s[j] - m);
+            l += s[j];
+        }
+        for (int64_t d = 0; d < D; ++d)
+            o[d] = 0.0;
+        for (int64_t j = 0; j < nk; ++j) {
+            const uint16_t *vrow = V + ((b * Sk + j) * H + h) * D;
+            for (int64_t d = 0; d < D; ++d)
+                o[d] += s[j] * decode(dtype, vrow[d]);
+        }
+        for (int64_t d = 0; d < D; ++d) {
+            o[d] = nk > 0 ? o[d] / l : 0.0;
+            outq[r * D + d] = encode(dtype, o[d]);
+        }
+        free(s);
+        free(q);
+    }
+    return bad ? OR_NO_MEMORY : OR_OK;
+}

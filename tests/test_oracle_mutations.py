@@ -29,9 +29,18 @@ MUTANTS = {
     "w4_scale_group_shift": ("scales[(k / group) * N + j]", "scales[((k / group + 1) % (K / group)) * N + j]"),
     "w4_scale_transposed": ("scales[(k / group) * N + j]", "scales[j * (K / group) + k / group]"),
     "w4_sign": ("((double)Q[k * N + j] - 8.0) *", "(8.0 - (double)Q[k * N + j]) *"),
+    "attn_no_scale": ("s[j] = scale * acc;", "s[j] = acc;"),
+    "attn_causal_strict": ("const int64_t nk = causal ? i + 1 : Sk;", "const int64_t nk = causal ? i : Sk;"),
+    "attn_no_max": ("s[j] = exp(s[j] - m);", "s[j] = exp(s[j]);"),
+    "attn_bhsd_keys": ("const uint16_t *krow = K + ((b * Sk + j) * H + h) * D;",
+                       "const uint16_t *krow = K + ((b * H + h) * Sk + j) * D;"),
+    "attn_bhsd_values": ("const uint16_t *vrow = V + ((b * Sk + j) * H + h) * D;",
+                         "const uint16_t *vrow = V + ((b * H + h) * Sk + j) * D;"),
+    "attn_unnormalized": ("o[d] = nk > 0 ? o[d] / l : 0.0;", "o[d] = nk > 0 ? o[d] : 0.0;"),
 }
 
 FAST_PINS = ["tests/test_oracle_codec.py", "tests/test_oracle_gemm.py", "tests/test_oracle_w4.py",
+             "tests/test_oracle_attention.py",
              "-k", "not workload_shapes and not blas and not thread_count"]
 
 
