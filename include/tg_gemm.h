@@ -212,6 +212,35 @@ tg_status tg_gemm_w4(int64_t M, int64_t N, int64_t K, tg_dtype dtype, const void
                      const void *scales, int64_t group, const void *bias, tg_epilogue epilogue, void *C,
                      void *stream);
 
+/*
+ * Attention forward, the fused kernel the TileLang pages build around the same
+ * tiles ("TileLang: writing LLM GPU kernels by thinking in tiles", section 5,
+ * "FlashAttention"; "TileLang: you write the dataflow, the compiler owns the
+ * schedule", "FlashAttention, in tiles"):
+ *
+ *   O[b][i][h][:] = sum_j softmax_j(scale * Q[b][i][h][:] . K[b][j][h][:]) V[b][j][h][:]
+ *
+ * over the visible keys j: all j < Sk, or with causal != 0 (which needs
+ * Sq == Sk) the keys j <= i.  The score matrix is never stored: key/value
+ * blocks stream through on-chip memory with an online softmax, fp32 scores
+ * and accumulation, and the probabilities rounded to `dtype` on their way
+ * into the second product.
+ *   batch, Sq, Sk, heads  sizes (>= 0); head_dim must be 128
+ *   Q, O      device pointers, [batch][Sq][heads][head_dim] row-major (BSHD)
+ *   K, V      device pointers, [batch][Sk][heads][head_dim]
+ *   scale     softmax scale > 0, or 0 for 1/sqrt(head_dim)
+ *   stream    hipStream_t or NULL
+ * Any 2-byte alignment.  A query with no visible key (Sk == 0) gets O = 0.
+ * Errors: INVALID_ARG for negative sizes, a bad dtype, causal with Sq != Sk,
+ * a negative or non-finite scale, null pointers where data is read or
+ * written; UNSUPPORTED for head_dim != 128, more than 65535 heads or
+ * batches, or Q/O or K/V (padded by a block of queries or keys) beyond 2 GiB
+ * less 64 KiB; then INVALID_ARG for O overlapping Q, K or V.
+ */
+tg_status tg_attention_fwd(int64_t batch, int64_t Sq, int64_t Sk, int64_t heads, int64_t head_dim, tg_dtype dtype,
+                           const void *Q, const void *K, const void *V, int causal, float scale, void *O,
+                           void *stream);
+
 /* Static, human-readable name of a status code ("TG_OK", ...). */
 const char *tg_status_string(tg_status status);
 

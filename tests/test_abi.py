@@ -215,6 +215,34 @@ def test_w4_pack_argument_checks(lib):
     assert tg.tg_w4_pack(0, 64, None, None, None) == tg.TG_OK
 
 
+def attn(Bn=1, Sq=256, Sk=256, H=2, Dh=128, dtype=I.F16, Q=PA, K=PB, V=PBIAS, causal=0, scale=0.0, O=PC):
+    return tg.tg_attention_fwd(Bn, Sq, Sk, H, Dh, dtype, Q, K, V, causal, scale, O, None)
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(Bn=-1), tg.TG_ERR_INVALID_ARG),
+    (dict(Sk=-1), tg.TG_ERR_INVALID_ARG),
+    (dict(dtype=2), tg.TG_ERR_INVALID_ARG),
+    (dict(causal=2), tg.TG_ERR_INVALID_ARG),
+    (dict(causal=1, Sk=128), tg.TG_ERR_INVALID_ARG),          # causal needs Sq == Sk
+    (dict(scale=-1.0), tg.TG_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), tg.TG_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), tg.TG_ERR_INVALID_ARG),
+    (dict(Q=None), tg.TG_ERR_INVALID_ARG),
+    (dict(V=None), tg.TG_ERR_INVALID_ARG),
+    (dict(O=None), tg.TG_ERR_INVALID_ARG),
+    (dict(O=PA + 256), tg.TG_ERR_INVALID_ARG),                # O overlaps Q
+    (dict(O=PBIAS + 64), tg.TG_ERR_INVALID_ARG),              # O overlaps V
+    (dict(Dh=64), tg.TG_ERR_UNSUPPORTED),
+    (dict(H=65536), tg.TG_ERR_UNSUPPORTED),
+    (dict(Sq=1 << 30), tg.TG_ERR_UNSUPPORTED),
+    (dict(Bn=0), tg.TG_OK),
+    (dict(Sq=0), tg.TG_OK),
+])
+def test_attention_argument_checks(lib, args, status):
+    assert attn(**args) == status
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(tg, "_lib", None)
     monkeypatch.setattr(tg, "LIBRARY", str(tmp_path / "missing.so"))

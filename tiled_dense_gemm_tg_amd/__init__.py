@@ -36,7 +36,7 @@ TG_EW_BIAS_ADD = 0
 TG_EW_GELU_TANH = 1
 
 EXPORTED = ("tg_gemm", "tg_gemm_path", "tg_gemm_plan", "tg_elementwise", "tg_gemm_unfused", "tg_w4_packed_bytes",
-            "tg_w4_pack", "tg_gemm_w4", "tg_status_string", "tg_version")
+            "tg_w4_pack", "tg_gemm_w4", "tg_attention_fwd", "tg_status_string", "tg_version")
 
 _lib = None
 
@@ -77,6 +77,8 @@ def load_library():
     lib.tg_w4_pack.restype = ci
     lib.tg_gemm_w4.argtypes = [i64, i64, i64, ci, vp, vp, vp, i64, vp, ci, vp, vp]
     lib.tg_gemm_w4.restype = ci
+    lib.tg_attention_fwd.argtypes = [i64, i64, i64, i64, i64, ci, vp, vp, vp, ci, ctypes.c_float, vp, vp]
+    lib.tg_attention_fwd.restype = ci
     lib.tg_status_string.argtypes = [ci]
     lib.tg_status_string.restype = ctypes.c_char_p
     lib.tg_version.argtypes = []
@@ -119,6 +121,10 @@ def tg_w4_pack(K, N, q, packed, stream) -> int:
 
 def tg_gemm_w4(M, N, K, dtype, A, packed, scales, group, bias, epilogue, C, stream) -> int:
     return load_library().tg_gemm_w4(M, N, K, dtype, A, packed, scales, group, bias, epilogue, C, stream)
+
+
+def tg_attention_fwd(batch, Sq, Sk, heads, head_dim, dtype, Q, K, V, causal, scale, O, stream) -> int:
+    return load_library().tg_attention_fwd(batch, Sq, Sk, heads, head_dim, dtype, Q, K, V, causal, scale, O, stream)
 
 
 def tg_status_string(status: int) -> str:
@@ -251,4 +257,30 @@ def gemm_w4(A, packed, scales, group: int, N: int, bias=None, epilogue: str = "n
                     bias.data_ptr() if bias is not None else None, epi, out.data_ptr(), s)
     if st != TG_OK:
         raise TgError(st, "tg_gemm_w4")
+    return out
+
+
+def attention(Q, K, V, causal: bool = False, scale: float = 0.0, out=None, stream=None):
+    """softmax(scale Q K^T) V over BSHD tensors: Q (batch, Sq, heads, 128),
+    K and V (batch, Sk, heads, 128), one 16-bit dtype; ``scale`` 0 means
+    1/sqrt(128).  Returns ``out`` (allocated like Q when not given)."""
+    import torch
+    if Q.dtype not in (torch.float16, torch.bfloat16) or Q.dim() != 4:
+        raise TypeError("Q must be a 4-D float16 or bfloat16 tensor (batch, seq, heads, dim)")
+    Bn, Sq, H, Dh = Q.shape
+    if K.shape != V.shape or K.dim() != 4 or K.shape[0] != Bn or K.shape[2] != H or K.shape[3] != Dh:
+        raise ValueError("K and V must be (batch, Sk, heads, dim) matching Q")
+    if K.dtype != Q.dtype or V.dtype != Q.dtype:
+        raise TypeError("Q, K and V must share one dtype")
+    if out is None:
+        out = torch.empty_like(Q)
+    for name, t in (("Q", Q), ("K", K), ("V", V), ("out", out)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    dtype = F16 if Q.dtype == torch.float16 else BF16
+    s = (stream if stream is not None else torch.cuda.current_stream(Q.device)).cuda_stream
+    st = tg_attention_fwd(Bn, Sq, K.shape[1], H, Dh, dtype, Q.data_ptr(), K.data_ptr(), V.data_ptr(),
+                          1 if causal else 0, float(scale), out.data_ptr(), s)
+    if st != TG_OK:
+        raise TgError(st, "tg_attention_fwd")
     return out

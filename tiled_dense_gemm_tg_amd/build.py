@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIBRARY = os.path.join(PKG, "libtg_gemm.so")
-SOURCES = ["tg_gemm_host.hip", "gemm_tiled.hip", "gemm_tiled_generic.hip", "gemm_skinny.hip", "elementwise.hip", "gemm_w4.hip"]
+SOURCES = ["tg_gemm_host.hip", "gemm_tiled.hip", "gemm_tiled_generic.hip", "gemm_skinny.hip", "elementwise.hip", "gemm_w4.hip", "attention_fwd.hip"]
 ARCH = "gfx950"
 
 

@@ -1,0 +1,382 @@
+// attention_fwd.hip -- FlashAttention forward for gfx950: O = softmax(scale Q K^T) V
+// per (batch, head), BSHD layout, head dim 128, fp16 or bf16, fp32 accumulate.
+//
+// The TileLang pages present this as the kernel where tiles matter most
+// ("TileLang: writing LLM GPU kernels by thinking in tiles", section 5,
+// "FlashAttention"; "TileLang: you write the dataflow, the compiler owns the
+// schedule", "FlashAttention, in tiles"): a block of queries stays on chip,
+// key/value blocks stream past it, the scores of each block go through an
+// online softmax (running row maximum, rescaling of the partial output,
+// running sum of exponentials, exp2 with log2(e) folded into the scale) and
+// straight into the second product, so the Sq x Sk score matrix never exists
+// in memory.  The CDNA4 design:
+//
+//   * a workgroup of 4 waves holds 256 queries of one (batch, head); each
+//     wave owns 64 of them as two 32-query sub-tiles, its Q fragments in
+//     registers for the whole loop;
+//   * key/value blocks of 64 tokens stream through a 3-stage LDS ring by
+//     direct-to-LDS loads (each block requested two blocks ahead);
+//   * both products are computed transposed on v_mfma_f32_32x32x16:
+//     S^T = K Q^T (K rows from LDS, Q^T from registers) and
+//     O^T = V^T P^T (V^T through the transposing LDS read), so every lane
+//     holds the scores and the output of one query column: the row maximum
+//     and sum need one exchange between the two lane halves, the rescaling
+//     factor is per lane, and the probabilities go from the S accumulators
+//     straight into the second MFMA's operand (the two halves of a lane's 8
+//     keys are 4-key groups, and V^T is read in the same key order);
+//   * rescaling is lazy: the running maximum used in the exponentials only
+//     moves when a block's maximum exceeds it by more than 8 (in log2 units),
+//     which keeps every exponential below 2^8 and rescales the output rarely;
+//     numerator and denominator always share the same maximum, so the
+//     quotient is unchanged;
+//   * causal masking (query i sees keys 0..i, Sq == Sk) and the key tail
+//     (k >= Sk) set scores to -inf in the blocks that need it; causal
+//     workgroups stop at their last visible block, and the query blocks with
+//     the most keys, over all heads, are dispatched first.
+#include "tg_device.h"
+#include "tg_launch.h"
+
+#include <type_traits>
+#include <utility>
+
+namespace tg {
+namespace {
+
+constexpr int HD = 128;                   // head dim
+constexpr int WAVES = 4;
+constexpr int NTHREADS = 64 * WAVES;
+constexpr int QW = 64;                    // queries per wave
+constexpr int BM = QW * WAVES;            // queries per workgroup
+constexpr int BN = 64;                    // keys per block
+constexpr int STAGES = 3;
+constexpr int KV_BYTES = BN * HD * 2;     // 16 KiB: one block of K (or V) in LDS
+constexpr int STAGE_BYTES = 2 * KV_BYTES;
+constexpr uint32_t SHIFT = 4096;          // buffers start 4 KiB before K and V
+constexpr uint32_t OOB_BUMP = 0x80000000u;
+constexpr float RESCALE_LOG2 = 8.0f;
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+__device__ __forceinline__ uint32_t lds_address(const void *p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p;
+}
+
+__device__ __forceinline__ i32x4 rsrc_words(const void *base, uint32_t bytes) {
+    const uint64_t p = reinterpret_cast<uint64_t>(base);
+    return i32x4{(int)(uint32_t)p, (int)(uint32_t)(p >> 32), (int)bytes, 0x00020000};
+}
+
+template <int OFF>
+__device__ __forceinline__ void dma16(const i32x4 &rsrc, uint32_t voffset, uint32_t m0) {
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen offset:%3 lds" ::"v"(voffset), "s"(rsrc), "{m0}"(m0),
+                 "i"(OFF));
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// K rows are 256 bytes = 16 chunks; the fragment read takes one chunk of 32
+// consecutive rows, so the chunk index is XOR-ed with row % 16.
+__device__ __forceinline__ int k_swz(int row) { return row & 15; }
+// V rows are read transposed, 4 consecutive rows per pass (as B in the GEMM).
+__device__ __forceinline__ int v_swz(int row) { return ((row & 1) ? 10 : 0) ^ ((row & 2) ? 4 : 0); }
+
+__device__ __forceinline__ u32x4 lds_u4(uint32_t byte) {
+    return *(__attribute__((address_space(3))) const u32x4 *)(uintptr_t)byte;
+}
+
+__device__ __forceinline__ u32x2 lds_tr(uint32_t byte) {
+    const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(uintptr_t)byte);
+    return __builtin_bit_cast(u32x2, v);
+}
+
+__device__ __forceinline__ float lane_swap32(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
+        (int)((((int)threadIdx.x & 63) ^ 32) << 2), __builtin_bit_cast(int, x)));
+}
+
+template <class T, bool CAUSAL>
+__global__ __launch_bounds__(NTHREADS) void attention_fwd_kernel(AttnArgs args) {
+    __shared__ __attribute__((aligned(16))) u32x4 smem[STAGES * STAGE_BYTES / 16];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    int h, b, qb;
+    if constexpr (CAUSAL) {
+        // one flat grid, heaviest query blocks (longest key range) of every
+        // head dispatched first, so the longest workgroups start earliest
+        const int bh = args.B * args.H;
+        const int nqb = (int)gridDim.x / bh;
+        const int id = (int)blockIdx.x;
+        qb = nqb - 1 - id / bh;
+        h = (id % bh) % args.H;
+        b = (id % bh) / args.H;
+    } else {
+        qb = (int)blockIdx.x;
+        h = (int)blockIdx.y;
+        b = (int)blockIdx.z;
+    }
+    const int q0 = qb * BM;
+    const int Sq = args.Sq, Sk = args.Sk, H = args.H;
+    const uint32_t tok = 2u * (uint32_t)H * (uint32_t)HD;   // bytes between tokens
+    const uint32_t lds0 = lds_address(smem);
+    auto stage = [&](int st) { return lds0 + (uint32_t)st * (uint32_t)STAGE_BYTES; };
+    const int lh = lane >> 5;    // lane half
+    const int lc = lane & 31;    // query column within a sub-tile
+
+    // ---- Q fragments: sub-tile q, d-step s: query q0 + 64 wave + 32 q + lc, d = 16 s + 8 lh .. +7
+    u32x4 qf[2][8];
+    {
+        const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(args.Q), (short)0, (int)((uint32_t)args.B * (uint32_t)Sq * tok), 0x00020000);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int qi = q0 + QW * wave + 32 * q + lc;
+            const uint32_t base = ((uint32_t)b * (uint32_t)Sq + (uint32_t)qi) * tok + 2u * (uint32_t)h * HD;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const uint32_t off = qi < Sq ? base + 2u * (uint32_t)(16 * s + 8 * lh) : 0xFFFFFFF0u;
+                qf[q][s] = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)off, 0, 0);
+            }
+        }
+    }
+
+    // The Q loads are the only loads the compiler tracks here; waiting for them
+    // now keeps it from waiting for every load in flight inside the loop.
+    wait_vmcnt<0>();
+
+    // ---- direct loads of one key/value block: wave w fills rows 16 w .. 16 w + 15
+    // of K and of V, 4 instructions each (4 rows of 256 bytes per instruction).
+    const uint32_t kv_bytes = (uint32_t)args.B * (uint32_t)Sk * tok;
+    const i32x4 rk = rsrc_words((const char *)args.K - SHIFT, kv_bytes + SHIFT);
+    const i32x4 rv = rsrc_words((const char *)args.V - SHIFT, kv_bytes + SHIFT);
+    uint32_t koff[4], voff[4];
+    int krow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = 16 * wave + 4 * i + (lane >> 4);
+        krow[i] = row;
+        const uint32_t tok_base = ((uint32_t)b * (uint32_t)Sk + (uint32_t)row) * tok + 2u * (uint32_t)h * HD;
+        koff[i] = SHIFT - 1024u * i + tok_base + 16u * (uint32_t)((lane & 15) ^ k_swz(row));
+        voff[i] = SHIFT - 1024u * i + tok_base + 16u * (uint32_t)((lane & 15) ^ v_swz(row));
+    }
+    const uint32_t m0_k = 4096u * (uint32_t)wave;
+    auto issue_block = [&](int blk, int st) __attribute__((always_inline)) {
+        const int kb = blk * BN;
+        const uint32_t adv = (uint32_t)kb * tok;
+        const uint32_t sb = stage(st);
+        auto one = [&](auto ic) __attribute__((always_inline)) {
+            constexpr int i = decltype(ic)::value;
+            const uint32_t mask = kb + krow[i] < Sk ? 0u : OOB_BUMP;
+            dma16<1024 * i>(rk, koff[i] + adv + mask, sb + m0_k);
+        };
+        auto onev = [&](auto ic) __attribute__((always_inline)) {
+            constexpr int i = decltype(ic)::value;
+            const uint32_t mask = kb + krow[i] < Sk ? 0u : OOB_BUMP;
+            dma16<1024 * i>(rv, voff[i] + adv + mask, sb + (uint32_t)KV_BYTES + m0_k);
+        };
+        one(std::integral_constant<int, 0>{});
+        one(std::integral_constant<int, 1>{});
+        one(std::integral_constant<int, 2>{});
+        one(std::integral_constant<int, 3>{});
+        onev(std::integral_constant<int, 0>{});
+        onev(std::integral_constant<int, 1>{});
+        onev(std::integral_constant<int, 2>{});
+        onev(std::integral_constant<int, 3>{});
+    };
+
+    // ---- fragment read addresses (bytes within a stage)
+    // K for S^T: key row 32 kt + lc, chunk 2 s + lh
+    uint32_t ka[2][8];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const int row = 32 * kt + lc;
+            ka[kt][s] = 256u * (uint32_t)row + 16u * (uint32_t)((2 * s + lh) ^ k_swz(row));
+        }
+    // V^T for O^T, d-tile dt, key step u: two transposed reads, key rows
+    // 16 u + 4 lh + (0..3) and 16 u + 8 + 4 lh + (0..3), columns 32 dt + lc.
+    const int G = lane >> 4;
+    const int qq = lane & 15;
+    uint32_t va[4];     // [dt], for u = 0, first read; + 256 * 16 u per step, + 2048 for the second read
+    {
+        const int row = 4 * (G >> 1) + (qq >> 2);
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+            const int chunk = 4 * dt + 2 * (G & 1) + ((qq & 3) >> 1);
+            va[dt] = (uint32_t)KV_BYTES + 256u * (uint32_t)row + 16u * (uint32_t)(chunk ^ v_swz(row)) +
+                     8u * (uint32_t)(qq & 1);
+        }
+    }
+
+    f32x16 o[2][4];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+            o[q][dt] = f32x16{};
+    float m_used[2] = {-INFINITY, -INFINITY};
+    float l_sum[2] = {0.f, 0.f};
+    const float c = args.scale_log2;
+
+    const int k_end = CAUSAL ? min(Sk, q0 + BM) : Sk;
+    const int nb = (k_end + BN - 1) / BN;
+    if (nb > 0)
+        issue_block(0, 0);
+    if (nb > 1) {
+        issue_block(1, 1);
+        wait_vmcnt<8>();
+    } else {
+        wait_vmcnt<0>();
+    }
+    __syncthreads();
+
+    for (int t = 0; t < nb; ++t) {
+        const uint32_t st = stage(t % STAGES);
+        if (t + 2 < nb)
+            issue_block(t + 2, (t + 2) % STAGES);
+        const int kb = t * BN;
+
+        // ---- S^T = K Q^T for both sub-tiles
+        f32x16 sacc[2][2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+                sacc[q][kt] = f32x16{};
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+                const u32x4 kf = lds_u4(st + ka[kt][s]);
+#pragma unroll
+                for (int q = 0; q < 2; ++q)
+                    sacc[q][kt] = T::mfma32(kf, qf[q][s], sacc[q][kt]);
+            }
+
+        // ---- online softmax (scores of key kb + 32 kt + 8 (e/4) + 4 lh + e%4)
+        const bool need_mask = kb + BN > Sk || (CAUSAL && kb + BN - 1 > q0);
+        u32x4 pf[2][4];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int qi = q0 + QW * wave + 32 * q + lc;
+            // key = kb + 4 lh + off(kt, e) with a compile-time off: visible if
+            // off < Sk - kb - 4 lh and (causal) off <= qi - kb - 4 lh
+            const int key0 = kb + 4 * lh;
+            const int tail = Sk - key0;
+            const int diag = qi - key0;
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    float v = sacc[q][kt][e];
+                    if (need_mask) {
+                        const int off = 32 * kt + 8 * (e >> 2) + (e & 3);
+                        const bool ok = off < tail && (!CAUSAL || off <= diag);
+                        v = ok ? v : -INFINITY;
+                        sacc[q][kt][e] = v;
+                    }
+                    mx = fmaxf(mx, v);
+                }
+            mx = fmaxf(mx, lane_swap32(mx));
+            const float m_blk = mx * c;
+            // lazy rescaling: move the maximum only when it grew by more than 2^8
+            if (__builtin_amdgcn_ballot_w64(m_blk > m_used[q] + RESCALE_LOG2) != 0) {
+                const float m_new = fmaxf(m_used[q], m_blk);
+                const float alpha = m_used[q] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_used[q] - m_new);
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt)
+                    o[q][dt] *= alpha;
+                l_sum[q] *= alpha;
+                m_used[q] = m_new;
+            }
+            const float m_ref = m_used[q] == -INFINITY ? 0.f : m_used[q];
+            float sum = 0.f;
+            uint16_t pb[2][16];
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const float p = __builtin_amdgcn_exp2f(fmaf(sacc[q][kt][e], c, -m_ref));
+                    sum += p;
+                    pb[kt][e] = T::from_f32(p);
+                }
+            l_sum[q] += sum;
+            // key step u = 2 kt + half: the lane's 8 keys are e = 8 half + 0..7 of tile kt
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int kt = u >> 1, e0 = 8 * (u & 1);
+                pf[q][u] = u32x4{pack2(pb[kt][e0], pb[kt][e0 + 1]), pack2(pb[kt][e0 + 2], pb[kt][e0 + 3]),
+                                 pack2(pb[kt][e0 + 4], pb[kt][e0 + 5]), pack2(pb[kt][e0 + 6], pb[kt][e0 + 7])};
+            }
+        }
+
+        // ---- O^T += V^T P^T
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+                const uint32_t a0 = st + va[dt] + 4096u * (uint32_t)u;   // 16 rows of 256 bytes per step
+                const u32x2 lo = lds_tr(a0);
+                const u32x2 hi = lds_tr(a0 + 2048u);                    // + 8 rows
+                const u32x4 vf = u32x4{lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+                for (int q = 0; q < 2; ++q)
+                    o[q][dt] = T::mfma32(vf, pf[q][u], o[q][dt]);
+            }
+
+        // next block landed (this wave's loads; the barrier covers everyone's),
+        // and every wave is done with this stage before it is refilled
+        if (t + 2 < nb)
+            wait_vmcnt<8>();
+        else
+            wait_vmcnt<0>();
+        __syncthreads();
+    }
+
+    // ---- normalise and store: lane holds O[query][d] for d = 32 dt + 8 (e/4) + 4 lh + e%4
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+        args.O, (short)0, (int)((uint32_t)args.B * (uint32_t)Sq * tok), 0x00020000);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const float l_tot = l_sum[q] + lane_swap32(l_sum[q]);
+        const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+        const int qi = q0 + QW * wave + 32 * q + lc;
+        const uint32_t base = ((uint32_t)b * (uint32_t)Sq + (uint32_t)qi) * tok + 2u * (uint32_t)h * HD;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                uint16_t w[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    w[r] = T::from_f32(o[q][dt][4 * g + r] * inv);
+                const uint32_t off = qi < Sq ? base + 2u * (uint32_t)(32 * dt + 8 * g + 4 * lh) : 0xFFFFFFF0u;
+                __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack2(w[0], w[1]), pack2(w[2], w[3])}, ro, (int)off,
+                                                      0, 0);
+            }
+    }
+}
+
+template <class T>
+hipError_t launch_typed(const AttnArgs &a, hipStream_t stream) {
+    const int nqb = (a.Sq + BM - 1) / BM;
+    if (a.causal)
+        hipLaunchKernelGGL((attention_fwd_kernel<T, true>), dim3(nqb * a.H * a.B), dim3(NTHREADS), 0, stream, a);
+    else
+        hipLaunchKernelGGL((attention_fwd_kernel<T, false>), dim3(nqb, a.H, a.B), dim3(NTHREADS), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attention_fwd(int dtype, const AttnArgs &a, hipStream_t stream) {
+    return dtype == 0 ? launch_typed<F16>(a, stream) : launch_typed<BF16>(a, stream);
+}
+
+}  // namespace tg

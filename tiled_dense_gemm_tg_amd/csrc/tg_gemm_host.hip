@@ -9,6 +9,7 @@
 #include "tg_launch.h"
 
 #include <atomic>
+#include <math.h>
 #include <stdint.h>
 
 #define TG_EXPORT extern "C" __attribute__((visibility("default")))
@@ -277,6 +278,52 @@ TG_EXPORT tg_status tg_gemm_w4(int64_t M, int64_t N, int64_t K, tg_dtype dtype, 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const hipError_t e = tg::launch_w4(dtype, epilogue, a, static_cast<const uint8_t *>(packed),
                                        static_cast<const uint16_t *>(scales), static_cast<int>(group), s);
+    return e == hipSuccess ? TG_OK : TG_ERR_LAUNCH;
+}
+
+TG_EXPORT tg_status tg_attention_fwd(int64_t batch, int64_t Sq, int64_t Sk, int64_t heads, int64_t head_dim,
+                                     tg_dtype dtype, const void *Q, const void *K, const void *V, int causal,
+                                     float scale, void *O, void *stream) {
+    if (batch < 0 || Sq < 0 || Sk < 0 || heads < 0 || head_dim < 0)
+        return TG_ERR_INVALID_ARG;
+    if (dtype != TG_F16 && dtype != TG_BF16)
+        return TG_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1)
+        return TG_ERR_INVALID_ARG;
+    if (causal && Sq != Sk)
+        return TG_ERR_INVALID_ARG;
+    if (!(scale >= 0.0f) || scale == HUGE_VALF)
+        return TG_ERR_INVALID_ARG;
+    if (batch == 0 || Sq == 0 || heads == 0 || head_dim == 0)
+        return TG_OK;
+    if (Q == nullptr || O == nullptr || (Sk > 0 && (K == nullptr || V == nullptr)))
+        return TG_ERR_INVALID_ARG;
+    // Sizes first (in double: the int64 products could overflow), then overlaps.
+    const double limit = double((int64_t(1) << 31) - 65536);
+    if (head_dim != 128 || heads > 65535 || batch > 65535 || double(batch) * double(heads) * double(Sq / 256 + 1) >= 2.0e9)
+        return TG_ERR_UNSUPPORTED;
+    if (2.0 * double(batch) * double(Sq + 256) * double(heads) * double(head_dim) >= limit ||
+        2.0 * double(batch) * double(Sk + 64) * double(heads) * double(head_dim) >= limit)
+        return TG_ERR_UNSUPPORTED;
+    const int64_t q_bytes = 2 * batch * Sq * heads * head_dim;
+    const int64_t kv_bytes = 2 * batch * Sk * heads * head_dim;
+    if (overlaps(O, q_bytes, Q, q_bytes) || overlaps(O, q_bytes, K, kv_bytes) || overlaps(O, q_bytes, V, kv_bytes))
+        return TG_ERR_INVALID_ARG;
+    if (scale == 0.0f)
+        scale = 1.0f / sqrtf((float)head_dim);
+    tg::AttnArgs a;
+    a.B = static_cast<int>(batch);
+    a.Sq = static_cast<int>(Sq);
+    a.Sk = static_cast<int>(Sk);
+    a.H = static_cast<int>(heads);
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.causal = causal;
+    a.Q = static_cast<const uint16_t *>(Q);
+    a.K = static_cast<const uint16_t *>(K);
+    a.V = static_cast<const uint16_t *>(V);
+    a.O = static_cast<uint16_t *>(O);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t e = tg::launch_attention_fwd(dtype, a, s);
     return e == hipSuccess ? TG_OK : TG_ERR_LAUNCH;
 }
 

@@ -40,6 +40,16 @@ hipError_t launch_w4(int dtype, int epi, const GemmArgs &a, const uint8_t *packe
 // q: K x N bytes (values 0..15), K % 32 == 0 -> packed (ceil(N/64) * 32 * K bytes).
 hipError_t launch_w4_pack(int K, int N, const uint8_t *q, uint8_t *packed, hipStream_t stream);
 
+// Attention forward, BSHD layout, head dim 128: O = softmax(scale Q K^T) V.
+struct AttnArgs {
+    int B, Sq, Sk, H;
+    float scale_log2;      // softmax scale times log2(e), > 0
+    int causal;            // query i sees keys 0..i (Sq == Sk)
+    const uint16_t *Q, *K, *V;
+    uint16_t *O;
+};
+hipError_t launch_attention_fwd(int dtype, const AttnArgs &a, hipStream_t stream);
+
 // Elementwise passes over an M x N matrix: Y = X + bias[n] or Y = GELU_tanh(X)
 // (Y may be X).  vec: N % 8 == 0 and X, Y (and bias for the add) 16-byte
 // aligned.  At most 8 workgroups per CU (num_cu <= 0: 256 CUs assumed).
