@@ -99,6 +99,32 @@ __device__ __forceinline__ float lane_swap32(float x) {
         (int)((((int)threadIdx.x & 63) ^ 32) << 2), __builtin_bit_cast(int, x)));
 }
 
+// acc *= alpha on accumulators that live in AGPRs, through inline assembly so
+// that the compiler keeps them there (a plain multiply makes it copy every
+// accumulator to VGPRs on each iteration, whether or not a rescale happens).
+// The caller first waits out the MFMA-write -> accumulator-read hazard
+// (hazard_fence); the s_nop after the writes covers accumulator-write ->
+// MFMA-read.
+__device__ __forceinline__ void scale_agpr(f32x16 &acc, float alpha) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        float x = acc[e];
+        float t;
+        asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                     : "+a"(x), "=&v"(t)
+                     : "v"(alpha));
+        acc[e] = x;
+    }
+    asm volatile("s_nop 4" : "+a"(acc));
+}
+
+// 32 wait states after the last MFMA that wrote any of the accumulators
+// (a 32x32 MFMA needs at most 18 before its result is read by another
+// instruction), ordered after those MFMAs through the operands.
+__device__ __forceinline__ void hazard_fence(f32x16 (&o)[4]) {
+    asm volatile("s_nop 15\n\ts_nop 15" : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]));
+}
+
 template <class T, bool CAUSAL>
 __global__ __launch_bounds__(NTHREADS) void attention_fwd_kernel(AttnArgs args) {
     __shared__ __attribute__((aligned(16))) u32x4 smem[STAGES * STAGE_BYTES / 16];
@@ -241,94 +267,102 @@ __global__ __launch_bounds__(NTHREADS) void attention_fwd_kernel(AttnArgs args) 
             issue_block(t + 2, (t + 2) % STAGES);
         const int kb = t * BN;
 
-        // ---- S^T = K Q^T for both sub-tiles
-        f32x16 sacc[2][2];
+        // The block is processed as two 32-key halves (kt), each through
+        // scores, online softmax and the second product, which keeps only one
+        // half's scores live.
+        const bool need_mask = kb + BN > Sk || (CAUSAL && kb + BN - 1 > q0);
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
+        for (int kt = 0; kt < 2; ++kt) {
+            // ---- S^T = K Q^T (32 keys x 32 queries per sub-tile)
+            f32x16 sacc[2];
+            sacc[0] = f32x16{};
+            sacc[1] = f32x16{};
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-                sacc[q][kt] = f32x16{};
-#pragma unroll
-        for (int s = 0; s < 8; ++s)
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
+            for (int s = 0; s < 8; ++s) {
                 const u32x4 kf = lds_u4(st + ka[kt][s]);
 #pragma unroll
                 for (int q = 0; q < 2; ++q)
-                    sacc[q][kt] = T::mfma32(kf, qf[q][s], sacc[q][kt]);
+                    sacc[q] = T::mfma32(kf, qf[q][s], sacc[q]);
             }
 
-        // ---- online softmax (scores of key kb + 32 kt + 8 (e/4) + 4 lh + e%4)
-        const bool need_mask = kb + BN > Sk || (CAUSAL && kb + BN - 1 > q0);
-        u32x4 pf[2][4];
+            // ---- online softmax: score e of the lane is key kb + 32 kt + 8 (e/4) + 4 lh + e%4
+            u32x4 pf[2][2];
+            auto softmax = [&](auto mask_c) __attribute__((always_inline)) {
+                constexpr bool MASK = decltype(mask_c)::value;
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int qi = q0 + QW * wave + 32 * q + lc;
-            // key = kb + 4 lh + off(kt, e) with a compile-time off: visible if
-            // off < Sk - kb - 4 lh and (causal) off <= qi - kb - 4 lh
-            const int key0 = kb + 4 * lh;
-            const int tail = Sk - key0;
-            const int diag = qi - key0;
-            float mx = -INFINITY;
+                for (int q = 0; q < 2; ++q) {
+                    const int qi = q0 + QW * wave + 32 * q + lc;
+                    // visible if off < Sk - key0 and (causal) off <= qi - key0, with a
+                    // compile-time off = 8 (e/4) + e%4
+                    const int key0 = kb + 32 * kt + 4 * lh;
+                    const int tail = Sk - key0;
+                    const int diag = qi - key0;
+                    float mx = -INFINITY;
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    float v = sacc[q][kt][e];
-                    if (need_mask) {
-                        const int off = 32 * kt + 8 * (e >> 2) + (e & 3);
-                        const bool ok = off < tail && (!CAUSAL || off <= diag);
-                        v = ok ? v : -INFINITY;
-                        sacc[q][kt][e] = v;
+                    for (int e = 0; e < 16; ++e) {
+                        float v = sacc[q][e];
+                        if constexpr (MASK) {
+                            const int off = 8 * (e >> 2) + (e & 3);
+                            const bool ok = off < tail && (!CAUSAL || off <= diag);
+                            v = ok ? v : -INFINITY;
+                            sacc[q][e] = v;
+                        }
+                        mx = fmaxf(mx, v);
                     }
-                    mx = fmaxf(mx, v);
+                    mx = fmaxf(mx, lane_swap32(mx));
+                    const float m_blk = mx * c;
+                    // lazy rescaling: move the maximum only when it grew by more than 2^8
+                    if (__builtin_amdgcn_ballot_w64(m_blk > m_used[q] + RESCALE_LOG2) != 0) {
+                        const float m_new = fmaxf(m_used[q], m_blk);
+                        const float alpha =
+                            m_used[q] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_used[q] - m_new);
+                        hazard_fence(o[q]);
+#pragma unroll
+                        for (int dt = 0; dt < 4; ++dt)
+                            scale_agpr(o[q][dt], alpha);
+                        l_sum[q] *= alpha;
+                        m_used[q] = m_new;
+                    }
+                    const float m_ref = m_used[q] == -INFINITY ? 0.f : m_used[q];
+                    float sum = 0.f;
+                    uint16_t pb[16];
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[q][e], c, -m_ref));
+                        sum += pv;
+                        pb[e] = T::from_f32(pv);
+                    }
+                    l_sum[q] += sum;
+                    // key step u = 2 kt + half: the lane's 8 keys are e = 8 half + 0..7
+#pragma unroll
+                    for (int hf = 0; hf < 2; ++hf) {
+                        const int e0 = 8 * hf;
+                        pf[q][hf] = u32x4{pack2(pb[e0], pb[e0 + 1]), pack2(pb[e0 + 2], pb[e0 + 3]),
+                                          pack2(pb[e0 + 4], pb[e0 + 5]), pack2(pb[e0 + 6], pb[e0 + 7])};
+                    }
                 }
-            mx = fmaxf(mx, lane_swap32(mx));
-            const float m_blk = mx * c;
-            // lazy rescaling: move the maximum only when it grew by more than 2^8
-            if (__builtin_amdgcn_ballot_w64(m_blk > m_used[q] + RESCALE_LOG2) != 0) {
-                const float m_new = fmaxf(m_used[q], m_blk);
-                const float alpha = m_used[q] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_used[q] - m_new);
+            };
+            if (need_mask)
+                softmax(std::true_type{});
+            else
+                softmax(std::false_type{});
+
+            // ---- O^T += V^T P^T over the half's two 16-key steps
 #pragma unroll
-                for (int dt = 0; dt < 4; ++dt)
-                    o[q][dt] *= alpha;
-                l_sum[q] *= alpha;
-                m_used[q] = m_new;
-            }
-            const float m_ref = m_used[q] == -INFINITY ? 0.f : m_used[q];
-            float sum = 0.f;
-            uint16_t pb[2][16];
+            for (int hf = 0; hf < 2; ++hf) {
+                const int u = 2 * kt + hf;
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
+                for (int dt = 0; dt < 4; ++dt) {
+                    const uint32_t a0 = st + va[dt] + 4096u * (uint32_t)u;   // 16 rows of 256 bytes per step
+                    const u32x2 lo = lds_tr(a0);
+                    const u32x2 hi = lds_tr(a0 + 2048u);                    // + 8 rows
+                    const u32x4 vf = u32x4{lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const float p = __builtin_amdgcn_exp2f(fmaf(sacc[q][kt][e], c, -m_ref));
-                    sum += p;
-                    pb[kt][e] = T::from_f32(p);
+                    for (int q = 0; q < 2; ++q)
+                        o[q][dt] = T::mfma32(vf, pf[q][hf], o[q][dt]);
                 }
-            l_sum[q] += sum;
-            // key step u = 2 kt + half: the lane's 8 keys are e = 8 half + 0..7 of tile kt
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int kt = u >> 1, e0 = 8 * (u & 1);
-                pf[q][u] = u32x4{pack2(pb[kt][e0], pb[kt][e0 + 1]), pack2(pb[kt][e0 + 2], pb[kt][e0 + 3]),
-                                 pack2(pb[kt][e0 + 4], pb[kt][e0 + 5]), pack2(pb[kt][e0 + 6], pb[kt][e0 + 7])};
             }
         }
-
-        // ---- O^T += V^T P^T
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt) {
-                const uint32_t a0 = st + va[dt] + 4096u * (uint32_t)u;   // 16 rows of 256 bytes per step
-                const u32x2 lo = lds_tr(a0);
-                const u32x2 hi = lds_tr(a0 + 2048u);                    // + 8 rows
-                const u32x4 vf = u32x4{lo.x, lo.y, hi.x, hi.y};
-#pragma unroll
-                for (int q = 0; q < 2; ++q)
-                    o[q][dt] = T::mfma32(vf, pf[q][u], o[q][dt]);
-            }
 
         // next block landed (this wave's loads; the barrier covers everyone's),
         // and every wave is done with this stage before it is refilled
