@@ -6,7 +6,9 @@ bias + GELU(tanh) epilogue (inputs resident in HBM), which runs every stage of
 the tiled path: tile raster, global->LDS staging, swizzled LDS, the
 double-buffered k-loop, MFMA accumulation, the fused epilogue and the store.
 The 4096-cube (MFMA-bound, no epilogue) and the M=16 decode shape (HBM-bound,
-the skinny kernel) are timed as secondary lines in the same JSON object.
+the skinny kernel), the weight-only 4-bit product at that decode shape and the
+attention forward at the FlashAttention benchmark shape are timed as secondary
+lines in the same JSON object.
 
 Timing: W warm-up launches, then K launches back to back on torch's current
 stream (the stream tg_gemm is given), bracketed by torch.cuda.synchronize()
@@ -44,8 +46,8 @@ MAIN = "gemm_f16_8192x8192x8192_bias_gelu_tanh"
 SQUARE = "gemm_f16_4096x4096x4096"
 SKINNY = "gemm_f16_skinny_16x11008x4096"
 RAGGED = "gemm_bf16_4000x4093x4111_bias_gelu_tanh"
-KERNEL_SOURCES = ["gemm_tiled.hip", "gemm_tiled_generic.hip", "gemm_skinny.hip", "gemm_w4.hip", "tg_device.h",
-                  "tg_tile.h", "tg_launch.h", "tg_gemm_host.hip"]
+KERNEL_SOURCES = ["gemm_tiled.hip", "gemm_tiled_generic.hip", "gemm_skinny.hip", "gemm_w4.hip", "attention_fwd.hip",
+                  "tg_device.h", "tg_tile.h", "tg_launch.h", "tg_gemm_host.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -189,6 +191,45 @@ def bench_w4(torch, tg, I, steps, warmup, copies=16):
     hot = time_calls(torch, lambda i: launch(i, sets[:1]), steps, warmup)
     nbytes = tg.tg_w4_packed_bytes(K, N) + 2 * (K // G) * N + 2 * M * K + 2 * M * N
     return wq["name"], ms, hot, nbytes
+
+
+def attention_flops(B: int, H: int, D: int, Sq: int, Sk: int, causal: bool) -> int:
+    """Two products of 2*D flops per visible (query, key) pair: 4*B*H*D*pairs;
+    with the causal mask (Sq == Sk) a query i sees keys 0..i."""
+    pairs = Sq * (Sq + 1) // 2 if causal else Sq * Sk
+    return 4 * B * H * D * pairs
+
+
+def bench_attention(torch, tg, I, steps, warmup):
+    """The attention forward at the benchmark shape, without and with the
+    causal mask: per-launch time and TFLOP/s."""
+    wa = I.ATTN_WORKLOAD
+    Bn, H, S, D, dt = wa["batch"], wa["heads"], wa["seq"], wa["head_dim"], wa["dtype"]
+    tdt = torch.float16 if dt == I.F16 else torch.bfloat16
+
+    def dev(seed):
+        bits = I.random_bits((Bn, S, H, D), wa["dist"], dt, seed)
+        return torch.from_numpy(bits.view(np.int16).reshape(Bn, S, H, D).copy()).view(tdt).cuda()
+
+    Q, K, V = (dev(s) for s in wa["seeds"])
+    O = torch.empty_like(Q)
+    handle = torch.cuda.current_stream().cuda_stream
+    out = {}
+    for causal in (False, True):
+        def launch(i, c=int(causal)):
+            st = tg.tg_attention_fwd(Bn, S, S, H, D, dt, Q.data_ptr(), K.data_ptr(), V.data_ptr(), c, 0.0,
+                                     O.data_ptr(), handle)
+            if st != tg.TG_OK:
+                raise RuntimeError(f"tg_attention_fwd failed: {tg.tg_status_string(st)}")
+
+        ms = time_calls(torch, launch, steps, warmup)
+        tf = attention_flops(Bn, H, D, S, S, causal) / (ms * 1e-3) / 1e12
+        key = "causal" if causal else "non_causal"
+        out[key] = {"us_per_launch": round(ms * 1e3, 2), "TFLOP/s": round(tf, 2),
+                    "frac_mfma_peak": round(tf / PEAK_MFMA_F16_TFLOPS, 4),
+                    "traffic": measured_traffic(f"{wa['name']} {key.replace('_', '-')}")}
+        log(f"{wa['name']} causal={causal}: {ms * 1e3:.1f} us, {tf:.1f} TFLOP/s")
+    return wa["name"], out
 
 
 def path_of(tg, w, operand_set):
@@ -382,6 +423,10 @@ def main() -> int:
                            "fusion_speedup": round(ms3u / ms3, 3),
                            "unfused_extra_bytes": EPILOGUE_PASSES[w3.epilogue] * 4 * w3.M * w3.N}
         del sets3
+        torch.cuda.empty_cache()
+        log("secondary: attention forward (FlashAttention benchmark shape)")
+        aname, ares = bench_attention(torch, tg, I, max(args.steps // 2, 20), args.warmup)
+        sec[aname] = ares
         sec["epilogue_fusion"] = fusion
         result["secondary"] = sec
 

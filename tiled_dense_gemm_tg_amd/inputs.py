@@ -164,3 +164,10 @@ def w4_weights(K: int, N: int, seed: int) -> np.ndarray:
 # M, N, K, with 128-row scale groups.
 W4_WORKLOAD = dict(name="gemm_w4_f16_16x11008x4096_g128", M=16, N=11008, K=4096, group=128, dtype=F16,
                    a_dist=("normal", 0.0, 1.0), scale_dist=("uniform", 0.001, 0.01), seeds=(6001, 6002, 6003))
+
+
+# The attention forward at the shape of the FlashAttention pages' benchmark:
+# batch 1, 32 heads of width 128, 4096 queries and keys, standard-normal
+# Q, K and V, timed without and with the causal mask.
+ATTN_WORKLOAD = dict(name="attention_fwd_f16_b1_h32_s4096_d128", batch=1, heads=32, seq=4096, head_dim=128,
+                     dtype=F16, dist=("normal", 0.0, 1.0), seeds=(7001, 7002, 7003))
