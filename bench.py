@@ -193,6 +193,92 @@ def bench_w4(torch, tg, I, steps, warmup, copies=16):
     return wq["name"], ms, hot, nbytes
 
 
+TILE_CONFIGS = {"256x256": 1, "256x128": 2, "128x256": 3, "128x128": 4}   # tg_tiles values
+
+
+def time_tiled(torch, tg, M, N, K, dtype, epi, A, B, bias, C, cfg, steps, warmup):
+    """Per-launch time (ms) of tg_gemm_tiled with tile configuration cfg
+    (0: the library's choice, through tg_gemm)."""
+    handle = torch.cuda.current_stream().cuda_stream
+    a, b, bi, c = A.data_ptr(), B.data_ptr(), bias.data_ptr() if bias is not None else None, C.data_ptr()
+
+    def launch(i):
+        st = (tg.tg_gemm_tiled(cfg, M, N, K, dtype, a, b, bi, epi, c, handle) if cfg
+              else tg.tg_gemm(M, N, K, dtype, a, b, bi, epi, c, handle))
+        if st != tg.TG_OK:
+            raise RuntimeError(f"tg_gemm_tiled failed: {tg.tg_status_string(st)}")
+
+    return time_calls(torch, launch, steps, warmup)
+
+
+def bench_tile_choice(torch, tg, I, steps, warmup):
+    """Every tile configuration, and the library's own choice, on the shape
+    classes the choice is for."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = {}
+    for name, w in I.TILE_WORKLOADS.items():
+        _, sets = device_operands(torch, I, w)
+        A, B, bias, C = sets[0]
+        flops = gemm_flops(w.M, w.N, w.K)
+        per = {}
+        for cname, cfg in TILE_CONFIGS.items():
+            per[cname] = time_tiled(torch, tg, w.M, w.N, w.K, w.dtype, w.epilogue, A, B, bias, C, cfg, steps, warmup)
+        ms_auto = time_tiled(torch, tg, w.M, w.N, w.K, w.dtype, w.epilogue, A, B, bias, C, 0, steps, warmup)
+        st, auto = tg.tg_gemm_tiles_plan(w.M, w.N, w.K, cus)
+        best = min(per, key=per.get)
+        out[name] = {"auto": tg.TILES_NAMES.get(auto, "?"), "auto_us": round(ms_auto * 1e3, 2),
+                     "auto_TFLOP/s": round(flops / (ms_auto * 1e-3) / 1e12, 1),
+                     "per_config_us": {k: round(v * 1e3, 2) for k, v in per.items()},
+                     "fastest": best, "auto_vs_fastest": round(per[best] / ms_auto, 3),
+                     "speedup_vs_256x256": round(per["256x256"] / ms_auto, 3)}
+        log(f"{name}: auto {tg.TILES_NAMES.get(auto)} {ms_auto * 1e3:.1f} us, fastest {best} "
+            f"{per[best] * 1e3:.1f} us, 256x256 {per['256x256'] * 1e3:.1f} us")
+        del sets, A, B, bias, C
+        torch.cuda.empty_cache()
+    return out
+
+
+def tile_sweep(torch, tg, I, steps, warmup):
+    """Measures the per-CU throughput of each tile configuration with one
+    tile per CU (r_single) and with many (r_full), relative to r_full of the
+    256 x 256 tile: the inputs of the library's tile-choice cost model.
+    Operands are normal(0, 0.1) fp16 drawn on the device (timing only)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(20001)
+
+    def operands(M, N, K):
+        A = (torch.randn((M, K), generator=gen, device="cuda") * 0.1).half()
+        B = (torch.randn((K, N), generator=gen, device="cuda") * 0.1).half()
+        return A, B, torch.empty((M, N), dtype=torch.float16, device="cuda")
+
+    res = {"cus": cus, "full": {}, "single": {}}
+    K = 8192
+    A, B, C = operands(8192, 8192, K)
+    for cname, cfg in TILE_CONFIGS.items():
+        ms = time_tiled(torch, tg, 8192, 8192, K, 0, 0, A, B, None, C, cfg, steps, warmup)
+        res["full"][cname] = {"us": round(ms * 1e3, 1), "TFLOP/s": round(gemm_flops(8192, 8192, K) / ms / 1e9, 1)}
+        log(f"sweep full 8192x8192x{K} {cname}: {ms * 1e3:.1f} us")
+    del A, B, C
+    tm = 16
+    tn = max(cus // tm, 1)
+    for cname, cfg in TILE_CONFIGS.items():
+        bm, bn = (int(v) for v in cname.split("x"))
+        M, N = tm * bm, tn * bn
+        A, B, C = operands(M, N, K)
+        ms = time_tiled(torch, tg, M, N, K, 0, 0, A, B, None, C, cfg, steps, warmup)
+        res["single"][cname] = {"shape": f"{M}x{N}x{K}", "us": round(ms * 1e3, 1),
+                                "TFLOP/s": round(gemm_flops(M, N, K) / ms / 1e9, 1)}
+        log(f"sweep single {M}x{N}x{K} {cname}: {ms * 1e3:.1f} us")
+        del A, B, C
+    ref = res["full"]["256x256"]["TFLOP/s"]
+    res["rates"] = {c: {"r_single": round(res["single"][c]["TFLOP/s"] / ref, 3),
+                        "r_full": round(res["full"][c]["TFLOP/s"] / ref, 3)} for c in TILE_CONFIGS}
+    res["shape_classes"] = bench_tile_choice(torch, tg, I, steps, warmup)
+    torch.cuda.empty_cache()
+    return res
+
+
 def attention_flops(B: int, H: int, D: int, Sq: int, Sk: int, causal: bool) -> int:
     """Two products of 2*D flops per visible (query, key) pair: 4*B*H*D*pairs;
     with the causal mask (Sq == Sk) a query i sees keys 0..i."""
@@ -295,6 +381,8 @@ def main() -> int:
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--workload", default=MAIN, help="workload timed as the main line (for profiling runs)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="only time every tile configuration of the tiled family (prints its own JSON line)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run torch's device copy of MIB MiB, 10 times (to scale HBM byte counters)")
     args = ap.parse_args()
@@ -322,6 +410,10 @@ def main() -> int:
     tg.load_library()
     props = torch.cuda.get_device_properties(0)
     log(f"device {props.name} ({getattr(props, 'gcnArchName', '?')}), {props.multi_processor_count} CUs")
+    if args.sweep:
+        print(json.dumps({"tile_sweep": tile_sweep(torch, tg, I, max(args.steps // 2, 20), args.warmup)}),
+              flush=True)
+        return 0
 
     w = I.WORKLOADS[args.workload]
     log(f"main workload {w.name}: generating inputs")
@@ -424,6 +516,8 @@ def main() -> int:
                            "unfused_extra_bytes": EPILOGUE_PASSES[w3.epilogue] * 4 * w3.M * w3.N}
         del sets3
         torch.cuda.empty_cache()
+        log("secondary: tile configurations on the mid-size shape classes")
+        sec["tile_choice"] = bench_tile_choice(torch, tg, I, max(args.steps // 2, 20), args.warmup)
         log("secondary: attention forward (FlashAttention benchmark shape)")
         aname, ares = bench_attention(torch, tg, I, max(args.steps // 2, 20), args.warmup)
         sec[aname] = ares

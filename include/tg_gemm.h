@@ -78,8 +78,10 @@ typedef enum {
  *   TG_PATH_SKINNY         M <= 16 (the decode-shaped product): streams B from
  *                          HBM once; needs K % 8 == 0, N % 4 == 0, A 16-byte
  *                          aligned, B, C and bias 8-byte aligned.
- *   TG_PATH_TILED          256x256 MFMA tiles staged through LDS by 16-byte
- *                          direct loads; any shape and alignment as long as A
+ *   TG_PATH_TILED          MFMA tiles (256x256 by default; see tg_tiles for
+ *                          the other sizes and how one is chosen) staged
+ *                          through LDS by 16-byte direct loads; any shape
+ *                          and alignment as long as A
  *                          and B, each padded to whole tiles, stay below 2 GiB
  *                          less 64 KiB: 2 (M + 256) K and 2 (K + 32) (N + 256)
  *                          both below 2^31 - 65536.  Fastest with K % 8 == 0,
@@ -132,6 +134,51 @@ tg_status tg_gemm_path(tg_path path, int64_t M, int64_t N, int64_t K, tg_dtype d
 tg_status tg_gemm_plan(int64_t M, int64_t N, int64_t K, tg_dtype dtype,
                        const void *A, const void *B, const void *bias, tg_epilogue epilogue,
                        const void *C, tg_path *path_out);
+
+/*
+ * Tile configurations of the TG_PATH_TILED family, BM x BN (rows by columns
+ * of C per workgroup).  The TileLang pages leave the tile size to the user
+ * and tune it per shape ("Designing high-performance GPU kernels with
+ * TileLang", "Performance Analysis and Autotuning": a benchmark sweep over
+ * block sizes picks the winner, most of all for non-standard dimensions;
+ * "TileLang: writing LLM GPU kernels by thinking in tiles", section 6: tile
+ * recommendation from hardware information and heuristics).  Here every
+ * configuration is one instance of the same kernel; TG_TILES_AUTO (what
+ * tg_gemm uses) takes the one a cost model built from a measured sweep
+ * predicts fastest: the number of rounds of tiles the persistent grid needs
+ * on the device's compute units, times the time of one round, which is the
+ * tile's size over that configuration's measured per-CU throughput.  The
+ * 256x256 tile is the most efficient per CU; the smaller ones keep more CUs
+ * busy when the output has few 256x256 tiles (the 128x128 tile runs two
+ * workgroups per CU).
+ */
+typedef enum {
+    TG_TILES_AUTO = 0,
+    TG_TILES_256x256 = 1,
+    TG_TILES_256x128 = 2,
+    TG_TILES_128x256 = 3,
+    TG_TILES_128x128 = 4
+} tg_tiles;
+
+/*
+ * As tg_gemm_path(TG_PATH_TILED, ...) with tile configuration `tiles`
+ * (TG_TILES_AUTO: the library's choice).  TG_ERR_INVALID_ARG for an unknown
+ * configuration, TG_ERR_UNSUPPORTED when the shape is outside the
+ * TG_PATH_TILED limit; otherwise the same argument rules, degenerate shapes
+ * and results (to the tolerance of fp32 accumulation in a different order;
+ * bit-identical on integer-valued inputs) as tg_gemm.  Meant for tests and
+ * for tuning sweeps.
+ */
+tg_status tg_gemm_tiled(tg_tiles tiles, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
+                        const void *A, const void *B, const void *bias, tg_epilogue epilogue,
+                        void *C, void *stream);
+
+/*
+ * The configuration TG_TILES_AUTO picks for an M x N x K product on a device
+ * with num_cu compute units (num_cu <= 0: 256, an MI355X), in *tiles_out.
+ * TG_ERR_INVALID_ARG for negative sizes or a NULL tiles_out.  Pure host code.
+ */
+tg_status tg_gemm_tiles_plan(int64_t M, int64_t N, int64_t K, int num_cu, tg_tiles *tiles_out);
 
 /*
  * Elementwise epilogue steps as passes of their own over a matrix in device

@@ -37,8 +37,9 @@ def to_bits(t) -> np.ndarray:
 
 
 def run(M, N, K, dtype, A_bits, B_bits, bias_bits=None, epilogue=I.EPI_NONE, path=tg.TG_PATH_AUTO,
-        out=None, stream=None, expect_path=None):
-    """Runs one GEMM through the C interface; returns the output tensor."""
+        out=None, stream=None, expect_path=None, tiles=tg.TG_TILES_AUTO):
+    """Runs one GEMM through the C interface (tg_gemm_path, or tg_gemm_tiled
+    when a tile configuration is given); returns the output tensor."""
     import torch
     dev = "cuda"
     A = to_device(A_bits.reshape(M, K), dtype) if M * K else torch.empty((M, K), dtype=torch_dtype(dtype), device=dev)
@@ -51,7 +52,7 @@ def run(M, N, K, dtype, A_bits, B_bits, bias_bits=None, epilogue=I.EPI_NONE, pat
                                 bias.data_ptr() if bias is not None else None, epilogue, out.data_ptr())
         assert st == tg.TG_OK and p == expect_path, (st, tg.PATH_NAMES.get(p))
     epi_name = {I.EPI_NONE: "none", I.EPI_BIAS: "bias", I.EPI_BIAS_GELU_TANH: "bias_gelu_tanh"}[epilogue]
-    tg.gemm(A, B, bias, epi_name, out=out, path=path, stream=stream)
+    tg.gemm(A, B, bias, epi_name, out=out, path=path, stream=stream, tiles=tiles)
     torch.cuda.synchronize()
     return out
 

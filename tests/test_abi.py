@@ -248,3 +248,50 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(tg, "LIBRARY", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         tg.load_library()
+
+
+# ------------------------------------------------------------ tile configurations
+
+def test_tiled_entry_point_checks_arguments(lib):
+    for bad in (-1, 5, 99):
+        assert tg.tg_gemm_tiled(bad, 64, 64, 64, I.F16, PA, PB, None, I.EPI_NONE, PC, None) == tg.TG_ERR_INVALID_ARG
+    # the tiled family's size limit applies to every configuration
+    for cfg in (tg.TG_TILES_AUTO, tg.TG_TILES_128x128):
+        assert tg.tg_gemm_tiled(cfg, 130812, 256, 8192, I.F16, PA, PB, None, I.EPI_NONE, PC, None) \
+            == tg.TG_ERR_UNSUPPORTED
+    # argument rules are tg_gemm's: bias with no epilogue, C overlapping A
+    assert tg.tg_gemm_tiled(tg.TG_TILES_256x128, 64, 64, 64, I.F16, PA, PB, PBIAS, I.EPI_NONE, PC, None) \
+        == tg.TG_ERR_INVALID_ARG
+    assert tg.tg_gemm_tiled(tg.TG_TILES_128x256, 64, 64, 64, I.F16, PA, PB, None, I.EPI_NONE, PA + 64, None) \
+        == tg.TG_ERR_INVALID_ARG
+    # nothing to compute: a no-op for every configuration, without a GPU
+    for cfg in tg.TILES_NAMES:
+        assert tg.tg_gemm_tiled(cfg, 0, 64, 64, I.F16, None, None, None, I.EPI_NONE, None, None) == tg.TG_OK
+
+
+def test_tiles_plan_checks_arguments(lib):
+    assert lib.tg_gemm_tiles_plan(64, 64, 64, 256, None) == tg.TG_ERR_INVALID_ARG
+    assert tg.tg_gemm_tiles_plan(-1, 64, 64, 256)[0] == tg.TG_ERR_INVALID_ARG
+    assert tg.tg_gemm_tiles_plan(64, 64, -1, 256)[0] == tg.TG_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("M,N,K,cfg", [
+    (8192, 8192, 8192, tg.TG_TILES_256x256),    # four 256x256 tiles per CU: the most efficient tile
+    (4096, 4096, 4096, tg.TG_TILES_256x256),    # exactly one per CU
+    (4000, 4093, 4111, tg.TG_TILES_256x256),
+    (2048, 2048, 2048, tg.TG_TILES_128x128),    # 64 tiles of 256x256 would leave 3/4 of the CUs idle
+    (1024, 1024, 8192, tg.TG_TILES_128x128),
+    (1000, 3000, 6000, tg.TG_TILES_128x128),
+    (512, 11008, 4096, tg.TG_TILES_128x256),    # 172 tiles either way; 128x256 is the faster of the two
+    (17, 11008, 4096, tg.TG_TILES_128x128),     # one row of tiles: the smallest tile wastes least
+])
+def test_tiles_plan_on_an_mi355x(lib, M, N, K, cfg):
+    """The choice on 256 CUs for the measured shape classes."""
+    assert tg.tg_gemm_tiles_plan(M, N, K, 256) == (tg.TG_OK, cfg)
+    assert tg.tg_gemm_tiles_plan(M, N, K, 0) == (tg.TG_OK, cfg)       # 0: an MI355X's 256 CUs assumed
+
+
+def test_tiles_plan_follows_the_cu_count(lib):
+    # with 4x the CUs the 4096-cube has too few 256x256 tiles; with 1/4 the 2048-cube has enough
+    assert tg.tg_gemm_tiles_plan(4096, 4096, 4096, 1024)[1] != tg.TG_TILES_256x256
+    assert tg.tg_gemm_tiles_plan(2048, 2048, 2048, 64)[1] == tg.TG_TILES_256x256

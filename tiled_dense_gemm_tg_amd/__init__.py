@@ -35,7 +35,15 @@ PATH_NAMES = {TG_PATH_AUTO: "auto", TG_PATH_TILED: "tiled", TG_PATH_TILED_GENERI
 TG_EW_BIAS_ADD = 0
 TG_EW_GELU_TANH = 1
 
-EXPORTED = ("tg_gemm", "tg_gemm_path", "tg_gemm_plan", "tg_elementwise", "tg_gemm_unfused", "tg_w4_packed_bytes",
+TG_TILES_AUTO = 0
+TG_TILES_256x256 = 1
+TG_TILES_256x128 = 2
+TG_TILES_128x256 = 3
+TG_TILES_128x128 = 4
+TILES_NAMES = {TG_TILES_AUTO: "auto", TG_TILES_256x256: "256x256", TG_TILES_256x128: "256x128",
+               TG_TILES_128x256: "128x256", TG_TILES_128x128: "128x128"}
+
+EXPORTED = ("tg_gemm", "tg_gemm_path", "tg_gemm_plan", "tg_gemm_tiled", "tg_gemm_tiles_plan", "tg_elementwise", "tg_gemm_unfused", "tg_w4_packed_bytes",
             "tg_w4_pack", "tg_gemm_w4", "tg_attention_fwd", "tg_status_string", "tg_version")
 
 _lib = None
@@ -67,6 +75,10 @@ def load_library():
     lib.tg_gemm_path.restype = ci
     lib.tg_gemm_plan.argtypes = [i64, i64, i64, ci, vp, vp, vp, ci, vp, ctypes.POINTER(ci)]
     lib.tg_gemm_plan.restype = ci
+    lib.tg_gemm_tiled.argtypes = [ci, i64, i64, i64, ci, vp, vp, vp, ci, vp, vp]
+    lib.tg_gemm_tiled.restype = ci
+    lib.tg_gemm_tiles_plan.argtypes = [i64, i64, i64, ci, ctypes.POINTER(ci)]
+    lib.tg_gemm_tiles_plan.restype = ci
     lib.tg_elementwise.argtypes = [ci, i64, i64, ci, vp, vp, vp, vp]
     lib.tg_elementwise.restype = ci
     lib.tg_gemm_unfused.argtypes = [i64, i64, i64, ci, vp, vp, vp, ci, vp, vp]
@@ -100,6 +112,17 @@ def tg_gemm_plan(M, N, K, dtype, A, B, bias, epilogue, C):
     """Returns (status, path) without touching the GPU."""
     out = ctypes.c_int(-1)
     st = load_library().tg_gemm_plan(M, N, K, dtype, A, B, bias, epilogue, C, ctypes.byref(out))
+    return st, out.value
+
+
+def tg_gemm_tiled(tiles, M, N, K, dtype, A, B, bias, epilogue, C, stream) -> int:
+    return load_library().tg_gemm_tiled(tiles, M, N, K, dtype, A, B, bias, epilogue, C, stream)
+
+
+def tg_gemm_tiles_plan(M, N, K, num_cu=0):
+    """Returns (status, tile configuration TG_TILES_AUTO would use)."""
+    out = ctypes.c_int(-1)
+    st = load_library().tg_gemm_tiles_plan(M, N, K, num_cu, ctypes.byref(out))
     return st, out.value
 
 
@@ -139,13 +162,15 @@ _EPI = {"none": EPI_NONE, "bias": EPI_BIAS, "bias_gelu_tanh": EPI_BIAS_GELU_TANH
 
 
 def gemm(A, B, bias=None, epilogue: str = "none", out=None, path: int = TG_PATH_AUTO, stream=None,
-         unfused: bool = False):
+         unfused: bool = False, tiles: int = TG_TILES_AUTO):
     """epilogue(A @ B [+ bias]) on torch device tensors (fp16 or bf16, row-major).
 
     Returns ``out`` (allocated when not given).  Runs on ``stream`` or torch's
     current stream; asynchronous like any torch op.  ``unfused=True`` calls
     tg_gemm_unfused (the product, then the epilogue steps as separate passes;
-    ``path`` must then be TG_PATH_AUTO).
+    ``path`` must then be TG_PATH_AUTO).  A ``tiles`` configuration other than
+    TG_TILES_AUTO calls tg_gemm_tiled (the tiled family with that tile size;
+    ``path`` must then be TG_PATH_AUTO or TG_PATH_TILED).
     """
     import torch
     if A.dtype not in (torch.float16, torch.bfloat16):
@@ -170,11 +195,16 @@ def gemm(A, B, bias=None, epilogue: str = "none", out=None, path: int = TG_PATH_
         raise ValueError("out has the wrong shape or dtype")
     dtype = F16 if A.dtype == torch.float16 else BF16
     s = (stream if stream is not None else torch.cuda.current_stream(A.device)).cuda_stream
+    if tiles != TG_TILES_AUTO and (unfused or path not in (TG_PATH_AUTO, TG_PATH_TILED)):
+        raise ValueError("a tile configuration applies to the tiled family only")
     if unfused:
         if path != TG_PATH_AUTO:
             raise ValueError("the unfused form chooses its own kernel family")
         st = tg_gemm_unfused(M, N, K, dtype, A.data_ptr(), B.data_ptr(),
                              bias.data_ptr() if bias is not None else None, epi, out.data_ptr(), s)
+    elif tiles != TG_TILES_AUTO:
+        st = tg_gemm_tiled(tiles, M, N, K, dtype, A.data_ptr(), B.data_ptr(),
+                           bias.data_ptr() if bias is not None else None, epi, out.data_ptr(), s)
     else:
         st = tg_gemm_path(path, M, N, K, dtype, A.data_ptr(), B.data_ptr(),
                           bias.data_ptr() if bias is not None else None, epi, out.data_ptr(), s)

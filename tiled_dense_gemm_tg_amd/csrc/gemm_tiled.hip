@@ -11,16 +11,19 @@
 // multiplied.  Sizes and mechanics are chosen for CDNA4 rather than taken from
 // the pages' NVIDIA example:
 //
-//   * tile 256 x 256, 256 threads = 4 wave64s, each owning a 128 x 128 quarter
-//     of C as 4 x 4 v_mfma_f32_32x32x16 accumulators (256 fp32 values per lane,
-//     in AGPRs);
-//   * k-slices of 32 in a ring of 4 LDS stages (4 x 32 KB of the 160 KB LDS),
-//     filled by buffer loads that write LDS directly (buffer_load_dwordx4 ...
-//     lds): no staging registers, no LDS store instructions, and each slice is
-//     requested two slices before it is used, so a whole slice of MFMA work
-//     hides the memory latency twice over; one barrier per slice;
-//   * A is staged as [256 m][32 k] (k-contiguous, what a 16-bit MFMA operand
-//     holds per lane) and read with ds_read_b128; B stays [32 k][256 n] as in
+//   * tile BM x BN with BM, BN in {128, 256} (the tile configuration is a
+//     template parameter; the host picks one per shape), 256 threads = 4
+//     wave64s in a 2 x 2 grid, each owning a BM/2 x BN/2 block of C as
+//     v_mfma_f32_32x32x16 accumulators in AGPRs (256 fp32 values per lane at
+//     256 x 256);
+//   * k-slices of 32 in a ring of 4 LDS stages (4 x 32 KB of the 160 KB LDS at
+//     256 x 256), filled by buffer loads that write LDS directly
+//     (buffer_load_dwordx4 ... lds): no staging registers, no LDS store
+//     instructions, and each slice is requested two slices before it is used,
+//     so a whole slice of MFMA work hides the memory latency twice over; one
+//     barrier per slice;
+//   * A is staged as [BM m][32 k] (k-contiguous, what a 16-bit MFMA operand
+//     holds per lane) and read with ds_read_b128; B stays [32 k][BN n] as in
 //     memory and its MFMA fragments come from ds_read_b64_tr_b16, which hands
 //     each lane one column of a 4 x 16 block of 16-bit values (lane i of a
 //     16-lane group gets element i%4 of the 8 bytes addressed by lane
@@ -32,9 +35,10 @@
 //   * MFMA fragments are double-buffered in registers: the reads for the next
 //     k-step are issued between the MFMAs of the current one;
 //   * the MFMA takes the B fragment first, so each lane ends up with 4
-//     consecutive output columns of a row, stored with one 8-byte write after
-//     the fused bias + GELU(tanh) epilogue (tg_tile.h);
-//   * XCD-aware grouped raster of the tiles (tg_tile.h).
+//     consecutive output columns of a row; after the fused bias + GELU(tanh)
+//     epilogue the tile goes through LDS and leaves as row segments;
+//   * persistent grid with an XCD-aware grouped raster of the tiles
+//     (tg_tile.h); the smaller tiles fit two workgroups per CU.
 //
 // The direct loads are issued from inline assembly and their completion is
 // awaited with explicit vmcnt waits: the compiler cannot tell that the LDS
@@ -57,19 +61,40 @@
 namespace tg {
 namespace {
 
-using tile::BM;
-using tile::BN;
 using tile::NTHREADS;
 constexpr int BK = 32;
 constexpr int STAGES = 4;
-constexpr int A_BYTES = BM * BK * 2;              // 16 KB: [256 m][32 k]
-constexpr int B_BYTES = BK * BN * 2;              // 16 KB: [32 k][256 n]
-constexpr int STAGE_BYTES = A_BYTES + B_BYTES;    // 32 KB
 constexpr uint32_t OOB_BUMP = 0x80000000u;        // + offset < 2^31 - 64 KiB -> beyond the operand's buffer
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Everything that follows from the tile size.  Waves form a 2 x 2 grid over
+// the tile; each owns WM x WN = (BM/2) x (BN/2) of C as I x J accumulators
+// of 32 x 32.  Per k-slice and wave: QA direct loads of A (16 rows of 64
+// bytes each) and QB of B (1 KB = RB k-rows each).
+template <int BM_, int BN_>
+struct Cfg {
+    static constexpr int BM = BM_, BN = BN_;
+    static_assert((BM == 128 || BM == 256) && (BN == 128 || BN == 256), "tile sizes");
+    static constexpr int WM = BM / 2, WN = BN / 2;
+    static constexpr int I = WM / 32, J = WN / 32;
+    static constexpr int A_BYTES = BM * BK * 2;             // [BM m][32 k]
+    static constexpr int B_BYTES = BK * BN * 2;             // [32 k][BN n]
+    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+    static constexpr int B_ROW = 2 * BN;                    // bytes per k-row of the B stage
+    static constexpr int CPR = BN / 8;                      // 16-byte chunks per B row (and per C row)
+    static constexpr int QA = BM / 64, QB = BN / 64;
+    static constexpr int D = QA + QB;                       // direct loads per slice per wave
+    static constexpr int RB = 512 / BN;                     // B k-rows per direct load
+    static constexpr int A_ROWS_PER_WAVE = BM / 4;
+    static constexpr int READS = I + 2 * J;                 // fragment reads per k-step
+    static constexpr int MFMAS = I * J;                     // MFMAs per k-step
+    static constexpr int OCCUPANCY = (STAGES * STAGE_BYTES <= 80 * 1024) ? 2 : 1;   // workgroups per CU
+    static_assert(D % 2 == 0, "loads split over the two k-steps of a slice");
+    static_assert(BM * BN * 2 <= STAGES * STAGE_BYTES, "the C tile fits the stage ring");
+};
 
 // A row = 32 k = 4 chunks of 16 B.  A fragment read takes one logical chunk
 // from 32 consecutive rows; with this swizzle any 8 consecutive rows of one
@@ -78,11 +103,23 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 // passes conflict free.
 __device__ __forceinline__ int a_swz(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
 
-// B row = 256 n = 32 chunks.  A transposed read pass touches 4 consecutive
-// k-rows (k % 4 = 0..3) and 2 (32-bank pass) or 4 (64-bank pass) adjacent
-// chunks; g(k%4) = {0, 10, 4, 14} gives those 4 rows distinct bits 1-2 and
-// distinct bits 2-3 of the slot, so every pass hits distinct banks.
+// B row = BN n = 32 or 16 chunks.  A transposed read pass touches 4
+// consecutive k-rows (k % 4 = 0..3) and 2 (32-bank pass) or 4 (64-bank pass)
+// adjacent chunks; g(k%4) = {0, 10, 4, 14} gives those 4 rows distinct bits
+// 1-2 and distinct bits 2-3 of the slot, so every pass hits distinct banks
+// (the 64 banks span 256 bytes, so only the chunk index mod 16 matters).
 __device__ __forceinline__ int b_swz(int k) { return ((k & 1) ? 10 : 0) ^ ((k & 2) ? 4 : 0); }
+
+// Chunk swizzle of the C tile staged in LDS for the store: the 32 rows one
+// epilogue write instruction touches land on different chunks (16-chunk
+// rows: rows r and r + 16 differ in bit 0 of the pattern).
+template <int CPR>
+__device__ __forceinline__ uint32_t c_swz(int row) {
+    if constexpr (CPR == 32)
+        return (uint32_t)(row & 31);
+    else
+        return (uint32_t)((row ^ (row >> 4)) & 15);
+}
 
 __device__ __forceinline__ uint32_t lds_address(const void *p) {
     return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p;
@@ -115,62 +152,68 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// Per-lane addressing of the 8 direct loads that fill one stage.  Wave w,
-// lane L, load q = 0..3:
-//   A: tile rows 64 w + 16 q + L/4, physical chunk L%4 -> logical chunk
-//      c = L%4 ^ a_swz(row) (8 k); destination stage + 4096 w + 1024 q;
-//   B: k-rows 8 w + 2 q + L/32, physical chunk L%32 -> logical chunk
-//      c = L%32 ^ b_swz(k) (8 n); destination stage + 16 KB + 4096 w + 1024 q.
-// The four loads of one operand share m0 (stage + 4096 w, or + 16 KB) and
-// reach their destination through the instruction offset 1024 q, which is
-// also added to the memory offset; the lane offsets subtract it back.  So
-// that they stay non-negative, the buffers start 4 KB before the operands
+// Per-lane addressing of the D direct loads that fill one stage.  Wave w,
+// lane L:
+//   A load q < QA: tile rows BM/4 w + 16 q + L/4, physical chunk L%4 ->
+//      logical chunk c = L%4 ^ a_swz(row) (8 k); destination
+//      stage + 16 BM w + 1024 q;
+//   B load q < QB: k-row 8 w + RB q + L/CPR, physical chunk L%CPR ->
+//      logical chunk c = L%CPR ^ b_swz(k) (8 n); destination
+//      stage + A_BYTES + 16 BN w + 1024 q.
+// The loads of one operand share m0 (their q = 0 destination) and reach
+// their destination through the instruction offset 1024 q, which is also
+// added to the memory offset; the lane offsets subtract it back.  So that
+// they stay non-negative, the buffers start 4 KB before the operands
 // (offsets are operand offsets + 4096) and are 4 KB longer.
+template <class C>
 struct Dma {
     static constexpr uint32_t SHIFT = 4096;
     i32x4 ra, rb;
-    uint32_t a_off[4];   // buffer offset of this lane's A chunk for load q, k0 = 0, minus 1024 q
-    int a_k;             // first k of the lane's A chunk within the slice
-    uint32_t b_off[4];   // buffer offset of this lane's B chunk for load q, k0 = 0, minus 1024 q
-    int b_k[4];          // k-row of load q within the slice
-    uint32_t b_row;      // bytes per row of B
-    uint32_t m0_a, m0_b; // LDS destinations of load q = 0 in stage 0
+    uint32_t a_off[C::QA];   // buffer offset of this lane's A chunk for load q, k0 = 0, minus 1024 q
+    int a_k;                 // first k of the lane's A chunk within the slice
+    uint32_t b_off[C::QB];   // buffer offset of this lane's B chunk for load q, k0 = 0, minus 1024 q
+    int b_k[C::QB];          // k-row of load q within the slice
+    uint32_t b_row;          // bytes per row of B
+    uint32_t m0_a, m0_b;     // LDS destinations of load q = 0 in stage 0
     int K;
 
     __device__ __forceinline__ Dma(const GemmArgs &g, int m0, int n0, int wave, int lane, uint32_t lds0) {
         ra = rsrc_words((const char *)g.A - SHIFT, 2u * (uint32_t)g.M * (uint32_t)g.K + SHIFT);
         rb = rsrc_words((const char *)g.B - SHIFT, 2u * (uint32_t)g.K * (uint32_t)g.N + SHIFT);
         K = g.K;
-        const int arow = 64 * wave + (lane >> 2);
+        const int arow = C::A_ROWS_PER_WAVE * wave + (lane >> 2);
         const int ac = (lane & 3) ^ a_swz(lane >> 2);
         a_k = 8 * ac;
         b_row = 2u * (uint32_t)g.N;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < C::QA; ++q)
             a_off[q] = SHIFT - 1024u * q + 2u * ((uint32_t)(m0 + arow + 16 * q) * (uint32_t)g.K + (uint32_t)a_k);
-            const int k = 8 * wave + 2 * q + (lane >> 5);
-            const int c = (lane & 31) ^ b_swz(k);
+#pragma unroll
+        for (int q = 0; q < C::QB; ++q) {
+            const int k = 8 * wave + C::RB * q + (int)((unsigned)lane / C::CPR);
+            const int c = (int)((unsigned)lane % C::CPR) ^ b_swz(k);
             b_k[q] = k;
             b_off[q] = SHIFT - 1024u * q + (uint32_t)k * b_row + 2u * (uint32_t)(n0 + 8 * c);
         }
-        m0_a = lds0 + 4096u * (uint32_t)wave;
-        m0_b = lds0 + (uint32_t)A_BYTES + 4096u * (uint32_t)wave;
+        m0_a = lds0 + 16u * C::BM * (uint32_t)wave;
+        m0_b = lds0 + (uint32_t)C::A_BYTES + 16u * C::BN * (uint32_t)wave;
     }
 
-    // Direct load d (0..7) of k-slice kt into LDS stage st: A load d for
-    // d < 4, B load d - 4 otherwise.  FULL: the slice lies inside [0, K), so
+    // Direct load d (0..D-1) of k-slice kt into LDS stage st: A load d for
+    // d < QA, B load d - QA otherwise.  FULL: the slice lies inside [0, K), so
     // no lane needs the K mask (only the last slice can be partial).
-    template <bool FULL, int D>
+    template <bool FULL, int DI>
     __device__ __forceinline__ void issue_one(int kt, int st) const {
-        constexpr int q = D & 3;
         const int k0 = kt * BK;
-        const uint32_t sbase = (uint32_t)st * (uint32_t)STAGE_BYTES;
-        if constexpr (D < 4) {
+        const uint32_t sbase = (uint32_t)st * (uint32_t)C::STAGE_BYTES;
+        if constexpr (DI < C::QA) {
+            constexpr int q = DI;
             uint32_t off = a_off[q] + 2u * (uint32_t)k0;
             if constexpr (!FULL)
                 off += (k0 + a_k < K) ? 0u : OOB_BUMP;
             dma16<1024 * q>(ra, off, m0_a + sbase);
         } else {
+            constexpr int q = DI - C::QA;
             uint32_t off = b_off[q] + (uint32_t)k0 * b_row;
             if constexpr (!FULL)
                 off += (k0 + b_k[q] < K) ? 0u : OOB_BUMP;
@@ -178,38 +221,37 @@ struct Dma {
         }
     }
 
+    template <int... DI>
+    __device__ __forceinline__ void issue_seq(int kt, int st, std::integer_sequence<int, DI...>) const {
+        (issue_one<false, DI>(kt, st), ...);
+    }
+
     // Request k-slice kt into LDS stage st.
     __device__ __forceinline__ void issue(int kt, int st) const {
-        issue_one<false, 0>(kt, st);
-        issue_one<false, 1>(kt, st);
-        issue_one<false, 2>(kt, st);
-        issue_one<false, 3>(kt, st);
-        issue_one<false, 4>(kt, st);
-        issue_one<false, 5>(kt, st);
-        issue_one<false, 6>(kt, st);
-        issue_one<false, 7>(kt, st);
+        issue_seq(kt, st, std::make_integer_sequence<int, C::D>{});
     }
 };
 
 // Per-lane LDS byte offsets (within a stage) of the fragment reads of k-step
 // s (16 k each):
-//   A, ds_read_b128: row wm*128 + 32 i + l%32, logical chunk 2 s + l/32;
+//   A, ds_read_b128: row wm*WM + 32 i + l%32, logical chunk 2 s + l/32;
 //   B, ds_read_b64_tr_b16 twice (k 0..3 and 4..7 of the lane's 8): lane
 //      16 G + q addresses k-row 16 s + 8 (G/2) + q/4 (+4), columns
-//      wn*128 + 32 j + 16 (G%2) + 4 (q%4) .. +3, so that lane l receives
-//      column wn*128 + 32 j + l%32, k = 16 s + 8 (l/32) + 0..7.
+//      wn*WN + 32 j + 16 (G%2) + 4 (q%4) .. +3, so that lane l receives
+//      column wn*WN + 32 j + l%32, k = 16 s + 8 (l/32) + 0..7.
+template <class C>
 struct FragAddr {
-    uint32_t a[2][4];    // [s][i]
-    uint32_t b[2][4];    // [s][j], first read; the second is +4 rows = +2048 bytes
+    uint32_t a[2][C::I];    // [s][i]
+    uint32_t b[2][C::J];    // [s][j], first read; the second is +4 rows
 
     __device__ __forceinline__ FragAddr(int wm, int wn, int lane) {
         const int lr = lane & 31;
-        const int row0 = wm * 128 + lr;
+        const int row0 = wm * C::WM + lr;
         const int sw = a_swz(lr);                     // a_swz depends on row bits 1..3 only
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < C::I; ++i) {
                 const int c = 2 * s + (lane >> 5);
                 a[s][i] = 16u * (uint32_t)((row0 + 32 * i) * 4 + (c ^ sw));
             }
@@ -220,17 +262,18 @@ struct FragAddr {
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int n = wn * 128 + 32 * j + 16 * (G & 1) + 4 * (q & 3);
+            for (int j = 0; j < C::J; ++j) {
+                const int n = wn * C::WN + 32 * j + 16 * (G & 1) + 4 * (q & 3);
                 const int c = (n >> 3) ^ bsw;
-                b[s][j] = (uint32_t)A_BYTES + 512u * (uint32_t)(kr + 16 * s) + 16u * (uint32_t)c +
+                b[s][j] = (uint32_t)C::A_BYTES + (uint32_t)C::B_ROW * (uint32_t)(kr + 16 * s) + 16u * (uint32_t)c +
                           8u * (uint32_t)(q & 1);
             }
     }
 };
 
+template <class C>
 struct Frag {
-    u32x4 a[4], b[4];
+    u32x4 a[C::I], b[C::J];
 };
 
 __device__ __forceinline__ u32x4 lds_u4(uint32_t byte) {
@@ -242,57 +285,81 @@ __device__ __forceinline__ u32x2 lds_tr(uint32_t byte) {
     return __builtin_bit_cast(u32x2, v);
 }
 
-// Fragment read number r (0..11) of k-step s: r < 4 is A row-block r, then
-// B column-block (r-4)/2, first (k 0..3) or second (k 4..7) half.
-__device__ __forceinline__ void read_one(Frag &f, const FragAddr &ad, uint32_t stage, int s, int r) {
-    if (r < 4) {
+// Fragment read number r (0..READS-1) of k-step s: r < I is A row-block r,
+// then B column-block (r-I)/2, first (k 0..3) or second (k 4..7) half.
+template <class C>
+__device__ __forceinline__ void read_one(Frag<C> &f, const FragAddr<C> &ad, uint32_t stage, int s, int r) {
+    if (r < C::I) {
         f.a[r] = lds_u4(stage + ad.a[s][r]);
     } else {
-        const int j = (r - 4) >> 1;
-        if (((r - 4) & 1) == 0) {
+        const int j = (r - C::I) >> 1;
+        if (((r - C::I) & 1) == 0) {
             const u32x2 v = lds_tr(stage + ad.b[s][j]);
             f.b[j].x = v.x;
             f.b[j].y = v.y;
         } else {
-            const u32x2 v = lds_tr(stage + ad.b[s][j] + 2048u);
+            const u32x2 v = lds_tr(stage + ad.b[s][j] + 4u * (uint32_t)C::B_ROW);
             f.b[j].z = v.x;
             f.b[j].w = v.y;
         }
     }
 }
 
-// One k-step in a fixed issue order: MFMA q (A block q/4 x B block q%4),
-// then fragment read q of the next step (q < 12), then one direct load
-// after MFMAs 1, 5, 9, 13 (`dma(d)` for d = 0..3).  sched_barrier keeps the
-// compiler from regrouping: spreading the direct loads lets the memory
-// pipeline take them while the matrix unit stays busy.
-template <class T, bool READ, bool DMA, int Q, typename DmaFn>
-__device__ __forceinline__ void kstep_one(const Frag &cur, Frag &nxt, f32x16 (&acc)[4][4], const FragAddr &ad,
-                                          uint32_t rstage, int rs, DmaFn &dma) {
-    acc[Q >> 2][Q & 3] = T::mfma32(cur.b[Q & 3], cur.a[Q >> 2], acc[Q >> 2][Q & 3]);
-    if constexpr (READ && Q < 12)
-        read_one(nxt, ad, rstage, rs, Q);
-    if constexpr (DMA && (Q & 3) == 1)
-        dma(std::integral_constant<int, (Q >> 2)>{});
+// Fragment reads issued after MFMA Q of a k-step: one each while there are
+// at least as many MFMAs as reads, else Q*R/M .. (Q+1)*R/M - 1.
+template <class C, int Q>
+struct ReadsAfter {
+    static constexpr int LO = C::READS <= C::MFMAS ? Q : Q * C::READS / C::MFMAS;
+    static constexpr int HI = C::READS <= C::MFMAS ? (Q < C::READS ? Q + 1 : Q) : (Q + 1) * C::READS / C::MFMAS;
+};
+
+// Direct load p (0..D/2-1) of a k-step's half goes after MFMA p*M/(D/2) + 1
+// (M >= 4 MFMAs per k-step, so that stays below M).
+template <class C, int Q>
+struct DmaAfter {
+    static constexpr int H = C::D / 2;
+    static constexpr int find(int p) { return p >= H ? -1 : ((p * C::MFMAS) / H + 1 == Q ? p : find(p + 1)); }
+    static constexpr int P = find(0);
+};
+
+template <class C, int R0, int... R>
+__device__ __forceinline__ void read_range(Frag<C> &nxt, const FragAddr<C> &ad, uint32_t rstage, int rs,
+                                           std::integer_sequence<int, R...>) {
+    (read_one<C>(nxt, ad, rstage, rs, R0 + R), ...);
+}
+
+// One k-step in a fixed issue order: MFMA Q (A block Q/J x B block Q%J),
+// then the fragment reads of the next step that follow it, then at most one
+// direct load (`dma(p)` for p = 0..D/2-1).  sched_barrier keeps the compiler
+// from regrouping: spreading the direct loads lets the memory pipeline take
+// them while the matrix unit stays busy.
+template <class C, class T, bool READ, bool DMA, int Q, typename DmaFn>
+__device__ __forceinline__ void kstep_one(const Frag<C> &cur, Frag<C> &nxt, f32x16 (&acc)[C::I][C::J],
+                                          const FragAddr<C> &ad, uint32_t rstage, int rs, DmaFn &dma) {
+    acc[Q / C::J][Q % C::J] = T::mfma32(cur.b[Q % C::J], cur.a[Q / C::J], acc[Q / C::J][Q % C::J]);
+    if constexpr (READ) {
+        constexpr int LO = ReadsAfter<C, Q>::LO, HI = ReadsAfter<C, Q>::HI;
+        if constexpr (HI > LO)
+            read_range<C, LO>(nxt, ad, rstage, rs, std::make_integer_sequence<int, HI - LO>{});
+    }
+    if constexpr (DMA && DmaAfter<C, Q>::P >= 0)
+        dma(std::integral_constant<int, DmaAfter<C, Q>::P>{});
     __builtin_amdgcn_sched_barrier(0);
 }
 
-template <class T, bool READ, bool DMA, typename DmaFn, int... Q>
-__device__ __forceinline__ void kstep_seq(const Frag &cur, Frag &nxt, f32x16 (&acc)[4][4], const FragAddr &ad,
-                                          uint32_t rstage, int rs, DmaFn &dma, std::integer_sequence<int, Q...>) {
-    (kstep_one<T, READ, DMA, Q>(cur, nxt, acc, ad, rstage, rs, dma), ...);
+template <class C, class T, bool READ, bool DMA, typename DmaFn, int... Q>
+__device__ __forceinline__ void kstep_seq(const Frag<C> &cur, Frag<C> &nxt, f32x16 (&acc)[C::I][C::J],
+                                          const FragAddr<C> &ad, uint32_t rstage, int rs, DmaFn &dma,
+                                          std::integer_sequence<int, Q...>) {
+    (kstep_one<C, T, READ, DMA, Q>(cur, nxt, acc, ad, rstage, rs, dma), ...);
 }
 
-template <class T, bool READ, bool DMA, typename DmaFn>
-__device__ __forceinline__ void kstep(const Frag &cur, Frag &nxt, f32x16 (&acc)[4][4], const FragAddr &ad,
-                                      uint32_t rstage, int rs, DmaFn dma) {
-    kstep_seq<T, READ, DMA>(cur, nxt, acc, ad, rstage, rs, dma, std::make_integer_sequence<int, 16>{});
+template <class C, class T, bool READ, bool DMA, typename DmaFn>
+__device__ __forceinline__ void kstep(const Frag<C> &cur, Frag<C> &nxt, f32x16 (&acc)[C::I][C::J],
+                                      const FragAddr<C> &ad, uint32_t rstage, int rs, DmaFn dma) {
+    kstep_seq<C, T, READ, DMA>(cur, nxt, acc, ad, rstage, rs, dma, std::make_integer_sequence<int, C::MFMAS>{});
 }
 
-// Persistent: the grid has at most one workgroup per CU, and workgroup g
-// computes tiles g, g + G, g + 2G, ... (G = grid size, a multiple of the 8
-// XCDs when the tile count allows, so every tile of a workgroup stays on its
-// XCD in the raster), which removes the dispatch gap between tiles.
 // Shapes with K % 8 != 0 or N % 8 != 0 (GEN): the direct loads still move
 // 16 bytes per lane, now at 2-byte-aligned addresses, which the hardware
 // takes.  Two kinds of chunk in the last k-slice then hold wrong data:
@@ -307,13 +374,14 @@ __device__ __forceinline__ void kstep(const Frag &cur, Frag &nxt, f32x16 (&acc)[
 // chunk is rewritten by a lane of the wave whose direct load wrote it, so
 // that wave's own wait orders the two writes.  Chunks of B rows crossing
 // n = N elsewhere only feed columns that are never stored.
-template <class T>
+template <class C, class T>
 __device__ __forceinline__ void fix_last_slice(const GemmArgs &g, int m0, int n0, int kl, uint32_t stage) {
     const int k0 = kl * BK;
     const int tid = threadIdx.x;
-    if (g.K % 8 != 0) {
+    const int wave = tid >> 6, lane = tid & 63;
+    if (g.K % 8 != 0 && lane < C::A_ROWS_PER_WAVE) {
         const __amdgpu_buffer_rsrc_t ra = tile::buffer_of(g.A, 2u * (uint32_t)g.M * (uint32_t)g.K);
-        const int r = tid;                       // tile row r was loaded by wave r / 64 = this wave
+        const int r = C::A_ROWS_PER_WAVE * wave + lane;   // tile row r was loaded by this wave
         const int cp = (g.K - k0) >> 3;          // the crossing chunk (< 4: the slice holds K - 1)
         const int v = (g.K - k0) & 7;            // its elements below K
         const uint32_t row = (uint32_t)(m0 + r); // rows >= M read zero (beyond the buffer)
@@ -325,7 +393,7 @@ __device__ __forceinline__ void fix_last_slice(const GemmArgs &g, int m0, int n0
         const u32x4 chunk = {pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]), pack2(e[6], e[7])};
         *(__attribute__((address_space(3))) u32x4 *)(uintptr_t)(stage + 64u * r + 16u * (cp ^ a_swz(r))) = chunk;
     }
-    if (g.N % 8 != 0 && n0 <= g.N - 1 && g.N - 1 < n0 + BN) {
+    if (g.N % 8 != 0 && n0 <= g.N - 1 && g.N - 1 < n0 + C::BN) {
         const int r = g.K - 1 - k0;              // B's last row, loaded by wave r / 8
         if (tid == 64 * (r >> 3)) {
             const __amdgpu_buffer_rsrc_t rb = tile::buffer_of(g.B, 2u * (uint32_t)g.K * (uint32_t)g.N);
@@ -336,38 +404,38 @@ __device__ __forceinline__ void fix_last_slice(const GemmArgs &g, int m0, int n0
             for (int q = 0; q < 8; ++q)
                 e[q] = __builtin_amdgcn_raw_buffer_load_b16(rb, (int)(base + 2u * q), 0, 0);
             const u32x4 chunk = {pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]), pack2(e[6], e[7])};
-            *(__attribute__((address_space(3))) u32x4 *)(uintptr_t)(stage + (uint32_t)A_BYTES + 512u * r +
+            *(__attribute__((address_space(3))) u32x4 *)(uintptr_t)(stage + (uint32_t)C::A_BYTES +
+                                                                    (uint32_t)C::B_ROW * r +
                                                                     16u * (c ^ b_swz(r))) = chunk;
         }
     }
 }
 
-// Epilogue and store through LDS.  After the k-loop the 128 KiB stage ring
-// is free and holds the whole 256 x 256 C tile of 16-bit values (512-byte
-// rows).  Each lane applies the epilogue to its accumulators and writes its
-// 4-column groups to LDS (16-byte chunk index XOR row % 32: the 32 rows one
-// instruction touches land on different chunks); then every wave copies whole
-// rows out, 16 bytes per lane, 2 rows of 512 bytes per instruction, so HBM
-// sees full row segments instead of 16-byte pieces of 32 rows (which, at
-// 2-byte-aligned row starts, split across write sectors).  Chunks that cross
-// column N go out element by element.  The caller's barrier after this keeps
-// the next tile's loads from overwriting LDS before every wave has read it.
-template <class T, int EPI, bool ALIGNED>
-__device__ __forceinline__ void store_tile_lds(const GemmArgs &args, const f32x16 (&acc)[4][4], int m0, int n0,
-                                               int wm, int wn, int lane, uint32_t lds0) {
+// Epilogue and store through LDS.  After the k-loop the stage ring is free
+// and holds the whole BM x BN C tile of 16-bit values (2 BN-byte rows).
+// Each lane applies the epilogue to its accumulators and writes its 4-column
+// groups to LDS (16-byte chunk index XOR c_swz(row)); then every wave copies
+// whole rows out, 16 bytes per lane, so HBM sees full row segments instead
+// of 16-byte pieces of 32 rows (which, at 2-byte-aligned row starts, split
+// across write sectors).  Chunks that cross column N go out element by
+// element.  The caller's barrier after this keeps the next tile's loads from
+// overwriting LDS before every wave has read it.
+template <class C, class T, int EPI, bool ALIGNED>
+__device__ __forceinline__ void store_tile_lds(const GemmArgs &args, const f32x16 (&acc)[C::I][C::J], int m0,
+                                               int n0, int wm, int wn, int lane, uint32_t lds0) {
     const int M = args.M, N = args.N;
     const int lr = lane & 31;
     const int lh = lane >> 5;
-    // The bias of all 16 four-column groups of this lane, requested at once
+    // The bias of all 4 J four-column groups of this lane, requested at once
     // (range-checked: columns past N read zero), before the barrier.
-    uint32_t braw[4][4][2];
+    uint32_t braw[C::J][4][2];
     if constexpr (EPI != EPI_NONE) {
         const __amdgpu_buffer_rsrc_t rb = tile::buffer_of(args.bias, 2u * (uint32_t)N);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < C::J; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const uint32_t off = 2u * (uint32_t)(n0 + wn * 128 + 32 * j + 8 * q + 4 * lh);
+                const uint32_t off = 2u * (uint32_t)(n0 + wn * C::WN + 32 * j + 8 * q + 4 * lh);
                 if constexpr (ALIGNED) {   // N % 8 == 0: a group is all inside or all outside
                     const u32x2 raw = __builtin_amdgcn_raw_buffer_load_b64(rb, (int)off, 0, 0);
                     braw[j][q][0] = raw.x;
@@ -384,10 +452,10 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs &args, const f32x1
     }
     __syncthreads();   // every wave is done reading the last slice
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < C::J; ++j) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int col = wn * 128 + 32 * j + 8 * q + 4 * lh;
+            const int col = wn * C::WN + 32 * j + 8 * q + 4 * lh;
             float bv[4] = {0.f, 0.f, 0.f, 0.f};
             if constexpr (EPI != EPI_NONE) {
                 bv[0] = T::to_f32((uint16_t)(braw[j][q][0] & 0xffff));
@@ -396,14 +464,14 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs &args, const f32x1
                 bv[3] = T::to_f32((uint16_t)(braw[j][q][1] >> 16));
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = wm * 128 + 32 * i + lr;
+            for (int i = 0; i < C::I; ++i) {
+                const int row = wm * C::WM + 32 * i + lr;
                 uint16_t o[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     o[r] = T::from_f32(epilogue<EPI>(acc[i][j][4 * q + r], bv[r]));
-                const uint32_t chunk = (uint32_t)(col >> 3) ^ (uint32_t)(row & 31);
-                const uint32_t addr = lds0 + 512u * (uint32_t)row + 16u * chunk + 8u * (uint32_t)lh;
+                const uint32_t chunk = (uint32_t)(col >> 3) ^ c_swz<C::CPR>(row);
+                const uint32_t addr = lds0 + (uint32_t)C::B_ROW * (uint32_t)row + 16u * chunk + 8u * (uint32_t)lh;
                 *(__attribute__((address_space(3))) u32x2 *)(uintptr_t)addr =
                     u32x2{pack2(o[0], o[1]), pack2(o[2], o[3])};
             }
@@ -413,14 +481,14 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs &args, const f32x1
     const __amdgpu_buffer_rsrc_t rc = tile::buffer_of(args.C, 2u * (uint32_t)M * (uint32_t)N);
     const int tid = threadIdx.x;
 #pragma unroll 4
-    for (int it = 0; it < 32; ++it) {
+    for (int it = 0; it < C::BM * C::CPR / NTHREADS; ++it) {
         const int idx = it * NTHREADS + tid;
-        const int row = idx >> 5;
-        const int c = idx & 31;
+        const int row = (int)((unsigned)idx / C::CPR);
+        const int c = (int)((unsigned)idx % C::CPR);
         const int m = m0 + row;
         const int n = n0 + 8 * c;
         const u32x4 v = *(__attribute__((address_space(3))) const u32x4 *)(uintptr_t)(
-            lds0 + 512u * (uint32_t)row + 16u * (uint32_t)(c ^ (row & 31)));
+            lds0 + (uint32_t)C::B_ROW * (uint32_t)row + 16u * ((uint32_t)c ^ c_swz<C::CPR>(row)));
         const uint32_t base = 2u * ((uint32_t)m * (uint32_t)N + (uint32_t)n);
         if (ALIGNED || n + 8 <= N) {
             const uint32_t off = (m < M && n < N) ? base : tile::OOB;
@@ -435,16 +503,24 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs &args, const f32x1
     }
 }
 
-template <class T, int EPI, bool GEN>
-__global__ __launch_bounds__(NTHREADS) void gemm_tiled_kernel(GemmArgs args) {
-    __shared__ __attribute__((aligned(16))) u32x4 smem[STAGES * STAGE_BYTES / 16];
+// Persistent: the grid has at most OCCUPANCY workgroups per CU, and
+// workgroup g computes tiles g, g + G, g + 2G, ... (G = grid size, a
+// multiple of the 8 XCDs when the tile count allows, so every tile of a
+// workgroup stays on its XCD in the raster), which removes the dispatch gap
+// between tiles.
+template <class C, class T, int EPI, bool GEN>
+__global__ __launch_bounds__(NTHREADS, C::OCCUPANCY) void gemm_tiled_kernel(GemmArgs args) {
+    __shared__ __attribute__((aligned(16))) u32x4 smem[STAGES * C::STAGE_BYTES / 16];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave >> 1;
     const int wn = wave & 1;
     const uint32_t lds0 = lds_address(smem);
-    auto stage = [&](int st) { return lds0 + (uint32_t)st * (uint32_t)STAGE_BYTES; };
-    const int total = ((args.M + BM - 1) / BM) * ((args.N + BN - 1) / BN);
+    auto stage = [&](int st) { return lds0 + (uint32_t)st * (uint32_t)C::STAGE_BYTES; };
+    const int tiles_m = (args.M + C::BM - 1) / C::BM;
+    const int tiles_n = (args.N + C::BN - 1) / C::BN;
+    const int total = tiles_m * tiles_n;
     const int nk = (args.K + BK - 1) / BK;
+    constexpr int D = C::D;
 
     for (int w = blockIdx.x; w < total; w += gridDim.x) {
         // The lane id is made opaque per tile so that the per-lane addresses
@@ -452,21 +528,21 @@ __global__ __launch_bounds__(NTHREADS) void gemm_tiled_kernel(GemmArgs args) {
         // the tile loop, where they would stay live through the k-loop.
         int lane = threadIdx.x & 63;
         asm volatile("" : "+v"(lane));
-        const FragAddr fad(wm, wn, lane);
+        const FragAddr<C> fad(wm, wn, lane);
         int tm, tn;
-        tile::tile_of_workgroup(args.M, args.N, w, tm, tn);
-        const int m0 = tm * BM;
-        const int n0 = tn * BN;
-        const Dma dma(args, m0, n0, wave, lane, lds0);
+        tile::tile_of_index(tiles_m, tiles_n, w, tm, tn);
+        const int m0 = tm * C::BM;
+        const int n0 = tn * C::BN;
+        const Dma<C> dma(args, m0, n0, wave, lane, lds0);
 
-        f32x16 acc[4][4];
+        f32x16 acc[C::I][C::J];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < C::I; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < C::J; ++j)
                 acc[i][j] = f32x16{};
 
-        Frag f0, f1;
+        Frag<C> f0, f1;
         // Prologue: request slices 0..2, wait for slice 0.  The previous
         // tile's C stores are older than these loads, so the same counts hold.
         if (nk > 0) {
@@ -475,20 +551,20 @@ __global__ __launch_bounds__(NTHREADS) void gemm_tiled_kernel(GemmArgs args) {
                 dma.issue(1, 1);
             if (nk > 2) {
                 dma.issue(2, 2);
-                wait_vmcnt<16>();
+                wait_vmcnt<2 * D>();
             } else if (nk > 1) {
-                wait_vmcnt<8>();
+                wait_vmcnt<D>();
             } else {
                 wait_vmcnt<0>();
                 if constexpr (GEN)
-                    fix_last_slice<T>(args, m0, n0, 0, stage(0));
+                    fix_last_slice<C, T>(args, m0, n0, 0, stage(0));
             }
         }
         __syncthreads();
         if (nk > 0) {
 #pragma unroll
-            for (int r = 0; r < 12; ++r)
-                read_one(f0, fad, stage(0), 0, r);
+            for (int r = 0; r < C::READS; ++r)
+                read_one<C>(f0, fad, stage(0), 0, r);
         }
 
         // Slice t in stage t%4, fragments of its first k-step already in f0:
@@ -499,8 +575,8 @@ __global__ __launch_bounds__(NTHREADS) void gemm_tiled_kernel(GemmArgs args) {
         //           (everyone's have, and everyone's reads of slice t are done);
         //   step 1: MFMAs on f1, reads of step 0 of slice t+1 into f0, second
         //           half of the direct loads of slice t+3.
-        // Loads issued after slice t+1's when waiting: all 8 of slice t+2 and
-        // the first 4 of slice t+3, hence vmcnt(12) in the steady state.
+        // Loads issued after slice t+1's when waiting: all D of slice t+2 and
+        // the first D/2 of slice t+3, hence vmcnt(3D/2) in the steady state.
         // ISSUE: 0 = no loads, 1 = loads of a full slice, 2 = loads of the
         // (possibly partial) last slice.
         auto slice = [&](int t, auto issue, auto wait, auto next) __attribute__((always_inline)) {
@@ -514,35 +590,35 @@ __global__ __launch_bounds__(NTHREADS) void gemm_tiled_kernel(GemmArgs args) {
                 dma.template issue_one<FULL, decltype(d)::value>(kt, kt & 3);
             };
             auto dma_hi = [&](auto d) __attribute__((always_inline)) {
-                dma.template issue_one<FULL, decltype(d)::value + 4>(kt, kt & 3);
+                dma.template issue_one<FULL, decltype(d)::value + D / 2>(kt, kt & 3);
             };
-            kstep<T, true, ISSUE>(f0, f1, acc, fad, st, 1, dma_lo);
+            kstep<C, T, true, ISSUE>(f0, f1, acc, fad, st, 1, dma_lo);
             if constexpr (NEXT) {
                 wait_vmcnt<decltype(wait)::value>();
                 // with nothing left in flight, slice t + 1 is the last one
                 if constexpr (GEN && decltype(wait)::value == 0)
-                    fix_last_slice<T>(args, m0, n0, t + 1, stage((t + 1) & 3));
+                    fix_last_slice<C, T>(args, m0, n0, t + 1, stage((t + 1) & 3));
                 __syncthreads();
             }
-            kstep<T, NEXT, ISSUE>(f1, f0, acc, fad, stage((t + 1) & 3), 0, dma_hi);
+            kstep<C, T, NEXT, ISSUE>(f1, f0, acc, fad, stage((t + 1) & 3), 0, dma_hi);
         };
         using yes = std::true_type;
         using no = std::false_type;
         using none = std::integral_constant<int, 0>;
         using full = std::integral_constant<int, 1>;
         using last = std::integral_constant<int, 2>;
-        using w12 = std::integral_constant<int, 12>;
-        using w8 = std::integral_constant<int, 8>;
+        using w_steady = std::integral_constant<int, 3 * D / 2>;
+        using w_two = std::integral_constant<int, D>;
         using w0 = std::integral_constant<int, 0>;
         int t = 0;
         for (; t + 4 < nk; ++t)
-            slice(t, full{}, w12{}, yes{});
+            slice(t, full{}, w_steady{}, yes{});
         if (t + 3 < nk) {
-            slice(t, last{}, w12{}, yes{});
+            slice(t, last{}, w_steady{}, yes{});
             ++t;
         }
         if (t + 3 == nk && t < nk) {
-            slice(t, none{}, w8{}, yes{});
+            slice(t, none{}, w_two{}, yes{});
             ++t;
         }
         if (t + 2 == nk && t < nk) {
@@ -552,41 +628,62 @@ __global__ __launch_bounds__(NTHREADS) void gemm_tiled_kernel(GemmArgs args) {
         if (t + 1 == nk)
             slice(t, none{}, w0{}, no{});
 
-        store_tile_lds<T, EPI, !GEN>(args, acc, m0, n0, wm, wn, lane, lds0);
+        store_tile_lds<C, T, EPI, !GEN>(args, acc, m0, n0, wm, wn, lane, lds0);
         // every wave is done reading LDS before the next tile's loads land
         __syncthreads();
     }
 }
 
-template <class T, int EPI>
+template <class C, class T, int EPI>
 hipError_t launch_typed(const GemmArgs &a, bool gen, int grid, hipStream_t stream) {
     if (gen)
-        hipLaunchKernelGGL((gemm_tiled_kernel<T, EPI, true>), dim3(grid), dim3(NTHREADS), 0, stream, a);
+        hipLaunchKernelGGL((gemm_tiled_kernel<C, T, EPI, true>), dim3(grid), dim3(NTHREADS), 0, stream, a);
     else
-        hipLaunchKernelGGL((gemm_tiled_kernel<T, EPI, false>), dim3(grid), dim3(NTHREADS), 0, stream, a);
+        hipLaunchKernelGGL((gemm_tiled_kernel<C, T, EPI, false>), dim3(grid), dim3(NTHREADS), 0, stream, a);
     return hipGetLastError();
 }
 
-template <class T>
+template <class C, class T>
 hipError_t launch_epi(int epi, const GemmArgs &a, bool gen, int grid, hipStream_t stream) {
     switch (epi) {
-    case EPI_NONE: return launch_typed<T, EPI_NONE>(a, gen, grid, stream);
-    case EPI_BIAS: return launch_typed<T, EPI_BIAS>(a, gen, grid, stream);
-    default: return launch_typed<T, EPI_BIAS_GELU_TANH>(a, gen, grid, stream);
+    case EPI_NONE: return launch_typed<C, T, EPI_NONE>(a, gen, grid, stream);
+    case EPI_BIAS: return launch_typed<C, T, EPI_BIAS>(a, gen, grid, stream);
+    default: return launch_typed<C, T, EPI_BIAS_GELU_TANH>(a, gen, grid, stream);
     }
+}
+
+template <class C>
+hipError_t launch_cfg(int dtype, int epi, const GemmArgs &a, bool aligned, int num_cu, hipStream_t stream) {
+    const int tiles = ((a.M + C::BM - 1) / C::BM) * ((a.N + C::BN - 1) / C::BN);
+    int grid = tiles;
+    const int slots = num_cu * C::OCCUPANCY;
+    if (num_cu > 0 && tiles > slots) {
+        // OCCUPANCY workgroups per CU, rounded down to a multiple of the XCD count
+        grid = slots >= tile::NUM_XCD ? slots - slots % tile::NUM_XCD : slots;
+    }
+    return dtype == 0 ? launch_epi<C, F16>(epi, a, !aligned, grid, stream)
+                      : launch_epi<C, BF16>(epi, a, !aligned, grid, stream);
 }
 
 }  // namespace
 
-hipError_t launch_tiled_vec(int dtype, int epi, const GemmArgs &a, bool aligned, int num_cu, hipStream_t stream) {
-    const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-    int grid = tiles;
-    if (num_cu > 0 && tiles > num_cu) {
-        // one workgroup per CU, rounded down to a multiple of the XCD count
-        grid = num_cu >= tile::NUM_XCD ? num_cu - num_cu % tile::NUM_XCD : num_cu;
+int tiled_occupancy(int tiles) {
+    switch (tiles) {
+    case TILES_256x128: return Cfg<256, 128>::OCCUPANCY;
+    case TILES_128x256: return Cfg<128, 256>::OCCUPANCY;
+    case TILES_128x128: return Cfg<128, 128>::OCCUPANCY;
+    default: return Cfg<256, 256>::OCCUPANCY;
     }
-    return dtype == 0 ? launch_epi<F16>(epi, a, !aligned, grid, stream)
-                      : launch_epi<BF16>(epi, a, !aligned, grid, stream);
+}
+
+hipError_t launch_tiled_vec(int dtype, int epi, const GemmArgs &a, bool aligned, int tiles, int num_cu,
+                            hipStream_t stream) {
+    switch (tiles) {
+    case TILES_256x128: return launch_cfg<Cfg<256, 128>>(dtype, epi, a, aligned, num_cu, stream);
+    case TILES_128x256: return launch_cfg<Cfg<128, 256>>(dtype, epi, a, aligned, num_cu, stream);
+    case TILES_128x128: return launch_cfg<Cfg<128, 128>>(dtype, epi, a, aligned, num_cu, stream);
+    default: return launch_cfg<Cfg<256, 256>>(dtype, epi, a, aligned, num_cu, stream);
+    }
 }
 
 }  // namespace tg

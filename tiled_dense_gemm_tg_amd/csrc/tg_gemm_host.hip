@@ -110,6 +110,50 @@ int num_cu_of(hipStream_t stream) {
     return n;
 }
 
+// Tile configuration for TG_TILES_AUTO: the one with the least predicted
+// time.  The persistent grid spreads the tiles evenly over the CUs, so the
+// busiest CU computes n = ceil(tiles / CUs) of them; n tiles of s = BM x BN
+// outputs take s / r_single when n == 1 and n s / r_full otherwise.  r_single
+// is the configuration's per-CU throughput with one tile per CU, r_full with
+// many (several workgroups per CU where the occupancy allows), both relative
+// to r_full of the 256 x 256 tile and measured on one MI355X by a sweep of
+// all configurations over such shapes (bench.py --sweep).  K only scales
+// every configuration alike.  Ties go to the larger tile.
+struct TileChoice {
+    tg_tiles tiles;
+    int bm, bn;
+    double r_single, r_full;
+};
+constexpr TileChoice kTileChoices[] = {
+    {TG_TILES_256x256, 256, 256, 1.00, 1.00},
+    {TG_TILES_256x128, 256, 128, 0.83, 0.74},
+    {TG_TILES_128x256, 128, 256, 0.88, 0.90},
+    {TG_TILES_128x128, 128, 128, 0.76, 0.68},
+};
+constexpr int kDefaultCUs = 256;
+
+double predicted_time(const TileChoice &c, int64_t M, int64_t N, int num_cu) {
+    const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
+    const int64_t n = (tiles + num_cu - 1) / num_cu;
+    const double s = double(c.bm) * c.bn;
+    return n <= 1 ? s / c.r_single : double(n) * s / c.r_full;
+}
+
+tg_tiles auto_tiles(int64_t M, int64_t N, int num_cu) {
+    if (num_cu <= 0)
+        num_cu = kDefaultCUs;
+    tg_tiles pick = TG_TILES_256x256;
+    double best = predicted_time(kTileChoices[0], M, N, num_cu);
+    for (const TileChoice &c : kTileChoices) {
+        const double t = predicted_time(c, M, N, num_cu);
+        if (t < best * (1.0 - 1e-9)) {
+            best = t;
+            pick = c.tiles;
+        }
+    }
+    return pick;
+}
+
 tg_path auto_path(int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *bias,
                   const void *C) {
     if (skinny_ok(M, N, K, A, B, bias, C))
@@ -133,10 +177,13 @@ TG_EXPORT tg_status tg_gemm_plan(int64_t M, int64_t N, int64_t K, tg_dtype dtype
     return TG_OK;
 }
 
-TG_EXPORT tg_status tg_gemm_path(tg_path path, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
-                                 const void *A, const void *B, const void *bias, tg_epilogue epilogue,
-                                 void *C, void *stream) {
+namespace {
+
+tg_status run_gemm(tg_path path, tg_tiles tiles, int64_t M, int64_t N, int64_t K, tg_dtype dtype, const void *A,
+                   const void *B, const void *bias, tg_epilogue epilogue, void *C, void *stream) {
     if (path != TG_PATH_AUTO && path != TG_PATH_TILED && path != TG_PATH_TILED_GENERIC && path != TG_PATH_SKINNY)
+        return TG_ERR_INVALID_ARG;
+    if (tiles < TG_TILES_AUTO || tiles > TG_TILES_128x128)
         return TG_ERR_INVALID_ARG;
     const Checked c = check_args(M, N, K, dtype, A, B, bias, epilogue, C);
     if (c.status != TG_OK || c.noop)
@@ -157,13 +204,38 @@ TG_EXPORT tg_status tg_gemm_path(tg_path path, int64_t M, int64_t N, int64_t K, 
     a.C = static_cast<uint16_t *>(C);
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
-    if (path == TG_PATH_SKINNY)
+    if (path == TG_PATH_SKINNY) {
         e = tg::launch_skinny(dtype, epilogue, a, s);
-    else if (path == TG_PATH_TILED)
-        e = tg::launch_tiled_vec(dtype, epilogue, a, tiled_aligned(N, K, A, B, bias, C), num_cu_of(s), s);
-    else
+    } else if (path == TG_PATH_TILED) {
+        const int cus = num_cu_of(s);
+        if (tiles == TG_TILES_AUTO)
+            tiles = auto_tiles(M, N, cus);
+        e = tg::launch_tiled_vec(dtype, epilogue, a, tiled_aligned(N, K, A, B, bias, C), tiles, cus, s);
+    } else {
         e = tg::launch_tiled_generic(dtype, epilogue, a, s);
+    }
     return e == hipSuccess ? TG_OK : TG_ERR_LAUNCH;
+}
+
+}  // namespace
+
+TG_EXPORT tg_status tg_gemm_path(tg_path path, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
+                                 const void *A, const void *B, const void *bias, tg_epilogue epilogue,
+                                 void *C, void *stream) {
+    return run_gemm(path, TG_TILES_AUTO, M, N, K, dtype, A, B, bias, epilogue, C, stream);
+}
+
+TG_EXPORT tg_status tg_gemm_tiled(tg_tiles tiles, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
+                                  const void *A, const void *B, const void *bias, tg_epilogue epilogue,
+                                  void *C, void *stream) {
+    return run_gemm(TG_PATH_TILED, tiles, M, N, K, dtype, A, B, bias, epilogue, C, stream);
+}
+
+TG_EXPORT tg_status tg_gemm_tiles_plan(int64_t M, int64_t N, int64_t K, int num_cu, tg_tiles *tiles_out) {
+    if (tiles_out == nullptr || M < 0 || N < 0 || K < 0)
+        return TG_ERR_INVALID_ARG;
+    *tiles_out = auto_tiles(M, N, num_cu);
+    return TG_OK;
 }
 
 TG_EXPORT tg_status tg_gemm(int64_t M, int64_t N, int64_t K, tg_dtype dtype, const void *A, const void *B,

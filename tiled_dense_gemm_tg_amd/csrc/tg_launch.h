@@ -18,13 +18,21 @@ struct GemmArgs {
 
 // dtype: 0 fp16, 1 bf16; epi: 0 none, 1 bias, 2 bias + GELU(tanh).
 
-// 256 x 256 tiles with 16-byte direct-to-LDS loads, any K and N and 2-byte
-// alignment, as long as 2 (M + 256) K and 2 (K + 32) (N + 256) stay below
-// 2^31 - 65536.  aligned: K % 8 == 0, N % 8 == 0, A, B, C 16-byte and bias
-// 8-byte aligned, which takes the instance without last-slice fix-ups and
-// with 8-byte stores throughout.
-// Persistent: at most num_cu workgroups (num_cu <= 0: one per tile).
-hipError_t launch_tiled_vec(int dtype, int epi, const GemmArgs &a, bool aligned, int num_cu, hipStream_t stream);
+// Tile configurations of the direct-load kernel (values as tg_tiles in
+// tg_gemm.h).
+enum TileCfg { TILES_256x256 = 1, TILES_256x128 = 2, TILES_128x256 = 3, TILES_128x128 = 4 };
+
+// BM x BN tiles (TileCfg) with 16-byte direct-to-LDS loads, any K and N and
+// 2-byte alignment, as long as 2 (M + 256) K and 2 (K + 32) (N + 256) stay
+// below 2^31 - 65536.  aligned: K % 8 == 0, N % 8 == 0, A, B, C 16-byte and
+// bias 8-byte aligned, which takes the instance without last-slice fix-ups
+// and with 16-byte stores throughout.
+// Persistent: at most tiled_occupancy(tiles) workgroups per CU (num_cu <= 0:
+// one workgroup per tile).
+hipError_t launch_tiled_vec(int dtype, int epi, const GemmArgs &a, bool aligned, int tiles, int num_cu,
+                            hipStream_t stream);
+// Workgroups of configuration `tiles` that fit on one CU at once.
+int tiled_occupancy(int tiles);
 
 // 256 x 256 tiles with element-granular loads and stores: any shape.
 hipError_t launch_tiled_generic(int dtype, int epi, const GemmArgs &a, hipStream_t stream);

@@ -77,6 +77,26 @@ WORKLOADS = {
 }
 WORKLOAD_ORDER = list(WORKLOADS)
 
+# Shape classes for the choice of tile size: outputs with few 256 x 256 tiles
+# next to the ones above.  The pages' own GEMM benchmark shape (a 2048-cube),
+# a batch of 512 rows through the decode shape's 11008-wide weight, a small
+# output with a deep K, and a ragged mid-size bf16 shape with the epilogue.
+# Same recipe, with workload numbers 11.. for the seeds.
+TILE_WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("gemm_f16_2048x2048x2048", 11, 2048, 2048, 2048, F16, EPI_NONE,
+                 ("normal", 0.0, 0.1), ("normal", 0.0, 0.1), None, 64),
+        Workload("gemm_f16_512x11008x4096", 12, 512, 11008, 4096, F16, EPI_NONE,
+                 ("normal", 0.0, 1.0), ("normal", 0.0, 0.02), None, 64),
+        Workload("gemm_f16_1024x1024x8192", 13, 1024, 1024, 8192, F16, EPI_NONE,
+                 ("normal", 0.0, 0.1), ("normal", 0.0, 0.1), None, 64),
+        Workload("gemm_bf16_1000x3000x6000_bias_gelu_tanh", 14, 1000, 3000, 6000, BF16,
+                 EPI_BIAS_GELU_TANH, ("uniform", -1.0, 1.0), ("uniform", -1.0, 1.0),
+                 ("uniform", -0.5, 0.5), 64),
+    ]
+}
+
 
 def _draw_f32(rng: np.random.Generator, shape, dist: Dist) -> np.ndarray:
     kind, p0, p1 = dist
