@@ -230,7 +230,8 @@ def bench_tile_choice(torch, tg, I, steps, warmup):
                      "auto_TFLOP/s": round(flops / (ms_auto * 1e-3) / 1e12, 1),
                      "per_config_us": {k: round(v * 1e3, 2) for k, v in per.items()},
                      "fastest": best, "auto_vs_fastest": round(per[best] / ms_auto, 3),
-                     "speedup_vs_256x256": round(per["256x256"] / ms_auto, 3)}
+                     "speedup_vs_256x256": round(per["256x256"] / ms_auto, 3),
+                     "traffic": measured_traffic(f"{name} {tg.TILES_NAMES.get(auto, '?')}")}
         log(f"{name}: auto {tg.TILES_NAMES.get(auto)} {ms_auto * 1e3:.1f} us, fastest {best} "
             f"{per[best] * 1e3:.1f} us, 256x256 {per['256x256'] * 1e3:.1f} us")
         del sets, A, B, bias, C
