@@ -11,9 +11,10 @@
 // straight into the second product, so the Sq x Sk score matrix never exists
 // in memory.  The CDNA4 design:
 //
-//   * a workgroup of 4 waves holds 256 queries of one (batch, head); each
-//     wave owns 64 of them as two 32-query sub-tiles, its Q fragments in
-//     registers for the whole loop;
+//   * a workgroup of 8 waves holds 256 queries of one (batch, head); each
+//     wave owns 32 of them, its Q fragments in registers for the whole loop
+//     and its 32 x 128 output in 64 fp32 registers; two waves share each
+//     SIMD, so one wave's softmax arithmetic overlaps the other's MFMAs;
 //   * key/value blocks of 64 tokens stream through a 3-stage LDS ring by
 //     direct-to-LDS loads (each block requested two blocks ahead);
 //   * both products are computed transposed on v_mfma_f32_32x32x16:
@@ -43,9 +44,9 @@ namespace tg {
 namespace {
 
 constexpr int HD = 128;                   // head dim
-constexpr int WAVES = 4;
+constexpr int WAVES = 8;
 constexpr int NTHREADS = 64 * WAVES;
-constexpr int QW = 64;                    // queries per wave
+constexpr int QW = 32;                    // queries per wave
 constexpr int BM = QW * WAVES;            // queries per workgroup
 constexpr int BN = 64;                    // keys per block
 constexpr int STAGES = 3;
@@ -99,34 +100,8 @@ __device__ __forceinline__ float lane_swap32(float x) {
         (int)((((int)threadIdx.x & 63) ^ 32) << 2), __builtin_bit_cast(int, x)));
 }
 
-// acc *= alpha on accumulators that live in AGPRs, through inline assembly so
-// that the compiler keeps them there (a plain multiply makes it copy every
-// accumulator to VGPRs on each iteration, whether or not a rescale happens).
-// The caller first waits out the MFMA-write -> accumulator-read hazard
-// (hazard_fence); the s_nop after the writes covers accumulator-write ->
-// MFMA-read.
-__device__ __forceinline__ void scale_agpr(f32x16 &acc, float alpha) {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        float x = acc[e];
-        float t;
-        asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
-                     : "+a"(x), "=&v"(t)
-                     : "v"(alpha));
-        acc[e] = x;
-    }
-    asm volatile("s_nop 4" : "+a"(acc));
-}
-
-// 32 wait states after the last MFMA that wrote any of the accumulators
-// (a 32x32 MFMA needs at most 18 before its result is read by another
-// instruction), ordered after those MFMAs through the operands.
-__device__ __forceinline__ void hazard_fence(f32x16 (&o)[4]) {
-    asm volatile("s_nop 15\n\ts_nop 15" : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]));
-}
-
 template <class T, bool CAUSAL>
-__global__ __launch_bounds__(NTHREADS) void attention_fwd_kernel(AttnArgs args) {
+__global__ __launch_bounds__(NTHREADS, 1) void attention_fwd_kernel(AttnArgs args) {
     __shared__ __attribute__((aligned(16))) u32x4 smem[STAGES * STAGE_BYTES / 16];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -153,20 +128,17 @@ __global__ __launch_bounds__(NTHREADS) void attention_fwd_kernel(AttnArgs args) 
     const int lh = lane >> 5;    // lane half
     const int lc = lane & 31;    // query column within a sub-tile
 
-    // ---- Q fragments: sub-tile q, d-step s: query q0 + 64 wave + 32 q + lc, d = 16 s + 8 lh .. +7
-    u32x4 qf[2][8];
+    // ---- Q fragments, d-step s: query qi = q0 + 32 wave + lc, d = 16 s + 8 lh .. +7
+    const int qi = q0 + QW * wave + lc;
+    u32x4 qf[8];
     {
         const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint16_t *>(args.Q), (short)0, (int)((uint32_t)args.B * (uint32_t)Sq * tok), 0x00020000);
+        const uint32_t base = ((uint32_t)b * (uint32_t)Sq + (uint32_t)qi) * tok + 2u * (uint32_t)h * HD;
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int qi = q0 + QW * wave + 32 * q + lc;
-            const uint32_t base = ((uint32_t)b * (uint32_t)Sq + (uint32_t)qi) * tok + 2u * (uint32_t)h * HD;
-#pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                const uint32_t off = qi < Sq ? base + 2u * (uint32_t)(16 * s + 8 * lh) : 0xFFFFFFF0u;
-                qf[q][s] = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)off, 0, 0);
-            }
+        for (int s = 0; s < 8; ++s) {
+            const uint32_t off = qi < Sq ? base + 2u * (uint32_t)(16 * s + 8 * lh) : 0xFFFFFFF0u;
+            qf[s] = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)off, 0, 0);
         }
     }
 
@@ -174,22 +146,22 @@ __global__ __launch_bounds__(NTHREADS) void attention_fwd_kernel(AttnArgs args) 
     // now keeps it from waiting for every load in flight inside the loop.
     wait_vmcnt<0>();
 
-    // ---- direct loads of one key/value block: wave w fills rows 16 w .. 16 w + 15
-    // of K and of V, 4 instructions each (4 rows of 256 bytes per instruction).
+    // ---- direct loads of one key/value block: wave w fills rows 8 w .. 8 w + 7
+    // of K and of V, 2 instructions each (4 rows of 256 bytes per instruction).
     const uint32_t kv_bytes = (uint32_t)args.B * (uint32_t)Sk * tok;
     const i32x4 rk = rsrc_words((const char *)args.K - SHIFT, kv_bytes + SHIFT);
     const i32x4 rv = rsrc_words((const char *)args.V - SHIFT, kv_bytes + SHIFT);
-    uint32_t koff[4], voff[4];
-    int krow[4];
+    uint32_t koff[2], voff[2];
+    int krow[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = 16 * wave + 4 * i + (lane >> 4);
+    for (int i = 0; i < 2; ++i) {
+        const int row = 8 * wave + 4 * i + (lane >> 4);
         krow[i] = row;
         const uint32_t tok_base = ((uint32_t)b * (uint32_t)Sk + (uint32_t)row) * tok + 2u * (uint32_t)h * HD;
         koff[i] = SHIFT - 1024u * i + tok_base + 16u * (uint32_t)((lane & 15) ^ k_swz(row));
         voff[i] = SHIFT - 1024u * i + tok_base + 16u * (uint32_t)((lane & 15) ^ v_swz(row));
     }
-    const uint32_t m0_k = 4096u * (uint32_t)wave;
+    const uint32_t m0_k = 2048u * (uint32_t)wave;
     auto issue_block = [&](int blk, int st) __attribute__((always_inline)) {
         const int kb = blk * BN;
         const uint32_t adv = (uint32_t)kb * tok;
@@ -206,12 +178,8 @@ __global__ __launch_bounds__(NTHREADS) void attention_fwd_kernel(AttnArgs args) 
         };
         one(std::integral_constant<int, 0>{});
         one(std::integral_constant<int, 1>{});
-        one(std::integral_constant<int, 2>{});
-        one(std::integral_constant<int, 3>{});
         onev(std::integral_constant<int, 0>{});
         onev(std::integral_constant<int, 1>{});
-        onev(std::integral_constant<int, 2>{});
-        onev(std::integral_constant<int, 3>{});
     };
 
     // ---- fragment read addresses (bytes within a stage)
@@ -239,14 +207,12 @@ __global__ __launch_bounds__(NTHREADS) void attention_fwd_kernel(AttnArgs args) 
         }
     }
 
-    f32x16 o[2][4];
+    f32x16 o[4];
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-            o[q][dt] = f32x16{};
-    float m_used[2] = {-INFINITY, -INFINITY};
-    float l_sum[2] = {0.f, 0.f};
+    for (int dt = 0; dt < 4; ++dt)
+        o[dt] = f32x16{};
+    float m_used = -INFINITY;
+    float l_sum = 0.f;
     const float c = args.scale_log2;
 
     const int k_end = CAUSAL ? min(Sk, q0 + BM) : Sk;
@@ -255,7 +221,7 @@ __global__ __launch_bounds__(NTHREADS) void attention_fwd_kernel(AttnArgs args) 
         issue_block(0, 0);
     if (nb > 1) {
         issue_block(1, 1);
-        wait_vmcnt<8>();
+        wait_vmcnt<4>();
     } else {
         wait_vmcnt<0>();
     }
@@ -273,73 +239,61 @@ __global__ __launch_bounds__(NTHREADS) void attention_fwd_kernel(AttnArgs args) 
         const bool need_mask = kb + BN > Sk || (CAUSAL && kb + BN - 1 > q0);
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
-            // ---- S^T = K Q^T (32 keys x 32 queries per sub-tile)
-            f32x16 sacc[2];
-            sacc[0] = f32x16{};
-            sacc[1] = f32x16{};
+            // ---- S^T = K Q^T (32 keys x 32 queries)
+            f32x16 sacc = f32x16{};
 #pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                const u32x4 kf = lds_u4(st + ka[kt][s]);
-#pragma unroll
-                for (int q = 0; q < 2; ++q)
-                    sacc[q] = T::mfma32(kf, qf[q][s], sacc[q]);
-            }
+            for (int s = 0; s < 8; ++s)
+                sacc = T::mfma32(lds_u4(st + ka[kt][s]), qf[s], sacc);
 
             // ---- online softmax: score e of the lane is key kb + 32 kt + 8 (e/4) + 4 lh + e%4
-            u32x4 pf[2][2];
+            u32x4 pf[2];
             auto softmax = [&](auto mask_c) __attribute__((always_inline)) {
                 constexpr bool MASK = decltype(mask_c)::value;
+                // visible if off < Sk - key0 and (causal) off <= qi - key0, with a
+                // compile-time off = 8 (e/4) + e%4
+                const int key0 = kb + 32 * kt + 4 * lh;
+                const int tail = Sk - key0;
+                const int diag = qi - key0;
+                float mx = -INFINITY;
 #pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                    const int qi = q0 + QW * wave + 32 * q + lc;
-                    // visible if off < Sk - key0 and (causal) off <= qi - key0, with a
-                    // compile-time off = 8 (e/4) + e%4
-                    const int key0 = kb + 32 * kt + 4 * lh;
-                    const int tail = Sk - key0;
-                    const int diag = qi - key0;
-                    float mx = -INFINITY;
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        float v = sacc[q][e];
-                        if constexpr (MASK) {
-                            const int off = 8 * (e >> 2) + (e & 3);
-                            const bool ok = off < tail && (!CAUSAL || off <= diag);
-                            v = ok ? v : -INFINITY;
-                            sacc[q][e] = v;
-                        }
-                        mx = fmaxf(mx, v);
+                for (int e = 0; e < 16; ++e) {
+                    float v = sacc[e];
+                    if constexpr (MASK) {
+                        const int off = 8 * (e >> 2) + (e & 3);
+                        const bool ok = off < tail && (!CAUSAL || off <= diag);
+                        v = ok ? v : -INFINITY;
+                        sacc[e] = v;
                     }
-                    mx = fmaxf(mx, lane_swap32(mx));
-                    const float m_blk = mx * c;
-                    // lazy rescaling: move the maximum only when it grew by more than 2^8
-                    if (__builtin_amdgcn_ballot_w64(m_blk > m_used[q] + RESCALE_LOG2) != 0) {
-                        const float m_new = fmaxf(m_used[q], m_blk);
-                        const float alpha =
-                            m_used[q] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_used[q] - m_new);
-                        hazard_fence(o[q]);
+                    mx = fmaxf(mx, v);
+                }
+                mx = fmaxf(mx, lane_swap32(mx));
+                const float m_blk = mx * c;
+                // lazy rescaling: move the maximum only when it grew by more than 2^8
+                if (__builtin_amdgcn_ballot_w64(m_blk > m_used + RESCALE_LOG2) != 0) {
+                    const float m_new = fmaxf(m_used, m_blk);
+                    const float alpha = m_used == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_used - m_new);
 #pragma unroll
-                        for (int dt = 0; dt < 4; ++dt)
-                            scale_agpr(o[q][dt], alpha);
-                        l_sum[q] *= alpha;
-                        m_used[q] = m_new;
-                    }
-                    const float m_ref = m_used[q] == -INFINITY ? 0.f : m_used[q];
-                    float sum = 0.f;
-                    uint16_t pb[16];
+                    for (int dt = 0; dt < 4; ++dt)
+                        o[dt] *= alpha;
+                    l_sum *= alpha;
+                    m_used = m_new;
+                }
+                const float m_ref = m_used == -INFINITY ? 0.f : m_used;
+                float sum = 0.f;
+                uint16_t pb[16];
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[q][e], c, -m_ref));
-                        sum += pv;
-                        pb[e] = T::from_f32(pv);
-                    }
-                    l_sum[q] += sum;
-                    // key step u = 2 kt + half: the lane's 8 keys are e = 8 half + 0..7
+                for (int e = 0; e < 16; ++e) {
+                    const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[e], c, -m_ref));
+                    sum += pv;
+                    pb[e] = T::from_f32(pv);
+                }
+                l_sum += sum;
+                // key step u = 2 kt + half: the lane's 8 keys are e = 8 half + 0..7
 #pragma unroll
-                    for (int hf = 0; hf < 2; ++hf) {
-                        const int e0 = 8 * hf;
-                        pf[q][hf] = u32x4{pack2(pb[e0], pb[e0 + 1]), pack2(pb[e0 + 2], pb[e0 + 3]),
-                                          pack2(pb[e0 + 4], pb[e0 + 5]), pack2(pb[e0 + 6], pb[e0 + 7])};
-                    }
+                for (int hf = 0; hf < 2; ++hf) {
+                    const int e0 = 8 * hf;
+                    pf[hf] = u32x4{pack2(pb[e0], pb[e0 + 1]), pack2(pb[e0 + 2], pb[e0 + 3]),
+                                   pack2(pb[e0 + 4], pb[e0 + 5]), pack2(pb[e0 + 6], pb[e0 + 7])};
                 }
             };
             if (need_mask)
@@ -356,10 +310,7 @@ __global__ __launch_bounds__(NTHREADS) void attention_fwd_kernel(AttnArgs args) 
                     const uint32_t a0 = st + va[dt] + 4096u * (uint32_t)u;   // 16 rows of 256 bytes per step
                     const u32x2 lo = lds_tr(a0);
                     const u32x2 hi = lds_tr(a0 + 2048u);                    // + 8 rows
-                    const u32x4 vf = u32x4{lo.x, lo.y, hi.x, hi.y};
-#pragma unroll
-                    for (int q = 0; q < 2; ++q)
-                        o[q][dt] = T::mfma32(vf, pf[q][hf], o[q][dt]);
+                    o[dt] = T::mfma32(u32x4{lo.x, lo.y, hi.x, hi.y}, pf[hf], o[dt]);
                 }
             }
         }
@@ -367,7 +318,7 @@ __global__ __launch_bounds__(NTHREADS) void attention_fwd_kernel(AttnArgs args) 
         // next block landed (this wave's loads; the barrier covers everyone's),
         // and every wave is done with this stage before it is refilled
         if (t + 2 < nb)
-            wait_vmcnt<8>();
+            wait_vmcnt<4>();
         else
             wait_vmcnt<0>();
         __syncthreads();
@@ -376,11 +327,9 @@ __global__ __launch_bounds__(NTHREADS) void attention_fwd_kernel(AttnArgs args) 
     // ---- normalise and store: lane holds O[query][d] for d = 32 dt + 8 (e/4) + 4 lh + e%4
     const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
         args.O, (short)0, (int)((uint32_t)args.B * (uint32_t)Sq * tok), 0x00020000);
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const float l_tot = l_sum[q] + lane_swap32(l_sum[q]);
+    {
+        const float l_tot = l_sum + lane_swap32(l_sum);
         const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-        const int qi = q0 + QW * wave + 32 * q + lc;
         const uint32_t base = ((uint32_t)b * (uint32_t)Sq + (uint32_t)qi) * tok + 2u * (uint32_t)h * HD;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
@@ -389,7 +338,7 @@ __global__ __launch_bounds__(NTHREADS) void attention_fwd_kernel(AttnArgs args) 
                 uint16_t w[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    w[r] = T::from_f32(o[q][dt][4 * g + r] * inv);
+                    w[r] = T::from_f32(o[dt][4 * g + r] * inv);
                 const uint32_t off = qi < Sq ? base + 2u * (uint32_t)(32 * dt + 8 * g + 4 * lh) : 0xFFFFFFF0u;
                 __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack2(w[0], w[1]), pack2(w[2], w[3])}, ro, (int)off,
                                                       0, 0);
