@@ -240,14 +240,21 @@ __global__ __launch_bounds__(NTHREADS, 1) void attention_fwd_kernel(AttnArgs arg
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
             // ---- S^T = K Q^T (32 keys x 32 queries)
+            // (the half's 8 K fragments are requested before the first MFMA,
+            // so that the MFMAs do not wait on their reads one by one)
+            u32x4 kf[8];
+#pragma unroll
+            for (int s = 0; s < 8; ++s)
+                kf[s] = lds_u4(st + ka[kt][s]);
+            __builtin_amdgcn_sched_barrier(0);
             f32x16 sacc = f32x16{};
 #pragma unroll
             for (int s = 0; s < 8; ++s)
-                sacc = T::mfma32(lds_u4(st + ka[kt][s]), qf[s], sacc);
+                sacc = T::mfma32(kf[s], qf[s], sacc);
 
             // ---- online softmax: score e of the lane is key kb + 32 kt + 8 (e/4) + 4 lh + e%4
-            u32x4 pf[2];
-            auto softmax = [&](auto mask_c) __attribute__((always_inline)) {
+            // masking (only in blocks that need it) and the block maximum
+            auto mask_max = [&](auto mask_c) __attribute__((always_inline)) {
                 constexpr bool MASK = decltype(mask_c)::value;
                 // visible if off < Sk - key0 and (causal) off <= qi - key0, with a
                 // compile-time off = 8 (e/4) + e%4
@@ -266,40 +273,39 @@ __global__ __launch_bounds__(NTHREADS, 1) void attention_fwd_kernel(AttnArgs arg
                     }
                     mx = fmaxf(mx, v);
                 }
-                mx = fmaxf(mx, lane_swap32(mx));
-                const float m_blk = mx * c;
-                // lazy rescaling: move the maximum only when it grew by more than 2^8
-                if (__builtin_amdgcn_ballot_w64(m_blk > m_used + RESCALE_LOG2) != 0) {
-                    const float m_new = fmaxf(m_used, m_blk);
-                    const float alpha = m_used == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_used - m_new);
-#pragma unroll
-                    for (int dt = 0; dt < 4; ++dt)
-                        o[dt] *= alpha;
-                    l_sum *= alpha;
-                    m_used = m_new;
-                }
-                const float m_ref = m_used == -INFINITY ? 0.f : m_used;
-                float sum = 0.f;
-                uint16_t pb[16];
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[e], c, -m_ref));
-                    sum += pv;
-                    pb[e] = T::from_f32(pv);
-                }
-                l_sum += sum;
-                // key step u = 2 kt + half: the lane's 8 keys are e = 8 half + 0..7
-#pragma unroll
-                for (int hf = 0; hf < 2; ++hf) {
-                    const int e0 = 8 * hf;
-                    pf[hf] = u32x4{pack2(pb[e0], pb[e0 + 1]), pack2(pb[e0 + 2], pb[e0 + 3]),
-                                   pack2(pb[e0 + 4], pb[e0 + 5]), pack2(pb[e0 + 6], pb[e0 + 7])};
-                }
+                return mx;
             };
-            if (need_mask)
-                softmax(std::true_type{});
-            else
-                softmax(std::false_type{});
+            float mx = need_mask ? mask_max(std::true_type{}) : mask_max(std::false_type{});
+            mx = fmaxf(mx, lane_swap32(mx));
+            const float m_blk = mx * c;
+            // lazy rescaling: move the maximum only when it grew by more than 2^8
+            if (__builtin_amdgcn_ballot_w64(m_blk > m_used + RESCALE_LOG2) != 0) {
+                const float m_new = fmaxf(m_used, m_blk);
+                const float alpha = m_used == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_used - m_new);
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt)
+                    o[dt] *= alpha;
+                l_sum *= alpha;
+                m_used = m_new;
+            }
+            const float m_ref = m_used == -INFINITY ? 0.f : m_used;
+            float sum = 0.f;
+            uint16_t pb[16];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[e], c, -m_ref));
+                sum += pv;
+                pb[e] = T::from_f32(pv);
+            }
+            l_sum += sum;
+            // key step u = 2 kt + half: the lane's 8 keys are e = 8 half + 0..7
+            u32x4 pf[2];
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const int e0 = 8 * hf;
+                pf[hf] = u32x4{pack2(pb[e0], pb[e0 + 1]), pack2(pb[e0 + 2], pb[e0 + 3]),
+                               pack2(pb[e0 + 4], pb[e0 + 5]), pack2(pb[e0 + 6], pb[e0 + 7])};
+            }
 
             // ---- O^T += V^T P^T over the half's two 16-key steps
 #pragma unroll
