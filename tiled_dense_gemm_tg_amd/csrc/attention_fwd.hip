@@ -86,6 +86,43 @@ __device__ __forceinline__ int k_swz(int row) { return row & 15; }
 // V rows are read transposed, 4 consecutive rows per pass (as B in the GEMM).
 __device__ __forceinline__ int v_swz(int row) { return ((row & 1) ? 10 : 0) ^ ((row & 2) ? 4 : 0); }
 
+typedef __attribute__((address_space(3))) const char *lds_ptr;
+
+// Fragment reads at an LDS pointer plus a compile-time offset, which the
+// assembler takes as the instruction's offset field.
+__device__ __forceinline__ u32x4 lds_u4_at(lds_ptr p) {
+    return *(__attribute__((address_space(3))) const u32x4 *)p;
+}
+__device__ __forceinline__ u32x2 lds_tr_at(lds_ptr p) {
+    const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p);
+    return __builtin_bit_cast(u32x2, v);
+}
+
+// Two probabilities rounded to the 16-bit format (nearest even) and packed,
+// and the sum of the two rounded values added to acc.
+template <class T> struct Prob;
+template <> struct Prob<F16> {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    static __device__ __forceinline__ uint32_t pack(float a, float b) {
+        typedef float f2 __attribute__((ext_vector_type(2)));
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{a, b}, h2));
+    }
+    static __device__ __forceinline__ float add_pair(uint32_t p, float acc) {
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, p), h2{(_Float16)1.0f, (_Float16)1.0f}, acc, false);
+    }
+};
+template <> struct Prob<BF16> {
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    static __device__ __forceinline__ uint32_t pack(float a, float b) {
+        typedef float f2 __attribute__((ext_vector_type(2)));
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{a, b}, b2));
+    }
+    static __device__ __forceinline__ float add_pair(uint32_t p, float acc) {
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, p), b2{(__bf16)1.0f, (__bf16)1.0f}, acc,
+                                               false);
+    }
+};
+
 __device__ __forceinline__ u32x4 lds_u4(uint32_t byte) {
     return *(__attribute__((address_space(3))) const u32x4 *)(uintptr_t)byte;
 }
@@ -207,6 +244,18 @@ __global__ __launch_bounds__(NTHREADS, 1) void attention_fwd_kernel(AttnArgs arg
         }
     }
 
+    // per-lane read pointers into the current stage: K fragment s of the
+    // first half, V^T tile dt of the first key step (the other halves and
+    // steps are compile-time offsets); they move to the next stage after
+    // every block
+    lds_ptr kp[8], vp[4];
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+        kp[s] = (lds_ptr)smem + ka[0][s];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+        vp[dt] = (lds_ptr)smem + va[dt];
+
     f32x16 o[4];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
@@ -228,7 +277,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void attention_fwd_kernel(AttnArgs arg
     __syncthreads();
 
     for (int t = 0; t < nb; ++t) {
-        const uint32_t st = stage(t % STAGES);
         if (t + 2 < nb)
             issue_block(t + 2, (t + 2) % STAGES);
         const int kb = t * BN;
@@ -245,7 +293,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attention_fwd_kernel(AttnArgs arg
             u32x4 kf[8];
 #pragma unroll
             for (int s = 0; s < 8; ++s)
-                kf[s] = lds_u4(st + ka[kt][s]);
+                kf[s] = lds_u4_at(kp[s] + 8192 * kt);   // + 32 rows
             __builtin_amdgcn_sched_barrier(0);
             f32x16 sacc = f32x16{};
 #pragma unroll
@@ -288,24 +336,21 @@ __global__ __launch_bounds__(NTHREADS, 1) void attention_fwd_kernel(AttnArgs arg
                 l_sum *= alpha;
                 m_used = m_new;
             }
+            // probabilities rounded to the input format; the running sum adds
+            // the rounded values, the same weights the second product uses
             const float m_ref = m_used == -INFINITY ? 0.f : m_used;
-            float sum = 0.f;
-            uint16_t pb[16];
+            uint32_t pw[8];
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[e], c, -m_ref));
-                sum += pv;
-                pb[e] = T::from_f32(pv);
+            for (int e = 0; e < 16; e += 2) {
+                pw[e / 2] = Prob<T>::pack(__builtin_amdgcn_exp2f(fmaf(sacc[e], c, -m_ref)),
+                                          __builtin_amdgcn_exp2f(fmaf(sacc[e + 1], c, -m_ref)));
+                l_sum = Prob<T>::add_pair(pw[e / 2], l_sum);
             }
-            l_sum += sum;
             // key step u = 2 kt + half: the lane's 8 keys are e = 8 half + 0..7
             u32x4 pf[2];
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                const int e0 = 8 * hf;
-                pf[hf] = u32x4{pack2(pb[e0], pb[e0 + 1]), pack2(pb[e0 + 2], pb[e0 + 3]),
-                               pack2(pb[e0 + 4], pb[e0 + 5]), pack2(pb[e0 + 6], pb[e0 + 7])};
-            }
+            for (int hf = 0; hf < 2; ++hf)
+                pf[hf] = u32x4{pw[4 * hf], pw[4 * hf + 1], pw[4 * hf + 2], pw[4 * hf + 3]};
 
             // ---- O^T += V^T P^T over the half's two 16-key steps
 #pragma unroll
@@ -313,9 +358,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void attention_fwd_kernel(AttnArgs arg
                 const int u = 2 * kt + hf;
 #pragma unroll
                 for (int dt = 0; dt < 4; ++dt) {
-                    const uint32_t a0 = st + va[dt] + 4096u * (uint32_t)u;   // 16 rows of 256 bytes per step
-                    const u32x2 lo = lds_tr(a0);
-                    const u32x2 hi = lds_tr(a0 + 2048u);                    // + 8 rows
+                    const u32x2 lo = lds_tr_at(vp[dt] + 4096 * u);          // 16 rows of 256 bytes per step
+                    const u32x2 hi = lds_tr_at(vp[dt] + 4096 * u + 2048);   // + 8 rows
                     o[dt] = T::mfma32(u32x4{lo.x, lo.y, hi.x, hi.y}, pf[hf], o[dt]);
                 }
             }
@@ -327,6 +371,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void attention_fwd_kernel(AttnArgs arg
             wait_vmcnt<4>();
         else
             wait_vmcnt<0>();
+        {
+            const int adv = (t % STAGES == STAGES - 1) ? -(STAGES - 1) * STAGE_BYTES : STAGE_BYTES;
+#pragma unroll
+            for (int s = 0; s < 8; ++s)
+                kp[s] += adv;
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+                vp[dt] += adv;
+        }
         __syncthreads();
     }
 
