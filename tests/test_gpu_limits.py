@@ -1,0 +1,77 @@
+"""GPU parity at the kernels' size limits, through the C interface.
+
+The direct-load tiled kernel addresses A and B with 32-bit byte offsets into
+buffers that start 4 KiB before each operand and take every operand padded
+to whole tiles below 2 GiB less 64 KiB; beyond that the register-gathered
+kernel takes over, up to 2^31 - 64 elements per operand (byte offsets near
+2^32).  These tests run both just below and just above that limit, in A and
+in B, and check sampled rows and columns that include the last ones (the
+largest offsets) bit-exactly against the oracle.
+
+Operands are integer-valued (a hash of the row and column, values -2..2, so
+every fp32 partial sum is exact and a row or column read from the wrong
+place shows as a mismatch) and are generated on the device; the oracle gets
+the sampled rows of A and columns of B only.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import tiled_dense_gemm_tg_amd as tg
+from tiled_dense_gemm_tg_amd import inputs as I
+from gpu_util import check_exact, log, to_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def _hashed(rows, cols, salt):
+    """(rows x cols) fp16 device tensor of small integers from a hash of (row, col)."""
+    import torch
+    r = torch.arange(rows, device="cuda", dtype=torch.int64)[:, None]
+    out = torch.empty((rows, cols), dtype=torch.float16, device="cuda")
+    step = max(1, (1 << 27) // cols)       # rows per chunk: bounded temporaries
+    c = torch.arange(cols, device="cuda", dtype=torch.int64)[None, :]
+    for r0 in range(0, rows, step):
+        rr = r[r0:r0 + step]
+        v = ((rr * 2654435761 + c * 40503 + salt * 97) >> 11) % 5 - 2
+        out[r0:r0 + step] = v.to(torch.float16)
+    return out
+
+
+def _sample(n, count, seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    idx = rng.choice(n, size=min(count, n), replace=False)
+    return np.unique(np.concatenate([idx, [0, n - 2, n - 1]])).astype(np.int64)
+
+
+@pytest.mark.parametrize("M,N,K,path", [
+    (130808, 256, 8192, tg.TG_PATH_TILED),           # A padded just below 2 GiB - 64 KiB
+    (130812, 256, 8192, tg.TG_PATH_TILED_GENERIC),   # A just above: 2.14 GB, offsets past 2^31
+    (256, 130296, 8192, tg.TG_PATH_TILED),           # B padded just below the limit
+    (256, 130304, 8192, tg.TG_PATH_TILED_GENERIC),   # B just above
+], ids=lambda v: str(v))
+def test_largest_operands(M, N, K, path):
+    import torch
+    dtype = I.F16
+    log(f"[limits] {M}x{N}x{K}: generating operands on the device")
+    A = _hashed(M, K, 1)
+    B = _hashed(K, N, 2)
+    bias = _hashed(1, N, 3).reshape(N)
+    C = torch.full((M, N), float("nan"), dtype=torch.float16, device="cuda")
+    st, p = tg.tg_gemm_plan(M, N, K, dtype, A.data_ptr(), B.data_ptr(), bias.data_ptr(), I.EPI_BIAS, C.data_ptr())
+    assert st == tg.TG_OK and p == path, (st, tg.PATH_NAMES.get(p))
+    log(f"[limits] {M}x{N}x{K}: GPU run on path {tg.PATH_NAMES[p]}")
+    tg.gemm(A, B, bias, "bias", out=C)
+    torch.cuda.synchronize()
+    rows = _sample(M, 24, 31 + M)
+    cols = _sample(N, 192, 37 + N)
+    a_rows = to_bits(A[torch.from_numpy(rows).cuda()])
+    b_cols = to_bits(B[:, torch.from_numpy(cols).cuda()])
+    bias_cols = to_bits(bias[torch.from_numpy(cols).cuda()])
+    got = to_bits(C[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()])
+    del A, B, C
+    torch.cuda.empty_cache()
+    log(f"[limits] {M}x{N}x{K}: oracle on {len(rows)} rows x {len(cols)} columns")
+    _, refq = oracle.gemm(len(rows), len(cols), K, dtype, a_rows.reshape(-1), b_cols.reshape(-1), bias_cols,
+                          I.EPI_BIAS)
+    check_exact(got, refq.reshape(len(rows), len(cols)), f"{M}x{N}x{K}")
