@@ -75,3 +75,37 @@ def test_largest_operands(M, N, K, path):
     _, refq = oracle.gemm(len(rows), len(cols), K, dtype, a_rows.reshape(-1), b_cols.reshape(-1), bias_cols,
                           I.EPI_BIAS)
     check_exact(got, refq.reshape(len(rows), len(cols)), f"{M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("Bn,S,H,causal", [
+    (1, 767, 8192, False),    # Q, K, V and O 1.6 GB each: padded just below the 2 GiB limit
+    (2, 767, 4096, True),
+], ids=lambda v: str(v))
+def test_attention_largest_tensors(Bn, S, H, causal):
+    """Attention with the largest tensors the kernel takes (token stride 2 MB
+    or 1 MB): sampled queries of sampled heads against the oracle."""
+    import torch
+    from gpu_util import check_tolerance
+    D = 128
+    dtype = I.F16
+    log(f"[limits] attention B={Bn} S={S} H={H} causal={causal}: generating inputs on the device")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(41 + H)
+    q = torch.randn((Bn, S, H, D), generator=gen, device="cuda").half()
+    k = torch.randn((Bn, S, H, D), generator=gen, device="cuda").half()
+    v = torch.randn((Bn, S, H, D), generator=gen, device="cuda").half()
+    o = torch.full_like(q, float("nan"))
+    log(f"[limits] attention B={Bn} S={S} H={H}: GPU run")
+    tg.attention(q, k, v, causal=causal, out=o)
+    torch.cuda.synchronize()
+    rng = np.random.Generator(np.random.PCG64(43))
+    heads = np.unique(np.concatenate([rng.choice(H, 4, replace=False), [0, H - 1]]))
+    for b in (0, Bn - 1):
+        for h in heads:
+            qs = np.unique(np.concatenate([rng.choice(S, 12, replace=False), [0, S - 1]]))
+            qh, kh, vh = (to_bits(x[b, :, int(h)]) for x in (q, k, v))     # (S, D) of this batch and head
+            triples = np.stack([np.zeros_like(qs), qs, np.zeros_like(qs)], axis=1)
+            ref64, _ = oracle.attention(1, S, S, 1, D, dtype, qh.reshape(-1), kh.reshape(-1), vh.reshape(-1),
+                                        causal=causal, queries=triples)
+            got = to_bits(o[b, torch.from_numpy(qs).cuda(), int(h)])
+            check_tolerance(dtype, got, ref64, f"attention b={b} h={h}")
