@@ -109,3 +109,59 @@ def test_attention_largest_tensors(Bn, S, H, causal):
                                         causal=causal, queries=triples)
             got = to_bits(o[b, torch.from_numpy(qs).cuda(), int(h)])
             check_tolerance(dtype, got, ref64, f"attention b={b} h={h}")
+
+
+def test_skinny_largest_weight():
+    """The decode-shaped kernel with B of 2^31 - 65536 elements (4.3 GB,
+    byte offsets up to 2^32 - 2^17): sampled columns, every row, exact."""
+    import torch
+    M, N, K = 16, 262136, 8192
+    dtype = I.F16
+    log(f"[limits] skinny {M}x{N}x{K}: generating operands on the device")
+    A = _hashed(M, K, 4)
+    B = _hashed(K, N, 5)
+    C = torch.full((M, N), float("nan"), dtype=torch.float16, device="cuda")
+    st, p = tg.tg_gemm_plan(M, N, K, dtype, A.data_ptr(), B.data_ptr(), None, I.EPI_NONE, C.data_ptr())
+    assert st == tg.TG_OK and p == tg.TG_PATH_SKINNY, (st, tg.PATH_NAMES.get(p))
+    log(f"[limits] skinny {M}x{N}x{K}: GPU run")
+    tg.gemm(A, B, out=C)
+    torch.cuda.synchronize()
+    cols = torch.from_numpy(_sample(N, 256, 47)).cuda()
+    b_cols = to_bits(B[:, cols])
+    got = to_bits(C[:, cols])
+    a_bits = to_bits(A)
+    del B, C
+    torch.cuda.empty_cache()
+    _, refq = oracle.gemm(M, len(cols), K, dtype, a_bits.reshape(-1), b_cols.reshape(-1))
+    check_exact(got, refq.reshape(M, len(cols)), "skinny at the limit")
+
+
+def test_w4_largest_weight():
+    """The 4-bit product with 2^31 - 2^20 weight codes (2.1 GB unpacked, 1.07 GB
+    packed) and power-of-two scales: sampled columns, every row, exact."""
+    import torch
+    M, N, K, G = 16, 131008, 16384, 128
+    dtype = I.F16
+    log(f"[limits] w4 {M}x{N}x{K}: generating operands on the device")
+    A = _hashed(M, K, 6)
+    r = torch.arange(K, device="cuda", dtype=torch.int64)[:, None]
+    q = torch.empty((K, N), dtype=torch.uint8, device="cuda")
+    c = torch.arange(N, device="cuda", dtype=torch.int64)[None, :]
+    step = (1 << 27) // N
+    for r0 in range(0, K, step):
+        q[r0:r0 + step] = (((r[r0:r0 + step] * 2246822519 + c * 3266489917) >> 9) % 16).to(torch.uint8)
+    e = (torch.arange(K // G, device="cuda")[:, None] * 3 + torch.arange(N, device="cuda")[None, :]) % 4
+    scales = torch.pow(2.0, -e.to(torch.float32)).half()      # 1, 1/2, 1/4, 1/8: exact products
+    packed = tg.w4_pack(q)
+    log(f"[limits] w4 {M}x{N}x{K}: GPU run")
+    C = tg.gemm_w4(A, packed, scales, G, N)
+    torch.cuda.synchronize()
+    cols = torch.from_numpy(_sample(N, 256, 53)).cuda()
+    q_cols = q[:, cols].cpu().numpy()
+    s_cols = to_bits(scales[:, cols])
+    got = to_bits(C[:, cols])
+    a_bits = to_bits(A)
+    del q, packed, C
+    torch.cuda.empty_cache()
+    _, refq = oracle.gemm_w4(M, len(cols), K, dtype, a_bits.reshape(-1), q_cols, s_cols, G)
+    check_exact(got, refq.reshape(M, len(cols)), "w4 at the limit")
