@@ -196,3 +196,14 @@ def test_automatic_choice_is_the_planned_configuration(M, N, K):
     auto = to_bits(run(M, N, K, dtype, A, B, expect_path=tg.TG_PATH_TILED))
     explicit = to_bits(run(M, N, K, dtype, A, B, tiles=cfg))
     assert np.array_equal(auto, explicit)
+
+
+@pytest.mark.parametrize("cfg", CONFIGS, ids=_name)
+@pytest.mark.parametrize("epi", [I.EPI_NONE, I.EPI_BIAS, I.EPI_BIAS_GELU_TANH])
+def test_empty_K_gives_epilogue_of_zero(cfg, epi):
+    M, N = 300, 264
+    bias = I.random_bits((N,), ("uniform", -2.0, 2.0), I.F16, 13600) if epi else None
+    _, refq = oracle.gemm(M, N, 0, I.F16, None, None, bias, epi)
+    log(f"[tiles-K=0] tiles={_name(cfg)} epi={epi}")
+    out = run(M, N, 0, I.F16, np.zeros(0, np.uint16), np.zeros(0, np.uint16), bias, epi, tiles=cfg)
+    check_exact(to_bits(out), refq, "K=0")
