@@ -15,8 +15,9 @@
 //     wave owns 32 of them, its Q fragments in registers for the whole loop
 //     and its 32 x 128 output in 64 fp32 registers; two waves share each
 //     SIMD, so one wave's softmax arithmetic overlaps the other's MFMAs;
-//   * key/value blocks of 64 tokens stream through a 3-stage LDS ring by
-//     direct-to-LDS loads (each block requested two blocks ahead);
+//   * key/value blocks of 128 tokens stream through a 2-stage LDS ring
+//     (128 KiB) by direct-to-LDS loads, each block requested one block
+//     ahead, one barrier per block;
 //   * both products are computed transposed on v_mfma_f32_32x32x16:
 //     S^T = K Q^T (K rows from LDS, Q^T from registers) and
 //     O^T = V^T P^T (V^T through the transposing LDS read), so every lane
@@ -48,8 +49,8 @@ constexpr int WAVES = 8;
 constexpr int NTHREADS = 64 * WAVES;
 constexpr int QW = 32;                    // queries per wave
 constexpr int BM = QW * WAVES;            // queries per workgroup
-constexpr int BN = 64;                    // keys per block
-constexpr int STAGES = 3;
+constexpr int BN = 128;                   // keys per block
+constexpr int STAGES = 2;
 constexpr int KV_BYTES = BN * HD * 2;     // 16 KiB: one block of K (or V) in LDS
 constexpr int STAGE_BYTES = 2 * KV_BYTES;
 constexpr uint32_t SHIFT = 4096;          // buffers start 4 KiB before K and V
@@ -183,22 +184,22 @@ __global__ __launch_bounds__(NTHREADS, 1) void attention_fwd_kernel(AttnArgs arg
     // now keeps it from waiting for every load in flight inside the loop.
     wait_vmcnt<0>();
 
-    // ---- direct loads of one key/value block: wave w fills rows 8 w .. 8 w + 7
-    // of K and of V, 2 instructions each (4 rows of 256 bytes per instruction).
+    // ---- direct loads of one key/value block: wave w fills rows 16 w .. 16 w + 15
+    // of K and of V, 4 instructions each (4 rows of 256 bytes per instruction).
     const uint32_t kv_bytes = (uint32_t)args.B * (uint32_t)Sk * tok;
     const i32x4 rk = rsrc_words((const char *)args.K - SHIFT, kv_bytes + SHIFT);
     const i32x4 rv = rsrc_words((const char *)args.V - SHIFT, kv_bytes + SHIFT);
-    uint32_t koff[2], voff[2];
-    int krow[2];
+    uint32_t koff[4], voff[4];
+    int krow[4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int row = 8 * wave + 4 * i + (lane >> 4);
+    for (int i = 0; i < 4; ++i) {
+        const int row = 16 * wave + 4 * i + (lane >> 4);
         krow[i] = row;
         const uint32_t tok_base = ((uint32_t)b * (uint32_t)Sk + (uint32_t)row) * tok + 2u * (uint32_t)h * HD;
         koff[i] = SHIFT - 1024u * i + tok_base + 16u * (uint32_t)((lane & 15) ^ k_swz(row));
         voff[i] = SHIFT - 1024u * i + tok_base + 16u * (uint32_t)((lane & 15) ^ v_swz(row));
     }
-    const uint32_t m0_k = 2048u * (uint32_t)wave;
+    const uint32_t m0_k = 4096u * (uint32_t)wave;
     auto issue_block = [&](int blk, int st) __attribute__((always_inline)) {
         const int kb = blk * BN;
         const uint32_t adv = (uint32_t)kb * tok;
@@ -215,8 +216,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void attention_fwd_kernel(AttnArgs arg
         };
         one(std::integral_constant<int, 0>{});
         one(std::integral_constant<int, 1>{});
+        one(std::integral_constant<int, 2>{});
+        one(std::integral_constant<int, 3>{});
         onev(std::integral_constant<int, 0>{});
         onev(std::integral_constant<int, 1>{});
+        onev(std::integral_constant<int, 2>{});
+        onev(std::integral_constant<int, 3>{});
     };
 
     // ---- fragment read addresses (bytes within a stage)
@@ -268,25 +273,22 @@ __global__ __launch_bounds__(NTHREADS, 1) void attention_fwd_kernel(AttnArgs arg
     const int nb = (k_end + BN - 1) / BN;
     if (nb > 0)
         issue_block(0, 0);
-    if (nb > 1) {
-        issue_block(1, 1);
-        wait_vmcnt<4>();
-    } else {
-        wait_vmcnt<0>();
-    }
+    wait_vmcnt<0>();
     __syncthreads();
 
     for (int t = 0; t < nb; ++t) {
-        if (t + 2 < nb)
-            issue_block(t + 2, (t + 2) % STAGES);
+        // the next block goes into the other stage, last read in block t - 1
+        // (before the barrier that ended it)
+        if (t + 1 < nb)
+            issue_block(t + 1, (t + 1) % STAGES);
         const int kb = t * BN;
 
-        // The block is processed as two 32-key halves (kt), each through
+        // The block is processed as four 32-key quarters (kt), each through
         // scores, online softmax and the second product, which keeps only one
-        // half's scores live.
+        // quarter's scores live.
         const bool need_mask = kb + BN > Sk || (CAUSAL && kb + BN - 1 > q0);
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
+        for (int kt = 0; kt < BN / 32; ++kt) {
             // ---- S^T = K Q^T (32 keys x 32 queries)
             // (the half's 8 K fragments are requested before the first MFMA,
             // so that the MFMAs do not wait on their reads one by one)
@@ -367,10 +369,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attention_fwd_kernel(AttnArgs arg
 
         // next block landed (this wave's loads; the barrier covers everyone's),
         // and every wave is done with this stage before it is refilled
-        if (t + 2 < nb)
-            wait_vmcnt<4>();
-        else
-            wait_vmcnt<0>();
+        wait_vmcnt<0>();
         {
             const int adv = (t % STAGES == STAGES - 1) ? -(STAGES - 1) * STAGE_BYTES : STAGE_BYTES;
 #pragma unroll
