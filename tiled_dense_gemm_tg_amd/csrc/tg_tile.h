@@ -1,6 +1,7 @@
-// tg_tile.h -- pieces shared by the two 256 x 256 tiled GEMM kernels: the
-// XCD-aware tile raster, buffer descriptors, the MFMA step and the fused
-// epilogue + store of a wave's 128 x 128 quarter of the C tile.
+// tg_tile.h -- pieces shared by the tiled GEMM kernels: the XCD-aware tile
+// raster (any tile size), buffer descriptors, and for the register-gathered
+// 256 x 256 kernel the MFMA step and the fused epilogue + store of a wave's
+// 128 x 128 quarter of the C tile.
 #pragma once
 
 #include "tg_device.h"
