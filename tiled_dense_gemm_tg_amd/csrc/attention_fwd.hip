@@ -287,20 +287,30 @@ __global__ __launch_bounds__(NTHREADS, 1) void attention_fwd_kernel(AttnArgs arg
         // scores, online softmax and the second product, which keeps only one
         // quarter's scores live.
         const bool need_mask = kb + BN > Sk || (CAUSAL && kb + BN - 1 > q0);
-#pragma unroll
-        for (int kt = 0; kt < BN / 32; ++kt) {
-            // ---- S^T = K Q^T (32 keys x 32 queries)
-            // (the half's 8 K fragments are requested before the first MFMA,
-            // so that the MFMAs do not wait on their reads one by one)
+        // ---- S^T = K Q^T (32 keys x 32 queries) of quarter kt: the 8 K
+        // fragments are requested before the first MFMA, so that the MFMAs
+        // do not wait on their reads one by one
+        auto scores = [&](int kt) __attribute__((always_inline)) {
             u32x4 kf[8];
 #pragma unroll
             for (int s = 0; s < 8; ++s)
                 kf[s] = lds_u4_at(kp[s] + 8192 * kt);   // + 32 rows
             __builtin_amdgcn_sched_barrier(0);
-            f32x16 sacc = f32x16{};
+            f32x16 sc = f32x16{};
 #pragma unroll
             for (int s = 0; s < 8; ++s)
-                sacc = T::mfma32(kf[s], qf[s], sacc);
+                sc = T::mfma32(kf[s], qf[s], sc);
+            return sc;
+        };
+        // The score MFMAs of quarter kt + 1 are issued before the softmax of
+        // quarter kt, so that the matrix unit works on them while the wave's
+        // vector ALU does the softmax.
+        f32x16 s_next = scores(0);
+#pragma unroll
+        for (int kt = 0; kt < BN / 32; ++kt) {
+            f32x16 sacc = s_next;
+            if (kt + 1 < BN / 32)
+                s_next = scores(kt + 1);
 
             // ---- online softmax: score e of the lane is key kb + 32 kt + 8 (e/4) + 4 lh + e%4
             // masking (only in blocks that need it) and the block maximum
