@@ -295,3 +295,12 @@ def test_tiles_plan_follows_the_cu_count(lib):
     # with 4x the CUs the 4096-cube has too few 256x256 tiles; with 1/4 the 2048-cube has enough
     assert tg.tg_gemm_tiles_plan(4096, 4096, 4096, 1024)[1] != tg.TG_TILES_256x256
     assert tg.tg_gemm_tiles_plan(2048, 2048, 2048, 64)[1] == tg.TG_TILES_256x256
+
+
+def test_smoke_cases_are_planned_as_smoke_expects(lib):
+    """smoke() asserts the family tg_gemm picks for each of its cases; the
+    plan is host logic, so check it here (allocations are at least 256-byte
+    aligned, as the made-up pointers are)."""
+    import __graft_entry__
+    for name, M, N, K, dtype, epi, want, _ in __graft_entry__.smoke_cases():
+        assert plan(M, N, K, dtype=dtype, epi=epi, bias=PBIAS if epi else None) == (tg.TG_OK, want), name
