@@ -19,7 +19,9 @@
 //     lane, one 16-byte load from L2) as its 16-column operand, so the 16
 //     MFMA columns are the (at most 16) rows of A;
 //   * loads come in batches of 2 steps, double-buffered in registers, so the
-//     next batch is in flight while the current one is multiplied;
+//     next batch is in flight while the current one is multiplied; a wave
+//     with at most 16 steps (K = 4096) first reads its whole slice of A into
+//     registers, so that its loop streams only B;
 //   * the 8 waves' fp32 partial sums are added in LDS in a fixed order (no
 //     atomics, so results are reproducible), then the fused epilogue and
 //     8-byte stores.
@@ -34,7 +36,13 @@ constexpr int SLAB = 64;       // columns per workgroup
 constexpr int WAVES = 8;       // waves per workgroup, splitting K
 constexpr int UNROLL = 2;      // 32-k steps per load batch (two batches in flight)
 constexpr int NTHREADS = 64 * WAVES;
+constexpr int PRE = 16;        // most 32-k steps per wave whose A slice is preloaded into registers
 constexpr uint32_t OOB = 0xFFFFFFF0u;    // byte offset beyond every operand
+
+struct APair {
+    u32x4 v[UNROLL];
+};
+__device__ __forceinline__ APair u32x4_pair(u32x4 a, u32x4 b) { return APair{{a, b}}; }
 
 template <class T, int EPI>
 __global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args) {
@@ -123,18 +131,56 @@ __global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args) {
     // range are masked, read nothing and give zeros.
     u32x2 vb0[UNROLL][8], vb1[UNROLL][8];
     u32x4 va0[UNROLL], va1[UNROLL];
-    load_batch(vb0, va0, s_begin);
-    for (int s0 = s_begin; s0 < s_end; s0 += 2 * UNROLL) {
-        load_batch(vb1, va1, s0 + UNROLL);
-        __builtin_amdgcn_sched_barrier(0);
-        mma_batch(vb0, va0);
-        __builtin_amdgcn_sched_barrier(0);
-        if (s0 + UNROLL >= s_end)
-            break;
-        load_batch(vb0, va0, s0 + 2 * UNROLL);
-        __builtin_amdgcn_sched_barrier(0);
-        mma_batch(vb1, va1);
-        __builtin_amdgcn_sched_barrier(0);
+    if (s_end - s_begin > PRE / 2 && s_end - s_begin <= PRE) {
+        // A wave with PRE / 2 < steps <= PRE (K = 4096 on 8 waves: 16) reads
+        // its whole slice of A (16 rows x 32 PRE k) into registers first, so
+        // the loop streams only B.
+        u32x4 pa[PRE];
+#pragma unroll
+        for (int i = 0; i < PRE; ++i) {
+            const int kb = (s_begin + i) * 32 + 8 * h;
+            const uint32_t mk = mask_of(s_begin + i < s_end && kb < K);
+            pa[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)((a_row + 2u * (uint32_t)kb) | mk), 0, 0);
+        }
+        auto load_b = [&](u32x2 (&vb)[UNROLL][8], int s0) __attribute__((always_inline)) {
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                const int kb = (s0 + u) * 32 + 8 * h;
+                const uint32_t mk = mask_of(s0 + u < s_end && kb < K);
+                const uint32_t boff = (uint32_t)kb * b_row + b_col;
+#pragma unroll
+                for (int r = 0; r < 8; ++r)
+                    vb[u][r] = __builtin_amdgcn_raw_buffer_load_b64(rb, (int)((boff + (uint32_t)r * b_row) | mk), 0,
+                                                                    0);
+            }
+        };
+        load_b(vb0, s_begin);
+#pragma unroll
+        for (int bi = 0; bi < PRE / UNROLL; bi += 2) {
+            load_b(vb1, s_begin + (bi + 1) * UNROLL);
+            __builtin_amdgcn_sched_barrier(0);
+            mma_batch(vb0, u32x4_pair(pa[bi * UNROLL], pa[bi * UNROLL + 1]).v);
+            __builtin_amdgcn_sched_barrier(0);
+            if (bi + 2 < PRE / UNROLL)
+                load_b(vb0, s_begin + (bi + 2) * UNROLL);
+            __builtin_amdgcn_sched_barrier(0);
+            mma_batch(vb1, u32x4_pair(pa[(bi + 1) * UNROLL], pa[(bi + 1) * UNROLL + 1]).v);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    } else {
+        load_batch(vb0, va0, s_begin);
+        for (int s0 = s_begin; s0 < s_end; s0 += 2 * UNROLL) {
+            load_batch(vb1, va1, s0 + UNROLL);
+            __builtin_amdgcn_sched_barrier(0);
+            mma_batch(vb0, va0);
+            __builtin_amdgcn_sched_barrier(0);
+            if (s0 + UNROLL >= s_end)
+                break;
+            load_batch(vb0, va0, s0 + 2 * UNROLL);
+            __builtin_amdgcn_sched_barrier(0);
+            mma_batch(vb1, va1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
 
     // acc[j][e] is D_j[row 4 h + e][col p]: C[m = p][n = nb + 16 h + 4 e + j].
