@@ -190,12 +190,13 @@ __global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args) {
         for (int e = 0; e < 4; ++e)
             red[wave][4 * e + j][lane] = acc[j][e];
     __syncthreads();
-    if (wave != 0)
+    // waves 0..3 each finish one of the four column groups e of every lane
+    if (wave >= 4)
         return;
 
     uint16_t *__restrict__ C = args.C;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
+    {
+        const int e = wave;
         const int n = nb + 16 * h + 4 * e;
         float y[4];
 #pragma unroll
@@ -207,7 +208,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args) {
             y[j] = s;
         }
         if (!row_ok || n >= N)
-            continue;
+            return;
         float bv[4] = {0.f, 0.f, 0.f, 0.f};
         if constexpr (EPI != EPI_NONE) {
             const u32x2 raw = *reinterpret_cast<const u32x2 *>(args.bias + n);
