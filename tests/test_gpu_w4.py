@@ -39,6 +39,8 @@ def _run(M, N, K, G, dtype, A, Q, S, bias, epi):
     (I.F16, 13, 1000, 256, 64, I.EPI_BIAS_GELU_TANH),    # ragged N, M < 16
     (I.BF16, 40, 300, 512, 256, I.EPI_BIAS),             # several 16-row blocks
     (I.F16, 7, 72, 96, 32, I.EPI_NONE),                  # fewer groups than waves
+    (I.F16, 9, 1001, 256, 64, I.EPI_BIAS),               # N % 4 != 0: scales read element by element
+    (I.BF16, 16, 70, 128, 32, I.EPI_BIAS_GELU_TANH),
 ])
 def test_w4_matches_oracle(dtype, M, N, K, G, epi):
     A = I.random_bits((M, K), ("normal", 0.0, 1.0), dtype, 500 + M)
@@ -77,3 +79,26 @@ def test_w4_empty_K_gives_epilogue_of_zero():
     assert st == tg.TG_OK
     torch.cuda.synchronize()
     check_exact(to_bits(out), refq, "w4 K=0")
+
+
+@pytest.mark.parametrize("dtype", [I.F16, I.BF16])
+def test_w4_scales_at_any_alignment(dtype):
+    """Scales starting 2 bytes past an 8-byte boundary (N % 4 == 0) take the
+    element-by-element scale loads; integer operands, exact."""
+    import torch
+    M, N, K, G = 16, 264, 256, 64
+    rng = np.random.Generator(np.random.PCG64(530))
+    A = I.small_int_bits((M, K), dtype, 531)
+    Q = I.w4_weights(K, N, 532)
+    S = I.values_bits(2.0 ** rng.integers(-3, 2, size=(K // G, N)), dtype)
+    _, refq = oracle.gemm_w4(M, N, K, dtype, A, Q, S, G)
+    packed = tg.w4_pack(torch.from_numpy(np.ascontiguousarray(Q)).cuda())
+    a = to_device(A.reshape(M, K), dtype)
+    flat = to_device(np.concatenate([np.zeros(1, np.uint16), S.reshape(-1)]), dtype)
+    s = flat[1:].view(K // G, N)
+    assert s.data_ptr() % 8 != 0
+    out = torch.full((M, N), float("nan"), dtype=a.dtype, device="cuda")
+    log(f"[w4 scales 2-byte aligned] dtype={dtype}")
+    tg.gemm_w4(a, packed, s, G, N, out=out)
+    torch.cuda.synchronize()
+    check_exact(to_bits(out), refq, "w4 misaligned scales")

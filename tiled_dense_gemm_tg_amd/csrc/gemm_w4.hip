@@ -78,7 +78,9 @@ struct GroupLoad {
     uint16_t s[4][4];   // [j][e] scale of column 16 j + 4 (l/16) + e
 };
 
-template <class T, int EPI, int GROUP>
+// SVEC: N % 4 == 0 and scales 8-byte aligned, so a lane's 4 consecutive
+// columns of a scale row come in one 8-byte load.
+template <class T, int EPI, int GROUP, bool SVEC>
 __global__ __launch_bounds__(NTHREADS) void gemm_w4_kernel(GemmArgs args, const uint8_t *__restrict__ packed,
                                                           const uint16_t *__restrict__ scales) {
     constexpr int STEPS = GROUP / 32;
@@ -120,14 +122,28 @@ __global__ __launch_bounds__(NTHREADS) void gemm_w4_kernel(GemmArgs args, const 
             g.w[u] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)masked(w_base + 1024u * t, live), 0, 0);
             g.a[u] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)masked(a_row + 64u * t, a_ok && live), 0, 0);
         }
+        if constexpr (SVEC) {
+            // columns n .. n + 3 are all below N or all past it (N % 4 == 0)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int n = n_lane + 16 * j + e;
+            for (int j = 0; j < 4; ++j) {
+                const int n = n_lane + 16 * j;
                 const uint32_t so = 2u * ((uint32_t)grp * (uint32_t)N + (uint32_t)n);
-                g.s[j][e] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)masked(so, live && n < N), 0, 0);
+                const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)masked(so, live && n < N), 0, 0);
+                g.s[j][0] = (uint16_t)(v.x & 0xffff);
+                g.s[j][1] = (uint16_t)(v.x >> 16);
+                g.s[j][2] = (uint16_t)(v.y & 0xffff);
+                g.s[j][3] = (uint16_t)(v.y >> 16);
             }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int n = n_lane + 16 * j + e;
+                    const uint32_t so = 2u * ((uint32_t)grp * (uint32_t)N + (uint32_t)n);
+                    g.s[j][e] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)masked(so, live && n < N), 0, 0);
+                }
+        }
     };
 
     f32x4 acc[4];
@@ -173,13 +189,14 @@ __global__ __launch_bounds__(NTHREADS) void gemm_w4_kernel(GemmArgs args, const 
         for (int e = 0; e < 4; ++e)
             red[wave][4 * j + e][lane] = acc[j][e];
     __syncthreads();
-    if (wave != 0)
+    // waves 0..3 each finish one column group j of every lane
+    if (wave >= 4)
         return;
     const int m = m0 + p;
     const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
         args.C, (short)0, (int)(2u * (uint32_t)M * (uint32_t)N), 0x00020000);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    {
+        const int j = wave;
         const int n = n_lane + 16 * j;
         uint16_t o[4];
 #pragma unroll
@@ -231,17 +248,33 @@ __global__ __launch_bounds__(256) void w4_pack_kernel(int K, int N, const uint8_
     out[d] = x;
 }
 
+template <class T, int EPI, bool SVEC>
+hipError_t launch_scales(const GemmArgs &a, const uint8_t *packed, const uint16_t *scales, int group,
+                         hipStream_t stream) {
+    const dim3 grid((a.N + 63) / 64, (a.M + 15) / 16);
+    switch (group) {
+    case 32:
+        hipLaunchKernelGGL((gemm_w4_kernel<T, EPI, 32, SVEC>), grid, dim3(NTHREADS), 0, stream, a, packed, scales);
+        break;
+    case 64:
+        hipLaunchKernelGGL((gemm_w4_kernel<T, EPI, 64, SVEC>), grid, dim3(NTHREADS), 0, stream, a, packed, scales);
+        break;
+    case 128:
+        hipLaunchKernelGGL((gemm_w4_kernel<T, EPI, 128, SVEC>), grid, dim3(NTHREADS), 0, stream, a, packed, scales);
+        break;
+    default:
+        hipLaunchKernelGGL((gemm_w4_kernel<T, EPI, 256, SVEC>), grid, dim3(NTHREADS), 0, stream, a, packed, scales);
+        break;
+    }
+    return hipGetLastError();
+}
+
 template <class T, int EPI>
 hipError_t launch_group(const GemmArgs &a, const uint8_t *packed, const uint16_t *scales, int group,
                         hipStream_t stream) {
-    const dim3 grid((a.N + 63) / 64, (a.M + 15) / 16);
-    switch (group) {
-    case 32: hipLaunchKernelGGL((gemm_w4_kernel<T, EPI, 32>), grid, dim3(NTHREADS), 0, stream, a, packed, scales); break;
-    case 64: hipLaunchKernelGGL((gemm_w4_kernel<T, EPI, 64>), grid, dim3(NTHREADS), 0, stream, a, packed, scales); break;
-    case 128: hipLaunchKernelGGL((gemm_w4_kernel<T, EPI, 128>), grid, dim3(NTHREADS), 0, stream, a, packed, scales); break;
-    default: hipLaunchKernelGGL((gemm_w4_kernel<T, EPI, 256>), grid, dim3(NTHREADS), 0, stream, a, packed, scales); break;
-    }
-    return hipGetLastError();
+    const bool svec = a.N % 4 == 0 && ((uintptr_t)scales & 7u) == 0;
+    return svec ? launch_scales<T, EPI, true>(a, packed, scales, group, stream)
+                : launch_scales<T, EPI, false>(a, packed, scales, group, stream);
 }
 
 template <class T>
