@@ -113,8 +113,7 @@ def log(msg: str) -> None:
 def time_gemm(torch, tg, w, sets, steps, warmup, unfused=False):
     """Per-launch time (ms) of tg_gemm (or, with `unfused`, of the three-launch
     tg_gemm_unfused) over `sets` rotating operand sets."""
-    stream = torch.cuda.current_stream()
-    handle = stream.cuda_stream
+    handle = torch.cuda.current_stream().cuda_stream
     calls = []
     for A, B, bias, C in sets:
         calls.append((A.data_ptr(), B.data_ptr(), bias.data_ptr() if bias is not None else None, C.data_ptr()))
@@ -126,6 +125,16 @@ def time_gemm(torch, tg, w, sets, steps, warmup, unfused=False):
         if st != tg.TG_OK:
             raise RuntimeError(f"tg_gemm failed: {tg.tg_status_string(st)}")
 
+    return time_calls(torch, launch, steps, warmup, with_wall=True)
+
+
+def time_calls(torch, launch, steps, warmup, with_wall=False):
+    """Per-launch time (ms) of launch(i) for i = 0 .. steps-1 on the current
+    stream: HIP events recorded on that stream around the timed launches,
+    after `warmup` untimed ones and a synchronisation; with `with_wall`, also
+    the host's wall time (s) from before the first timed launch to after the
+    closing synchronisation."""
+    stream = torch.cuda.current_stream()
     for i in range(warmup):
         launch(i)
     torch.cuda.synchronize()
@@ -138,23 +147,8 @@ def time_gemm(torch, tg, w, sets, steps, warmup, unfused=False):
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return ev0.elapsed_time(ev1) / steps, wall
-
-
-def time_calls(torch, launch, steps, warmup):
-    """Per-launch time (ms) of launch(i) for i = 0 .. steps-1 on the current stream."""
-    stream = torch.cuda.current_stream()
-    for i in range(warmup):
-        launch(i)
-    torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for i in range(steps):
-        launch(i)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    return ev0.elapsed_time(ev1) / steps
+    ms = ev0.elapsed_time(ev1) / steps
+    return (ms, wall) if with_wall else ms
 
 
 def bench_w4(torch, tg, I, steps, warmup, copies=16):
@@ -332,7 +326,6 @@ def device_operands(torch, I, w, copies=1):
     tdt = torch.float16 if w.dtype == I.F16 else torch.bfloat16
 
     def dev(bits, shape):
-        import numpy as np
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(tdt).reshape(shape).to("cuda")
 
     A = dev(ops.A, (w.M, w.K))
@@ -348,7 +341,6 @@ def device_operands(torch, I, w, copies=1):
 
 def cpu_baseline(I, w, ops, budget_s):
     """The oracle on a bounded sample of rows of workload w (test infrastructure)."""
-    import numpy as np
     import oracle
     probes = []
     for k in (2, 34):
