@@ -181,6 +181,61 @@ tg_status tg_gemm_tiled(tg_tiles tiles, int64_t M, int64_t N, int64_t K, tg_dtyp
 tg_status tg_gemm_tiles_plan(int64_t M, int64_t N, int64_t K, int num_cu, tg_tiles *tiles_out);
 
 /*
+ * Split-K for the TG_PATH_SKINNY family.  A decode-shaped product (M <= 16)
+ * costs what it takes to stream B from HBM once ("TileLang: writing LLM GPU
+ * kernels by thinking in tiles", section 2, "A back-of-the-envelope
+ * calculation"), and the skinny kernel gives each 64-column slab of B to one
+ * workgroup, so a narrow B (N = 4096: 64 slabs) leaves most of a 256-CU
+ * device idle.  The pages have no split-K; this library adds one: the K range
+ * of each slab is divided over `splits` workgroups, each writes its fp32
+ * partial 16 x 64 block to a workspace and counts itself in that slab's
+ * counter, and the last to arrive adds the partials in split order, applies
+ * the epilogue and stores C.  No workgroup waits for another.
+ *
+ * tg_gemm_split: as tg_gemm, with the skinny family's K range split over
+ * `splits` workgroups per slab (0: the library's choice, reported by
+ * tg_gemm_split_plan for the device of `stream`; 1: no split, no workspace;
+ * at most 64).  Shapes that do not take the skinny path run as in tg_gemm
+ * and leave the workspace alone.
+ *   workspace        device memory, 16-byte aligned, at least
+ *                    tg_gemm_split_workspace_bytes(N, splits) bytes (NULL
+ *                    allowed when that is 0), not overlapping A, B, bias or
+ *                    C.  Its first 4 ceil(N / 64) bytes are counters that
+ *                    must be zero before the first call (zero-fill the
+ *                    workspace once); every call that completes leaves
+ *                    them zero.  Calls that may run at the same time
+ *                    (other streams) need workspaces of their own.
+ *   workspace_bytes  its size in bytes.
+ * TG_ERR_INVALID_ARG for splits outside 0..64 or a workspace that is
+ * missing, too small, misaligned or overlapping; otherwise the argument
+ * rules and results of tg_gemm (to the tolerance of fp32 accumulation in
+ * another order; bit-identical on integer-valued inputs, and the same for
+ * every call with the same splits).
+ */
+tg_status tg_gemm_split(int splits, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
+                        const void *A, const void *B, const void *bias, tg_epilogue epilogue,
+                        void *C, void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
+ * Workspace bytes tg_gemm_split needs for N columns and `splits` splits
+ * (0 for splits <= 1; -1 for N outside 0..2^30 or splits outside 0..64).
+ * Pure host code.
+ */
+int64_t tg_gemm_split_workspace_bytes(int64_t N, int splits);
+
+/*
+ * The split count tg_gemm_split(0, ...) uses for an M x N x K product on a
+ * device with num_cu compute units (num_cu <= 0: 256), in *splits_out (1 for
+ * M > 16 or an empty product), and the workspace bytes it needs, in
+ * *workspace_bytes_out.  The count is the largest with slabs x splits at
+ * most num_cu (one round of workgroups; a second costs more than splitting
+ * gains) and at least 16 32-k steps per workgroup.  TG_ERR_INVALID_ARG
+ * for negative or too large sizes or NULL outputs.  Pure host code.
+ */
+tg_status tg_gemm_split_plan(int64_t M, int64_t N, int64_t K, int num_cu, int *splits_out,
+                             int64_t *workspace_bytes_out);
+
+/*
  * Elementwise epilogue steps as passes of their own over a matrix in device
  * memory -- the unfused form of the epilogue that the fourth TileLang page
  * ("Designing high-performance GPU kernels with TileLang", part 3 "Epilogue
@@ -258,6 +313,41 @@ tg_status tg_w4_pack(int64_t K, int64_t N, const void *q, void *packed, void *st
 tg_status tg_gemm_w4(int64_t M, int64_t N, int64_t K, tg_dtype dtype, const void *A, const void *packed,
                      const void *scales, int64_t group, const void *bias, tg_epilogue epilogue, void *C,
                      void *stream);
+
+/*
+ * Split-K of the 4-bit product, as tg_gemm_split is for the skinny kernel
+ * (same workspace protocol, not on the pages): the scale groups of each
+ * output block (16 rows x 64 columns) are divided over `splits` workgroups
+ * (0: the library's choice, tg_gemm_w4_split_plan for the device of
+ * `stream`; 1: no split; at most 64).  workspace: device memory, 16-byte
+ * aligned, at least tg_gemm_w4_split_workspace_bytes(M, N, splits) bytes,
+ * overlapping no operand, its first 4 ceil(M / 16) ceil(N / 64) bytes zero
+ * before the first call and left zero by every completed call; one per
+ * stream.  TG_ERR_INVALID_ARG for splits outside 0..64 or a missing, small,
+ * misaligned or overlapping workspace; otherwise the rules and results of
+ * tg_gemm_w4 (to the tolerance of fp32 accumulation in another order;
+ * bit-identical on integer-valued inputs and from call to call).
+ */
+tg_status tg_gemm_w4_split(int splits, int64_t M, int64_t N, int64_t K, tg_dtype dtype, const void *A,
+                           const void *packed, const void *scales, int64_t group, const void *bias,
+                           tg_epilogue epilogue, void *C, void *workspace, int64_t workspace_bytes,
+                           void *stream);
+
+/* Workspace bytes of tg_gemm_w4_split for an M x N output and `splits`
+ * splits (0 for splits <= 1; -1 for sizes outside the limits of tg_gemm_w4
+ * or splits outside 0..64).  Pure host code. */
+int64_t tg_gemm_w4_split_workspace_bytes(int64_t M, int64_t N, int splits);
+
+/*
+ * The split count tg_gemm_w4_split(0, ...) uses on a device with num_cu
+ * compute units (num_cu <= 0: 256) and its workspace bytes: the largest
+ * count with ceil(M / 16) ceil(N / 64) splits at most num_cu and at least 8
+ * scale groups (one per wave) per workgroup; 1 for an empty product.
+ * TG_ERR_INVALID_ARG for invalid sizes or group, or NULL outputs.  Pure
+ * host code.
+ */
+tg_status tg_gemm_w4_split_plan(int64_t M, int64_t N, int64_t K, int64_t group, int num_cu, int *splits_out,
+                                int64_t *workspace_bytes_out);
 
 /*
  * Attention forward, the fused kernel the TileLang pages build around the same

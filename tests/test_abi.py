@@ -304,3 +304,79 @@ def test_smoke_cases_are_planned_as_smoke_expects(lib):
     import __graft_entry__
     for name, M, N, K, dtype, epi, want, _ in __graft_entry__.smoke_cases():
         assert plan(M, N, K, dtype=dtype, epi=epi, bias=PBIAS if epi else None) == (tg.TG_OK, want), name
+
+
+# ------------------------------------------------------------ split-K
+
+def test_split_workspace_bytes(lib):
+    # counters (4 bytes per 64-column slab, padded to 256), then 4 KiB per slab and split
+    assert tg.tg_gemm_split_workspace_bytes(4096, 4) == 256 + 64 * 4 * 4096
+    assert tg.tg_gemm_split_workspace_bytes(11008, 2) == 768 + 172 * 2 * 4096
+    assert tg.tg_gemm_split_workspace_bytes(4100, 3) == 512 + 65 * 3 * 4096
+    for splits in (0, 1):
+        assert tg.tg_gemm_split_workspace_bytes(4096, splits) == 0
+    assert tg.tg_gemm_split_workspace_bytes(0, 8) == 0
+    for N, splits in ((-1, 2), (4096, -1), (4096, 65), (2 ** 30 + 1, 2)):
+        assert tg.tg_gemm_split_workspace_bytes(N, splits) == -1
+
+
+def test_split_entry_point_checks_arguments(lib):
+    ws = 0x7F4000000000
+    need = tg.tg_gemm_split_workspace_bytes(4096, 4)
+
+    def call(splits, M=16, N=4096, K=4096, ws=ws, nbytes=need, C=PC, bias=None, epi=I.EPI_NONE):
+        return tg.tg_gemm_split(splits, M, N, K, I.F16, PA, PB, bias, epi, C, ws, nbytes, None)
+
+    for bad in (-1, 65, 1000):
+        assert call(bad) == tg.TG_ERR_INVALID_ARG
+    assert call(4, nbytes=-1) == tg.TG_ERR_INVALID_ARG
+    assert call(4, ws=None) == tg.TG_ERR_INVALID_ARG                      # a split needs a workspace
+    assert call(4, nbytes=need - 1) == tg.TG_ERR_INVALID_ARG              # too small
+    assert call(4, ws=ws + 8) == tg.TG_ERR_INVALID_ARG                    # not 16-byte aligned
+    assert call(4, ws=PC + 1024) == tg.TG_ERR_INVALID_ARG                 # overlaps C
+    assert call(4, ws=PA) == tg.TG_ERR_INVALID_ARG                        # overlaps A
+    assert call(4, ws=PB + 4096) == tg.TG_ERR_INVALID_ARG                 # overlaps B
+    assert call(4, ws=PBIAS, bias=PBIAS, epi=I.EPI_BIAS) == tg.TG_ERR_INVALID_ARG
+    # tg_gemm's own rules come first
+    assert call(4, bias=PBIAS) == tg.TG_ERR_INVALID_ARG                   # bias with no epilogue
+    assert call(4, C=PA + 64) == tg.TG_ERR_INVALID_ARG                    # C overlapping A
+    # nothing to compute: a no-op whatever the workspace, without a GPU
+    assert tg.tg_gemm_split(4, 0, 4096, 4096, I.F16, None, None, None, I.EPI_NONE, None, None, 0, None) == tg.TG_OK
+
+
+def test_split_plan_checks_arguments(lib):
+    st = ctypes.c_int()
+    nb = ctypes.c_int64()
+    assert lib.tg_gemm_split_plan(16, 4096, 4096, 256, None, ctypes.byref(nb)) == tg.TG_ERR_INVALID_ARG
+    assert lib.tg_gemm_split_plan(16, 4096, 4096, 256, ctypes.byref(st), None) == tg.TG_ERR_INVALID_ARG
+    for M, N, K in ((-1, 64, 64), (16, -1, 64), (16, 64, -1), (16, 2 ** 30 + 1, 64)):
+        assert tg.tg_gemm_split_plan(M, N, K, 256)[0] == tg.TG_ERR_INVALID_ARG
+    # off the skinny path, and empty products, never split
+    assert tg.tg_gemm_split_plan(17, 4096, 11008, 256) == (tg.TG_OK, 1, 0)
+    assert tg.tg_gemm_split_plan(0, 4096, 11008, 256) == (tg.TG_OK, 1, 0)
+    assert tg.tg_gemm_split_plan(16, 0, 11008, 256) == (tg.TG_OK, 1, 0)
+
+
+def test_split_plan_workspace_matches_its_split_count(lib):
+    for M, N, K in ((16, 4096, 11008), (16, 11008, 4096), (1, 2048, 8192), (16, 4096, 256), (8, 64, 65536)):
+        for cus in (0, 64, 256, 1024):
+            st, splits, nbytes = tg.tg_gemm_split_plan(M, N, K, cus)
+            assert st == tg.TG_OK and 1 <= splits <= 64
+            assert nbytes == tg.tg_gemm_split_workspace_bytes(N, splits)
+            assert 32 * 16 * splits <= max(K, 32 * 16) + 31       # at least 16 32-k steps per split
+
+
+@pytest.mark.parametrize("M,N,K,splits", [
+    (16, 4096, 11008, 4),     # 64 slabs: four splits fill 256 CUs
+    (16, 4096, 4096, 4),
+    (16, 1024, 4096, 8),      # 16 slabs: 16 splits would leave 8 steps each; 8 keeps 16
+    (16, 11008, 4096, 1),     # 172 slabs: a second round of workgroups costs more than a split gains
+    (8, 28672, 4096, 1),
+    (16, 4096, 256, 1),       # 8 steps in all: too few to split
+    (1, 64, 65536, 64),       # one slab, deep K: capped at 64 splits
+])
+def test_split_plan_on_an_mi355x(lib, M, N, K, splits):
+    st, got, nbytes = tg.tg_gemm_split_plan(M, N, K, 256)
+    assert (st, got) == (tg.TG_OK, splits)
+    assert tg.tg_gemm_split_plan(M, N, K, 0)[1] == splits              # 0: 256 CUs assumed
+    assert nbytes == tg.tg_gemm_split_workspace_bytes(N, splits)

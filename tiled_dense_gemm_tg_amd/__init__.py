@@ -43,8 +43,10 @@ TG_TILES_128x128 = 4
 TILES_NAMES = {TG_TILES_AUTO: "auto", TG_TILES_256x256: "256x256", TG_TILES_256x128: "256x128",
                TG_TILES_128x256: "128x256", TG_TILES_128x128: "128x128"}
 
-EXPORTED = ("tg_gemm", "tg_gemm_path", "tg_gemm_plan", "tg_gemm_tiled", "tg_gemm_tiles_plan", "tg_elementwise", "tg_gemm_unfused", "tg_w4_packed_bytes",
-            "tg_w4_pack", "tg_gemm_w4", "tg_attention_fwd", "tg_status_string", "tg_version")
+EXPORTED = ("tg_gemm", "tg_gemm_path", "tg_gemm_plan", "tg_gemm_tiled", "tg_gemm_tiles_plan", "tg_gemm_split",
+            "tg_gemm_split_workspace_bytes", "tg_gemm_split_plan", "tg_elementwise", "tg_gemm_unfused",
+            "tg_w4_packed_bytes", "tg_w4_pack", "tg_gemm_w4", "tg_gemm_w4_split", "tg_gemm_w4_split_workspace_bytes",
+            "tg_gemm_w4_split_plan", "tg_attention_fwd", "tg_status_string", "tg_version")
 
 _lib = None
 
@@ -79,6 +81,12 @@ def load_library():
     lib.tg_gemm_tiled.restype = ci
     lib.tg_gemm_tiles_plan.argtypes = [i64, i64, i64, ci, ctypes.POINTER(ci)]
     lib.tg_gemm_tiles_plan.restype = ci
+    lib.tg_gemm_split.argtypes = [ci, i64, i64, i64, ci, vp, vp, vp, ci, vp, vp, i64, vp]
+    lib.tg_gemm_split.restype = ci
+    lib.tg_gemm_split_workspace_bytes.argtypes = [i64, ci]
+    lib.tg_gemm_split_workspace_bytes.restype = i64
+    lib.tg_gemm_split_plan.argtypes = [i64, i64, i64, ci, ctypes.POINTER(ci), ctypes.POINTER(i64)]
+    lib.tg_gemm_split_plan.restype = ci
     lib.tg_elementwise.argtypes = [ci, i64, i64, ci, vp, vp, vp, vp]
     lib.tg_elementwise.restype = ci
     lib.tg_gemm_unfused.argtypes = [i64, i64, i64, ci, vp, vp, vp, ci, vp, vp]
@@ -89,6 +97,12 @@ def load_library():
     lib.tg_w4_pack.restype = ci
     lib.tg_gemm_w4.argtypes = [i64, i64, i64, ci, vp, vp, vp, i64, vp, ci, vp, vp]
     lib.tg_gemm_w4.restype = ci
+    lib.tg_gemm_w4_split.argtypes = [ci, i64, i64, i64, ci, vp, vp, vp, i64, vp, ci, vp, vp, i64, vp]
+    lib.tg_gemm_w4_split.restype = ci
+    lib.tg_gemm_w4_split_workspace_bytes.argtypes = [i64, i64, ci]
+    lib.tg_gemm_w4_split_workspace_bytes.restype = i64
+    lib.tg_gemm_w4_split_plan.argtypes = [i64, i64, i64, i64, ci, ctypes.POINTER(ci), ctypes.POINTER(i64)]
+    lib.tg_gemm_w4_split_plan.restype = ci
     lib.tg_attention_fwd.argtypes = [i64, i64, i64, i64, i64, ci, vp, vp, vp, ci, ctypes.c_float, vp, vp]
     lib.tg_attention_fwd.restype = ci
     lib.tg_status_string.argtypes = [ci]
@@ -126,6 +140,40 @@ def tg_gemm_tiles_plan(M, N, K, num_cu=0):
     return st, out.value
 
 
+def tg_gemm_split(splits, M, N, K, dtype, A, B, bias, epilogue, C, workspace, workspace_bytes, stream) -> int:
+    return load_library().tg_gemm_split(splits, M, N, K, dtype, A, B, bias, epilogue, C, workspace,
+                                        workspace_bytes, stream)
+
+
+def tg_gemm_split_workspace_bytes(N, splits) -> int:
+    return load_library().tg_gemm_split_workspace_bytes(N, splits)
+
+
+def tg_gemm_split_plan(M, N, K, num_cu=0):
+    """Returns (status, splits, workspace bytes) that tg_gemm_split(0, ...) uses."""
+    splits, nbytes = ctypes.c_int(-1), ctypes.c_int64(-1)
+    st = load_library().tg_gemm_split_plan(M, N, K, num_cu, ctypes.byref(splits), ctypes.byref(nbytes))
+    return st, splits.value, nbytes.value
+
+
+def split_workspace(M, N, K, splits=0, device=None):
+    """A zero-filled workspace (uint8 torch tensor) for tg_gemm_split with
+    `splits` (0: the count the library chooses on `device`), or None when
+    that needs none."""
+    import torch
+    device = torch.device("cuda" if device is None else device)
+    if splits == 0:
+        cus = torch.cuda.get_device_properties(device).multi_processor_count
+        st, _, nbytes = tg_gemm_split_plan(M, N, K, cus)
+        if st != TG_OK:
+            raise TgError(st, "tg_gemm_split_plan")
+    else:
+        nbytes = tg_gemm_split_workspace_bytes(N, splits)
+        if nbytes < 0:
+            raise TgError(TG_ERR_INVALID_ARG, "tg_gemm_split_workspace_bytes")
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device) if nbytes > 0 else None
+
+
 def tg_elementwise(op, M, N, dtype, bias, X, Y, stream) -> int:
     return load_library().tg_elementwise(op, M, N, dtype, bias, X, Y, stream)
 
@@ -146,6 +194,41 @@ def tg_gemm_w4(M, N, K, dtype, A, packed, scales, group, bias, epilogue, C, stre
     return load_library().tg_gemm_w4(M, N, K, dtype, A, packed, scales, group, bias, epilogue, C, stream)
 
 
+def tg_gemm_w4_split(splits, M, N, K, dtype, A, packed, scales, group, bias, epilogue, C, workspace,
+                     workspace_bytes, stream) -> int:
+    return load_library().tg_gemm_w4_split(splits, M, N, K, dtype, A, packed, scales, group, bias, epilogue, C,
+                                           workspace, workspace_bytes, stream)
+
+
+def tg_gemm_w4_split_workspace_bytes(M, N, splits) -> int:
+    return load_library().tg_gemm_w4_split_workspace_bytes(M, N, splits)
+
+
+def tg_gemm_w4_split_plan(M, N, K, group, num_cu=0):
+    """Returns (status, splits, workspace bytes) that tg_gemm_w4_split(0, ...) uses."""
+    splits, nbytes = ctypes.c_int(-1), ctypes.c_int64(-1)
+    st = load_library().tg_gemm_w4_split_plan(M, N, K, group, num_cu, ctypes.byref(splits), ctypes.byref(nbytes))
+    return st, splits.value, nbytes.value
+
+
+def w4_split_workspace(M, N, K, group, splits=0, device=None):
+    """A zero-filled workspace (uint8 torch tensor) for tg_gemm_w4_split with
+    `splits` (0: the count the library chooses on `device`), or None when
+    that needs none."""
+    import torch
+    device = torch.device("cuda" if device is None else device)
+    if splits == 0:
+        cus = torch.cuda.get_device_properties(device).multi_processor_count
+        st, _, nbytes = tg_gemm_w4_split_plan(M, N, K, group, cus)
+        if st != TG_OK:
+            raise TgError(st, "tg_gemm_w4_split_plan")
+    else:
+        nbytes = tg_gemm_w4_split_workspace_bytes(M, N, splits)
+        if nbytes < 0:
+            raise TgError(TG_ERR_INVALID_ARG, "tg_gemm_w4_split_workspace_bytes")
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device) if nbytes > 0 else None
+
+
 def tg_attention_fwd(batch, Sq, Sk, heads, head_dim, dtype, Q, K, V, causal, scale, O, stream) -> int:
     return load_library().tg_attention_fwd(batch, Sq, Sk, heads, head_dim, dtype, Q, K, V, causal, scale, O, stream)
 
@@ -162,7 +245,7 @@ _EPI = {"none": EPI_NONE, "bias": EPI_BIAS, "bias_gelu_tanh": EPI_BIAS_GELU_TANH
 
 
 def gemm(A, B, bias=None, epilogue: str = "none", out=None, path: int = TG_PATH_AUTO, stream=None,
-         unfused: bool = False, tiles: int = TG_TILES_AUTO):
+         unfused: bool = False, tiles: int = TG_TILES_AUTO, splits=None, workspace=None):
     """epilogue(A @ B [+ bias]) on torch device tensors (fp16 or bf16, row-major).
 
     Returns ``out`` (allocated when not given).  Runs on ``stream`` or torch's
@@ -170,7 +253,11 @@ def gemm(A, B, bias=None, epilogue: str = "none", out=None, path: int = TG_PATH_
     tg_gemm_unfused (the product, then the epilogue steps as separate passes;
     ``path`` must then be TG_PATH_AUTO).  A ``tiles`` configuration other than
     TG_TILES_AUTO calls tg_gemm_tiled (the tiled family with that tile size;
-    ``path`` must then be TG_PATH_AUTO or TG_PATH_TILED).
+    ``path`` must then be TG_PATH_AUTO or TG_PATH_TILED).  ``splits`` (0 for
+    the library's choice) calls tg_gemm_split with ``workspace`` (a
+    zero-filled uint8 GPU tensor from :func:`split_workspace`, allocated here
+    when not given; reuse one per stream to skip that); ``path`` must then be
+    TG_PATH_AUTO.
     """
     import torch
     if A.dtype not in (torch.float16, torch.bfloat16):
@@ -197,6 +284,22 @@ def gemm(A, B, bias=None, epilogue: str = "none", out=None, path: int = TG_PATH_
     s = (stream if stream is not None else torch.cuda.current_stream(A.device)).cuda_stream
     if tiles != TG_TILES_AUTO and (unfused or path not in (TG_PATH_AUTO, TG_PATH_TILED)):
         raise ValueError("a tile configuration applies to the tiled family only")
+    if splits is not None and (unfused or path != TG_PATH_AUTO or tiles != TG_TILES_AUTO):
+        raise ValueError("split-K goes with the library's own choice of kernel")
+    if workspace is not None and splits is None:
+        raise ValueError("a workspace goes with split-K (splits)")
+    if splits is not None:
+        if workspace is None:
+            workspace = split_workspace(M, N, K, splits, A.device)
+        elif workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous uint8 GPU tensor")
+        st = tg_gemm_split(splits, M, N, K, dtype, A.data_ptr(), B.data_ptr(),
+                           bias.data_ptr() if bias is not None else None, epi, out.data_ptr(),
+                           workspace.data_ptr() if workspace is not None else None,
+                           workspace.numel() if workspace is not None else 0, s)
+        if st != TG_OK:
+            raise TgError(st, "tg_gemm_split")
+        return out
     if unfused:
         if path != TG_PATH_AUTO:
             raise ValueError("the unfused form chooses its own kernel family")
@@ -263,10 +366,13 @@ def w4_pack(q, stream=None):
     return packed
 
 
-def gemm_w4(A, packed, scales, group: int, N: int, bias=None, epilogue: str = "none", out=None, stream=None):
+def gemm_w4(A, packed, scales, group: int, N: int, bias=None, epilogue: str = "none", out=None, stream=None,
+            splits=None, workspace=None):
     """epilogue(A @ W [+ bias]) with W[k, n] = (q[k, n] - 8) * scales[k // group, n]
     and q packed by :func:`w4_pack`; A (M, K) and scales (K // group, N) share
-    one 16-bit dtype."""
+    one 16-bit dtype.  ``splits`` (0 for the library's choice) calls
+    tg_gemm_w4_split with ``workspace`` (from :func:`w4_split_workspace`,
+    allocated here when not given)."""
     import torch
     if A.dtype not in (torch.float16, torch.bfloat16) or A.dim() != 2:
         raise TypeError("A must be a 2-D float16 or bfloat16 tensor")
@@ -283,6 +389,20 @@ def gemm_w4(A, packed, scales, group: int, N: int, bias=None, epilogue: str = "n
             raise ValueError(f"{name} must be a contiguous GPU tensor")
     dtype = F16 if A.dtype == torch.float16 else BF16
     s = (stream if stream is not None else torch.cuda.current_stream(A.device)).cuda_stream
+    if workspace is not None and splits is None:
+        raise ValueError("a workspace goes with split-K (splits)")
+    if splits is not None:
+        if workspace is None:
+            workspace = w4_split_workspace(M, N, K, group, splits, A.device)
+        elif workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous uint8 GPU tensor")
+        st = tg_gemm_w4_split(splits, M, N, K, dtype, A.data_ptr(), packed.data_ptr(), scales.data_ptr(), group,
+                              bias.data_ptr() if bias is not None else None, epi, out.data_ptr(),
+                              workspace.data_ptr() if workspace is not None else None,
+                              workspace.numel() if workspace is not None else 0, s)
+        if st != TG_OK:
+            raise TgError(st, "tg_gemm_w4_split")
+        return out
     st = tg_gemm_w4(M, N, K, dtype, A.data_ptr(), packed.data_ptr(), scales.data_ptr(), group,
                     bias.data_ptr() if bias is not None else None, epi, out.data_ptr(), s)
     if st != TG_OK:

@@ -24,10 +24,15 @@
 //     registers, so that its loop streams only B;
 //   * the 8 waves' fp32 partial sums are added in LDS in a fixed order (no
 //     atomics, so results are reproducible), then the fused epilogue and
-//     8-byte stores.
+//     8-byte stores;
+//   * split-K (splits > 1, a grid of slabs x splits): when there are too few
+//     slabs to fill the chip, each slab's K range is also divided over
+//     `splits` workgroups, which pass their partial slabs through a
+//     workspace; the last to arrive adds them in split order and finishes.
 // Loads are range-checked buffer loads; k >= K reads zero in both operands.
 #include "tg_device.h"
 #include "tg_launch.h"
+#include "tg_split.h"
 
 namespace tg {
 namespace {
@@ -45,7 +50,7 @@ struct APair {
 __device__ __forceinline__ APair u32x4_pair(u32x4 a, u32x4 b) { return APair{{a, b}}; }
 
 template <class T, int EPI>
-__global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args) {
+__global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args, SplitWs ws) {
     __shared__ float red[WAVES][16][64];
     const int M = args.M, N = args.N, K = args.K;
     const uint16_t *__restrict__ A = args.A;
@@ -59,9 +64,15 @@ __global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args) {
     const int ncol = nb + 4 * p;              // N % 4 == 0: all four columns valid or none
     const bool row_ok = p < M;
 
+    // this workgroup's part of the 32-k steps (all of them without split-K),
+    // divided over its waves
     const int steps = (K + 31) / 32;
-    const int s_begin = (int)(((int64_t)steps * wave) / WAVES);
-    const int s_end = (int)(((int64_t)steps * (wave + 1)) / WAVES);
+    const int splits = ws.splits;
+    const int split = blockIdx.y;
+    const int sp_begin = (int)(((int64_t)steps * split) / splits);
+    const int sp_len = (int)(((int64_t)steps * (split + 1)) / splits) - sp_begin;
+    const int s_begin = sp_begin + (int)(((int64_t)sp_len * wave) / WAVES);
+    const int s_end = sp_begin + (int)(((int64_t)sp_len * (wave + 1)) / WAVES);
 
     f32x4 acc[4];
 #pragma unroll
@@ -191,14 +202,9 @@ __global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args) {
             red[wave][4 * e + j][lane] = acc[j][e];
     __syncthreads();
     // waves 0..3 each finish one of the four column groups e of every lane
-    if (wave >= 4)
-        return;
-
-    uint16_t *__restrict__ C = args.C;
-    {
-        const int e = wave;
-        const int n = nb + 16 * h + 4 * e;
-        float y[4];
+    const int e = wave & 3;
+    float y[4] = {0.f, 0.f, 0.f, 0.f};
+    if (wave < 4) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             float s = 0.f;
@@ -207,6 +213,15 @@ __global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args) {
                 s += red[w][4 * e + j][lane];
             y[j] = s;
         }
+    }
+    if (splits > 1 && !split_exchange(ws, blockIdx.x, split, y, e))
+        return;
+    if (wave >= 4)
+        return;
+
+    uint16_t *__restrict__ C = args.C;
+    {
+        const int n = nb + 16 * h + 4 * e;
         if (!row_ok || n >= N)
             return;
         float bv[4] = {0.f, 0.f, 0.f, 0.f};
@@ -226,25 +241,25 @@ __global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args) {
 }
 
 template <class T, int EPI>
-hipError_t launch_typed(const GemmArgs &a, hipStream_t stream) {
+hipError_t launch_typed(const GemmArgs &a, const SplitWs &ws, hipStream_t stream) {
     const int slabs = (a.N + SLAB - 1) / SLAB;
-    hipLaunchKernelGGL((gemm_skinny_kernel<T, EPI>), dim3(slabs), dim3(NTHREADS), 0, stream, a);
+    hipLaunchKernelGGL((gemm_skinny_kernel<T, EPI>), dim3(slabs, ws.splits), dim3(NTHREADS), 0, stream, a, ws);
     return hipGetLastError();
 }
 
 template <class T>
-hipError_t launch_epi(int epi, const GemmArgs &a, hipStream_t stream) {
+hipError_t launch_epi(int epi, const GemmArgs &a, const SplitWs &ws, hipStream_t stream) {
     switch (epi) {
-    case EPI_NONE: return launch_typed<T, EPI_NONE>(a, stream);
-    case EPI_BIAS: return launch_typed<T, EPI_BIAS>(a, stream);
-    default: return launch_typed<T, EPI_BIAS_GELU_TANH>(a, stream);
+    case EPI_NONE: return launch_typed<T, EPI_NONE>(a, ws, stream);
+    case EPI_BIAS: return launch_typed<T, EPI_BIAS>(a, ws, stream);
+    default: return launch_typed<T, EPI_BIAS_GELU_TANH>(a, ws, stream);
     }
 }
 
 }  // namespace
 
-hipError_t launch_skinny(int dtype, int epi, const GemmArgs &a, hipStream_t stream) {
-    return dtype == 0 ? launch_epi<F16>(epi, a, stream) : launch_epi<BF16>(epi, a, stream);
+hipError_t launch_skinny(int dtype, int epi, const GemmArgs &a, const SplitWs &ws, hipStream_t stream) {
+    return dtype == 0 ? launch_epi<F16>(epi, a, ws, stream) : launch_epi<BF16>(epi, a, ws, stream);
 }
 
 }  // namespace tg

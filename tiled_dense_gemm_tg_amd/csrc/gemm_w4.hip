@@ -25,11 +25,15 @@
 // j is column 16 j + l % 16) and A as the 16-column operand.  The MFMA
 // multiplies the integers q - 8 (exact in both 16-bit formats), and the
 // group's scale is applied once per group to the fp32 partial product, so
-// each weight is rounded nowhere.  One group's loads are in flight while the
-// previous group is multiplied; the waves' sums are added in LDS in a fixed
-// order, then the fused epilogue and the stores.
+// each weight is rounded nowhere.  Each wave keeps 16 steps' loads in flight
+// (8 with 32-k groups) in a ring of scale groups, refilling a group's slot as
+// soon as it has been multiplied; the waves' sums are added in LDS in a fixed
+// order, then the fused epilogue and the stores.  With split-K (splits > 1,
+// a grid of slabs x row blocks x splits) each workgroup takes a part of the
+// scale groups and the partial blocks meet through the workspace.
 #include "tg_device.h"
 #include "tg_launch.h"
+#include "tg_split.h"
 
 namespace tg {
 namespace {
@@ -49,41 +53,70 @@ __device__ __forceinline__ uint32_t masked(uint32_t off, bool ok) {
     return off | m;
 }
 
-// Pair m (m = 0..3) of the 8 nibbles: k-indices 2m (low half) and 2m+1 as
-// 16-bit q - 8 values of the format of T.
+// (x & mask) | bits in one instruction (the two constants stay in registers:
+// a three-operand instruction takes no literal here).
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t bits) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(mask), "v"(bits));
+    return r;
+}
+
+// The 8 nibbles of x as 16-bit q - 8 values of the format of T, pair m
+// (k-indices 2m in the low half, 2m+1 in the high half) from the nibbles at
+// bits 4m and 16 + 4m.
 template <class T>
-__device__ __forceinline__ uint32_t dequant_pair(uint32_t x, int m) {
-    const uint32_t magic = ((x >> (4 * m)) & 0x000F000Fu) | 0x64006400u;   // fp16 1024 + q
-    const h2 v = __builtin_bit_cast(h2, magic) - h2{(_Float16)1032.0f, (_Float16)1032.0f};
+__device__ __forceinline__ u32x4 dequant8(uint32_t x, uint32_t magic) {
     if constexpr (__is_same(T, F16)) {
-        return __builtin_bit_cast(uint32_t, v);
+        // A nibble at bits 0..3 of a half under the fp16 pattern of 1024 reads
+        // 1024 + q, at bits 4..7 it reads 1024 + 16 q; one packed subtract, or
+        // one packed multiply-add by 1/16 and -72, gives q - 8 (all exact).
+        // Pairs 2 and 3 use the same two masks on x >> 8.
+        const uint32_t y = x >> 8;
+        const h2 sub = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+        const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+        const h2 off = {(_Float16)-72.0f, (_Float16)-72.0f};
+        const h2 p0 = __builtin_bit_cast(h2, and_or(x, 0x000F000Fu, magic)) + sub;
+        const h2 p1 = __builtin_bit_cast(h2, and_or(x, 0x00F000F0u, magic)) * sixteenth + off;
+        const h2 p2 = __builtin_bit_cast(h2, and_or(y, 0x000F000Fu, magic)) + sub;
+        const h2 p3 = __builtin_bit_cast(h2, and_or(y, 0x00F000F0u, magic)) * sixteenth + off;
+        return u32x4{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                     __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
     } else {
-        // small integers: exact in bf16, whose bits are the top half of fp32
-        const uint32_t lo = __builtin_bit_cast(uint32_t, (float)v.x);
-        const uint32_t hi = __builtin_bit_cast(uint32_t, (float)v.y);
-        return perm_hi(lo, hi);
+        // through fp16 as above, then widened: small integers are exact in
+        // bf16, whose bits are the top half of fp32
+        u32x4 r;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const h2 v = __builtin_bit_cast(h2, and_or(x >> (4 * m), 0x000F000Fu, magic)) -
+                         h2{(_Float16)1032.0f, (_Float16)1032.0f};
+            r[m] = perm_hi(__builtin_bit_cast(uint32_t, (float)v.x), __builtin_bit_cast(uint32_t, (float)v.y));
+        }
+        return r;
     }
 }
 
-template <class T>
-__device__ __forceinline__ u32x4 dequant8(uint32_t x) {
-    return u32x4{dequant_pair<T>(x, 0), dequant_pair<T>(x, 1), dequant_pair<T>(x, 2), dequant_pair<T>(x, 3)};
-}
-
-// One scale group's operands for one lane: STEPS 32-k steps of packed W and A.
-template <int STEPS>
+// One scale group's operands for one lane: STEPS 32-k steps of packed W and
+// A, and the scales of its 16 columns, [j][e] for column 16 j + 4 (l/16) + e
+// (SVEC: two per dword, e = 2 i + half).
+template <int STEPS, bool SVEC>
 struct GroupLoad {
     u32x4 w[STEPS];
     u32x4 a[STEPS];
-    uint16_t s[4][4];   // [j][e] scale of column 16 j + 4 (l/16) + e
+    u32x2 sv[SVEC ? 4 : 1];
+    uint16_t s[SVEC ? 1 : 4][4];
 };
 
 // SVEC: N % 4 == 0 and scales 8-byte aligned, so a lane's 4 consecutive
 // columns of a scale row come in one 8-byte load.
 template <class T, int EPI, int GROUP, bool SVEC>
 __global__ __launch_bounds__(NTHREADS) void gemm_w4_kernel(GemmArgs args, const uint8_t *__restrict__ packed,
-                                                          const uint16_t *__restrict__ scales) {
+                                                          const uint16_t *__restrict__ scales, SplitWs ws) {
     constexpr int STEPS = GROUP / 32;
+    // groups in flight per wave: 16 steps' loads, or 8 where the scales take
+    // as many registers as the weights (32-k groups, element-wise scale
+    // loads), and at least two groups
+    constexpr int RING_STEPS = (SVEC && GROUP >= 64) ? 16 : 8;
+    constexpr int RING = RING_STEPS / STEPS >= 2 ? RING_STEPS / STEPS : 2;
     __shared__ float red[WAVES][16][64];
     const int M = args.M, N = args.N, K = args.K;
     const int tid = threadIdx.x;
@@ -94,9 +127,15 @@ __global__ __launch_bounds__(NTHREADS) void gemm_w4_kernel(GemmArgs args, const 
     const int slab = blockIdx.x;
     const int m0 = blockIdx.y * 16;
     const int ktiles = K / 32;
+    // this workgroup's scale groups (all of them without split-K), divided
+    // over its waves
     const int groups = K / GROUP;
-    const int g_begin = (int)(((int64_t)groups * wave) / WAVES);
-    const int g_end = (int)(((int64_t)groups * (wave + 1)) / WAVES);
+    const int splits = ws.splits;
+    const int split = blockIdx.z;
+    const int sp_begin = (int)(((int64_t)groups * split) / splits);
+    const int sp_len = (int)(((int64_t)groups * (split + 1)) / splits) - sp_begin;
+    const int g_begin = sp_begin + (int)(((int64_t)sp_len * wave) / WAVES);
+    const int g_end = sp_begin + (int)(((int64_t)sp_len * (wave + 1)) / WAVES);
 
     const __amdgpu_buffer_rsrc_t ra =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(args.A), (short)0,
@@ -114,7 +153,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_w4_kernel(GemmArgs args, const 
     const uint32_t w_base = 1024u * (uint32_t)slab * (uint32_t)ktiles + 16u * (uint32_t)lane;
     const int n_lane = slab * 64 + 4 * h;   // + 16 j + e
 
-    auto load_group = [&](GroupLoad<STEPS> &g, int grp) __attribute__((always_inline)) {
+    auto load_group = [&](GroupLoad<STEPS, SVEC> &g, int grp) __attribute__((always_inline)) {
         const bool live = grp < g_end;    // wave-uniform; past the range everything reads zero
 #pragma unroll
         for (int u = 0; u < STEPS; ++u) {
@@ -128,11 +167,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_w4_kernel(GemmArgs args, const 
             for (int j = 0; j < 4; ++j) {
                 const int n = n_lane + 16 * j;
                 const uint32_t so = 2u * ((uint32_t)grp * (uint32_t)N + (uint32_t)n);
-                const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)masked(so, live && n < N), 0, 0);
-                g.s[j][0] = (uint16_t)(v.x & 0xffff);
-                g.s[j][1] = (uint16_t)(v.x >> 16);
-                g.s[j][2] = (uint16_t)(v.y & 0xffff);
-                g.s[j][3] = (uint16_t)(v.y >> 16);
+                g.sv[j] = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)masked(so, live && n < N), 0, 0);
             }
         } else {
 #pragma unroll
@@ -150,7 +185,8 @@ __global__ __launch_bounds__(NTHREADS) void gemm_w4_kernel(GemmArgs args, const 
 #pragma unroll
     for (int j = 0; j < 4; ++j)
         acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    auto mma_group = [&](const GroupLoad<STEPS> &g) __attribute__((always_inline)) {
+    const uint32_t magic = 0x64006400u;   // fp16 1024 in both halves
+    auto mma_group = [&](const GroupLoad<STEPS, SVEC> &g) __attribute__((always_inline)) {
         f32x4 part[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
@@ -159,27 +195,41 @@ __global__ __launch_bounds__(NTHREADS) void gemm_w4_kernel(GemmArgs args, const 
         for (int u = 0; u < STEPS; ++u)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                part[j] = T::mfma16(dequant8<T>(g.w[u][j]), g.a[u], part[j]);
+                part[j] = T::mfma16(dequant8<T>(g.w[u][j], magic), g.a[u], part[j]);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                acc[j][e] += T::to_f32(g.s[j][e]) * part[j][e];
+            for (int e = 0; e < 4; ++e) {
+                uint16_t sb;
+                if constexpr (SVEC)
+                    sb = (uint16_t)(g.sv[j][e >> 1] >> (16 * (e & 1)));
+                else
+                    sb = g.s[j][e];
+                acc[j][e] += T::to_f32(sb) * part[j][e];
+            }
     };
 
-    GroupLoad<STEPS> b0, b1;
-    load_group(b0, g_begin);
-    for (int g = g_begin; g < g_end; g += 2) {
-        load_group(b1, g + 1);
+    // A ring of RING groups: each group's slot is refilled with the group
+    // RING places further on as soon as it has been multiplied.
+    GroupLoad<STEPS, SVEC> ring[RING];
+#pragma unroll
+    for (int r = 0; r < RING; ++r)
+        load_group(ring[r], g_begin + r);
+    int g = g_begin;
+    for (; g + RING < g_end; g += RING) {
+#pragma unroll
+        for (int r = 0; r < RING; ++r) {
+            __builtin_amdgcn_sched_barrier(0);
+            mma_group(ring[r]);
+            __builtin_amdgcn_sched_barrier(0);
+            load_group(ring[r], g + RING + r);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < RING; ++r) {
         __builtin_amdgcn_sched_barrier(0);
-        mma_group(b0);
-        __builtin_amdgcn_sched_barrier(0);
-        if (g + 1 >= g_end)
-            break;
-        load_group(b0, g + 2);
-        __builtin_amdgcn_sched_barrier(0);
-        mma_group(b1);
-        __builtin_amdgcn_sched_barrier(0);
+        if (g + r < g_end)
+            mma_group(ring[r]);
     }
 
     // acc[j][e] = C[m0 + p][n_lane + 16 j + e] (this wave's groups)
@@ -190,25 +240,31 @@ __global__ __launch_bounds__(NTHREADS) void gemm_w4_kernel(GemmArgs args, const 
             red[wave][4 * j + e][lane] = acc[j][e];
     __syncthreads();
     // waves 0..3 each finish one column group j of every lane
+    const int j = wave & 3;
+    float y[4] = {0.f, 0.f, 0.f, 0.f};
+    if (wave < 4) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int w = 0; w < WAVES; ++w)
+                y[e] += red[w][4 * j + e][lane];
+    }
+    if (splits > 1 && !split_exchange(ws, (int64_t)blockIdx.y * gridDim.x + blockIdx.x, split, y, j))
+        return;
     if (wave >= 4)
         return;
     const int m = m0 + p;
     const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
         args.C, (short)0, (int)(2u * (uint32_t)M * (uint32_t)N), 0x00020000);
     {
-        const int j = wave;
         const int n = n_lane + 16 * j;
         uint16_t o[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            float y = 0.f;
-#pragma unroll
-            for (int w = 0; w < WAVES; ++w)
-                y += red[w][4 * j + e][lane];
             float b = 0.f;
             if constexpr (EPI != EPI_NONE)
                 b = n + e < N ? T::to_f32(args.bias[n + e]) : 0.f;
-            o[e] = T::from_f32(epilogue<EPI>(y, b));
+            o[e] = T::from_f32(epilogue<EPI>(y[e], b));
         }
         const uint32_t base = 2u * ((uint32_t)m * (uint32_t)N + (uint32_t)n);
         if (n + 3 < N) {
@@ -250,20 +306,20 @@ __global__ __launch_bounds__(256) void w4_pack_kernel(int K, int N, const uint8_
 
 template <class T, int EPI, bool SVEC>
 hipError_t launch_scales(const GemmArgs &a, const uint8_t *packed, const uint16_t *scales, int group,
-                         hipStream_t stream) {
-    const dim3 grid((a.N + 63) / 64, (a.M + 15) / 16);
+                         const SplitWs &ws, hipStream_t stream) {
+    const dim3 grid((a.N + 63) / 64, (a.M + 15) / 16, ws.splits);
     switch (group) {
     case 32:
-        hipLaunchKernelGGL((gemm_w4_kernel<T, EPI, 32, SVEC>), grid, dim3(NTHREADS), 0, stream, a, packed, scales);
+        hipLaunchKernelGGL((gemm_w4_kernel<T, EPI, 32, SVEC>), grid, dim3(NTHREADS), 0, stream, a, packed, scales, ws);
         break;
     case 64:
-        hipLaunchKernelGGL((gemm_w4_kernel<T, EPI, 64, SVEC>), grid, dim3(NTHREADS), 0, stream, a, packed, scales);
+        hipLaunchKernelGGL((gemm_w4_kernel<T, EPI, 64, SVEC>), grid, dim3(NTHREADS), 0, stream, a, packed, scales, ws);
         break;
     case 128:
-        hipLaunchKernelGGL((gemm_w4_kernel<T, EPI, 128, SVEC>), grid, dim3(NTHREADS), 0, stream, a, packed, scales);
+        hipLaunchKernelGGL((gemm_w4_kernel<T, EPI, 128, SVEC>), grid, dim3(NTHREADS), 0, stream, a, packed, scales, ws);
         break;
     default:
-        hipLaunchKernelGGL((gemm_w4_kernel<T, EPI, 256, SVEC>), grid, dim3(NTHREADS), 0, stream, a, packed, scales);
+        hipLaunchKernelGGL((gemm_w4_kernel<T, EPI, 256, SVEC>), grid, dim3(NTHREADS), 0, stream, a, packed, scales, ws);
         break;
     }
     return hipGetLastError();
@@ -271,28 +327,28 @@ hipError_t launch_scales(const GemmArgs &a, const uint8_t *packed, const uint16_
 
 template <class T, int EPI>
 hipError_t launch_group(const GemmArgs &a, const uint8_t *packed, const uint16_t *scales, int group,
-                        hipStream_t stream) {
+                        const SplitWs &ws, hipStream_t stream) {
     const bool svec = a.N % 4 == 0 && ((uintptr_t)scales & 7u) == 0;
-    return svec ? launch_scales<T, EPI, true>(a, packed, scales, group, stream)
-                : launch_scales<T, EPI, false>(a, packed, scales, group, stream);
+    return svec ? launch_scales<T, EPI, true>(a, packed, scales, group, ws, stream)
+                : launch_scales<T, EPI, false>(a, packed, scales, group, ws, stream);
 }
 
 template <class T>
 hipError_t launch_epi(int epi, const GemmArgs &a, const uint8_t *packed, const uint16_t *scales, int group,
-                      hipStream_t stream) {
+                      const SplitWs &ws, hipStream_t stream) {
     switch (epi) {
-    case EPI_NONE: return launch_group<T, EPI_NONE>(a, packed, scales, group, stream);
-    case EPI_BIAS: return launch_group<T, EPI_BIAS>(a, packed, scales, group, stream);
-    default: return launch_group<T, EPI_BIAS_GELU_TANH>(a, packed, scales, group, stream);
+    case EPI_NONE: return launch_group<T, EPI_NONE>(a, packed, scales, group, ws, stream);
+    case EPI_BIAS: return launch_group<T, EPI_BIAS>(a, packed, scales, group, ws, stream);
+    default: return launch_group<T, EPI_BIAS_GELU_TANH>(a, packed, scales, group, ws, stream);
     }
 }
 
 }  // namespace
 
 hipError_t launch_w4(int dtype, int epi, const GemmArgs &a, const uint8_t *packed, const uint16_t *scales, int group,
-                     hipStream_t stream) {
-    return dtype == 0 ? launch_epi<F16>(epi, a, packed, scales, group, stream)
-                      : launch_epi<BF16>(epi, a, packed, scales, group, stream);
+                     const SplitWs &ws, hipStream_t stream) {
+    return dtype == 0 ? launch_epi<F16>(epi, a, packed, scales, group, ws, stream)
+                      : launch_epi<BF16>(epi, a, packed, scales, group, ws, stream);
 }
 
 hipError_t launch_w4_pack(int K, int N, const uint8_t *q, uint8_t *packed, hipStream_t stream) {

@@ -37,14 +37,45 @@ int tiled_occupancy(int tiles);
 // 256 x 256 tiles with element-granular loads and stores: any shape.
 hipError_t launch_tiled_generic(int dtype, int epi, const GemmArgs &a, hipStream_t stream);
 
-// M <= 16, K % 8 == 0, N % 4 == 0, aligned operands.
-hipError_t launch_skinny(int dtype, int epi, const GemmArgs &a, hipStream_t stream);
+// Split-K workspace of the M <= 16 kernels.  With splits > 1 the K range of
+// each output block (16 rows x 64 columns) is divided over `splits`
+// workgroups: each writes its fp32 partial block (1024 values) to part and
+// counts itself in that block's counter; the last to arrive adds the
+// partials in split order (so the result does not depend on the arrival
+// order), applies the epilogue, stores C and resets the counter to zero.
+// No workgroup waits for another.
+struct SplitWs {
+    int splits;          // 1: no workspace (part, count unused)
+    float *part;         // [block][split][1024], 16-byte aligned
+    uint32_t *count;     // [block], zero before the launch, zero after it
+};
+// Bytes of workspace for `blocks` output blocks and `splits` splits: the
+// counters (padded to 256 bytes), then the partial blocks.
+inline size_t split_ws_bytes(int64_t blocks, int splits) {
+    if (splits <= 1)
+        return 0;
+    return (size_t)((blocks * 4 + 255) / 256 * 256) + (size_t)blocks * (size_t)splits * 4096u;
+}
+inline SplitWs split_ws(void *ws, int64_t blocks, int splits) {
+    SplitWs w{splits, nullptr, nullptr};
+    if (splits > 1) {
+        w.count = static_cast<uint32_t *>(ws);
+        w.part = reinterpret_cast<float *>(static_cast<char *>(ws) + (blocks * 4 + 255) / 256 * 256);
+    }
+    return w;
+}
+
+// M <= 16, K % 8 == 0, N % 4 == 0, aligned operands; ws.splits >= 1 (at most
+// ceil(K / 32)), its workspace laid out by split_ws for ceil(N / 64) blocks.
+hipError_t launch_skinny(int dtype, int epi, const GemmArgs &a, const SplitWs &ws, hipStream_t stream);
 
 // Weight-only 4-bit product: packed weights in the layout of launch_w4_pack,
 // scales (K/group x N), group in {32, 64, 128, 256}, K % group == 0; any M
-// (16-row blocks), any N, 2-byte alignment.
+// (16-row blocks), any N, 2-byte alignment.  ws.splits >= 1 divides the
+// scale groups; its workspace is laid out by split_ws for
+// ceil(N / 64) ceil(M / 16) blocks (block = row block x slabs + slab).
 hipError_t launch_w4(int dtype, int epi, const GemmArgs &a, const uint8_t *packed, const uint16_t *scales, int group,
-                     hipStream_t stream);
+                     const SplitWs &ws, hipStream_t stream);
 // q: K x N bytes (values 0..15), K % 32 == 0 -> packed (ceil(N/64) * 32 * K bytes).
 hipError_t launch_w4_pack(int K, int N, const uint8_t *q, uint8_t *packed, hipStream_t stream);
 
