@@ -47,7 +47,8 @@ SQUARE = "gemm_f16_4096x4096x4096"
 SKINNY = "gemm_f16_skinny_16x11008x4096"
 RAGGED = "gemm_bf16_4000x4093x4111_bias_gelu_tanh"
 KERNEL_SOURCES = ["gemm_tiled.hip", "gemm_tiled_generic.hip", "gemm_skinny.hip", "gemm_w4.hip", "attention_fwd.hip",
-                  "tg_device.h", "tg_tile.h", "tg_launch.h", "tg_gemm_host.hip"]
+                  "elementwise.hip", "tg_device.h", "tg_tile.h", "tg_launch.h", "tg_split.h", "tg_direct.h",
+                  "tg_gemm_host.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 

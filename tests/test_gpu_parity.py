@@ -123,6 +123,30 @@ def test_skinny_every_row_count(dtype):
 
 
 @pytest.mark.parametrize("dtype", [I.F16, I.BF16])
+@pytest.mark.parametrize("M,N,K", [
+    (16, 4 * 97, 4096),   # 16 steps of 32 k per wave
+    (5, 4 * 97, 2400),    # 75 steps: 9 or 10 per wave
+    (1, 520, 4008),       # 126 steps, the last with 8 of its 32 k
+    (11, 68, 3336),       # 105 steps: 13 or 14 per wave; one partial slab
+])
+def test_skinny_preloaded_A(dtype, M, N, K):
+    # Shapes where every wave has 9..16 steps of 32 k, so the skinny kernel
+    # stages its slice of A through LDS before streaming B.
+    A = I.random_bits((M, K), ("normal", 0.0, 1.0), dtype, 900 + M)
+    B = I.random_bits((K, N), ("normal", 0.0, 0.02), dtype, 901 + M)
+    bias = I.random_bits((N,), ("normal", 0.0, 0.1), dtype, 902 + M)
+    log(f"[skinny preload] {I.DTYPE_NAMES[dtype]} M={M} N={N} K={K}")
+    ref64, _ = oracle.gemm(M, N, K, dtype, A, B, bias, I.EPI_BIAS_GELU_TANH)
+    out = run(M, N, K, dtype, A, B, bias, I.EPI_BIAS_GELU_TANH, expect_path=tg.TG_PATH_SKINNY)
+    check_tolerance(dtype, to_bits(out), ref64, f"skinny preload M={M} K={K}")
+    Ai = I.small_int_bits((M, K), dtype, 903 + M)
+    Bi = I.small_int_bits((K, N), dtype, 904 + M)
+    _, refq = oracle.gemm(M, N, K, dtype, Ai, Bi)
+    check_exact(to_bits(run(M, N, K, dtype, Ai, Bi, expect_path=tg.TG_PATH_SKINNY)), refq,
+                f"skinny preload integers M={M} K={K}")
+
+
+@pytest.mark.parametrize("dtype", [I.F16, I.BF16])
 def test_identity_and_permutation_products(dtype):
     """MFMA operand/output layouts: one non-zero term per sum, so results are exact."""
     rng = np.random.Generator(np.random.PCG64(31))

@@ -41,6 +41,10 @@ def _run(M, N, K, G, dtype, A, Q, S, bias, epi):
     (I.F16, 7, 72, 96, 32, I.EPI_NONE),                  # fewer groups than waves
     (I.F16, 9, 1001, 256, 64, I.EPI_BIAS),               # N % 4 != 0: scales read element by element
     (I.BF16, 16, 70, 128, 32, I.EPI_BIAS_GELU_TANH),
+    # A staged through LDS (every wave's groups span 9..16 steps of 32 k)
+    (I.F16, 5, 388, 3584, 128, I.EPI_BIAS_GELU_TANH),   # 3 or 4 groups per wave, ragged N, M < 16
+    (I.BF16, 20, 264, 4096, 64, I.EPI_BIAS),            # two 16-row blocks, the second partial
+    (I.F16, 16, 388, 4096, 256, I.EPI_NONE),            # two 256-k groups per wave
 ])
 def test_w4_matches_oracle(dtype, M, N, K, G, epi):
     A = I.random_bits((M, K), ("normal", 0.0, 1.0), dtype, 500 + M)

@@ -32,6 +32,7 @@
 // Loads are range-checked buffer loads; k >= K reads zero in both operands.
 #include "tg_device.h"
 #include "tg_launch.h"
+#include "tg_direct.h"
 #include "tg_split.h"
 
 namespace tg {
@@ -43,15 +44,25 @@ constexpr int UNROLL = 2;      // 32-k steps per load batch (two batches in flig
 constexpr int NTHREADS = 64 * WAVES;
 constexpr int PRE = 16;        // most 32-k steps per wave whose A slice is preloaded into registers
 constexpr uint32_t OOB = 0xFFFFFFF0u;    // byte offset beyond every operand
+constexpr uint32_t ASHIFT = 4096;        // the staged-A buffer starts this far before A
+
+using namespace direct;
 
 struct APair {
     u32x4 v[UNROLL];
 };
 __device__ __forceinline__ APair u32x4_pair(u32x4 a, u32x4 b) { return APair{{a, b}}; }
 
-template <class T, int EPI>
+template <class T, int EPI, bool PRELOAD>
 __global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args, SplitWs ws) {
-    __shared__ float red[WAVES][16][64];
+    // Per wave 16 KB: its slice of A when that is staged (the preload path
+    // below), then, after its k-loop, its 16 x 64 fp32 partial sums (the
+    // first 4 KB).  Each wave touches only its own region until the
+    // barrier before the cross-wave reduction.
+    __shared__ __attribute__((aligned(16))) u32x4 smem[WAVES * 1024];
+    auto red = [&](int w, int i, int l) __attribute__((always_inline)) -> float & {
+        return reinterpret_cast<float *>(smem)[4096 * w + 64 * i + l];
+    };
     const int M = args.M, N = args.N, K = args.K;
     const uint16_t *__restrict__ A = args.A;
     const uint16_t *__restrict__ B = args.B;
@@ -142,16 +153,39 @@ __global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args, Sp
     // range are masked, read nothing and give zeros.
     u32x2 vb0[UNROLL][8], vb1[UNROLL][8];
     u32x4 va0[UNROLL], va1[UNROLL];
-    if (s_end - s_begin > PRE / 2 && s_end - s_begin <= PRE) {
-        // A wave with PRE / 2 < steps <= PRE (K = 4096 on 8 waves: 16) reads
-        // its whole slice of A (16 rows x 32 PRE k) into registers first, so
-        // the loop streams only B.
-        u32x4 pa[PRE];
+    if constexpr (PRELOAD) {
+        // Every wave has PRE / 2 < steps <= PRE (K = 4096 on 8 waves: 16;
+        // the host picks this instance only then) and reads its whole slice
+        // of A (16 rows x 32 PRE k) into registers first, so the loop
+        // streams only B.  A separate instance rather than a branch: merged
+        // with the other loop, the compiler's wait counts would stall on
+        // loads of the path not taken.
+        // The slice goes through the wave's LDS region: 16 direct loads,
+        // each of 4 rows x 256 contiguous bytes (half the cache lines of
+        // 16 rows x 64 bytes), then 16-byte reads in the MFMA layout.
+        // Load j = 4 c4 + rq: row r = 4 rq + lane / 16 and k = 32 s_begin +
+        // 128 c4 + 8 c, where the lane's 16-byte slot lane % 16 of the row
+        // holds logical chunk c = slot ^ r (the swizzle that makes the reads
+        // of 16 rows' same chunk hit 16 different bank groups).  LDS byte
+        // 4096 c4 + 256 r + 16 slot of the region.  Chunks at k >= K or past
+        // the wave's steps, and rows >= M, are out of range and read zero.
+        const uint32_t region = lds_address(smem) + 16384u * (uint32_t)wave;
+        {
+            const i32x4 rs = rsrc_words((const char *)A - ASHIFT, 2u * (uint32_t)M * (uint32_t)K + ASHIFT);
+            const int r0 = lane >> 4;
+            const int slot = lane & 15;
+            const int kend = min(K, 32 * s_end);   // k past the wave's range reads zero too
 #pragma unroll
-        for (int i = 0; i < PRE; ++i) {
-            const int kb = (s_begin + i) * 32 + 8 * h;
-            const uint32_t mk = mask_of(s_begin + i < s_end && kb < K);
-            pa[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)((a_row + 2u * (uint32_t)kb) | mk), 0, 0);
+            for (int c4 = 0; c4 < PRE / 4; ++c4) {
+#pragma unroll
+                for (int rq = 0; rq < 4; ++rq) {
+                    const int r = 4 * rq + r0;
+                    const int k = 32 * s_begin + 128 * c4 + 8 * (slot ^ r);
+                    const uint32_t off = (ASHIFT - 1024u * (uint32_t)rq + 2u * ((uint32_t)r * (uint32_t)K + (uint32_t)k)) +
+                                         (k < kend ? 0u : 0x80000000u);
+                    dma16_rq(rq, rs, off, region + 4096u * (uint32_t)c4);
+                }
+            }
         }
         auto load_b = [&](u32x2 (&vb)[UNROLL][8], int s0) __attribute__((always_inline)) {
 #pragma unroll
@@ -166,6 +200,15 @@ __global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args, Sp
             }
         };
         load_b(vb0, s_begin);
+        // the 16 A loads are older than the 8 UNROLL B loads just issued
+        wait_vmcnt<8 * UNROLL>();
+        u32x4 pa[PRE];
+#pragma unroll
+        for (int i = 0; i < PRE; ++i) {
+            const uint32_t c = (uint32_t)((4 * (i & 3) + h) ^ p);
+            pa[i] = *(__attribute__((address_space(3))) const u32x4 *)(uintptr_t)(region + 4096u * (uint32_t)(i >> 2) +
+                                                                                 256u * (uint32_t)p + 16u * c);
+        }
 #pragma unroll
         for (int bi = 0; bi < PRE / UNROLL; bi += 2) {
             load_b(vb1, s_begin + (bi + 1) * UNROLL);
@@ -199,7 +242,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args, Sp
     for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            red[wave][4 * e + j][lane] = acc[j][e];
+            red(wave, 4 * e + j, lane) = acc[j][e];
     __syncthreads();
     // waves 0..3 each finish one of the four column groups e of every lane
     const int e = wave & 3;
@@ -210,7 +253,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args, Sp
             float s = 0.f;
 #pragma unroll
             for (int w = 0; w < WAVES; ++w)
-                s += red[w][4 * e + j][lane];
+                s += red(w, 4 * e + j, lane);
             y[j] = s;
         }
     }
@@ -243,7 +286,16 @@ __global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args, Sp
 template <class T, int EPI>
 hipError_t launch_typed(const GemmArgs &a, const SplitWs &ws, hipStream_t stream) {
     const int slabs = (a.N + SLAB - 1) / SLAB;
-    hipLaunchKernelGGL((gemm_skinny_kernel<T, EPI>), dim3(slabs, ws.splits), dim3(NTHREADS), 0, stream, a, ws);
+    // every wave's share of the 32-k steps is floor or ceil of a split's
+    // share / WAVES, and a split's share floor or ceil of steps / splits
+    const int64_t steps = (a.K + 31) / 32;
+    const int64_t lo = steps / ws.splits, hi = (steps + ws.splits - 1) / ws.splits;
+    if (lo / WAVES > PRE / 2 && (hi + WAVES - 1) / WAVES <= PRE)
+        hipLaunchKernelGGL((gemm_skinny_kernel<T, EPI, true>), dim3(slabs, ws.splits), dim3(NTHREADS), 0, stream, a,
+                           ws);
+    else
+        hipLaunchKernelGGL((gemm_skinny_kernel<T, EPI, false>), dim3(slabs, ws.splits), dim3(NTHREADS), 0, stream, a,
+                           ws);
     return hipGetLastError();
 }
 

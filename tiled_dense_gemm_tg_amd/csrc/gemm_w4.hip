@@ -33,14 +33,18 @@
 // scale groups and the partial blocks meet through the workspace.
 #include "tg_device.h"
 #include "tg_launch.h"
+#include "tg_direct.h"
 #include "tg_split.h"
 
 namespace tg {
 namespace {
 
+using namespace direct;
+
 constexpr int WAVES = 8;
 constexpr int NTHREADS = 64 * WAVES;
 constexpr uint32_t OOB = 0xFFFFFFF0u;
+constexpr uint32_t ASHIFT = 4096;        // the staged-A buffer starts this far before A
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
@@ -108,7 +112,12 @@ struct GroupLoad {
 
 // SVEC: N % 4 == 0 and scales 8-byte aligned, so a lane's 4 consecutive
 // columns of a scale row come in one 8-byte load.
-template <class T, int EPI, int GROUP, bool SVEC>
+// LDSA: every wave's share of A is at most 16 steps (the host picks this
+// instance only then, and only with SVEC and groups of at least 64 k) and is
+// staged once through the wave's LDS region by direct loads, each of 4 rows
+// x 256 contiguous bytes (half the cache lines of the 16 rows x 64 bytes a
+// step's A fragment spans), instead of riding in the ring of loads.
+template <class T, int EPI, int GROUP, bool SVEC, bool LDSA>
 __global__ __launch_bounds__(NTHREADS) void gemm_w4_kernel(GemmArgs args, const uint8_t *__restrict__ packed,
                                                           const uint16_t *__restrict__ scales, SplitWs ws) {
     constexpr int STEPS = GROUP / 32;
@@ -117,7 +126,15 @@ __global__ __launch_bounds__(NTHREADS) void gemm_w4_kernel(GemmArgs args, const 
     // loads), and at least two groups
     constexpr int RING_STEPS = (SVEC && GROUP >= 64) ? 16 : 8;
     constexpr int RING = RING_STEPS / STEPS >= 2 ? RING_STEPS / STEPS : 2;
-    __shared__ float red[WAVES][16][64];
+    static_assert(!LDSA || (SVEC && GROUP >= 64), "staged A goes with 16-step rings");
+    // per wave: its staged slice of A (LDSA), then its 16 x 64 fp32 partial
+    // sums (the first 4 KB), each wave touching only its own region until
+    // the barrier before the cross-wave reduction
+    constexpr int REGION = LDSA ? 16384 : 4096;
+    __shared__ __attribute__((aligned(16))) u32x4 smem[WAVES * REGION / 16];
+    auto red = [&](int w, int i, int l) __attribute__((always_inline)) -> float & {
+        return reinterpret_cast<float *>(smem)[REGION / 4 * w + 64 * i + l];
+    };
     const int M = args.M, N = args.N, K = args.K;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -159,7 +176,9 @@ __global__ __launch_bounds__(NTHREADS) void gemm_w4_kernel(GemmArgs args, const 
         for (int u = 0; u < STEPS; ++u) {
             const uint32_t t = (uint32_t)(grp * STEPS + u);
             g.w[u] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)masked(w_base + 1024u * t, live), 0, 0);
-            g.a[u] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)masked(a_row + 64u * t, a_ok && live), 0, 0);
+            if constexpr (!LDSA)
+                g.a[u] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)masked(a_row + 64u * t, a_ok && live), 0,
+                                                               0);
         }
         if constexpr (SVEC) {
             // columns n .. n + 3 are all below N or all past it (N % 4 == 0)
@@ -186,16 +205,32 @@ __global__ __launch_bounds__(NTHREADS) void gemm_w4_kernel(GemmArgs args, const 
     for (int j = 0; j < 4; ++j)
         acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     const uint32_t magic = 0x64006400u;   // fp16 1024 in both halves
-    auto mma_group = [&](const GroupLoad<STEPS, SVEC> &g) __attribute__((always_inline)) {
+    // staged A: step i of the wave's slice, row p, logical 16-byte chunk
+    // 4 (i % 4) + h of 128-k block i / 4, at slot chunk ^ p of the row
+    const uint32_t region = lds_address(smem) + (uint32_t)REGION * (uint32_t)wave;
+    const uint32_t a_lds = region + 256u * (uint32_t)p;
+    const uint32_t hp = (uint32_t)(h ^ p);
+    auto mma_group = [&](const GroupLoad<STEPS, SVEC> &g, int grp) __attribute__((always_inline)) {
         f32x4 part[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             part[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        u32x4 av[STEPS];
+#pragma unroll
+        for (int u = 0; u < STEPS; ++u) {
+            if constexpr (LDSA) {
+                const uint32_t i = (uint32_t)((grp - g_begin) * STEPS + u);
+                av[u] = *(__attribute__((address_space(3))) const u32x4 *)(uintptr_t)(
+                    a_lds + 4096u * (i >> 2) + 16u * (hp ^ (4u * (i & 3u))));
+            } else {
+                av[u] = g.a[u];
+            }
+        }
 #pragma unroll
         for (int u = 0; u < STEPS; ++u)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                part[j] = T::mfma16(dequant8<T>(g.w[u][j], magic), g.a[u], part[j]);
+                part[j] = T::mfma16(dequant8<T>(g.w[u][j], magic), av[u], part[j]);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -211,16 +246,44 @@ __global__ __launch_bounds__(NTHREADS) void gemm_w4_kernel(GemmArgs args, const 
 
     // A ring of RING groups: each group's slot is refilled with the group
     // RING places further on as soon as it has been multiplied.
+    if constexpr (LDSA) {
+        // Load j = 4 c4 + rq: row r = 4 rq + lane / 16 of the block, k = the
+        // slice's first k + 128 c4 + 8 c, where the lane's slot lane % 16 of
+        // the row holds logical chunk c = slot ^ r; LDS byte 4096 c4 + 256 r
+        // + 16 slot of the region.  Chunks past the wave's range or K and
+        // rows >= M are out of range and read zero.
+        const i32x4 rsa = rsrc_words((const char *)args.A - ASHIFT, 2u * (uint32_t)M * (uint32_t)K + ASHIFT);
+        const int r0 = lane >> 4;
+        const int slot = lane & 15;
+        const int k_first = 32 * STEPS * g_begin;
+        const int kend = min(K, 32 * STEPS * g_end);
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+                const int r = 4 * rq + r0;
+                const int k = k_first + 128 * c4 + 8 * (slot ^ r);
+                const uint32_t off =
+                    (ASHIFT - 1024u * (uint32_t)rq + 2u * ((uint32_t)(m0 + r) * (uint32_t)K + (uint32_t)k)) +
+                    (k < kend ? 0u : 0x80000000u);
+                dma16_rq(rq, rsa, off, region + 4096u * (uint32_t)c4);
+            }
+        }
+    }
     GroupLoad<STEPS, SVEC> ring[RING];
 #pragma unroll
     for (int r = 0; r < RING; ++r)
         load_group(ring[r], g_begin + r);
+    if constexpr (LDSA) {
+        // the 16 A loads are older than the ring's STEPS + 4 loads per group
+        wait_vmcnt<RING * (STEPS + 4)>();
+    }
     int g = g_begin;
     for (; g + RING < g_end; g += RING) {
 #pragma unroll
         for (int r = 0; r < RING; ++r) {
             __builtin_amdgcn_sched_barrier(0);
-            mma_group(ring[r]);
+            mma_group(ring[r], g + r);
             __builtin_amdgcn_sched_barrier(0);
             load_group(ring[r], g + RING + r);
         }
@@ -229,7 +292,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_w4_kernel(GemmArgs args, const 
     for (int r = 0; r < RING; ++r) {
         __builtin_amdgcn_sched_barrier(0);
         if (g + r < g_end)
-            mma_group(ring[r]);
+            mma_group(ring[r], g + r);
     }
 
     // acc[j][e] = C[m0 + p][n_lane + 16 j + e] (this wave's groups)
@@ -237,7 +300,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_w4_kernel(GemmArgs args, const 
     for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            red[wave][4 * j + e][lane] = acc[j][e];
+            red(wave, 4 * j + e, lane) = acc[j][e];
     __syncthreads();
     // waves 0..3 each finish one column group j of every lane
     const int j = wave & 3;
@@ -247,7 +310,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_w4_kernel(GemmArgs args, const 
         for (int e = 0; e < 4; ++e)
 #pragma unroll
             for (int w = 0; w < WAVES; ++w)
-                y[e] += red[w][4 * j + e][lane];
+                y[e] += red(w, 4 * j + e, lane);
     }
     if (splits > 1 && !split_exchange(ws, (int64_t)blockIdx.y * gridDim.x + blockIdx.x, split, y, j))
         return;
@@ -304,23 +367,35 @@ __global__ __launch_bounds__(256) void w4_pack_kernel(int K, int N, const uint8_
     out[d] = x;
 }
 
+template <class T, int EPI, int GROUP, bool SVEC>
+void launch_one(const GemmArgs &a, const uint8_t *packed, const uint16_t *scales, const SplitWs &ws,
+                hipStream_t stream) {
+    const dim3 grid((a.N + 63) / 64, (a.M + 15) / 16, ws.splits);
+    // staged A when every wave's groups span at most 16 steps (and more than
+    // 8, so the 128 KB of LDS pays): a wave gets floor or ceil of a split's
+    // groups / WAVES, a split floor or ceil of groups / splits
+    bool ldsa = false;
+    if constexpr (SVEC && GROUP >= 64) {
+        const int64_t groups = a.K / GROUP;
+        const int64_t lo = groups / ws.splits, hi = (groups + ws.splits - 1) / ws.splits;
+        ldsa = (lo / WAVES) * (GROUP / 32) > 8 && ((hi + WAVES - 1) / WAVES) * (GROUP / 32) <= 16;
+    }
+    if (ldsa)
+        hipLaunchKernelGGL((gemm_w4_kernel<T, EPI, GROUP, SVEC, SVEC && GROUP >= 64>), grid, dim3(NTHREADS), 0,
+                           stream, a, packed, scales, ws);
+    else
+        hipLaunchKernelGGL((gemm_w4_kernel<T, EPI, GROUP, SVEC, false>), grid, dim3(NTHREADS), 0, stream, a, packed,
+                           scales, ws);
+}
+
 template <class T, int EPI, bool SVEC>
 hipError_t launch_scales(const GemmArgs &a, const uint8_t *packed, const uint16_t *scales, int group,
                          const SplitWs &ws, hipStream_t stream) {
-    const dim3 grid((a.N + 63) / 64, (a.M + 15) / 16, ws.splits);
     switch (group) {
-    case 32:
-        hipLaunchKernelGGL((gemm_w4_kernel<T, EPI, 32, SVEC>), grid, dim3(NTHREADS), 0, stream, a, packed, scales, ws);
-        break;
-    case 64:
-        hipLaunchKernelGGL((gemm_w4_kernel<T, EPI, 64, SVEC>), grid, dim3(NTHREADS), 0, stream, a, packed, scales, ws);
-        break;
-    case 128:
-        hipLaunchKernelGGL((gemm_w4_kernel<T, EPI, 128, SVEC>), grid, dim3(NTHREADS), 0, stream, a, packed, scales, ws);
-        break;
-    default:
-        hipLaunchKernelGGL((gemm_w4_kernel<T, EPI, 256, SVEC>), grid, dim3(NTHREADS), 0, stream, a, packed, scales, ws);
-        break;
+    case 32: launch_one<T, EPI, 32, SVEC>(a, packed, scales, ws, stream); break;
+    case 64: launch_one<T, EPI, 64, SVEC>(a, packed, scales, ws, stream); break;
+    case 128: launch_one<T, EPI, 128, SVEC>(a, packed, scales, ws, stream); break;
+    default: launch_one<T, EPI, 256, SVEC>(a, packed, scales, ws, stream); break;
     }
     return hipGetLastError();
 }

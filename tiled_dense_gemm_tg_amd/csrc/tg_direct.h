@@ -1,0 +1,56 @@
+// tg_direct.h -- direct-to-LDS buffer loads for the M <= 16 kernels (gfx950).
+//
+// A buffer load with the lds modifier writes each lane's 16 bytes straight
+// into LDS (at m0 + instruction offset + 16 * lane) without passing through
+// registers.  The loads are written as inline assembly, so the compiler does
+// not count them: whoever reads the LDS they fill waits for them with
+// wait_vmcnt first.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tg {
+namespace direct {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ i32x4 rsrc_words(const void *base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    return i32x4{(int)(uint32_t)a, (int)(uint32_t)(a >> 32), (int)bytes, 0x00020000};
+}
+
+__device__ __forceinline__ uint32_t lds_address(const void *q) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)q;
+}
+
+// One 16-byte-per-lane buffer load into LDS: lane L reads 16 bytes at byte
+// offset voffset + OFF of the buffer and writes them to LDS at m0 + OFF + 16 L.
+template <int OFF>
+__device__ __forceinline__ void dma16(const i32x4 &rsrc, uint32_t voffset, uint32_t m0) {
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen offset:%3 lds" ::"v"(voffset), "s"(rsrc), "{m0}"(m0),
+                 "i"(OFF));
+}
+
+// dma16 with the instruction offset 1024 rq (rq = 0..3, a compile-time value
+// after unrolling): loads of one 4 KB block share m0.
+__device__ __forceinline__ void dma16_rq(int rq, const i32x4 &rsrc, uint32_t voffset, uint32_t m0) {
+    switch (rq) {
+    case 0: dma16<0>(rsrc, voffset, m0); break;
+    case 1: dma16<1024>(rsrc, voffset, m0); break;
+    case 2: dma16<2048>(rsrc, voffset, m0); break;
+    default: dma16<3072>(rsrc, voffset, m0); break;
+    }
+}
+
+// s_waitcnt with only the vector-memory counter constrained (vmcnt[3:0] |
+// expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14).  The direct loads come
+// from inline assembly, so the compiler does not wait for them by itself.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+}  // namespace direct
+}  // namespace tg
