@@ -55,6 +55,7 @@ CASES = [
     (1, 64, 8, 4),
     (16, 4100, 2056, 64),
     (12, 520, 4104, 7),
+    (5, 260, 8008, 2),      # 125 or 126 steps per split: the A slice staged through LDS
 ]
 
 
@@ -194,6 +195,7 @@ W4_CASES = [
     (9, 1001, 512, 32, 5),
     (3, 128, 256, 128, 4),
     (16, 512, 8192, 256, 8),
+    (11, 320, 8192, 128, 2),   # 4 groups of 4 steps per wave: A staged through LDS
 ]
 
 
