@@ -19,9 +19,11 @@
 //     lane, one 16-byte load from L2) as its 16-column operand, so the 16
 //     MFMA columns are the (at most 16) rows of A;
 //   * loads come in batches of 2 steps, double-buffered in registers, so the
-//     next batch is in flight while the current one is multiplied; a wave
-//     with at most 16 steps (K = 4096) first reads its whole slice of A into
-//     registers, so that its loop streams only B;
+//     next batch is in flight while the current one is multiplied; where
+//     every wave has 9 to 16 steps (K = 4096: 16) a wave first copies its
+//     whole slice of A into its own 16 KB of LDS by direct loads of 4 rows x
+//     256 contiguous bytes and reads it into registers in the MFMA layout,
+//     so that its loop streams only B;
 //   * the 8 waves' fp32 partial sums are added in LDS in a fixed order (no
 //     atomics, so results are reproducible), then the fused epilogue and
 //     8-byte stores;

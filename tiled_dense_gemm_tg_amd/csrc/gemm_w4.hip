@@ -20,7 +20,9 @@
 //
 // Work: one workgroup per (16-row block of A, 64-column slab); its 8 waves
 // split the scale groups.  Per 32-k step a lane loads its 16 bytes of the
-// block (the wave reads 1 KiB contiguously) and 8 k of one A row, and runs
+// block (the wave reads 1 KiB contiguously) and 8 k of one A row (from the
+// wave's copy of its A slice in LDS where every wave has 9 to 16 steps and
+// the groups are at least 64 k; see LDSA below), and runs
 // four v_mfma_f32_16x16x32 with W^T as the 16-row operand (row l % 16 of MFMA
 // j is column 16 j + l % 16) and A as the 16-column operand.  The MFMA
 // multiplies the integers q - 8 (exact in both 16-bit formats), and the
