@@ -143,21 +143,19 @@ __global__ __launch_bounds__(NTHREADS, 1) void attention_fwd_kernel(AttnArgs arg
     __shared__ __attribute__((aligned(16))) u32x4 smem[STAGES * STAGE_BYTES / 16];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    int h, b, qb;
-    if constexpr (CAUSAL) {
-        // one flat grid, heaviest query blocks (longest key range) of every
-        // head dispatched first, so the longest workgroups start earliest
-        const int bh = args.B * args.H;
-        const int nqb = (int)gridDim.x / bh;
-        const int id = (int)blockIdx.x;
-        qb = nqb - 1 - id / bh;
-        h = (id % bh) % args.H;
-        b = (id % bh) / args.H;
-    } else {
-        qb = (int)blockIdx.x;
-        h = (int)blockIdx.y;
-        b = (int)blockIdx.z;
-    }
+    // One flat grid in which consecutive workgroups take the same query
+    // block of consecutive (batch, head) pairs.  The XCDs take workgroups in
+    // turn, so with B * H a multiple of the 8 XCDs every query block of a
+    // head runs on one XCD and reads that head's K and V through one L2
+    // (query blocks of one head spread over all XCDs fetched K and V once
+    // per XCD).  Causal: the heaviest query blocks (longest key range) come
+    // first, so the longest workgroups start earliest.
+    const int bh = args.B * args.H;
+    const int nqb = (int)gridDim.x / bh;
+    const int id = (int)blockIdx.x;
+    const int qb = CAUSAL ? nqb - 1 - id / bh : id / bh;
+    const int h = (id % bh) % args.H;
+    const int b = (id % bh) / args.H;
     const int q0 = qb * BM;
     const int Sq = args.Sq, Sk = args.Sk, H = args.H;
     const uint32_t tok = 2u * (uint32_t)H * (uint32_t)HD;   // bytes between tokens
@@ -420,7 +418,7 @@ hipError_t launch_typed(const AttnArgs &a, hipStream_t stream) {
     if (a.causal)
         hipLaunchKernelGGL((attention_fwd_kernel<T, true>), dim3(nqb * a.H * a.B), dim3(NTHREADS), 0, stream, a);
     else
-        hipLaunchKernelGGL((attention_fwd_kernel<T, false>), dim3(nqb, a.H, a.B), dim3(NTHREADS), 0, stream, a);
+        hipLaunchKernelGGL((attention_fwd_kernel<T, false>), dim3(nqb * a.H * a.B), dim3(NTHREADS), 0, stream, a);
     return hipGetLastError();
 }
 
