@@ -172,6 +172,22 @@ __global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args, Sp
         // 4096 c4 + 256 r + 16 slot of the region.  Chunks at k >= K or past
         // the wave's steps, and rows >= M, are out of range and read zero.
         const uint32_t region = lds_address(smem) + 16384u * (uint32_t)wave;
+        auto load_b = [&](u32x2 (&vb)[UNROLL][8], int s0) __attribute__((always_inline)) {
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                const int kb = (s0 + u) * 32 + 8 * h;
+                const uint32_t mk = mask_of(s0 + u < s_end && kb < K);
+                const uint32_t boff = (uint32_t)kb * b_row + b_col;
+#pragma unroll
+                for (int r = 0; r < 8; ++r)
+                    vb[u][r] = __builtin_amdgcn_raw_buffer_load_b64(rb, (int)((boff + (uint32_t)r * b_row) | mk), 0,
+                                                                    0);
+            }
+        };
+        // B's first two batches go out around the A loads, so that the wait
+        // for A below leaves a full batch of B in flight (waiting for A
+        // before issuing the second batch cost 1.7 us per launch)
+        load_b(vb0, s_begin);
         {
             const i32x4 rs = rsrc_words((const char *)A - ASHIFT, 2u * (uint32_t)M * (uint32_t)K + ASHIFT);
             const int r0 = lane >> 4;
@@ -189,20 +205,8 @@ __global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args, Sp
                 }
             }
         }
-        auto load_b = [&](u32x2 (&vb)[UNROLL][8], int s0) __attribute__((always_inline)) {
-#pragma unroll
-            for (int u = 0; u < UNROLL; ++u) {
-                const int kb = (s0 + u) * 32 + 8 * h;
-                const uint32_t mk = mask_of(s0 + u < s_end && kb < K);
-                const uint32_t boff = (uint32_t)kb * b_row + b_col;
-#pragma unroll
-                for (int r = 0; r < 8; ++r)
-                    vb[u][r] = __builtin_amdgcn_raw_buffer_load_b64(rb, (int)((boff + (uint32_t)r * b_row) | mk), 0,
-                                                                    0);
-            }
-        };
-        load_b(vb0, s_begin);
-        // the 16 A loads are older than the 8 UNROLL B loads just issued
+        load_b(vb1, s_begin + UNROLL);
+        // the 16 A loads are older than the second batch's 8 UNROLL B loads
         wait_vmcnt<8 * UNROLL>();
         u32x4 pa[PRE];
 #pragma unroll
@@ -213,7 +217,8 @@ __global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args, Sp
         }
 #pragma unroll
         for (int bi = 0; bi < PRE / UNROLL; bi += 2) {
-            load_b(vb1, s_begin + (bi + 1) * UNROLL);
+            if (bi > 0)
+                load_b(vb1, s_begin + (bi + 1) * UNROLL);
             __builtin_amdgcn_sched_barrier(0);
             mma_batch(vb0, u32x4_pair(pa[bi * UNROLL], pa[bi * UNROLL + 1]).v);
             __builtin_amdgcn_sched_barrier(0);
