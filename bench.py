@@ -13,7 +13,9 @@ lines in the same JSON object.
 Timing: W warm-up launches, then K launches back to back on torch's current
 stream (the stream tg_gemm is given), bracketed by torch.cuda.synchronize()
 and HIP events recorded on that stream; the per-launch time is the events'
-elapsed time / K.  The skinny shape rotates over 8 independent operand sets
+elapsed time / K.  Each secondary line also runs untimed launches for a
+quarter of a second before its timed ones, so that it is timed at the clock
+its own load settles at rather than the previous line's.  The skinny shape rotates over 8 independent operand sets
 (720 MB, more than the 256 MB Infinity Cache) so every launch streams B from
 HBM.
 
@@ -50,6 +52,7 @@ KERNEL_SOURCES = ["gemm_tiled.hip", "gemm_tiled_generic.hip", "gemm_skinny.hip",
                   "elementwise.hip", "tg_device.h", "tg_tile.h", "tg_launch.h", "tg_split.h", "tg_direct.h",
                   "tg_gemm_host.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+SETTLE_S = 0.25   # untimed launches before each secondary line, in seconds of wall time
 
 
 # ---------------------------------------------------------------- accounting
@@ -111,7 +114,7 @@ def log(msg: str) -> None:
 
 # ---------------------------------------------------------------- timing
 
-def time_gemm(torch, tg, w, sets, steps, warmup, unfused=False):
+def time_gemm(torch, tg, w, sets, steps, warmup, unfused=False, settle_s=SETTLE_S):
     """Per-launch time (ms) of tg_gemm (or, with `unfused`, of the three-launch
     tg_gemm_unfused) over `sets` rotating operand sets."""
     handle = torch.cuda.current_stream().cuda_stream
@@ -126,19 +129,31 @@ def time_gemm(torch, tg, w, sets, steps, warmup, unfused=False):
         if st != tg.TG_OK:
             raise RuntimeError(f"tg_gemm failed: {tg.tg_status_string(st)}")
 
-    return time_calls(torch, launch, steps, warmup, with_wall=True)
+    return time_calls(torch, launch, steps, warmup, with_wall=True, settle_s=settle_s)
 
 
-def time_calls(torch, launch, steps, warmup, with_wall=False):
+def time_calls(torch, launch, steps, warmup, with_wall=False, settle_s=SETTLE_S):
     """Per-launch time (ms) of launch(i) for i = 0 .. steps-1 on the current
     stream: HIP events recorded on that stream around the timed launches,
-    after `warmup` untimed ones and a synchronisation; with `with_wall`, also
-    the host's wall time (s) from before the first timed launch to after the
-    closing synchronisation."""
+    after `warmup` untimed ones, then further untimed ones until `settle_s`
+    seconds have passed (the clock takes a few tens of milliseconds to settle
+    after a change of load: the first ~15 ms of a 150-us kernel ran 10 %
+    slower), and a synchronisation; with `with_wall`, also the host's wall
+    time (s) from before the first timed launch to after the closing
+    synchronisation.  The main line passes settle_s = 0: it does exactly the
+    requested warm-up steps."""
     stream = torch.cuda.current_stream()
     for i in range(warmup):
         launch(i)
     torch.cuda.synchronize()
+    if settle_s > 0:
+        t_end = time.perf_counter() + settle_s
+        i = warmup
+        while time.perf_counter() < t_end:
+            for _ in range(20):
+                launch(i)
+                i += 1
+            torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -412,7 +427,7 @@ def main() -> int:
     w = I.WORKLOADS[args.workload]
     log(f"main workload {w.name}: generating inputs")
     ops, sets = device_operands(torch, I, w)
-    ms, wall = time_gemm(torch, tg, w, sets, args.steps, args.warmup)
+    ms, wall = time_gemm(torch, tg, w, sets, args.steps, args.warmup, settle_s=0.0)
     flops = gemm_flops(w.M, w.N, w.K)
     tflops = flops / (ms * 1e-3) / 1e12
     log(f"{w.name}: {ms * 1e3:.1f} us/launch, {tflops:.1f} TFLOP/s")
