@@ -47,6 +47,10 @@ constexpr int NTHREADS = 64 * WAVES;
 constexpr int PRE = 16;        // most 32-k steps per wave whose A slice is preloaded into registers
 constexpr uint32_t OOB = 0xFFFFFFF0u;    // byte offset beyond every operand
 constexpr uint32_t ASHIFT = 4096;        // the staged-A buffer starts this far before A
+// Cache policy of the B loads: non-temporal.  Each B element is read once,
+// so its lines need not displace the A rows every workgroup re-reads from
+// L2 (16x4096x11008: 20.35 -> 19.8 us per launch).
+constexpr int CPOL_NT = 2;
 
 using namespace direct;
 
@@ -125,7 +129,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args, Sp
             const uint32_t boff = (uint32_t)kb * b_row + b_col;
 #pragma unroll
             for (int r = 0; r < 8; ++r)
-                vb[u][r] = __builtin_amdgcn_raw_buffer_load_b64(rb, (int)((boff + (uint32_t)r * b_row) | mk), 0, 0);
+                vb[u][r] = __builtin_amdgcn_raw_buffer_load_b64(rb, (int)((boff + (uint32_t)r * b_row) | mk), 0, CPOL_NT);
         }
     };
     auto mma_batch = [&](const u32x2 (&vb)[UNROLL][8], const u32x4 (&va)[UNROLL]) __attribute__((always_inline)) {
@@ -181,7 +185,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args, Sp
 #pragma unroll
                 for (int r = 0; r < 8; ++r)
                     vb[u][r] = __builtin_amdgcn_raw_buffer_load_b64(rb, (int)((boff + (uint32_t)r * b_row) | mk), 0,
-                                                                    0);
+                                                                    CPOL_NT);
             }
         };
         // B's first two batches go out around the A loads, so that the wait

@@ -47,6 +47,9 @@ constexpr int WAVES = 8;
 constexpr int NTHREADS = 64 * WAVES;
 constexpr uint32_t OOB = 0xFFFFFFF0u;
 constexpr uint32_t ASHIFT = 4096;        // the staged-A buffer starts this far before A
+// Cache policy of the weight and scale loads: non-temporal (each is read
+// once; A is what the workgroups re-read from L2).
+constexpr int CPOL_NT = 2;
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
@@ -177,7 +180,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_w4_kernel(GemmArgs args, const 
 #pragma unroll
         for (int u = 0; u < STEPS; ++u) {
             const uint32_t t = (uint32_t)(grp * STEPS + u);
-            g.w[u] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)masked(w_base + 1024u * t, live), 0, 0);
+            g.w[u] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)masked(w_base + 1024u * t, live), 0, CPOL_NT);
             if constexpr (!LDSA)
                 g.a[u] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)masked(a_row + 64u * t, a_ok && live), 0,
                                                                0);
@@ -188,7 +191,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_w4_kernel(GemmArgs args, const 
             for (int j = 0; j < 4; ++j) {
                 const int n = n_lane + 16 * j;
                 const uint32_t so = 2u * ((uint32_t)grp * (uint32_t)N + (uint32_t)n);
-                g.sv[j] = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)masked(so, live && n < N), 0, 0);
+                g.sv[j] = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)masked(so, live && n < N), 0, CPOL_NT);
             }
         } else {
 #pragma unroll
@@ -197,7 +200,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_w4_kernel(GemmArgs args, const 
                 for (int e = 0; e < 4; ++e) {
                     const int n = n_lane + 16 * j + e;
                     const uint32_t so = 2u * ((uint32_t)grp * (uint32_t)N + (uint32_t)n);
-                    g.s[j][e] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)masked(so, live && n < N), 0, 0);
+                    g.s[j][e] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)masked(so, live && n < N), 0, CPOL_NT);
                 }
         }
     };
