@@ -54,3 +54,23 @@ def test_workload_accounting_matches_the_stated_figures():
     assert bench.gemm_flops(8192, 8192, 8192) == 1_099_511_627_776
     assert bench.gemm_alg_bytes(8192, 8192, 8192, bias=True) == 402_669_568
     assert bench.gemm_alg_bytes(16, 11008, 4096) == 90_660_864
+
+
+def test_traffic_hash_covers_every_kernel_source():
+    # The measured HBM traffic in profiles/traffic.json is reported only while
+    # the hash of the kernel sources matches; every file the library is built
+    # from must be part of that hash, or a change to it would leave stale
+    # figures in the bench line.
+    csrc = os.path.join(os.path.dirname(bench.__file__), "tiled_dense_gemm_tg_amd", "csrc")
+    sources = sorted(f for f in os.listdir(csrc) if f.endswith((".hip", ".h")))
+    assert sorted(bench.KERNEL_SOURCES) == sources
+
+
+def test_committed_traffic_matches_the_kernel_sources():
+    # Every workload in the committed traffic file was measured on the
+    # current sources (re-profile after any kernel change).
+    with open(bench.TRAFFIC_FILE) as fh:
+        rec = json.load(fh)
+    h = bench.kernel_source_hash()
+    stale = [k for k, v in rec.items() if isinstance(v, dict) and v.get("kernel_hash") != h]
+    assert not stale, stale
