@@ -337,6 +337,45 @@ def path_of(tg, w, operand_set):
     return tg.PATH_NAMES.get(path, "?") if st == tg.TG_OK else "error"
 
 
+def bench_rows(torch, tg, I, steps, warmup, copies=8):
+    """17 <= M <= 48 at the decode width (N = 11008, K = 4096, fp16, no
+    epilogue): the skinny kernel with two and three 16-row blocks per
+    workgroup (the library's choice there), and the tiled family on the same
+    operands for comparison, over `copies` rotating weight sets so that B
+    streams from HBM."""
+    N, K = 11008, 4096
+    handle = torch.cuda.current_stream().cuda_stream
+
+    def dev(bits, shape):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.float16).reshape(shape).to("cuda")
+
+    Bs = [dev(I.random_bits((K, N), ("normal", 0.0, 0.02), I.F16, 4100 + c), (K, N)) for c in range(copies)]
+    res = {}
+    for M in (32, 48):
+        A = dev(I.random_bits((M, K), ("normal", 0.0, 1.0), I.F16, 4200 + M), (M, K))
+        C = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        st, path = tg.tg_gemm_plan(M, N, K, I.F16, A.data_ptr(), Bs[0].data_ptr(), None, I.EPI_NONE, C.data_ptr())
+        assert st == tg.TG_OK, st
+        times = {}
+        for p in (tg.TG_PATH_AUTO, tg.TG_PATH_TILED):
+            def launch(i, p=p):
+                st = tg.tg_gemm_path(p, M, N, K, I.F16, A.data_ptr(), Bs[i % copies].data_ptr(), None, I.EPI_NONE,
+                                     C.data_ptr(), handle)
+                if st != tg.TG_OK:
+                    raise RuntimeError(f"tg_gemm_path: {tg.tg_status_string(st)}")
+            times[p] = time_calls(torch, launch, steps, warmup)
+        nbytes = gemm_alg_bytes(M, N, K)
+        ms = times[tg.TG_PATH_AUTO]
+        res[f"gemm_f16_rows_{M}x{N}x{K}"] = {
+            "us_per_launch": round(ms * 1e3, 3), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "frac_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+            "path": tg.PATH_NAMES[path], "tiled_us": round(times[tg.TG_PATH_TILED] * 1e3, 3),
+            "speedup_vs_tiled": round(times[tg.TG_PATH_TILED] / ms, 3),
+            "traffic": measured_traffic(f"gemm_f16_rows_{M}x{N}x{K}")}
+        log(f"rows M={M}: {ms * 1e3:.2f} us ({tg.PATH_NAMES[path]}), tiled {times[tg.TG_PATH_TILED] * 1e3:.2f} us")
+    return res
+
+
 def device_operands(torch, I, w, copies=1):
     ops = I.make_operands(w)
     tdt = torch.float16 if w.dtype == I.F16 else torch.bfloat16
@@ -499,6 +538,9 @@ def main() -> int:
                         "path": path_of(tg, w4, sets4[0]), "traffic": measured_traffic(w4.name)}
         log(f"{w4.name}: {ms4 * 1e3:.2f} us, {gbps:.0f} GB/s")
         del sets4
+        torch.cuda.empty_cache()
+        log("secondary: 32 and 48 rows at the decode width (8 rotating weight sets)")
+        sec.update(bench_rows(torch, tg, I, max(args.steps, 400), args.warmup))
         torch.cuda.empty_cache()
         log("secondary: weight-only 4-bit product at the same shape (16 rotating weight sets)")
         wname, msq, hotq, qbytes = bench_w4(torch, tg, I, max(args.steps, 400), args.warmup)

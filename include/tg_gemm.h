@@ -75,9 +75,11 @@ typedef enum {
 
 /*
  * Kernel families.  TG_PATH_AUTO lets the library choose:
- *   TG_PATH_SKINNY         M <= 16 (the decode-shaped product): streams B from
+ *   TG_PATH_SKINNY         M <= 48 (the decode-shaped product): streams B from
  *                          HBM once; needs K % 8 == 0, N % 4 == 0, A 16-byte
- *                          aligned, B, C and bias 8-byte aligned.
+ *                          aligned, B, C and bias 8-byte aligned.  Chosen
+ *                          automatically for M <= 16, and for 17 <= M <= 48
+ *                          while N <= 16384 (wider B runs faster tiled).
  *   TG_PATH_TILED          MFMA tiles (256x256 by default; see tg_tiles for
  *                          the other sizes and how one is chosen) staged
  *                          through LDS by 16-byte direct loads; any shape
@@ -195,7 +197,8 @@ tg_status tg_gemm_tiles_plan(int64_t M, int64_t N, int64_t K, int num_cu, tg_til
  * tg_gemm_split: as tg_gemm, with the skinny family's K range split over
  * `splits` workgroups per slab (0: the library's choice, reported by
  * tg_gemm_split_plan for the device of `stream`; 1: no split, no workspace;
- * at most 64).  Shapes that do not take the skinny path run as in tg_gemm
+ * at most 64).  Shapes that do not take the skinny path, and those with
+ * M > 16 (several row blocks per workgroup, never split), run as in tg_gemm
  * and leave the workspace alone.
  *   workspace        device memory, 16-byte aligned, at least
  *                    tg_gemm_split_workspace_bytes(N, splits) bytes (NULL

@@ -110,7 +110,12 @@ def test_empty_K_allows_null_operands(lib):
     (16, 11008, 4096, {}, tg.TG_PATH_SKINNY),          # decode shape
     (1, 4, 8, {}, tg.TG_PATH_SKINNY),
     (16, 12, 8, {}, tg.TG_PATH_SKINNY),                 # N % 4 == 0 is enough
-    (17, 11008, 4096, {}, tg.TG_PATH_TILED),
+    (17, 11008, 4096, {}, tg.TG_PATH_SKINNY),          # two row blocks per workgroup
+    (48, 16384, 4096, {}, tg.TG_PATH_SKINNY),          # three, 256 slabs: one round on 256 CUs
+    (48, 16388, 4096, {}, tg.TG_PATH_TILED),           # a second round of slabs: tiled is faster
+    (17, 28672, 4096, {}, tg.TG_PATH_TILED),
+    (16, 28672, 4096, {}, tg.TG_PATH_SKINNY),          # one row block: skinny at any width
+    (49, 11008, 4096, {}, tg.TG_PATH_TILED),
     (16, 11008, 4100, {}, tg.TG_PATH_TILED),            # K % 8 != 0: not skinny, tiled takes any shape
     (16, 11010, 4096, {}, tg.TG_PATH_TILED),            # N % 4 != 0
     (16, 11008, 4096, {"A": PA + 8}, tg.TG_PATH_TILED),
@@ -132,9 +137,9 @@ def test_kernel_family_choice(lib, M, N, K, ptrs, path):
 
 
 def test_explicit_path_requirements(lib):
-    # the skinny family needs M <= 16, K % 8 == 0, N % 4 == 0 and alignment;
+    # the skinny family needs M <= 48, K % 8 == 0, N % 4 == 0 and alignment;
     # the tiled family needs operands below its size limit
-    assert tg.tg_gemm_path(tg.TG_PATH_SKINNY, 17, 64, 64, I.F16, PA, PB, None, 0, PC, None) == tg.TG_ERR_UNSUPPORTED
+    assert tg.tg_gemm_path(tg.TG_PATH_SKINNY, 49, 64, 64, I.F16, PA, PB, None, 0, PC, None) == tg.TG_ERR_UNSUPPORTED
     assert tg.tg_gemm_path(tg.TG_PATH_SKINNY, 16, 64, 60, I.F16, PA, PB, None, 0, PC, None) == tg.TG_ERR_UNSUPPORTED
     assert tg.tg_gemm_path(tg.TG_PATH_SKINNY, 16, 64, 64, I.F16, PA + 4, PB, None, 0, PC, None) \
         == tg.TG_ERR_UNSUPPORTED

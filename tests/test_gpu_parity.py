@@ -70,7 +70,7 @@ def test_workload_small_integers_bit_exact(name):
 
 def _families(M, N, K):
     fams = [tg.TG_PATH_TILED_GENERIC, tg.TG_PATH_TILED]
-    if M <= 16 and K % 8 == 0 and N % 4 == 0:
+    if M <= 48 and K % 8 == 0 and N % 4 == 0:
         fams.append(tg.TG_PATH_SKINNY)
     return fams
 
@@ -120,6 +120,45 @@ def test_skinny_every_row_count(dtype):
         ref64, _ = oracle.gemm(M, N, K, dtype, A, B, bias, I.EPI_BIAS_GELU_TANH)
         out = run(M, N, K, dtype, A, B, bias, I.EPI_BIAS_GELU_TANH, expect_path=tg.TG_PATH_SKINNY)
         check_tolerance(dtype, to_bits(out), ref64, f"skinny M={M}")
+
+
+@pytest.mark.parametrize("dtype", [I.F16, I.BF16])
+def test_skinny_row_blocks_every_row_count(dtype):
+    # 17 <= M <= 48: the skinny kernel carries 2 or 3 blocks of 16 rows per
+    # workgroup, all multiplying the same B vectors
+    N, K = 4 * 97, 8 * 75
+    for M in range(17, 49):
+        A = I.random_bits((M, K), ("normal", 0.0, 1.0), dtype, 1800 + M)
+        B = I.random_bits((K, N), ("normal", 0.0, 0.02), dtype, 1850 + M)
+        bias = I.random_bits((N,), ("normal", 0.0, 0.1), dtype, 1870 + M)
+        log(f"[skinny rows] {I.DTYPE_NAMES[dtype]} M={M}")
+        ref64, _ = oracle.gemm(M, N, K, dtype, A, B, bias, I.EPI_BIAS_GELU_TANH)
+        out = run(M, N, K, dtype, A, B, bias, I.EPI_BIAS_GELU_TANH, path=tg.TG_PATH_SKINNY)
+        check_tolerance(dtype, to_bits(out), ref64, f"skinny M={M}")
+        if M in (17, 32, 33, 48):
+            Ai = I.small_int_bits((M, K), dtype, 1880 + M)
+            Bi = I.small_int_bits((K, N), dtype, 1890 + M)
+            bi = I.small_int_bits((N,), dtype, 1895 + M)
+            _, refq = oracle.gemm(M, N, K, dtype, Ai, Bi, bi, I.EPI_BIAS)
+            check_exact(to_bits(run(M, N, K, dtype, Ai, Bi, bi, I.EPI_BIAS, path=tg.TG_PATH_SKINNY)), refq,
+                        f"skinny integers M={M}")
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (48, 11008, 4096),    # three full row blocks at the decode width
+    (40, 16384, 4096),    # three blocks, the last with 8 rows; 256 slabs
+    (24, 68, 3336),       # one partial slab, ragged last step
+    (45, 4100, 8200),     # partial slab, three blocks, 257 steps
+])
+def test_skinny_row_blocks_full_size(M, N, K):
+    dtype = I.F16
+    A = I.random_bits((M, K), ("normal", 0.0, 1.0), dtype, 1900 + M)
+    B = I.random_bits((K, N), ("normal", 0.0, 0.02), dtype, 1901 + M)
+    bias = I.random_bits((N,), ("normal", 0.0, 0.1), dtype, 1902 + M)
+    log(f"[skinny rows full] M={M} N={N} K={K}")
+    ref64, _ = oracle.gemm(M, N, K, dtype, A, B, bias, I.EPI_BIAS_GELU_TANH)
+    out = run(M, N, K, dtype, A, B, bias, I.EPI_BIAS_GELU_TANH, path=tg.TG_PATH_SKINNY)
+    check_tolerance(dtype, to_bits(out), ref64, f"skinny rows M={M} N={N} K={K}")
 
 
 @pytest.mark.parametrize("dtype", [I.F16, I.BF16])

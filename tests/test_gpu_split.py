@@ -136,8 +136,9 @@ def test_split_auto_matches_its_plan():
 
 
 def test_split_off_the_skinny_path_leaves_workspace_alone():
-    """M > 16 takes the tiled family: tg_gemm_split then runs as tg_gemm and
-    never touches the workspace (filled with a pattern it would change)."""
+    """Split-K is for M <= 16 only: with more rows tg_gemm_split runs as
+    tg_gemm (unsplit) and never touches the workspace (filled with a pattern
+    it would change)."""
     import torch
     dtype = I.BF16
     M, N, K = 40, 520, 264

@@ -1,4 +1,4 @@
-// gemm_skinny.hip -- the M <= 16 (decode-shaped) GEMM for gfx950.
+// gemm_skinny.hip -- the M <= 48 (decode-shaped) GEMM for gfx950.
 //
 // With at most 16 rows of A the product does 2*M flops per B element, far
 // below what keeps MFMA busy, so the kernel is shaped by HBM: B is read from
@@ -24,6 +24,9 @@
 //     whole slice of A into its own 16 KB of LDS by direct loads of 4 rows x
 //     256 contiguous bytes and reads it into registers in the MFMA layout,
 //     so that its loop streams only B;
+//   * 17 <= M <= 48: two or three such 16-row blocks of A per workgroup,
+//     each with its own MFMAs on the same transposed B vectors, so B is
+//     still read once (A then comes from L2 in every step; no preload);
 //   * the 8 waves' fp32 partial sums are added in LDS in a fixed order (no
 //     atomics, so results are reproducible), then the fused epilogue and
 //     8-byte stores;
@@ -54,20 +57,27 @@ constexpr int CPOL_NT = 2;
 
 using namespace direct;
 
-struct APair {
-    u32x4 v[UNROLL];
+template <int RB>
+struct ABatch {
+    u32x4 v[UNROLL][RB];
 };
-__device__ __forceinline__ APair u32x4_pair(u32x4 a, u32x4 b) { return APair{{a, b}}; }
+__device__ __forceinline__ ABatch<1> u32x4_pair(u32x4 a, u32x4 b) { return ABatch<1>{{{a}, {b}}}; }
 
-template <class T, int EPI, bool PRELOAD>
+// RB: 16-row blocks of A (and C) per workgroup, 1..3 (M <= 16 RB).  Every
+// block multiplies the same B vectors, so B is still read once; the preload
+// path and split-K are for RB = 1 only.  (Four blocks need more than the 256
+// registers a lane has at two waves per SIMD and spill: 2-3x slower than
+// three.)
+template <class T, int EPI, bool PRELOAD, int RB>
 __global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args, SplitWs ws) {
+    static_assert(RB >= 1 && RB <= 3 && (RB == 1 || !PRELOAD), "row blocks");
     // Per wave 16 KB: its slice of A when that is staged (the preload path
-    // below), then, after its k-loop, its 16 x 64 fp32 partial sums (the
-    // first 4 KB).  Each wave touches only its own region until the
-    // barrier before the cross-wave reduction.
+    // below), then, after its k-loop, its RB 16 x 64 fp32 partial sums (4 KB
+    // each).  Each wave touches only its own region until the barrier
+    // before the cross-wave reduction.
     __shared__ __attribute__((aligned(16))) u32x4 smem[WAVES * 1024];
-    auto red = [&](int w, int i, int l) __attribute__((always_inline)) -> float & {
-        return reinterpret_cast<float *>(smem)[4096 * w + 64 * i + l];
+    auto red = [&](int w, int b, int i, int l) __attribute__((always_inline)) -> float & {
+        return reinterpret_cast<float *>(smem)[4096 * w + 1024 * b + 64 * i + l];
     };
     const int M = args.M, N = args.N, K = args.K;
     const uint16_t *__restrict__ A = args.A;
@@ -79,7 +89,6 @@ __global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args, Sp
     const int h = lane >> 4;
     const int nb = blockIdx.x * SLAB;
     const int ncol = nb + 4 * p;              // N % 4 == 0: all four columns valid or none
-    const bool row_ok = p < M;
 
     // this workgroup's part of the 32-k steps (all of them without split-K),
     // divided over its waves
@@ -91,10 +100,12 @@ __global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args, Sp
     const int s_begin = sp_begin + (int)(((int64_t)sp_len * wave) / WAVES);
     const int s_end = sp_begin + (int)(((int64_t)sp_len * (wave + 1)) / WAVES);
 
-    f32x4 acc[4];
+    f32x4 acc[RB][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-        acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < RB; ++b)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[b][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // Batches of UNROLL 32-k steps, double-buffered in registers: the loads
     // of the next batch are in flight while the current one is multiplied.
@@ -107,7 +118,8 @@ __global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args, Sp
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(B), (short)0,
                                                                         (int)(2u * (uint32_t)K * (uint32_t)N),
                                                                         0x00020000);
-    const uint32_t a_row = 2u * (uint32_t)p * (uint32_t)K;
+    const uint32_t a_row = 2u * (uint32_t)p * (uint32_t)K;   // row p of block 0; block b is 16 b rows further
+    const uint32_t a_blk = 32u * (uint32_t)K;
     const uint32_t b_col = 2u * (uint32_t)ncol;
     const uint32_t b_row = 2u * (uint32_t)N;
     // Offsets of masked loads are OR-ed with OOB; the mask goes through an
@@ -118,21 +130,24 @@ __global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args, Sp
         asm volatile("" : "+v"(m));
         return m;
     };
-    auto load_batch = [&](u32x2 (&vb)[UNROLL][8], u32x4 (&va)[UNROLL], int s0) __attribute__((always_inline)) {
+    auto load_batch = [&](u32x2 (&vb)[UNROLL][8], ABatch<RB> &va, int s0) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             const int kb = (s0 + u) * 32 + 8 * h;
             // K % 8 == 0, so rows kb .. kb + 7 (and the A chunk's 8 k) are
             // all inside [0, K) or all outside.
             const uint32_t mk = mask_of(s0 + u < s_end && kb < K);
-            va[u] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)((a_row + 2u * (uint32_t)kb) | mk), 0, 0);
+#pragma unroll
+            for (int b = 0; b < RB; ++b)
+                va.v[u][b] = __builtin_amdgcn_raw_buffer_load_b128(
+                    ra, (int)((a_row + (uint32_t)b * a_blk + 2u * (uint32_t)kb) | mk), 0, 0);
             const uint32_t boff = (uint32_t)kb * b_row + b_col;
 #pragma unroll
             for (int r = 0; r < 8; ++r)
                 vb[u][r] = __builtin_amdgcn_raw_buffer_load_b64(rb, (int)((boff + (uint32_t)r * b_row) | mk), 0, CPOL_NT);
         }
     };
-    auto mma_batch = [&](const u32x2 (&vb)[UNROLL][8], const u32x4 (&va)[UNROLL]) __attribute__((always_inline)) {
+    auto mma_batch = [&](const u32x2 (&vb)[UNROLL][8], const ABatch<RB> &va) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
 #pragma unroll
@@ -150,7 +165,9 @@ __global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args, Sp
                     w.z = perm_lo(vb[u][4][d], vb[u][5][d]);
                     w.w = perm_lo(vb[u][6][d], vb[u][7][d]);
                 }
-                acc[j] = T::mfma16(w, va[u], acc[j]);
+#pragma unroll
+                for (int b = 0; b < RB; ++b)
+                    acc[b][j] = T::mfma16(w, va.v[u][b], acc[b][j]);
             }
         }
     };
@@ -158,7 +175,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args, Sp
     // multiplied (sched_barrier keeps that order); loads past the wave's
     // range are masked, read nothing and give zeros.
     u32x2 vb0[UNROLL][8], vb1[UNROLL][8];
-    u32x4 va0[UNROLL], va1[UNROLL];
+    ABatch<RB> va0, va1;
     if constexpr (PRELOAD) {
         // Every wave has PRE / 2 < steps <= PRE (K = 4096 on 8 waves: 16;
         // the host picks this instance only then) and reads its whole slice
@@ -224,12 +241,12 @@ __global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args, Sp
             if (bi > 0)
                 load_b(vb1, s_begin + (bi + 1) * UNROLL);
             __builtin_amdgcn_sched_barrier(0);
-            mma_batch(vb0, u32x4_pair(pa[bi * UNROLL], pa[bi * UNROLL + 1]).v);
+            mma_batch(vb0, u32x4_pair(pa[bi * UNROLL], pa[bi * UNROLL + 1]));
             __builtin_amdgcn_sched_barrier(0);
             if (bi + 2 < PRE / UNROLL)
                 load_b(vb0, s_begin + (bi + 2) * UNROLL);
             __builtin_amdgcn_sched_barrier(0);
-            mma_batch(vb1, u32x4_pair(pa[(bi + 1) * UNROLL], pa[(bi + 1) * UNROLL + 1]).v);
+            mma_batch(vb1, u32x4_pair(pa[(bi + 1) * UNROLL], pa[(bi + 1) * UNROLL + 1]));
             __builtin_amdgcn_sched_barrier(0);
         }
     } else {
@@ -248,35 +265,33 @@ __global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args, Sp
         }
     }
 
-    // acc[j][e] is D_j[row 4 h + e][col p]: C[m = p][n = nb + 16 h + 4 e + j].
+    // acc[b][j][e] is D_j[row 4 h + e][col p] of row block b:
+    // C[m = 16 b + p][n = nb + 16 h + 4 e + j].
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int b = 0; b < RB; ++b)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            red(wave, 4 * e + j, lane) = acc[j][e];
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                red(wave, b, 4 * e + j, lane) = acc[b][j][e];
     __syncthreads();
-    // waves 0..3 each finish one of the four column groups e of every lane
-    const int e = wave & 3;
-    float y[4] = {0.f, 0.f, 0.f, 0.f};
-    if (wave < 4) {
+
+    // the sum over the waves of (row block b, column group e) for every lane
+    auto wave_sum = [&](int b, int e, float (&y)[4]) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             float s = 0.f;
 #pragma unroll
             for (int w = 0; w < WAVES; ++w)
-                s += red(w, 4 * e + j, lane);
+                s += red(w, b, 4 * e + j, lane);
             y[j] = s;
         }
-    }
-    if (splits > 1 && !split_exchange(ws, blockIdx.x, split, y, e))
-        return;
-    if (wave >= 4)
-        return;
-
+    };
     uint16_t *__restrict__ C = args.C;
-    {
+    auto finish = [&](int b, int e, const float (&y)[4]) __attribute__((always_inline)) {
+        const int m = 16 * b + p;
         const int n = nb + 16 * h + 4 * e;
-        if (!row_ok || n >= N)
+        if (m >= M || n >= N)
             return;
         float bv[4] = {0.f, 0.f, 0.f, 0.f};
         if constexpr (EPI != EPI_NONE) {
@@ -290,23 +305,57 @@ __global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args, Sp
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             o[j] = T::from_f32(epilogue<EPI>(y[j], bv[j]));
-        *reinterpret_cast<u32x2 *>(C + (uint32_t)p * (uint32_t)N + n) = u32x2{pack2(o[0], o[1]), pack2(o[2], o[3])};
+        *reinterpret_cast<u32x2 *>(C + (uint32_t)m * (uint32_t)N + n) = u32x2{pack2(o[0], o[1]), pack2(o[2], o[3])};
+    };
+    if constexpr (RB == 1) {
+        // waves 0..3 each finish one of the four column groups e of every lane
+        const int e = wave & 3;
+        float y[4] = {0.f, 0.f, 0.f, 0.f};
+        if (wave < 4)
+            wave_sum(0, e, y);
+        if (splits > 1 && !split_exchange(ws, blockIdx.x, split, y, e))
+            return;
+        if (wave < 4)
+            finish(0, e, y);
+    } else {
+        // the 4 RB (row block, column group) pairs are spread over the waves
+#pragma unroll
+        for (int q0 = 0; q0 < 4 * RB; q0 += WAVES) {
+            const int q = q0 + wave;
+            if (q < 4 * RB) {
+                float y[4];
+                wave_sum(q >> 2, q & 3, y);
+                finish(q >> 2, q & 3, y);
+            }
+        }
     }
+}
+
+template <class T, int EPI, int RB>
+hipError_t launch_rows(const GemmArgs &a, const SplitWs &ws, hipStream_t stream) {
+    const int slabs = (a.N + SLAB - 1) / SLAB;
+    hipLaunchKernelGGL((gemm_skinny_kernel<T, EPI, false, RB>), dim3(slabs, ws.splits), dim3(NTHREADS), 0, stream, a,
+                       ws);
+    return hipGetLastError();
 }
 
 template <class T, int EPI>
 hipError_t launch_typed(const GemmArgs &a, const SplitWs &ws, hipStream_t stream) {
     const int slabs = (a.N + SLAB - 1) / SLAB;
+    if (a.M > 16) {   // several row blocks: no split-K (the host passes splits = 1)
+        if (ws.splits != 1 || a.M > 48)
+            return hipErrorInvalidValue;
+        return a.M <= 32 ? launch_rows<T, EPI, 2>(a, ws, stream) : launch_rows<T, EPI, 3>(a, ws, stream);
+    }
     // every wave's share of the 32-k steps is floor or ceil of a split's
     // share / WAVES, and a split's share floor or ceil of steps / splits
     const int64_t steps = (a.K + 31) / 32;
     const int64_t lo = steps / ws.splits, hi = (steps + ws.splits - 1) / ws.splits;
     if (lo / WAVES > PRE / 2 && (hi + WAVES - 1) / WAVES <= PRE)
-        hipLaunchKernelGGL((gemm_skinny_kernel<T, EPI, true>), dim3(slabs, ws.splits), dim3(NTHREADS), 0, stream, a,
+        hipLaunchKernelGGL((gemm_skinny_kernel<T, EPI, true, 1>), dim3(slabs, ws.splits), dim3(NTHREADS), 0, stream, a,
                            ws);
     else
-        hipLaunchKernelGGL((gemm_skinny_kernel<T, EPI, false>), dim3(slabs, ws.splits), dim3(NTHREADS), 0, stream, a,
-                           ws);
+        return launch_rows<T, EPI, 1>(a, ws, stream);
     return hipGetLastError();
 }
 

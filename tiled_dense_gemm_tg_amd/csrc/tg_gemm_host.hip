@@ -71,8 +71,17 @@ Checked check_args(int64_t M, int64_t N, int64_t K, int dtype, const void *A, co
     return {TG_OK, false};
 }
 
+// The skinny kernel carries up to three 16-row blocks of A per workgroup.
+constexpr int64_t kSkinnyMaxM = 48;
+// Above 16 rows the skinny kernel re-reads A from L2 in every step and beats
+// the tiled family only while its 64-column slabs fit one round of
+// workgroups (one per CU): measured on an MI355X at K = 4096, M = 17..48
+// runs 1.4-1.8x faster than tiled for N = 4096 and 11008 (M = 32, N = 11008:
+// 27.2 against 42.7 us), but 1.1-1.35x slower for N = 28672 (448 slabs).
+constexpr int64_t kRowBlocksMaxN = 256 * 64;
+
 bool skinny_ok(int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *bias, const void *C) {
-    return M <= 16 && K % 8 == 0 && N % 4 == 0 && aligned(A, 16) && aligned(B, 8) && aligned(C, 8) &&
+    return M <= kSkinnyMaxM && K % 8 == 0 && N % 4 == 0 && aligned(A, 16) && aligned(B, 8) && aligned(C, 8) &&
            aligned(bias, 8);
 }
 
@@ -156,7 +165,7 @@ tg_tiles auto_tiles(int64_t M, int64_t N, int num_cu) {
 
 tg_path auto_path(int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *bias,
                   const void *C) {
-    if (skinny_ok(M, N, K, A, B, bias, C))
+    if (skinny_ok(M, N, K, A, B, bias, C) && (M <= 16 || N <= kRowBlocksMaxN))
         return TG_PATH_SKINNY;
     if (tiled_fits(M, N, K))
         return TG_PATH_TILED;
@@ -228,6 +237,8 @@ tg_status run_gemm(tg_path path, tg_tiles tiles, int64_t M, int64_t N, int64_t K
     hipError_t e;
     if (path == TG_PATH_SKINNY) {
         const int64_t slabs = (N + 63) / 64;
+        if (M > 16)   // split-K is for a single row block; more rows run unsplit
+            splits = 1;
         if (splits == 0)
             splits = auto_splits(N, K, num_cu_of(s));
         if (splits > 1) {
