@@ -338,8 +338,8 @@ def path_of(tg, w, operand_set):
 
 
 def bench_rows(torch, tg, I, steps, warmup, copies=8):
-    """17 <= M <= 48 at the decode width (N = 11008, K = 4096, fp16, no
-    epilogue): the skinny kernel with two and three 16-row blocks per
+    """17 <= M <= 64 at the decode width (N = 11008, K = 4096, fp16, no
+    epilogue): the skinny kernel with two, three and four 16-row blocks per
     workgroup (the library's choice there), and the tiled family on the same
     operands for comparison, over `copies` rotating weight sets so that B
     streams from HBM."""
@@ -351,7 +351,7 @@ def bench_rows(torch, tg, I, steps, warmup, copies=8):
 
     Bs = [dev(I.random_bits((K, N), ("normal", 0.0, 0.02), I.F16, 4100 + c), (K, N)) for c in range(copies)]
     res = {}
-    for M in (32, 48):
+    for M in (32, 48, 64):
         A = dev(I.random_bits((M, K), ("normal", 0.0, 1.0), I.F16, 4200 + M), (M, K))
         C = torch.empty((M, N), dtype=torch.float16, device="cuda")
         st, path = tg.tg_gemm_plan(M, N, K, I.F16, A.data_ptr(), Bs[0].data_ptr(), None, I.EPI_NONE, C.data_ptr())
@@ -539,7 +539,7 @@ def main() -> int:
         log(f"{w4.name}: {ms4 * 1e3:.2f} us, {gbps:.0f} GB/s")
         del sets4
         torch.cuda.empty_cache()
-        log("secondary: 32 and 48 rows at the decode width (8 rotating weight sets)")
+        log("secondary: 32, 48 and 64 rows at the decode width (8 rotating weight sets)")
         sec.update(bench_rows(torch, tg, I, max(args.steps, 400), args.warmup))
         torch.cuda.empty_cache()
         log("secondary: weight-only 4-bit product at the same shape (16 rotating weight sets)")

@@ -75,10 +75,10 @@ typedef enum {
 
 /*
  * Kernel families.  TG_PATH_AUTO lets the library choose:
- *   TG_PATH_SKINNY         M <= 48 (the decode-shaped product): streams B from
+ *   TG_PATH_SKINNY         M <= 64 (the decode-shaped product): streams B from
  *                          HBM once; needs K % 8 == 0, N % 4 == 0, A 16-byte
  *                          aligned, B, C and bias 8-byte aligned.  Chosen
- *                          automatically for M <= 16, and for 17 <= M <= 48
+ *                          automatically for M <= 16, and for 17 <= M <= 64
  *                          while N <= 16384 (wider B runs faster tiled).
  *   TG_PATH_TILED          MFMA tiles (256x256 by default; see tg_tiles for
  *                          the other sizes and how one is chosen) staged

@@ -103,7 +103,8 @@ def test_empty_output_is_a_noop(lib, M, N, K):
 
 
 def test_empty_K_allows_null_operands(lib):
-    assert plan(64, 64, 0, A=None, B=None, bias=PBIAS, epi=I.EPI_BIAS) == (tg.TG_OK, tg.TG_PATH_TILED)
+    assert plan(80, 64, 0, A=None, B=None, bias=PBIAS, epi=I.EPI_BIAS) == (tg.TG_OK, tg.TG_PATH_TILED)
+    assert plan(64, 64, 0, A=None, B=None, bias=PBIAS, epi=I.EPI_BIAS) == (tg.TG_OK, tg.TG_PATH_SKINNY)
 
 
 @pytest.mark.parametrize("M,N,K,ptrs,path", [
@@ -112,10 +113,11 @@ def test_empty_K_allows_null_operands(lib):
     (16, 12, 8, {}, tg.TG_PATH_SKINNY),                 # N % 4 == 0 is enough
     (17, 11008, 4096, {}, tg.TG_PATH_SKINNY),          # two row blocks per workgroup
     (48, 16384, 4096, {}, tg.TG_PATH_SKINNY),          # three, 256 slabs: one round on 256 CUs
+    (64, 16384, 4096, {}, tg.TG_PATH_SKINNY),          # four
     (48, 16388, 4096, {}, tg.TG_PATH_TILED),           # a second round of slabs: tiled is faster
     (17, 28672, 4096, {}, tg.TG_PATH_TILED),
     (16, 28672, 4096, {}, tg.TG_PATH_SKINNY),          # one row block: skinny at any width
-    (49, 11008, 4096, {}, tg.TG_PATH_TILED),
+    (65, 11008, 4096, {}, tg.TG_PATH_TILED),
     (16, 11008, 4100, {}, tg.TG_PATH_TILED),            # K % 8 != 0: not skinny, tiled takes any shape
     (16, 11010, 4096, {}, tg.TG_PATH_TILED),            # N % 4 != 0
     (16, 11008, 4096, {"A": PA + 8}, tg.TG_PATH_TILED),
@@ -137,9 +139,9 @@ def test_kernel_family_choice(lib, M, N, K, ptrs, path):
 
 
 def test_explicit_path_requirements(lib):
-    # the skinny family needs M <= 48, K % 8 == 0, N % 4 == 0 and alignment;
+    # the skinny family needs M <= 64, K % 8 == 0, N % 4 == 0 and alignment;
     # the tiled family needs operands below its size limit
-    assert tg.tg_gemm_path(tg.TG_PATH_SKINNY, 49, 64, 64, I.F16, PA, PB, None, 0, PC, None) == tg.TG_ERR_UNSUPPORTED
+    assert tg.tg_gemm_path(tg.TG_PATH_SKINNY, 65, 64, 64, I.F16, PA, PB, None, 0, PC, None) == tg.TG_ERR_UNSUPPORTED
     assert tg.tg_gemm_path(tg.TG_PATH_SKINNY, 16, 64, 60, I.F16, PA, PB, None, 0, PC, None) == tg.TG_ERR_UNSUPPORTED
     assert tg.tg_gemm_path(tg.TG_PATH_SKINNY, 16, 64, 64, I.F16, PA + 4, PB, None, 0, PC, None) \
         == tg.TG_ERR_UNSUPPORTED

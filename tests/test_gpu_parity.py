@@ -70,7 +70,7 @@ def test_workload_small_integers_bit_exact(name):
 
 def _families(M, N, K):
     fams = [tg.TG_PATH_TILED_GENERIC, tg.TG_PATH_TILED]
-    if M <= 48 and K % 8 == 0 and N % 4 == 0:
+    if M <= 64 and K % 8 == 0 and N % 4 == 0:
         fams.append(tg.TG_PATH_SKINNY)
     return fams
 
@@ -124,10 +124,10 @@ def test_skinny_every_row_count(dtype):
 
 @pytest.mark.parametrize("dtype", [I.F16, I.BF16])
 def test_skinny_row_blocks_every_row_count(dtype):
-    # 17 <= M <= 48: the skinny kernel carries 2 or 3 blocks of 16 rows per
-    # workgroup, all multiplying the same B vectors
+    # 17 <= M <= 64: the skinny kernel carries 2, 3 or 4 blocks of 16 rows
+    # per workgroup, all multiplying the same B vectors (4 blocks on 4 waves)
     N, K = 4 * 97, 8 * 75
-    for M in range(17, 49):
+    for M in range(17, 65):
         A = I.random_bits((M, K), ("normal", 0.0, 1.0), dtype, 1800 + M)
         B = I.random_bits((K, N), ("normal", 0.0, 0.02), dtype, 1850 + M)
         bias = I.random_bits((N,), ("normal", 0.0, 0.1), dtype, 1870 + M)
@@ -135,7 +135,7 @@ def test_skinny_row_blocks_every_row_count(dtype):
         ref64, _ = oracle.gemm(M, N, K, dtype, A, B, bias, I.EPI_BIAS_GELU_TANH)
         out = run(M, N, K, dtype, A, B, bias, I.EPI_BIAS_GELU_TANH, path=tg.TG_PATH_SKINNY)
         check_tolerance(dtype, to_bits(out), ref64, f"skinny M={M}")
-        if M in (17, 32, 33, 48):
+        if M in (17, 32, 33, 48, 49, 64):
             Ai = I.small_int_bits((M, K), dtype, 1880 + M)
             Bi = I.small_int_bits((K, N), dtype, 1890 + M)
             bi = I.small_int_bits((N,), dtype, 1895 + M)
@@ -149,6 +149,8 @@ def test_skinny_row_blocks_every_row_count(dtype):
     (40, 16384, 4096),    # three blocks, the last with 8 rows; 256 slabs
     (24, 68, 3336),       # one partial slab, ragged last step
     (45, 4100, 8200),     # partial slab, three blocks, 257 steps
+    (64, 11008, 4096),    # four full blocks on four waves
+    (57, 4100, 8200),     # four blocks, the last with 9 rows; partial slab
 ])
 def test_skinny_row_blocks_full_size(M, N, K):
     dtype = I.F16
@@ -234,18 +236,21 @@ def test_gelu_epilogue_tight(dtype):
 @pytest.mark.parametrize("epi", [I.EPI_NONE, I.EPI_BIAS, I.EPI_BIAS_GELU_TANH])
 def test_empty_K_gives_epilogue_of_zero(path, epi):
     import torch
-    M, N = 16, 264
+    N = 264
     bias = I.random_bits((N,), ("uniform", -2.0, 2.0), I.F16, 50) if epi else None
-    _, refq = oracle.gemm(M, N, 0, I.F16, None, None, bias, epi)
-    log(f"[K=0] path={tg.PATH_NAMES[path]} epi={epi}")
-    out = run(M, N, 0, I.F16, np.zeros(0, np.uint16), np.zeros(0, np.uint16), bias, epi, path=path)
-    check_exact(to_bits(out), refq, "K=0")
+    for M in (16, 40, 64):   # one, three and four row blocks on the skinny path
+        _, refq = oracle.gemm(M, N, 0, I.F16, None, None, bias, epi)
+        log(f"[K=0] path={tg.PATH_NAMES[path]} M={M} epi={epi}")
+        out = run(M, N, 0, I.F16, np.zeros(0, np.uint16), np.zeros(0, np.uint16), bias, epi, path=path)
+        check_exact(to_bits(out), refq, f"K=0 M={M}")
 
 
 @pytest.mark.parametrize("path,M,N,K", [
     (tg.TG_PATH_TILED, 300, 264, 200),
     (tg.TG_PATH_TILED_GENERIC, 301, 263, 201),
     (tg.TG_PATH_SKINNY, 13, 260, 200),
+    (tg.TG_PATH_SKINNY, 37, 260, 200),
+    (tg.TG_PATH_SKINNY, 61, 260, 200),
 ])
 def test_guard_bands_untouched(path, M, N, K):
     """C sits inside a larger buffer; the bytes around it must survive."""

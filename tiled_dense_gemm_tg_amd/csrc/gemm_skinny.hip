@@ -1,4 +1,4 @@
-// gemm_skinny.hip -- the M <= 48 (decode-shaped) GEMM for gfx950.
+// gemm_skinny.hip -- the M <= 64 (decode-shaped) GEMM for gfx950.
 //
 // With at most 16 rows of A the product does 2*M flops per B element, far
 // below what keeps MFMA busy, so the kernel is shaped by HBM: B is read from
@@ -24,9 +24,10 @@
 //     whole slice of A into its own 16 KB of LDS by direct loads of 4 rows x
 //     256 contiguous bytes and reads it into registers in the MFMA layout,
 //     so that its loop streams only B;
-//   * 17 <= M <= 48: two or three such 16-row blocks of A per workgroup,
+//   * 17 <= M <= 64: two to four such 16-row blocks of A per workgroup,
 //     each with its own MFMAs on the same transposed B vectors, so B is
 //     still read once (A then comes from L2 in every step; no preload);
+//     four blocks run 4 waves per workgroup (one per SIMD) for registers;
 //   * the 8 waves' fp32 partial sums are added in LDS in a fixed order (no
 //     atomics, so results are reproducible), then the fused epilogue and
 //     8-byte stores;
@@ -63,19 +64,20 @@ struct ABatch {
 };
 __device__ __forceinline__ ABatch<1> u32x4_pair(u32x4 a, u32x4 b) { return ABatch<1>{{{a}, {b}}}; }
 
-// RB: 16-row blocks of A (and C) per workgroup, 1..3 (M <= 16 RB).  Every
+// RB: 16-row blocks of A (and C) per workgroup, 1..4 (M <= 16 RB).  Every
 // block multiplies the same B vectors, so B is still read once; the preload
-// path and split-K are for RB = 1 only.  (Four blocks need more than the 256
-// registers a lane has at two waves per SIMD and spill: 2-3x slower than
-// three.)
-template <class T, int EPI, bool PRELOAD, int RB>
-__global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args, SplitWs ws) {
-    static_assert(RB >= 1 && RB <= 3 && (RB == 1 || !PRELOAD), "row blocks");
+// path and split-K are for RB = 1 only.  W: waves per workgroup, splitting
+// K.  Four blocks need more than the 256 registers a lane has at two waves
+// per SIMD (with 8 waves they spilled and ran 2-3x slower than three), so
+// they run with W = 4, one wave per SIMD and up to 512 registers a lane.
+template <class T, int EPI, bool PRELOAD, int RB, int W = WAVES>
+__global__ __launch_bounds__(64 * W) void gemm_skinny_kernel(GemmArgs args, SplitWs ws) {
+    static_assert(RB >= 1 && RB <= 4 && (RB == 1 || !PRELOAD) && (W == WAVES || (RB == 4 && W == 4)), "row blocks");
     // Per wave 16 KB: its slice of A when that is staged (the preload path
     // below), then, after its k-loop, its RB 16 x 64 fp32 partial sums (4 KB
     // each).  Each wave touches only its own region until the barrier
     // before the cross-wave reduction.
-    __shared__ __attribute__((aligned(16))) u32x4 smem[WAVES * 1024];
+    __shared__ __attribute__((aligned(16))) u32x4 smem[W * 1024];
     auto red = [&](int w, int b, int i, int l) __attribute__((always_inline)) -> float & {
         return reinterpret_cast<float *>(smem)[4096 * w + 1024 * b + 64 * i + l];
     };
@@ -97,8 +99,8 @@ __global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args, Sp
     const int split = blockIdx.y;
     const int sp_begin = (int)(((int64_t)steps * split) / splits);
     const int sp_len = (int)(((int64_t)steps * (split + 1)) / splits) - sp_begin;
-    const int s_begin = sp_begin + (int)(((int64_t)sp_len * wave) / WAVES);
-    const int s_end = sp_begin + (int)(((int64_t)sp_len * (wave + 1)) / WAVES);
+    const int s_begin = sp_begin + (int)(((int64_t)sp_len * wave) / W);
+    const int s_end = sp_begin + (int)(((int64_t)sp_len * (wave + 1)) / W);
 
     f32x4 acc[RB][4];
 #pragma unroll
@@ -282,7 +284,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args, Sp
         for (int j = 0; j < 4; ++j) {
             float s = 0.f;
 #pragma unroll
-            for (int w = 0; w < WAVES; ++w)
+            for (int w = 0; w < W; ++w)
                 s += red(w, b, 4 * e + j, lane);
             y[j] = s;
         }
@@ -320,7 +322,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args, Sp
     } else {
         // the 4 RB (row block, column group) pairs are spread over the waves
 #pragma unroll
-        for (int q0 = 0; q0 < 4 * RB; q0 += WAVES) {
+        for (int q0 = 0; q0 < 4 * RB; q0 += W) {
             const int q = q0 + wave;
             if (q < 4 * RB) {
                 float y[4];
@@ -331,10 +333,10 @@ __global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args, Sp
     }
 }
 
-template <class T, int EPI, int RB>
+template <class T, int EPI, int RB, int W = WAVES>
 hipError_t launch_rows(const GemmArgs &a, const SplitWs &ws, hipStream_t stream) {
     const int slabs = (a.N + SLAB - 1) / SLAB;
-    hipLaunchKernelGGL((gemm_skinny_kernel<T, EPI, false, RB>), dim3(slabs, ws.splits), dim3(NTHREADS), 0, stream, a,
+    hipLaunchKernelGGL((gemm_skinny_kernel<T, EPI, false, RB, W>), dim3(slabs, ws.splits), dim3(64 * W), 0, stream, a,
                        ws);
     return hipGetLastError();
 }
@@ -343,8 +345,10 @@ template <class T, int EPI>
 hipError_t launch_typed(const GemmArgs &a, const SplitWs &ws, hipStream_t stream) {
     const int slabs = (a.N + SLAB - 1) / SLAB;
     if (a.M > 16) {   // several row blocks: no split-K (the host passes splits = 1)
-        if (ws.splits != 1 || a.M > 48)
+        if (ws.splits != 1 || a.M > 64)
             return hipErrorInvalidValue;
+        if (a.M > 48)
+            return launch_rows<T, EPI, 4, 4>(a, ws, stream);
         return a.M <= 32 ? launch_rows<T, EPI, 2>(a, ws, stream) : launch_rows<T, EPI, 3>(a, ws, stream);
     }
     // every wave's share of the 32-k steps is floor or ceil of a split's
