@@ -27,7 +27,7 @@
 //   * 17 <= M <= 64: two to four such 16-row blocks of A per workgroup,
 //     each with its own MFMAs on the same transposed B vectors, so B is
 //     still read once (A then comes from L2 in every step; no preload);
-//     four blocks run 4 waves per workgroup (one per SIMD) for registers;
+//     these run 4 waves per workgroup (one per SIMD) for registers;
 //   * the 8 waves' fp32 partial sums are added in LDS in a fixed order (no
 //     atomics, so results are reproducible), then the fused epilogue and
 //     8-byte stores;
@@ -67,12 +67,13 @@ __device__ __forceinline__ ABatch<1> u32x4_pair(u32x4 a, u32x4 b) { return ABatc
 // RB: 16-row blocks of A (and C) per workgroup, 1..4 (M <= 16 RB).  Every
 // block multiplies the same B vectors, so B is still read once; the preload
 // path and split-K are for RB = 1 only.  W: waves per workgroup, splitting
-// K.  Four blocks need more than the 256 registers a lane has at two waves
-// per SIMD (with 8 waves they spilled and ran 2-3x slower than three), so
-// they run with W = 4, one wave per SIMD and up to 512 registers a lane.
+// K: 8 for one block, 4 (one wave per SIMD, up to 512 registers a lane) for
+// several.  Four blocks need more than the 256 registers a lane has at two
+// waves per SIMD (with 8 waves they spilled and ran 2-3x slower than three
+// blocks), and two or three blocks ran 0-5 % faster on 4 waves than on 8.
 template <class T, int EPI, bool PRELOAD, int RB, int W = WAVES>
 __global__ __launch_bounds__(64 * W) void gemm_skinny_kernel(GemmArgs args, SplitWs ws) {
-    static_assert(RB >= 1 && RB <= 4 && (RB == 1 || !PRELOAD) && (W == WAVES || (RB == 4 && W == 4)), "row blocks");
+    static_assert(RB >= 1 && RB <= 4 && (RB == 1 || !PRELOAD) && (RB == 1 ? W == WAVES : W == 4), "row blocks");
     // Per wave 16 KB: its slice of A when that is staged (the preload path
     // below), then, after its k-loop, its RB 16 x 64 fp32 partial sums (4 KB
     // each).  Each wave touches only its own region until the barrier
@@ -349,7 +350,7 @@ hipError_t launch_typed(const GemmArgs &a, const SplitWs &ws, hipStream_t stream
             return hipErrorInvalidValue;
         if (a.M > 48)
             return launch_rows<T, EPI, 4, 4>(a, ws, stream);
-        return a.M <= 32 ? launch_rows<T, EPI, 2>(a, ws, stream) : launch_rows<T, EPI, 3>(a, ws, stream);
+        return a.M <= 32 ? launch_rows<T, EPI, 2, 4>(a, ws, stream) : launch_rows<T, EPI, 3, 4>(a, ws, stream);
     }
     // every wave's share of the 32-k steps is floor or ceil of a split's
     // share / WAVES, and a split's share floor or ceil of steps / splits
