@@ -165,13 +165,14 @@ def test_skinny_row_blocks_full_size(M, N, K):
 
 @pytest.mark.parametrize("dtype", [I.F16, I.BF16])
 @pytest.mark.parametrize("M,N,K", [
-    (16, 4 * 97, 4096),   # 16 steps of 32 k per wave
-    (5, 4 * 97, 2400),    # 75 steps: 9 or 10 per wave
+    (16, 4 * 97, 4096),   # 32 steps of 32 k per wave
+    (5, 4 * 97, 2400),    # 75 steps: 18 or 19 per wave
     (1, 520, 4008),       # 126 steps, the last with 8 of its 32 k
-    (11, 68, 3336),       # 105 steps: 13 or 14 per wave; one partial slab
+    (11, 68, 3336),       # 105 steps: 26 or 27 per wave; one partial slab
+    (7, 132, 2184),       # 69 steps: 17 or 18 per wave, the fewest that preload
 ])
 def test_skinny_preloaded_A(dtype, M, N, K):
-    # Shapes where every wave has 9..16 steps of 32 k, so the skinny kernel
+    # Shapes where every wave has 17..32 steps of 32 k, so the skinny kernel
     # stages its slice of A through LDS before streaming B.
     A = I.random_bits((M, K), ("normal", 0.0, 1.0), dtype, 900 + M)
     B = I.random_bits((K, N), ("normal", 0.0, 0.02), dtype, 901 + M)

@@ -9,7 +9,8 @@
 // moving each value, not the arithmetic.
 //
 // Layout of the work:
-//   * one workgroup per 64-column slab of B and C; its 8 waves split the K
+//   * one workgroup per 64-column slab of B and C; its 4 waves (one per
+//     SIMD, so a lane may hold up to 512 registers) split the K
 //     range into contiguous parts and each streams its part of the slab;
 //   * per 32-k step a lane loads rows kb + 8 h + r (r = 0..7, h = lane/16) of
 //     the four columns 4 p .. 4 p + 3 (p = lane % 16) and transposes them in
@@ -20,15 +21,14 @@
 //     MFMA columns are the (at most 16) rows of A;
 //   * loads come in batches of 2 steps, double-buffered in registers, so the
 //     next batch is in flight while the current one is multiplied; where
-//     every wave has 9 to 16 steps (K = 4096: 16) a wave first copies its
-//     whole slice of A into its own 16 KB of LDS by direct loads of 4 rows x
+//     every wave has 17 to 32 steps (K = 4096: 32) a wave first copies its
+//     whole slice of A into its own 32 KB of LDS by direct loads of 4 rows x
 //     256 contiguous bytes and reads it into registers in the MFMA layout,
 //     so that its loop streams only B;
 //   * 17 <= M <= 64: two to four such 16-row blocks of A per workgroup,
 //     each with its own MFMAs on the same transposed B vectors, so B is
 //     still read once (A then comes from L2 in every step; no preload);
-//     these run 4 waves per workgroup (one per SIMD) for registers;
-//   * the 8 waves' fp32 partial sums are added in LDS in a fixed order (no
+//   * the 4 waves' fp32 partial sums are added in LDS in a fixed order (no
 //     atomics, so results are reproducible), then the fused epilogue and
 //     8-byte stores;
 //   * split-K (splits > 1, a grid of slabs x splits): when there are too few
@@ -45,10 +45,10 @@ namespace tg {
 namespace {
 
 constexpr int SLAB = 64;       // columns per workgroup
-constexpr int WAVES = 8;       // waves per workgroup, splitting K
+constexpr int WAVES = 4;       // waves per workgroup (one per SIMD), splitting K
 constexpr int UNROLL = 2;      // 32-k steps per load batch (two batches in flight)
 constexpr int NTHREADS = 64 * WAVES;
-constexpr int PRE = 16;        // most 32-k steps per wave whose A slice is preloaded into registers
+constexpr int PRE = 32;        // most 32-k steps per wave whose A slice is preloaded into registers
 constexpr uint32_t OOB = 0xFFFFFFF0u;    // byte offset beyond every operand
 constexpr uint32_t ASHIFT = 4096;        // the staged-A buffer starts this far before A
 // Cache policy of the B loads: non-temporal.  Each B element is read once,
@@ -66,21 +66,22 @@ __device__ __forceinline__ ABatch<1> u32x4_pair(u32x4 a, u32x4 b) { return ABatc
 
 // RB: 16-row blocks of A (and C) per workgroup, 1..4 (M <= 16 RB).  Every
 // block multiplies the same B vectors, so B is still read once; the preload
-// path and split-K are for RB = 1 only.  W: waves per workgroup, splitting
-// K: 8 for one block, 4 (one wave per SIMD, up to 512 registers a lane) for
-// several.  Four blocks need more than the 256 registers a lane has at two
-// waves per SIMD (with 8 waves they spilled and ran 2-3x slower than three
-// blocks), and two or three blocks ran 0-5 % faster on 4 waves than on 8.
-template <class T, int EPI, bool PRELOAD, int RB, int W = WAVES>
-__global__ __launch_bounds__(64 * W) void gemm_skinny_kernel(GemmArgs args, SplitWs ws) {
-    static_assert(RB >= 1 && RB <= 4 && (RB == 1 || !PRELOAD) && (RB == 1 ? W == WAVES : W == 4), "row blocks");
-    // Per wave 16 KB: its slice of A when that is staged (the preload path
-    // below), then, after its k-loop, its RB 16 x 64 fp32 partial sums (4 KB
-    // each).  Each wave touches only its own region until the barrier
-    // before the cross-wave reduction.
-    __shared__ __attribute__((aligned(16))) u32x4 smem[W * 1024];
+// path and split-K are for RB = 1 only.  One wave per SIMD gives a lane up
+// to 512 registers: four blocks need more than the 256 of two waves per
+// SIMD (with 8 waves they spilled and ran 2-3x slower than three blocks),
+// and every instance ran as fast or faster on 4 waves than on 8 (M = 16,
+// K = 4096 with the preload: 18.95 against 19.86 us).
+template <class T, int EPI, bool PRELOAD, int RB>
+__global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args, SplitWs ws) {
+    static_assert(RB >= 1 && RB <= 4 && (RB == 1 || !PRELOAD), "row blocks");
+    // Per wave RS floats of LDS: 32 KB with the preload (its slice of A,
+    // 16 rows x 32 PRE k), else 16 KB; after its k-loop, its RB 16 x 64 fp32
+    // partial sums (4 KB each).  Each wave touches only its own region until
+    // the barrier before the cross-wave reduction.
+    constexpr int RS = PRELOAD ? 256 * PRE : 4096;
+    __shared__ __attribute__((aligned(16))) u32x4 smem[WAVES * RS / 4];
     auto red = [&](int w, int b, int i, int l) __attribute__((always_inline)) -> float & {
-        return reinterpret_cast<float *>(smem)[4096 * w + 1024 * b + 64 * i + l];
+        return reinterpret_cast<float *>(smem)[RS * w + 1024 * b + 64 * i + l];
     };
     const int M = args.M, N = args.N, K = args.K;
     const uint16_t *__restrict__ A = args.A;
@@ -100,8 +101,8 @@ __global__ __launch_bounds__(64 * W) void gemm_skinny_kernel(GemmArgs args, Spli
     const int split = blockIdx.y;
     const int sp_begin = (int)(((int64_t)steps * split) / splits);
     const int sp_len = (int)(((int64_t)steps * (split + 1)) / splits) - sp_begin;
-    const int s_begin = sp_begin + (int)(((int64_t)sp_len * wave) / W);
-    const int s_end = sp_begin + (int)(((int64_t)sp_len * (wave + 1)) / W);
+    const int s_begin = sp_begin + (int)(((int64_t)sp_len * wave) / WAVES);
+    const int s_end = sp_begin + (int)(((int64_t)sp_len * (wave + 1)) / WAVES);
 
     f32x4 acc[RB][4];
 #pragma unroll
@@ -180,13 +181,13 @@ __global__ __launch_bounds__(64 * W) void gemm_skinny_kernel(GemmArgs args, Spli
     u32x2 vb0[UNROLL][8], vb1[UNROLL][8];
     ABatch<RB> va0, va1;
     if constexpr (PRELOAD) {
-        // Every wave has PRE / 2 < steps <= PRE (K = 4096 on 8 waves: 16;
+        // Every wave has PRE / 2 < steps <= PRE (K = 4096 on 4 waves: 32;
         // the host picks this instance only then) and reads its whole slice
         // of A (16 rows x 32 PRE k) into registers first, so the loop
         // streams only B.  A separate instance rather than a branch: merged
         // with the other loop, the compiler's wait counts would stall on
         // loads of the path not taken.
-        // The slice goes through the wave's LDS region: 16 direct loads,
+        // The slice goes through the wave's LDS region: PRE direct loads,
         // each of 4 rows x 256 contiguous bytes (half the cache lines of
         // 16 rows x 64 bytes), then 16-byte reads in the MFMA layout.
         // Load j = 4 c4 + rq: row r = 4 rq + lane / 16 and k = 32 s_begin +
@@ -195,7 +196,7 @@ __global__ __launch_bounds__(64 * W) void gemm_skinny_kernel(GemmArgs args, Spli
         // of 16 rows' same chunk hit 16 different bank groups).  LDS byte
         // 4096 c4 + 256 r + 16 slot of the region.  Chunks at k >= K or past
         // the wave's steps, and rows >= M, are out of range and read zero.
-        const uint32_t region = lds_address(smem) + 16384u * (uint32_t)wave;
+        const uint32_t region = lds_address(smem) + 4u * RS * (uint32_t)wave;
         auto load_b = [&](u32x2 (&vb)[UNROLL][8], int s0) __attribute__((always_inline)) {
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u) {
@@ -230,7 +231,7 @@ __global__ __launch_bounds__(64 * W) void gemm_skinny_kernel(GemmArgs args, Spli
             }
         }
         load_b(vb1, s_begin + UNROLL);
-        // the 16 A loads are older than the second batch's 8 UNROLL B loads
+        // the PRE A loads are older than the second batch's 8 UNROLL B loads
         wait_vmcnt<8 * UNROLL>();
         u32x4 pa[PRE];
 #pragma unroll
@@ -285,7 +286,7 @@ __global__ __launch_bounds__(64 * W) void gemm_skinny_kernel(GemmArgs args, Spli
         for (int j = 0; j < 4; ++j) {
             float s = 0.f;
 #pragma unroll
-            for (int w = 0; w < W; ++w)
+            for (int w = 0; w < WAVES; ++w)
                 s += red(w, b, 4 * e + j, lane);
             y[j] = s;
         }
@@ -323,7 +324,7 @@ __global__ __launch_bounds__(64 * W) void gemm_skinny_kernel(GemmArgs args, Spli
     } else {
         // the 4 RB (row block, column group) pairs are spread over the waves
 #pragma unroll
-        for (int q0 = 0; q0 < 4 * RB; q0 += W) {
+        for (int q0 = 0; q0 < 4 * RB; q0 += WAVES) {
             const int q = q0 + wave;
             if (q < 4 * RB) {
                 float y[4];
@@ -334,10 +335,10 @@ __global__ __launch_bounds__(64 * W) void gemm_skinny_kernel(GemmArgs args, Spli
     }
 }
 
-template <class T, int EPI, int RB, int W = WAVES>
+template <class T, int EPI, int RB>
 hipError_t launch_rows(const GemmArgs &a, const SplitWs &ws, hipStream_t stream) {
     const int slabs = (a.N + SLAB - 1) / SLAB;
-    hipLaunchKernelGGL((gemm_skinny_kernel<T, EPI, false, RB, W>), dim3(slabs, ws.splits), dim3(64 * W), 0, stream, a,
+    hipLaunchKernelGGL((gemm_skinny_kernel<T, EPI, false, RB>), dim3(slabs, ws.splits), dim3(NTHREADS), 0, stream, a,
                        ws);
     return hipGetLastError();
 }
@@ -349,8 +350,8 @@ hipError_t launch_typed(const GemmArgs &a, const SplitWs &ws, hipStream_t stream
         if (ws.splits != 1 || a.M > 64)
             return hipErrorInvalidValue;
         if (a.M > 48)
-            return launch_rows<T, EPI, 4, 4>(a, ws, stream);
-        return a.M <= 32 ? launch_rows<T, EPI, 2, 4>(a, ws, stream) : launch_rows<T, EPI, 3, 4>(a, ws, stream);
+            return launch_rows<T, EPI, 4>(a, ws, stream);
+        return a.M <= 32 ? launch_rows<T, EPI, 2>(a, ws, stream) : launch_rows<T, EPI, 3>(a, ws, stream);
     }
     // every wave's share of the 32-k steps is floor or ceil of a split's
     // share / WAVES, and a split's share floor or ceil of steps / splits
