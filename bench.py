@@ -10,21 +10,33 @@ the skinny kernel), the weight-only 4-bit product at that decode shape and the
 attention forward at the FlashAttention benchmark shape are timed as secondary
 lines in the same JSON object.
 
-Timing: W warm-up launches, then K launches back to back on torch's current
+Timing: W warm-up launches, then further untimed launches until a quarter of
+a second has passed (the clock takes a few tens of milliseconds to settle
+after a change of load), then K launches back to back on torch's current
 stream (the stream tg_gemm is given), bracketed by torch.cuda.synchronize()
 and HIP events recorded on that stream; the per-launch time is the events'
-elapsed time / K.  Each secondary line also runs untimed launches for a
-quarter of a second before its timed ones, so that it is timed at the clock
-its own load settles at rather than the previous line's.  The skinny shape rotates over 8 independent operand sets
-(720 MB, more than the 256 MB Infinity Cache) so every launch streams B from
-HBM.
+elapsed time / K.  Every secondary line settles the same way before it is
+timed.  The fused and unfused forms of an epilogue workload (and the product
+without epilogue) are timed in alternating blocks and compared by their
+medians.  The skinny shape rotates over 8 independent operand sets (720 MB,
+more than the 256 MB Infinity Cache) so every launch streams B from HBM.
 
 Roofline: FLOPs = 2*M*N*K (padded-tile work and the epilogue's few flops per
 output are not counted); algorithmic bytes = every operand once + C once (+
 bias).  Peaks are MI355X's published dense fp16/bf16 MFMA rate (2.5 PFLOP/s)
-and HBM3E bandwidth (8 TB/s).  The CPU baseline is the oracle (test
+and HBM3E bandwidth (8 TB/s).  HBM traffic, MFMA utilisation and the shader
+clock come from rocprofv3 counter runs of this same script, summarised into
+profiles/counters.json by `bench.py --summarise` (reported only while the
+kernel sources are the ones profiled).  The CPU baseline is the oracle (test
 infrastructure, untuned) timed on a bounded sample of rows of the same
 workload on the host cores.
+
+Profiling: `--dispatch-log FILE` records, in launch order, a label for every
+kernel this script launches through the library; `--profile-run` drops the
+settling and shortens every line (for counter runs, which serialise
+dispatches).  `--summarise DIR` reads the rocprofv3 CSV output of the runs
+that PROFILE_COMMANDS lists, together with their dispatch logs, and writes
+the summaries under profiles/.
 """
 from __future__ import annotations
 
@@ -43,6 +55,7 @@ if ROOT not in sys.path:
 
 PEAK_MFMA_F16_TFLOPS = 2500.0   # MI355X dense fp16/bf16 MFMA
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
+MFMA_FLOP_PER_CLK_SIMD = 1024   # dense fp16/bf16 MFMA: 2.5 PFLOP/s = 1024 SIMDs x 1024 x 2.4 GHz
 METRIC = "GEMM TFLOP/s and % MFMA peak at 4096³/8192³ fp16; HBM GB/s at M=16"
 MAIN = "gemm_f16_8192x8192x8192_bias_gelu_tanh"
 SQUARE = "gemm_f16_4096x4096x4096"
@@ -51,8 +64,9 @@ RAGGED = "gemm_bf16_4000x4093x4111_bias_gelu_tanh"
 KERNEL_SOURCES = ["gemm_tiled.hip", "gemm_tiled_generic.hip", "gemm_skinny.hip", "gemm_w4.hip", "attention_fwd.hip",
                   "elementwise.hip", "tg_device.h", "tg_tile.h", "tg_launch.h", "tg_split.h", "tg_direct.h",
                   "tg_gemm_host.hip"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-SETTLE_S = 0.25   # untimed launches before each secondary line, in seconds of wall time
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
+SETTLE_S = 0.25   # untimed launches before every timed line, in seconds of wall time
+FUSION_ROUNDS = 4  # alternating blocks of fused / unfused / no-epilogue launches
 
 
 # ---------------------------------------------------------------- accounting
@@ -87,6 +101,13 @@ def accumulator_regs_per_thread(bm: int, bn: int, threads: int, acc_bytes: int =
     return bm * bn * acc_bytes // 4 // threads
 
 
+def attention_flops(B: int, H: int, D: int, Sq: int, Sk: int, causal: bool) -> int:
+    """Two products of 2*D flops per visible (query, key) pair: 4*B*H*D*pairs;
+    with the causal mask (Sq == Sk) a query i sees keys 0..i."""
+    pairs = Sq * (Sq + 1) // 2 if causal else Sq * Sk
+    return 4 * B * H * D * pairs
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
@@ -95,44 +116,67 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
-    were taken on the current kernel sources; else None."""
+def measured(label: str):
+    """The committed counter record of one bench line (HBM traffic, MFMA
+    utilisation, shader clock), if it was taken on the current kernel
+    sources; else None."""
     try:
-        with open(TRAFFIC_FILE) as fh:
-            rec = json.load(fh).get(workload)
+        with open(COUNTERS_FILE) as fh:
+            rec = json.load(fh).get("lines", {}).get(label)
     except (OSError, ValueError):
         return None
     if not rec or rec.get("kernel_hash") != kernel_source_hash():
         return None
-    return rec.get("bytes_per_launch")
+    return rec
+
+
+def measured_traffic(label: str):
+    """HBM bytes per launch (fetched + written past L2) of one bench line."""
+    rec = measured(label)
+    return rec.get("bytes_per_launch") if rec else None
 
 
 def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+class DispatchLog:
+    """A label for every kernel the bench launches through the library, in
+    launch order, run-length encoded as [label, kernels]; written with
+    --dispatch-log so that the profile summariser can tell which dispatch of
+    a rocprofv3 run belongs to which bench line."""
+
+    def __init__(self):
+        self.entries = []
+
+    def note(self, label: str, kernels: int = 1) -> None:
+        if self.entries and self.entries[-1][0] == label:
+            self.entries[-1][1] += kernels
+        else:
+            self.entries.append([label, kernels])
+
+    def expand(self):
+        return [lab for lab, n in self.entries for _ in range(n)]
+
+
+LOG = DispatchLog()
+UNFUSED_PARTS = {1: ["product", "bias pass"], 2: ["product", "bias pass", "GELU pass"]}
+
+
 # ---------------------------------------------------------------- timing
 
-def time_gemm(torch, tg, w, sets, steps, warmup, unfused=False, settle_s=SETTLE_S):
-    """Per-launch time (ms) of tg_gemm (or, with `unfused`, of the three-launch
-    tg_gemm_unfused) over `sets` rotating operand sets."""
-    handle = torch.cuda.current_stream().cuda_stream
-    calls = []
-    for A, B, bias, C in sets:
-        calls.append((A.data_ptr(), B.data_ptr(), bias.data_ptr() if bias is not None else None, C.data_ptr()))
-
-    def launch(i):
-        a, b, bi, c = calls[i % len(calls)]
-        fn = tg.tg_gemm_unfused if unfused else tg.tg_gemm
-        st = fn(w.M, w.N, w.K, w.dtype, a, b, bi, w.epilogue, c, handle)
-        if st != tg.TG_OK:
-            raise RuntimeError(f"tg_gemm failed: {tg.tg_status_string(st)}")
-
-    return time_calls(torch, launch, steps, warmup, with_wall=True, settle_s=settle_s)
+class Timing:
+    """How lines are timed: settle seconds before each timed line, and a
+    divisor for the step counts (profile runs shorten everything)."""
+    settle_s = SETTLE_S
+    short = False
 
 
-def time_calls(torch, launch, steps, warmup, with_wall=False, settle_s=SETTLE_S):
+def steps_for(n: int) -> int:
+    return max(2, n // 10) if Timing.short else n
+
+
+def time_calls(torch, launch, steps, warmup, with_wall=False, settle_s=None):
     """Per-launch time (ms) of launch(i) for i = 0 .. steps-1 on the current
     stream: HIP events recorded on that stream around the timed launches,
     after `warmup` untimed ones, then further untimed ones until `settle_s`
@@ -140,8 +184,9 @@ def time_calls(torch, launch, steps, warmup, with_wall=False, settle_s=SETTLE_S)
     after a change of load: the first ~15 ms of a 150-us kernel ran 10 %
     slower), and a synchronisation; with `with_wall`, also the host's wall
     time (s) from before the first timed launch to after the closing
-    synchronisation.  The main line passes settle_s = 0: it does exactly the
-    requested warm-up steps."""
+    synchronisation."""
+    if settle_s is None:
+        settle_s = Timing.settle_s
     stream = torch.cuda.current_stream()
     for i in range(warmup):
         launch(i)
@@ -167,6 +212,59 @@ def time_calls(torch, launch, steps, warmup, with_wall=False, settle_s=SETTLE_S)
     return (ms, wall) if with_wall else ms
 
 
+def gemm_launcher(torch, tg, w, sets, label, mode="fused"):
+    """launch(i) for tg_gemm over `sets` rotating operand sets; mode
+    "unfused" runs tg_gemm_unfused (product, then one pass per epilogue
+    step), "none" the product without epilogue."""
+    handle = torch.cuda.current_stream().cuda_stream
+    calls = [(A.data_ptr(), B.data_ptr(), bias.data_ptr() if bias is not None else None, C.data_ptr())
+             for A, B, bias, C in sets]
+    nk = 1 + (EPILOGUE_PASSES[w.epilogue] if mode == "unfused" else 0)
+
+    def launch(i):
+        a, b, bi, c = calls[i % len(calls)]
+        LOG.note(label, nk)
+        if mode == "unfused":
+            st = tg.tg_gemm_unfused(w.M, w.N, w.K, w.dtype, a, b, bi, w.epilogue, c, handle)
+        elif mode == "none":
+            st = tg.tg_gemm(w.M, w.N, w.K, w.dtype, a, b, None, 0, c, handle)
+        else:
+            st = tg.tg_gemm(w.M, w.N, w.K, w.dtype, a, b, bi, w.epilogue, c, handle)
+        if st != tg.TG_OK:
+            raise RuntimeError(f"tg_gemm failed: {tg.tg_status_string(st)}")
+
+    return launch
+
+
+def time_gemm(torch, tg, w, sets, steps, warmup, label=None, mode="fused", settle_s=None):
+    """Per-launch time (ms) and wall time (s) of one gemm line."""
+    launch = gemm_launcher(torch, tg, w, sets, label or w.name, mode)
+    return time_calls(torch, launch, steps, warmup, with_wall=True, settle_s=settle_s)
+
+
+def fusion_comparison(torch, tg, w, sets, steps, warmup):
+    """The fused epilogue against the unfused form (product, then a pass per
+    epilogue step) and against the product alone, timed in alternating
+    blocks under the same conditions: one settle before the first block,
+    then FUSION_ROUNDS rounds of one block of each form, the order reversed
+    every round; each form's time is the median over its blocks."""
+    modes = ["fused", "unfused", "none"]
+    labels = {"fused": w.name, "unfused": f"{w.name} unfused", "none": f"{w.name} no epilogue"}
+    launch = {m: gemm_launcher(torch, tg, w, sets, labels[m], m) for m in modes}
+    time_calls(torch, launch["fused"], 1, warmup)   # settle
+    times = {m: [] for m in modes}
+    for r in range(FUSION_ROUNDS):
+        for m in (modes if r % 2 == 0 else modes[::-1]):
+            times[m].append(time_calls(torch, launch[m], steps, 2, settle_s=0.0))
+    med = {m: sorted(v)[len(v) // 2] for m, v in times.items()}
+    return {"fused_us": round(med["fused"] * 1e3, 2), "unfused_us": round(med["unfused"] * 1e3, 2),
+            "no_epilogue_us": round(med["none"] * 1e3, 2),
+            "fusion_speedup": round(med["unfused"] / med["fused"], 3),
+            "epilogue_cost": round(med["fused"] / med["none"] - 1.0, 4),
+            "blocks": FUSION_ROUNDS, "launches_per_block": steps,
+            "unfused_extra_bytes": EPILOGUE_PASSES[w.epilogue] * 4 * w.M * w.N}
+
+
 def bench_w4(torch, tg, I, steps, warmup, copies=16):
     """The weight-only 4-bit product at the decode shape, with `copies`
     rotating weight sets (more bytes than the 256 MB MALL) so the packed
@@ -183,6 +281,7 @@ def bench_w4(torch, tg, I, steps, warmup, copies=16):
     sets = []
     for c in range(copies):
         q = torch.from_numpy(I.w4_weights(K, N, sq + 10 * c)).cuda()
+        LOG.note("w4 weight packing")
         packed = tg.w4_pack(q)
         del q
         S = dev(I.random_bits((K // G, N), wq["scale_dist"], dt, ss + 10 * c), (K // G, N))
@@ -190,15 +289,16 @@ def bench_w4(torch, tg, I, steps, warmup, copies=16):
         sets.append((packed, S, C))
     handle = torch.cuda.current_stream().cuda_stream
 
-    def launch(i, pool=sets):
+    def launch(i, pool=sets, label=wq["name"]):
         packed, S, C = pool[i % len(pool)]
+        LOG.note(label)
         st = tg.tg_gemm_w4(M, N, K, dt, A.data_ptr(), packed.data_ptr(), S.data_ptr(), G, None, I.EPI_NONE,
                            C.data_ptr(), handle)
         if st != tg.TG_OK:
             raise RuntimeError(f"tg_gemm_w4 failed: {tg.tg_status_string(st)}")
 
     ms = time_calls(torch, launch, steps, warmup)
-    hot = time_calls(torch, lambda i: launch(i, sets[:1]), steps, warmup)
+    hot = time_calls(torch, lambda i: launch(i, sets[:1], f"{wq['name']} hot"), steps, warmup)
     nbytes = tg.tg_w4_packed_bytes(K, N) + 2 * (K // G) * N + 2 * M * K + 2 * M * N
     return wq["name"], ms, hot, nbytes
 
@@ -206,13 +306,14 @@ def bench_w4(torch, tg, I, steps, warmup, copies=16):
 TILE_CONFIGS = {"256x256": 1, "256x128": 2, "128x256": 3, "128x128": 4}   # tg_tiles values
 
 
-def time_tiled(torch, tg, M, N, K, dtype, epi, A, B, bias, C, cfg, steps, warmup):
+def time_tiled(torch, tg, M, N, K, dtype, epi, A, B, bias, C, cfg, steps, warmup, label):
     """Per-launch time (ms) of tg_gemm_tiled with tile configuration cfg
     (0: the library's choice, through tg_gemm)."""
     handle = torch.cuda.current_stream().cuda_stream
     a, b, bi, c = A.data_ptr(), B.data_ptr(), bias.data_ptr() if bias is not None else None, C.data_ptr()
 
     def launch(i):
+        LOG.note(label)
         st = (tg.tg_gemm_tiled(cfg, M, N, K, dtype, a, b, bi, epi, c, handle) if cfg
               else tg.tg_gemm(M, N, K, dtype, a, b, bi, epi, c, handle))
         if st != tg.TG_OK:
@@ -232,8 +333,10 @@ def bench_tile_choice(torch, tg, I, steps, warmup):
         flops = gemm_flops(w.M, w.N, w.K)
         per = {}
         for cname, cfg in TILE_CONFIGS.items():
-            per[cname] = time_tiled(torch, tg, w.M, w.N, w.K, w.dtype, w.epilogue, A, B, bias, C, cfg, steps, warmup)
-        ms_auto = time_tiled(torch, tg, w.M, w.N, w.K, w.dtype, w.epilogue, A, B, bias, C, 0, steps, warmup)
+            per[cname] = time_tiled(torch, tg, w.M, w.N, w.K, w.dtype, w.epilogue, A, B, bias, C, cfg, steps, warmup,
+                                    f"{name} {cname}")
+        ms_auto = time_tiled(torch, tg, w.M, w.N, w.K, w.dtype, w.epilogue, A, B, bias, C, 0, steps, warmup,
+                             f"{name} auto")
         st, auto = tg.tg_gemm_tiles_plan(w.M, w.N, w.K, cus)
         best = min(per, key=per.get)
         out[name] = {"auto": tg.TILES_NAMES.get(auto, "?"), "auto_us": round(ms_auto * 1e3, 2),
@@ -241,7 +344,7 @@ def bench_tile_choice(torch, tg, I, steps, warmup):
                      "per_config_us": {k: round(v * 1e3, 2) for k, v in per.items()},
                      "fastest": best, "auto_vs_fastest": round(per[best] / ms_auto, 3),
                      "speedup_vs_256x256": round(per["256x256"] / ms_auto, 3),
-                     "traffic": measured_traffic(f"{name} {tg.TILES_NAMES.get(auto, '?')}")}
+                     "traffic": measured_traffic(f"{name} auto")}
         log(f"{name}: auto {tg.TILES_NAMES.get(auto)} {ms_auto * 1e3:.1f} us, fastest {best} "
             f"{per[best] * 1e3:.1f} us, 256x256 {per['256x256'] * 1e3:.1f} us")
         del sets, A, B, bias, C
@@ -267,7 +370,7 @@ def tile_sweep(torch, tg, I, steps, warmup):
     K = 8192
     A, B, C = operands(8192, 8192, K)
     for cname, cfg in TILE_CONFIGS.items():
-        ms = time_tiled(torch, tg, 8192, 8192, K, 0, 0, A, B, None, C, cfg, steps, warmup)
+        ms = time_tiled(torch, tg, 8192, 8192, K, 0, 0, A, B, None, C, cfg, steps, warmup, f"sweep full {cname}")
         res["full"][cname] = {"us": round(ms * 1e3, 1), "TFLOP/s": round(gemm_flops(8192, 8192, K) / ms / 1e9, 1)}
         log(f"sweep full 8192x8192x{K} {cname}: {ms * 1e3:.1f} us")
     del A, B, C
@@ -277,7 +380,7 @@ def tile_sweep(torch, tg, I, steps, warmup):
         bm, bn = (int(v) for v in cname.split("x"))
         M, N = tm * bm, tn * bn
         A, B, C = operands(M, N, K)
-        ms = time_tiled(torch, tg, M, N, K, 0, 0, A, B, None, C, cfg, steps, warmup)
+        ms = time_tiled(torch, tg, M, N, K, 0, 0, A, B, None, C, cfg, steps, warmup, f"sweep single {cname}")
         res["single"][cname] = {"shape": f"{M}x{N}x{K}", "us": round(ms * 1e3, 1),
                                 "TFLOP/s": round(gemm_flops(M, N, K) / ms / 1e9, 1)}
         log(f"sweep single {M}x{N}x{K} {cname}: {ms * 1e3:.1f} us")
@@ -288,13 +391,6 @@ def tile_sweep(torch, tg, I, steps, warmup):
     res["shape_classes"] = bench_tile_choice(torch, tg, I, steps, warmup)
     torch.cuda.empty_cache()
     return res
-
-
-def attention_flops(B: int, H: int, D: int, Sq: int, Sk: int, causal: bool) -> int:
-    """Two products of 2*D flops per visible (query, key) pair: 4*B*H*D*pairs;
-    with the causal mask (Sq == Sk) a query i sees keys 0..i."""
-    pairs = Sq * (Sq + 1) // 2 if causal else Sq * Sk
-    return 4 * B * H * D * pairs
 
 
 def bench_attention(torch, tg, I, steps, warmup):
@@ -313,7 +409,11 @@ def bench_attention(torch, tg, I, steps, warmup):
     handle = torch.cuda.current_stream().cuda_stream
     out = {}
     for causal in (False, True):
-        def launch(i, c=int(causal)):
+        key = "causal" if causal else "non_causal"
+        label = f"{wa['name']} {key.replace('_', '-')}"
+
+        def launch(i, c=int(causal), label=label):
+            LOG.note(label)
             st = tg.tg_attention_fwd(Bn, S, S, H, D, dt, Q.data_ptr(), K.data_ptr(), V.data_ptr(), c, 0.0,
                                      O.data_ptr(), handle)
             if st != tg.TG_OK:
@@ -321,10 +421,9 @@ def bench_attention(torch, tg, I, steps, warmup):
 
         ms = time_calls(torch, launch, steps, warmup)
         tf = attention_flops(Bn, H, D, S, S, causal) / (ms * 1e-3) / 1e12
-        key = "causal" if causal else "non_causal"
         out[key] = {"us_per_launch": round(ms * 1e3, 2), "TFLOP/s": round(tf, 2),
                     "frac_mfma_peak": round(tf / PEAK_MFMA_F16_TFLOPS, 4),
-                    "traffic": measured_traffic(f"{wa['name']} {key.replace('_', '-')}")}
+                    "traffic": measured_traffic(label)}
         log(f"{wa['name']} causal={causal}: {ms * 1e3:.1f} us, {tf:.1f} TFLOP/s")
     return wa["name"], out
 
@@ -356,9 +455,13 @@ def bench_rows(torch, tg, I, steps, warmup, copies=8):
         C = torch.empty((M, N), dtype=torch.float16, device="cuda")
         st, path = tg.tg_gemm_plan(M, N, K, I.F16, A.data_ptr(), Bs[0].data_ptr(), None, I.EPI_NONE, C.data_ptr())
         assert st == tg.TG_OK, st
+        name = f"gemm_f16_rows_{M}x{N}x{K}"
         times = {}
         for p in (tg.TG_PATH_AUTO, tg.TG_PATH_TILED):
-            def launch(i, p=p):
+            label = name if p == tg.TG_PATH_AUTO else f"{name} tiled"
+
+            def launch(i, p=p, label=label):
+                LOG.note(label)
                 st = tg.tg_gemm_path(p, M, N, K, I.F16, A.data_ptr(), Bs[i % copies].data_ptr(), None, I.EPI_NONE,
                                      C.data_ptr(), handle)
                 if st != tg.TG_OK:
@@ -366,12 +469,12 @@ def bench_rows(torch, tg, I, steps, warmup, copies=8):
             times[p] = time_calls(torch, launch, steps, warmup)
         nbytes = gemm_alg_bytes(M, N, K)
         ms = times[tg.TG_PATH_AUTO]
-        res[f"gemm_f16_rows_{M}x{N}x{K}"] = {
+        res[name] = {
             "us_per_launch": round(ms * 1e3, 3), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
             "frac_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
             "path": tg.PATH_NAMES[path], "tiled_us": round(times[tg.TG_PATH_TILED] * 1e3, 3),
             "speedup_vs_tiled": round(times[tg.TG_PATH_TILED] / ms, 3),
-            "traffic": measured_traffic(f"gemm_f16_rows_{M}x{N}x{K}")}
+            "traffic": measured_traffic(name)}
         log(f"rows M={M}: {ms * 1e3:.2f} us ({tg.PATH_NAMES[path]}), tiled {times[tg.TG_PATH_TILED] * 1e3:.2f} us")
     return res
 
@@ -392,6 +495,17 @@ def device_operands(torch, I, w, copies=1):
                      None if bias is None else (bias if c == 0 else bias.clone()),
                      torch.empty((w.M, w.N), dtype=tdt, device="cuda")))
     return ops, sets
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(I, w, ops, budget_s):
@@ -415,10 +529,229 @@ def cpu_baseline(I, w, ops, budget_s):
         "unit": "TFLOP/s",
         "cores": oracle.max_threads(),
         "kind": "oracle",
+        "cpu_model": cpu_model(),
         "sample": f"{n} of {w.M} rows of {w.name} (all {w.N} columns, K={w.K}), fp64 accumulate, "
                   f"{dt:.2f} s wall incl. decoding B",
     }
 
+
+# ---------------------------------------------------------------- profile summaries
+
+def _csv_rows(run_dir: str, pattern: str):
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(run_dir, pattern), recursive=True))
+    if not files:
+        raise FileNotFoundError(f"no {pattern} under {run_dir}")
+    out = []
+    for f in files:
+        with open(f) as fh:
+            out += list(csv.DictReader(fh))
+    return out
+
+
+def _dispatches(run_dir: str, csv_pattern: str, counters: bool):
+    """The library's dispatches of one rocprofv3 run (kernel names in namespace
+    tg::) in dispatch order, each paired with the label its run's dispatch
+    log gives the same position: [(label, {"name", "dur_us", counters...})]."""
+    recs = {}
+    for r in _csv_rows(run_dir, csv_pattern):
+        name = r["Kernel_Name"]
+        if "tg::" not in name:
+            continue
+        d = recs.setdefault(int(r["Dispatch_Id"]), {"name": name})
+        d["dur_us"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        if counters:
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    with open(os.path.join(run_dir, "dispatch_log.json")) as fh:
+        labels = DispatchLog()
+        labels.entries = json.load(fh)["entries"]
+    lab = labels.expand()
+    ids = sorted(recs)
+    if len(ids) != len(lab):
+        raise ValueError(f"{run_dir}: {len(ids)} library dispatches in the trace, {len(lab)} in the dispatch log")
+    out = []
+    run_start = 0
+    for i, did in enumerate(ids):
+        label = lab[i]
+        if i == 0 or lab[i - 1] != label:
+            run_start = i
+        if label.endswith(" unfused"):   # the product, then one elementwise pass per epilogue step
+            parts = ["product", "bias pass", "GELU pass"][:3 if "gelu" in label else 2]
+            label = f"{label} {parts[(i - run_start) % len(parts)]}"
+        out.append((label, recs[did]))
+    return out
+
+
+def _group(disp):
+    g = {}
+    for lab, rec in disp:
+        g.setdefault(lab, []).append(rec)
+    return g
+
+
+def _mean(v):
+    return sum(v) / len(v) if v else float("nan")
+
+
+def _bench_json(path: str):
+    with open(path) as fh:
+        lines = [ln for ln in fh.read().splitlines() if ln.startswith("{")]
+    return json.loads(lines[-1]) if lines else {}
+
+
+def _alg(label: str, I, tg):
+    """(flops, algorithmic bytes) of one bench line's launch, or (None, None)."""
+    base = label.split(" ")[0]
+    if base.startswith("attention"):
+        wa = I.ATTN_WORKLOAD
+        B, H, S, D = wa["batch"], wa["heads"], wa["seq"], wa["head_dim"]
+        return attention_flops(B, H, D, S, S, "non-causal" not in label), 4 * B * H * S * D * 2
+    if base == I.W4_WORKLOAD["name"]:
+        wq = I.W4_WORKLOAD
+        M, N, K, G = wq["M"], wq["N"], wq["K"], wq["group"]
+        return gemm_flops(M, N, K), tg.tg_w4_packed_bytes(K, N) + 2 * (K // G) * N + 2 * M * K + 2 * M * N
+    if base.startswith("gemm_f16_rows_"):
+        M, N, K = (int(v) for v in base[len("gemm_f16_rows_"):].split("x"))
+        return gemm_flops(M, N, K), gemm_alg_bytes(M, N, K)
+    w = I.WORKLOADS.get(base) or I.TILE_WORKLOADS.get(base)
+    if w is None:
+        return None, None
+    if label.endswith(("bias pass", "GELU pass")):
+        return None, 4 * w.M * w.N
+    epi = w.epilogue != I.EPI_NONE and "no epilogue" not in label and "product" not in label
+    return gemm_flops(w.M, w.N, w.K), gemm_alg_bytes(w.M, w.N, w.K, bias=epi)
+
+
+MFMA_COUNTERS = ["SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES",
+                 "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE"]
+PROFILE_COMMANDS = {
+    "bench": "python3 bench.py > <out>/bench.json",
+    "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d <out>/trace -o run -- "
+             "python3 bench.py --no-cpu-baseline --dispatch-log <out>/trace/dispatch_log.json "
+             "> <out>/trace/bench.json",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/fetch -o run -- "
+             "python3 bench.py --profile-run --dispatch-log <out>/fetch/dispatch_log.json",
+    "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/write -o run -- "
+             "python3 bench.py --profile-run --dispatch-log <out>/write/dispatch_log.json",
+    "copy_fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/copy_fetch -o run -- "
+                  "python3 bench.py --copy-calibration 1024",
+    "copy_write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/copy_write -o run -- "
+                  "python3 bench.py --copy-calibration 1024",
+    "mfma": "rocprofv3 --pmc " + " ".join(MFMA_COUNTERS) + " --output-format csv -d <out>/mfma -o run -- "
+            "python3 bench.py --profile-run --dispatch-log <out>/mfma/dispatch_log.json",
+    "summarise": "python3 bench.py --summarise <out>",
+}
+
+
+def summarise_profiles(run_dir: str, out_dir: str) -> None:
+    """Writes profiles/{kernel_trace,hbm_traffic,counters_mfma_lds}.md and
+    profiles/counters.json from the rocprofv3 runs under run_dir (the
+    commands in PROFILE_COMMANDS, each in the subdirectory of its name).
+
+    HBM traffic: FETCH_SIZE and WRITE_SIZE (KiB per dispatch, each from a
+    run of its own) are scaled by what the same counter reads for a 1 GiB
+    device copy.  Shader clock: GRBM_GUI_ACTIVE counts busy cycles of each of
+    the 8 XCDs' graphics engines and rocprofv3 sums the 8, so the clock is
+    GRBM_GUI_ACTIVE / 8 / the dispatch's duration.  MFMA utilisation:
+    SQ_VALU_MFMA_BUSY_CYCLES (summed over the 1024 SIMDs) / (1024 x
+    GRBM_GUI_ACTIVE / 8), the fraction of SIMD cycles at that clock in which
+    the matrix core was busy; SQ_INSTS_VALU_MFMA_MOPS_* x 512 cross-checks
+    the flops.  Counter runs serialise dispatches, so their clock is that of
+    the counter run, not of the timed bench."""
+    import statistics
+    import tiled_dense_gemm_tg_amd as tg
+    from tiled_dense_gemm_tg_amd import inputs as I
+    os.makedirs(out_dir, exist_ok=True)
+    khash = kernel_source_hash()
+    cmd_lines = ["```", "cd /tmp && export TMPDIR=/tmp   # rocprofv3 writes temporary files there",
+                 "cd /root/repo"] + [PROFILE_COMMANDS[k].replace("<out>", "$OUT") for k in PROFILE_COMMANDS] + ["```"]
+
+    # kernel trace
+    trace = _group(_dispatches(os.path.join(run_dir, "trace"), "**/*kernel_trace.csv", False))
+    tres = _bench_json(os.path.join(run_dir, "trace", "bench.json")) if os.path.exists(
+        os.path.join(run_dir, "trace", "bench.json")) else {}
+    bres = _bench_json(os.path.join(run_dir, "bench.json")) if os.path.exists(os.path.join(run_dir, "bench.json")) else {}
+    lines = ["# Kernel trace of the default bench (rocprofv3 --kernel-trace --stats)", "",
+             "Commands (one MI355X; `$OUT` a scratch directory; committed files only):", ""] + cmd_lines + [
+             "", f"Kernel sources: `bench.kernel_source_hash()` = `{khash}`.", "",
+             "Per-dispatch durations from the trace, grouped by the bench line each dispatch belongs to (the "
+             "dispatch log that `--dispatch-log` writes labels every library launch; warm-up and settling "
+             "dispatches included):", "",
+             "| bench line | kernel | calls | average us | median us | min us | max us |", "|---|---|---|---|---|---|---|"]
+    for lab, recs in trace.items():
+        ds = [r["dur_us"] for r in recs]
+        lines.append(f"| {lab} | `{recs[0]['name']}` | {len(ds)} | {_mean(ds):.2f} | {statistics.median(ds):.2f} | "
+                     f"{min(ds):.2f} | {max(ds):.2f} |")
+    if tres:
+        lines += ["", f"The traced run's own line: {tres.get('value')} {tres.get('unit')}, "
+                      f"{tres.get('ms_per_step', 0) * 1e3:.1f} us per launch (HIP events, back to back)."]
+    if bres:
+        lines += ["", f"The unprofiled run: {bres.get('value')} {bres.get('unit')}, "
+                      f"{bres.get('ms_per_step', 0) * 1e3:.1f} us per launch."]
+    with open(os.path.join(out_dir, "kernel_trace_bench_default.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+    # HBM traffic
+    def copy_value(sub, cname):
+        rs = _csv_rows(os.path.join(run_dir, sub), "**/*counter_collection.csv")
+        return max(float(r["Counter_Value"]) for r in rs if r["Counter_Name"] == cname)
+
+    fscale = 1024 * 1024 / copy_value("copy_fetch", "FETCH_SIZE")
+    wscale = 1024 * 1024 / copy_value("copy_write", "WRITE_SIZE")
+    fetch = _group(_dispatches(os.path.join(run_dir, "fetch"), "**/*counter_collection.csv", True))
+    write = _group(_dispatches(os.path.join(run_dir, "write"), "**/*counter_collection.csv", True))
+    mfma = _group(_dispatches(os.path.join(run_dir, "mfma"), "**/*counter_collection.csv", True))
+    record = {"_about": summarise_profiles.__doc__.split("\n\n", 1)[1].strip(), "kernel_hash": khash,
+              "fetch_scale": round(fscale, 5), "write_scale": round(wscale, 5), "lines": {}}
+    h = ["# HBM traffic per launch (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)", "",
+         "Commands:", ""] + cmd_lines + [
+         "", f"Calibration: a 1 GiB device copy reads FETCH_SIZE x {fscale:.4f} and WRITE_SIZE x {wscale:.4f} "
+             "KiB per GiB moved, so fetched bytes = FETCH_SIZE x 1024 x that factor (written likewise).", "",
+         "| bench line | fetched MB | written MB | total MB | algorithmic MB | total / algorithmic |",
+         "|---|---|---|---|---|---|"]
+    m = ["# MFMA utilisation, shader clock and LDS counters (rocprofv3 --pmc)", "",
+         "Commands:", ""] + cmd_lines + [
+         "", "Derivations (per dispatch, then the mean over the bench line's dispatches):",
+         "* clock = GRBM_GUI_ACTIVE / 8 XCDs / dispatch duration (rocprofv3 sums the 8 XCDs' counters);",
+         "* MFMA utilisation = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8);",
+         "* MFMA flops = (SQ_INSTS_VALU_MFMA_MOPS_F16 + _BF16) x 512, against 2MNK.",
+         "Counter runs serialise the dispatches, so the clock is the counter run's, not the timed bench's.", "",
+         "| bench line | duration us | clock GHz | MFMA util | MFMA flops / 2MNK | LDS instr | LDS bank conflicts |",
+         "|---|---|---|---|---|---|---|"]
+    for lab in fetch:
+        if lab.startswith(("w4 weight packing", "sweep")):
+            continue
+        fb = _mean([r["FETCH_SIZE"] for r in fetch[lab]]) * 1024 * fscale
+        wb = _mean([r["WRITE_SIZE"] for r in write.get(lab, [])]) * 1024 * wscale if lab in write else float("nan")
+        flops, ab = _alg(lab, I, tg)
+        rec = {"kernel": fetch[lab][0]["name"], "kernel_hash": khash, "bytes_per_launch": int(fb + wb),
+               "fetched_bytes": int(fb), "written_bytes": int(wb), "algorithmic_bytes": ab}
+        h.append(f"| {lab} | {fb / 1e6:.1f} | {wb / 1e6:.1f} | {(fb + wb) / 1e6:.1f} | "
+                 f"{ab / 1e6 if ab else float('nan'):.1f} | {(fb + wb) / ab if ab else float('nan'):.2f} |")
+        if lab in mfma:
+            rs = mfma[lab]
+            clk = [r["GRBM_GUI_ACTIVE"] / 8 / (r["dur_us"] * 1e3) for r in rs]
+            util = [r["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * r["GRBM_GUI_ACTIVE"] / 8) for r in rs]
+            mops = _mean([r["SQ_INSTS_VALU_MFMA_MOPS_F16"] + r["SQ_INSTS_VALU_MFMA_MOPS_BF16"] for r in rs]) * 512
+            rec.update({"sclk_ghz": round(_mean(clk), 3), "mfma_util": round(_mean(util), 4),
+                        "counter_run_us": round(_mean([r["dur_us"] for r in rs]), 2),
+                        "mfma_flops": mops, "lds_instructions": _mean([r["SQ_INSTS_LDS"] for r in rs]),
+                        "lds_bank_conflicts": _mean([r["SQ_LDS_BANK_CONFLICT"] for r in rs])})
+            m.append(f"| {lab} | {rec['counter_run_us']:.1f} | {rec['sclk_ghz']:.3f} | {rec['mfma_util']:.3f} | "
+                     f"{mops / flops if flops else float('nan'):.3f} | {rec['lds_instructions']:.0f} | "
+                     f"{rec['lds_bank_conflicts']:.0f} |")
+        record["lines"][lab] = rec
+    with open(os.path.join(out_dir, "hbm_traffic.md"), "w") as fh:
+        fh.write("\n".join(h) + "\n")
+    with open(os.path.join(out_dir, "counters_mfma_lds.md"), "w") as fh:
+        fh.write("\n".join(m) + "\n")
+    with open(os.path.join(out_dir, "counters.json"), "w") as fh:
+        json.dump(record, fh, indent=1)
+        fh.write("\n")
+
+
+# ---------------------------------------------------------------- main
 
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -433,11 +766,25 @@ def main() -> int:
                     help="only time every tile configuration of the tiled family (prints its own JSON line)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run torch's device copy of MIB MiB, 10 times (to scale HBM byte counters)")
+    ap.add_argument("--dispatch-log", default=None, metavar="FILE",
+                    help="write the label of every library kernel launch, in order, to FILE (JSON)")
+    ap.add_argument("--profile-run", action="store_true",
+                    help="no settling, short lines: for rocprofv3 counter runs")
+    ap.add_argument("--summarise", default=None, metavar="DIR",
+                    help="only summarise the rocprofv3 runs under DIR into profiles/")
     args = ap.parse_args()
+    if args.summarise:
+        summarise_profiles(args.summarise, os.path.join(ROOT, "profiles"))
+        return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this GEMM runs on a single "
               "MI355X and has no multi-GPU path.", file=sys.stderr)
         return 2
+    if args.profile_run:
+        Timing.settle_s = 0.0
+        Timing.short = True
+        args.steps, args.warmup = 3, 1
+        args.no_cpu_baseline = True
 
     import torch
     import tiled_dense_gemm_tg_amd as tg
@@ -466,14 +813,14 @@ def main() -> int:
     w = I.WORKLOADS[args.workload]
     log(f"main workload {w.name}: generating inputs")
     ops, sets = device_operands(torch, I, w)
-    ms, wall = time_gemm(torch, tg, w, sets, args.steps, args.warmup, settle_s=0.0)
+    ms, wall = time_gemm(torch, tg, w, sets, args.steps, args.warmup)
     flops = gemm_flops(w.M, w.N, w.K)
     tflops = flops / (ms * 1e-3) / 1e12
     log(f"{w.name}: {ms * 1e3:.1f} us/launch, {tflops:.1f} TFLOP/s")
     path_name = {I.EPI_NONE: "none", I.EPI_BIAS: "bias", I.EPI_BIAS_GELU_TANH: "bias + GELU(tanh)"}[w.epilogue]
     st, path = tg.tg_gemm_plan(w.M, w.N, w.K, w.dtype, *[sets[0][i].data_ptr() if sets[0][i] is not None else None
                                                         for i in (0, 1, 2)], w.epilogue, sets[0][3].data_ptr())
-
+    cnt = measured(w.name) or {}
     result = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -496,7 +843,13 @@ def main() -> int:
             "peak": PEAK_MFMA_F16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(tflops / PEAK_MFMA_F16_TFLOPS, 4),
-            "traffic": measured_traffic(w.name),
+            "traffic": cnt.get("bytes_per_launch"),
+            "mfma_util": cnt.get("mfma_util"),
+            "sclk_ghz": cnt.get("sclk_ghz"),
+            "counters": ("profiles/counters.json: rocprofv3 --pmc runs of this script on the current kernel "
+                         "sources; clock = GRBM_GUI_ACTIVE / 8 XCDs / dispatch time, MFMA util = "
+                         "SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x that cycle count), both in the counter run")
+            if cnt else None,
             "algorithmic_flops_per_launch": flops,
             "algorithmic_bytes_per_launch": gemm_alg_bytes(w.M, w.N, w.K, bias=w.epilogue != I.EPI_NONE),
             "timed_region_wall_s": round(wall, 4),
@@ -504,11 +857,9 @@ def main() -> int:
     }
     fusion = {}
     if not args.no_secondary and w.epilogue != I.EPI_NONE:
-        log(f"{w.name}: unfused (product, bias pass, GELU pass)")
-        msu, _ = time_gemm(torch, tg, w, sets, max(args.steps // 2, 20), args.warmup, unfused=True)
-        fusion[w.name] = {"fused_us": round(ms * 1e3, 2), "unfused_us": round(msu * 1e3, 2),
-                          "fusion_speedup": round(msu / ms, 3),
-                          "unfused_extra_bytes": EPILOGUE_PASSES[w.epilogue] * 4 * w.M * w.N}
+        log(f"{w.name}: fused, unfused (product, bias pass, GELU pass) and no epilogue, alternating")
+        fusion[w.name] = fusion_comparison(torch, tg, w, sets, steps_for(10), args.warmup)
+        log(f"{w.name}: {fusion[w.name]}")
     del sets
     torch.cuda.empty_cache()
 
@@ -517,18 +868,21 @@ def main() -> int:
         w2 = I.WORKLOADS[SQUARE]
         log(f"secondary {w2.name}")
         _, sets2 = device_operands(torch, I, w2)
-        ms2, _ = time_gemm(torch, tg, w2, sets2, max(args.steps, 50), args.warmup)
+        ms2, _ = time_gemm(torch, tg, w2, sets2, steps_for(max(args.steps, 50)), args.warmup)
         t2 = gemm_flops(w2.M, w2.N, w2.K) / (ms2 * 1e-3) / 1e12
+        c2 = measured(w2.name) or {}
         sec[w2.name] = {"us_per_launch": round(ms2 * 1e3, 2), "TFLOP/s": round(t2, 2),
                         "frac_mfma_peak": round(t2 / PEAK_MFMA_F16_TFLOPS, 4), "path": path_of(tg, w2, sets2[0]),
-                        "traffic": measured_traffic(w2.name)}
+                        "traffic": c2.get("bytes_per_launch"), "mfma_util": c2.get("mfma_util"),
+                        "sclk_ghz": c2.get("sclk_ghz")}
         del sets2
         torch.cuda.empty_cache()
         w4 = I.WORKLOADS[SKINNY]
         log(f"secondary {w4.name} (8 rotating operand sets)")
         _, sets4 = device_operands(torch, I, w4, copies=8)
-        ms4, _ = time_gemm(torch, tg, w4, sets4, max(args.steps, 400), args.warmup)
-        hot, _ = time_gemm(torch, tg, w4, sets4[:1], max(args.steps, 400), args.warmup)
+        ms4, _ = time_gemm(torch, tg, w4, sets4, steps_for(max(args.steps, 400)), args.warmup)
+        hot, _ = time_gemm(torch, tg, w4, sets4[:1], steps_for(max(args.steps, 400)), args.warmup,
+                           label=f"{w4.name} hot")
         nbytes = gemm_alg_bytes(w4.M, w4.N, w4.K)
         gbps = nbytes / (ms4 * 1e-3) / 1e9
         sec[w4.name] = {"us_per_launch": round(ms4 * 1e3, 3), "GB/s": round(gbps, 1),
@@ -540,10 +894,10 @@ def main() -> int:
         del sets4
         torch.cuda.empty_cache()
         log("secondary: 32, 48 and 64 rows at the decode width (8 rotating weight sets)")
-        sec.update(bench_rows(torch, tg, I, max(args.steps, 400), args.warmup))
+        sec.update(bench_rows(torch, tg, I, steps_for(max(args.steps, 400)), args.warmup))
         torch.cuda.empty_cache()
         log("secondary: weight-only 4-bit product at the same shape (16 rotating weight sets)")
-        wname, msq, hotq, qbytes = bench_w4(torch, tg, I, max(args.steps, 400), args.warmup)
+        wname, msq, hotq, qbytes = bench_w4(torch, tg, I, steps_for(max(args.steps, 400)), args.warmup)
         qgbps = qbytes / (msq * 1e-3) / 1e9
         sec[wname] = {"us_per_launch": round(msq * 1e3, 3), "GB/s": round(qgbps, 1),
                       "frac_hbm_peak": round(qgbps / PEAK_HBM_GBPS, 4),
@@ -555,22 +909,21 @@ def main() -> int:
         w3 = I.WORKLOADS[RAGGED]
         log(f"secondary {w3.name}")
         _, sets3 = device_operands(torch, I, w3)
-        ms3, _ = time_gemm(torch, tg, w3, sets3, max(args.steps // 2, 20), args.warmup)
+        ms3, _ = time_gemm(torch, tg, w3, sets3, steps_for(max(args.steps, 50)), args.warmup)
         t3 = gemm_flops(w3.M, w3.N, w3.K) / (ms3 * 1e-3) / 1e12
+        c3 = measured(w3.name) or {}
         sec[w3.name] = {"us_per_launch": round(ms3 * 1e3, 2), "TFLOP/s": round(t3, 2),
                         "frac_mfma_peak": round(t3 / PEAK_MFMA_F16_TFLOPS, 4), "path": path_of(tg, w3, sets3[0]),
-                        "traffic": measured_traffic(w3.name)}
-        log(f"{w3.name}: unfused")
-        ms3u, _ = time_gemm(torch, tg, w3, sets3, max(args.steps // 2, 20), args.warmup, unfused=True)
-        fusion[w3.name] = {"fused_us": round(ms3 * 1e3, 2), "unfused_us": round(ms3u * 1e3, 2),
-                           "fusion_speedup": round(ms3u / ms3, 3),
-                           "unfused_extra_bytes": EPILOGUE_PASSES[w3.epilogue] * 4 * w3.M * w3.N}
+                        "traffic": c3.get("bytes_per_launch"), "mfma_util": c3.get("mfma_util"),
+                        "sclk_ghz": c3.get("sclk_ghz")}
+        log(f"{w3.name}: {ms3 * 1e3:.1f} us; fused, unfused and no epilogue, alternating")
+        fusion[w3.name] = fusion_comparison(torch, tg, w3, sets3, steps_for(50), args.warmup)
         del sets3
         torch.cuda.empty_cache()
         log("secondary: tile configurations on the mid-size shape classes")
-        sec["tile_choice"] = bench_tile_choice(torch, tg, I, max(args.steps // 2, 20), args.warmup)
+        sec["tile_choice"] = bench_tile_choice(torch, tg, I, steps_for(max(args.steps // 2, 20)), args.warmup)
         log("secondary: attention forward (FlashAttention benchmark shape)")
-        aname, ares = bench_attention(torch, tg, I, max(args.steps // 2, 20), args.warmup)
+        aname, ares = bench_attention(torch, tg, I, steps_for(max(args.steps // 2, 20)), args.warmup)
         sec[aname] = ares
         sec["epilogue_fusion"] = fusion
         result["secondary"] = sec
@@ -579,6 +932,10 @@ def main() -> int:
         log("cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(I, w, ops, args.cpu_budget)
 
+    if args.dispatch_log:
+        os.makedirs(os.path.dirname(os.path.abspath(args.dispatch_log)), exist_ok=True)
+        with open(args.dispatch_log, "w") as fh:
+            json.dump({"argv": sys.argv[1:], "entries": LOG.entries}, fh)
     print(json.dumps(result), flush=True)
     return 0
 

@@ -56,21 +56,50 @@ def test_workload_accounting_matches_the_stated_figures():
     assert bench.gemm_alg_bytes(16, 11008, 4096) == 90_660_864
 
 
-def test_traffic_hash_covers_every_kernel_source():
-    # The measured HBM traffic in profiles/traffic.json is reported only while
-    # the hash of the kernel sources matches; every file the library is built
-    # from must be part of that hash, or a change to it would leave stale
-    # figures in the bench line.
+def test_counter_hash_covers_every_kernel_source():
+    # The measured HBM traffic, MFMA utilisation and clock in
+    # profiles/counters.json are reported only while the hash of the kernel
+    # sources matches; every file the library is built from must be part of
+    # that hash, or a change to it would leave stale figures in the bench line.
     csrc = os.path.join(os.path.dirname(bench.__file__), "tiled_dense_gemm_tg_amd", "csrc")
     sources = sorted(f for f in os.listdir(csrc) if f.endswith((".hip", ".h")))
     assert sorted(bench.KERNEL_SOURCES) == sources
 
 
-def test_committed_traffic_matches_the_kernel_sources():
-    # Every workload in the committed traffic file was measured on the
-    # current sources (re-profile after any kernel change).
-    with open(bench.TRAFFIC_FILE) as fh:
-        rec = json.load(fh)
-    h = bench.kernel_source_hash()
-    stale = [k for k, v in rec.items() if isinstance(v, dict) and v.get("kernel_hash") != h]
-    assert not stale, stale
+def test_stale_counters_are_not_reported(tmp_path, monkeypatch):
+    # A counter record taken on other kernel sources gives None, a current
+    # one its figures.
+    path = tmp_path / "counters.json"
+    rec = {"lines": {"w": {"kernel_hash": bench.kernel_source_hash(), "bytes_per_launch": 123, "mfma_util": 0.5},
+                     "old": {"kernel_hash": "0" * 16, "bytes_per_launch": 456}}}
+    path.write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "COUNTERS_FILE", str(path))
+    assert bench.measured_traffic("w") == 123
+    assert bench.measured("w")["mfma_util"] == 0.5
+    assert bench.measured_traffic("old") is None
+    assert bench.measured_traffic("missing") is None
+
+
+def test_dispatch_log_labels_the_unfused_passes(tmp_path):
+    # The summariser pairs the library's dispatches of a rocprofv3 run with
+    # the bench's dispatch log, position by position, and names the three
+    # launches of an unfused call after their roles.
+    run = tmp_path / "run"
+    run.mkdir()
+    log = bench.DispatchLog()
+    log.note("main", 2)
+    log.note("main unfused_gelu unfused", 6)
+    log.note("main")
+    (run / "dispatch_log.json").write_text(json.dumps({"entries": log.entries}))
+    hdr = "Dispatch_Id,Kernel_Name,Start_Timestamp,End_Timestamp\n"
+    rows = [f"{i + 1},tg::k{i},{1000 * i},{1000 * i + 500}" for i in range(9)]
+    rows.insert(3, "99,torch_kernel,0,1")   # not a library kernel: skipped
+    (run / "run_kernel_trace.csv").write_text(hdr + "\n".join(rows) + "\n")
+    got = bench._dispatches(str(run), "*kernel_trace.csv", False)
+    labels = [lab for lab, _ in got]
+    assert labels == ["main", "main",
+                      "main unfused_gelu unfused product", "main unfused_gelu unfused bias pass",
+                      "main unfused_gelu unfused GELU pass"] * 1 + [
+                      "main unfused_gelu unfused product", "main unfused_gelu unfused bias pass",
+                      "main unfused_gelu unfused GELU pass", "main"]
+    assert all(rec["dur_us"] == 0.5 for _, rec in got)

@@ -36,6 +36,7 @@
 //     workgroups stop at their last visible block, and the query blocks with
 //     the most keys, over all heads, are dispatched first.
 #include "tg_device.h"
+#include "tg_direct.h"
 #include "tg_launch.h"
 
 #include <type_traits>
@@ -57,29 +58,10 @@ constexpr uint32_t SHIFT = 4096;          // buffers start 4 KiB before K and V
 constexpr uint32_t OOB_BUMP = 0x80000000u;
 constexpr float RESCALE_LOG2 = 8.0f;
 
-typedef int i32x4 __attribute__((ext_vector_type(4)));
+using namespace direct;
+
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
-__device__ __forceinline__ uint32_t lds_address(const void *p) {
-    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p;
-}
-
-__device__ __forceinline__ i32x4 rsrc_words(const void *base, uint32_t bytes) {
-    const uint64_t p = reinterpret_cast<uint64_t>(base);
-    return i32x4{(int)(uint32_t)p, (int)(uint32_t)(p >> 32), (int)bytes, 0x00020000};
-}
-
-template <int OFF>
-__device__ __forceinline__ void dma16(const i32x4 &rsrc, uint32_t voffset, uint32_t m0) {
-    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen offset:%3 lds" ::"v"(voffset), "s"(rsrc), "{m0}"(m0),
-                 "i"(OFF));
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
 
 // K rows are 256 bytes = 16 chunks; the fragment read takes one chunk of 32
 // consecutive rows, so the chunk index is XOR-ed with row % 16.

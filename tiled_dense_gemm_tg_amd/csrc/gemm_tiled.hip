@@ -40,10 +40,8 @@
 //   * persistent grid with an XCD-aware grouped raster of the tiles
 //     (tg_tile.h); the smaller tiles fit two workgroups per CU.
 //
-// The direct loads are issued from inline assembly and their completion is
-// awaited with explicit vmcnt waits: the compiler cannot tell that the LDS
-// they write is not the LDS being read, and would otherwise wait for every
-// load in flight before each use of LDS data.
+// The direct loads (tg_direct.h) are issued from inline assembly and their
+// completion is awaited with explicit vmcnt waits.
 //
 // Rows need not be 16-byte aligned: the direct loads take 2-byte-aligned
 // addresses, and the few chunks that then hold wrong data in the last
@@ -53,6 +51,7 @@
 // an out-of-range lane writes zeros.  k >= K is pushed out of range (offset +
 // 2^31) in both A and B, so the K tail is zero on both sides; rows m >= M and
 // columns n >= N are never stored, so what they load does not matter.
+#include "tg_direct.h"
 #include "tg_tile.h"
 
 #include <type_traits>
@@ -62,11 +61,11 @@ namespace tg {
 namespace {
 
 using tile::NTHREADS;
+using namespace direct;
 constexpr int BK = 32;
 constexpr int STAGES = 4;
 constexpr uint32_t OOB_BUMP = 0x80000000u;        // + offset < 2^31 - 64 KiB -> beyond the operand's buffer
 
-typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
@@ -119,37 +118,6 @@ __device__ __forceinline__ uint32_t c_swz(int row) {
         return (uint32_t)(row & 31);
     else
         return (uint32_t)((row ^ (row >> 4)) & 15);
-}
-
-__device__ __forceinline__ uint32_t lds_address(const void *p) {
-    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p;
-}
-
-// Buffer resource words for the inline-asm load: base, stride 0, byte range,
-// word 3 of the gfx9 family (32-bit data format).
-__device__ __forceinline__ i32x4 rsrc_words(const void *base, uint32_t bytes) {
-    const uint64_t p = reinterpret_cast<uint64_t>(base);
-    return i32x4{(int)(uint32_t)p, (int)(uint32_t)(p >> 32), (int)bytes, 0x00020000};
-}
-
-// One 16-byte-per-lane buffer load into LDS: lane L reads 16 bytes at byte
-// offset voffset + OFF of the buffer and writes them to LDS at m0 + OFF + 16 L
-// (the instruction offset moves both addresses).  Loads that share m0 keep
-// the wave from rewriting m0 between them, which stalls until the previous
-// direct load has taken its value.
-template <int OFF>
-__device__ __forceinline__ void dma16(const i32x4 &rsrc, uint32_t voffset, uint32_t m0) {
-    static_assert(OFF >= 0 && OFF < 4096, "12-bit instruction offset");
-    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen offset:%3 lds" ::"v"(voffset), "s"(rsrc), "{m0}"(m0),
-                 "i"(OFF));
-}
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
-// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
 // Per-lane addressing of the D direct loads that fill one stage.  Wave w,

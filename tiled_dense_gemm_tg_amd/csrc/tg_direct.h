@@ -1,10 +1,14 @@
-// tg_direct.h -- direct-to-LDS buffer loads for the M <= 16 kernels (gfx950).
+// tg_direct.h -- direct-to-LDS buffer loads (gfx950), shared by every kernel
+// that stages operands with them: the tiled GEMM, the M <= 16 kernels and the
+// attention forward.
 //
 // A buffer load with the lds modifier writes each lane's 16 bytes straight
 // into LDS (at m0 + instruction offset + 16 * lane) without passing through
 // registers.  The loads are written as inline assembly, so the compiler does
 // not count them: whoever reads the LDS they fill waits for them with
-// wait_vmcnt first.
+// wait_vmcnt first (the compiler cannot tell that the LDS they write is not
+// the LDS being read, and would otherwise wait for every load in flight
+// before each use of LDS data).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -15,19 +19,27 @@ namespace direct {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
+// Buffer resource words for the inline-asm load: base, stride 0, byte range,
+// word 3 of the gfx9 family (32-bit data format).  Loads beyond the range
+// write zeros to LDS.
 __device__ __forceinline__ i32x4 rsrc_words(const void *base, uint32_t bytes) {
     const uint64_t a = reinterpret_cast<uint64_t>(base);
     return i32x4{(int)(uint32_t)a, (int)(uint32_t)(a >> 32), (int)bytes, 0x00020000};
 }
 
+// The 32-bit LDS byte address of a __shared__ object.
 __device__ __forceinline__ uint32_t lds_address(const void *q) {
     return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)q;
 }
 
 // One 16-byte-per-lane buffer load into LDS: lane L reads 16 bytes at byte
-// offset voffset + OFF of the buffer and writes them to LDS at m0 + OFF + 16 L.
+// offset voffset + OFF of the buffer and writes them to LDS at m0 + OFF + 16 L
+// (the instruction offset moves both addresses).  Loads that share m0 keep
+// the wave from rewriting m0 between them, which stalls until the previous
+// direct load has taken its value.
 template <int OFF>
 __device__ __forceinline__ void dma16(const i32x4 &rsrc, uint32_t voffset, uint32_t m0) {
+    static_assert(OFF >= 0 && OFF < 4096, "12-bit instruction offset");
     asm volatile("buffer_load_dwordx4 %0, %1, 0 offen offset:%3 lds" ::"v"(voffset), "s"(rsrc), "{m0}"(m0),
                  "i"(OFF));
 }
@@ -43,9 +55,8 @@ __device__ __forceinline__ void dma16_rq(int rq, const i32x4 &rsrc, uint32_t vof
     }
 }
 
-// s_waitcnt with only the vector-memory counter constrained (vmcnt[3:0] |
-// expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14).  The direct loads come
-// from inline assembly, so the compiler does not wait for them by itself.
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
