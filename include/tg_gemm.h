@@ -239,6 +239,34 @@ tg_status tg_gemm_split_plan(int64_t M, int64_t N, int64_t K, int num_cu, int *s
                              int64_t *workspace_bytes_out);
 
 /*
+ * Split-K of the skinny family without any workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): tg_gemm_split with the
+ * workspace taken from a static device array inside the library,
+ * TG_SCRATCH_BYTES bytes per GPU, held until the process ends.  The library
+ * allocates and frees nothing in this call.
+ *   splits   as for tg_gemm_split (0: tg_gemm_split_plan's choice; 1: no
+ *            split; at most 64).  Shapes that do not take the skinny path,
+ *            M > 16, and a resolved count of 1 run exactly as tg_gemm.
+ * Limits: ceil(N / 64) x splits at most 1024 (the partial blocks, 4 KiB
+ * each) and ceil(N / 64) at most 16384 (the counters), else
+ * TG_ERR_UNSUPPORTED; splits outside 0..64 is TG_ERR_INVALID_ARG; the other
+ * rules and results are those of tg_gemm_split with the same splits
+ * (bit-identical to it).
+ * The array is shared by every call on one GPU: calls that may overlap on
+ * one GPU (other streams, other threads) race and must not be made; calls
+ * on one stream are ordered and safe.  The first call on a device looks the
+ * array up (switching the current device for that moment) and enqueues a
+ * kernel that zeroes its counters; make it outside graph capture.  Every
+ * completed call leaves the counters zero again.
+ */
+#define TG_SCRATCH_BYTES (4259840)   /* 64 KiB of counters + 4 MiB of partial blocks */
+
+tg_status tg_gemm_split_static(int splits, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
+                               const void *A, const void *B, const void *bias, tg_epilogue epilogue,
+                               void *C, void *stream);
+
+/*
  * Elementwise epilogue steps as passes of their own over a matrix in device
  * memory -- the unfused form of the epilogue that the fourth TileLang page
  * ("Designing high-performance GPU kernels with TileLang", part 3 "Epilogue

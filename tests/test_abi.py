@@ -387,3 +387,20 @@ def test_split_plan_on_an_mi355x(lib, M, N, K, splits):
     assert (st, got) == (tg.TG_OK, splits)
     assert tg.tg_gemm_split_plan(M, N, K, 0)[1] == splits              # 0: 256 CUs assumed
     assert nbytes == tg.tg_gemm_split_workspace_bytes(N, splits)
+
+
+def test_static_split_checks_arguments_before_any_device_work(lib):
+    # Invalid split counts and scratch overflows are refused on the host,
+    # before the first HIP call, like every other argument error.
+    args = (16, 4096, 4096, I.F16, PA, PB, None, I.EPI_NONE, PC, None)
+    assert lib.tg_gemm_split_static(-1, *args) == tg.TG_ERR_INVALID_ARG
+    assert lib.tg_gemm_split_static(65, *args) == tg.TG_ERR_INVALID_ARG
+    # 64 slabs x 32 splits = 2048 partial blocks of 4 KiB: above the 4 MiB scratch
+    assert lib.tg_gemm_split_static(32, *args) == tg.TG_ERR_UNSUPPORTED
+    # more than 16384 slabs: more counters than the scratch holds
+    wide = (16, 16384 * 64 + 64, 4096, I.F16, PA, PB, None, I.EPI_NONE, PC, None)
+    assert lib.tg_gemm_split_static(2, *wide) == tg.TG_ERR_UNSUPPORTED
+    # the tg_gemm rules come first
+    assert lib.tg_gemm_split_static(4, -1, 4096, 4096, I.F16, PA, PB, None, I.EPI_NONE, PC, None) == \
+        tg.TG_ERR_INVALID_ARG
+    assert lib.tg_gemm_split_static(4, 16, 0, 4096, I.F16, PA, PB, None, I.EPI_NONE, PC, None) == tg.TG_OK

@@ -44,7 +44,7 @@ TILES_NAMES = {TG_TILES_AUTO: "auto", TG_TILES_256x256: "256x256", TG_TILES_256x
                TG_TILES_128x256: "128x256", TG_TILES_128x128: "128x128"}
 
 EXPORTED = ("tg_gemm", "tg_gemm_path", "tg_gemm_plan", "tg_gemm_tiled", "tg_gemm_tiles_plan", "tg_gemm_split",
-            "tg_gemm_split_workspace_bytes", "tg_gemm_split_plan", "tg_elementwise", "tg_gemm_unfused",
+            "tg_gemm_split_workspace_bytes", "tg_gemm_split_plan", "tg_gemm_split_static", "tg_elementwise", "tg_gemm_unfused",
             "tg_w4_packed_bytes", "tg_w4_pack", "tg_gemm_w4", "tg_gemm_w4_split", "tg_gemm_w4_split_workspace_bytes",
             "tg_gemm_w4_split_plan", "tg_attention_fwd", "tg_status_string", "tg_version")
 
@@ -83,6 +83,8 @@ def load_library():
     lib.tg_gemm_tiles_plan.restype = ci
     lib.tg_gemm_split.argtypes = [ci, i64, i64, i64, ci, vp, vp, vp, ci, vp, vp, i64, vp]
     lib.tg_gemm_split.restype = ci
+    lib.tg_gemm_split_static.argtypes = [ci, i64, i64, i64, ci, vp, vp, vp, ci, vp, vp]
+    lib.tg_gemm_split_static.restype = ci
     lib.tg_gemm_split_workspace_bytes.argtypes = [i64, ci]
     lib.tg_gemm_split_workspace_bytes.restype = i64
     lib.tg_gemm_split_plan.argtypes = [i64, i64, i64, ci, ctypes.POINTER(ci), ctypes.POINTER(i64)]
@@ -143,6 +145,11 @@ def tg_gemm_tiles_plan(M, N, K, num_cu=0):
 def tg_gemm_split(splits, M, N, K, dtype, A, B, bias, epilogue, C, workspace, workspace_bytes, stream) -> int:
     return load_library().tg_gemm_split(splits, M, N, K, dtype, A, B, bias, epilogue, C, workspace,
                                         workspace_bytes, stream)
+
+
+def tg_gemm_split_static(splits, M, N, K, dtype, A, B, bias, epilogue, C, stream) -> int:
+    """tg_gemm_split with the library's static workspace (no allocation)."""
+    return load_library().tg_gemm_split_static(splits, M, N, K, dtype, A, B, bias, epilogue, C, stream)
 
 
 def tg_gemm_split_workspace_bytes(N, splits) -> int:

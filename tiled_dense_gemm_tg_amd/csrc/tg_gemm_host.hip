@@ -10,6 +10,7 @@
 
 #include <atomic>
 #include <math.h>
+#include <mutex>
 #include <stdint.h>
 
 #define TG_EXPORT extern "C" __attribute__((visibility("default")))
@@ -313,6 +314,107 @@ TG_EXPORT tg_status tg_gemm_split(int splits, int64_t M, int64_t N, int64_t K, t
         return TG_ERR_INVALID_ARG;
     return run_gemm(TG_PATH_AUTO, TG_TILES_AUTO, M, N, K, dtype, A, B, bias, epilogue, C, stream, splits, workspace,
                     workspace_bytes);
+}
+
+namespace {
+
+// Allocation-free split-K (tg_gemm_split_static): the workspace is a static
+// device array, one copy per GPU, which the library holds until the process
+// ends.  Its first kScratchCounterBytes hold the per-slab arrival counters,
+// always at the same place, so that no call's partial sums ever land where
+// another call expects zero counters; the partial blocks follow.  In host
+// code `scratch` only names the host-side stand-in of the symbol: the device
+// address of each GPU's copy comes from hipGetSymbolAddress, taken once per
+// device with that device current, and only that address is used.
+constexpr int64_t kScratchCounterBytes = int64_t(64) << 10;   // 16384 slab counters
+constexpr int64_t kScratchPartialBytes = int64_t(4) << 20;    // 1024 partial blocks of 16 x 64 fp32
+constexpr int64_t kScratchBytes = kScratchCounterBytes + kScratchPartialBytes;
+static_assert(kScratchBytes == TG_SCRATCH_BYTES, "tg_gemm.h states the scratch size");
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+__global__ void zero_words_kernel(uint32_t *p, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n)
+        p[i] = 0u;
+}
+
+std::mutex g_scratch_mutex;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+
+// The device address of `scratch` on the device of `stream`, set up on the
+// first call for that device: symbol lookup with the device current, then a
+// fill kernel on `stream` that zeroes the counters (every complete call
+// leaves them zero again).  nullptr if the device is unknown or the lookup
+// fails.
+void *scratch_of(hipStream_t stream) {
+    int dev = -1;
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return nullptr;
+    void *ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (ptr != nullptr)
+        return ptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (ptr != nullptr)
+        return ptr;
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess)
+        return nullptr;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess)
+        return nullptr;
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev)
+        (void)hipSetDevice(cur);
+    if (e != hipSuccess || p == nullptr)
+        return nullptr;
+    constexpr int words = static_cast<int>(kScratchCounterBytes / 4);
+    hipLaunchKernelGGL(zero_words_kernel, dim3(words / 256), dim3(256), 0, stream, static_cast<uint32_t *>(p), words);
+    if (hipGetLastError() != hipSuccess)
+        return nullptr;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+    return p;
+}
+
+}  // namespace
+
+TG_EXPORT tg_status tg_gemm_split_static(int splits, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
+                                         const void *A, const void *B, const void *bias, tg_epilogue epilogue,
+                                         void *C, void *stream) {
+    if (splits < 0 || splits > kMaxSplits)
+        return TG_ERR_INVALID_ARG;
+    const Checked c = check_args(M, N, K, dtype, A, B, bias, epilogue, C);
+    if (c.status != TG_OK || c.noop)
+        return c.status;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const tg_path path = auto_path(M, N, K, A, B, bias, C);
+    if (path != TG_PATH_SKINNY || M > 16)   // no split, no workspace: exactly tg_gemm
+        return run_gemm(TG_PATH_AUTO, TG_TILES_AUTO, M, N, K, dtype, A, B, bias, epilogue, C, stream);
+    if (splits == 0)
+        splits = auto_splits(N, K, num_cu_of(s));
+    if (splits <= 1)
+        return run_gemm(TG_PATH_AUTO, TG_TILES_AUTO, M, N, K, dtype, A, B, bias, epilogue, C, stream);
+    const int64_t slabs = (N + 63) / 64;
+    if (slabs * 4 > kScratchCounterBytes || slabs * splits * 4096 > kScratchPartialBytes)
+        return TG_ERR_UNSUPPORTED;
+    char *ws = static_cast<char *>(scratch_of(s));
+    if (ws == nullptr)
+        return TG_ERR_LAUNCH;
+    tg::GemmArgs a;
+    a.M = static_cast<int>(M);
+    a.N = static_cast<int>(N);
+    a.K = static_cast<int>(K);
+    a.A = static_cast<const uint16_t *>(A);
+    a.B = static_cast<const uint16_t *>(B);
+    a.bias = static_cast<const uint16_t *>(bias);
+    a.C = static_cast<uint16_t *>(C);
+    tg::SplitWs w;
+    w.splits = splits;
+    w.count = reinterpret_cast<uint32_t *>(ws);
+    w.part = reinterpret_cast<float *>(ws + kScratchCounterBytes);
+    const hipError_t e = tg::launch_skinny(dtype, epilogue, a, w, s);
+    return e == hipSuccess ? TG_OK : TG_ERR_LAUNCH;
 }
 
 TG_EXPORT tg_status tg_elementwise(tg_elementwise_op op, int64_t M, int64_t N, tg_dtype dtype, const void *bias,
