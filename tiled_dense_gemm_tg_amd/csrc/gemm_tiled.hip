@@ -36,7 +36,8 @@
 //     k-step are issued between the MFMAs of the current one;
 //   * the MFMA takes the B fragment first, so each lane ends up with 4
 //     consecutive output columns of a row; after the fused bias + GELU(tanh)
-//     epilogue the tile goes through LDS and leaves as row segments;
+//     epilogue each wave's block of C goes through LDS 32 rows at a time
+//     and leaves as row segments;
 //   * persistent grid with an XCD-aware grouped raster of the tiles
 //     (tg_tile.h); the smaller tiles fit two workgroups per CU.
 //
@@ -92,7 +93,6 @@ struct Cfg {
     static constexpr int MFMAS = I * J;                     // MFMAs per k-step
     static constexpr int OCCUPANCY = (STAGES * STAGE_BYTES <= 80 * 1024) ? 2 : 1;   // workgroups per CU
     static_assert(D % 2 == 0, "loads split over the two k-steps of a slice");
-    static_assert(BM * BN * 2 <= STAGES * STAGE_BYTES, "the C tile fits the stage ring");
 };
 
 // A row = 32 k = 4 chunks of 16 B.  A fragment read takes one logical chunk
@@ -108,17 +108,6 @@ __device__ __forceinline__ int a_swz(int row) { return ((row >> 1) ^ (row >> 2))
 // 1-2 and distinct bits 2-3 of the slot, so every pass hits distinct banks
 // (the 64 banks span 256 bytes, so only the chunk index mod 16 matters).
 __device__ __forceinline__ int b_swz(int k) { return ((k & 1) ? 10 : 0) ^ ((k & 2) ? 4 : 0); }
-
-// Chunk swizzle of the C tile staged in LDS for the store: the 32 rows one
-// epilogue write instruction touches land on different chunks (16-chunk
-// rows: rows r and r + 16 differ in bit 0 of the pattern).
-template <int CPR>
-__device__ __forceinline__ uint32_t c_swz(int row) {
-    if constexpr (CPR == 32)
-        return (uint32_t)(row & 31);
-    else
-        return (uint32_t)((row ^ (row >> 4)) & 15);
-}
 
 // Per-lane addressing of the D direct loads that fill one stage.  Wave w,
 // lane L:
@@ -379,23 +368,46 @@ __device__ __forceinline__ void fix_last_slice(const GemmArgs &g, int m0, int n0
     }
 }
 
-// Epilogue and store through LDS.  After the k-loop the stage ring is free
-// and holds the whole BM x BN C tile of 16-bit values (2 BN-byte rows).
-// Each lane applies the epilogue to its accumulators and writes its 4-column
-// groups to LDS (16-byte chunk index XOR c_swz(row)); then every wave copies
-// whole rows out, 16 bytes per lane, so HBM sees full row segments instead
-// of 16-byte pieces of 32 rows (which, at 2-byte-aligned row starts, split
-// across write sectors).  Chunks that cross column N go out element by
-// element.  The caller's barrier after this keeps the next tile's loads from
-// overwriting LDS before every wave has read it.
+// Epilogue and store through LDS, one wave at a time.  Each wave takes its
+// WM x WN block of C 32 rows (one accumulator row block i) at a time: the
+// lanes apply the epilogue to their accumulators and write their 4-column
+// groups (8 bytes) to the wave's own LDS buffer of 32 rows x WN 16-bit
+// values (chunk index XOR a row swizzle), then the wave reads the rows back
+// 16 bytes per lane and stores them, 2 WN contiguous bytes per row, so HBM
+// sees row segments instead of 16-byte pieces of 32 rows (which, at
+// 2-byte-aligned row starts, split across write sectors); chunks that cross
+// column N go out element by element.  The buffers lie in stages the k-loop
+// is done with in every wave -- not the stage of the last slice, which a
+// slower wave may still be reading -- so no barrier is needed, and LDS
+// processes one wave's accesses in order, so a buffer is rewritten only
+// after its previous rows were read.  The epilogue arithmetic of one row
+// block overlaps the stores of the previous one.  The caller's barrier
+// after this keeps the next tile's loads out of the buffers until every
+// wave has read its rows.
+template <class C>
+struct WaveStage {
+    static constexpr int CPRW = C::WN / 8;                     // 16-byte chunks per buffer row
+    static constexpr int BUF = 32 * C::WN * 2;                 // bytes per wave: 32 rows x WN
+    static constexpr int PER_STAGE = C::STAGE_BYTES / BUF;     // buffers per stage
+    static_assert(PER_STAGE >= 2 && (4 + PER_STAGE - 1) / PER_STAGE <= 3, "wave buffers fit 3 stages");
+    static __device__ __forceinline__ uint32_t swz(int row) {
+        return (uint32_t)((row ^ (row / CPRW)) & (CPRW - 1));
+    }
+};
+
 template <class C, class T, int EPI, bool ALIGNED>
-__device__ __forceinline__ void store_tile_lds(const GemmArgs &args, const f32x16 (&acc)[C::I][C::J], int m0,
-                                               int n0, int wm, int wn, int lane, uint32_t lds0) {
+__device__ __forceinline__ void store_tile_wave(const GemmArgs &args, const f32x16 (&acc)[C::I][C::J], int m0,
+                                                int n0, int wm, int wn, int wave, int lane, uint32_t lds0,
+                                                int nk) {
+    using W = WaveStage<C>;
     const int M = args.M, N = args.N;
     const int lr = lane & 31;
     const int lh = lane >> 5;
-    // The bias of all 4 J four-column groups of this lane, requested at once
-    // (range-checked: columns past N read zero), before the barrier.
+    // the stage of the last slice is (nk - 1) & 3; the next ones are free
+    const uint32_t buf = lds0 + (uint32_t)(((nk + wave / W::PER_STAGE) & 3) * C::STAGE_BYTES) +
+                         (uint32_t)((wave % W::PER_STAGE) * W::BUF);
+    // The bias of all J four-column groups of this lane, requested at once
+    // (range-checked: columns past N read zero).
     uint32_t braw[C::J][4][2];
     if constexpr (EPI != EPI_NONE) {
         const __amdgpu_buffer_rsrc_t rb = tile::buffer_of(args.bias, 2u * (uint32_t)N);
@@ -418,54 +430,51 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs &args, const f32x1
                 }
             }
     }
-    __syncthreads();   // every wave is done reading the last slice
+    const __amdgpu_buffer_rsrc_t rc = tile::buffer_of(args.C, 2u * (uint32_t)M * (uint32_t)N);
 #pragma unroll
-    for (int j = 0; j < C::J; ++j) {
+    for (int i = 0; i < C::I; ++i) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int col = wn * C::WN + 32 * j + 8 * q + 4 * lh;
-            float bv[4] = {0.f, 0.f, 0.f, 0.f};
-            if constexpr (EPI != EPI_NONE) {
-                bv[0] = T::to_f32((uint16_t)(braw[j][q][0] & 0xffff));
-                bv[1] = T::to_f32((uint16_t)(braw[j][q][0] >> 16));
-                bv[2] = T::to_f32((uint16_t)(braw[j][q][1] & 0xffff));
-                bv[3] = T::to_f32((uint16_t)(braw[j][q][1] >> 16));
-            }
+        for (int j = 0; j < C::J; ++j) {
 #pragma unroll
-            for (int i = 0; i < C::I; ++i) {
-                const int row = wm * C::WM + 32 * i + lr;
+            for (int q = 0; q < 4; ++q) {
+                float bv[4] = {0.f, 0.f, 0.f, 0.f};
+                if constexpr (EPI != EPI_NONE) {
+                    bv[0] = T::to_f32((uint16_t)(braw[j][q][0] & 0xffff));
+                    bv[1] = T::to_f32((uint16_t)(braw[j][q][0] >> 16));
+                    bv[2] = T::to_f32((uint16_t)(braw[j][q][1] & 0xffff));
+                    bv[3] = T::to_f32((uint16_t)(braw[j][q][1] >> 16));
+                }
                 uint16_t o[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     o[r] = T::from_f32(epilogue<EPI>(acc[i][j][4 * q + r], bv[r]));
-                const uint32_t chunk = (uint32_t)(col >> 3) ^ c_swz<C::CPR>(row);
-                const uint32_t addr = lds0 + (uint32_t)C::B_ROW * (uint32_t)row + 16u * chunk + 8u * (uint32_t)lh;
-                *(__attribute__((address_space(3))) u32x2 *)(uintptr_t)addr =
+                const uint32_t chunk = (uint32_t)(4 * j + q) ^ W::swz(lr);
+                *(__attribute__((address_space(3))) u32x2 *)(uintptr_t)(
+                    buf + (uint32_t)(2 * C::WN * lr) + 16u * chunk + 8u * (uint32_t)lh) =
                     u32x2{pack2(o[0], o[1]), pack2(o[2], o[3])};
             }
         }
-    }
-    __syncthreads();
-    const __amdgpu_buffer_rsrc_t rc = tile::buffer_of(args.C, 2u * (uint32_t)M * (uint32_t)N);
-    const int tid = threadIdx.x;
-#pragma unroll 4
-    for (int it = 0; it < C::BM * C::CPR / NTHREADS; ++it) {
-        const int idx = it * NTHREADS + tid;
-        const int row = (int)((unsigned)idx / C::CPR);
-        const int c = (int)((unsigned)idx % C::CPR);
-        const int m = m0 + row;
-        const int n = n0 + 8 * c;
-        const u32x4 v = *(__attribute__((address_space(3))) const u32x4 *)(uintptr_t)(
-            lds0 + (uint32_t)C::B_ROW * (uint32_t)row + 16u * ((uint32_t)c ^ c_swz<C::CPR>(row)));
-        const uint32_t base = 2u * ((uint32_t)m * (uint32_t)N + (uint32_t)n);
-        if (ALIGNED || n + 8 <= N) {
-            const uint32_t off = (m < M && n < N) ? base : tile::OOB;
-            __builtin_amdgcn_raw_buffer_store_b128(v, rc, (int)off, 0, 0);
-        } else {
+        // rows wm*WM + 32 i + 0..31 of the tile, columns wn*WN ..: 64 / CPRW
+        // rows per read
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t off = (m < M && n + e < N) ? base + 2u * e : tile::OOB;
-                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(v[e >> 1] >> (16 * (e & 1))), rc, (int)off, 0, 0);
+        for (int it = 0; it < 32 * W::CPRW / 64; ++it) {
+            const int row = it * (64 / W::CPRW) + lane / W::CPRW;
+            const int c = lane % W::CPRW;
+            const int m = m0 + wm * C::WM + 32 * i + row;
+            const int n = n0 + wn * C::WN + 8 * c;
+            const u32x4 v = *(__attribute__((address_space(3))) const u32x4 *)(uintptr_t)(
+                buf + (uint32_t)(2 * C::WN * row) + 16u * ((uint32_t)c ^ W::swz(row)));
+            const uint32_t base = 2u * ((uint32_t)m * (uint32_t)N + (uint32_t)n);
+            if (ALIGNED || n + 8 <= N) {
+                const uint32_t off = (m < M && n < N) ? base : tile::OOB;
+                __builtin_amdgcn_raw_buffer_store_b128(v, rc, (int)off, 0, 0);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t off = (m < M && n + e < N) ? base + 2u * e : tile::OOB;
+                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(v[e >> 1] >> (16 * (e & 1))), rc, (int)off, 0,
+                                                          0);
+                }
             }
         }
     }
@@ -596,7 +605,7 @@ __global__ __launch_bounds__(NTHREADS, C::OCCUPANCY) void gemm_tiled_kernel(Gemm
         if (t + 1 == nk)
             slice(t, none{}, w0{}, no{});
 
-        store_tile_lds<C, T, EPI, !GEN>(args, acc, m0, n0, wm, wn, lane, lds0);
+        store_tile_wave<C, T, EPI, !GEN>(args, acc, m0, n0, wm, wn, wave, lane, lds0, nk);
         // every wave is done reading LDS before the next tile's loads land
         __syncthreads();
     }

@@ -61,12 +61,14 @@ struct BF16 {
 
 // GELU, tanh form, via the identity 0.5*y*(1 + tanh(z)) = y * sigmoid(2z)
 // = y / (1 + exp(-2z)), z = sqrt(2/pi) * (y + 0.044715 * y^3).  exp(-2z) is
-// taken as exp2(-2*log2(e)*z) on the hardware exp2; for z -> -inf the
-// reciprocal of +inf gives 0 and the result -0, for z -> +inf it gives y.
+// taken as exp2(t) on the hardware exp2, with t = -2*log2(e)*z evaluated as
+// y * (k0 + k1 * y^2) (one multiply, one fma, one multiply); for z -> -inf
+// the reciprocal of +inf gives 0 and the result -0, for z -> +inf it gives y.
 static __device__ __forceinline__ float gelu_tanh(float y) {
-    const float k = -2.0f * 1.4426950408889634f * 0.7978845608028654f;  // -2*log2(e)*sqrt(2/pi)
-    float t = k * (y + 0.044715f * y * y * y);
-    float e = __builtin_amdgcn_exp2f(t);
+    const float k0 = -2.0f * 1.4426950408889634f * 0.7978845608028654f;  // -2*log2(e)*sqrt(2/pi)
+    const float k1 = k0 * 0.044715f;
+    const float t = y * __builtin_fmaf(y * y, k1, k0);
+    const float e = __builtin_amdgcn_exp2f(t);
     return y * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
