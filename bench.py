@@ -63,7 +63,7 @@ SKINNY = "gemm_f16_skinny_16x11008x4096"
 RAGGED = "gemm_bf16_4000x4093x4111_bias_gelu_tanh"
 KERNEL_SOURCES = ["gemm_tiled.hip", "gemm_tiled_generic.hip", "gemm_skinny.hip", "gemm_w4.hip", "attention_fwd.hip",
                   "elementwise.hip", "tg_device.h", "tg_tile.h", "tg_launch.h", "tg_split.h", "tg_direct.h",
-                  "tg_gemm_host.hip"]
+                  "tg_gemm_host.hip", "tg_tile_model.inc"]
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
 SETTLE_S = 0.25   # untimed launches before every timed line, in seconds of wall time
 FUSION_ROUNDS = 4  # alternating blocks of fused / unfused / no-epilogue launches
@@ -303,40 +303,57 @@ def bench_w4(torch, tg, I, steps, warmup, copies=16):
     return wq["name"], ms, hot, nbytes
 
 
-TILE_CONFIGS = {"256x256": 1, "256x128": 2, "128x256": 3, "128x128": 4}   # tg_tiles values
+def tile_configs(tg):
+    """Every tile configuration of the tiled family: name -> tg_tiles value."""
+    return {tg.TILES_NAMES[c]: c for c in sorted(tg.TILES_AXES)}
 
 
-def time_tiled(torch, tg, M, N, K, dtype, epi, A, B, bias, C, cfg, steps, warmup, label):
-    """Per-launch time (ms) of tg_gemm_tiled with tile configuration cfg
-    (0: the library's choice, through tg_gemm)."""
+def time_alternating(torch, launches, steps, rounds=3, settle_s=None):
+    """Median per-launch time (ms) of each launch(i) in `launches` (name ->
+    fn), timed in `rounds` rounds of one block each, the order reversed every
+    round, after one settle: so that forms compared with each other see the
+    same clock."""
+    names = list(launches)
+    time_calls(torch, launches[names[0]], 1, 2, settle_s=settle_s)
+    times = {n: [] for n in names}
+    for r in range(rounds):
+        for n in (names if r % 2 == 0 else names[::-1]):
+            times[n].append(time_calls(torch, launches[n], steps, 1, settle_s=0.0))
+    return {n: sorted(v)[len(v) // 2] for n, v in times.items()}
+
+
+def tiled_launcher(torch, tg, M, N, K, dtype, epi, A, B, bias, C, cfg, label, group_m=0):
+    """launch(i) of tg_gemm_tiled_grouped with configuration cfg (0: the
+    library's choice, through tg_gemm)."""
     handle = torch.cuda.current_stream().cuda_stream
     a, b, bi, c = A.data_ptr(), B.data_ptr(), bias.data_ptr() if bias is not None else None, C.data_ptr()
 
     def launch(i):
         LOG.note(label)
-        st = (tg.tg_gemm_tiled(cfg, M, N, K, dtype, a, b, bi, epi, c, handle) if cfg
+        st = (tg.tg_gemm_tiled_grouped(cfg, group_m, M, N, K, dtype, a, b, bi, epi, c, handle) if cfg or group_m
               else tg.tg_gemm(M, N, K, dtype, a, b, bi, epi, c, handle))
         if st != tg.TG_OK:
-            raise RuntimeError(f"tg_gemm_tiled failed: {tg.tg_status_string(st)}")
+            raise RuntimeError(f"tg_gemm_tiled_grouped failed: {tg.tg_status_string(st)}")
 
-    return time_calls(torch, launch, steps, warmup)
+    return launch
 
 
 def bench_tile_choice(torch, tg, I, steps, warmup):
     """Every tile configuration, and the library's own choice, on the shape
-    classes the choice is for."""
+    classes the choice is for, timed in alternating blocks."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
+    configs = tile_configs(tg)
     out = {}
     for name, w in I.TILE_WORKLOADS.items():
         _, sets = device_operands(torch, I, w)
         A, B, bias, C = sets[0]
         flops = gemm_flops(w.M, w.N, w.K)
-        per = {}
-        for cname, cfg in TILE_CONFIGS.items():
-            per[cname] = time_tiled(torch, tg, w.M, w.N, w.K, w.dtype, w.epilogue, A, B, bias, C, cfg, steps, warmup,
-                                    f"{name} {cname}")
-        ms_auto = time_tiled(torch, tg, w.M, w.N, w.K, w.dtype, w.epilogue, A, B, bias, C, 0, steps, warmup,
-                             f"{name} auto")
+        launches = {cname: tiled_launcher(torch, tg, w.M, w.N, w.K, w.dtype, w.epilogue, A, B, bias, C, cfg,
+                                          f"{name} {cname}") for cname, cfg in configs.items()}
+        launches["auto"] = tiled_launcher(torch, tg, w.M, w.N, w.K, w.dtype, w.epilogue, A, B, bias, C, 0,
+                                          f"{name} auto")
+        per = time_alternating(torch, launches, steps)
+        ms_auto = per.pop("auto")
         st, auto = tg.tg_gemm_tiles_plan(w.M, w.N, w.K, cus)
         best = min(per, key=per.get)
         out[name] = {"auto": tg.TILES_NAMES.get(auto, "?"), "auto_us": round(ms_auto * 1e3, 2),
@@ -347,16 +364,86 @@ def bench_tile_choice(torch, tg, I, steps, warmup):
                      "traffic": measured_traffic(f"{name} auto")}
         log(f"{name}: auto {tg.TILES_NAMES.get(auto)} {ms_auto * 1e3:.1f} us, fastest {best} "
             f"{per[best] * 1e3:.1f} us, 256x256 {per['256x256'] * 1e3:.1f} us")
-        del sets, A, B, bias, C
+        del sets, A, B, bias, C, launches
         torch.cuda.empty_cache()
     return out
 
 
+def fit_tile_model(meas, cus):
+    """The tile-choice cost model's parameters from the sweep's timings (us):
+    per configuration, a1 + b1 K for a round of one tile per CU on every CU
+    (two points in K), a2 + b2 K for a round of two per CU (two workgroups per
+    CU only), kappa (a round on a fraction u of the CUs takes 1 - kappa (1 - u)
+    of the full-load time: less contention), phi (rounds after the first:
+    the 8192-cube's time over its rounds' prediction) and rho (misaligned
+    shapes, K and N not multiples of 8: time over the aligned time)."""
+    out = {}
+    for name, m in meas.items():
+        k1, k2 = m["k"]
+        b1 = (m["solo"][1] - m["solo"][0]) / (k2 - k1)
+        a1 = m["solo"][0] - b1 * k1
+        rec = {"a1": a1, "b1": b1}
+        if "pair" in m:
+            b2 = (m["pair"][1] - m["pair"][0]) / (k2 - k1)
+            rec.update(a2=m["pair"][0] - b2 * k1, b2=b2)
+        rec["kappa"] = max(0.0, min(0.9, (1.0 - m["quarter"] / (a1 + b1 * k2)) / 0.75))
+        pred = predict_tile_time(dict(rec, phi=1.0, rho=1.0, bm=m["bm"], bn=m["bn"], occ=m["occ"]),
+                                 *m["full_shape"], cus, True)
+        rec["phi"] = m["full"] / pred
+        rec["rho"] = m["ragged"] / m["solo"][1]
+        out[name] = {k: round(v, 6) for k, v in rec.items()}
+    return out
+
+
+def predict_tile_time(p, M, N, K, cus, aligned):
+    """The cost model (mirrors the library's auto_tiles): the sum over the
+    rounds of the persistent grid of each round's time."""
+    tiles = -(-M // p["bm"]) * -(-N // p["bn"])
+    per_round = cus * p["occ"]
+    t, left, rounds = 0.0, tiles, 0
+    while left > 0:
+        busy = min(left, per_round)
+        if busy > cus:    # some CUs hold two workgroups
+            t += p["a2"] + p["b2"] * K
+        else:
+            t += (p["a1"] + p["b1"] * K) * (1.0 - p["kappa"] * (1.0 - busy / cus))
+        left -= busy
+        rounds += 1
+    if rounds > 1:
+        t *= p["phi"]
+    return t if aligned else t * p["rho"]
+
+
+TILE_MODEL_INC = os.path.join(ROOT, "tiled_dense_gemm_tg_amd", "csrc", "tg_tile_model.inc")
+
+
+def write_tile_model(sweep: dict, path: str = TILE_MODEL_INC) -> None:
+    """Writes the cost model's parameter table (the rows of kTileChoices in
+    tg_gemm_host.hip) from a --sweep result; the default configuration comes
+    first (ties go to earlier rows)."""
+    model = sweep["tile_sweep"]["model"] if "tile_sweep" in sweep else sweep["model"]
+    enum = {"256x256": "TG_TILES_256x256", "256x128": "TG_TILES_256x128", "128x256": "TG_TILES_128x256",
+            "128x128": "TG_TILES_128x128", "256x256_k64": "TG_TILES_256x256_K64",
+            "256x128_k64": "TG_TILES_256x128_K64", "128x256_k64": "TG_TILES_128x256_K64",
+            "128x128_k64": "TG_TILES_128x128_K64", "256x256_w8": "TG_TILES_256x256_W8"}
+    lines = ["// tg_tile_model.inc -- parameters of the tile-choice cost model (see auto_tiles in",
+             "// tg_gemm_host.hip), written by bench.py from `python3 bench.py --sweep` on one MI355X:",
+             "// {tiles, BM, BN, workgroups per CU, a1, b1, a2, b2, kappa, phi, rho}, times in us."]
+    for name in enum:
+        p = model[name]
+        bm, bn = (int(v) for v in name.split("_")[0].split("x"))
+        occ = 2 if (bm, bn) == (128, 128) else 1
+        lines.append(f"    {{{enum[name]}, {bm}, {bn}, {occ}, {p['a1']:.6g}, {p['b1']:.6g}, {p.get('a2', 0.0):.6g}, "
+                     f"{p.get('b2', 0.0):.6g}, {p['kappa']:.6g}, {p['phi']:.6g}, {p['rho']:.6g}}},")
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
 def tile_sweep(torch, tg, I, steps, warmup):
-    """Measures the per-CU throughput of each tile configuration with one
-    tile per CU (r_single) and with many (r_full), relative to r_full of the
-    256 x 256 tile: the inputs of the library's tile-choice cost model.
-    Operands are normal(0, 0.1) fp16 drawn on the device (timing only)."""
+    """Measures what the library's tile-choice cost model needs for every
+    configuration (fit_tile_model), the raster group sizes on the large
+    shapes, and the shape classes.  Operands are normal(0, 0.1) fp16 drawn on
+    the device (timing only)."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     gen = torch.Generator(device="cuda")
     gen.manual_seed(20001)
@@ -366,28 +453,42 @@ def tile_sweep(torch, tg, I, steps, warmup):
         B = (torch.randn((K, N), generator=gen, device="cuda") * 0.1).half()
         return A, B, torch.empty((M, N), dtype=torch.float16, device="cuda")
 
-    res = {"cus": cus, "full": {}, "single": {}}
-    K = 8192
-    A, B, C = operands(8192, 8192, K)
-    for cname, cfg in TILE_CONFIGS.items():
-        ms = time_tiled(torch, tg, 8192, 8192, K, 0, 0, A, B, None, C, cfg, steps, warmup, f"sweep full {cname}")
-        res["full"][cname] = {"us": round(ms * 1e3, 1), "TFLOP/s": round(gemm_flops(8192, 8192, K) / ms / 1e9, 1)}
-        log(f"sweep full 8192x8192x{K} {cname}: {ms * 1e3:.1f} us")
-    del A, B, C
-    tm = 16
-    tn = max(cus // tm, 1)
-    for cname, cfg in TILE_CONFIGS.items():
-        bm, bn = (int(v) for v in cname.split("x"))
-        M, N = tm * bm, tn * bn
+    def one(cfg, M, N, K, label, group_m=0):
         A, B, C = operands(M, N, K)
-        ms = time_tiled(torch, tg, M, N, K, 0, 0, A, B, None, C, cfg, steps, warmup, f"sweep single {cname}")
-        res["single"][cname] = {"shape": f"{M}x{N}x{K}", "us": round(ms * 1e3, 1),
-                                "TFLOP/s": round(gemm_flops(M, N, K) / ms / 1e9, 1)}
-        log(f"sweep single {M}x{N}x{K} {cname}: {ms * 1e3:.1f} us")
+        t = time_alternating(torch, {"x": tiled_launcher(torch, tg, M, N, K, 0, 0, A, B, None, C, cfg, label,
+                                                         group_m)}, steps, rounds=1)["x"] * 1e3
         del A, B, C
-    ref = res["full"]["256x256"]["TFLOP/s"]
-    res["rates"] = {c: {"r_single": round(res["single"][c]["TFLOP/s"] / ref, 3),
-                        "r_full": round(res["full"][c]["TFLOP/s"] / ref, 3)} for c in TILE_CONFIGS}
+        return t
+
+    meas = {}
+    ks = (2048, 8192)
+    side = int(round(cus ** 0.5))
+    for cname, cfg in tile_configs(tg).items():
+        bm, bn, bk, stages, waves = tg.TILES_AXES[cfg]
+        occ = 2 if (bm, bn) == (128, 128) else 1
+        m = {"bm": bm, "bn": bn, "occ": occ, "k": ks}
+        tm, tn = side, cus // side
+        m["solo"] = [one(cfg, tm * bm, tn * bn, k, f"sweep {cname} solo") for k in ks]
+        if occ == 2:
+            m["pair"] = [one(cfg, tm * bm, 2 * tn * bn, k, f"sweep {cname} pair") for k in ks]
+        m["quarter"] = one(cfg, (tm // 2) * bm, (tn // 2) * bn, ks[1], f"sweep {cname} quarter")
+        m["full_shape"] = (8192, 8192, 8192)
+        m["full"] = one(cfg, 8192, 8192, 8192, f"sweep {cname} full")
+        m["ragged"] = one(cfg, tm * bm - 3, tn * bn - 3, ks[1] - 5, f"sweep {cname} ragged")
+        meas[cname] = m
+        log(f"sweep {cname}: {m}")
+    res = {"cus": cus, "measured_us": meas, "model": fit_tile_model(meas, cus)}
+    groups = {}
+    for M, N, K in ((8192, 8192, 8192), (4096, 4096, 4096), (512, 11008, 4096)):
+        st, auto = tg.tg_gemm_tiles_plan(M, N, K, cus)
+        A, B, C = operands(M, N, K)
+        launches = {f"group_m={gm}": tiled_launcher(torch, tg, M, N, K, 0, 0, A, B, None, C, auto,
+                                                    f"sweep group {gm}", gm) for gm in (1, 2, 4, 8, 16)}
+        groups[f"{M}x{N}x{K} {tg.TILES_NAMES[auto]}"] = {k: round(v * 1e3, 2)
+                                                         for k, v in time_alternating(torch, launches, steps).items()}
+        log(f"sweep raster groups {M}x{N}x{K}: {groups[f'{M}x{N}x{K} {tg.TILES_NAMES[auto]}']}")
+        del A, B, C, launches
+    res["raster_groups"] = groups
     res["shape_classes"] = bench_tile_choice(torch, tg, I, steps, warmup)
     torch.cuda.empty_cache()
     return res
@@ -778,9 +879,15 @@ def main() -> int:
                     help="no settling, short lines: for rocprofv3 counter runs")
     ap.add_argument("--summarise", default=None, metavar="DIR",
                     help="only summarise the rocprofv3 runs under DIR into profiles/")
+    ap.add_argument("--write-tile-model", default=None, metavar="SWEEP_JSON",
+                    help="only write the tile-choice model table from a --sweep output line")
     args = ap.parse_args()
     if args.summarise:
         summarise_profiles(args.summarise, os.path.join(ROOT, "profiles"))
+        return 0
+    if args.write_tile_model:
+        with open(args.write_tile_model) as fh:
+            write_tile_model(json.loads([ln for ln in fh.read().splitlines() if ln.startswith("{")][-1]))
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this GEMM runs on a single "

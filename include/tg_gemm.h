@@ -85,7 +85,7 @@ typedef enum {
  *                          through LDS by 16-byte direct loads; any shape
  *                          and alignment as long as A
  *                          and B, each padded to whole tiles, stay below 2 GiB
- *                          less 64 KiB: 2 (M + 256) K and 2 (K + 32) (N + 256)
+ *                          less 64 KiB: 2 (M + 256) K and 2 (K + 64) (N + 256)
  *                          both below 2^31 - 65536.  Fastest with K % 8 == 0,
  *                          N % 8 == 0, A, B, C 16-byte and bias 8-byte
  *                          aligned.
@@ -138,28 +138,47 @@ tg_status tg_gemm_plan(int64_t M, int64_t N, int64_t K, tg_dtype dtype,
                        const void *C, tg_path *path_out);
 
 /*
- * Tile configurations of the TG_PATH_TILED family, BM x BN (rows by columns
- * of C per workgroup).  The TileLang pages leave the tile size to the user
- * and tune it per shape ("Designing high-performance GPU kernels with
- * TileLang", "Performance Analysis and Autotuning": a benchmark sweep over
- * block sizes picks the winner, most of all for non-standard dimensions;
+ * Tile configurations of the TG_PATH_TILED family: BM x BN (rows by columns
+ * of C per workgroup), the k-extent BK of each pipeline stage, the number of
+ * LDS stages and the number of waves per workgroup.  The TileLang pages
+ * leave these to the user and tune them per shape ("Designing
+ * high-performance GPU kernels with TileLang", "Performance Analysis and
+ * Autotuning": a benchmark sweep over block sizes, pipeline stages and
+ * thread counts picks the winner, most of all for non-standard dimensions;
+ * "TileLang: you write the dataflow, the compiler owns the schedule", "What
+ * a tile costs, exactly": the stage count sets the shared-memory footprint;
  * "TileLang: writing LLM GPU kernels by thinking in tiles", section 6: tile
  * recommendation from hardware information and heuristics).  Here every
  * configuration is one instance of the same kernel; TG_TILES_AUTO (what
  * tg_gemm uses) takes the one a cost model built from a measured sweep
  * predicts fastest: the number of rounds of tiles the persistent grid needs
- * on the device's compute units, times the time of one round, which is the
- * tile's size over that configuration's measured per-CU throughput.  The
- * 256x256 tile is the most efficient per CU; the smaller ones keep more CUs
- * busy when the output has few 256x256 tiles (the 128x128 tile runs two
+ * on the device's compute units, times the time of one round, a fixed
+ * per-tile cost plus K over the configuration's measured per-CU throughput.
+ * The 256x256 tile is the most efficient per CU; the smaller ones keep more
+ * CUs busy when the output has few 256x256 tiles (the 128x128 tiles run two
  * workgroups per CU).
+ *                          BM x BN    BK  stages  waves
+ *   TG_TILES_256x256       256x256    32    4       4
+ *   TG_TILES_256x128       256x128    32    4       4
+ *   TG_TILES_128x256       128x256    32    4       4
+ *   TG_TILES_128x128       128x128    32    4       4   (2 per CU)
+ *   TG_TILES_256x256_K64   256x256    64    2       4
+ *   TG_TILES_256x128_K64   256x128    64    3       4
+ *   TG_TILES_128x256_K64   128x256    64    3       4
+ *   TG_TILES_128x128_K64   128x128    64    2       4   (2 per CU)
+ *   TG_TILES_256x256_W8    256x256    32    4       8   (2 per SIMD, 128x64 each)
  */
 typedef enum {
     TG_TILES_AUTO = 0,
     TG_TILES_256x256 = 1,
     TG_TILES_256x128 = 2,
     TG_TILES_128x256 = 3,
-    TG_TILES_128x128 = 4
+    TG_TILES_128x128 = 4,
+    TG_TILES_256x256_K64 = 5,
+    TG_TILES_256x128_K64 = 6,
+    TG_TILES_128x256_K64 = 7,
+    TG_TILES_128x128_K64 = 8,
+    TG_TILES_256x256_W8 = 9
 } tg_tiles;
 
 /*
@@ -174,6 +193,18 @@ typedef enum {
 tg_status tg_gemm_tiled(tg_tiles tiles, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
                         const void *A, const void *B, const void *bias, tg_epilogue epilogue,
                         void *C, void *stream);
+
+/*
+ * As tg_gemm_tiled, with the raster of the tiles chosen too: each XCD walks
+ * its share of the output tiles group_m tile-rows at a time, column by
+ * column, so that the tiles running together share A and B panels in that
+ * XCD's L2 (0: the library's choice, 4).  group_m 1..64; other values are
+ * TG_ERR_INVALID_ARG.  Results do not depend on group_m.  Meant for tuning
+ * sweeps.
+ */
+tg_status tg_gemm_tiled_grouped(tg_tiles tiles, int group_m, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
+                                const void *A, const void *B, const void *bias, tg_epilogue epilogue,
+                                void *C, void *stream);
 
 /*
  * The configuration TG_TILES_AUTO picks for an M x N x K product on a device

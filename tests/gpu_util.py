@@ -37,7 +37,7 @@ def to_bits(t) -> np.ndarray:
 
 
 def run(M, N, K, dtype, A_bits, B_bits, bias_bits=None, epilogue=I.EPI_NONE, path=tg.TG_PATH_AUTO,
-        out=None, stream=None, expect_path=None, tiles=tg.TG_TILES_AUTO):
+        out=None, stream=None, expect_path=None, tiles=tg.TG_TILES_AUTO, group_m=0):
     """Runs one GEMM through the C interface (tg_gemm_path, or tg_gemm_tiled
     when a tile configuration is given); returns the output tensor."""
     import torch
@@ -52,7 +52,7 @@ def run(M, N, K, dtype, A_bits, B_bits, bias_bits=None, epilogue=I.EPI_NONE, pat
                                 bias.data_ptr() if bias is not None else None, epilogue, out.data_ptr())
         assert st == tg.TG_OK and p == expect_path, (st, tg.PATH_NAMES.get(p))
     epi_name = {I.EPI_NONE: "none", I.EPI_BIAS: "bias", I.EPI_BIAS_GELU_TANH: "bias_gelu_tanh"}[epilogue]
-    tg.gemm(A, B, bias, epi_name, out=out, path=path, stream=stream, tiles=tiles)
+    tg.gemm(A, B, bias, epi_name, out=out, path=path, stream=stream, tiles=tiles, group_m=group_m)
     torch.cuda.synchronize()
     return out
 

@@ -127,8 +127,8 @@ def test_empty_K_allows_null_operands(lib):
     (4000, 4096, 4104, {}, tg.TG_PATH_TILED),           # ragged M is fine for the vector path
     (130808, 256, 8192, {}, tg.TG_PATH_TILED),          # 2 (M + 256) K just below 2^31 - 64 Ki
     (130812, 256, 8192, {}, tg.TG_PATH_TILED_GENERIC),  # ... and at it
-    (256, 130296, 8192, {}, tg.TG_PATH_TILED),          # 2 (K + 32) (N + 256) just below
-    (256, 130304, 8192, {}, tg.TG_PATH_TILED_GENERIC),
+    (256, 129792, 8192, {}, tg.TG_PATH_TILED),          # 2 (K + 64) (N + 256) just below
+    (256, 129800, 8192, {}, tg.TG_PATH_TILED_GENERIC),
     (256, 256, 256, {"C": PC + 8}, tg.TG_PATH_TILED),
     (256, 256, 256, {"B": PB + 2}, tg.TG_PATH_TILED),
     (256, 256, 256, {"bias": PBIAS + 2, "epi": I.EPI_BIAS}, tg.TG_PATH_TILED),
@@ -260,8 +260,15 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
 # ------------------------------------------------------------ tile configurations
 
 def test_tiled_entry_point_checks_arguments(lib):
-    for bad in (-1, 5, 99):
+    for bad in (-1, max(tg.TILES_NAMES) + 1, 99):
         assert tg.tg_gemm_tiled(bad, 64, 64, 64, I.F16, PA, PB, None, I.EPI_NONE, PC, None) == tg.TG_ERR_INVALID_ARG
+    # raster groups of 1..64 tile rows (0: the library's choice)
+    for bad in (-1, 65):
+        assert tg.tg_gemm_tiled_grouped(tg.TG_TILES_256x256, bad, 64, 64, 64, I.F16, PA, PB, None, I.EPI_NONE, PC,
+                                        None) == tg.TG_ERR_INVALID_ARG
+    for ok in (0, 1, 64):
+        assert tg.tg_gemm_tiled_grouped(tg.TG_TILES_256x256, ok, 0, 64, 64, I.F16, None, None, None, I.EPI_NONE,
+                                        None, None) == tg.TG_OK
     # the tiled family's size limit applies to every configuration
     for cfg in (tg.TG_TILES_AUTO, tg.TG_TILES_128x128):
         assert tg.tg_gemm_tiled(cfg, 130812, 256, 8192, I.F16, PA, PB, None, I.EPI_NONE, PC, None) \
@@ -301,7 +308,7 @@ def test_tiles_plan_on_an_mi355x(lib, M, N, K, cfg):
 def test_tiles_plan_follows_the_cu_count(lib):
     # with 4x the CUs the 4096-cube has too few 256x256 tiles; with 1/4 the 2048-cube has enough
     assert tg.tg_gemm_tiles_plan(4096, 4096, 4096, 1024)[1] != tg.TG_TILES_256x256
-    assert tg.tg_gemm_tiles_plan(2048, 2048, 2048, 64)[1] == tg.TG_TILES_256x256
+    assert tg.TILES_AXES[tg.tg_gemm_tiles_plan(2048, 2048, 2048, 64)[1]][:2] == (256, 256)
 
 
 def test_smoke_cases_are_planned_as_smoke_expects(lib):

@@ -62,7 +62,7 @@ def test_counter_hash_covers_every_kernel_source():
     # sources matches; every file the library is built from must be part of
     # that hash, or a change to it would leave stale figures in the bench line.
     csrc = os.path.join(os.path.dirname(bench.__file__), "tiled_dense_gemm_tg_amd", "csrc")
-    sources = sorted(f for f in os.listdir(csrc) if f.endswith((".hip", ".h")))
+    sources = sorted(f for f in os.listdir(csrc) if f.endswith((".hip", ".h", ".inc")))
     assert sorted(bench.KERNEL_SOURCES) == sources
 
 

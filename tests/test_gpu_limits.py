@@ -47,8 +47,8 @@ def _sample(n, count, seed):
 @pytest.mark.parametrize("M,N,K,path", [
     (130808, 256, 8192, tg.TG_PATH_TILED),           # A padded just below 2 GiB - 64 KiB
     (130812, 256, 8192, tg.TG_PATH_TILED_GENERIC),   # A just above: 2.14 GB, offsets past 2^31
-    (256, 130296, 8192, tg.TG_PATH_TILED),           # B padded just below the limit
-    (256, 130304, 8192, tg.TG_PATH_TILED_GENERIC),   # B just above
+    (256, 129792, 8192, tg.TG_PATH_TILED),           # B padded just below the limit
+    (256, 129800, 8192, tg.TG_PATH_TILED_GENERIC),   # B just above
 ], ids=lambda v: str(v))
 def test_largest_operands(M, N, K, path):
     import torch

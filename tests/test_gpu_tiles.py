@@ -19,9 +19,8 @@ from gpu_util import check_exact, check_tolerance, log, run, to_bits, to_device
 
 pytestmark = pytest.mark.gpu
 
-CONFIGS = [tg.TG_TILES_256x256, tg.TG_TILES_256x128, tg.TG_TILES_128x256, tg.TG_TILES_128x128]
-TILE_SHAPE = {tg.TG_TILES_256x256: (256, 256), tg.TG_TILES_256x128: (256, 128),
-              tg.TG_TILES_128x256: (128, 256), tg.TG_TILES_128x128: (128, 128)}
+CONFIGS = sorted(tg.TILES_AXES)
+TILE_SHAPE = {cfg: axes[:2] for cfg, axes in tg.TILES_AXES.items()}
 EDGE = [1, 2, 7, 8, 15, 16, 17, 31, 33, 63, 64, 65, 127, 129, 255, 257]
 EPI_NAMES = {I.EPI_NONE: "none", I.EPI_BIAS: "bias", I.EPI_BIAS_GELU_TANH: "bias_gelu_tanh"}
 
@@ -99,7 +98,7 @@ def test_any_alignment(cfg, M, N, K, offsets):
 
 
 @pytest.mark.parametrize("cfg", CONFIGS, ids=_name)
-@pytest.mark.parametrize("K", [37, 8, 33])
+@pytest.mark.parametrize("K", [37, 8, 33, 71, 100])
 def test_k_tail_does_not_mix_rows(cfg, K):
     """Odd rows of A hold +inf at k = 0; with K % 8 != 0 the chunk crossing
     k = K of an even row also covers the odd row's first elements, which
@@ -121,6 +120,12 @@ def test_k_tail_does_not_mix_rows(cfg, K):
     (tg.TG_TILES_128x256, 4224, 2304, 72),
     (tg.TG_TILES_128x128, 3000, 3100, 40),   # 600 tiles: more than two per CU, ragged
     (tg.TG_TILES_128x128, 4096, 4096, 24),   # 1024 tiles, a multiple of the 8 XCDs
+    (tg.TG_TILES_256x256, 4352, 4352, 48),   # 289 tiles
+    (tg.TG_TILES_256x256_K64, 4352, 4352, 136),
+    (tg.TG_TILES_256x128_K64, 2304, 4224, 200),
+    (tg.TG_TILES_128x256_K64, 4224, 2304, 72),
+    (tg.TG_TILES_128x128_K64, 3000, 3100, 130),
+    (tg.TG_TILES_256x256_W8, 4352, 4352, 72),
 ], ids=lambda v: str(v))
 def test_persistent_grid_covers_every_tile(cfg, M, N, K):
     dtype = I.F16
@@ -207,3 +212,38 @@ def test_empty_K_gives_epilogue_of_zero(cfg, epi):
     log(f"[tiles-K=0] tiles={_name(cfg)} epi={epi}")
     out = run(M, N, 0, I.F16, np.zeros(0, np.uint16), np.zeros(0, np.uint16), bias, epi, tiles=cfg)
     check_exact(to_bits(out), refq, "K=0")
+
+
+@pytest.mark.parametrize("cfg", CONFIGS, ids=_name)
+def test_every_pipeline_depth(cfg):
+    """K from one slice to several more than the stage ring holds, exact and
+    ragged, so every prologue, steady, last-request and tail step of the
+    pipeline runs (integers: exact)."""
+    dtype = I.BF16
+    M, N = 136, 264
+    bk = tg.TILES_AXES[cfg][2]
+    for n in range(1, 8):
+        for K in (n * bk, n * bk - 5):
+            A = I.small_int_bits((M, K), dtype, 13700 + K)
+            B = I.small_int_bits((K, N), dtype, 13800 + K)
+            bias = I.small_int_bits((N,), dtype, 13900 + K)
+            _, refq = oracle.gemm(M, N, K, dtype, A, B, bias, I.EPI_BIAS)
+            log(f"[tiles-depth] tiles={_name(cfg)} K={K}")
+            check_exact(to_bits(run(M, N, K, dtype, A, B, bias, I.EPI_BIAS, tiles=cfg)), refq, f"K={K}")
+
+
+@pytest.mark.parametrize("group_m", [1, 2, 3, 8, 64])
+def test_raster_group_changes_nothing_but_the_order(group_m):
+    """tg_gemm_tiled_grouped: every group size covers every tile once
+    (integers: exact), also groups taller than the tile rows and sizes that
+    do not divide them, on a persistent grid with several tiles per CU."""
+    dtype = I.F16
+    M, N, K = 2600, 3000, 40
+    A = I.small_int_bits((M, K), dtype, 14000)
+    B = I.small_int_bits((K, N), dtype, 14001)
+    bias = I.small_int_bits((N,), dtype, 14002)
+    _, refq = oracle.gemm(M, N, K, dtype, A, B, bias, I.EPI_BIAS)
+    for cfg in (tg.TG_TILES_256x256, tg.TG_TILES_128x128):
+        log(f"[tiles-group] tiles={_name(cfg)} group_m={group_m}")
+        got = to_bits(run(M, N, K, dtype, A, B, bias, I.EPI_BIAS, tiles=cfg, group_m=group_m))
+        check_exact(got, refq, f"group_m={group_m} tiles={_name(cfg)}")

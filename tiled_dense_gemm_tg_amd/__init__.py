@@ -40,10 +40,25 @@ TG_TILES_256x256 = 1
 TG_TILES_256x128 = 2
 TG_TILES_128x256 = 3
 TG_TILES_128x128 = 4
+TG_TILES_256x256_K64 = 5
+TG_TILES_256x128_K64 = 6
+TG_TILES_128x256_K64 = 7
+TG_TILES_128x128_K64 = 8
+TG_TILES_256x256_W8 = 9
 TILES_NAMES = {TG_TILES_AUTO: "auto", TG_TILES_256x256: "256x256", TG_TILES_256x128: "256x128",
-               TG_TILES_128x256: "128x256", TG_TILES_128x128: "128x128"}
+               TG_TILES_128x256: "128x256", TG_TILES_128x128: "128x128",
+               TG_TILES_256x256_K64: "256x256_k64", TG_TILES_256x128_K64: "256x128_k64",
+               TG_TILES_128x256_K64: "128x256_k64", TG_TILES_128x128_K64: "128x128_k64",
+               TG_TILES_256x256_W8: "256x256_w8"}
+# (BM, BN, BK, stages, waves) of each configuration
+TILES_AXES = {TG_TILES_256x256: (256, 256, 32, 4, 4), TG_TILES_256x128: (256, 128, 32, 4, 4),
+              TG_TILES_128x256: (128, 256, 32, 4, 4), TG_TILES_128x128: (128, 128, 32, 4, 4),
+              TG_TILES_256x256_K64: (256, 256, 64, 2, 4), TG_TILES_256x128_K64: (256, 128, 64, 3, 4),
+              TG_TILES_128x256_K64: (128, 256, 64, 3, 4), TG_TILES_128x128_K64: (128, 128, 64, 2, 4),
+              TG_TILES_256x256_W8: (256, 256, 32, 4, 8)}
 
-EXPORTED = ("tg_gemm", "tg_gemm_path", "tg_gemm_plan", "tg_gemm_tiled", "tg_gemm_tiles_plan", "tg_gemm_split",
+EXPORTED = ("tg_gemm", "tg_gemm_path", "tg_gemm_plan", "tg_gemm_tiled", "tg_gemm_tiled_grouped", "tg_gemm_tiles_plan",
+            "tg_gemm_split",
             "tg_gemm_split_workspace_bytes", "tg_gemm_split_plan", "tg_gemm_split_static", "tg_elementwise", "tg_gemm_unfused",
             "tg_w4_packed_bytes", "tg_w4_pack", "tg_gemm_w4", "tg_gemm_w4_split", "tg_gemm_w4_split_workspace_bytes",
             "tg_gemm_w4_split_plan", "tg_attention_fwd", "tg_status_string", "tg_version")
@@ -79,6 +94,8 @@ def load_library():
     lib.tg_gemm_plan.restype = ci
     lib.tg_gemm_tiled.argtypes = [ci, i64, i64, i64, ci, vp, vp, vp, ci, vp, vp]
     lib.tg_gemm_tiled.restype = ci
+    lib.tg_gemm_tiled_grouped.argtypes = [ci, ci, i64, i64, i64, ci, vp, vp, vp, ci, vp, vp]
+    lib.tg_gemm_tiled_grouped.restype = ci
     lib.tg_gemm_tiles_plan.argtypes = [i64, i64, i64, ci, ctypes.POINTER(ci)]
     lib.tg_gemm_tiles_plan.restype = ci
     lib.tg_gemm_split.argtypes = [ci, i64, i64, i64, ci, vp, vp, vp, ci, vp, vp, i64, vp]
@@ -133,6 +150,10 @@ def tg_gemm_plan(M, N, K, dtype, A, B, bias, epilogue, C):
 
 def tg_gemm_tiled(tiles, M, N, K, dtype, A, B, bias, epilogue, C, stream) -> int:
     return load_library().tg_gemm_tiled(tiles, M, N, K, dtype, A, B, bias, epilogue, C, stream)
+
+
+def tg_gemm_tiled_grouped(tiles, group_m, M, N, K, dtype, A, B, bias, epilogue, C, stream) -> int:
+    return load_library().tg_gemm_tiled_grouped(tiles, group_m, M, N, K, dtype, A, B, bias, epilogue, C, stream)
 
 
 def tg_gemm_tiles_plan(M, N, K, num_cu=0):
@@ -252,7 +273,7 @@ _EPI = {"none": EPI_NONE, "bias": EPI_BIAS, "bias_gelu_tanh": EPI_BIAS_GELU_TANH
 
 
 def gemm(A, B, bias=None, epilogue: str = "none", out=None, path: int = TG_PATH_AUTO, stream=None,
-         unfused: bool = False, tiles: int = TG_TILES_AUTO, splits=None, workspace=None):
+         unfused: bool = False, tiles: int = TG_TILES_AUTO, splits=None, workspace=None, group_m: int = 0):
     """epilogue(A @ B [+ bias]) on torch device tensors (fp16 or bf16, row-major).
 
     Returns ``out`` (allocated when not given).  Runs on ``stream`` or torch's
@@ -260,7 +281,9 @@ def gemm(A, B, bias=None, epilogue: str = "none", out=None, path: int = TG_PATH_
     tg_gemm_unfused (the product, then the epilogue steps as separate passes;
     ``path`` must then be TG_PATH_AUTO).  A ``tiles`` configuration other than
     TG_TILES_AUTO calls tg_gemm_tiled (the tiled family with that tile size;
-    ``path`` must then be TG_PATH_AUTO or TG_PATH_TILED).  ``splits`` (0 for
+    ``path`` must then be TG_PATH_AUTO or TG_PATH_TILED); ``group_m`` > 0 sets
+    the tile rows per raster group of that call (tg_gemm_tiled_grouped).
+    ``splits`` (0 for
     the library's choice) calls tg_gemm_split with ``workspace`` (a
     zero-filled uint8 GPU tensor from :func:`split_workspace`, allocated here
     when not given; reuse one per stream to skip that); ``path`` must then be
@@ -289,7 +312,7 @@ def gemm(A, B, bias=None, epilogue: str = "none", out=None, path: int = TG_PATH_
         raise ValueError("out has the wrong shape or dtype")
     dtype = F16 if A.dtype == torch.float16 else BF16
     s = (stream if stream is not None else torch.cuda.current_stream(A.device)).cuda_stream
-    if tiles != TG_TILES_AUTO and (unfused or path not in (TG_PATH_AUTO, TG_PATH_TILED)):
+    if (tiles != TG_TILES_AUTO or group_m) and (unfused or path not in (TG_PATH_AUTO, TG_PATH_TILED)):
         raise ValueError("a tile configuration applies to the tiled family only")
     if splits is not None and (unfused or path != TG_PATH_AUTO or tiles != TG_TILES_AUTO):
         raise ValueError("split-K goes with the library's own choice of kernel")
@@ -312,9 +335,9 @@ def gemm(A, B, bias=None, epilogue: str = "none", out=None, path: int = TG_PATH_
             raise ValueError("the unfused form chooses its own kernel family")
         st = tg_gemm_unfused(M, N, K, dtype, A.data_ptr(), B.data_ptr(),
                              bias.data_ptr() if bias is not None else None, epi, out.data_ptr(), s)
-    elif tiles != TG_TILES_AUTO:
-        st = tg_gemm_tiled(tiles, M, N, K, dtype, A.data_ptr(), B.data_ptr(),
-                           bias.data_ptr() if bias is not None else None, epi, out.data_ptr(), s)
+    elif tiles != TG_TILES_AUTO or group_m:
+        st = tg_gemm_tiled_grouped(tiles, group_m, M, N, K, dtype, A.data_ptr(), B.data_ptr(),
+                                   bias.data_ptr() if bias is not None else None, epi, out.data_ptr(), s)
     else:
         st = tg_gemm_path(path, M, N, K, dtype, A.data_ptr(), B.data_ptr(),
                           bias.data_ptr() if bias is not None else None, epi, out.data_ptr(), s)

@@ -11,19 +11,20 @@
 // multiplied.  Sizes and mechanics are chosen for CDNA4 rather than taken from
 // the pages' NVIDIA example:
 //
-//   * tile BM x BN with BM, BN in {128, 256} (the tile configuration is a
-//     template parameter; the host picks one per shape), 256 threads = 4
-//     wave64s in a 2 x 2 grid, each owning a BM/2 x BN/2 block of C as
-//     v_mfma_f32_32x32x16 accumulators in AGPRs (256 fp32 values per lane at
-//     256 x 256);
-//   * k-slices of 32 in a ring of 4 LDS stages (4 x 32 KB of the 160 KB LDS at
-//     256 x 256), filled by buffer loads that write LDS directly
-//     (buffer_load_dwordx4 ... lds): no staging registers, no LDS store
-//     instructions, and each slice is requested two slices before it is used,
-//     so a whole slice of MFMA work hides the memory latency twice over; one
-//     barrier per slice;
-//   * A is staged as [BM m][32 k] (k-contiguous, what a 16-bit MFMA operand
-//     holds per lane) and read with ds_read_b128; B stays [32 k][BN n] as in
+//   * tile BM x BN with BM, BN in {128, 256}, k-slices of BK in {32, 64}, a
+//     ring of S LDS stages and 4 or 8 wave64s in a WGM x WGN grid, each wave
+//     owning a BM/WGM x BN/WGN block of C as v_mfma_f32_32x32x16
+//     accumulators in AGPRs (256 fp32 values per lane at 256 x 256 on 4
+//     waves); the configuration is a template parameter and the host picks
+//     one per shape (the default: 256 x 256, BK = 32, 4 stages, 4 waves);
+//   * the stages (4 x 32 KB of the 160 KB LDS at 256 x 256, BK = 32) are
+//     filled by buffer loads that write LDS directly (buffer_load_dwordx4 ...
+//     lds): no staging registers, no LDS store instructions; with S >= 3
+//     stages each slice is requested S - 2 slices before it is used, with 2
+//     stages right after the barrier that frees its stage; one barrier per
+//     slice, before its last k-step;
+//   * A is staged as [BM m][BK k] (k-contiguous, what a 16-bit MFMA operand
+//     holds per lane) and read with ds_read_b128; B stays [BK k][BN n] as in
 //     memory and its MFMA fragments come from ds_read_b64_tr_b16, which hands
 //     each lane one column of a 4 x 16 block of 16-bit values (lane i of a
 //     16-lane group gets element i%4 of the 8 bytes addressed by lane
@@ -61,46 +62,71 @@
 namespace tg {
 namespace {
 
-using tile::NTHREADS;
 using namespace direct;
-constexpr int BK = 32;
-constexpr int STAGES = 4;
 constexpr uint32_t OOB_BUMP = 0x80000000u;        // + offset < 2^31 - 64 KiB -> beyond the operand's buffer
+constexpr int LDS_BYTES = 160 * 1024;             // per CU on gfx950
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-// Everything that follows from the tile size.  Waves form a 2 x 2 grid over
-// the tile; each owns WM x WN = (BM/2) x (BN/2) of C as I x J accumulators
-// of 32 x 32.  Per k-slice and wave: QA direct loads of A (16 rows of 64
-// bytes each) and QB of B (1 KB = RB k-rows each).
-template <int BM_, int BN_>
+// Everything that follows from the configuration: tile BM x BN, k-slice BK,
+// S LDS stages, WGM x WGN waves.  Each wave owns WM x WN = (BM/WGM) x
+// (BN/WGN) of C as I x J accumulators of 32 x 32, and takes KS = BK/16
+// k-steps per slice.  Per k-slice and wave: QA direct loads of A (RPD rows
+// of 2 BK bytes each) and QB of B (1 KB = RB k-rows each).
+template <int BM_, int BN_, int BK_ = 32, int S_ = 4, int WGM_ = 2, int WGN_ = 2>
 struct Cfg {
-    static constexpr int BM = BM_, BN = BN_;
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, S = S_, WGM = WGM_, WGN = WGN_;
     static_assert((BM == 128 || BM == 256) && (BN == 128 || BN == 256), "tile sizes");
-    static constexpr int WM = BM / 2, WN = BN / 2;
+    static_assert(BK == 32 || BK == 64, "k-slice");
+    static constexpr int WAVES = WGM * WGN;
+    static constexpr int THREADS = 64 * WAVES;
+    static constexpr int WM = BM / WGM, WN = BN / WGN;
     static constexpr int I = WM / 32, J = WN / 32;
-    static constexpr int A_BYTES = BM * BK * 2;             // [BM m][32 k]
-    static constexpr int B_BYTES = BK * BN * 2;             // [32 k][BN n]
+    static_assert(I >= 1 && J >= 1, "at least one 32 x 32 block per wave");
+    static constexpr int KS = BK / 16;                      // k-steps per slice
+    static constexpr int ACH = BK / 8;                      // 16-byte chunks per A row of the stage
+    static constexpr int A_ROW = 2 * BK;                    // bytes per row of the A stage
+    static constexpr int A_BYTES = BM * BK * 2;             // [BM m][BK k]
+    static constexpr int B_BYTES = BK * BN * 2;             // [BK k][BN n]
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
     static constexpr int B_ROW = 2 * BN;                    // bytes per k-row of the B stage
-    static constexpr int CPR = BN / 8;                      // 16-byte chunks per B row (and per C row)
-    static constexpr int QA = BM / 64, QB = BN / 64;
+    static constexpr int CPR = BN / 8;                      // 16-byte chunks per B row
+    static constexpr int RPD = 1024 / A_ROW;                // A rows per direct load
+    static constexpr int RB = 1024 / B_ROW;                 // B k-rows per direct load
+    static constexpr int A_ROWS_PER_WAVE = BM / WAVES;
+    static constexpr int B_ROWS_PER_WAVE = BK / WAVES;
+    static constexpr int QA = A_ROWS_PER_WAVE / RPD, QB = B_ROWS_PER_WAVE / RB;
+    static_assert(QA * RPD == A_ROWS_PER_WAVE && QB * RB == B_ROWS_PER_WAVE && QA >= 1 && QB >= 1, "load split");
     static constexpr int D = QA + QB;                       // direct loads per slice per wave
-    static constexpr int RB = 512 / BN;                     // B k-rows per direct load
-    static constexpr int A_ROWS_PER_WAVE = BM / 4;
     static constexpr int READS = I + 2 * J;                 // fragment reads per k-step
     static constexpr int MFMAS = I * J;                     // MFMAs per k-step
-    static constexpr int OCCUPANCY = (STAGES * STAGE_BYTES <= 80 * 1024) ? 2 : 1;   // workgroups per CU
-    static_assert(D % 2 == 0, "loads split over the two k-steps of a slice");
+    static_assert(S >= 2 && S * STAGE_BYTES <= LDS_BYTES, "stages fit LDS");
+    // with S >= 3 stages each k-step of slice t issues D/KS loads of slice
+    // t + S - 1; with 2 stages the last k-step issues all D loads of slice t + 2
+    static_assert(S == 2 ? D <= 2 * MFMAS : (D % KS == 0 && D / KS <= MFMAS), "loads fit the k-steps");
+    static constexpr int OCCUPANCY = (S * STAGE_BYTES <= LDS_BYTES / 2 && WAVES == 4) ? 2 : 1;   // workgroups per CU
+    // this wave's loads pending, when waiting for slice t + 1 at the barrier of
+    // slice t in the steady state: slices t + 2 .. t + S - 2 and the part of
+    // slice t + S - 1 issued before the barrier
+    static constexpr int WAIT_STEADY = S == 2 ? 0 : (S - 3) * D + (KS - 1) * (D / KS);
 };
 
-// A row = 32 k = 4 chunks of 16 B.  A fragment read takes one logical chunk
-// from 32 consecutive rows; with this swizzle any 8 consecutive rows of one
-// parity and any 16 consecutive rows of one residue mod 4 use 4 different
-// slots, which keeps both 32-bank (8 lanes x 16 B) and 64-bank (16 lanes)
-// passes conflict free.
-__device__ __forceinline__ int a_swz(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
+// A row = BK k = ACH chunks of 16 B.  A fragment read takes one logical
+// chunk from 32 consecutive rows.  ACH = 4 (64-byte rows): any 8 consecutive
+// rows of one parity and any 16 consecutive rows of one residue mod 4 use 4
+// different slots; ACH = 8 (128-byte rows, two per 256-byte bank cycle): any
+// 8 consecutive rows (aligned to 8) use 8 different slots and any 16
+// consecutive rows (aligned to 16) 16 different (row parity, slot) pairs.
+// Both keep 32-bank (8 lanes x 16 B) and 64-bank (16 lanes) passes conflict
+// free.
+template <int ACH>
+__device__ __forceinline__ int a_swz(int row) {
+    if constexpr (ACH == 4)
+        return ((row >> 1) ^ (row >> 2)) & 3;
+    else
+        return (row & 7) ^ ((row >> 3) & 1);
+}
 
 // B row = BN n = 32 or 16 chunks.  A transposed read pass touches 4
 // consecutive k-rows (k % 4 = 0..3) and 2 (32-bank pass) or 4 (64-bank pass)
@@ -111,24 +137,24 @@ __device__ __forceinline__ int b_swz(int k) { return ((k & 1) ? 10 : 0) ^ ((k & 
 
 // Per-lane addressing of the D direct loads that fill one stage.  Wave w,
 // lane L:
-//   A load q < QA: tile rows BM/4 w + 16 q + L/4, physical chunk L%4 ->
-//      logical chunk c = L%4 ^ a_swz(row) (8 k); destination
-//      stage + 16 BM w + 1024 q;
-//   B load q < QB: k-row 8 w + RB q + L/CPR, physical chunk L%CPR ->
-//      logical chunk c = L%CPR ^ b_swz(k) (8 n); destination
-//      stage + A_BYTES + 16 BN w + 1024 q.
-// The loads of one operand share m0 (their q = 0 destination) and reach
-// their destination through the instruction offset 1024 q, which is also
-// added to the memory offset; the lane offsets subtract it back.  So that
-// they stay non-negative, the buffers start 4 KB before the operands
-// (offsets are operand offsets + 4096) and are 4 KB longer.
+//   A load q < QA: tile rows A_ROWS_PER_WAVE w + RPD q + L/ACH, physical
+//      chunk L%ACH -> logical chunk c = L%ACH ^ a_swz(row) (8 k);
+//      destination stage + A_BYTES/WAVES w + 1024 q;
+//   B load q < QB: k-row B_ROWS_PER_WAVE w + RB q + L/CPR, physical chunk
+//      L%CPR -> logical chunk c = L%CPR ^ b_swz(k) (8 n); destination
+//      stage + A_BYTES + B_BYTES/WAVES w + 1024 q.
+// Loads of one operand share m0 in groups of four (their destination is m0
+// + 4096 (q/4), the group's m0, plus the instruction offset 1024 (q%4),
+// which is also added to the memory offset; the lane offsets subtract it
+// back).  So that they stay non-negative, the buffers start 4 KB before the
+// operands (offsets are operand offsets + 4096) and are 4 KB longer.
 template <class C>
 struct Dma {
     static constexpr uint32_t SHIFT = 4096;
     i32x4 ra, rb;
-    uint32_t a_off[C::QA];   // buffer offset of this lane's A chunk for load q, k0 = 0, minus 1024 q
-    int a_k;                 // first k of the lane's A chunk within the slice
-    uint32_t b_off[C::QB];   // buffer offset of this lane's B chunk for load q, k0 = 0, minus 1024 q
+    uint32_t a_off[C::QA];   // buffer offset of this lane's A chunk for load q, k0 = 0, minus 1024 (q%4)
+    int a_k[C::QA];          // first k of the lane's A chunk of load q within the slice
+    uint32_t b_off[C::QB];   // buffer offset of this lane's B chunk for load q, k0 = 0, minus 1024 (q%4)
     int b_k[C::QB];          // k-row of load q within the slice
     uint32_t b_row;          // bytes per row of B
     uint32_t m0_a, m0_b;     // LDS destinations of load q = 0 in stage 0
@@ -138,22 +164,24 @@ struct Dma {
         ra = rsrc_words((const char *)g.A - SHIFT, 2u * (uint32_t)g.M * (uint32_t)g.K + SHIFT);
         rb = rsrc_words((const char *)g.B - SHIFT, 2u * (uint32_t)g.K * (uint32_t)g.N + SHIFT);
         K = g.K;
-        const int arow = C::A_ROWS_PER_WAVE * wave + (lane >> 2);
-        const int ac = (lane & 3) ^ a_swz(lane >> 2);
-        a_k = 8 * ac;
+        const int arow = C::A_ROWS_PER_WAVE * wave + (int)((unsigned)lane / C::ACH);
         b_row = 2u * (uint32_t)g.N;
 #pragma unroll
-        for (int q = 0; q < C::QA; ++q)
-            a_off[q] = SHIFT - 1024u * q + 2u * ((uint32_t)(m0 + arow + 16 * q) * (uint32_t)g.K + (uint32_t)a_k);
+        for (int q = 0; q < C::QA; ++q) {
+            const int row = arow + C::RPD * q;   // row within the tile
+            a_k[q] = 8 * ((int)((unsigned)lane % C::ACH) ^ a_swz<C::ACH>(row));
+            a_off[q] = SHIFT - 1024u * (q & 3) +
+                       2u * ((uint32_t)(m0 + row) * (uint32_t)g.K + (uint32_t)a_k[q]);
+        }
 #pragma unroll
         for (int q = 0; q < C::QB; ++q) {
-            const int k = 8 * wave + C::RB * q + (int)((unsigned)lane / C::CPR);
+            const int k = C::B_ROWS_PER_WAVE * wave + C::RB * q + (int)((unsigned)lane / C::CPR);
             const int c = (int)((unsigned)lane % C::CPR) ^ b_swz(k);
             b_k[q] = k;
-            b_off[q] = SHIFT - 1024u * q + (uint32_t)k * b_row + 2u * (uint32_t)(n0 + 8 * c);
+            b_off[q] = SHIFT - 1024u * (q & 3) + (uint32_t)k * b_row + 2u * (uint32_t)(n0 + 8 * c);
         }
-        m0_a = lds0 + 16u * C::BM * (uint32_t)wave;
-        m0_b = lds0 + (uint32_t)C::A_BYTES + 16u * C::BN * (uint32_t)wave;
+        m0_a = lds0 + (uint32_t)(C::A_BYTES / C::WAVES) * (uint32_t)wave;
+        m0_b = lds0 + (uint32_t)C::A_BYTES + (uint32_t)(C::B_BYTES / C::WAVES) * (uint32_t)wave;
     }
 
     // Direct load d (0..D-1) of k-slice kt into LDS stage st: A load d for
@@ -161,20 +189,20 @@ struct Dma {
     // no lane needs the K mask (only the last slice can be partial).
     template <bool FULL, int DI>
     __device__ __forceinline__ void issue_one(int kt, int st) const {
-        const int k0 = kt * BK;
+        const int k0 = kt * C::BK;
         const uint32_t sbase = (uint32_t)st * (uint32_t)C::STAGE_BYTES;
         if constexpr (DI < C::QA) {
             constexpr int q = DI;
             uint32_t off = a_off[q] + 2u * (uint32_t)k0;
             if constexpr (!FULL)
-                off += (k0 + a_k < K) ? 0u : OOB_BUMP;
-            dma16<1024 * q>(ra, off, m0_a + sbase);
+                off += (k0 + a_k[q] < K) ? 0u : OOB_BUMP;
+            dma16<1024 * (q & 3)>(ra, off, m0_a + sbase + 4096u * (q >> 2));
         } else {
             constexpr int q = DI - C::QA;
             uint32_t off = b_off[q] + (uint32_t)k0 * b_row;
             if constexpr (!FULL)
                 off += (k0 + b_k[q] < K) ? 0u : OOB_BUMP;
-            dma16<1024 * q>(rb, off, m0_b + sbase);
+            dma16<1024 * (q & 3)>(rb, off, m0_b + sbase + 4096u * (q >> 2));
         }
     }
 
@@ -183,7 +211,8 @@ struct Dma {
         (issue_one<false, DI>(kt, st), ...);
     }
 
-    // Request k-slice kt into LDS stage st.
+    // Request k-slice kt into LDS stage st (prologue: no slice is partial
+    // there unless it is also the last, which the K mask then covers).
     __device__ __forceinline__ void issue(int kt, int st) const {
         issue_seq(kt, st, std::make_integer_sequence<int, C::D>{});
     }
@@ -198,33 +227,31 @@ struct Dma {
 //      column wn*WN + 32 j + l%32, k = 16 s + 8 (l/32) + 0..7.
 template <class C>
 struct FragAddr {
-    uint32_t a[2][C::I];    // [s][i]
-    uint32_t b[2][C::J];    // [s][j], first read; the second is +4 rows
+    uint32_t a[C::KS][C::I];   // [s][i]
+    uint32_t b[C::J];          // step 0, first read; step s is + 16 s rows, the second read + 4 rows
 
     __device__ __forceinline__ FragAddr(int wm, int wn, int lane) {
         const int lr = lane & 31;
-        const int row0 = wm * C::WM + lr;
-        const int sw = a_swz(lr);                     // a_swz depends on row bits 1..3 only
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
+        for (int i = 0; i < C::I; ++i) {
+            const int row = wm * C::WM + 32 * i + lr;
+            const int sw = a_swz<C::ACH>(row);
 #pragma unroll
-            for (int i = 0; i < C::I; ++i) {
+            for (int s = 0; s < C::KS; ++s) {
                 const int c = 2 * s + (lane >> 5);
-                a[s][i] = 16u * (uint32_t)((row0 + 32 * i) * 4 + (c ^ sw));
+                a[s][i] = (uint32_t)(C::A_ROW * row) + 16u * (uint32_t)(c ^ sw);
             }
+        }
         const int G = lane >> 4;
         const int q = lane & 15;
         const int kr = 8 * (G >> 1) + (q >> 2);      // k-row for s = 0, first read; kr % 4 = q / 4
         const int bsw = b_swz(kr);
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
-#pragma unroll
-            for (int j = 0; j < C::J; ++j) {
-                const int n = wn * C::WN + 32 * j + 16 * (G & 1) + 4 * (q & 3);
-                const int c = (n >> 3) ^ bsw;
-                b[s][j] = (uint32_t)C::A_BYTES + (uint32_t)C::B_ROW * (uint32_t)(kr + 16 * s) + 16u * (uint32_t)c +
-                          8u * (uint32_t)(q & 1);
-            }
+        for (int j = 0; j < C::J; ++j) {
+            const int n = wn * C::WN + 32 * j + 16 * (G & 1) + 4 * (q & 3);
+            const int c = (n >> 3) ^ bsw;
+            b[j] = (uint32_t)C::A_BYTES + (uint32_t)C::B_ROW * (uint32_t)kr + 16u * (uint32_t)c + 8u * (uint32_t)(q & 1);
+        }
     }
 };
 
@@ -250,12 +277,13 @@ __device__ __forceinline__ void read_one(Frag<C> &f, const FragAddr<C> &ad, uint
         f.a[r] = lds_u4(stage + ad.a[s][r]);
     } else {
         const int j = (r - C::I) >> 1;
+        const uint32_t b = stage + ad.b[j] + (uint32_t)(16 * C::B_ROW * s);
         if (((r - C::I) & 1) == 0) {
-            const u32x2 v = lds_tr(stage + ad.b[s][j]);
+            const u32x2 v = lds_tr(b);
             f.b[j].x = v.x;
             f.b[j].y = v.y;
         } else {
-            const u32x2 v = lds_tr(stage + ad.b[s][j] + 4u * (uint32_t)C::B_ROW);
+            const u32x2 v = lds_tr(b + 4u * (uint32_t)C::B_ROW);
             f.b[j].z = v.x;
             f.b[j].w = v.y;
         }
@@ -270,13 +298,13 @@ struct ReadsAfter {
     static constexpr int HI = C::READS <= C::MFMAS ? (Q < C::READS ? Q + 1 : Q) : (Q + 1) * C::READS / C::MFMAS;
 };
 
-// Direct load p (0..D/2-1) of a k-step's half goes after MFMA p*M/(D/2) + 1
-// (M >= 4 MFMAs per k-step, so that stays below M).
-template <class C, int Q>
+// A k-step with H direct loads: load p (0..H-1) goes after MFMA
+// (p*M/H + 1) mod M (M MFMAs per k-step).
+template <class C, int Q, int H>
 struct DmaAfter {
-    static constexpr int H = C::D / 2;
-    static constexpr int find(int p) { return p >= H ? -1 : ((p * C::MFMAS) / H + 1 == Q ? p : find(p + 1)); }
-    static constexpr int P = find(0);
+    static constexpr int pos(int p) { return ((p * C::MFMAS) / H + 1) % C::MFMAS; }
+    static constexpr int find(int p) { return p >= H ? -1 : (pos(p) == Q ? p : find(p + 1)); }
+    static constexpr int P = H > 0 ? find(0) : -1;
 };
 
 template <class C, int R0, int... R>
@@ -286,11 +314,12 @@ __device__ __forceinline__ void read_range(Frag<C> &nxt, const FragAddr<C> &ad, 
 }
 
 // One k-step in a fixed issue order: MFMA Q (A block Q/J x B block Q%J),
-// then the fragment reads of the next step that follow it, then at most one
-// direct load (`dma(p)` for p = 0..D/2-1).  sched_barrier keeps the compiler
-// from regrouping: spreading the direct loads lets the memory pipeline take
-// them while the matrix unit stays busy.
-template <class C, class T, bool READ, bool DMA, int Q, typename DmaFn>
+// then the fragment reads of the next step that follow it, then the direct
+// loads placed after it (`dma(p)`, p = 0..H-1; with H > M some MFMAs are
+// followed by two).  sched_barrier keeps the compiler from regrouping:
+// spreading the direct loads lets the memory pipeline take them while the
+// matrix unit stays busy.
+template <class C, class T, bool READ, int H, int Q, typename DmaFn>
 __device__ __forceinline__ void kstep_one(const Frag<C> &cur, Frag<C> &nxt, f32x16 (&acc)[C::I][C::J],
                                           const FragAddr<C> &ad, uint32_t rstage, int rs, DmaFn &dma) {
     acc[Q / C::J][Q % C::J] = T::mfma32(cur.b[Q % C::J], cur.a[Q / C::J], acc[Q / C::J][Q % C::J]);
@@ -299,22 +328,31 @@ __device__ __forceinline__ void kstep_one(const Frag<C> &cur, Frag<C> &nxt, f32x
         if constexpr (HI > LO)
             read_range<C, LO>(nxt, ad, rstage, rs, std::make_integer_sequence<int, HI - LO>{});
     }
-    if constexpr (DMA && DmaAfter<C, Q>::P >= 0)
-        dma(std::integral_constant<int, DmaAfter<C, Q>::P>{});
+    if constexpr (H <= C::MFMAS) {
+        if constexpr (DmaAfter<C, Q, H>::P >= 0)
+            dma(std::integral_constant<int, DmaAfter<C, Q, H>::P>{});
+    } else {   // two per MFMA for the first H - M MFMAs
+        constexpr int P0 = Q < H - C::MFMAS ? 2 * Q : (H - C::MFMAS) + Q;
+        dma(std::integral_constant<int, P0>{});
+        if constexpr (Q < H - C::MFMAS)
+            dma(std::integral_constant<int, P0 + 1>{});
+    }
     __builtin_amdgcn_sched_barrier(0);
 }
 
-template <class C, class T, bool READ, bool DMA, typename DmaFn, int... Q>
+template <class C, class T, bool READ, int H, typename DmaFn, int... Q>
 __device__ __forceinline__ void kstep_seq(const Frag<C> &cur, Frag<C> &nxt, f32x16 (&acc)[C::I][C::J],
                                           const FragAddr<C> &ad, uint32_t rstage, int rs, DmaFn &dma,
                                           std::integer_sequence<int, Q...>) {
-    (kstep_one<C, T, READ, DMA, Q>(cur, nxt, acc, ad, rstage, rs, dma), ...);
+    (kstep_one<C, T, READ, H, Q>(cur, nxt, acc, ad, rstage, rs, dma), ...);
 }
 
-template <class C, class T, bool READ, bool DMA, typename DmaFn>
+// One k-step: MFMAs on `cur`; with READ the fragments of k-step rs of the
+// stage at rstage are read into `nxt`; H direct loads through dma(p).
+template <class C, class T, bool READ, int H, typename DmaFn>
 __device__ __forceinline__ void kstep(const Frag<C> &cur, Frag<C> &nxt, f32x16 (&acc)[C::I][C::J],
                                       const FragAddr<C> &ad, uint32_t rstage, int rs, DmaFn dma) {
-    kstep_seq<C, T, READ, DMA>(cur, nxt, acc, ad, rstage, rs, dma, std::make_integer_sequence<int, C::MFMAS>{});
+    kstep_seq<C, T, READ, H>(cur, nxt, acc, ad, rstage, rs, dma, std::make_integer_sequence<int, C::MFMAS>{});
 }
 
 // Shapes with K % 8 != 0 or N % 8 != 0 (GEN): the direct loads still move
@@ -333,13 +371,13 @@ __device__ __forceinline__ void kstep(const Frag<C> &cur, Frag<C> &nxt, f32x16 (
 // n = N elsewhere only feed columns that are never stored.
 template <class C, class T>
 __device__ __forceinline__ void fix_last_slice(const GemmArgs &g, int m0, int n0, int kl, uint32_t stage) {
-    const int k0 = kl * BK;
+    const int k0 = kl * C::BK;
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     if (g.K % 8 != 0 && lane < C::A_ROWS_PER_WAVE) {
         const __amdgpu_buffer_rsrc_t ra = tile::buffer_of(g.A, 2u * (uint32_t)g.M * (uint32_t)g.K);
         const int r = C::A_ROWS_PER_WAVE * wave + lane;   // tile row r was loaded by this wave
-        const int cp = (g.K - k0) >> 3;          // the crossing chunk (< 4: the slice holds K - 1)
+        const int cp = (g.K - k0) >> 3;          // the crossing chunk (< ACH: the slice holds K - 1)
         const int v = (g.K - k0) & 7;            // its elements below K
         const uint32_t row = (uint32_t)(m0 + r); // rows >= M read zero (beyond the buffer)
         const uint32_t base = 2u * (row * (uint32_t)g.K + (uint32_t)(k0 + 8 * cp));
@@ -348,11 +386,12 @@ __device__ __forceinline__ void fix_last_slice(const GemmArgs &g, int m0, int n0
         for (int q = 0; q < 8; ++q)
             e[q] = q < v ? __builtin_amdgcn_raw_buffer_load_b16(ra, (int)(base + 2u * q), 0, 0) : (uint16_t)0;
         const u32x4 chunk = {pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]), pack2(e[6], e[7])};
-        *(__attribute__((address_space(3))) u32x4 *)(uintptr_t)(stage + 64u * r + 16u * (cp ^ a_swz(r))) = chunk;
+        *(__attribute__((address_space(3))) u32x4 *)(uintptr_t)(stage + (uint32_t)(C::A_ROW * r) +
+                                                                16u * (uint32_t)(cp ^ a_swz<C::ACH>(r))) = chunk;
     }
     if (g.N % 8 != 0 && n0 <= g.N - 1 && g.N - 1 < n0 + C::BN) {
-        const int r = g.K - 1 - k0;              // B's last row, loaded by wave r / 8
-        if (tid == 64 * (r >> 3)) {
+        const int r = g.K - 1 - k0;              // B's last row, loaded by wave r / B_ROWS_PER_WAVE
+        if (tid == 64 * (r / C::B_ROWS_PER_WAVE)) {
             const __amdgpu_buffer_rsrc_t rb = tile::buffer_of(g.B, 2u * (uint32_t)g.K * (uint32_t)g.N);
             const int c = (g.N - 1 - n0) >> 3;
             const uint32_t base = 2u * ((uint32_t)(g.K - 1) * (uint32_t)g.N + (uint32_t)(n0 + 8 * c));
@@ -389,7 +428,8 @@ struct WaveStage {
     static constexpr int CPRW = C::WN / 8;                     // 16-byte chunks per buffer row
     static constexpr int BUF = 32 * C::WN * 2;                 // bytes per wave: 32 rows x WN
     static constexpr int PER_STAGE = C::STAGE_BYTES / BUF;     // buffers per stage
-    static_assert(PER_STAGE >= 2 && (4 + PER_STAGE - 1) / PER_STAGE <= 3, "wave buffers fit 3 stages");
+    static_assert(PER_STAGE >= 1 && (C::WAVES + PER_STAGE - 1) / PER_STAGE <= C::S - 1,
+                  "wave buffers fit the stages other than the last slice's");
     static __device__ __forceinline__ uint32_t swz(int row) {
         return (uint32_t)((row ^ (row / CPRW)) & (CPRW - 1));
     }
@@ -403,8 +443,8 @@ __device__ __forceinline__ void store_tile_wave(const GemmArgs &args, const f32x
     const int M = args.M, N = args.N;
     const int lr = lane & 31;
     const int lh = lane >> 5;
-    // the stage of the last slice is (nk - 1) & 3; the next ones are free
-    const uint32_t buf = lds0 + (uint32_t)(((nk + wave / W::PER_STAGE) & 3) * C::STAGE_BYTES) +
+    // the stage of the last slice is (nk - 1) % S; the next ones are free
+    const uint32_t buf = lds0 + (uint32_t)(((nk + wave / W::PER_STAGE) % C::S) * C::STAGE_BYTES) +
                          (uint32_t)((wave % W::PER_STAGE) * W::BUF);
     // The bias of all J four-column groups of this lane, requested at once
     // (range-checked: columns past N read zero).
@@ -480,24 +520,47 @@ __device__ __forceinline__ void store_tile_wave(const GemmArgs &args, const f32x
     }
 }
 
+// f(integral_constant<int, I>) for I = 0 .. N-1, in order.
+template <typename F, int... I>
+__device__ __forceinline__ void for_each_index(F &&f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+
+// Prologue wait for slice 0 when `issued` slices (1..P) were requested:
+// (issued - 1) D loads of this wave are younger than slice 0's.
+template <int D, int P>
+__device__ __forceinline__ void wait_prologue(int issued) {
+    if constexpr (P <= 1) {
+        wait_vmcnt<0>();
+    } else {
+        if (issued >= P)
+            wait_vmcnt<(P - 1) * D>();
+        else
+            wait_prologue<D, P - 1>(issued);
+    }
+}
+
 // Persistent: the grid has at most OCCUPANCY workgroups per CU, and
 // workgroup g computes tiles g, g + G, g + 2G, ... (G = grid size, a
 // multiple of the 8 XCDs when the tile count allows, so every tile of a
 // workgroup stays on its XCD in the raster), which removes the dispatch gap
 // between tiles.
 template <class C, class T, int EPI, bool GEN>
-__global__ __launch_bounds__(NTHREADS, C::OCCUPANCY) void gemm_tiled_kernel(GemmArgs args) {
-    __shared__ __attribute__((aligned(16))) u32x4 smem[STAGES * C::STAGE_BYTES / 16];
+__global__ __launch_bounds__(C::THREADS, C::OCCUPANCY) void gemm_tiled_kernel(GemmArgs args) {
+    __shared__ __attribute__((aligned(16))) u32x4 smem[C::S * C::STAGE_BYTES / 16];
+    constexpr int D = C::D, S = C::S, KS = C::KS;
+    // slice t requests slice t + LEAD: S - 1 with S >= 3 stages (before and
+    // after its barrier), 2 with two stages (after its barrier)
+    constexpr int LEAD = S == 2 ? 2 : S - 1;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wm = wave >> 1;
-    const int wn = wave & 1;
+    const int wm = wave / C::WGN;
+    const int wn = wave % C::WGN;
     const uint32_t lds0 = lds_address(smem);
     auto stage = [&](int st) { return lds0 + (uint32_t)st * (uint32_t)C::STAGE_BYTES; };
     const int tiles_m = (args.M + C::BM - 1) / C::BM;
     const int tiles_n = (args.N + C::BN - 1) / C::BN;
     const int total = tiles_m * tiles_n;
-    const int nk = (args.K + BK - 1) / BK;
-    constexpr int D = C::D;
+    const int nk = (args.K + C::BK - 1) / C::BK;
 
     for (int w = blockIdx.x; w < total; w += gridDim.x) {
         // The lane id is made opaque per tile so that the per-lane addresses
@@ -507,7 +570,7 @@ __global__ __launch_bounds__(NTHREADS, C::OCCUPANCY) void gemm_tiled_kernel(Gemm
         asm volatile("" : "+v"(lane));
         const FragAddr<C> fad(wm, wn, lane);
         int tm, tn;
-        tile::tile_of_index(tiles_m, tiles_n, w, tm, tn);
+        tile::tile_of_index(tiles_m, tiles_n, w, args.group_m, tm, tn);
         const int m0 = tm * C::BM;
         const int n0 = tn * C::BN;
         const Dma<C> dma(args, m0, n0, wave, lane, lds0);
@@ -519,91 +582,98 @@ __global__ __launch_bounds__(NTHREADS, C::OCCUPANCY) void gemm_tiled_kernel(Gemm
             for (int j = 0; j < C::J; ++j)
                 acc[i][j] = f32x16{};
 
-        Frag<C> f0, f1;
-        // Prologue: request slices 0..2, wait for slice 0.  The previous
-        // tile's C stores are older than these loads, so the same counts hold.
+        Frag<C> f[2];
+        // Prologue: request slices 0 .. min(LEAD, nk) - 1, wait for slice 0.
+        // The previous tile's C stores only add to the count: loads complete
+        // in order, so slice 0 has landed once no more than the younger
+        // loads are pending.
         if (nk > 0) {
-            dma.issue(0, 0);
-            if (nk > 1)
-                dma.issue(1, 1);
-            if (nk > 2) {
-                dma.issue(2, 2);
-                wait_vmcnt<2 * D>();
-            } else if (nk > 1) {
-                wait_vmcnt<D>();
-            } else {
-                wait_vmcnt<0>();
-                if constexpr (GEN)
+#pragma unroll
+            for (int p = 0; p < LEAD; ++p)
+                if (p < nk)
+                    dma.issue(p, p);
+            const int issued = nk < LEAD ? nk : LEAD;
+            wait_prologue<D, LEAD>(issued);
+            if constexpr (GEN)
+                if (nk == 1)
                     fix_last_slice<C, T>(args, m0, n0, 0, stage(0));
-            }
         }
         __syncthreads();
         if (nk > 0) {
 #pragma unroll
             for (int r = 0; r < C::READS; ++r)
-                read_one<C>(f0, fad, stage(0), 0, r);
+                read_one<C>(f[0], fad, stage(0), 0, r);
         }
 
-        // Slice t in stage t%4, fragments of its first k-step already in f0:
-        //   step 0: MFMAs on f0, reads of step 1 into f1, first half of the
-        //           direct loads of slice t+3 into stage (t+3)%4 (that stage was
-        //           last read in slice t-1, before the previous barrier);
-        //   wait until this wave's loads of slice t+1 have landed, barrier
-        //           (everyone's have, and everyone's reads of slice t are done);
-        //   step 1: MFMAs on f1, reads of step 0 of slice t+1 into f0, second
-        //           half of the direct loads of slice t+3.
-        // Loads issued after slice t+1's when waiting: all D of slice t+2 and
-        // the first D/2 of slice t+3, hence vmcnt(3D/2) in the steady state.
+        // Slice t in stage t % S, fragments of its first k-step already in f[0]:
+        //   k-steps 0 .. KS-2: MFMAs on f[s % 2], reads of step s + 1 into
+        //       f[(s + 1) % 2] and (S >= 3) D/KS direct loads each of slice
+        //       t + S - 1 into stage (t - 1) % S, last read in slice t - 1,
+        //       before its barrier;
+        //   wait until this wave's loads of slice t + 1 have landed, barrier
+        //       (everyone's have, and everyone's reads of slice t are done);
+        //   k-step KS-1: MFMAs, reads of step 0 of slice t + 1 into f[0], and
+        //       the last D/KS loads of slice t + S - 1 (S >= 3) or all D loads
+        //       of slice t + 2 into stage t % 2, just freed (S == 2).
         // ISSUE: 0 = no loads, 1 = loads of a full slice, 2 = loads of the
-        // (possibly partial) last slice.
-        auto slice = [&](int t, auto issue, auto wait, auto next) __attribute__((always_inline)) {
-            const uint32_t st = stage(t & 3);
-            constexpr int ISSUE_KIND = decltype(issue)::value;
-            constexpr bool ISSUE = ISSUE_KIND != 0;
-            constexpr bool FULL = ISSUE_KIND == 1;
+        // (possibly partial) last slice.  WAIT: this wave's loads younger than
+        // slice t + 1's at the barrier.  FIX: slice t + 1 is the last one of a
+        // GEN shape.
+        auto slice = [&](int t, auto issue, auto wait, auto next, auto fix) __attribute__((always_inline)) {
+            constexpr int IK = decltype(issue)::value;
+            constexpr bool FULL = IK == 1;
             constexpr bool NEXT = decltype(next)::value;
-            const int kt = t + 3;
-            auto dma_lo = [&](auto d) __attribute__((always_inline)) {
-                dma.template issue_one<FULL, decltype(d)::value>(kt, kt & 3);
+            constexpr int HP = (S >= 3 && IK != 0) ? D / KS : 0;            // loads per step before the barrier
+            constexpr int HL = IK == 0 ? 0 : (S >= 3 ? D / KS : D);         // loads in the last step
+            constexpr int BL = S >= 3 ? (KS - 1) * (D / KS) : 0;            // first load index of the last step
+            const uint32_t st = stage(t % S);
+            const int kt = t + LEAD;
+            const int kst = kt % S;
+            auto pre = [&](auto s) __attribute__((always_inline)) {
+                constexpr int SI = decltype(s)::value;
+                auto dma_s = [&](auto p) __attribute__((always_inline)) {
+                    dma.template issue_one<FULL, SI * HP + decltype(p)::value>(kt, kst);
+                };
+                kstep<C, T, true, HP>(f[SI & 1], f[(SI + 1) & 1], acc, fad, st, SI + 1, dma_s);
             };
-            auto dma_hi = [&](auto d) __attribute__((always_inline)) {
-                dma.template issue_one<FULL, decltype(d)::value + D / 2>(kt, kt & 3);
-            };
-            kstep<C, T, true, ISSUE>(f0, f1, acc, fad, st, 1, dma_lo);
+            for_each_index(pre, std::make_integer_sequence<int, KS - 1>{});
             if constexpr (NEXT) {
                 wait_vmcnt<decltype(wait)::value>();
-                // with nothing left in flight, slice t + 1 is the last one
-                if constexpr (GEN && decltype(wait)::value == 0)
-                    fix_last_slice<C, T>(args, m0, n0, t + 1, stage((t + 1) & 3));
+                if constexpr (GEN && decltype(fix)::value)
+                    fix_last_slice<C, T>(args, m0, n0, t + 1, stage((t + 1) % S));
                 __syncthreads();
             }
-            kstep<C, T, NEXT, ISSUE>(f1, f0, acc, fad, stage((t + 1) & 3), 0, dma_hi);
+            auto dma_l = [&](auto p) __attribute__((always_inline)) {
+                dma.template issue_one<FULL, BL + decltype(p)::value>(kt, kst);
+            };
+            kstep<C, T, NEXT, HL>(f[(KS - 1) & 1], f[0], acc, fad, stage((t + 1) % S), 0, dma_l);
         };
         using yes = std::true_type;
         using no = std::false_type;
-        using none = std::integral_constant<int, 0>;
         using full = std::integral_constant<int, 1>;
         using last = std::integral_constant<int, 2>;
-        using w_steady = std::integral_constant<int, 3 * D / 2>;
-        using w_two = std::integral_constant<int, D>;
-        using w0 = std::integral_constant<int, 0>;
+        using w_steady = std::integral_constant<int, C::WAIT_STEADY>;
         int t = 0;
-        for (; t + 4 < nk; ++t)
-            slice(t, full{}, w_steady{}, yes{});
-        if (t + 3 < nk) {
-            slice(t, last{}, w_steady{}, yes{});
+        for (; t + LEAD < nk - 1; ++t)
+            slice(t, full{}, w_steady{}, yes{}, no{});
+        if (t + LEAD == nk - 1) {
+            slice(t, last{}, w_steady{}, yes{}, no{});
             ++t;
         }
-        if (t + 3 == nk && t < nk) {
-            slice(t, none{}, w_two{}, yes{});
-            ++t;
-        }
-        if (t + 2 == nk && t < nk) {
-            slice(t, none{}, w0{}, yes{});
-            ++t;
-        }
-        if (t + 1 == nk)
-            slice(t, none{}, w0{}, no{});
+        // the last LEAD slices request nothing: slice nk - 1 - j waits for
+        // its successor with slices t + 2 .. nk - 1 (j - 1 of them) pending
+        auto tail = [&](auto jj) __attribute__((always_inline)) {
+            constexpr int J = LEAD - 1 - decltype(jj)::value;
+            if (t == nk - 1 - J) {
+                if constexpr (J == 0)
+                    slice(t, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, no{}, no{});
+                else
+                    slice(t, std::integral_constant<int, 0>{}, std::integral_constant<int, (J - 1) * D>{}, yes{},
+                          std::integral_constant<bool, J == 1>{});
+                ++t;
+            }
+        };
+        for_each_index(tail, std::make_integer_sequence<int, LEAD>{});
 
         store_tile_wave<C, T, EPI, !GEN>(args, acc, m0, n0, wm, wn, wave, lane, lds0, nk);
         // every wave is done reading LDS before the next tile's loads land
@@ -614,9 +684,9 @@ __global__ __launch_bounds__(NTHREADS, C::OCCUPANCY) void gemm_tiled_kernel(Gemm
 template <class C, class T, int EPI>
 hipError_t launch_typed(const GemmArgs &a, bool gen, int grid, hipStream_t stream) {
     if (gen)
-        hipLaunchKernelGGL((gemm_tiled_kernel<C, T, EPI, true>), dim3(grid), dim3(NTHREADS), 0, stream, a);
+        hipLaunchKernelGGL((gemm_tiled_kernel<C, T, EPI, true>), dim3(grid), dim3(C::THREADS), 0, stream, a);
     else
-        hipLaunchKernelGGL((gemm_tiled_kernel<C, T, EPI, false>), dim3(grid), dim3(NTHREADS), 0, stream, a);
+        hipLaunchKernelGGL((gemm_tiled_kernel<C, T, EPI, false>), dim3(grid), dim3(C::THREADS), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -642,24 +712,52 @@ hipError_t launch_cfg(int dtype, int epi, const GemmArgs &a, bool aligned, int n
                       : launch_epi<C, BF16>(epi, a, !aligned, grid, stream);
 }
 
+// The configurations of TileCfg: tile, k-slice, stages, waves.
+template <int TILES>
+struct CfgOf;
+template <> struct CfgOf<TILES_256x256> { using type = Cfg<256, 256, 32, 4>; };
+template <> struct CfgOf<TILES_256x128> { using type = Cfg<256, 128, 32, 4>; };
+template <> struct CfgOf<TILES_128x256> { using type = Cfg<128, 256, 32, 4>; };
+template <> struct CfgOf<TILES_128x128> { using type = Cfg<128, 128, 32, 4>; };
+template <> struct CfgOf<TILES_256x256_K64> { using type = Cfg<256, 256, 64, 2>; };
+template <> struct CfgOf<TILES_256x128_K64> { using type = Cfg<256, 128, 64, 3>; };
+template <> struct CfgOf<TILES_128x256_K64> { using type = Cfg<128, 256, 64, 3>; };
+template <> struct CfgOf<TILES_128x128_K64> { using type = Cfg<128, 128, 64, 2>; };
+template <> struct CfgOf<TILES_256x256_W8> { using type = Cfg<256, 256, 32, 4, 2, 4>; };
+
 }  // namespace
 
 int tiled_occupancy(int tiles) {
     switch (tiles) {
-    case TILES_256x128: return Cfg<256, 128>::OCCUPANCY;
-    case TILES_128x256: return Cfg<128, 256>::OCCUPANCY;
-    case TILES_128x128: return Cfg<128, 128>::OCCUPANCY;
-    default: return Cfg<256, 256>::OCCUPANCY;
+    case TILES_256x128: return CfgOf<TILES_256x128>::type::OCCUPANCY;
+    case TILES_128x256: return CfgOf<TILES_128x256>::type::OCCUPANCY;
+    case TILES_128x128: return CfgOf<TILES_128x128>::type::OCCUPANCY;
+    case TILES_256x256_K64: return CfgOf<TILES_256x256_K64>::type::OCCUPANCY;
+    case TILES_256x128_K64: return CfgOf<TILES_256x128_K64>::type::OCCUPANCY;
+    case TILES_128x256_K64: return CfgOf<TILES_128x256_K64>::type::OCCUPANCY;
+    case TILES_128x128_K64: return CfgOf<TILES_128x128_K64>::type::OCCUPANCY;
+    case TILES_256x256_W8: return CfgOf<TILES_256x256_W8>::type::OCCUPANCY;
+    default: return CfgOf<TILES_256x256>::type::OCCUPANCY;
     }
 }
 
 hipError_t launch_tiled_vec(int dtype, int epi, const GemmArgs &a, bool aligned, int tiles, int num_cu,
                             hipStream_t stream) {
     switch (tiles) {
-    case TILES_256x128: return launch_cfg<Cfg<256, 128>>(dtype, epi, a, aligned, num_cu, stream);
-    case TILES_128x256: return launch_cfg<Cfg<128, 256>>(dtype, epi, a, aligned, num_cu, stream);
-    case TILES_128x128: return launch_cfg<Cfg<128, 128>>(dtype, epi, a, aligned, num_cu, stream);
-    default: return launch_cfg<Cfg<256, 256>>(dtype, epi, a, aligned, num_cu, stream);
+    case TILES_256x128: return launch_cfg<CfgOf<TILES_256x128>::type>(dtype, epi, a, aligned, num_cu, stream);
+    case TILES_128x256: return launch_cfg<CfgOf<TILES_128x256>::type>(dtype, epi, a, aligned, num_cu, stream);
+    case TILES_128x128: return launch_cfg<CfgOf<TILES_128x128>::type>(dtype, epi, a, aligned, num_cu, stream);
+    case TILES_256x256_K64:
+        return launch_cfg<CfgOf<TILES_256x256_K64>::type>(dtype, epi, a, aligned, num_cu, stream);
+    case TILES_256x128_K64:
+        return launch_cfg<CfgOf<TILES_256x128_K64>::type>(dtype, epi, a, aligned, num_cu, stream);
+    case TILES_128x256_K64:
+        return launch_cfg<CfgOf<TILES_128x256_K64>::type>(dtype, epi, a, aligned, num_cu, stream);
+    case TILES_128x128_K64:
+        return launch_cfg<CfgOf<TILES_128x128_K64>::type>(dtype, epi, a, aligned, num_cu, stream);
+    case TILES_256x256_W8:
+        return launch_cfg<CfgOf<TILES_256x256_W8>::type>(dtype, epi, a, aligned, num_cu, stream);
+    default: return launch_cfg<CfgOf<TILES_256x256>::type>(dtype, epi, a, aligned, num_cu, stream);
     }
 }
 

@@ -94,7 +94,7 @@ bool skinny_ok(int64_t M, int64_t N, int64_t K, const void *A, const void *B, co
 // 2 GiB less 64 KiB.  Any shape and any 2-byte alignment within that.
 bool tiled_fits(int64_t M, int64_t N, int64_t K) {
     const int64_t limit = (int64_t(1) << 31) - 65536;
-    return 2 * (M + 256) * K < limit && 2 * (K + 32) * (N + 256) < limit;
+    return 2 * (M + 256) * K < limit && 2 * (K + 64) * (N + 256) < limit;
 }
 
 // The tiled kernel's instance without last-slice fix-ups and with 8-byte
@@ -122,42 +122,55 @@ int num_cu_of(hipStream_t stream) {
 }
 
 // Tile configuration for TG_TILES_AUTO: the one with the least predicted
-// time.  The persistent grid spreads the tiles evenly over the CUs, so the
-// busiest CU computes n = ceil(tiles / CUs) of them; n tiles of s = BM x BN
-// outputs take s / r_single when n == 1 and n s / r_full otherwise.  r_single
-// is the configuration's per-CU throughput with one tile per CU, r_full with
-// many (several workgroups per CU where the occupancy allows), both relative
-// to r_full of the 256 x 256 tile and measured on one MI355X by a sweep of
-// all configurations over such shapes (bench.py --sweep).  K only scales
-// every configuration alike.  Ties go to the larger tile.
+// time.  The persistent grid runs the tiles in rounds of one (two for the
+// 128 x 128 tiles) workgroup per CU; a round of one tile per CU on every CU
+// takes a1 + b1 K, a round with two on some CUs a2 + b2 K, and a round on a
+// fraction u of the CUs (1 - kappa (1 - u)) of the full-load time (less
+// contention for caches and memory); rounds after the first take phi times
+// longer, and misaligned shapes (K or N not a multiple of 8, or unaligned
+// pointers) rho times longer.  The parameters come from a sweep of every
+// configuration on one MI355X (bench.py --sweep: one tile per CU at two K,
+// two per CU, a quarter of the CUs, the 8192-cube and a ragged shape); only
+// their ratios between configurations matter.  A later configuration must
+// beat the best earlier one by 2 % to be chosen, so that timing noise in the
+// sweep does not decide between near-equal ones.
 struct TileChoice {
     tg_tiles tiles;
-    int bm, bn;
-    double r_single, r_full;
+    int bm, bn, occ;
+    double a1, b1, a2, b2, kappa, phi, rho;
 };
 constexpr TileChoice kTileChoices[] = {
-    {TG_TILES_256x256, 256, 256, 1.00, 1.00},
-    {TG_TILES_256x128, 256, 128, 0.83, 0.74},
-    {TG_TILES_128x256, 128, 256, 0.88, 0.90},
-    {TG_TILES_128x128, 128, 128, 0.76, 0.68},
+#include "tg_tile_model.inc"
 };
 constexpr int kDefaultCUs = 256;
 
-double predicted_time(const TileChoice &c, int64_t M, int64_t N, int num_cu) {
-    const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
-    const int64_t n = (tiles + num_cu - 1) / num_cu;
-    const double s = double(c.bm) * c.bn;
-    return n <= 1 ? s / c.r_single : double(n) * s / c.r_full;
+double predicted_time(const TileChoice &c, int64_t M, int64_t N, int64_t K, int num_cu, bool aligned) {
+    int64_t left = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
+    const int64_t per_round = int64_t(num_cu) * c.occ;
+    double t = 0.0;
+    int rounds = 0;
+    while (left > 0) {
+        const int64_t busy = left < per_round ? left : per_round;
+        if (busy > num_cu)
+            t += c.a2 + c.b2 * double(K);
+        else
+            t += (c.a1 + c.b1 * double(K)) * (1.0 - c.kappa * (1.0 - double(busy) / double(num_cu)));
+        left -= busy;
+        ++rounds;
+    }
+    if (rounds > 1)
+        t *= c.phi;
+    return aligned ? t : t * c.rho;
 }
 
-tg_tiles auto_tiles(int64_t M, int64_t N, int num_cu) {
+tg_tiles auto_tiles(int64_t M, int64_t N, int64_t K, int num_cu, bool aligned) {
     if (num_cu <= 0)
         num_cu = kDefaultCUs;
-    tg_tiles pick = TG_TILES_256x256;
-    double best = predicted_time(kTileChoices[0], M, N, num_cu);
+    tg_tiles pick = kTileChoices[0].tiles;
+    double best = predicted_time(kTileChoices[0], M, N, K, num_cu, aligned);
     for (const TileChoice &c : kTileChoices) {
-        const double t = predicted_time(c, M, N, num_cu);
-        if (t < best * (1.0 - 1e-9)) {
+        const double t = predicted_time(c, M, N, K, num_cu, aligned);
+        if (t < best * 0.98) {
             best = t;
             pick = c.tiles;
         }
@@ -211,12 +224,17 @@ int auto_splits(int64_t N, int64_t K, int num_cu) {
     return s > 1 ? static_cast<int>(s) : 1;
 }
 
+constexpr int kDefaultGroupM = 4;
+constexpr int kMaxGroupM = 64;
+
 tg_status run_gemm(tg_path path, tg_tiles tiles, int64_t M, int64_t N, int64_t K, tg_dtype dtype, const void *A,
                    const void *B, const void *bias, tg_epilogue epilogue, void *C, void *stream,
-                   int splits = 1, void *workspace = nullptr, int64_t workspace_bytes = 0) {
+                   int splits = 1, void *workspace = nullptr, int64_t workspace_bytes = 0, int group_m = 0) {
     if (path != TG_PATH_AUTO && path != TG_PATH_TILED && path != TG_PATH_TILED_GENERIC && path != TG_PATH_SKINNY)
         return TG_ERR_INVALID_ARG;
-    if (tiles < TG_TILES_AUTO || tiles > TG_TILES_128x128)
+    if (tiles < TG_TILES_AUTO || tiles > tg::TILES_LAST)
+        return TG_ERR_INVALID_ARG;
+    if (group_m < 0 || group_m > kMaxGroupM)
         return TG_ERR_INVALID_ARG;
     const Checked c = check_args(M, N, K, dtype, A, B, bias, epilogue, C);
     if (c.status != TG_OK || c.noop)
@@ -231,6 +249,7 @@ tg_status run_gemm(tg_path path, tg_tiles tiles, int64_t M, int64_t N, int64_t K
     a.M = static_cast<int>(M);
     a.N = static_cast<int>(N);
     a.K = static_cast<int>(K);
+    a.group_m = group_m > 0 ? group_m : kDefaultGroupM;
     a.A = static_cast<const uint16_t *>(A);
     a.B = static_cast<const uint16_t *>(B);
     a.bias = static_cast<const uint16_t *>(bias);
@@ -255,9 +274,10 @@ tg_status run_gemm(tg_path path, tg_tiles tiles, int64_t M, int64_t N, int64_t K
         e = tg::launch_skinny(dtype, epilogue, a, tg::split_ws(workspace, slabs, splits), s);
     } else if (path == TG_PATH_TILED) {
         const int cus = num_cu_of(s);
+        const bool al = tiled_aligned(N, K, A, B, bias, C);
         if (tiles == TG_TILES_AUTO)
-            tiles = auto_tiles(M, N, cus);
-        e = tg::launch_tiled_vec(dtype, epilogue, a, tiled_aligned(N, K, A, B, bias, C), tiles, cus, s);
+            tiles = auto_tiles(M, N, K, cus, al);
+        e = tg::launch_tiled_vec(dtype, epilogue, a, al, tiles, cus, s);
     } else {
         e = tg::launch_tiled_generic(dtype, epilogue, a, s);
     }
@@ -278,10 +298,18 @@ TG_EXPORT tg_status tg_gemm_tiled(tg_tiles tiles, int64_t M, int64_t N, int64_t 
     return run_gemm(TG_PATH_TILED, tiles, M, N, K, dtype, A, B, bias, epilogue, C, stream);
 }
 
+TG_EXPORT tg_status tg_gemm_tiled_grouped(tg_tiles tiles, int group_m, int64_t M, int64_t N, int64_t K,
+                                          tg_dtype dtype, const void *A, const void *B, const void *bias,
+                                          tg_epilogue epilogue, void *C, void *stream) {
+    if (group_m < 0 || group_m > kMaxGroupM)
+        return TG_ERR_INVALID_ARG;
+    return run_gemm(TG_PATH_TILED, tiles, M, N, K, dtype, A, B, bias, epilogue, C, stream, 1, nullptr, 0, group_m);
+}
+
 TG_EXPORT tg_status tg_gemm_tiles_plan(int64_t M, int64_t N, int64_t K, int num_cu, tg_tiles *tiles_out) {
     if (tiles_out == nullptr || M < 0 || N < 0 || K < 0)
         return TG_ERR_INVALID_ARG;
-    *tiles_out = auto_tiles(M, N, num_cu);
+    *tiles_out = auto_tiles(M, N, K, num_cu, K % 8 == 0 && N % 8 == 0);
     return TG_OK;
 }
 
@@ -405,6 +433,7 @@ TG_EXPORT tg_status tg_gemm_split_static(int splits, int64_t M, int64_t N, int64
     a.M = static_cast<int>(M);
     a.N = static_cast<int>(N);
     a.K = static_cast<int>(K);
+    a.group_m = kDefaultGroupM;
     a.A = static_cast<const uint16_t *>(A);
     a.B = static_cast<const uint16_t *>(B);
     a.bias = static_cast<const uint16_t *>(bias);
@@ -533,6 +562,7 @@ tg_status run_w4(int64_t M, int64_t N, int64_t K, tg_dtype dtype, const void *A,
     a.M = static_cast<int>(M);
     a.N = static_cast<int>(N);
     a.K = static_cast<int>(K);
+    a.group_m = kDefaultGroupM;
     a.A = static_cast<const uint16_t *>(A);
     a.B = nullptr;
     a.bias = static_cast<const uint16_t *>(bias);

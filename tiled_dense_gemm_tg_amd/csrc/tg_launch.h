@@ -10,6 +10,7 @@ namespace tg {
 // is at most 4 GiB (2^31 16-bit elements).
 struct GemmArgs {
     int M, N, K;
+    int group_m;           // tiled raster: tile rows per group (>= 1)
     const uint16_t *A;     // M x K row-major
     const uint16_t *B;     // K x N row-major
     const uint16_t *bias;  // N entries or nullptr
@@ -19,11 +20,22 @@ struct GemmArgs {
 // dtype: 0 fp16, 1 bf16; epi: 0 none, 1 bias, 2 bias + GELU(tanh).
 
 // Tile configurations of the direct-load kernel (values as tg_tiles in
-// tg_gemm.h).
-enum TileCfg { TILES_256x256 = 1, TILES_256x128 = 2, TILES_128x256 = 3, TILES_128x128 = 4 };
+// tg_gemm.h): tile BM x BN, k-slice BK, LDS stages, waves.
+enum TileCfg {
+    TILES_256x256 = 1,       // BK 32, 4 stages, 4 waves
+    TILES_256x128 = 2,       // BK 32, 4 stages, 4 waves
+    TILES_128x256 = 3,       // BK 32, 4 stages, 4 waves
+    TILES_128x128 = 4,       // BK 32, 4 stages, 4 waves, 2 workgroups per CU
+    TILES_256x256_K64 = 5,   // BK 64, 2 stages, 4 waves
+    TILES_256x128_K64 = 6,   // BK 64, 3 stages, 4 waves
+    TILES_128x256_K64 = 7,   // BK 64, 3 stages, 4 waves
+    TILES_128x128_K64 = 8,   // BK 64, 2 stages, 4 waves, 2 workgroups per CU
+    TILES_256x256_W8 = 9,    // BK 32, 4 stages, 8 waves (2 x 4) of 128 x 64
+};
+constexpr int TILES_LAST = TILES_256x256_W8;
 
 // BM x BN tiles (TileCfg) with 16-byte direct-to-LDS loads, any K and N and
-// 2-byte alignment, as long as 2 (M + 256) K and 2 (K + 32) (N + 256) stay
+// 2-byte alignment, as long as 2 (M + 256) K and 2 (K + 64) (N + 256) stay
 // below 2^31 - 65536.  aligned: K % 8 == 0, N % 8 == 0, A, B, C 16-byte and
 // bias 8-byte aligned, which takes the instance without last-slice fix-ups
 // and with 16-byte stores throughout.

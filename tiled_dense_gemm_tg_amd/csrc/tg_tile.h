@@ -13,7 +13,7 @@ namespace tile {
 constexpr int BM = 256;
 constexpr int BN = 256;
 constexpr int NTHREADS = 256;             // 4 wave64s, each owning 128 x 128 of C
-constexpr int GROUP_M = 4;                // tile rows per raster group
+constexpr int GROUP_M = 4;                // tile rows per raster group unless the caller picks another
 constexpr int NUM_XCD = 8;
 constexpr uint32_t OOB = 0xFFFFFFF0u;     // byte offset beyond every operand (< 2^32 - 32 bytes)
 
@@ -21,21 +21,21 @@ constexpr uint32_t OOB = 0xFFFFFFF0u;     // byte offset beyond every operand (<
 // on XCD x = w % 8 (also for a persistent grid whose size is a multiple of
 // 8) as the (w / 8)-th tile there.  Give each XCD a contiguous range of
 // logical tiles (the first total % 8 XCDs one more than the others: XCD x
-// runs exactly that many ids), and walk them GROUP_M tile-rows at a time,
+// runs exactly that many ids), and walk them group_m tile-rows at a time,
 // column by column, so that the tiles running together on one XCD share A
 // row-panels and B column-panels in that XCD's L2.  A bijection on
-// [0, tiles_m * tiles_n), for any tile size and count.
-__device__ __forceinline__ void tile_of_index(int tiles_m, int tiles_n, int w, int &tm, int &tn) {
+// [0, tiles_m * tiles_n), for any tile size and count and group_m >= 1.
+__device__ __forceinline__ void tile_of_index(int tiles_m, int tiles_n, int w, int group_m, int &tm, int &tn) {
     const int total = tiles_m * tiles_n;
     {
         const int q = total / NUM_XCD, r = total % NUM_XCD;
         const int x = w % NUM_XCD;
         w = x * q + min(x, r) + w / NUM_XCD;
     }
-    const int per_group = GROUP_M * tiles_n;
+    const int per_group = group_m * tiles_n;
     const int grp = w / per_group;
-    const int first_m = grp * GROUP_M;
-    const int rows = min(tiles_m - first_m, GROUP_M);
+    const int first_m = grp * group_m;
+    const int rows = min(tiles_m - first_m, group_m);
     const int rem = w - grp * per_group;
     tm = first_m + rem % rows;
     tn = rem / rows;
@@ -43,7 +43,7 @@ __device__ __forceinline__ void tile_of_index(int tiles_m, int tiles_n, int w, i
 
 // The raster of 256 x 256 tiles over an M x N output.
 __device__ __forceinline__ void tile_of_workgroup(int M, int N, int w, int &tm, int &tn) {
-    tile_of_index((M + BM - 1) / BM, (N + BN - 1) / BN, w, tm, tn);
+    tile_of_index((M + BM - 1) / BM, (N + BN - 1) / BN, w, GROUP_M, tm, tn);
 }
 
 // Raw buffer (stride 0) over [base, base + bytes): loads beyond the range
