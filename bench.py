@@ -598,6 +598,21 @@ def device_operands(torch, I, w, copies=1):
     return ops, sets
 
 
+def workload_named(I, name: str):
+    """A workload by name: the fixed ones, or a decode shape
+    gemm_f16_skinny_MxNxK with the decode workload's distributions and
+    seeds (for profiling other widths)."""
+    import dataclasses
+    import re
+    if name in I.WORKLOADS:
+        return I.WORKLOADS[name]
+    m = re.fullmatch(r"gemm_f16_skinny_(\d+)x(\d+)x(\d+)", name)
+    if not m:
+        raise SystemExit(f"unknown workload {name}")
+    M, N, K = (int(v) for v in m.groups())
+    return dataclasses.replace(I.WORKLOADS[SKINNY], name=name, M=M, N=N, K=K)
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as fh:
@@ -923,7 +938,7 @@ def main() -> int:
               flush=True)
         return 0
 
-    w = I.WORKLOADS[args.workload]
+    w = workload_named(I, args.workload)
     log(f"main workload {w.name}: generating inputs")
     ops, sets = device_operands(torch, I, w)
     ms, wall = time_gemm(torch, tg, w, sets, args.steps, args.warmup)
