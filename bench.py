@@ -212,19 +212,24 @@ def time_calls(torch, launch, steps, warmup, with_wall=False, settle_s=None):
     return (ms, wall) if with_wall else ms
 
 
-def gemm_launcher(torch, tg, w, sets, label, mode="fused"):
+def gemm_launcher(torch, tg, w, sets, label, mode="fused", ws=None, splits=0):
     """launch(i) for tg_gemm over `sets` rotating operand sets; mode
     "unfused" runs tg_gemm_unfused (product, then one pass per epilogue
-    step), "none" the product without epilogue."""
+    step), "none" the product without epilogue, "split" tg_gemm_split with
+    `splits` and the workspace `ws` (allocated and zeroed before the timed
+    region, as a caller holds one per stream)."""
     handle = torch.cuda.current_stream().cuda_stream
     calls = [(A.data_ptr(), B.data_ptr(), bias.data_ptr() if bias is not None else None, C.data_ptr())
              for A, B, bias, C in sets]
     nk = 1 + (EPILOGUE_PASSES[w.epilogue] if mode == "unfused" else 0)
+    wsp, wsn = (ws.data_ptr(), ws.numel()) if ws is not None else (None, 0)
 
     def launch(i):
         a, b, bi, c = calls[i % len(calls)]
         LOG.note(label, nk)
-        if mode == "unfused":
+        if mode == "split":
+            st = tg.tg_gemm_split(splits, w.M, w.N, w.K, w.dtype, a, b, bi, w.epilogue, c, wsp, wsn, handle)
+        elif mode == "unfused":
             st = tg.tg_gemm_unfused(w.M, w.N, w.K, w.dtype, a, b, bi, w.epilogue, c, handle)
         elif mode == "none":
             st = tg.tg_gemm(w.M, w.N, w.K, w.dtype, a, b, None, 0, c, handle)
@@ -236,9 +241,9 @@ def gemm_launcher(torch, tg, w, sets, label, mode="fused"):
     return launch
 
 
-def time_gemm(torch, tg, w, sets, steps, warmup, label=None, mode="fused", settle_s=None):
+def time_gemm(torch, tg, w, sets, steps, warmup, label=None, mode="fused", settle_s=None, ws=None, splits=0):
     """Per-launch time (ms) and wall time (s) of one gemm line."""
-    launch = gemm_launcher(torch, tg, w, sets, label or w.name, mode)
+    launch = gemm_launcher(torch, tg, w, sets, label or w.name, mode, ws, splits)
     return time_calls(torch, launch, steps, warmup, with_wall=True, settle_s=settle_s)
 
 
@@ -1008,17 +1013,25 @@ def main() -> int:
         w4 = I.WORKLOADS[SKINNY]
         log(f"secondary {w4.name} (8 rotating operand sets)")
         _, sets4 = device_operands(torch, I, w4, copies=8)
-        ms4, _ = time_gemm(torch, tg, w4, sets4, steps_for(max(args.steps, 400)), args.warmup)
-        hot, _ = time_gemm(torch, tg, w4, sets4[:1], steps_for(max(args.steps, 400)), args.warmup,
-                           label=f"{w4.name} hot")
+        steps4 = steps_for(max(args.steps, 400))
+        ms4, _ = time_gemm(torch, tg, w4, sets4, steps4, args.warmup)
+        hot, _ = time_gemm(torch, tg, w4, sets4[:1], steps4, args.warmup, label=f"{w4.name} hot")
+        # stream-K over every CU, the opt-in split mode (not the library's
+        # choice at this shape): its time, for the record
+        ws4 = torch.zeros(tg.tg_gemm_split_workspace_bytes(w4.N, tg.TG_SPLIT_STREAM_K), dtype=torch.uint8,
+                          device="cuda")
+        msk, _ = time_gemm(torch, tg, w4, sets4, steps4, args.warmup, label=f"{w4.name} stream-K", mode="split",
+                           ws=ws4, splits=tg.TG_SPLIT_STREAM_K)
+        del ws4
         nbytes = gemm_alg_bytes(w4.M, w4.N, w4.K)
         gbps = nbytes / (ms4 * 1e-3) / 1e9
         sec[w4.name] = {"us_per_launch": round(ms4 * 1e3, 3), "GB/s": round(gbps, 1),
                         "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
                         "hot_cache_GB/s_not_the_metric": round(nbytes / (hot * 1e-3) / 1e9, 1),
+                        "stream_k_us": round(msk * 1e3, 3),
                         "TFLOP/s": round(gemm_flops(w4.M, w4.N, w4.K) / (ms4 * 1e-3) / 1e12, 2),
                         "path": path_of(tg, w4, sets4[0]), "traffic": measured_traffic(w4.name)}
-        log(f"{w4.name}: {ms4 * 1e3:.2f} us, {gbps:.0f} GB/s")
+        log(f"{w4.name}: {ms4 * 1e3:.2f} us, {gbps:.0f} GB/s; stream-K {msk * 1e3:.2f} us")
         del sets4
         torch.cuda.empty_cache()
         log("secondary: 32, 48 and 64 rows at the decode width (8 rotating weight sets)")

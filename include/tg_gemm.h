@@ -219,52 +219,74 @@ tg_status tg_gemm_tiles_plan(int64_t M, int64_t N, int64_t K, int num_cu, tg_til
  * kernels by thinking in tiles", section 2, "A back-of-the-envelope
  * calculation"), and the skinny kernel gives each 64-column slab of B to one
  * workgroup, so a narrow B (N = 4096: 64 slabs) leaves most of a 256-CU
- * device idle.  The pages have no split-K; this library adds one: the K range
- * of each slab is divided over `splits` workgroups, each writes its fp32
- * partial 16 x 64 block to a workspace and counts itself in that slab's
- * counter, and the last to arrive adds the partials in split order, applies
- * the epilogue and stores C.  No workgroup waits for another.
+ * device idle, and a slab count that does not divide the CU count (N =
+ * 11008: 172 slabs) leaves the rest idle.  Each CU streams at a limited
+ * rate of its own, so the time is that of the busiest CU.  The pages have
+ * no split-K; this library adds two forms:
+ *   even split (splits >= 2): the K range of each slab is divided over
+ *     `splits` workgroups;
+ *   stream-K (splits = TG_SPLIT_STREAM_K): the 32-k steps of all slabs, slab
+ *     after slab, are cut into one equal contiguous range per CU (at most
+ *     1024 workgroups, at least 16 steps each), so a workgroup finishes some
+ *     slabs and shares the slabs at its range's ends with its neighbours.
+ * In both, each workgroup with part of a slab writes its fp32 partial
+ * 16 x 64 block to a workspace and counts itself in that slab's counter,
+ * and the last to arrive adds the partials in K order, applies the epilogue
+ * and stores C.  No workgroup waits for another.
  *
- * tg_gemm_split: as tg_gemm, with the skinny family's K range split over
- * `splits` workgroups per slab (0: the library's choice, reported by
- * tg_gemm_split_plan for the device of `stream`; 1: no split, no workspace;
- * at most 64).  Shapes that do not take the skinny path, and those with
- * M > 16 (several row blocks per workgroup, never split), run as in tg_gemm
- * and leave the workspace alone.
+ * tg_gemm_split: as tg_gemm, with the skinny family's K range divided as
+ * `splits` says (0: the library's choice, reported by tg_gemm_split_plan for
+ * the device of `stream`; 1: no split, no workspace; 2..64 even splits;
+ * TG_SPLIT_STREAM_K).  Shapes that do not take the skinny path, those with
+ * M > 16 (several row blocks per workgroup, never split) and K = 0 run as in
+ * tg_gemm and leave the workspace alone.
  *   workspace        device memory, 16-byte aligned, at least
- *                    tg_gemm_split_workspace_bytes(N, splits) bytes (NULL
+ *                    tg_gemm_split_workspace_bytes(N, splits) bytes (for
+ *                    splits 0, the bytes tg_gemm_split_plan reports; NULL
  *                    allowed when that is 0), not overlapping A, B, bias or
- *                    C.  Its first 4 ceil(N / 64) bytes are counters that
- *                    must be zero before the first call (zero-fill the
- *                    workspace once); every call that completes leaves
- *                    them zero.  Calls that may run at the same time
- *                    (other streams) need workspaces of their own.
+ *                    C.  Its first max(64 KiB, 4 ceil(N / 64) bytes) are
+ *                    counters that must be zero before the first call
+ *                    (zero-fill the workspace once); every call that
+ *                    completes leaves them zero, and partial blocks go
+ *                    only after them, so one workspace serves calls of
+ *                    every shape with N up to 2^20 (larger N move the
+ *                    partials: zero the counters again when N changes).
+ *                    Calls that may run at the same time (other streams)
+ *                    need workspaces of their own.
  *   workspace_bytes  its size in bytes.
- * TG_ERR_INVALID_ARG for splits outside 0..64 or a workspace that is
- * missing, too small, misaligned or overlapping; otherwise the argument
- * rules and results of tg_gemm (to the tolerance of fp32 accumulation in
- * another order; bit-identical on integer-valued inputs, and the same for
- * every call with the same splits).
+ * TG_ERR_INVALID_ARG for splits outside TG_SPLIT_STREAM_K..64 or a workspace
+ * that is missing, too small, misaligned or overlapping; otherwise the
+ * argument rules and results of tg_gemm (to the tolerance of fp32
+ * accumulation in another order; bit-identical on integer-valued inputs,
+ * and the same for every call with the same splits on the same device).
  */
+#define TG_SPLIT_STREAM_K (-1)
+
 tg_status tg_gemm_split(int splits, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
                         const void *A, const void *B, const void *bias, tg_epilogue epilogue,
                         void *C, void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
- * Workspace bytes tg_gemm_split needs for N columns and `splits` splits
- * (0 for splits <= 1; -1 for N outside 0..2^30 or splits outside 0..64).
- * Pure host code.
+ * Workspace bytes tg_gemm_split needs for N columns and `splits` splits:
+ * 0 for splits 0 and 1 (for 0, ask tg_gemm_split_plan); for
+ * TG_SPLIT_STREAM_K, enough for any device (up to 1024 workgroups); -1 for
+ * N outside 0..2^30 or splits outside TG_SPLIT_STREAM_K..64.  Pure host code.
  */
 int64_t tg_gemm_split_workspace_bytes(int64_t N, int splits);
 
 /*
- * The split count tg_gemm_split(0, ...) uses for an M x N x K product on a
+ * The split mode tg_gemm_split(0, ...) uses for an M x N x K product on a
  * device with num_cu compute units (num_cu <= 0: 256), in *splits_out (1 for
- * M > 16 or an empty product), and the workspace bytes it needs, in
- * *workspace_bytes_out.  The count is the largest with slabs x splits at
- * most num_cu (one round of workgroups; a second costs more than splitting
- * gains) and at least 16 32-k steps per workgroup.  TG_ERR_INVALID_ARG
- * for negative or too large sizes or NULL outputs.  Pure host code.
+ * M > 16 or an empty product; 2..64; or TG_SPLIT_STREAM_K), and the
+ * workspace bytes it needs there, in *workspace_bytes_out.  The even count
+ * is the largest with slabs x splits at most num_cu (one round of
+ * workgroups; a second costs more than splitting gains) and at least 16
+ * 32-k steps per workgroup; stream-K replaces it where a cost model fitted
+ * to MI355X times predicts it faster: long K with slabs that leave CUs idle
+ * (16 x 11008 x 11008), not the decode shape 16 x 11008 x 4096, where the
+ * exchange of partial sums costs more than the idle CUs would gain.
+ * TG_ERR_INVALID_ARG for negative or too large sizes or NULL outputs.  Pure
+ * host code.
  */
 tg_status tg_gemm_split_plan(int64_t M, int64_t N, int64_t K, int num_cu, int *splits_out,
                              int64_t *workspace_bytes_out);
@@ -277,10 +299,12 @@ tg_status tg_gemm_split_plan(int64_t M, int64_t N, int64_t K, int num_cu, int *s
  * TG_SCRATCH_BYTES bytes per GPU, held until the process ends.  The library
  * allocates and frees nothing in this call.
  *   splits   as for tg_gemm_split (0: tg_gemm_split_plan's choice; 1: no
- *            split; at most 64).  Shapes that do not take the skinny path,
- *            M > 16, and a resolved count of 1 run exactly as tg_gemm.
- * Limits: ceil(N / 64) x splits at most 1024 (the partial blocks, 4 KiB
- * each) and ceil(N / 64) at most 16384 (the counters), else
+ *            split; 2..64; TG_SPLIT_STREAM_K).  Shapes that do not take the
+ *            skinny path, M > 16, K = 0 and a resolved count of 1 run
+ *            exactly as tg_gemm.
+ * Limits: ceil(N / 64) x splits (stream-K: workgroups + ceil(N / 64) - 1)
+ * at most 1024 (the partial blocks, 4 KiB each) and ceil(N / 64) at most
+ * 16384 (the counters), else
  * TG_ERR_UNSUPPORTED; splits outside 0..64 is TG_ERR_INVALID_ARG; the other
  * rules and results are those of tg_gemm_split with the same splits
  * (bit-identical to it).
@@ -383,9 +407,9 @@ tg_status tg_gemm_w4(int64_t M, int64_t N, int64_t K, tg_dtype dtype, const void
  * (0: the library's choice, tg_gemm_w4_split_plan for the device of
  * `stream`; 1: no split; at most 64).  workspace: device memory, 16-byte
  * aligned, at least tg_gemm_w4_split_workspace_bytes(M, N, splits) bytes,
- * overlapping no operand, its first 4 ceil(M / 16) ceil(N / 64) bytes zero
- * before the first call and left zero by every completed call; one per
- * stream.  TG_ERR_INVALID_ARG for splits outside 0..64 or a missing, small,
+ * overlapping no operand, its first max(64 KiB, 4 ceil(M / 16) ceil(N / 64)
+ * bytes) zero before the first call and left zero by every completed call
+ * (the counters, as for tg_gemm_split); one per stream.  TG_ERR_INVALID_ARG for splits outside 0..64 or a missing, small,
  * misaligned or overlapping workspace; otherwise the rules and results of
  * tg_gemm_w4 (to the tolerance of fp32 accumulation in another order;
  * bit-identical on integer-valued inputs and from call to call).

@@ -323,14 +323,21 @@ def test_smoke_cases_are_planned_as_smoke_expects(lib):
 # ------------------------------------------------------------ split-K
 
 def test_split_workspace_bytes(lib):
-    # counters (4 bytes per 64-column slab, padded to 256), then 4 KiB per slab and split
-    assert tg.tg_gemm_split_workspace_bytes(4096, 4) == 256 + 64 * 4 * 4096
-    assert tg.tg_gemm_split_workspace_bytes(11008, 2) == 768 + 172 * 2 * 4096
-    assert tg.tg_gemm_split_workspace_bytes(4100, 3) == 512 + 65 * 3 * 4096
+    # counters (4 bytes per 64-column slab, in a region of at least 64 KiB,
+    # so the partials start at the same place for every N up to 2^20), then
+    # 4 KiB per slab and split
+    assert tg.tg_gemm_split_workspace_bytes(4096, 4) == 65536 + 64 * 4 * 4096
+    assert tg.tg_gemm_split_workspace_bytes(11008, 2) == 65536 + 172 * 2 * 4096
+    assert tg.tg_gemm_split_workspace_bytes(4100, 3) == 65536 + 65 * 3 * 4096
+    assert tg.tg_gemm_split_workspace_bytes(2 ** 20 + 64, 2) == 65792 + 16385 * 2 * 4096
     for splits in (0, 1):
         assert tg.tg_gemm_split_workspace_bytes(4096, splits) == 0
     assert tg.tg_gemm_split_workspace_bytes(0, 8) == 0
-    for N, splits in ((-1, 2), (4096, -1), (4096, 65), (2 ** 30 + 1, 2)):
+    # stream-K: counters, then one partial block per (slab, workgroup) pair,
+    # for up to 1024 workgroups
+    assert tg.tg_gemm_split_workspace_bytes(11008, tg.TG_SPLIT_STREAM_K) == 65536 + (1024 + 172 - 1) * 4096
+    assert tg.tg_gemm_split_workspace_bytes(64, tg.TG_SPLIT_STREAM_K) == 65536 + 1024 * 4096
+    for N, splits in ((-1, 2), (4096, -2), (4096, 65), (2 ** 30 + 1, 2), (2 ** 30 + 1, tg.TG_SPLIT_STREAM_K)):
         assert tg.tg_gemm_split_workspace_bytes(N, splits) == -1
 
 
@@ -341,7 +348,7 @@ def test_split_entry_point_checks_arguments(lib):
     def call(splits, M=16, N=4096, K=4096, ws=ws, nbytes=need, C=PC, bias=None, epi=I.EPI_NONE):
         return tg.tg_gemm_split(splits, M, N, K, I.F16, PA, PB, bias, epi, C, ws, nbytes, None)
 
-    for bad in (-1, 65, 1000):
+    for bad in (-2, 65, 1000):
         assert call(bad) == tg.TG_ERR_INVALID_ARG
     assert call(4, nbytes=-1) == tg.TG_ERR_INVALID_ARG
     assert call(4, ws=None) == tg.TG_ERR_INVALID_ARG                      # a split needs a workspace
@@ -371,21 +378,40 @@ def test_split_plan_checks_arguments(lib):
     assert tg.tg_gemm_split_plan(16, 0, 11008, 256) == (tg.TG_OK, 1, 0)
 
 
+def _streamk_groups(N, K, cus):
+    """Stream-K workgroups: one per CU (256 if unknown), at most 1024, at
+    least 16 32-k steps each, at least one."""
+    total = -(-N // 64) * -(-K // 32)
+    return max(1, min(cus or 256, 1024, total // 16))
+
+
 def test_split_plan_workspace_matches_its_split_count(lib):
-    for M, N, K in ((16, 4096, 11008), (16, 11008, 4096), (1, 2048, 8192), (16, 4096, 256), (8, 64, 65536)):
+    for M, N, K in ((16, 4096, 11008), (16, 11008, 4096), (1, 2048, 8192), (16, 4096, 256), (8, 64, 65536),
+                    (16, 28672, 4096), (16, 8256, 512)):
         for cus in (0, 64, 256, 1024):
             st, splits, nbytes = tg.tg_gemm_split_plan(M, N, K, cus)
-            assert st == tg.TG_OK and 1 <= splits <= 64
-            assert nbytes == tg.tg_gemm_split_workspace_bytes(N, splits)
-            assert 32 * 16 * splits <= max(K, 32 * 16) + 31       # at least 16 32-k steps per split
+            assert st == tg.TG_OK and (1 <= splits <= 64 or splits == tg.TG_SPLIT_STREAM_K)
+            if splits == tg.TG_SPLIT_STREAM_K:
+                slabs = -(-N // 64)
+                groups = _streamk_groups(N, K, cus)
+                assert nbytes == 65536 + (groups + slabs - 1) * 4096
+                assert nbytes <= tg.tg_gemm_split_workspace_bytes(N, splits)
+            else:
+                assert nbytes == tg.tg_gemm_split_workspace_bytes(N, splits)
+                assert 32 * 16 * splits <= max(K, 32 * 16) + 31       # at least 16 32-k steps per split
 
 
 @pytest.mark.parametrize("M,N,K,splits", [
     (16, 4096, 11008, 4),     # 64 slabs: four splits fill 256 CUs
     (16, 4096, 4096, 4),
     (16, 1024, 4096, 8),      # 16 slabs: 16 splits would leave 8 steps each; 8 keeps 16
-    (16, 11008, 4096, 1),     # 172 slabs: a second round of workgroups costs more than a split gains
-    (8, 28672, 4096, 1),
+    # 172 slabs: even splits need a second round of workgroups, and stream-K's
+    # 86 steps per CU do not pay for its exchange (measured 23.6 against 19.1 us)
+    (16, 11008, 4096, 1),
+    # long K: stream-K's 231 steps per CU against 344 (47.5 against 55.0 us)
+    (16, 11008, 11008, tg.TG_SPLIT_STREAM_K),
+    (8, 28672, 4096, 1),      # 448 slabs: 2 rounds of 128 steps, 46.3 us; stream-K 48.3 us
+    (16, 16384, 4096, 1),     # 256 slabs: one per CU, nothing to gain
     (16, 4096, 256, 1),       # 8 steps in all: too few to split
     (1, 64, 65536, 64),       # one slab, deep K: capped at 64 splits
 ])
@@ -393,20 +419,27 @@ def test_split_plan_on_an_mi355x(lib, M, N, K, splits):
     st, got, nbytes = tg.tg_gemm_split_plan(M, N, K, 256)
     assert (st, got) == (tg.TG_OK, splits)
     assert tg.tg_gemm_split_plan(M, N, K, 0)[1] == splits              # 0: 256 CUs assumed
-    assert nbytes == tg.tg_gemm_split_workspace_bytes(N, splits)
+    if splits == tg.TG_SPLIT_STREAM_K:
+        slabs = -(-N // 64)
+        assert nbytes == 65536 + (256 + slabs - 1) * 4096
+    else:
+        assert nbytes == tg.tg_gemm_split_workspace_bytes(N, splits)
 
 
 def test_static_split_checks_arguments_before_any_device_work(lib):
     # Invalid split counts and scratch overflows are refused on the host,
     # before the first HIP call, like every other argument error.
     args = (16, 4096, 4096, I.F16, PA, PB, None, I.EPI_NONE, PC, None)
-    assert lib.tg_gemm_split_static(-1, *args) == tg.TG_ERR_INVALID_ARG
+    assert lib.tg_gemm_split_static(-2, *args) == tg.TG_ERR_INVALID_ARG
     assert lib.tg_gemm_split_static(65, *args) == tg.TG_ERR_INVALID_ARG
     # 64 slabs x 32 splits = 2048 partial blocks of 4 KiB: above the 4 MiB scratch
     assert lib.tg_gemm_split_static(32, *args) == tg.TG_ERR_UNSUPPORTED
     # more than 16384 slabs: more counters than the scratch holds
     wide = (16, 16384 * 64 + 64, 4096, I.F16, PA, PB, None, I.EPI_NONE, PC, None)
     assert lib.tg_gemm_split_static(2, *wide) == tg.TG_ERR_UNSUPPORTED
+    # stream-K on 256 CUs (none here: 256 assumed) over 800 slabs: 1055 partial blocks
+    many = (16, 800 * 64, 4096, I.F16, PA, PB, None, I.EPI_NONE, PC, None)
+    assert lib.tg_gemm_split_static(tg.TG_SPLIT_STREAM_K, *many) == tg.TG_ERR_UNSUPPORTED
     # the tg_gemm rules come first
     assert lib.tg_gemm_split_static(4, -1, 4096, 4096, I.F16, PA, PB, None, I.EPI_NONE, PC, None) == \
         tg.TG_ERR_INVALID_ARG

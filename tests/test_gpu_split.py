@@ -121,7 +121,7 @@ def test_split_auto_matches_its_plan():
     import torch
     dtype = I.F16
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    for M, N, K in [(16, 4096, 11008), (16, 11008, 4096), (4, 2048, 8192)]:
+    for M, N, K in [(16, 4096, 11008), (16, 11008, 4096), (4, 2048, 8192), (16, 11008, 11008)]:
         st, splits, nbytes = tg.tg_gemm_split_plan(M, N, K, cus)
         assert st == tg.TG_OK
         A = I.random_bits((M, K), ("normal", 0.0, 1.0), dtype, 34000 + N)
@@ -129,6 +129,8 @@ def test_split_auto_matches_its_plan():
         log(f"[split auto] M={M} N={N} K={K}: plan {splits} splits, {nbytes} bytes")
         C_auto, _ = _split_run(M, N, K, dtype, A, B, None, I.EPI_NONE, 0)
         C_plan, _ = _split_run(M, N, K, dtype, A, B, None, I.EPI_NONE, splits)
+        if (M, N, K) == (16, 11008, 11008):
+            assert splits == tg.TG_SPLIT_STREAM_K
         assert torch.equal(C_auto.view(torch.int16), C_plan.view(torch.int16))
         rows = np.arange(M)[:: max(1, M // 4)]
         ref64, _ = oracle.gemm(M, N, K, dtype, A, B, None, I.EPI_NONE, rows)
@@ -159,12 +161,93 @@ def test_split_decode_shapes_full_size(M, N, K):
     A = I.random_bits((M, K), ("normal", 0.0, 1.0), dtype, 36000 + N)
     B = I.random_bits((K, N), ("normal", 0.0, 0.02), dtype, 36001 + N)
     ref64, _ = oracle.gemm(M, N, K, dtype, A, B, None, I.EPI_NONE)
-    for splits in (0, 2, 8):
+    for splits in (0, 2, 8, tg.TG_SPLIT_STREAM_K):
         what = f"M={M} N={N} K={K} splits={splits}"
         log(f"[split full] {what}")
         C, ws = _split_run(M, N, K, dtype, A, B, None, I.EPI_NONE, splits)
         check_tolerance(dtype, to_bits(C), ref64, what)
         assert _counters_zero(ws, N), what
+
+
+# ------------------------------------------------------------ stream-K
+
+SK = tg.TG_SPLIT_STREAM_K
+
+SK_CASES = [
+    # M, N, K: the decode shape (172 slabs on the CUs: 86 steps per workgroup,
+    # parts of one or two slabs each); ragged N and K with a few steps per
+    # workgroup; one step in all (one workgroup); 16-step slabs under
+    # 18-19-step ranges (workgroups that finish a whole slab between two
+    # shared ones); few slabs (fewer workgroups than CUs)
+    (16, 11008, 4096),
+    (7, 1028, 1000),
+    (1, 64, 8),
+    (16, 19200, 512),
+    (12, 520, 4104),
+    (5, 8256, 8008),
+]
+
+
+@pytest.mark.parametrize("dtype", [I.F16, I.BF16])
+@pytest.mark.parametrize("M,N,K", SK_CASES)
+def test_streamk_parity(dtype, M, N, K):
+    rows = np.arange(M) if N * K <= 4096 * 4096 else np.arange(M)[:: max(1, M // 4)]
+    for epi in (I.EPI_NONE, I.EPI_BIAS_GELU_TANH):
+        seed = 38000 + 97 * M + epi + 5 * dtype + N % 1000
+        A = I.random_bits((M, K), ("normal", 0.0, 1.0), dtype, seed)
+        B = I.random_bits((K, N), ("normal", 0.0, 0.02), dtype, seed + 1)
+        bias = I.random_bits((N,), ("normal", 0.0, 0.1), dtype, seed + 2) if epi else None
+        what = f"stream-K {I.DTYPE_NAMES[dtype]} M={M} N={N} K={K} epi={epi}"
+        log(f"[stream-K] {what}")
+        C, ws = _split_run(M, N, K, dtype, A, B, bias, epi, SK)
+        ref64, _ = oracle.gemm(M, N, K, dtype, A, B, bias, epi, rows)
+        check_tolerance(dtype, to_bits(C)[rows], ref64, what)
+        assert np.isfinite(C.float().cpu().numpy()).all(), what
+        assert _counters_zero(ws, N), what
+
+
+@pytest.mark.parametrize("dtype", [I.F16, I.BF16])
+@pytest.mark.parametrize("M,N,K", SK_CASES[1:])
+def test_streamk_integers_bit_exact(dtype, M, N, K):
+    seed = 39000 + 97 * M + 5 * dtype + N % 1000
+    A = I.small_int_bits((M, K), dtype, seed)
+    B = I.small_int_bits((K, N), dtype, seed + 1)
+    bias = I.small_int_bits((N,), dtype, seed + 2)
+    what = f"stream-K {I.DTYPE_NAMES[dtype]} M={M} N={N} K={K} (integers)"
+    log(f"[stream-K exact] {what}")
+    C, _ = _split_run(M, N, K, dtype, A, B, bias, I.EPI_BIAS, SK)
+    _, refq = oracle.gemm(M, N, K, dtype, A, B, bias, I.EPI_BIAS)
+    check_exact(to_bits(C), refq, what)
+
+
+def test_streamk_reuses_one_workspace_and_is_deterministic():
+    """One workspace through stream-K calls of several shapes, even splits
+    between them: the call's counters end at zero and a repeated
+    call is bit-identical (the parts of a slab are added in K order,
+    whichever workgroup comes last)."""
+    import torch
+    dtype = I.F16
+    shapes = [(16, 11008, 4096, SK), (16, 4096, 2048, 4), (16, 11008, 4096, SK), (3, 19200, 512, SK),
+              (16, 11008, 4096, SK)]
+    need = max(tg.tg_gemm_split_workspace_bytes(N, s) for (_, N, _, s) in shapes)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    first = {}
+    for i, (M, N, K, splits) in enumerate(shapes):
+        A = I.random_bits((M, K), ("normal", 0.0, 1.0), dtype, 40000 + N)
+        B = I.random_bits((K, N), ("normal", 0.0, 0.02), dtype, 40100 + N)
+        what = f"M={M} N={N} K={K} splits={splits} call {i}"
+        log(f"[stream-K reuse] {what}")
+        C, _ = _split_run(M, N, K, dtype, A, B, None, I.EPI_NONE, splits, ws)
+        assert _counters_zero(ws, N), what     # the counters of this call's slabs
+        bits = to_bits(C)
+        key = (M, N, K, splits)
+        if key in first:
+            assert np.array_equal(first[key], bits), what + ": not bit-identical to the first call"
+        else:
+            first[key] = bits
+            rows = np.arange(M)[:: max(1, M // 4)]
+            ref64, _ = oracle.gemm(M, N, K, dtype, A, B, None, I.EPI_NONE, rows)
+            check_tolerance(dtype, bits[rows], ref64, what)
 
 
 # ------------------------------------------------------------ 4-bit weights

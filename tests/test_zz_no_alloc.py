@@ -66,10 +66,27 @@ def test_static_split_matches_workspace_split_twice(dtype):
             check_tolerance(dtype, got, ref64, what)
 
 
+@pytest.mark.parametrize("dtype", [I.F16, I.BF16])
+def test_static_streamk_matches_workspace_streamk_twice(dtype):
+    calls = [
+        # M, N, K: 172 slabs over the CUs (427 partial blocks), then 17 slabs
+        # (a smaller input whose partials overwrite the first call's)
+        (16, 11008, 4096),
+        (7, 1028, 1000),
+    ]
+    for i, (M, N, K) in enumerate(calls):
+        for epi in (I.EPI_NONE, I.EPI_BIAS_GELU_TANH):
+            what = f"static stream-K {I.DTYPE_NAMES[dtype]} M={M} N={N} K={K} epi={epi} call {i}"
+            log(f"[no-alloc] {what}")
+            got, want, ref64 = _both(M, N, K, dtype, epi, tg.TG_SPLIT_STREAM_K, 54000 + 100 * i + 10 * dtype + epi)
+            check_exact(got, want, what)
+            check_tolerance(dtype, got, ref64, what)
+
+
 def test_static_split_library_choice_and_unsplit_shapes():
     # splits = 0 takes the plan's count; M > 16 and off-skinny shapes run as
     # tg_gemm and give its result.
-    for M, N, K in ((16, 4096, 4096), (40, 1024, 512), (300, 263, 201)):
+    for M, N, K in ((16, 4096, 4096), (16, 11008, 4096), (40, 1024, 512), (300, 263, 201)):
         dtype, epi = I.F16, I.EPI_BIAS_GELU_TANH
         what = f"static split auto M={M} N={N} K={K}"
         log(f"[no-alloc] {what}")

@@ -35,6 +35,8 @@ PATH_NAMES = {TG_PATH_AUTO: "auto", TG_PATH_TILED: "tiled", TG_PATH_TILED_GENERI
 TG_EW_BIAS_ADD = 0
 TG_EW_GELU_TANH = 1
 
+TG_SPLIT_STREAM_K = -1   # tg_gemm_split: stream-K division of all slabs' 32-k steps over the CUs
+
 TG_TILES_AUTO = 0
 TG_TILES_256x256 = 1
 TG_TILES_256x128 = 2

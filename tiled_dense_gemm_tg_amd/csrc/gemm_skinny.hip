@@ -64,6 +64,26 @@ struct ABatch {
 };
 __device__ __forceinline__ ABatch<1> u32x4_pair(u32x4 a, u32x4 b) { return ABatch<1>{{{a}, {b}}}; }
 
+// LDS of the kernel, per wave: RS floats, 32 KB with the preload (its slice
+// of A, 16 rows x 32 PRE k), else 16 KB; after its k-loop, its RB 16 x 64
+// fp32 partial sums (4 KB each) at red(wave, b, i, lane).  Each wave touches
+// only its own region until the barrier before the cross-wave reduction.
+template <bool BIG>
+constexpr int region_floats() { return BIG ? 256 * PRE : 4096; }
+
+template <bool BIG>
+__device__ __forceinline__ float &red_at(u32x4 *smem, int w, int b, int i, int l) {
+    return reinterpret_cast<float *>(smem)[region_floats<BIG>() * w + 1024 * b + 64 * i + l];
+}
+
+// Where a wave's k-loop takes A from (RB = 1 for the last two):
+//   A_GLOBAL   16-byte loads from L2 in every step, beside B's;
+//   A_PRELOAD  the wave's whole slice (PRE / 2 < steps <= PRE) into LDS by
+//              direct loads, then into registers, before the loop;
+//   A_STAGED   the wave's steps in chunks of at most PRE: each chunk's slice
+//              into LDS by direct loads, then one 16-byte LDS read per step.
+constexpr int A_GLOBAL = 0, A_PRELOAD = 1, A_STAGED = 2;
+
 // RB: 16-row blocks of A (and C) per workgroup, 1..4 (M <= 16 RB).  Every
 // block multiplies the same B vectors, so B is still read once; the preload
 // path and split-K are for RB = 1 only.  One wave per SIMD gives a lane up
@@ -71,18 +91,16 @@ __device__ __forceinline__ ABatch<1> u32x4_pair(u32x4 a, u32x4 b) { return ABatc
 // SIMD (with 8 waves they spilled and ran 2-3x slower than three blocks),
 // and every instance ran as fast or faster on 4 waves than on 8 (M = 16,
 // K = 4096 with the preload: 18.95 against 19.86 us).
-template <class T, int EPI, bool PRELOAD, int RB>
-__global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args, SplitWs ws) {
-    static_assert(RB >= 1 && RB <= 4 && (RB == 1 || !PRELOAD), "row blocks");
-    // Per wave RS floats of LDS: 32 KB with the preload (its slice of A,
-    // 16 rows x 32 PRE k), else 16 KB; after its k-loop, its RB 16 x 64 fp32
-    // partial sums (4 KB each).  Each wave touches only its own region until
-    // the barrier before the cross-wave reduction.
-    constexpr int RS = PRELOAD ? 256 * PRE : 4096;
-    __shared__ __attribute__((aligned(16))) u32x4 smem[WAVES * RS / 4];
-    auto red = [&](int w, int b, int i, int l) __attribute__((always_inline)) -> float & {
-        return reinterpret_cast<float *>(smem)[RS * w + 1024 * b + 64 * i + l];
-    };
+//
+// slab_part: the workgroup's sums over the 32-k steps [sp_begin, sp_begin +
+// sp_len) of slab `slab`, left in every wave's LDS region; returns after the
+// barrier that makes them visible to every wave.
+template <class T, int AMODE, int RB>
+__device__ __forceinline__ void slab_part(const GemmArgs &args, u32x4 *smem, int slab, int sp_begin, int sp_len) {
+    static_assert(RB >= 1 && RB <= 4 && (RB == 1 || AMODE == A_GLOBAL), "row blocks");
+    constexpr bool PRELOAD = AMODE == A_PRELOAD;
+    constexpr bool BIG = AMODE != A_GLOBAL;
+    constexpr int RS = region_floats<BIG>();
     const int M = args.M, N = args.N, K = args.K;
     const uint16_t *__restrict__ A = args.A;
     const uint16_t *__restrict__ B = args.B;
@@ -91,16 +109,10 @@ __global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args, Sp
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: loop control stays scalar
     const int p = lane & 15;
     const int h = lane >> 4;
-    const int nb = blockIdx.x * SLAB;
+    const int nb = slab * SLAB;
     const int ncol = nb + 4 * p;              // N % 4 == 0: all four columns valid or none
 
-    // this workgroup's part of the 32-k steps (all of them without split-K),
-    // divided over its waves
-    const int steps = (K + 31) / 32;
-    const int splits = ws.splits;
-    const int split = blockIdx.y;
-    const int sp_begin = (int)(((int64_t)steps * split) / splits);
-    const int sp_len = (int)(((int64_t)steps * (split + 1)) / splits) - sp_begin;
+    // this workgroup's part of the slab's 32-k steps, divided over its waves
     const int s_begin = sp_begin + (int)(((int64_t)sp_len * wave) / WAVES);
     const int s_end = sp_begin + (int)(((int64_t)sp_len * (wave + 1)) / WAVES);
 
@@ -253,6 +265,72 @@ __global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args, Sp
             mma_batch(vb1, u32x4_pair(pa[(bi + 1) * UNROLL], pa[(bi + 1) * UNROLL + 1]));
             __builtin_amdgcn_sched_barrier(0);
         }
+    } else if constexpr (AMODE == A_STAGED) {
+        // Chunks of at most PRE steps of the wave's range.  A chunk's slice
+        // of A goes to the wave's LDS region by the direct loads of the
+        // preload (same layout and swizzle), only its ceil(n / 4) groups of
+        // 4 steps; steps past the chunk read zero in both operands, and every
+        // group of 4 steps the loop touches was loaded (so no stale LDS data
+        // reaches an MFMA).  The chunk's first two batches of B go out around
+        // the A loads, as in the preload.
+        const uint32_t region = lds_address(smem) + 4u * RS * (uint32_t)wave;
+        const i32x4 rs = rsrc_words((const char *)A - ASHIFT, 2u * (uint32_t)M * (uint32_t)K + ASHIFT);
+        const int r0 = lane >> 4;
+        const int slot = lane & 15;
+        for (int c0 = s_begin; c0 < s_end; c0 += PRE) {
+            const int cn = min(PRE, s_end - c0);
+            const int c_end = c0 + cn;
+            auto load_b = [&](u32x2 (&vb)[UNROLL][8], int s0) __attribute__((always_inline)) {
+#pragma unroll
+                for (int u = 0; u < UNROLL; ++u) {
+                    const int kb = (s0 + u) * 32 + 8 * h;
+                    const uint32_t mk = mask_of(s0 + u < c_end && kb < K);
+                    const uint32_t boff = (uint32_t)kb * b_row + b_col;
+#pragma unroll
+                    for (int r = 0; r < 8; ++r)
+                        vb[u][r] = __builtin_amdgcn_raw_buffer_load_b64(rb, (int)((boff + (uint32_t)r * b_row) | mk),
+                                                                        0, CPOL_NT);
+                }
+            };
+            auto a_at = [&](int i) __attribute__((always_inline)) {
+                const uint32_t c = (uint32_t)((4 * (i & 3) + h) ^ p);
+                return *(__attribute__((address_space(3))) const u32x4 *)(uintptr_t)(
+                    region + 4096u * (uint32_t)(i >> 2) + 256u * (uint32_t)p + 16u * c);
+            };
+            load_b(vb0, c0);
+            {
+                const int kend = min(K, 32 * c_end);
+#pragma unroll
+                for (int c4 = 0; c4 < PRE / 4; ++c4) {
+                    if (4 * c4 < cn) {
+#pragma unroll
+                        for (int rq = 0; rq < 4; ++rq) {
+                            const int r = 4 * rq + r0;
+                            const int k = 32 * c0 + 128 * c4 + 8 * (slot ^ r);
+                            const uint32_t off =
+                                (ASHIFT - 1024u * (uint32_t)rq + 2u * ((uint32_t)r * (uint32_t)K + (uint32_t)k)) +
+                                (k < kend ? 0u : 0x80000000u);
+                            dma16_rq(rq, rs, off, region + 4096u * (uint32_t)c4);
+                        }
+                    }
+                }
+            }
+            load_b(vb1, c0 + UNROLL);
+            // the chunk's A loads are older than the second batch's 8 UNROLL B loads
+            wait_vmcnt<8 * UNROLL>();
+            for (int i = 0; i < cn; i += 2 * UNROLL) {
+                if (i > 0)
+                    load_b(vb1, c0 + i + UNROLL);
+                __builtin_amdgcn_sched_barrier(0);
+                mma_batch(vb0, u32x4_pair(a_at(i), a_at(i + 1)));
+                __builtin_amdgcn_sched_barrier(0);
+                if (i + 2 * UNROLL < cn)
+                    load_b(vb0, c0 + i + 2 * UNROLL);
+                __builtin_amdgcn_sched_barrier(0);
+                mma_batch(vb1, u32x4_pair(a_at(i + 2), a_at(i + 3)));
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
     } else {
         load_batch(vb0, va0, s_begin);
         for (int s0 = s_begin; s0 < s_end; s0 += 2 * UNROLL) {
@@ -277,50 +355,70 @@ __global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args, Sp
         for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                red(wave, b, 4 * e + j, lane) = acc[b][j][e];
+                red_at<BIG>(smem, wave, b, 4 * e + j, lane) = acc[b][j][e];
     __syncthreads();
+}
 
-    // the sum over the waves of (row block b, column group e) for every lane
-    auto wave_sum = [&](int b, int e, float (&y)[4]) __attribute__((always_inline)) {
+// The sum over the waves of (row block b, column group e) for this lane,
+// in wave order.
+template <bool BIG>
+__device__ __forceinline__ void wave_sum(u32x4 *smem, int b, int e, int lane, float (&y)[4]) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            float s = 0.f;
+    for (int j = 0; j < 4; ++j) {
+        float s = 0.f;
 #pragma unroll
-            for (int w = 0; w < WAVES; ++w)
-                s += red(w, b, 4 * e + j, lane);
-            y[j] = s;
-        }
-    };
-    uint16_t *__restrict__ C = args.C;
-    auto finish = [&](int b, int e, const float (&y)[4]) __attribute__((always_inline)) {
-        const int m = 16 * b + p;
-        const int n = nb + 16 * h + 4 * e;
-        if (m >= M || n >= N)
-            return;
-        float bv[4] = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (EPI != EPI_NONE) {
-            const u32x2 raw = *reinterpret_cast<const u32x2 *>(args.bias + n);
-            bv[0] = T::to_f32((uint16_t)(raw.x & 0xffff));
-            bv[1] = T::to_f32((uint16_t)(raw.x >> 16));
-            bv[2] = T::to_f32((uint16_t)(raw.y & 0xffff));
-            bv[3] = T::to_f32((uint16_t)(raw.y >> 16));
-        }
-        uint16_t o[4];
+        for (int w = 0; w < WAVES; ++w)
+            s += red_at<BIG>(smem, w, b, 4 * e + j, lane);
+        y[j] = s;
+    }
+}
+
+// The epilogue and the 8-byte store of C[16 b + p][n .. n + 3], n = 64 slab
+// + 16 h + 4 e, from the lane's four sums.
+template <class T, int EPI>
+__device__ __forceinline__ void finish(const GemmArgs &args, int slab, int b, int e, int lane, const float (&y)[4]) {
+    const int p = lane & 15;
+    const int h = lane >> 4;
+    const int m = 16 * b + p;
+    const int n = slab * SLAB + 16 * h + 4 * e;
+    if (m >= args.M || n >= args.N)
+        return;
+    float bv[4] = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (EPI != EPI_NONE) {
+        const u32x2 raw = *reinterpret_cast<const u32x2 *>(args.bias + n);
+        bv[0] = T::to_f32((uint16_t)(raw.x & 0xffff));
+        bv[1] = T::to_f32((uint16_t)(raw.x >> 16));
+        bv[2] = T::to_f32((uint16_t)(raw.y & 0xffff));
+        bv[3] = T::to_f32((uint16_t)(raw.y >> 16));
+    }
+    uint16_t o[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            o[j] = T::from_f32(epilogue<EPI>(y[j], bv[j]));
-        *reinterpret_cast<u32x2 *>(C + (uint32_t)m * (uint32_t)N + n) = u32x2{pack2(o[0], o[1]), pack2(o[2], o[3])};
-    };
+    for (int j = 0; j < 4; ++j)
+        o[j] = T::from_f32(epilogue<EPI>(y[j], bv[j]));
+    *reinterpret_cast<u32x2 *>(args.C + (uint32_t)m * (uint32_t)args.N + n) = u32x2{pack2(o[0], o[1]), pack2(o[2], o[3])};
+}
+
+// One workgroup per slab (grid.x), its K range split over grid.y =
+// ws.splits workgroups (split-K, RB = 1; 1: no split).
+template <class T, int EPI, bool PRELOAD, int RB>
+__global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args, SplitWs ws) {
+    __shared__ __attribute__((aligned(16))) u32x4 smem[WAVES * region_floats<PRELOAD>() / 4];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int steps = (args.K + 31) / 32;
+    const int splits = ws.splits;
+    const int split = blockIdx.y;
+    const int sp_begin = (int)(((int64_t)steps * split) / splits);
+    const int sp_len = (int)(((int64_t)steps * (split + 1)) / splits) - sp_begin;
+    slab_part<T, PRELOAD ? A_PRELOAD : A_GLOBAL, RB>(args, smem, blockIdx.x, sp_begin, sp_len);
     if constexpr (RB == 1) {
         // waves 0..3 each finish one of the four column groups e of every lane
-        const int e = wave & 3;
-        float y[4] = {0.f, 0.f, 0.f, 0.f};
-        if (wave < 4)
-            wave_sum(0, e, y);
+        const int e = wave;
+        float y[4];
+        wave_sum<PRELOAD>(smem, 0, e, lane, y);
         if (splits > 1 && !split_exchange(ws, blockIdx.x, split, y, e))
             return;
-        if (wave < 4)
-            finish(0, e, y);
+        finish<T, EPI>(args, blockIdx.x, 0, e, lane, y);
     } else {
         // the 4 RB (row block, column group) pairs are spread over the waves
 #pragma unroll
@@ -328,9 +426,87 @@ __global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args, Sp
             const int q = q0 + wave;
             if (q < 4 * RB) {
                 float y[4];
-                wave_sum(q >> 2, q & 3, y);
-                finish(q >> 2, q & 3, y);
+                wave_sum<PRELOAD>(smem, q >> 2, q & 3, lane, y);
+                finish<T, EPI>(args, blockIdx.x, q >> 2, q & 3, lane, y);
             }
+        }
+    }
+}
+
+// Stream-K (M <= 16): the slabs' 32-k steps, slab after slab, form one
+// sequence of slabs x steps units, cut into gridDim.x equal contiguous
+// ranges, one per workgroup.  A workgroup walks its range slab by slab: a
+// slab it covers whole it finishes itself; its part of a slab it shares
+// (at most two: the first and the last of its range) it publishes as a
+// partial block, and after its whole range it counts its arrival at those
+// slabs, the last to arrive adding the parts in K order and finishing.
+// Deferring the arrivals to the end keeps the wait for the partial stores
+// and the counter round trip out of the middle of the range.  Workgroup g's
+// part of slab s has partial slot g + s (the (slab, workgroup) pairs in
+// sequence order), so the slots of one slab are consecutive.  With every
+// slab the same size, no CU holds more than ceil(slabs x steps /
+// workgroups) steps, where an even split leaves CUs idle whenever the slab
+// count does not divide the CU count (N = 11008: 172 slabs of 128 steps on
+// 256 CUs, 86 steps per workgroup instead of 128).  Each wave stages its A
+// slice through 32 KB of LDS, so one workgroup fills a CU: the limit per CU
+// is its loads in flight, and two workgroups on one CU would leave another
+// idle.
+template <class T, int EPI>
+__global__ __launch_bounds__(NTHREADS) void gemm_skinny_streamk_kernel(GemmArgs args, SplitWs ws) {
+    __shared__ __attribute__((aligned(16))) u32x4 smem[WAVES * region_floats<true>() / 4];
+    __shared__ uint32_t last_of[2];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t steps = (args.K + 31) / 32;
+    const int64_t total = (int64_t)((args.N + SLAB - 1) / SLAB) * steps;
+    const int64_t G = gridDim.x, g = blockIdx.x;
+    // workgroup g covers units [g total / G, (g + 1) total / G); unit x lies
+    // in the range of workgroup ((x + 1) G - 1) / total
+    auto owner = [&](int64_t x) __attribute__((always_inline)) { return (int)(((x + 1) * G - 1) / total); };
+    // the shared slabs of the range: slab, its first workgroup, its parts
+    int sh_slab[2] = {0, 0}, sh_first[2] = {0, 0}, sh_parts[2] = {1, 1};
+    int nsh = 0;
+    const int64_t x1 = (g + 1) * total / G;
+    for (int64_t x = g * total / G; x < x1;) {
+        const int s = (int)(x / steps);
+        const int64_t base = (int64_t)s * steps;
+        const int64_t xe = x1 < base + steps ? x1 : base + steps;
+        slab_part<T, A_STAGED, 1>(args, smem, s, (int)(x - base), (int)(xe - x));
+        float y[4];
+        wave_sum<true>(smem, 0, wave, lane, y);
+        if (x == base && xe == base + steps) {
+            finish<T, EPI>(args, s, 0, wave, lane, y);
+        } else {
+            const int first = owner(base);
+            const int parts = owner(base + steps - 1) - first + 1;
+            part_publish(ws.part + (int64_t)(first + s) * 1024, parts, (int)g - first, y, wave);
+            if (nsh == 0) {
+                sh_slab[0] = s, sh_first[0] = first, sh_parts[0] = parts;
+            } else {
+                sh_slab[1] = s, sh_first[1] = first, sh_parts[1] = parts;
+            }
+            ++nsh;
+        }
+        __syncthreads();   // every wave has read the LDS sums before the next part rewrites them
+        x = xe;
+    }
+    if (nsh == 0)
+        return;
+    // the partial stores are complete before any arrival is counted
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        last_of[0] = part_arrive(ws.count + sh_slab[0], sh_parts[0]);
+        if (nsh > 1)
+            last_of[1] = part_arrive(ws.count + sh_slab[1], sh_parts[1]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        if (i < nsh && last_of[i]) {
+            float y[4];
+            part_sum(ws.part + (int64_t)(sh_first[i] + sh_slab[i]) * 1024, sh_parts[i], y, wave);
+            finish<T, EPI>(args, sh_slab[i], 0, wave, lane, y);
         }
     }
 }
@@ -353,9 +529,15 @@ hipError_t launch_typed(const GemmArgs &a, const SplitWs &ws, hipStream_t stream
             return launch_rows<T, EPI, 4>(a, ws, stream);
         return a.M <= 32 ? launch_rows<T, EPI, 2>(a, ws, stream) : launch_rows<T, EPI, 3>(a, ws, stream);
     }
+    const int64_t steps = (a.K + 31) / 32;
+    if (ws.streamk > 0) {   // 1 <= workgroups <= slabs x steps, checked by the host
+        if ((int64_t)ws.streamk > slabs * steps)
+            return hipErrorInvalidValue;
+        hipLaunchKernelGGL((gemm_skinny_streamk_kernel<T, EPI>), dim3(ws.streamk), dim3(NTHREADS), 0, stream, a, ws);
+        return hipGetLastError();
+    }
     // every wave's share of the 32-k steps is floor or ceil of a split's
     // share / WAVES, and a split's share floor or ceil of steps / splits
-    const int64_t steps = (a.K + 31) / 32;
     const int64_t lo = steps / ws.splits, hi = (steps + ws.splits - 1) / ws.splits;
     if (lo / WAVES > PRE / 2 && (hi + WAVES - 1) / WAVES <= PRE)
         hipLaunchKernelGGL((gemm_skinny_kernel<T, EPI, true, 1>), dim3(slabs, ws.splits), dim3(NTHREADS), 0, stream, a,

@@ -208,7 +208,7 @@ namespace {
 // costs once the workgroups need a second round on the CUs (one workgroup
 // fits a CU): measured on an MI355X, 64 slabs (N = 4096) run 1.8-2.6x faster
 // with 4 splits, 16 slabs 2.4x with 8, while 172 slabs (N = 11008) run 20-50 %
-// slower with any split.  So the count is the largest that keeps
+// slower with any even split.  So the count is the largest that keeps
 // slabs x splits within the CU count, and leaves each workgroup at least
 // kMinSplitSteps 32-k steps.
 constexpr int kMaxSplits = 64;
@@ -222,6 +222,60 @@ int auto_splits(int64_t N, int64_t K, int num_cu) {
     s = s < steps / kMinSplitSteps ? s : steps / kMinSplitSteps;
     s = s < kMaxSplits ? s : kMaxSplits;
     return s > 1 ? static_cast<int>(s) : 1;
+}
+
+// Stream-K of the skinny kernel (TG_SPLIT_STREAM_K): the slabs x steps
+// 32-k steps cut into equal contiguous ranges, one workgroup per CU, at
+// least kMinSplitSteps steps each, at most kMaxStreamKGroups workgroups.
+constexpr int kMaxStreamKGroups = 1024;
+
+int streamk_groups(int64_t N, int64_t K, int num_cu) {
+    if (num_cu <= 0)
+        num_cu = kDefaultCUs;
+    const int64_t total = ((N + 63) / 64) * ((K + 31) / 32);
+    int64_t g = num_cu < kMaxStreamKGroups ? num_cu : kMaxStreamKGroups;
+    g = g < total / kMinSplitSteps ? g : total / kMinSplitSteps;
+    return g > 1 ? static_cast<int>(g) : 1;
+}
+
+// splits 0 on the skinny path: the even split above, or stream-K where it
+// is predicted faster.  Cost in 32-k steps of the busiest CU, each step
+// about 0.166 us on an MI355X whether 172 or 256 CUs stream: rounds of
+// workgroups x steps per workgroup, plus the fixed cost of sharing slabs
+// between workgroups, fitted to measured times of 16-row products (fp16,
+// N = 4096, 11008, 16384, 19200, 28672; K = 512 .. 11008): about 7 us (42
+// steps) for an even split (the partial stores, the counter round trip and
+// the last workgroup's reads, one after the other at the end), about 12 us
+// (71 steps) for stream-K (the same exchange, the loop through staged A
+// slices, and workgroups streaming unrelated rows of B instead of the
+// neighbouring slabs' same rows).  So stream-K pays only for long K where
+// the slabs leave CUs idle (16 x 11008 x 11008: 47.5 against 55.0 us), not
+// at the decode shape (16 x 11008 x 4096: 23.6 against 19.1 us).
+constexpr int64_t kSplitFixedSteps = 42;
+constexpr int64_t kStreamKFixedSteps = 71;
+
+int auto_split_mode(int64_t N, int64_t K, int num_cu) {
+    if (num_cu <= 0)
+        num_cu = kDefaultCUs;
+    const int64_t slabs = (N + 63) / 64, steps = (K + 31) / 32;
+    const int s = auto_splits(N, K, num_cu);
+    const int64_t rounds = (slabs * s + num_cu - 1) / num_cu;
+    const int64_t even = rounds * ((steps + s - 1) / s) + (s > 1 ? kSplitFixedSteps : 0);
+    const int g = streamk_groups(N, K, num_cu);
+    const int64_t per = slabs * steps / g;   // the shorter ranges; the longer have one step more
+    if (per < 1)
+        return s;
+    const int64_t parts = (steps + per - 1) / per + 1;   // the partial blocks a slab's last workgroup reads
+    const int64_t sk = per + 1 + parts + kStreamKFixedSteps;
+    return sk < even ? TG_SPLIT_STREAM_K : s;
+}
+
+// Workspace bytes of the skinny kernel's split mode (splits >= 1, or
+// TG_SPLIT_STREAM_K with `groups` workgroups).
+int64_t skinny_ws_bytes(int64_t slabs, int splits, int groups) {
+    if (splits == TG_SPLIT_STREAM_K)
+        return static_cast<int64_t>(tg::streamk_ws_bytes(slabs, groups));
+    return static_cast<int64_t>(tg::split_ws_bytes(slabs, splits));
 }
 
 constexpr int kDefaultGroupM = 4;
@@ -261,9 +315,12 @@ tg_status run_gemm(tg_path path, tg_tiles tiles, int64_t M, int64_t N, int64_t K
         if (M > 16)   // split-K is for a single row block; more rows run unsplit
             splits = 1;
         if (splits == 0)
-            splits = auto_splits(N, K, num_cu_of(s));
-        if (splits > 1) {
-            const int64_t need = static_cast<int64_t>(tg::split_ws_bytes(slabs, splits));
+            splits = auto_split_mode(N, K, num_cu_of(s));
+        if (K == 0)   // nothing to divide
+            splits = 1;
+        const int groups = splits == TG_SPLIT_STREAM_K ? streamk_groups(N, K, num_cu_of(s)) : 0;
+        if (splits > 1 || splits == TG_SPLIT_STREAM_K) {
+            const int64_t need = skinny_ws_bytes(slabs, splits, groups);
             if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16))
                 return TG_ERR_INVALID_ARG;
             const int64_t na = elements(M, K), nb = elements(K, N), nc = elements(M, N);
@@ -271,7 +328,9 @@ tg_status run_gemm(tg_path path, tg_tiles tiles, int64_t M, int64_t N, int64_t K
                 overlaps(workspace, need, C, 2 * nc) || overlaps(workspace, need, bias, bias ? 2 * N : 0))
                 return TG_ERR_INVALID_ARG;
         }
-        e = tg::launch_skinny(dtype, epilogue, a, tg::split_ws(workspace, slabs, splits), s);
+        e = tg::launch_skinny(dtype, epilogue, a,
+                              groups > 0 ? tg::streamk_ws(workspace, slabs, groups) : tg::split_ws(workspace, slabs, splits),
+                              s);
     } else if (path == TG_PATH_TILED) {
         const int cus = num_cu_of(s);
         const bool al = tiled_aligned(N, K, A, B, bias, C);
@@ -323,22 +382,22 @@ TG_EXPORT tg_status tg_gemm_split_plan(int64_t M, int64_t N, int64_t K, int num_
     if (splits_out == nullptr || workspace_bytes_out == nullptr || M < 0 || N < 0 || K < 0 || N > kMaxDim ||
         K > kMaxDim)
         return TG_ERR_INVALID_ARG;
-    const int splits = (M <= 16 && M > 0 && N > 0) ? auto_splits(N, K, num_cu) : 1;
+    const int splits = (M <= 16 && M > 0 && N > 0 && K > 0) ? auto_split_mode(N, K, num_cu) : 1;
     *splits_out = splits;
-    *workspace_bytes_out = static_cast<int64_t>(tg::split_ws_bytes((N + 63) / 64, splits));
+    *workspace_bytes_out = skinny_ws_bytes((N + 63) / 64, splits, streamk_groups(N, K, num_cu));
     return TG_OK;
 }
 
 TG_EXPORT int64_t tg_gemm_split_workspace_bytes(int64_t N, int splits) {
-    if (N < 0 || N > kMaxDim || splits < 0 || splits > kMaxSplits)
+    if (N < 0 || N > kMaxDim || splits < TG_SPLIT_STREAM_K || splits > kMaxSplits)
         return -1;
-    return static_cast<int64_t>(tg::split_ws_bytes((N + 63) / 64, splits));
+    return skinny_ws_bytes((N + 63) / 64, splits, kMaxStreamKGroups);
 }
 
 TG_EXPORT tg_status tg_gemm_split(int splits, int64_t M, int64_t N, int64_t K, tg_dtype dtype, const void *A,
                                   const void *B, const void *bias, tg_epilogue epilogue, void *C, void *workspace,
                                   int64_t workspace_bytes, void *stream) {
-    if (splits < 0 || splits > kMaxSplits || workspace_bytes < 0)
+    if (splits < TG_SPLIT_STREAM_K || splits > kMaxSplits || workspace_bytes < 0)
         return TG_ERR_INVALID_ARG;
     return run_gemm(TG_PATH_AUTO, TG_TILES_AUTO, M, N, K, dtype, A, B, bias, epilogue, C, stream, splits, workspace,
                     workspace_bytes);
@@ -354,7 +413,7 @@ namespace {
 // code `scratch` only names the host-side stand-in of the symbol: the device
 // address of each GPU's copy comes from hipGetSymbolAddress, taken once per
 // device with that device current, and only that address is used.
-constexpr int64_t kScratchCounterBytes = int64_t(64) << 10;   // 16384 slab counters
+constexpr int64_t kScratchCounterBytes = tg::kSplitCounterBytes;   // 16384 slab counters, as in a workspace
 constexpr int64_t kScratchPartialBytes = int64_t(4) << 20;    // 1024 partial blocks of 16 x 64 fp32
 constexpr int64_t kScratchBytes = kScratchCounterBytes + kScratchPartialBytes;
 static_assert(kScratchBytes == TG_SCRATCH_BYTES, "tg_gemm.h states the scratch size");
@@ -410,21 +469,23 @@ void *scratch_of(hipStream_t stream) {
 TG_EXPORT tg_status tg_gemm_split_static(int splits, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
                                          const void *A, const void *B, const void *bias, tg_epilogue epilogue,
                                          void *C, void *stream) {
-    if (splits < 0 || splits > kMaxSplits)
+    if (splits < TG_SPLIT_STREAM_K || splits > kMaxSplits)
         return TG_ERR_INVALID_ARG;
     const Checked c = check_args(M, N, K, dtype, A, B, bias, epilogue, C);
     if (c.status != TG_OK || c.noop)
         return c.status;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const tg_path path = auto_path(M, N, K, A, B, bias, C);
-    if (path != TG_PATH_SKINNY || M > 16)   // no split, no workspace: exactly tg_gemm
+    if (path != TG_PATH_SKINNY || M > 16 || K == 0)   // no split, no workspace: exactly tg_gemm
         return run_gemm(TG_PATH_AUTO, TG_TILES_AUTO, M, N, K, dtype, A, B, bias, epilogue, C, stream);
     if (splits == 0)
-        splits = auto_splits(N, K, num_cu_of(s));
-    if (splits <= 1)
+        splits = auto_split_mode(N, K, num_cu_of(s));
+    if (splits == 1)
         return run_gemm(TG_PATH_AUTO, TG_TILES_AUTO, M, N, K, dtype, A, B, bias, epilogue, C, stream);
     const int64_t slabs = (N + 63) / 64;
-    if (slabs * 4 > kScratchCounterBytes || slabs * splits * 4096 > kScratchPartialBytes)
+    const int groups = splits == TG_SPLIT_STREAM_K ? streamk_groups(N, K, num_cu_of(s)) : 0;
+    const int64_t parts = groups > 0 ? groups + slabs - 1 : slabs * splits;
+    if (slabs * 4 > kScratchCounterBytes || parts * 4096 > kScratchPartialBytes)
         return TG_ERR_UNSUPPORTED;
     char *ws = static_cast<char *>(scratch_of(s));
     if (ws == nullptr)
@@ -439,7 +500,8 @@ TG_EXPORT tg_status tg_gemm_split_static(int splits, int64_t M, int64_t N, int64
     a.bias = static_cast<const uint16_t *>(bias);
     a.C = static_cast<uint16_t *>(C);
     tg::SplitWs w;
-    w.splits = splits;
+    w.splits = groups > 0 ? 1 : splits;
+    w.streamk = groups;
     w.count = reinterpret_cast<uint32_t *>(ws);
     w.part = reinterpret_cast<float *>(ws + kScratchCounterBytes);
     const hipError_t e = tg::launch_skinny(dtype, epilogue, a, w, s);

@@ -58,27 +58,53 @@ hipError_t launch_tiled_generic(int dtype, int epi, const GemmArgs &a, hipStream
 // No workgroup waits for another.
 struct SplitWs {
     int splits;          // 1: no workspace (part, count unused)
-    float *part;         // [block][split][1024], 16-byte aligned
+    float *part;         // [block][split][1024], 16-byte aligned; stream-K: [slot][1024]
     uint32_t *count;     // [block], zero before the launch, zero after it
+    int streamk = 0;     // > 0: stream-K over this many workgroups (M <= 16 skinny kernel; splits unused)
 };
-// Bytes of workspace for `blocks` output blocks and `splits` splits: the
-// counters (padded to 256 bytes), then the partial blocks.
+// Workspace layout of the split modes: the per-block arrival counters
+// first, in a region of at least 64 KiB (16384 blocks) so that the partial
+// blocks after it start at the same place for every shape up to that many
+// blocks, and a partial block of one call never lands on the counters of
+// another call through the same workspace; then the partial blocks.
+constexpr int64_t kSplitCounterBytes = int64_t(64) << 10;
+inline int64_t split_counter_bytes(int64_t blocks) {
+    const int64_t c = (blocks * 4 + 255) / 256 * 256;
+    return c > kSplitCounterBytes ? c : kSplitCounterBytes;
+}
+// Bytes of workspace for `blocks` output blocks and `splits` splits.
 inline size_t split_ws_bytes(int64_t blocks, int splits) {
-    if (splits <= 1)
+    if (splits <= 1 || blocks <= 0)
         return 0;
-    return (size_t)((blocks * 4 + 255) / 256 * 256) + (size_t)blocks * (size_t)splits * 4096u;
+    return (size_t)split_counter_bytes(blocks) + (size_t)blocks * (size_t)splits * 4096u;
 }
 inline SplitWs split_ws(void *ws, int64_t blocks, int splits) {
     SplitWs w{splits, nullptr, nullptr};
     if (splits > 1) {
         w.count = static_cast<uint32_t *>(ws);
-        w.part = reinterpret_cast<float *>(static_cast<char *>(ws) + (blocks * 4 + 255) / 256 * 256);
+        w.part = reinterpret_cast<float *>(static_cast<char *>(ws) + split_counter_bytes(blocks));
     }
     return w;
 }
+// Stream-K over `groups` workgroups: the counters of `blocks` slabs, then
+// one partial block per (slab, workgroup) pair, groups + blocks - 1 of them.
+inline size_t streamk_ws_bytes(int64_t blocks, int groups) {
+    if (blocks <= 0)
+        return 0;
+    return (size_t)split_counter_bytes(blocks) + (size_t)(groups + blocks - 1) * 4096u;
+}
+inline SplitWs streamk_ws(void *ws, int64_t blocks, int groups) {
+    SplitWs w{1, nullptr, nullptr};
+    w.streamk = groups;
+    w.count = static_cast<uint32_t *>(ws);
+    w.part = reinterpret_cast<float *>(static_cast<char *>(ws) + split_counter_bytes(blocks));
+    return w;
+}
 
-// M <= 16, K % 8 == 0, N % 4 == 0, aligned operands; ws.splits >= 1 (at most
-// ceil(K / 32)), its workspace laid out by split_ws for ceil(N / 64) blocks.
+// M <= 64, K % 8 == 0, N % 4 == 0, aligned operands; ws.splits >= 1 (at most
+// ceil(K / 32)), its workspace laid out by split_ws for ceil(N / 64) blocks,
+// or (M <= 16) ws.streamk workgroups, 1 .. ceil(N / 64) ceil(K / 32), with
+// the workspace of streamk_ws.
 hipError_t launch_skinny(int dtype, int epi, const GemmArgs &a, const SplitWs &ws, hipStream_t stream);
 
 // Weight-only 4-bit product: packed weights in the layout of launch_w4_pack,
