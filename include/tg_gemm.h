@@ -58,19 +58,27 @@
 extern "C" {
 #endif
 
-typedef enum { TG_F16 = 0, TG_BF16 = 1 } tg_dtype;
+/*
+ * Every enum below has a last enumerator of INT_MIN (-0x7fffffff - 1): the
+ * type is then an int whose every value is a value of the type, so a caller
+ * may pass any int and the library's checks (not undefined behaviour)
+ * decide what it means.
+ */
+typedef enum { TG_F16 = 0, TG_BF16 = 1, TG_DTYPE_FORCE_INT = -0x7fffffff - 1 } tg_dtype;
 
 typedef enum {
     TG_EPI_NONE = 0,
     TG_EPI_BIAS = 1,
-    TG_EPI_BIAS_GELU_TANH = 2
+    TG_EPI_BIAS_GELU_TANH = 2,
+    TG_EPILOGUE_FORCE_INT = -0x7fffffff - 1
 } tg_epilogue;
 
 typedef enum {
     TG_OK = 0,
     TG_ERR_INVALID_ARG = 1,
     TG_ERR_UNSUPPORTED = 2,
-    TG_ERR_LAUNCH = 3
+    TG_ERR_LAUNCH = 3,
+    TG_STATUS_FORCE_INT = -0x7fffffff - 1
 } tg_status;
 
 /*
@@ -101,7 +109,8 @@ typedef enum {
     TG_PATH_TILED = 1,
     TG_PATH_TILED_GENERIC = 2,
     TG_PATH_SKINNY = 3,
-    TG_PATH_NONE = 4
+    TG_PATH_NONE = 4,
+    TG_PATH_FORCE_INT = -0x7fffffff - 1
 } tg_path;
 
 /*
@@ -178,7 +187,8 @@ typedef enum {
     TG_TILES_256x128_K64 = 6,
     TG_TILES_128x256_K64 = 7,
     TG_TILES_128x128_K64 = 8,
-    TG_TILES_256x256_W8 = 9
+    TG_TILES_256x256_W8 = 9,
+    TG_TILES_FORCE_INT = -0x7fffffff - 1
 } tg_tiles;
 
 /*
@@ -340,7 +350,8 @@ tg_status tg_gemm_split_static(int splits, int64_t M, int64_t N, int64_t K, tg_d
  */
 typedef enum {
     TG_EW_BIAS_ADD = 0,
-    TG_EW_GELU_TANH = 1
+    TG_EW_GELU_TANH = 1,
+    TG_EW_FORCE_INT = -0x7fffffff - 1
 } tg_elementwise_op;
 
 tg_status tg_elementwise(tg_elementwise_op op, int64_t M, int64_t N, tg_dtype dtype,

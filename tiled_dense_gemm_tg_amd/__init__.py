@@ -17,7 +17,9 @@ from typing import Optional
 from .inputs import BF16, EPI_BIAS, EPI_BIAS_GELU_TANH, EPI_NONE, F16  # noqa: F401
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIBRARY = os.path.join(PKG, "libtg_gemm.so")
+# TG_GEMM_LIBRARY lets the sanitizer test load an instrumented build of the
+# same sources.
+LIBRARY = os.environ.get("TG_GEMM_LIBRARY") or os.path.join(PKG, "libtg_gemm.so")
 
 TG_OK = 0
 TG_ERR_INVALID_ARG = 1
