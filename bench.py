@@ -343,6 +343,15 @@ def tiled_launcher(torch, tg, M, N, K, dtype, epi, A, B, bias, C, cfg, label, gr
     return launch
 
 
+def axes_of(tg, cfg):
+    """The tuning axes of a tile configuration, with the raster group the
+    library uses unless a call picks another (tg_gemm_tiled_grouped)."""
+    if cfg not in tg.TILES_AXES:
+        return None
+    bm, bn, bk, stages, waves = tg.TILES_AXES[cfg]
+    return {"BM": bm, "BN": bn, "BK": bk, "stages": stages, "waves": waves, "group_m": 4}
+
+
 def bench_tile_choice(torch, tg, I, steps, warmup):
     """Every tile configuration, and the library's own choice, on the shape
     classes the choice is for, timed in alternating blocks."""
@@ -361,10 +370,12 @@ def bench_tile_choice(torch, tg, I, steps, warmup):
         ms_auto = per.pop("auto")
         st, auto = tg.tg_gemm_tiles_plan(w.M, w.N, w.K, cus)
         best = min(per, key=per.get)
-        out[name] = {"auto": tg.TILES_NAMES.get(auto, "?"), "auto_us": round(ms_auto * 1e3, 2),
+        out[name] = {"auto": tg.TILES_NAMES.get(auto, "?"), "auto_axes": axes_of(tg, auto),
+                     "auto_us": round(ms_auto * 1e3, 2),
                      "auto_TFLOP/s": round(flops / (ms_auto * 1e-3) / 1e12, 1),
                      "per_config_us": {k: round(v * 1e3, 2) for k, v in per.items()},
-                     "fastest": best, "auto_vs_fastest": round(per[best] / ms_auto, 3),
+                     "fastest": best, "fastest_axes": axes_of(tg, configs[best]),
+                     "auto_vs_fastest": round(per[best] / ms_auto, 3),
                      "speedup_vs_256x256": round(per["256x256"] / ms_auto, 3),
                      "traffic": measured_traffic(f"{name} auto")}
         log(f"{name}: auto {tg.TILES_NAMES.get(auto)} {ms_auto * 1e3:.1f} us, fastest {best} "
