@@ -757,6 +757,10 @@ def _alg(label: str, I, tg):
 
 MFMA_COUNTERS = ["SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES",
                  "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE"]
+# LDS occupancy and MFMA / VALU overlap: a pass of its own (at most 8 SQ
+# counters per pass)
+LDS_COUNTERS = ["SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT", "SQ_ACTIVE_INST_LDS", "SQ_VALU_MFMA_BUSY_CYCLES",
+                "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_INSTS_VALU_TRANS_F32", "GRBM_GUI_ACTIVE"]
 PROFILE_COMMANDS = {
     "bench": "python3 bench.py > <out>/bench.json",
     "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d <out>/trace -o run -- "
@@ -772,6 +776,8 @@ PROFILE_COMMANDS = {
                   "python3 bench.py --copy-calibration 1024",
     "mfma": "rocprofv3 --pmc " + " ".join(MFMA_COUNTERS) + " --output-format csv -d <out>/mfma -o run -- "
             "python3 bench.py --profile-run --dispatch-log <out>/mfma/dispatch_log.json",
+    "lds": "rocprofv3 --pmc " + " ".join(LDS_COUNTERS) + " --output-format csv -d <out>/lds -o run -- "
+           "python3 bench.py --profile-run --dispatch-log <out>/lds/dispatch_log.json",
     "summarise": "python3 bench.py --summarise <out>",
 }
 
@@ -880,6 +886,33 @@ def summarise_profiles(run_dir: str, out_dir: str) -> None:
                      f"{mops / flops if flops else float('nan'):.3f} | {rec['lds_instructions']:.0f} | "
                      f"{rec['lds_bank_conflicts']:.0f} |")
         record["lines"][lab] = rec
+    lds_dir = os.path.join(run_dir, "lds")
+    if os.path.isdir(lds_dir):
+        lds = _group(_dispatches(lds_dir, "**/*counter_collection.csv", True))
+        m += ["", "LDS occupancy and MFMA / VALU overlap (the `lds` pass), per dispatch, then the mean:",
+              "* LDS busy = SQ_LDS_IDX_ACTIVE / (256 CUs x GRBM_GUI_ACTIVE / 8): the fraction of CU cycles in "
+              "which the LDS serves indexed (ds_*) accesses; the direct-to-LDS buffer loads are not indexed "
+              "accesses;",
+              "* MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8), as above;",
+              "* co-issue = SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES: the share of the matrix "
+              "core's busy cycles in which the same SIMD's VALU also issued;",
+              "* VALU active = SQ_ACTIVE_INST_VALU x 4 (quad-cycles) / (1024 x GRBM_GUI_ACTIVE / 8);",
+              "* exp2/rcp per SIMD cycle = SQ_INSTS_VALU_TRANS_F32 / (1024 x GRBM_GUI_ACTIVE / 8).", "",
+              "| bench line | duration us | LDS busy | MFMA busy | co-issue | VALU active | trans instr / SIMD cycle |",
+              "|---|---|---|---|---|---|---|"]
+        for lab, rs in lds.items():
+            if lab.startswith(("w4 weight packing", "sweep")):
+                continue
+            simd = [1024 * r["GRBM_GUI_ACTIVE"] / 8 for r in rs]
+            busy = _mean([r["SQ_LDS_IDX_ACTIVE"] / (256 * r["GRBM_GUI_ACTIVE"] / 8) for r in rs])
+            mb = _mean([r["SQ_VALU_MFMA_BUSY_CYCLES"] / c for r, c in zip(rs, simd)])
+            co = _mean([r["SQ_VALU_MFMA_COEXEC_CYCLES"] / max(r["SQ_VALU_MFMA_BUSY_CYCLES"], 1) for r in rs])
+            va = _mean([4 * r["SQ_ACTIVE_INST_VALU"] / c for r, c in zip(rs, simd)])
+            tr = _mean([r["SQ_INSTS_VALU_TRANS_F32"] / c for r, c in zip(rs, simd)])
+            m.append(f"| {lab} | {_mean([r['dur_us'] for r in rs]):.1f} | {busy:.3f} | {mb:.3f} | {co:.3f} | "
+                     f"{va:.3f} | {tr:.4f} |")
+            if lab in record["lines"]:
+                record["lines"][lab].update({"lds_busy": round(busy, 4), "mfma_valu_coissue": round(co, 4)})
     with open(os.path.join(out_dir, "hbm_traffic.md"), "w") as fh:
         fh.write("\n".join(h) + "\n")
     with open(os.path.join(out_dir, "counters_mfma_lds.md"), "w") as fh:
