@@ -34,7 +34,10 @@
 //   * split-K (splits > 1, a grid of slabs x splits): when there are too few
 //     slabs to fill the chip, each slab's K range is also divided over
 //     `splits` workgroups, which pass their partial slabs through a
-//     workspace; the last to arrive adds them in split order and finishes.
+//     workspace; the last to arrive adds them in split order and finishes;
+//   * stream-K (a grid of one workgroup per CU): the 32-k steps of all slabs
+//     cut into equal contiguous ranges, shared slabs meeting in the same
+//     workspace (gemm_skinny_streamk_kernel below).
 // Loads are range-checked buffer loads; k >= K reads zero in both operands.
 #include "tg_device.h"
 #include "tg_launch.h"

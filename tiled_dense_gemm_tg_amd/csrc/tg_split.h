@@ -1,12 +1,13 @@
 // tg_split.h -- the cross-workgroup step of split-K in the M <= 16 kernels.
 //
-// With splits > 1 several workgroups compute partial sums of the same 16 x 64
-// output block over parts of the K range.  Each publishes its partial block
+// Several workgroups compute partial sums of the same 16 x 64 output block
+// over parts of the K range (an even split of every block's K range, or the
+// stream-K ranges of the skinny kernel).  Each publishes its partial block
 // to the workspace and counts itself in the block's counter; the last to
-// arrive reads every split's partial, adds them in split order (so the sum
-// does not depend on which workgroup came last), finishes the block and
-// resets the counter to zero.  No workgroup ever waits for another, so no
-// schedule of the workgroups can deadlock.
+// arrive reads every part, adds them in K order (so the sum does not depend
+// on which workgroup came last), finishes the block and resets the counter
+// to zero.  No workgroup ever waits for another, so no schedule of the
+// workgroups can deadlock.
 //
 // Visibility without cache-wide fences: the partials are stored and loaded
 // at device scope (sc1: written through to, and read from, the level all
