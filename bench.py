@@ -109,10 +109,17 @@ def attention_flops(B: int, H: int, D: int, Sq: int, Sk: int, causal: bool) -> i
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources with comments and runs of white space
+    removed: a change of comments alone leaves the compiled kernels, and so
+    the counters taken on them, as they were."""
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "tiled_dense_gemm_tg_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "tiled_dense_gemm_tg_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
