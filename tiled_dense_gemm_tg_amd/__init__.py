@@ -190,8 +190,8 @@ def tg_gemm_split_plan(M, N, K, num_cu=0):
 
 def split_workspace(M, N, K, splits=0, device=None):
     """A zero-filled workspace (uint8 torch tensor) for tg_gemm_split with
-    `splits` (0: the count the library chooses on `device`), or None when
-    that needs none."""
+    `splits` (0: the mode the library chooses on `device`; TG_SPLIT_STREAM_K:
+    enough for stream-K on any device), or None when that needs none."""
     import torch
     device = torch.device("cuda" if device is None else device)
     if splits == 0:
@@ -288,7 +288,8 @@ def gemm(A, B, bias=None, epilogue: str = "none", out=None, path: int = TG_PATH_
     ``path`` must then be TG_PATH_AUTO or TG_PATH_TILED); ``group_m`` > 0 sets
     the tile rows per raster group of that call (tg_gemm_tiled_grouped).
     ``splits`` (0 for
-    the library's choice) calls tg_gemm_split with ``workspace`` (a
+    the library's choice, 2..64 even splits, TG_SPLIT_STREAM_K for stream-K
+    over the CUs) calls tg_gemm_split with ``workspace`` (a
     zero-filled uint8 GPU tensor from :func:`split_workspace`, allocated here
     when not given; reuse one per stream to skip that); ``path`` must then be
     TG_PATH_AUTO.
