@@ -24,10 +24,11 @@
 //     every wave has 17 to 32 steps (K = 4096: 32) a wave first copies its
 //     whole slice of A into its own 32 KB of LDS by direct loads of 4 rows x
 //     256 contiguous bytes and reads it into registers in the MFMA layout,
-//     so that its loop streams only B;
+//     so that its loop streams only B; with more steps, the slice goes
+//     through the same 32 KB in chunks, read from LDS step by step;
 //   * 17 <= M <= 64: two to four such 16-row blocks of A per workgroup,
 //     each with its own MFMAs on the same transposed B vectors, so B is
-//     still read once (A then comes from L2 in every step; no preload);
+//     still read once; their slices of A are staged in chunks the same way;
 //   * the 4 waves' fp32 partial sums are added in LDS in a fixed order (no
 //     atomics, so results are reproducible), then the fused epilogue and
 //     8-byte stores;
@@ -83,8 +84,9 @@ __device__ __forceinline__ float &red_at(u32x4 *smem, int w, int b, int i, int l
 //   A_GLOBAL   16-byte loads from L2 in every step, beside B's;
 //   A_PRELOAD  the wave's whole slice (PRE / 2 < steps <= PRE) into LDS by
 //              direct loads, then into registers, before the loop;
-//   A_STAGED   the wave's steps in chunks of at most PRE: each chunk's slice
-//              into LDS by direct loads, then one 16-byte LDS read per step.
+//   A_STAGED   the wave's steps in chunks of at most PRE / RB (a multiple of
+//              4): each chunk's slice of every row block into LDS by direct
+//              loads, then one 16-byte LDS read per step and row block.
 constexpr int A_GLOBAL = 0, A_PRELOAD = 1, A_STAGED = 2;
 
 // RB: 16-row blocks of A (and C) per workgroup, 1..4 (M <= 16 RB).  Every
@@ -100,7 +102,7 @@ constexpr int A_GLOBAL = 0, A_PRELOAD = 1, A_STAGED = 2;
 // barrier that makes them visible to every wave.
 template <class T, int AMODE, int RB>
 __device__ __forceinline__ void slab_part(const GemmArgs &args, u32x4 *smem, int slab, int sp_begin, int sp_len) {
-    static_assert(RB >= 1 && RB <= 4 && (RB == 1 || AMODE == A_GLOBAL), "row blocks");
+    static_assert(RB >= 1 && RB <= 4 && (RB == 1 || AMODE != A_PRELOAD), "row blocks");
     constexpr bool PRELOAD = AMODE == A_PRELOAD;
     constexpr bool BIG = AMODE != A_GLOBAL;
     constexpr int RS = region_floats<BIG>();
@@ -269,19 +271,24 @@ __device__ __forceinline__ void slab_part(const GemmArgs &args, u32x4 *smem, int
             __builtin_amdgcn_sched_barrier(0);
         }
     } else if constexpr (AMODE == A_STAGED) {
-        // Chunks of at most PRE steps of the wave's range.  A chunk's slice
-        // of A goes to the wave's LDS region by the direct loads of the
-        // preload (same layout and swizzle), only its ceil(n / 4) groups of
-        // 4 steps; steps past the chunk read zero in both operands, and every
-        // group of 4 steps the loop touches was loaded (so no stale LDS data
-        // reaches an MFMA).  The chunk's first two batches of B go out around
-        // the A loads, as in the preload.
+        // Chunks of at most CH steps of the wave's range.  A chunk's slice of
+        // each row block b goes to block b's part of the wave's LDS region
+        // (CH / 4 pieces of 4 KB) by the direct loads of the preload (same
+        // layout and swizzle), only its ceil(n / 4) groups of 4 steps: 4 rows
+        // x 256 contiguous bytes per load, whole cache lines, where a
+        // 16-byte A load per step takes half lines.  Steps past the chunk
+        // read zero in both operands, and every group of 4 steps the loop
+        // touches was loaded (so no stale LDS data reaches an MFMA).  The
+        // chunk's first two batches of B go out around the A loads, as in
+        // the preload.
+        constexpr int CH = PRE / RB / 4 * 4;
+        static_assert(CH >= 4 && RB * CH * 1024 <= 4 * RS, "staged slices fit the wave's region");
         const uint32_t region = lds_address(smem) + 4u * RS * (uint32_t)wave;
         const i32x4 rs = rsrc_words((const char *)A - ASHIFT, 2u * (uint32_t)M * (uint32_t)K + ASHIFT);
         const int r0 = lane >> 4;
         const int slot = lane & 15;
-        for (int c0 = s_begin; c0 < s_end; c0 += PRE) {
-            const int cn = min(PRE, s_end - c0);
+        for (int c0 = s_begin; c0 < s_end; c0 += CH) {
+            const int cn = min(CH, s_end - c0);
             const int c_end = c0 + cn;
             auto load_b = [&](u32x2 (&vb)[UNROLL][8], int s0) __attribute__((always_inline)) {
 #pragma unroll
@@ -295,28 +302,41 @@ __device__ __forceinline__ void slab_part(const GemmArgs &args, u32x4 *smem, int
                                                                         0, CPOL_NT);
                 }
             };
-            auto a_at = [&](int i) __attribute__((always_inline)) {
+            // the 16-byte A fragment of row block b, chunk step i
+            auto a_at = [&](int b, int i) __attribute__((always_inline)) {
                 const uint32_t c = (uint32_t)((4 * (i & 3) + h) ^ p);
                 return *(__attribute__((address_space(3))) const u32x4 *)(uintptr_t)(
-                    region + 4096u * (uint32_t)(i >> 2) + 256u * (uint32_t)p + 16u * c);
+                    region + 1024u * CH * (uint32_t)b + 4096u * (uint32_t)(i >> 2) + 256u * (uint32_t)p + 16u * c);
+            };
+            auto a_pair = [&](int i) __attribute__((always_inline)) {
+                ABatch<RB> va;
+#pragma unroll
+                for (int u = 0; u < UNROLL; ++u)
+#pragma unroll
+                    for (int b = 0; b < RB; ++b)
+                        va.v[u][b] = a_at(b, i + u);
+                return va;
             };
             load_b(vb0, c0);
             {
                 const int kend = min(K, 32 * c_end);
 #pragma unroll
-                for (int c4 = 0; c4 < PRE / 4; ++c4) {
-                    if (4 * c4 < cn) {
+                for (int b = 0; b < RB; ++b)
 #pragma unroll
-                        for (int rq = 0; rq < 4; ++rq) {
-                            const int r = 4 * rq + r0;
-                            const int k = 32 * c0 + 128 * c4 + 8 * (slot ^ r);
-                            const uint32_t off =
-                                (ASHIFT - 1024u * (uint32_t)rq + 2u * ((uint32_t)r * (uint32_t)K + (uint32_t)k)) +
-                                (k < kend ? 0u : 0x80000000u);
-                            dma16_rq(rq, rs, off, region + 4096u * (uint32_t)c4);
+                    for (int c4 = 0; c4 < CH / 4; ++c4) {
+                        if (4 * c4 < cn) {
+#pragma unroll
+                            for (int rq = 0; rq < 4; ++rq) {
+                                // row 16 b + r of A; rows >= M lie past the buffer and read zero
+                                const int r = 16 * b + 4 * rq + r0;
+                                const int k = 32 * c0 + 128 * c4 + 8 * (slot ^ (r & 15));
+                                const uint32_t off =
+                                    (ASHIFT - 1024u * (uint32_t)rq + 2u * ((uint32_t)r * (uint32_t)K + (uint32_t)k)) +
+                                    (k < kend ? 0u : 0x80000000u);
+                                dma16_rq(rq, rs, off, region + 1024u * CH * (uint32_t)b + 4096u * (uint32_t)c4);
+                            }
                         }
                     }
-                }
             }
             load_b(vb1, c0 + UNROLL);
             // the chunk's A loads are older than the second batch's 8 UNROLL B loads
@@ -325,12 +345,12 @@ __device__ __forceinline__ void slab_part(const GemmArgs &args, u32x4 *smem, int
                 if (i > 0)
                     load_b(vb1, c0 + i + UNROLL);
                 __builtin_amdgcn_sched_barrier(0);
-                mma_batch(vb0, u32x4_pair(a_at(i), a_at(i + 1)));
+                mma_batch(vb0, a_pair(i));
                 __builtin_amdgcn_sched_barrier(0);
                 if (i + 2 * UNROLL < cn)
                     load_b(vb0, c0 + i + 2 * UNROLL);
                 __builtin_amdgcn_sched_barrier(0);
-                mma_batch(vb1, u32x4_pair(a_at(i + 2), a_at(i + 3)));
+                mma_batch(vb1, a_pair(i + UNROLL));
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -403,9 +423,10 @@ __device__ __forceinline__ void finish(const GemmArgs &args, int slab, int b, in
 
 // One workgroup per slab (grid.x), its K range split over grid.y =
 // ws.splits workgroups (split-K, RB = 1; 1: no split).
-template <class T, int EPI, bool PRELOAD, int RB>
+template <class T, int EPI, int AMODE, int RB>
 __global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args, SplitWs ws) {
-    __shared__ __attribute__((aligned(16))) u32x4 smem[WAVES * region_floats<PRELOAD>() / 4];
+    constexpr bool BIG = AMODE != A_GLOBAL;
+    __shared__ __attribute__((aligned(16))) u32x4 smem[WAVES * region_floats<BIG>() / 4];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int steps = (args.K + 31) / 32;
@@ -413,12 +434,12 @@ __global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args, Sp
     const int split = blockIdx.y;
     const int sp_begin = (int)(((int64_t)steps * split) / splits);
     const int sp_len = (int)(((int64_t)steps * (split + 1)) / splits) - sp_begin;
-    slab_part<T, PRELOAD ? A_PRELOAD : A_GLOBAL, RB>(args, smem, blockIdx.x, sp_begin, sp_len);
+    slab_part<T, AMODE, RB>(args, smem, blockIdx.x, sp_begin, sp_len);
     if constexpr (RB == 1) {
         // waves 0..3 each finish one of the four column groups e of every lane
         const int e = wave;
         float y[4];
-        wave_sum<PRELOAD>(smem, 0, e, lane, y);
+        wave_sum<BIG>(smem, 0, e, lane, y);
         if (splits > 1 && !split_exchange(ws, blockIdx.x, split, y, e))
             return;
         finish<T, EPI>(args, blockIdx.x, 0, e, lane, y);
@@ -429,7 +450,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(GemmArgs args, Sp
             const int q = q0 + wave;
             if (q < 4 * RB) {
                 float y[4];
-                wave_sum<PRELOAD>(smem, q >> 2, q & 3, lane, y);
+                wave_sum<BIG>(smem, q >> 2, q & 3, lane, y);
                 finish<T, EPI>(args, blockIdx.x, q >> 2, q & 3, lane, y);
             }
         }
@@ -514,11 +535,27 @@ __global__ __launch_bounds__(NTHREADS) void gemm_skinny_streamk_kernel(GemmArgs 
     }
 }
 
+// The instances without the preload (row blocks, and one block where the
+// preload does not apply) stage A through LDS in chunks, except where every
+// wave has at most kGlobalASteps 32-k steps: there the chunk's start-up
+// costs more than the half-line A loads.  Measured on an MI355X (fp16,
+// rotating weight sets): 32 x 11008 x 4096 25.8 -> 22.2 us, 48 rows 30.0 ->
+// 24.7 us, 64 rows 33.9 -> 26.7 us, 16 x 11008 x 8192 40.7 -> 37.9 us,
+// 16 x 11008 x 11008 55.0 -> 50.8 us; 16 x 4096 x 4096 in 4 splits (8 steps
+// per wave) 10.1 -> 10.5 us, hence the threshold.
+constexpr int kGlobalASteps = 8;
+
 template <class T, int EPI, int RB>
 hipError_t launch_rows(const GemmArgs &a, const SplitWs &ws, hipStream_t stream) {
     const int slabs = (a.N + SLAB - 1) / SLAB;
-    hipLaunchKernelGGL((gemm_skinny_kernel<T, EPI, false, RB>), dim3(slabs, ws.splits), dim3(NTHREADS), 0, stream, a,
-                       ws);
+    const int64_t steps = (a.K + 31) / 32;
+    const int64_t hi = (steps + ws.splits - 1) / ws.splits;   // a split's share, rounded up
+    if ((hi + WAVES - 1) / WAVES <= kGlobalASteps)
+        hipLaunchKernelGGL((gemm_skinny_kernel<T, EPI, A_GLOBAL, RB>), dim3(slabs, ws.splits), dim3(NTHREADS), 0,
+                           stream, a, ws);
+    else
+        hipLaunchKernelGGL((gemm_skinny_kernel<T, EPI, A_STAGED, RB>), dim3(slabs, ws.splits), dim3(NTHREADS), 0,
+                           stream, a, ws);
     return hipGetLastError();
 }
 
@@ -543,7 +580,7 @@ hipError_t launch_typed(const GemmArgs &a, const SplitWs &ws, hipStream_t stream
     // share / WAVES, and a split's share floor or ceil of steps / splits
     const int64_t lo = steps / ws.splits, hi = (steps + ws.splits - 1) / ws.splits;
     if (lo / WAVES > PRE / 2 && (hi + WAVES - 1) / WAVES <= PRE)
-        hipLaunchKernelGGL((gemm_skinny_kernel<T, EPI, true, 1>), dim3(slabs, ws.splits), dim3(NTHREADS), 0, stream, a,
+        hipLaunchKernelGGL((gemm_skinny_kernel<T, EPI, A_PRELOAD, 1>), dim3(slabs, ws.splits), dim3(NTHREADS), 0, stream, a,
                            ws);
     else
         return launch_rows<T, EPI, 1>(a, ws, stream);

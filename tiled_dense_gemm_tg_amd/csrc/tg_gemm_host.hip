@@ -74,12 +74,13 @@ Checked check_args(int64_t M, int64_t N, int64_t K, int dtype, const void *A, co
 
 // The skinny kernel carries up to four 16-row blocks of A per workgroup.
 constexpr int64_t kSkinnyMaxM = 64;
-// Above 16 rows the skinny kernel re-reads A from L2 in every step and beats
-// the tiled family only while its 64-column slabs fit one round of
-// workgroups (one per CU): measured on an MI355X at K = 4096, M = 17..48
-// runs 1.3-1.8x faster than tiled for N = 4096 .. 16384 (N = 11008: M = 32 in
-// 26.9 against 42.4 us, M = 64 in 33.8 against 43.6 us), but 1.1-1.35x
-// slower for N = 28672 (448 slabs).
+// Above 16 rows the skinny kernel beats the tiled family only while its
+// 64-column slabs fit one round of workgroups (one per CU): measured on an
+// MI355X at K = 4096 (A staged through LDS), M = 17..64 runs 1.5-2.0x faster
+// than tiled for N = 4096 .. 16384 (N = 11008: M = 32 in 22.2 against 42.1
+// us, M = 64 in 26.7 against 43.3 us; N = 16384: 26.3-30.1 against 43.0-45.0
+// us), but 1.05-1.4x slower for N = 16388 .. 28672 (257-448 slabs: a second
+// round of slabs).
 constexpr int64_t kRowBlocksMaxN = 256 * 64;
 
 bool skinny_ok(int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *bias, const void *C) {
