@@ -123,15 +123,19 @@ def test_skinny_every_row_count(dtype):
 
 
 @pytest.mark.parametrize("dtype", [I.F16, I.BF16])
-def test_skinny_row_blocks_every_row_count(dtype):
+@pytest.mark.parametrize("K", [8 * 75, 2056])
+def test_skinny_row_blocks_every_row_count(dtype, K):
     # 17 <= M <= 64: the skinny kernel carries 2, 3 or 4 blocks of 16 rows
-    # per workgroup, all multiplying the same B vectors (4 blocks on 4 waves)
-    N, K = 4 * 97, 8 * 75
+    # per workgroup, all multiplying the same B vectors (4 blocks on 4 waves);
+    # K = 600 gives every wave at most 5 steps (A loaded per step), K = 2056
+    # 16 or 17 (A staged through LDS in chunks of 16 or 8 steps, the last
+    # step ragged)
+    N = 4 * 97
     for M in range(17, 65):
         A = I.random_bits((M, K), ("normal", 0.0, 1.0), dtype, 1800 + M)
         B = I.random_bits((K, N), ("normal", 0.0, 0.02), dtype, 1850 + M)
         bias = I.random_bits((N,), ("normal", 0.0, 0.1), dtype, 1870 + M)
-        log(f"[skinny rows] {I.DTYPE_NAMES[dtype]} M={M}")
+        log(f"[skinny rows] {I.DTYPE_NAMES[dtype]} M={M} K={K}")
         ref64, _ = oracle.gemm(M, N, K, dtype, A, B, bias, I.EPI_BIAS_GELU_TANH)
         out = run(M, N, K, dtype, A, B, bias, I.EPI_BIAS_GELU_TANH, path=tg.TG_PATH_SKINNY)
         check_tolerance(dtype, to_bits(out), ref64, f"skinny M={M}")
@@ -170,10 +174,13 @@ def test_skinny_row_blocks_full_size(M, N, K):
     (1, 520, 4008),       # 126 steps, the last with 8 of its 32 k
     (11, 68, 3336),       # 105 steps: 26 or 27 per wave; one partial slab
     (7, 132, 2184),       # 69 steps: 17 or 18 per wave, the fewest that preload
+    (16, 4 * 97, 8200),   # 257 steps: 64 or 65 per wave, A staged in chunks of 32 steps
+    (3, 132, 5128),       # 161 steps: 40 or 41 per wave, the second chunk of 8 or 9 steps
 ])
 def test_skinny_preloaded_A(dtype, M, N, K):
-    # Shapes where every wave has 17..32 steps of 32 k, so the skinny kernel
-    # stages its slice of A through LDS before streaming B.
+    # Shapes where every wave has more than 16 steps of 32 k, so the skinny
+    # kernel stages its slice of A through LDS (whole, or in chunks of 32
+    # steps) instead of loading A with every step of B.
     A = I.random_bits((M, K), ("normal", 0.0, 1.0), dtype, 900 + M)
     B = I.random_bits((K, N), ("normal", 0.0, 0.02), dtype, 901 + M)
     bias = I.random_bits((N,), ("normal", 0.0, 0.1), dtype, 902 + M)
