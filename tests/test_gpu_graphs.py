@@ -75,3 +75,63 @@ def test_replays_match_eager_calls():
         torch.cuda.synchronize()
         for name, t, e in zip(("tiled", "skinny", "w4", "attention"), (C1, C2, C3, O), eager):
             assert np.array_equal(to_bits(t), e), f"replay {rep}: {name} differs from the eager call"
+
+
+def test_static_split_replays_match_eager_calls():
+    """The allocation-free split-K entry point (tg_gemm_split_static) is for
+    callers under graph capture: after one eager call on the device (which
+    looks its scratch array up and zeroes the counters, outside capture),
+    even splits and stream-K captured into one graph replay to the eager
+    bits, every replay leaving the counters zero for the next."""
+    import torch
+    dt = I.F16
+    shapes = [(16, 4096, 2048, 4), (7, 2048, 4104, tg.TG_SPLIT_STREAM_K), (16, 11008, 1024, 0)]
+    ops = []
+    for i, (M, N, K, splits) in enumerate(shapes):
+        A = to_device(I.random_bits((M, K), ("normal", 0.0, 1.0), dt, 14100 + i).reshape(M, K), dt)
+        B = to_device(I.random_bits((K, N), ("normal", 0.0, 0.02), dt, 14110 + i).reshape(K, N), dt)
+        bias = to_device(I.random_bits((N,), ("normal", 0.0, 0.1), dt, 14120 + i), dt)
+        C = torch.empty((M, N), dtype=A.dtype, device="cuda")
+        ops.append((M, N, K, splits, A, B, bias, C))
+
+    def calls():
+        stream = torch.cuda.current_stream().cuda_stream   # the capture stream inside torch.cuda.graph
+        for M, N, K, splits, A, B, bias, C in ops:
+            st = tg.tg_gemm_split_static(splits, M, N, K, dt, A.data_ptr(), B.data_ptr(), bias.data_ptr(),
+                                         I.EPI_BIAS_GELU_TANH, C.data_ptr(), stream)
+            assert st == tg.TG_OK, tg.tg_status_string(st)
+
+    log("[graph static] eager calls")
+    calls()
+    torch.cuda.synchronize()
+    eager = [to_bits(op[7]) for op in ops]
+    for (M, N, K, splits, A, B, bias, C), e in zip(ops, eager):
+        rows = np.arange(M)
+        ref64, _ = oracle.gemm(M, N, K, dt, to_bits(A).reshape(-1), to_bits(B).reshape(-1), to_bits(bias),
+                               I.EPI_BIAS_GELU_TANH, rows)
+        check_tolerance(dt, e, ref64, f"eager static split M={M} N={N} K={K} splits={splits}")
+
+    log("[graph static] capture")
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g):
+            calls()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for op in ops:
+            op[7].fill_(float("nan"))
+        ops[0][4].float().sum().item()   # unrelated eager work between replays
+        log(f"[graph static] replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        for (M, N, K, splits, *_rest), e in zip(ops, eager):
+            assert np.array_equal(to_bits(_rest[-1]), e), \
+                f"replay {rep}: M={M} N={N} K={K} splits={splits} differs from the eager call"
+    # eager calls after the replays still see zero counters
+    calls()
+    torch.cuda.synchronize()
+    for op, e in zip(ops, eager):
+        assert np.array_equal(to_bits(op[7]), e), "eager call after the replays"
