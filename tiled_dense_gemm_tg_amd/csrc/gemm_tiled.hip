@@ -23,6 +23,11 @@
 //     stages each slice is requested S - 2 slices before it is used, with 2
 //     stages right after the barrier that frees its stage; one barrier per
 //     slice, before its last k-step;
+//   * LDS holds the A tiles of all stages, then their B tiles, and the k-loop
+//     is unrolled over the ring, so a fragment read names its stage in the
+//     instruction's offset field instead of adding it to the lane's address
+//     (24 fewer vector adds per slice at 256 x 256; the per-lane address
+//     registers hold the offsets within a tile, plus the B region's start);
 //   * A is staged as [BM m][BK k] (k-contiguous, what a 16-bit MFMA operand
 //     holds per lane) and read with ds_read_b128; B stays [BK k][BN n] as in
 //     memory and its MFMA fragments come from ds_read_b64_tr_b16, which hands
@@ -106,6 +111,8 @@ struct Cfg {
     // t + S - 1; with 2 stages the last k-step issues all D loads of slice t + 2
     static_assert(S == 2 ? D <= 2 * MFMAS : (D % KS == 0 && D / KS <= MFMAS), "loads fit the k-steps");
     static constexpr int OCCUPANCY = (S * STAGE_BYTES <= LDS_BYTES / 2 && WAVES == 4) ? 2 : 1;   // workgroups per CU
+    // LDS: the A tiles of the S stages, then their B tiles
+    static constexpr int B_REGION = S * A_BYTES;
     // this wave's loads pending, when waiting for slice t + 1 at the barrier of
     // slice t in the steady state: slices t + 2 .. t + S - 2 and the part of
     // slice t + S - 1 issued before the barrier
@@ -135,14 +142,28 @@ __device__ __forceinline__ int a_swz(int row) {
 // (the 64 banks span 256 bytes, so only the chunk index mod 16 matters).
 __device__ __forceinline__ int b_swz(int k) { return ((k & 1) ? 10 : 0) ^ ((k & 2) ? 4 : 0); }
 
+// LDS addresses of one stage's A and B tiles.  All stages' A tiles come
+// first and then all B tiles, so that with the stage known at compile time
+// (the k-loop is unrolled over the ring) a fragment read's address is the
+// lane's register plus an instruction offset below 64 KiB, with no add per
+// read, wherever the A tiles and the B tiles each span at most 64 KiB.
+struct StageAt {
+    uint32_t a, b;
+};
+template <class C>
+__device__ __forceinline__ StageAt stage_at(uint32_t lds0, int st) {
+    return StageAt{lds0 + (uint32_t)st * (uint32_t)C::A_BYTES,
+                   lds0 + (uint32_t)C::B_REGION + (uint32_t)st * (uint32_t)C::B_BYTES};
+}
+
 // Per-lane addressing of the D direct loads that fill one stage.  Wave w,
 // lane L:
 //   A load q < QA: tile rows A_ROWS_PER_WAVE w + RPD q + L/ACH, physical
 //      chunk L%ACH -> logical chunk c = L%ACH ^ a_swz(row) (8 k);
-//      destination stage + A_BYTES/WAVES w + 1024 q;
+//      destination the stage's A tile + A_BYTES/WAVES w + 1024 q;
 //   B load q < QB: k-row B_ROWS_PER_WAVE w + RB q + L/CPR, physical chunk
 //      L%CPR -> logical chunk c = L%CPR ^ b_swz(k) (8 n); destination
-//      stage + A_BYTES + B_BYTES/WAVES w + 1024 q.
+//      the stage's B tile + B_BYTES/WAVES w + 1024 q.
 // Loads of one operand share m0 in groups of four (their destination is m0
 // + 4096 (q/4), the group's m0, plus the instruction offset 1024 (q%4),
 // which is also added to the memory offset; the lane offsets subtract it
@@ -181,7 +202,7 @@ struct Dma {
             b_off[q] = SHIFT - 1024u * (q & 3) + (uint32_t)k * b_row + 2u * (uint32_t)(n0 + 8 * c);
         }
         m0_a = lds0 + (uint32_t)(C::A_BYTES / C::WAVES) * (uint32_t)wave;
-        m0_b = lds0 + (uint32_t)C::A_BYTES + (uint32_t)(C::B_BYTES / C::WAVES) * (uint32_t)wave;
+        m0_b = lds0 + (uint32_t)C::B_REGION + (uint32_t)(C::B_BYTES / C::WAVES) * (uint32_t)wave;
     }
 
     // Direct load d (0..D-1) of k-slice kt into LDS stage st: A load d for
@@ -189,20 +210,19 @@ struct Dma {
     // no lane needs the K mask (only the last slice can be partial).
     template <bool FULL, int DI>
     __device__ __forceinline__ void issue_one(int kt, int st) const {
-        const int k0 = kt * C::BK;
-        const uint32_t sbase = (uint32_t)st * (uint32_t)C::STAGE_BYTES;
+        const int k0 = __builtin_amdgcn_readfirstlane(kt * C::BK);   // uniform: address arithmetic in SGPRs
         if constexpr (DI < C::QA) {
             constexpr int q = DI;
             uint32_t off = a_off[q] + 2u * (uint32_t)k0;
             if constexpr (!FULL)
                 off += (k0 + a_k[q] < K) ? 0u : OOB_BUMP;
-            dma16<1024 * (q & 3)>(ra, off, m0_a + sbase + 4096u * (q >> 2));
+            dma16<1024 * (q & 3)>(ra, off, m0_a + (uint32_t)st * (uint32_t)C::A_BYTES + 4096u * (q >> 2));
         } else {
             constexpr int q = DI - C::QA;
             uint32_t off = b_off[q] + (uint32_t)k0 * b_row;
             if constexpr (!FULL)
                 off += (k0 + b_k[q] < K) ? 0u : OOB_BUMP;
-            dma16<1024 * (q & 3)>(rb, off, m0_b + sbase + 4096u * (q >> 2));
+            dma16<1024 * (q & 3)>(rb, off, m0_b + (uint32_t)st * (uint32_t)C::B_BYTES + 4096u * (q >> 2));
         }
     }
 
@@ -218,8 +238,9 @@ struct Dma {
     }
 };
 
-// Per-lane LDS byte offsets (within a stage) of the fragment reads of k-step
-// s (16 k each):
+// Per-lane LDS byte offsets of the fragment reads of k-step s (16 k each),
+// for A from the stage's A tile, for B from the start of all stages' B tiles
+// (the stage's place among them is added to it):
 //   A, ds_read_b128: row wm*WM + 32 i + l%32, logical chunk 2 s + l/32;
 //   B, ds_read_b64_tr_b16 twice (k 0..3 and 4..7 of the lane's 8): lane
 //      16 G + q addresses k-row 16 s + 8 (G/2) + q/4 (+4), columns
@@ -250,7 +271,8 @@ struct FragAddr {
         for (int j = 0; j < C::J; ++j) {
             const int n = wn * C::WN + 32 * j + 16 * (G & 1) + 4 * (q & 3);
             const int c = (n >> 3) ^ bsw;
-            b[j] = (uint32_t)C::A_BYTES + (uint32_t)C::B_ROW * (uint32_t)kr + 16u * (uint32_t)c + 8u * (uint32_t)(q & 1);
+            b[j] = (uint32_t)C::B_REGION + (uint32_t)C::B_ROW * (uint32_t)kr + 16u * (uint32_t)c +
+                   8u * (uint32_t)(q & 1);
         }
     }
 };
@@ -272,12 +294,14 @@ __device__ __forceinline__ u32x2 lds_tr(uint32_t byte) {
 // Fragment read number r (0..READS-1) of k-step s: r < I is A row-block r,
 // then B column-block (r-I)/2, first (k 0..3) or second (k 4..7) half.
 template <class C>
-__device__ __forceinline__ void read_one(Frag<C> &f, const FragAddr<C> &ad, uint32_t stage, int s, int r) {
+__device__ __forceinline__ void read_one(Frag<C> &f, const FragAddr<C> &ad, StageAt stage, int s, int r) {
     if (r < C::I) {
-        f.a[r] = lds_u4(stage + ad.a[s][r]);
+        f.a[r] = lds_u4(stage.a + ad.a[s][r]);
     } else {
         const int j = (r - C::I) >> 1;
-        const uint32_t b = stage + ad.b[j] + (uint32_t)(16 * C::B_ROW * s);
+        // ad.b holds the B region's base, so that what is added to it is the
+        // stage's place within the region (an instruction offset)
+        const uint32_t b = (stage.b - (uint32_t)C::B_REGION) + ad.b[j] + (uint32_t)(16 * C::B_ROW * s);
         if (((r - C::I) & 1) == 0) {
             const u32x2 v = lds_tr(b);
             f.b[j].x = v.x;
@@ -308,7 +332,7 @@ struct DmaAfter {
 };
 
 template <class C, int R0, int... R>
-__device__ __forceinline__ void read_range(Frag<C> &nxt, const FragAddr<C> &ad, uint32_t rstage, int rs,
+__device__ __forceinline__ void read_range(Frag<C> &nxt, const FragAddr<C> &ad, StageAt rstage, int rs,
                                            std::integer_sequence<int, R...>) {
     (read_one<C>(nxt, ad, rstage, rs, R0 + R), ...);
 }
@@ -321,7 +345,7 @@ __device__ __forceinline__ void read_range(Frag<C> &nxt, const FragAddr<C> &ad, 
 // matrix unit stays busy.
 template <class C, class T, bool READ, int H, int Q, typename DmaFn>
 __device__ __forceinline__ void kstep_one(const Frag<C> &cur, Frag<C> &nxt, f32x16 (&acc)[C::I][C::J],
-                                          const FragAddr<C> &ad, uint32_t rstage, int rs, DmaFn &dma) {
+                                          const FragAddr<C> &ad, StageAt rstage, int rs, DmaFn &dma) {
     acc[Q / C::J][Q % C::J] = T::mfma32(cur.b[Q % C::J], cur.a[Q / C::J], acc[Q / C::J][Q % C::J]);
     if constexpr (READ) {
         constexpr int LO = ReadsAfter<C, Q>::LO, HI = ReadsAfter<C, Q>::HI;
@@ -342,7 +366,7 @@ __device__ __forceinline__ void kstep_one(const Frag<C> &cur, Frag<C> &nxt, f32x
 
 template <class C, class T, bool READ, int H, typename DmaFn, int... Q>
 __device__ __forceinline__ void kstep_seq(const Frag<C> &cur, Frag<C> &nxt, f32x16 (&acc)[C::I][C::J],
-                                          const FragAddr<C> &ad, uint32_t rstage, int rs, DmaFn &dma,
+                                          const FragAddr<C> &ad, StageAt rstage, int rs, DmaFn &dma,
                                           std::integer_sequence<int, Q...>) {
     (kstep_one<C, T, READ, H, Q>(cur, nxt, acc, ad, rstage, rs, dma), ...);
 }
@@ -351,7 +375,7 @@ __device__ __forceinline__ void kstep_seq(const Frag<C> &cur, Frag<C> &nxt, f32x
 // stage at rstage are read into `nxt`; H direct loads through dma(p).
 template <class C, class T, bool READ, int H, typename DmaFn>
 __device__ __forceinline__ void kstep(const Frag<C> &cur, Frag<C> &nxt, f32x16 (&acc)[C::I][C::J],
-                                      const FragAddr<C> &ad, uint32_t rstage, int rs, DmaFn dma) {
+                                      const FragAddr<C> &ad, StageAt rstage, int rs, DmaFn dma) {
     kstep_seq<C, T, READ, H>(cur, nxt, acc, ad, rstage, rs, dma, std::make_integer_sequence<int, C::MFMAS>{});
 }
 
@@ -370,7 +394,7 @@ __device__ __forceinline__ void kstep(const Frag<C> &cur, Frag<C> &nxt, f32x16 (
 // that wave's own wait orders the two writes.  Chunks of B rows crossing
 // n = N elsewhere only feed columns that are never stored.
 template <class C, class T>
-__device__ __forceinline__ void fix_last_slice(const GemmArgs &g, int m0, int n0, int kl, uint32_t stage) {
+__device__ __forceinline__ void fix_last_slice(const GemmArgs &g, int m0, int n0, int kl, StageAt stage) {
     const int k0 = kl * C::BK;
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
@@ -386,7 +410,7 @@ __device__ __forceinline__ void fix_last_slice(const GemmArgs &g, int m0, int n0
         for (int q = 0; q < 8; ++q)
             e[q] = q < v ? __builtin_amdgcn_raw_buffer_load_b16(ra, (int)(base + 2u * q), 0, 0) : (uint16_t)0;
         const u32x4 chunk = {pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]), pack2(e[6], e[7])};
-        *(__attribute__((address_space(3))) u32x4 *)(uintptr_t)(stage + (uint32_t)(C::A_ROW * r) +
+        *(__attribute__((address_space(3))) u32x4 *)(uintptr_t)(stage.a + (uint32_t)(C::A_ROW * r) +
                                                                 16u * (uint32_t)(cp ^ a_swz<C::ACH>(r))) = chunk;
     }
     if (g.N % 8 != 0 && n0 <= g.N - 1 && g.N - 1 < n0 + C::BN) {
@@ -400,8 +424,7 @@ __device__ __forceinline__ void fix_last_slice(const GemmArgs &g, int m0, int n0
             for (int q = 0; q < 8; ++q)
                 e[q] = __builtin_amdgcn_raw_buffer_load_b16(rb, (int)(base + 2u * q), 0, 0);
             const u32x4 chunk = {pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]), pack2(e[6], e[7])};
-            *(__attribute__((address_space(3))) u32x4 *)(uintptr_t)(stage + (uint32_t)C::A_BYTES +
-                                                                    (uint32_t)C::B_ROW * r +
+            *(__attribute__((address_space(3))) u32x4 *)(uintptr_t)(stage.b + (uint32_t)C::B_ROW * r +
                                                                     16u * (c ^ b_swz(r))) = chunk;
         }
     }
@@ -427,11 +450,19 @@ template <class C>
 struct WaveStage {
     static constexpr int CPRW = C::WN / 8;                     // 16-byte chunks per buffer row
     static constexpr int BUF = 32 * C::WN * 2;                 // bytes per wave: 32 rows x WN
-    static constexpr int PER_STAGE = C::STAGE_BYTES / BUF;     // buffers per stage
+    static constexpr int PER_A = C::A_BYTES / BUF;             // buffers in a stage's A tile
+    static constexpr int PER_STAGE = PER_A + C::B_BYTES / BUF; // and in its B tile
+    static_assert(PER_A * BUF == C::A_BYTES && (PER_STAGE - PER_A) * BUF == C::B_BYTES, "buffers tile the stage");
     static_assert(PER_STAGE >= 1 && (C::WAVES + PER_STAGE - 1) / PER_STAGE <= C::S - 1,
                   "wave buffers fit the stages other than the last slice's");
     static __device__ __forceinline__ uint32_t swz(int row) {
         return (uint32_t)((row ^ (row / CPRW)) & (CPRW - 1));
+    }
+    // wave w's buffer: in the stages after the last slice's (nk - 1) % S
+    static __device__ __forceinline__ uint32_t buffer(uint32_t lds0, int nk, int w) {
+        const StageAt st = stage_at<C>(lds0, (nk + w / PER_STAGE) % C::S);
+        const int p = w % PER_STAGE;
+        return p < PER_A ? st.a + (uint32_t)(p * BUF) : st.b + (uint32_t)((p - PER_A) * BUF);
     }
 };
 
@@ -444,8 +475,7 @@ __device__ __forceinline__ void store_tile_wave(const GemmArgs &args, const f32x
     const int lr = lane & 31;
     const int lh = lane >> 5;
     // the stage of the last slice is (nk - 1) % S; the next ones are free
-    const uint32_t buf = lds0 + (uint32_t)(((nk + wave / W::PER_STAGE) % C::S) * C::STAGE_BYTES) +
-                         (uint32_t)((wave % W::PER_STAGE) * W::BUF);
+    const uint32_t buf = W::buffer(lds0, nk, wave);
     // The bias of all J four-column groups of this lane, requested at once
     // (range-checked: columns past N read zero).
     uint32_t braw[C::J][4][2];
@@ -556,7 +586,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCCUPANCY) void gemm_tiled_kernel(Ge
     const int wm = wave / C::WGN;
     const int wn = wave % C::WGN;
     const uint32_t lds0 = lds_address(smem);
-    auto stage = [&](int st) { return lds0 + (uint32_t)st * (uint32_t)C::STAGE_BYTES; };
+    auto stage = [&](int st) { return stage_at<C>(lds0, st); };
     const int tiles_m = (args.M + C::BM - 1) / C::BM;
     const int tiles_n = (args.N + C::BN - 1) / C::BN;
     const int total = tiles_m * tiles_n;
@@ -615,20 +645,24 @@ __global__ __launch_bounds__(C::THREADS, C::OCCUPANCY) void gemm_tiled_kernel(Ge
         //   k-step KS-1: MFMAs, reads of step 0 of slice t + 1 into f[0], and
         //       the last D/KS loads of slice t + S - 1 (S >= 3) or all D loads
         //       of slice t + 2 into stage t % 2, just freed (S == 2).
-        // ISSUE: 0 = no loads, 1 = loads of a full slice, 2 = loads of the
-        // (possibly partial) last slice.  WAIT: this wave's loads younger than
-        // slice t + 1's at the barrier.  FIX: slice t + 1 is the last one of a
-        // GEN shape.
-        auto slice = [&](int t, auto issue, auto wait, auto next, auto fix) __attribute__((always_inline)) {
+        // RES: t % S when known at compile time (the stages' LDS addresses
+        // are then constants), -1 otherwise.  ISSUE: 0 = no loads, 1 = loads
+        // of a full slice, 2 = loads of the (possibly partial) last slice.
+        // WAIT: this wave's loads younger than slice t + 1's at the barrier.
+        // FIX: slice t + 1 is the last one of a GEN shape.
+        auto slice = [&](int t, auto res, auto issue, auto wait, auto next, auto fix) __attribute__((always_inline)) {
+            constexpr int R = decltype(res)::value;
             constexpr int IK = decltype(issue)::value;
             constexpr bool FULL = IK == 1;
             constexpr bool NEXT = decltype(next)::value;
             constexpr int HP = (S >= 3 && IK != 0) ? D / KS : 0;            // loads per step before the barrier
             constexpr int HL = IK == 0 ? 0 : (S >= 3 ? D / KS : D);         // loads in the last step
             constexpr int BL = S >= 3 ? (KS - 1) * (D / KS) : 0;            // first load index of the last step
-            const uint32_t st = stage(t % S);
+            const int r0 = R >= 0 ? R : t % S;
+            const int r1 = R >= 0 ? (R + 1) % S : (t + 1) % S;
+            const int kst = R >= 0 ? (R + LEAD) % S : (t + LEAD) % S;
+            const StageAt st = stage(r0);
             const int kt = t + LEAD;
-            const int kst = kt % S;
             auto pre = [&](auto s) __attribute__((always_inline)) {
                 constexpr int SI = decltype(s)::value;
                 auto dma_s = [&](auto p) __attribute__((always_inline)) {
@@ -640,24 +674,30 @@ __global__ __launch_bounds__(C::THREADS, C::OCCUPANCY) void gemm_tiled_kernel(Ge
             if constexpr (NEXT) {
                 wait_vmcnt<decltype(wait)::value>();
                 if constexpr (GEN && decltype(fix)::value)
-                    fix_last_slice<C, T>(args, m0, n0, t + 1, stage((t + 1) % S));
+                    fix_last_slice<C, T>(args, m0, n0, t + 1, stage(r1));
                 __syncthreads();
             }
             auto dma_l = [&](auto p) __attribute__((always_inline)) {
                 dma.template issue_one<FULL, BL + decltype(p)::value>(kt, kst);
             };
-            kstep<C, T, NEXT, HL>(f[(KS - 1) & 1], f[0], acc, fad, stage((t + 1) % S), 0, dma_l);
+            kstep<C, T, NEXT, HL>(f[(KS - 1) & 1], f[0], acc, fad, stage(r1), 0, dma_l);
         };
         using yes = std::true_type;
         using no = std::false_type;
         using full = std::integral_constant<int, 1>;
         using last = std::integral_constant<int, 2>;
         using w_steady = std::integral_constant<int, C::WAIT_STEADY>;
+        using any = std::integral_constant<int, -1>;
         int t = 0;
+        // full slices S at a time, each with its stage fixed at compile time
+        for (; t + S - 1 + LEAD < nk - 1; t += S)
+            for_each_index([&](auto r) __attribute__((always_inline)) {
+                slice(t + decltype(r)::value, r, full{}, w_steady{}, yes{}, no{});
+            }, std::make_integer_sequence<int, S>{});
         for (; t + LEAD < nk - 1; ++t)
-            slice(t, full{}, w_steady{}, yes{}, no{});
+            slice(t, any{}, full{}, w_steady{}, yes{}, no{});
         if (t + LEAD == nk - 1) {
-            slice(t, last{}, w_steady{}, yes{}, no{});
+            slice(t, any{}, last{}, w_steady{}, yes{}, no{});
             ++t;
         }
         // the last LEAD slices request nothing: slice nk - 1 - j waits for
@@ -666,10 +706,10 @@ __global__ __launch_bounds__(C::THREADS, C::OCCUPANCY) void gemm_tiled_kernel(Ge
             constexpr int J = LEAD - 1 - decltype(jj)::value;
             if (t == nk - 1 - J) {
                 if constexpr (J == 0)
-                    slice(t, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, no{}, no{});
+                    slice(t, any{}, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, no{}, no{});
                 else
-                    slice(t, std::integral_constant<int, 0>{}, std::integral_constant<int, (J - 1) * D>{}, yes{},
-                          std::integral_constant<bool, J == 1>{});
+                    slice(t, any{}, std::integral_constant<int, 0>{}, std::integral_constant<int, (J - 1) * D>{},
+                          yes{}, std::integral_constant<bool, J == 1>{});
                 ++t;
             }
         };
