@@ -397,7 +397,8 @@ def fit_tile_model(meas, cus):
     per configuration, a1 + b1 K for a round of one tile per CU on every CU
     (two points in K), a2 + b2 K for a round of two per CU (two workgroups per
     CU only), kappa (a round on a fraction u of the CUs takes 1 - kappa (1 - u)
-    of the full-load time: less contention), phi (rounds after the first:
+    of the full-load time: less contention; measured at u = 1/4, and u below
+    that is priced as 1/4), phi (rounds after the first:
     the 8192-cube's time over its rounds' prediction) and rho (misaligned
     shapes, K and N not multiples of 8: time over the aligned time)."""
     out = {}
@@ -429,7 +430,7 @@ def predict_tile_time(p, M, N, K, cus, aligned):
         if busy > cus:    # some CUs hold two workgroups
             t += p["a2"] + p["b2"] * K
         else:
-            t += (p["a1"] + p["b1"] * K) * (1.0 - p["kappa"] * (1.0 - busy / cus))
+            t += (p["a1"] + p["b1"] * K) * (1.0 - p["kappa"] * (1.0 - max(busy / cus, 0.25)))
         left -= busy
         rounds += 1
     if rounds > 1:

@@ -296,7 +296,7 @@ def test_tiles_plan_checks_arguments(lib):
     (2048, 2048, 2048, tg.TG_TILES_128x128),    # 64 tiles of 256x256 would leave 3/4 of the CUs idle
     (1024, 1024, 8192, tg.TG_TILES_128x128),
     (1000, 3000, 6000, tg.TG_TILES_128x128),
-    (512, 11008, 4096, tg.TG_TILES_128x256),    # 172 tiles either way; 128x256 is the faster of the two
+    (512, 11008, 4096, tg.TG_TILES_256x128_K64),   # 172 tiles of 256x128 or 128x256; the k64 one is fastest
     (17, 11008, 4096, tg.TG_TILES_128x128),     # one row of tiles: the smallest tile wastes least
 ])
 def test_tiles_plan_on_an_mi355x(lib, M, N, K, cfg):

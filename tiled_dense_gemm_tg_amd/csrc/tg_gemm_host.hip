@@ -127,7 +127,9 @@ int num_cu_of(hipStream_t stream) {
 // 128 x 128 tiles) workgroup per CU; a round of one tile per CU on every CU
 // takes a1 + b1 K, a round with two on some CUs a2 + b2 K, and a round on a
 // fraction u of the CUs (1 - kappa (1 - u)) of the full-load time (less
-// contention for caches and memory); rounds after the first take phi times
+// contention for caches and memory), with u taken as at least a quarter, the
+// smallest fraction the sweep measures (a round on fewer CUs is not priced
+// below it); rounds after the first take phi times
 // longer, and misaligned shapes (K or N not a multiple of 8, or unaligned
 // pointers) rho times longer.  The parameters come from a sweep of every
 // configuration on one MI355X (bench.py --sweep: one tile per CU at two K,
@@ -154,8 +156,10 @@ double predicted_time(const TileChoice &c, int64_t M, int64_t N, int64_t K, int 
         const int64_t busy = left < per_round ? left : per_round;
         if (busy > num_cu)
             t += c.a2 + c.b2 * double(K);
-        else
-            t += (c.a1 + c.b1 * double(K)) * (1.0 - c.kappa * (1.0 - double(busy) / double(num_cu)));
+        else {
+            const double u = double(busy) / double(num_cu);
+            t += (c.a1 + c.b1 * double(K)) * (1.0 - c.kappa * (1.0 - (u > 0.25 ? u : 0.25)));
+        }
         left -= busy;
         ++rounds;
     }
