@@ -216,13 +216,14 @@ def test_empty_K_gives_epilogue_of_zero(cfg, epi):
 
 @pytest.mark.parametrize("cfg", CONFIGS, ids=_name)
 def test_every_pipeline_depth(cfg):
-    """K from one slice to several more than the stage ring holds, exact and
-    ragged, so every prologue, steady, last-request and tail step of the
-    pipeline runs (integers: exact)."""
+    """K from one slice to two turns of the stage ring past the first
+    requests, exact and ragged, so every prologue, steady (unrolled over the
+    ring, and its remainders of 0 .. S-1 slices), last-request and tail step
+    of the pipeline runs (integers: exact)."""
     dtype = I.BF16
     M, N = 136, 264
-    bk = tg.TILES_AXES[cfg][2]
-    for n in range(1, 8):
+    bk, stages = tg.TILES_AXES[cfg][2], tg.TILES_AXES[cfg][3]
+    for n in range(1, 2 * stages + 6):
         for K in (n * bk, n * bk - 5):
             A = I.small_int_bits((M, K), dtype, 13700 + K)
             B = I.small_int_bits((K, N), dtype, 13800 + K)
