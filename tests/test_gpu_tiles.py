@@ -233,6 +233,55 @@ def test_every_pipeline_depth(cfg):
             check_exact(to_bits(run(M, N, K, dtype, A, B, bias, I.EPI_BIAS, tiles=cfg)), refq, f"K={K}")
 
 
+def _odd_n_shapes(cfg):
+    bn, bk = TILE_SHAPE[cfg][1], tg.TILES_AXES[cfg][2]
+    ns = [1, 3, bn - 1, bn + 1, 2 * bn + 1, 2 * bn + 5, 2 * bn + 7, 2 * bn + 9]
+    ks = [1, 2, bk, 3 * bk, 3 * bk - 2, 3 * bk - 1, 5 * bk + 6]
+    return [(ns[i % len(ns)], ks[i % len(ks)]) for i in range(len(ns) * len(ks))][::3]
+
+
+@pytest.mark.parametrize("cfg", CONFIGS, ids=_name)
+def test_odd_n_every_chunk_of_the_last_row(cfg):
+    """N odd (every other k-row of B starts 2 bytes past a 4-byte boundary):
+    widths that end in every position of a tile and one element past it,
+    with K even and odd (B's last row, whose chunk crossing N is rewritten
+    from element loads, odd or even) and exact or ragged in k; integers:
+    exact."""
+    dtype = I.F16
+    M = 72
+    for idx, (N, K) in enumerate(_odd_n_shapes(cfg)):
+        A = I.small_int_bits((M, K), dtype, 14200 + idx)
+        B = I.small_int_bits((K, N), dtype, 14300 + idx)
+        bias = I.small_int_bits((N,), dtype, 14400 + idx)
+        _, refq = oracle.gemm(M, N, K, dtype, A, B, bias, I.EPI_BIAS)
+        what = f"tiles={_name(cfg)} M={M} N={N} K={K}"
+        log(f"[tiles-odd-n] {what}")
+        check_exact(to_bits(run(M, N, K, dtype, A, B, bias, I.EPI_BIAS, tiles=cfg)), refq, what)
+
+
+@pytest.mark.parametrize("cfg", CONFIGS, ids=_name)
+@pytest.mark.parametrize("K", [96, 95, 70])
+def test_odd_n_does_not_mix_columns(cfg, K):
+    """N odd: the last column of every tile holds +inf in every row of B, so
+    exactly those columns of C are infinite; a chunk put one column off
+    would move an infinity into a neighbour."""
+    bn = TILE_SHAPE[cfg][1]
+    M, N = 136, 3 * bn + 17
+    dtype = I.BF16
+    A = I.random_bits((M, K), ("uniform", 0.5, 1.0), dtype, 14500)
+    B = I.random_bits((K, N), ("uniform", -1.0, 1.0), dtype, 14501).reshape(K, N).copy()
+    inf_cols = np.arange(bn - 1, N, bn)
+    B[:, inf_cols] = np.uint16(0x7F80)
+    ref64, _ = oracle.gemm(M, N, K, dtype, A, B.reshape(-1))
+    log(f"[tiles-odd-n-inf] tiles={_name(cfg)} K={K}")
+    bits = to_bits(run(M, N, K, dtype, A, B.reshape(-1), tiles=cfg)).reshape(M, N)
+    got = oracle.decode(dtype, bits)
+    assert np.isposinf(got[:, inf_cols]).all()
+    finite = np.setdiff1d(np.arange(N), inf_cols)
+    check_tolerance(dtype, np.ascontiguousarray(bits[:, finite]).reshape(-1),
+                    ref64.reshape(M, N)[:, finite].reshape(-1), "finite columns")
+
+
 @pytest.mark.parametrize("group_m", [1, 2, 3, 8, 64])
 def test_raster_group_changes_nothing_but_the_order(group_m):
     """tg_gemm_tiled_grouped: every group size covers every tile once
