@@ -48,6 +48,10 @@ def _sample(Bn, Sq, H, n, seed):
     (I.F16, 1, 5, 777, 2, False),
     (I.F16, 1, 4096, 4096, 32, True),     # the measured shape, sampled queries
     (I.BF16, 1, 4096, 4096, 32, False),
+    (I.BF16, 2, 700, 700, 3, True),       # causal, ragged last query and key blocks, two batches
+    (I.F16, 1, 257, 257, 2, True),        # one query past a query block
+    (I.F16, 1, 1000, 130, 4, False),      # many query blocks over a short, ragged key range
+    (I.F16, 1, 8192, 8192, 8, True),      # the longer sequence the notes quote, sampled queries
 ])
 def test_attention_matches_oracle(dtype, Bn, Sq, Sk, H, causal):
     Q = I.random_bits((Bn, Sq, H, D), ("normal", 0.0, 1.0), dtype, 700 + Sq)
@@ -58,6 +62,22 @@ def test_attention_matches_oracle(dtype, Bn, Sq, Sk, H, causal):
     log(f"[attn] dtype={dtype} B={Bn} Sq={Sq} Sk={Sk} H={H} causal={causal}")
     got = _run(Bn, Sq, Sk, H, dtype, Q, K, V, causal)
     check_tolerance(dtype, got[idx], ref64, "attention")
+
+
+@pytest.mark.parametrize("dtype,causal", [(I.F16, False), (I.BF16, True)])
+def test_attention_large_scores(dtype, causal):
+    """Q and K drawn 4x wider, so scores spread over hundreds (in log2
+    units) and the reference maximum of the online softmax moves many times
+    (every move rescales the partial output and sum)."""
+    Bn, Sq, Sk, H = 1, 600, 600 if causal else 900, 2
+    Q = I.random_bits((Bn, Sq, H, D), ("normal", 0.0, 4.0), dtype, 720)
+    K = I.random_bits((Bn, Sk, H, D), ("normal", 0.0, 4.0), dtype, 721)
+    V = I.random_bits((Bn, Sk, H, D), ("normal", 0.0, 1.0), dtype, 722)
+    idx, qs = _sample(Bn, Sq, H, 96, 723)
+    ref64, _ = oracle.attention(Bn, Sq, Sk, H, D, dtype, Q, K, V, causal=causal, queries=qs)
+    log(f"[attn-large] dtype={dtype} causal={causal}")
+    got = _run(Bn, Sq, Sk, H, dtype, Q, K, V, causal)
+    check_tolerance(dtype, got[idx], ref64, "attention, large scores")
 
 
 @pytest.mark.parametrize("dtype", [I.F16, I.BF16])
