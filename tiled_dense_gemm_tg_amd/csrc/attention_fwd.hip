@@ -115,9 +115,25 @@ __device__ __forceinline__ u32x2 lds_tr(uint32_t byte) {
     return __builtin_bit_cast(u32x2, v);
 }
 
-__device__ __forceinline__ float lane_swap32(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
-        (int)((((int)threadIdx.x & 63) ^ 32) << 2), __builtin_bit_cast(int, x)));
+// The maximum and the sum of x over lanes l and l ^ 32, in every lane, from
+// v_permlane32_swap (a VALU exchange of one register's lanes 32-63 with
+// another's lanes 0-31, no LDS round trip): with x in both registers, the
+// first ends up holding the lower half's x in both halves and the second the
+// upper half's, and one more VALU op combines them.  Written as assembly
+// because the compiler's builtin for the instruction returns its first
+// result for both at -O3; the combining op sits in the same block so the
+// compiler adds no NaN-quieting ops around an opaque result.  Two wait
+// states separate the exchange from the VALU write of its operands and from
+// the VALU read of its results.
+__device__ __forceinline__ float max_of_halves(float x) {
+    float a = x, b = x;
+    asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1\n\tv_max_f32 %0, %0, %1" : "+v"(a), "+v"(b));
+    return a;
+}
+__device__ __forceinline__ float sum_of_halves(float x) {   // lower half's x + upper half's x
+    float a = x, b = x;
+    asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1\n\tv_add_f32 %0, %0, %1" : "+v"(a), "+v"(b));
+    return a;
 }
 
 template <class T, bool CAUSAL>
@@ -316,7 +332,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attention_fwd_kernel(AttnArgs arg
                 return mx;
             };
             float mx = need_mask ? mask_max(std::true_type{}) : mask_max(std::false_type{});
-            mx = fmaxf(mx, lane_swap32(mx));
+            mx = max_of_halves(mx);
             const float m_blk = mx * c;
             // lazy rescaling: move the maximum only when it grew by more than 2^8
             if (__builtin_amdgcn_ballot_w64(m_blk > m_used + RESCALE_LOG2) != 0) {
@@ -376,7 +392,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attention_fwd_kernel(AttnArgs arg
     const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
         args.O, (short)0, (int)((uint32_t)args.B * (uint32_t)Sq * tok), 0x00020000);
     {
-        const float l_tot = l_sum + lane_swap32(l_sum);
+        const float l_tot = sum_of_halves(l_sum);
         const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
         const uint32_t base = ((uint32_t)b * (uint32_t)Sq + (uint32_t)qi) * tok + 2u * (uint32_t)h * HD;
 #pragma unroll
