@@ -313,18 +313,18 @@ __global__ __launch_bounds__(NTHREADS, 1) void attention_fwd_kernel(AttnArgs arg
             auto mask_max = [&](auto mask_c) __attribute__((always_inline)) {
                 constexpr bool MASK = decltype(mask_c)::value;
                 // visible if off < Sk - key0 and (causal) off <= qi - key0, with a
-                // compile-time off = 8 (e/4) + e%4
+                // compile-time off = 8 (e/4) + e%4: one compare against the
+                // smaller bound
                 const int key0 = kb + 32 * kt + 4 * lh;
                 const int tail = Sk - key0;
-                const int diag = qi - key0;
+                const int lim = CAUSAL ? min(tail, qi - key0 + 1) : tail;
                 float mx = -INFINITY;
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     float v = sacc[e];
                     if constexpr (MASK) {
                         const int off = 8 * (e >> 2) + (e & 3);
-                        const bool ok = off < tail && (!CAUSAL || off <= diag);
-                        v = ok ? v : -INFINITY;
+                        v = off < lim ? v : -INFINITY;
                         sacc[e] = v;
                     }
                     mx = fmaxf(mx, v);
