@@ -52,7 +52,7 @@ constexpr int QW = 32;                    // queries per wave
 constexpr int BM = QW * WAVES;            // queries per workgroup
 constexpr int BN = 128;                   // keys per block
 constexpr int STAGES = 2;
-constexpr int KV_BYTES = BN * HD * 2;     // 16 KiB: one block of K (or V) in LDS
+constexpr int KV_BYTES = BN * HD * 2;     // 32 KiB: one block of K (or V) in LDS
 constexpr int STAGE_BYTES = 2 * KV_BYTES;
 constexpr uint32_t SHIFT = 4096;          // buffers start 4 KiB before K and V
 constexpr uint32_t OOB_BUMP = 0x80000000u;
