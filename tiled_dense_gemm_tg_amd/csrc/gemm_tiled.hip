@@ -41,9 +41,10 @@
 //   * MFMA fragments are double-buffered in registers: the reads for the next
 //     k-step are issued between the MFMAs of the current one;
 //   * the MFMA takes the B fragment first, so each lane ends up with 4
-//     consecutive output columns of a row; after the fused bias + GELU(tanh)
-//     epilogue each wave's block of C goes through LDS 32 rows at a time
-//     and leaves as row segments;
+//     consecutive output columns of a row; the accumulators of a tile start
+//     at the bias of their columns, so after the k-loop only GELU(tanh) and
+//     the rounding are left, and each wave's block of C then goes through
+//     LDS 32 rows at a time and leaves as row segments;
 //   * persistent grid with an XCD-aware grouped raster of the tiles
 //     (tg_tile.h); the smaller tiles fit two workgroups per CU.
 //
@@ -466,6 +467,52 @@ struct WaveStage {
     }
 };
 
+// The accumulators of a tile start at the bias of their columns (zero
+// without a bias): the fused epilogue's bias then enters the fp32 sum first
+// instead of last, which is another rounding order of the same sum (integer
+// valued sums stay exact), and the epilogue after the k-loop is left with
+// GELU and the conversion.  Element 4 q + r of block (i, j) of lane l holds
+// column wn WN + 32 j + 8 q + 4 (l / 32) + r for every i.  Range-checked
+// loads: columns past N read zero.
+template <class C, class T, int EPI, bool ALIGNED>
+__device__ __forceinline__ void init_acc(f32x16 (&acc)[C::I][C::J], const GemmArgs &args, int n0, int wn,
+                                         int lane) {
+    f32x16 first[C::J];
+#pragma unroll
+    for (int j = 0; j < C::J; ++j)
+        first[j] = f32x16{};
+    if constexpr (EPI != EPI_NONE) {
+        const __amdgpu_buffer_rsrc_t rb = tile::buffer_of(args.bias, 2u * (uint32_t)args.N);
+        const int lh = lane >> 5;
+#pragma unroll
+        for (int j = 0; j < C::J; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t off = 2u * (uint32_t)(n0 + wn * C::WN + 32 * j + 8 * q + 4 * lh);
+                uint16_t e[4];
+                if constexpr (ALIGNED) {   // N % 8 == 0: a group is all inside or all outside
+                    const u32x2 raw = __builtin_amdgcn_raw_buffer_load_b64(rb, (int)off, 0, 0);
+                    e[0] = (uint16_t)(raw.x & 0xffff);
+                    e[1] = (uint16_t)(raw.x >> 16);
+                    e[2] = (uint16_t)(raw.y & 0xffff);
+                    e[3] = (uint16_t)(raw.y >> 16);
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        e[r] = __builtin_amdgcn_raw_buffer_load_b16(rb, (int)(off + 2u * r), 0, 0);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    first[j][4 * q + r] = T::to_f32(e[r]);
+            }
+    }
+#pragma unroll
+    for (int i = 0; i < C::I; ++i)
+#pragma unroll
+        for (int j = 0; j < C::J; ++j)
+            acc[i][j] = first[j];
+}
+
 // C leaves with the non-temporal cache policy: nothing reads it again in the
 // kernel, and lines of C kept in L2 would only displace the A and B panels
 // the other tiles of the XCD still read (≈1 % on every tiled shape measured).
@@ -481,30 +528,6 @@ __device__ __forceinline__ void store_tile_wave(const GemmArgs &args, const f32x
     const int lh = lane >> 5;
     // the stage of the last slice is (nk - 1) % S; the next ones are free
     const uint32_t buf = W::buffer(lds0, nk, wave);
-    // The bias of all J four-column groups of this lane, requested at once
-    // (range-checked: columns past N read zero).
-    uint32_t braw[C::J][4][2];
-    if constexpr (EPI != EPI_NONE) {
-        const __amdgpu_buffer_rsrc_t rb = tile::buffer_of(args.bias, 2u * (uint32_t)N);
-#pragma unroll
-        for (int j = 0; j < C::J; ++j)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint32_t off = 2u * (uint32_t)(n0 + wn * C::WN + 32 * j + 8 * q + 4 * lh);
-                if constexpr (ALIGNED) {   // N % 8 == 0: a group is all inside or all outside
-                    const u32x2 raw = __builtin_amdgcn_raw_buffer_load_b64(rb, (int)off, 0, 0);
-                    braw[j][q][0] = raw.x;
-                    braw[j][q][1] = raw.y;
-                } else {
-                    uint16_t e[4];
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        e[r] = __builtin_amdgcn_raw_buffer_load_b16(rb, (int)(off + 2u * r), 0, 0);
-                    braw[j][q][0] = pack2(e[0], e[1]);
-                    braw[j][q][1] = pack2(e[2], e[3]);
-                }
-            }
-    }
     const __amdgpu_buffer_rsrc_t rc = tile::buffer_of(args.C, 2u * (uint32_t)M * (uint32_t)N);
 #pragma unroll
     for (int i = 0; i < C::I; ++i) {
@@ -512,17 +535,11 @@ __device__ __forceinline__ void store_tile_wave(const GemmArgs &args, const f32x
         for (int j = 0; j < C::J; ++j) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                float bv[4] = {0.f, 0.f, 0.f, 0.f};
-                if constexpr (EPI != EPI_NONE) {
-                    bv[0] = T::to_f32((uint16_t)(braw[j][q][0] & 0xffff));
-                    bv[1] = T::to_f32((uint16_t)(braw[j][q][0] >> 16));
-                    bv[2] = T::to_f32((uint16_t)(braw[j][q][1] & 0xffff));
-                    bv[3] = T::to_f32((uint16_t)(braw[j][q][1] >> 16));
-                }
                 uint16_t o[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    o[r] = T::from_f32(epilogue<EPI>(acc[i][j][4 * q + r], bv[r]));
+                for (int r = 0; r < 4; ++r)   // the bias is in the accumulator already
+                    o[r] = T::from_f32(EPI == EPI_BIAS_GELU_TANH ? gelu_tanh(acc[i][j][4 * q + r])
+                                                                 : acc[i][j][4 * q + r]);
                 const uint32_t chunk = (uint32_t)(4 * j + q) ^ W::swz(lr);
                 *(__attribute__((address_space(3))) u32x2 *)(uintptr_t)(
                     buf + (uint32_t)(2 * C::WN * lr) + 16u * chunk + 8u * (uint32_t)lh) =
@@ -611,11 +628,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCCUPANCY) void gemm_tiled_kernel(Ge
         const Dma<C> dma(args, m0, n0, wave, lane, lds0);
 
         f32x16 acc[C::I][C::J];
-#pragma unroll
-        for (int i = 0; i < C::I; ++i)
-#pragma unroll
-            for (int j = 0; j < C::J; ++j)
-                acc[i][j] = f32x16{};
+        init_acc<C, T, EPI, !GEN>(acc, args, n0, wn, lane);
 
         Frag<C> f[2];
         // Prologue: request slices 0 .. min(LEAD, nk) - 1, wait for slice 0.
