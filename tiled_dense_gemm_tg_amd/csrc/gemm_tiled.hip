@@ -170,13 +170,24 @@ __device__ __forceinline__ StageAt stage_at(uint32_t lds0, int st) {
 // which is also added to the memory offset; the lane offsets subtract it
 // back).  So that they stay non-negative, the buffers start 4 KB before the
 // operands (offsets are operand offsets + 4096) and are 4 KB longer.
-template <class C>
+// Lanes whose rows lie at m >= M (A) or whose whole chunk lies at n >= N (B)
+// only feed outputs that are never stored: their offset is 2^31, beyond every
+// buffer, so they read zeros.  The slices of the steady loop (all but the
+// prologue's and the last) lie inside [0, K - 1), so there every other A
+// lane's chunk is inside A, and the slice's k offset goes into the load's
+// soffset, with no vector add.  B does the same when SOFF_B: with N % 8 == 0
+// (so N >= 8) a B chunk that crosses N ends inside the next k-row, which
+// exists; with N < 8 it could run past B's last row, so the other instance
+// adds the k offset to the lane offset, where the range check sees it.  The
+// prologue's and the last slice add it to the lane offset too and send
+// k >= K beyond the buffer, as the range check zeroes them.
+template <class C, bool SOFF_B>
 struct Dma {
     static constexpr uint32_t SHIFT = 4096;
     i32x4 ra, rb;
-    uint32_t a_off[C::QA];   // buffer offset of this lane's A chunk for load q, k0 = 0, minus 1024 (q%4)
+    uint32_t a_off[C::QA];   // buffer offset of this lane's A chunk for load q, k0 = 0, minus 1024 (q%4); 2^31 for m >= M
     int a_k[C::QA];          // first k of the lane's A chunk of load q within the slice
-    uint32_t b_off[C::QB];   // buffer offset of this lane's B chunk for load q, k0 = 0, minus 1024 (q%4)
+    uint32_t b_off[C::QB];   // the same for B; 2^31 for a chunk at n >= N
     int b_k[C::QB];          // k-row of load q within the slice
     uint32_t b_row;          // bytes per row of B
     uint32_t m0_a, m0_b;     // LDS destinations of load q = 0 in stage 0
@@ -192,15 +203,17 @@ struct Dma {
         for (int q = 0; q < C::QA; ++q) {
             const int row = arow + C::RPD * q;   // row within the tile
             a_k[q] = 8 * ((int)((unsigned)lane % C::ACH) ^ a_swz<C::ACH>(row));
-            a_off[q] = SHIFT - 1024u * (q & 3) +
-                       2u * ((uint32_t)(m0 + row) * (uint32_t)g.K + (uint32_t)a_k[q]);
+            a_off[q] = m0 + row < g.M ? SHIFT - 1024u * (q & 3) +
+                                            2u * ((uint32_t)(m0 + row) * (uint32_t)g.K + (uint32_t)a_k[q])
+                                      : OOB_BUMP;
         }
 #pragma unroll
         for (int q = 0; q < C::QB; ++q) {
             const int k = C::B_ROWS_PER_WAVE * wave + C::RB * q + (int)((unsigned)lane / C::CPR);
             const int c = (int)((unsigned)lane % C::CPR) ^ b_swz(k);
             b_k[q] = k;
-            b_off[q] = SHIFT - 1024u * (q & 3) + (uint32_t)k * b_row + 2u * (uint32_t)(n0 + 8 * c);
+            b_off[q] = n0 + 8 * c < g.N ? SHIFT - 1024u * (q & 3) + (uint32_t)k * b_row + 2u * (uint32_t)(n0 + 8 * c)
+                                        : OOB_BUMP;
         }
         m0_a = lds0 + (uint32_t)(C::A_BYTES / C::WAVES) * (uint32_t)wave;
         m0_b = lds0 + (uint32_t)C::B_REGION + (uint32_t)(C::B_BYTES / C::WAVES) * (uint32_t)wave;
@@ -214,16 +227,24 @@ struct Dma {
         const int k0 = __builtin_amdgcn_readfirstlane(kt * C::BK);   // uniform: address arithmetic in SGPRs
         if constexpr (DI < C::QA) {
             constexpr int q = DI;
-            uint32_t off = a_off[q] + 2u * (uint32_t)k0;
-            if constexpr (!FULL)
-                off += (k0 + a_k[q] < K) ? 0u : OOB_BUMP;
-            dma16<1024 * (q & 3)>(ra, off, m0_a + (uint32_t)st * (uint32_t)C::A_BYTES + 4096u * (q >> 2));
+            const uint32_t m0 = m0_a + (uint32_t)st * (uint32_t)C::A_BYTES + 4096u * (q >> 2);
+            if constexpr (FULL) {
+                dma16s<1024 * (q & 3)>(ra, a_off[q], 2u * (uint32_t)k0, m0);
+            } else {
+                const uint32_t off = (a_off[q] + 2u * (uint32_t)k0) | ((k0 + a_k[q] < K) ? 0u : OOB_BUMP);
+                dma16<1024 * (q & 3)>(ra, off, m0);
+            }
         } else {
             constexpr int q = DI - C::QA;
-            uint32_t off = b_off[q] + (uint32_t)k0 * b_row;
-            if constexpr (!FULL)
-                off += (k0 + b_k[q] < K) ? 0u : OOB_BUMP;
-            dma16<1024 * (q & 3)>(rb, off, m0_b + (uint32_t)st * (uint32_t)C::B_BYTES + 4096u * (q >> 2));
+            const uint32_t m0 = m0_b + (uint32_t)st * (uint32_t)C::B_BYTES + 4096u * (q >> 2);
+            if constexpr (FULL && SOFF_B) {
+                dma16s<1024 * (q & 3)>(rb, b_off[q], __builtin_amdgcn_readfirstlane((uint32_t)k0 * b_row), m0);
+            } else if constexpr (FULL) {
+                dma16<1024 * (q & 3)>(rb, b_off[q] + (uint32_t)k0 * b_row, m0);
+            } else {
+                const uint32_t off = (b_off[q] + (uint32_t)k0 * b_row) | ((k0 + b_k[q] < K) ? 0u : OOB_BUMP);
+                dma16<1024 * (q & 3)>(rb, off, m0);
+            }
         }
     }
 
@@ -625,7 +646,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCCUPANCY) void gemm_tiled_kernel(Ge
         tile::tile_of_index(tiles_m, tiles_n, w, args.group_m, tm, tn);
         const int m0 = tm * C::BM;
         const int n0 = tn * C::BN;
-        const Dma<C> dma(args, m0, n0, wave, lane, lds0);
+        const Dma<C, !GEN> dma(args, m0, n0, wave, lane, lds0);
 
         f32x16 acc[C::I][C::J];
         init_acc<C, T, EPI, !GEN>(acc, args, n0, wn, lane);

@@ -44,6 +44,19 @@ __device__ __forceinline__ void dma16(const i32x4 &rsrc, uint32_t voffset, uint3
                  "i"(OFF));
 }
 
+// dma16 with a wave-uniform byte offset in an SGPR (the instruction's
+// soffset), added to every lane's address without a vector add.  Whether the
+// range check of the buffer covers soffset is not relied on: a caller passes
+// it only where voffset + soffset + OFF lies inside the buffer for every lane
+// whose voffset + OFF does, and gives a lane that must read zeros a voffset
+// of 2^31 or more (with voffset + soffset + OFF still below 2^32).
+template <int OFF>
+__device__ __forceinline__ void dma16s(const i32x4 &rsrc, uint32_t voffset, uint32_t soffset, uint32_t m0) {
+    static_assert(OFF >= 0 && OFF < 4096, "12-bit instruction offset");
+    asm volatile("buffer_load_dwordx4 %0, %1, %2 offen offset:%4 lds" ::"v"(voffset), "s"(rsrc), "s"(soffset),
+                 "{m0}"(m0), "i"(OFF));
+}
+
 // dma16 with the instruction offset 1024 rq (rq = 0..3, a compile-time value
 // after unrolling): loads of one 4 KB block share m0.
 __device__ __forceinline__ void dma16_rq(int rq, const i32x4 &rsrc, uint32_t voffset, uint32_t m0) {
