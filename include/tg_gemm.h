@@ -17,6 +17,9 @@
  *   gelu_tanh(x) = 0.5*x*(1 + tanh(sqrt(2/pi)*(x + 0.044715*x^3)))
  *
  * followed by one round-to-nearest-even conversion to the output format.
+ * The order of the fp32 additions is the kernel's; with a bias epilogue the
+ * bias may enter the fp32 sum as its first term (y + bias[j] up to that
+ * rounding order; exact whenever every partial sum is).
  *
  * Layout and ownership
  *   All matrices are dense, row-major and packed: A has row stride K, B has
