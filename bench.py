@@ -44,6 +44,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -441,26 +442,97 @@ def predict_tile_time(p, M, N, K, cus, aligned):
 TILE_MODEL_INC = os.path.join(ROOT, "tiled_dense_gemm_tg_amd", "csrc", "tg_tile_model.inc")
 
 
+# The rows of the model table in the library's order (the default first).
+TILE_ENUM = {"256x256": "TG_TILES_256x256", "256x128": "TG_TILES_256x128", "128x256": "TG_TILES_128x256",
+             "128x128": "TG_TILES_128x128", "256x256_k64": "TG_TILES_256x256_K64",
+             "256x128_k64": "TG_TILES_256x128_K64", "128x256_k64": "TG_TILES_128x256_K64",
+             "128x128_k64": "TG_TILES_128x128_K64", "256x256_w8": "TG_TILES_256x256_W8"}
+TILE_SWEEP_MD = os.path.join(ROOT, "profiles", "tile_sweep.md")
+
+
+def _tile_row(name, p):
+    bm, bn = (int(v) for v in name.split("_")[0].split("x"))
+    occ = 2 if (bm, bn) == (128, 128) else 1
+    return dict(p, bm=bm, bn=bn, occ=occ, a2=p.get("a2", 0.0), b2=p.get("b2", 0.0))
+
+
+def model_choice(model, M, N, K, cus, aligned=True):
+    """The configuration the library's auto_tiles picks with these model
+    parameters: rows in table order, a row taking over only when its
+    prediction is below 0.98 of the best so far."""
+    pick, best = None, None
+    for name in TILE_ENUM:
+        t = predict_tile_time(_tile_row(name, model[name]), M, N, K, cus, aligned)
+        if best is None or t < best * 0.98:
+            pick, best = name, t
+    return pick
+
+
 def write_tile_model(sweep: dict, path: str = TILE_MODEL_INC) -> None:
     """Writes the cost model's parameter table (the rows of kTileChoices in
     tg_gemm_host.hip) from a --sweep result; the default configuration comes
     first (ties go to earlier rows)."""
     model = sweep["tile_sweep"]["model"] if "tile_sweep" in sweep else sweep["model"]
-    enum = {"256x256": "TG_TILES_256x256", "256x128": "TG_TILES_256x128", "128x256": "TG_TILES_128x256",
-            "128x128": "TG_TILES_128x128", "256x256_k64": "TG_TILES_256x256_K64",
-            "256x128_k64": "TG_TILES_256x128_K64", "128x256_k64": "TG_TILES_128x256_K64",
-            "128x128_k64": "TG_TILES_128x128_K64", "256x256_w8": "TG_TILES_256x256_W8"}
     lines = ["// tg_tile_model.inc -- parameters of the tile-choice cost model (see auto_tiles in",
              "// tg_gemm_host.hip), written by bench.py from `python3 bench.py --sweep` on one MI355X:",
              "// {tiles, BM, BN, workgroups per CU, a1, b1, a2, b2, kappa, phi, rho}, times in us."]
-    for name in enum:
-        p = model[name]
-        bm, bn = (int(v) for v in name.split("_")[0].split("x"))
-        occ = 2 if (bm, bn) == (128, 128) else 1
-        lines.append(f"    {{{enum[name]}, {bm}, {bn}, {occ}, {p['a1']:.6g}, {p['b1']:.6g}, {p.get('a2', 0.0):.6g}, "
-                     f"{p.get('b2', 0.0):.6g}, {p['kappa']:.6g}, {p['phi']:.6g}, {p['rho']:.6g}}},")
+    for name in TILE_ENUM:
+        p = _tile_row(name, model[name])
+        lines.append(f"    {{{TILE_ENUM[name]}, {p['bm']}, {p['bn']}, {p['occ']}, {p['a1']:.6g}, {p['b1']:.6g}, "
+                     f"{p['a2']:.6g}, {p['b2']:.6g}, {p['kappa']:.6g}, {p['phi']:.6g}, {p['rho']:.6g}}},")
     with open(path, "w") as fh:
         fh.write("\n".join(lines) + "\n")
+
+
+def write_sweep_summary(sweep: dict, path: str = TILE_SWEEP_MD) -> None:
+    """profiles/tile_sweep.md from a --sweep result: the measured times, the
+    fitted parameters, the raster-group sweep and, per shape class, the
+    configuration the model fitted from this sweep picks (model_choice)
+    against the fastest measured."""
+    d = sweep["tile_sweep"] if "tile_sweep" in sweep else sweep
+    meas, model, cus = d["measured_us"], d["model"], d["cus"]
+
+    def f(v):
+        return v if isinstance(v, str) else f"{v:.1f}"
+    L = ["# Tile-configuration sweep (tiled family)", "",
+         "Commands (one MI355X, committed files only; the second writes `tiled_dense_gemm_tg_amd/csrc/tg_tile_model.inc`",
+         "and this file):", "",
+         "```", "python3 bench.py --sweep > sweep.json", "python3 bench.py --write-tile-model sweep.json", "```", "",
+         f"CUs: {cus}. fp16 operands normal(0, 0.1), no epilogue. Times in us, one block of launches each after a settle.", "",
+         "| configuration (BM x BN, BK, stages, waves) | one tile per CU, K=2048 | K=8192 | two per CU, K=2048 | K=8192 "
+         "| a quarter of the CUs, K=8192 | 8192-cube | ragged (K, N not multiples of 8), K=8187 |",
+         "|---|---|---|---|---|---|---|---|"]
+    for name, m in meas.items():
+        bm, bn = (int(v) for v in name.split("_")[0].split("x"))
+        bk = 64 if "k64" in name else 32
+        stages = {"256x256_k64": 2, "128x128_k64": 2}.get(name, 3 if "k64" in name else 4)
+        waves = 8 if name.endswith("_w8") else 4
+        pair = m.get("pair", ["-", "-"])
+        L.append(f"| {name} ({bm}x{bn}, {bk}, {stages}, {waves}) | {f(m['solo'][0])} | {f(m['solo'][1])} | "
+                 f"{f(pair[0])} | {f(pair[1])} | {f(m['quarter'])} | {f(m['full'])} | {f(m['ragged'])} |")
+    L += ["", "Fitted model parameters (`fit_tile_model` in bench.py; the table the library compiles in). A round on a "
+          "fraction u of", "the CUs is priced at (1 - kappa (1 - max(u, 1/4))) of a full round: the sweep measures "
+          "u = 1/4 and nothing below it.", "",
+          "| configuration | a1 | b1 | a2 | b2 | kappa | phi | rho |", "|---|---|---|---|---|---|---|---|"]
+    for name, p in model.items():
+        L.append(f"| {name} | {p['a1']:.3f} | {p['b1']:.6f} | {p.get('a2', 0):.3f} | {p.get('b2', 0):.6f} | "
+                 f"{p['kappa']:.3f} | {p['phi']:.3f} | {p['rho']:.3f} |")
+    L += ["", "Raster group size (tile rows per group, `tg_gemm_tiled_grouped`), configuration the library picks:", "",
+          "| shape | group_m=1 | group_m=2 | group_m=4 | group_m=8 | group_m=16 |", "|---|---|---|---|---|---|"]
+    for shape, g in d["raster_groups"].items():
+        L.append(f"| {shape} | " + " | ".join(f"{g[f'group_m={k}']:.1f}" for k in (1, 2, 4, 8, 16)) + " |")
+    L += ["", "Shape classes, every configuration in alternating blocks (the same function as the bench line "
+          "`tile_choice`); `auto` is", "the configuration the model fitted from this sweep picks (`model_choice`, "
+          "the library's `auto_tiles` rule), priced at this sweep's time:", "",
+          "| shape | auto | auto us | fastest | fastest us | auto / fastest |", "|---|---|---|---|---|---|"]
+    for shape, c in d["shape_classes"].items():
+        M, N, K = (int(x) for x in re.search(r"(\d+)x(\d+)x(\d+)", shape).groups())
+        auto = model_choice(model, M, N, K, cus)
+        pc = c["per_config_us"]
+        fastest = min(pc, key=pc.get)
+        L.append(f"| {shape} | {auto} | {pc[auto]} | {fastest} | {pc[fastest]} | {pc[auto] / pc[fastest]:.3f} |")
+    with open(path, "w") as fh:
+        fh.write("\n".join(L) + "\n")
 
 
 def tile_sweep(torch, tg, I, steps, warmup):
@@ -952,14 +1024,16 @@ def main() -> int:
     ap.add_argument("--summarise", default=None, metavar="DIR",
                     help="only summarise the rocprofv3 runs under DIR into profiles/")
     ap.add_argument("--write-tile-model", default=None, metavar="SWEEP_JSON",
-                    help="only write the tile-choice model table from a --sweep output line")
+                    help="only write the tile-choice model table and profiles/tile_sweep.md from a --sweep output line")
     args = ap.parse_args()
     if args.summarise:
         summarise_profiles(args.summarise, os.path.join(ROOT, "profiles"))
         return 0
     if args.write_tile_model:
         with open(args.write_tile_model) as fh:
-            write_tile_model(json.loads([ln for ln in fh.read().splitlines() if ln.startswith("{")][-1]))
+            sweep = json.loads([ln for ln in fh.read().splitlines() if ln.startswith("{")][-1])
+        write_tile_model(sweep)
+        write_sweep_summary(sweep)
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this GEMM runs on a single "
