@@ -806,6 +806,19 @@ def _mean(v):
     return sum(v) / len(v) if v else float("nan")
 
 
+def counter_means(run_dir: str) -> dict:
+    """Per bench line of one rocprofv3 --pmc run under run_dir (its CSV and
+    the dispatch log bench.py wrote beside it): the number of the library's
+    dispatches, their mean duration and the mean of every counter over them
+    (each counter summed over its dimensions, as rocprofv3 reports it)."""
+    out = {}
+    for label, recs in _group(_dispatches(run_dir, "**/*counter_collection.csv", True)).items():
+        keys = sorted({k for r in recs for k in r if k not in ("name", "dur_us")})
+        out[label] = {"dispatches": len(recs), "dur_us": _mean([r["dur_us"] for r in recs]),
+                      **{k: _mean([r.get(k, 0.0) for r in recs]) for k in keys}}
+    return out
+
+
 def _bench_json(path: str):
     with open(path) as fh:
         lines = [ln for ln in fh.read().splitlines() if ln.startswith("{")]
@@ -1023,11 +1036,16 @@ def main() -> int:
                     help="no settling, short lines: for rocprofv3 counter runs")
     ap.add_argument("--summarise", default=None, metavar="DIR",
                     help="only summarise the rocprofv3 runs under DIR into profiles/")
+    ap.add_argument("--counter-means", default=None, metavar="DIR",
+                    help="only print, per bench line, the mean of every counter of the rocprofv3 --pmc run under DIR")
     ap.add_argument("--write-tile-model", default=None, metavar="SWEEP_JSON",
                     help="only write the tile-choice model table and profiles/tile_sweep.md from a --sweep output line")
     args = ap.parse_args()
     if args.summarise:
         summarise_profiles(args.summarise, os.path.join(ROOT, "profiles"))
+        return 0
+    if args.counter_means:
+        print(json.dumps(counter_means(args.counter_means), indent=1))
         return 0
     if args.write_tile_model:
         with open(args.write_tile_model) as fh:

@@ -103,3 +103,24 @@ def test_dispatch_log_labels_the_unfused_passes(tmp_path):
                       "main unfused_gelu unfused product", "main unfused_gelu unfused bias pass",
                       "main unfused_gelu unfused GELU pass", "main"]
     assert all(rec["dur_us"] == 0.5 for _, rec in got)
+
+
+def test_counter_means_per_bench_line(tmp_path):
+    # --counter-means averages every counter of a --pmc run over the
+    # dispatches of each bench line (rows of one dispatch and counter are
+    # summed first, as rocprofv3 splits some counters over dimensions).
+    run = tmp_path / "run"
+    run.mkdir()
+    log = bench.DispatchLog()
+    log.note("a", 2)
+    log.note("b", 1)
+    (run / "dispatch_log.json").write_text(json.dumps({"entries": log.entries}))
+    hdr = "Dispatch_Id,Kernel_Name,Start_Timestamp,End_Timestamp,Counter_Name,Counter_Value\n"
+    rows = ["1,tg::k,0,2000,X,10", "1,tg::k,0,2000,X,5", "1,tg::k,0,2000,Y,1",
+            "2,tg::k,0,4000,X,30", "2,tg::k,0,4000,Y,3",
+            "7,other_kernel,0,1,X,1000",
+            "3,tg::k,0,1000,X,7", "3,tg::k,0,1000,Y,0"]
+    (run / "run_counter_collection.csv").write_text(hdr + "\n".join(rows) + "\n")
+    got = bench.counter_means(str(run))
+    assert got == {"a": {"dispatches": 2, "dur_us": 3.0, "X": 22.5, "Y": 2.0},
+                   "b": {"dispatches": 1, "dur_us": 1.0, "X": 7.0, "Y": 0.0}}
